@@ -1,0 +1,156 @@
+"""TurboQuant hot path for AMD MI355X (gfx950).
+
+Python face of libtq.so: quantize key/value vectors into the packed rotated-codebook +
+QJL-sign format, run decode attention and inner-product top-k search straight from the
+packed bytes.  These wrappers only check shapes/dtypes, allocate outputs with torch and
+pass pointers and the current HIP stream to the C ABI declared in include/tq.h; all
+arithmetic runs in the library's kernels.  A missing library raises, never falls back.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import numpy as np
+
+from ._lib import (LIB_PATH, TQ_BF16, TQ_F16, TQ_F32, Format, Tables, TQError, build_codebook,
+                   load)
+
+__all__ = ["Format", "Tables", "TQError", "build_codebook", "quantize_kv", "attend_decode",
+           "ip_search", "attend_workspace_bytes", "search_workspace_bytes", "LIB_PATH", "load"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    if t.dtype == torch.float16:
+        return TQ_F16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise TQError(code, what)
+
+
+def quantize_kv(x, fmt: Format, tables: Tables, counters=None, codes=None, norms=None):
+    """Quantize the rows of x ([..., d_in], fp32 / bf16 / fp16 CUDA tensor, unit stride in
+    the last dim).  Returns (codes uint8 [n, record_bytes], norms fp16 [n, 2]); pass
+    preallocated `codes`/`norms` to write in place.  `counters` (int64 CUDA tensor of 4)
+    accumulates the diagnostics documented in tq.h."""
+    torch = _torch()
+    if not x.is_cuda:
+        raise ValueError("x must be a CUDA tensor")
+    d_in = x.shape[-1]
+    x2 = x.reshape(-1, d_in)
+    if x2.stride(-1) != 1:
+        x2 = x2.contiguous()
+    n = x2.shape[0]
+    rb = fmt.record_bytes()
+    if codes is None:
+        codes = torch.empty((n, rb), dtype=torch.uint8, device=x.device)
+    if norms is None:
+        norms = torch.empty((n, 2), dtype=torch.float16, device=x.device)
+    if codes.numel() < n * rb or norms.numel() < 2 * n:
+        raise ValueError("output buffers too small")
+    f, t = fmt.c(), tables.c()
+    rc = load().tq_quantize_kv(ctypes.byref(f), ctypes.byref(t), _ptr(x2), _dtype_code(x2), n,
+                               d_in, x2.stride(0) if n > 1 else d_in, _ptr(codes), _ptr(norms),
+                               _ptr(counters), _stream(x.device))
+    _check(rc, "tq_quantize_kv")
+    return codes, norms
+
+
+def attend_workspace_bytes(batch, hq, hkv, capacity, d=128) -> int:
+    n = load().tq_attend_workspace_bytes(batch, hq, hkv, capacity, d)
+    if n < 0:
+        raise TQError(-2, "tq_attend_workspace_bytes")
+    return int(n)
+
+
+def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format,
+                  tables_k: Tables, fmt_v: Format = None, tables_v: Tables = None,
+                  scale: float = None, tau: float = 0.0, logits: bool = False,
+                  skipped=None, workspace=None, out=None):
+    """One decode step.  q [batch, hq, d]; codes_k [batch, hkv, capacity, rbk] uint8;
+    norms_k [batch, hkv, capacity, 2] fp16; the same for v; seq_lens int32 [batch] (CUDA).
+    Returns out fp32 [batch, hq, d] (and logits fp32 [batch, hq, capacity] if asked)."""
+    torch = _torch()
+    fmt_v = fmt_k if fmt_v is None else fmt_v
+    tables_v = tables_k if tables_v is None else tables_v
+    batch, hq, d = q.shape
+    _, hkv, capacity, _ = codes_k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for t, rb in ((codes_k, fmt_k.record_bytes()), (codes_v, fmt_v.record_bytes())):
+        if t.dtype != torch.uint8 or t.shape[:3] != (batch, hkv, capacity) or t.shape[3] != rb \
+                or not t.is_contiguous():
+            raise ValueError("bad packed cache tensor")
+    for t in (norms_k, norms_v):
+        if t.shape != (batch, hkv, capacity, 2) or not t.is_contiguous():
+            raise ValueError("bad norms tensor")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != batch:
+        raise ValueError("seq_lens must be int32 [batch]")
+    q = q.contiguous()
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
+    lg = torch.empty((batch, hq, capacity), dtype=torch.float32, device=q.device) if logits else None
+    wsb = attend_workspace_bytes(batch, hq, hkv, capacity, d)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    fk, fv, tk, tv = fmt_k.c(), fmt_v.c(), tables_k.c(), tables_v.c()
+    rc = load().tq_attend_decode(ctypes.byref(fk), ctypes.byref(tk), ctypes.byref(fv),
+                                 ctypes.byref(tv), _ptr(q), _dtype_code(q), batch, hq, hkv,
+                                 _ptr(codes_k), _ptr(norms_k), _ptr(codes_v), _ptr(norms_v),
+                                 capacity, _ptr(seq_lens), float(scale), float(tau), _ptr(out),
+                                 _ptr(lg), _ptr(skipped), _ptr(workspace), workspace.numel(),
+                                 _stream(q.device))
+    _check(rc, "tq_attend_decode")
+    return (out, lg) if logits else out
+
+
+def search_workspace_bytes(n_q, k, n_db, d) -> int:
+    n = load().tq_search_workspace_bytes(n_q, k, n_db, d)
+    if n < 0:
+        raise TQError(-2, "tq_search_workspace_bytes")
+    return int(n)
+
+
+def ip_search(queries, codes_db, norms_db, fmt: Format, tables: Tables, k: int = 10,
+              workspace=None):
+    """Top-k estimated inner products of fp32 queries [n_q, d_in] against a packed database.
+    Returns (ids int64 [n_q, k], scores fp32 [n_q, k])."""
+    torch = _torch()
+    n_q, d_in = queries.shape
+    n_db = codes_db.shape[0]
+    queries = queries.contiguous()
+    if queries.dtype != torch.float32:
+        raise TypeError("queries must be fp32")
+    ids = torch.empty((n_q, k), dtype=torch.int64, device=queries.device)
+    scores = torch.empty((n_q, k), dtype=torch.float32, device=queries.device)
+    wsb = search_workspace_bytes(n_q, k, n_db, fmt.d)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=queries.device)
+    f, t = fmt.c(), tables.c()
+    rc = load().tq_ip_search(ctypes.byref(f), ctypes.byref(t), _ptr(codes_db), _ptr(norms_db),
+                             n_db, _ptr(queries), d_in, n_q, k, _ptr(ids), _ptr(scores),
+                             _ptr(workspace), workspace.numel(), _stream(queries.device))
+    _check(rc, "tq_ip_search")
+    return ids, scores

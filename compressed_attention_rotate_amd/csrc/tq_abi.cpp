@@ -1,0 +1,175 @@
+// C ABI: argument validation and dispatch.  Every check runs on the host before any
+// launch; nothing here allocates, frees or synchronizes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_widths(int d, int lo, int hi) {
+  if (d == 128)
+    return (lo == hi && lo >= 1 && lo <= 3) || (lo == 3 && hi == 2) || (lo == 2 && hi == 1);
+  if (d == 256) return lo == hi && (lo == 2 || lo == 3);
+  return false;
+}
+
+// The kernels use the positive half of a codebook and mirror it, so tables must be
+// exactly symmetric, ascending, and the middle boundary must be 0.
+int check_codebook(int bits, const float* c, const float* b) {
+  if (!c || !b) return TQ_ERR_ARG;
+  const int L = 1 << bits;
+  for (int m = 0; m < L; ++m) {
+    if (!std::isfinite(c[m]) || c[m] != -c[L - 1 - m]) return TQ_ERR_ARG;
+    if (m + 1 < L && !(c[m] < c[m + 1])) return TQ_ERR_ARG;
+  }
+  for (int m = 0; m + 1 < L; ++m) {
+    if (b[m] != -b[L - 2 - m]) return TQ_ERR_ARG;
+    if (!(c[m] <= b[m] && b[m] <= c[m + 1])) return TQ_ERR_ARG;
+  }
+  return TQ_OK;
+}
+
+int check_tables(const tq_format* f, const tq_tables* t) {
+  if (!t || !t->signs || !t->S) return TQ_ERR_ARG;
+  if (!aligned(t->S, 16)) return TQ_ERR_ALIGN;
+  for (int j = 0; j < f->d; ++j)
+    if (t->signs[j] != 1 && t->signs[j] != -1) return TQ_ERR_ARG;
+  int rc = check_codebook(f->bits_lo, t->centroids_lo, t->bounds_lo);
+  if (rc) return rc;
+  return check_codebook(f->bits_hi, t->centroids_hi, t->bounds_hi);
+}
+
+bool dtype_ok(int dt) { return dt == TQ_F32 || dt == TQ_BF16 || dt == TQ_F16; }
+uintptr_t dtype_size(int dt) { return dt == TQ_F32 ? 4 : 2; }
+
+}  // namespace
+
+int tq_num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+extern "C" {
+
+int tq_check_format(const tq_format* f) {
+  if (!f) return TQ_ERR_ARG;
+  if (f->d != 128 && f->d != 256) return TQ_ERR_SHAPE;
+  if (f->split <= 0 || f->split > f->d || (f->split % 32)) return TQ_ERR_SHAPE;
+  const int hi = (f->split == f->d) ? f->bits_lo : f->bits_hi;
+  if (f->split == f->d && f->bits_hi != f->bits_lo) return TQ_ERR_SHAPE;
+  if (!supported_widths(f->d, f->bits_lo, hi)) return TQ_ERR_SHAPE;
+  return TQ_OK;
+}
+
+int64_t tq_record_bytes(const tq_format* f) {
+  if (tq_check_format(f) != TQ_OK) return -1;
+  const int lo_blocks = f->split / 32, hi_blocks = (f->d - f->split) / 32;
+  return 4 * ((int64_t)lo_blocks * (f->bits_lo + 1) + (int64_t)hi_blocks * (f->bits_hi + 1));
+}
+
+int tq_quantize_kv(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
+                   int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
+                   int64_t* counters, tq_stream_t stream) {
+  int rc = tq_check_format(f);
+  if (rc) return rc;
+  if (n < 0 || !dtype_ok(x_dtype)) return TQ_ERR_ARG;
+  if (d_in <= 0 || d_in > f->d || ld_x < d_in) return TQ_ERR_SHAPE;
+  rc = check_tables(f, t);
+  if (rc) return rc;
+  if (n == 0) return TQ_OK;
+  if (!x || !codes || !norms) return TQ_ERR_ARG;
+  if (!aligned(x, dtype_size(x_dtype)) || !aligned(codes, 16) || !aligned(norms, 4) ||
+      (counters && !aligned(counters, 8)))
+    return TQ_ERR_ALIGN;
+  return tq_launch_quantize(f, t, x, x_dtype, n, d_in, ld_x, codes, norms, counters,
+                            reinterpret_cast<hipStream_t>(stream));
+}
+
+int64_t tq_attend_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int64_t capacity,
+                                  int32_t d) {
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || capacity < 0 || d != 128 || hq % hkv) return -1;
+  return tq_plan_decode(batch, hq, hkv, capacity, d).ws_bytes;
+}
+
+int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                     const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
+                     int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                     const void* codes_v, const uint16_t* norms_v, int64_t capacity,
+                     const int32_t* seq_lens, float scale, float tau, float* out,
+                     float* logits, int64_t* skipped, void* workspace,
+                     int64_t workspace_bytes, tq_stream_t stream) {
+  int rc = tq_check_format(fk);
+  if (rc) return rc;
+  if ((rc = tq_check_format(fv))) return rc;
+  if (fk->d != 128 || fv->d != 128) return TQ_ERR_SHAPE;
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || capacity < 0) return TQ_ERR_ARG;
+  if (hq % hkv) return TQ_ERR_SHAPE;
+  const int g = hq / hkv;
+  if (g > 4 && g % 4) return TQ_ERR_SHAPE;
+  if (!dtype_ok(q_dtype) || !std::isfinite(scale) || !(tau >= 0.0f) || !(tau <= 1.0f)) return TQ_ERR_ARG;
+  if ((rc = check_tables(fk, tk)) || (rc = check_tables(fv, tv))) return rc;
+  if (!q || !out || !seq_lens || !workspace) return TQ_ERR_ARG;
+  if (capacity > 0 && (!codes_k || !norms_k || !codes_v || !norms_v)) return TQ_ERR_ARG;
+  if (!aligned(q, dtype_size(q_dtype)) || !aligned(codes_k, 16) || !aligned(codes_v, 16) ||
+      !aligned(norms_k, 4) || !aligned(norms_v, 4) || !aligned(seq_lens, 4) || !aligned(out, 16) ||
+      (logits && !aligned(logits, 4)) || (skipped && !aligned(skipped, 8)) || !aligned(workspace, 16))
+    return TQ_ERR_ALIGN;
+  const tq_decode_plan plan = tq_plan_decode(batch, hq, hkv, capacity, fk->d);
+  if (workspace_bytes < plan.ws_bytes) return TQ_ERR_WORKSPACE;
+  return tq_launch_decode(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
+                          norms_v, capacity, seq_lens, scale, tau, out, logits, skipped, workspace,
+                          plan, reinterpret_cast<hipStream_t>(stream));
+}
+
+int64_t tq_search_workspace_bytes(int64_t n_q, int32_t k, int64_t n_db, int32_t d) {
+  if (n_q < 0 || k < 1 || k > 64 || n_db < k || (d != 128 && d != 256)) return -1;
+  return tq_plan_search(n_q, k, n_db, d).ws_bytes;
+}
+
+int tq_ip_search(const tq_format* f, const tq_tables* t, const void* codes_db,
+                 const uint16_t* norms_db, int64_t n_db, const float* queries, int32_t d_in,
+                 int64_t n_q, int32_t k, int64_t* out_ids, float* out_scores, void* workspace,
+                 int64_t workspace_bytes, tq_stream_t stream) {
+  int rc = tq_check_format(f);
+  if (rc) return rc;
+  if (n_q < 0 || n_db < 0 || k < 1 || k > 64 || k > n_db) return TQ_ERR_ARG;
+  if (d_in <= 0 || d_in > f->d) return TQ_ERR_SHAPE;
+  if ((rc = check_tables(f, t))) return rc;
+  if (n_q == 0) return TQ_OK;
+  if (!codes_db || !norms_db || !queries || !out_ids || !out_scores || !workspace) return TQ_ERR_ARG;
+  if (!aligned(codes_db, 16) || !aligned(norms_db, 4) || !aligned(queries, 4) ||
+      !aligned(out_ids, 8) || !aligned(out_scores, 4) || !aligned(workspace, 16))
+    return TQ_ERR_ALIGN;
+  const tq_search_plan plan = tq_plan_search(n_q, k, n_db, f->d);
+  if (workspace_bytes < plan.ws_bytes) return TQ_ERR_WORKSPACE;
+  return tq_launch_search(f, t, codes_db, norms_db, n_db, queries, d_in, n_q, k, out_ids,
+                          out_scores, workspace, plan, reinterpret_cast<hipStream_t>(stream));
+}
+
+const char* tq_strerror(int code) {
+  switch (code) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_ARG: return "invalid argument";
+    case TQ_ERR_SHAPE: return "unsupported shape or format";
+    case TQ_ERR_ALIGN: return "misaligned device pointer";
+    case TQ_ERR_HIP: return "HIP runtime error";
+    case TQ_ERR_NOCONV: return "codebook iteration did not converge";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status code";
+  }
+}
+
+}  // extern "C"

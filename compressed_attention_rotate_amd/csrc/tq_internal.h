@@ -1,0 +1,46 @@
+// Internal launch entry points behind the C ABI (not exported in tq.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+// Compute units of the current device (cached per device); <= 0 on failure.
+int tq_num_cus();
+
+int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
+                       int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
+                       int64_t* counters, hipStream_t stream);
+
+struct tq_decode_plan {
+  int32_t n_split;        // token splits per (batch, kv head)
+  int32_t waves;          // waves per scan workgroup
+  int32_t parts;          // partial results per (batch, q head) = n_split * waves
+  int64_t tokens_per_split;
+  int64_t ws_qrot_off;    // byte offsets inside the workspace
+  int64_t ws_part_off;
+  int64_t ws_bytes;
+};
+
+tq_decode_plan tq_plan_decode(int32_t batch, int32_t hq, int32_t hkv, int64_t capacity, int32_t d);
+
+int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                     const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
+                     int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                     const void* codes_v, const uint16_t* norms_v, int64_t capacity,
+                     const int32_t* seq_lens, float scale, float tau, float* out, float* logits,
+                     int64_t* skipped, void* workspace, const tq_decode_plan& plan,
+                     hipStream_t stream);
+
+struct tq_search_plan {
+  int32_t n_chunks;       // database chunks scanned independently
+  int64_t chunk_len;
+  int64_t ws_q_off, ws_cand_off, ws_bytes;
+};
+
+tq_search_plan tq_plan_search(int64_t n_q, int32_t k, int64_t n_db, int32_t d);
+
+int tq_launch_search(const tq_format* f, const tq_tables* t, const void* codes_db,
+                     const uint16_t* norms_db, int64_t n_db, const float* queries, int32_t d_in,
+                     int64_t n_q, int32_t k, int64_t* out_ids, float* out_scores,
+                     void* workspace, const tq_search_plan& plan, hipStream_t stream);

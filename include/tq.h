@@ -1,0 +1,187 @@
+/*
+ * tq.h -- C ABI of the TurboQuant hot path on AMD MI355X (gfx950).
+ *
+ * The library compresses key/value vectors with the two-stage scheme the pages
+ * describe and runs decode attention and inner-product search directly on the
+ * compressed bytes:
+ *   stage 1 ("PolarQuant"): random rotation (sign flip, then Walsh-Hadamard), one
+ *     stored fp16 norm, and a precomputed per-coordinate Lloyd-Max codebook with
+ *     (b-1) bits -- 163.com explainer (m.163.com/dy/article/KOV7P8JI0556C3J2),
+ *     section "第一步：PolarQuant"; Walsh-Hadamard with a random sign flip -- zhidx
+ *     turboquant_plus article (course.zhidx.com), section "01 turboquant_plus：介绍与详解";
+ *   stage 2 ("QJL"): a 1-bit sign sketch of the residual under a Gaussian
+ *     Johnson-Lindenstrauss matrix, giving an unbiased inner-product estimator --
+ *     163.com explainer, section "第二步：QJL".
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns int: TQ_OK (0) or a negative TQ_ERR_* code.  Nothing
+ *     throws, nothing prints.  tq_strerror() names a code.
+ *   - Argument errors are detected on the host before anything is launched; then no
+ *     output is touched.
+ *   - Device entry points are asynchronous on `stream` (a hipStream_t, NULL = the
+ *     null stream).  They never allocate, free or synchronize.  A device-side fault
+ *     surfaces at the caller's next synchronization; a failed launch returns
+ *     TQ_ERR_HIP.
+ *   - The caller owns every buffer.  Pointers marked "device" must be device memory
+ *     that stays valid until the stream work that reads it has finished.  Pointers
+ *     marked "host" are read during the call only.
+ *   - Device pointers must be 16-byte aligned (TQ_ERR_ALIGN otherwise).
+ *
+ * Packed vector format (tq_format)
+ *   d in {128, 256}; coordinates j < split use bits_lo codebook bits, the others
+ *   bits_hi (split a multiple of 32; split == d means a single width).  For each block
+ *   of 32 coordinates, in order: bits_B code bit-planes (plane p holds bit p of every
+ *   code), then one word of QJL sign bits.  Bit i of a word belongs to coordinate
+ *   (or projection) 32*block + i; words are little-endian uint32; the words of one
+ *   vector are contiguous and vectors are contiguous (tq_record_bytes() bytes each).
+ *   Norms live in a separate uint16 array [n][2]: fp16 ||x|| then fp16 ||r||.
+ *   Supported widths: d = 128: (bits_lo, bits_hi) in {(1,1), (2,2), (3,3), (3,2),
+ *   (2,1)}; d = 256: (2,2), (3,3).  The "block-32" layout follows the zhidx article
+ *   (section "01 turboquant_plus：介绍与详解").
+ *
+ * Rotation (tq_tables)
+ *   y = H (D x) / sqrt(d): D = diag(signs), H the natural-order Sylvester Hadamard
+ *   matrix.  S is the d x d Gaussian JL matrix (row-major fp32, device memory);
+ *   sign bit i of a vector is 1 when (S r)_i >= 0, r its rotated-domain residual.
+ *   signs and the codebooks are host memory, copied into each launch.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_OK            0
+#define TQ_ERR_ARG      -1  /* null pointer, bad enum, negative size            */
+#define TQ_ERR_SHAPE    -2  /* unsupported d / bits / split, hq % hkv, d_in > d */
+#define TQ_ERR_ALIGN    -3  /* device pointer not 16-byte aligned               */
+#define TQ_ERR_HIP      -4  /* a HIP runtime call or kernel launch failed       */
+#define TQ_ERR_NOCONV   -5  /* codebook iteration did not converge              */
+#define TQ_ERR_WORKSPACE -6 /* workspace smaller than the *_workspace_bytes size */
+
+#define TQ_F32  0
+#define TQ_BF16 1
+#define TQ_F16  2
+
+typedef void* tq_stream_t;  /* hipStream_t */
+
+typedef struct tq_format {
+  int32_t d;        /* 128 or 256 */
+  int32_t bits_lo;  /* codebook bits (b - 1) for coordinates j < split */
+  int32_t bits_hi;  /* codebook bits for coordinates j >= split          */
+  int32_t split;    /* multiple of 32, 0 < split <= d                    */
+} tq_format;
+
+typedef struct tq_tables {
+  const float* centroids_lo;  /* host, 2^bits_lo ascending fp32 (tq_build_codebook) */
+  const float* bounds_lo;     /* host, 2^bits_lo - 1 ascending fp32                  */
+  const float* centroids_hi;  /* host, 2^bits_hi (may equal the lo pointers)         */
+  const float* bounds_hi;     /* host, 2^bits_hi - 1                                 */
+  const int8_t* signs;        /* host, d entries, each +1 or -1                      */
+  const float* S;             /* device, d x d row-major fp32                        */
+} tq_tables;
+
+/* Lloyd-Max codebook for one coordinate of a uniformly random unit vector in R^d
+ * (density proportional to (1 - t^2)^((d-3)/2) on [-1, 1]) with 2^bits levels: the
+ * fixed table that is computed once and looked up online (163.com explainer,
+ * section "第一步：PolarQuant").  Host only, synchronous, deterministic.
+ *   d        : power of two, 8 <= d <= 4096
+ *   bits     : 1..4
+ *   centroids: out, host, 2^bits fp32, ascending, exactly mirror-symmetric
+ *   bounds   : out, host, 2^bits - 1 fp32 midpoints of adjacent centroids
+ *   mse      : out, host, nullable: expected squared error per coordinate
+ * Errors: TQ_ERR_ARG, TQ_ERR_SHAPE, TQ_ERR_NOCONV. */
+int tq_build_codebook(int32_t d, int32_t bits, float* centroids, float* bounds, double* mse);
+
+/* Bytes of one packed vector's code words (norms excluded); < 0 on a bad format. */
+int64_t tq_record_bytes(const tq_format* fmt);
+
+/* TQ_OK when the kernels support `fmt`, else TQ_ERR_ARG / TQ_ERR_SHAPE. */
+int tq_check_format(const tq_format* fmt);
+
+/* Quantize n vectors (rotation, norm, codebook encode, residual, QJL signs, pack).
+ * Each vector is compressed independently with no calibration input (163.com
+ * explainer, sections "TurboQuant 怎么做的" and "四个工程属性").
+ *   x        : device, n rows of d_in elements (dtype x_dtype: TQ_F32 / TQ_BF16 /
+ *              TQ_F16), row stride ld_x elements; coordinates d_in..d-1 are zero
+ *   codes    : device out, n * tq_record_bytes(fmt) bytes
+ *   norms    : device out, n * 2 uint16 (fp16 ||x||, fp16 ||r||)
+ *   counters : device, nullable, 4 int64 the call ADDS to (caller zeroes):
+ *              [0] coordinates within 1e-6 of a codebook boundary,
+ *              [1] projections with |S r/||r|| |_i < 1e-6 (after fp64 recheck),
+ *              [2] projections rechecked in fp64 (|.| < 1e-5 in fp32),
+ *              [3] vectors whose norm overflowed fp16 (stored as +inf)
+ * n == 0 is a no-op.  Errors: TQ_ERR_ARG, TQ_ERR_SHAPE, TQ_ERR_ALIGN, TQ_ERR_HIP. */
+int tq_quantize_kv(const tq_format* fmt, const tq_tables* tab, const void* x, int32_t x_dtype,
+                   int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
+                   int64_t* counters, tq_stream_t stream);
+
+/* Workspace bytes tq_attend_decode needs for this shape. */
+int64_t tq_attend_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int64_t capacity,
+                                  int32_t d);
+
+/* One decode step of attention straight from the packed cache: logits by the
+ * unbiased estimator n16 <q_rot, c[idx]> + gamma r16 <S q_rot, 2 sigma - 1>, times
+ * `scale`; softmax; value rows dequantized and accumulated in the rotated domain
+ * and rotated back once per head (163.com explainer, sections "第二步：QJL" and
+ * "速度").  Grouped-query layout: query head h reads KV head h / (hq / hkv).
+ *   fk, tk / fv, tv : formats and tables of the key and value caches (asymmetric
+ *              K/V widths allowed: zhidx article, section "01 turboquant_plus：介绍与详解")
+ *   q        : device [batch][hq][d], dtype q_dtype (TQ_F32 / TQ_BF16 / TQ_F16)
+ *   codes_k  : device [batch][hkv][capacity] records of tq_record_bytes(fk) bytes
+ *   norms_k  : device [batch][hkv][capacity][2] uint16
+ *   codes_v, norms_v : the same for values with fv
+ *   seq_lens : device int32 [batch], each in [0, capacity]; tokens t < seq_len attend
+ *   scale    : logit scale, normally 1/sqrt(d)
+ *   tau      : Sparse-V gate (zhidx article, section "01 turboquant_plus：介绍与详解"):
+ *              0 disables it; otherwise a value row's contribution to head h is
+ *              dropped when its running softmax weight estimate is < tau.  The
+ *              estimate bounds the final weight from above, so only rows whose
+ *              final weight is < tau are dropped; the softmax denominator keeps
+ *              every row.  A row dropped by all heads of its group is not read.
+ *   out      : device out fp32 [batch][hq][d]
+ *   logits   : device out, nullable, fp32 [batch][hq][capacity] (scaled logits for
+ *              t < seq_len; other entries untouched)
+ *   skipped  : device, nullable, int64 the call ADDS the number of value rows it
+ *              did not read to
+ *   workspace: device, >= tq_attend_workspace_bytes(...) bytes, no initial contents
+ * Errors: TQ_ERR_ARG, TQ_ERR_SHAPE (d != 128, hq % hkv, unsupported widths),
+ * TQ_ERR_ALIGN, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                     const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
+                     int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                     const void* codes_v, const uint16_t* norms_v, int64_t capacity,
+                     const int32_t* seq_lens, float scale, float tau, float* out,
+                     float* logits, int64_t* skipped, void* workspace,
+                     int64_t workspace_bytes, tq_stream_t stream);
+
+/* Workspace bytes tq_ip_search needs. */
+int64_t tq_search_workspace_bytes(int64_t n_q, int32_t k, int64_t n_db, int32_t d);
+
+/* Exhaustive top-k inner-product search over a packed database: score_i =
+ * n16_i <q_rot, c[idx_i]> + gamma r16_i <S q_rot, 2 sigma_i - 1>, the same estimator
+ * (163.com explainer, section "向量搜索").  Larger scores first; equal scores go to
+ * the lower id.
+ *   codes_db, norms_db : device, n_db packed vectors of format fmt
+ *   queries  : device fp32 [n_q][d_in], d_in <= d (zero-padded to d)
+ *   k        : 1..64, k <= n_db
+ *   out_ids  : device out int64 [n_q][k]
+ *   out_scores: device out fp32 [n_q][k]
+ *   workspace: device, >= tq_search_workspace_bytes(n_q, k, n_db, fmt->d)
+ * Errors: TQ_ERR_ARG, TQ_ERR_SHAPE, TQ_ERR_ALIGN, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_ip_search(const tq_format* fmt, const tq_tables* tab, const void* codes_db,
+                 const uint16_t* norms_db, int64_t n_db, const float* queries, int32_t d_in,
+                 int64_t n_q, int32_t k, int64_t* out_ids, float* out_scores,
+                 void* workspace, int64_t workspace_bytes, tq_stream_t stream);
+
+/* Static string naming a status code. */
+const char* tq_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */
