@@ -118,7 +118,7 @@ int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
   if (batch <= 0 || hq <= 0 || hkv <= 0 || capacity < 0) return TQ_ERR_ARG;
   if (hq % hkv) return TQ_ERR_SHAPE;
   const int g = hq / hkv;
-  if (g > 4 && g % 4) return TQ_ERR_SHAPE;
+  if (g != 1 && g != 2 && g % 4) return TQ_ERR_SHAPE;
   if (!dtype_ok(q_dtype) || !std::isfinite(scale) || !(tau >= 0.0f) || !(tau <= 1.0f)) return TQ_ERR_ARG;
   if ((rc = check_tables(fk, tk)) || (rc = check_tables(fv, tv))) return rc;
   if (!q || !out || !seq_lens || !workspace) return TQ_ERR_ARG;

@@ -260,9 +260,13 @@ def quantize(x: np.ndarray, fmt: Format, signs: np.ndarray, S: np.ndarray,
         if not cols.any():
             continue
         zc = z[:, cols]
-        ic = np.sum(cb.bounds[None, None, :] < zc[:, :, None], axis=2)
+        # idx = #{m : t_m < z}: searchsorted(side="left") returns exactly that count
+        ic = np.searchsorted(cb.bounds, zc, side="left")
         idx[:, cols] = ic
-        amb_code[:, cols] = np.min(np.abs(zc[:, :, None] - cb.bounds[None, None, :]), axis=2) < CODE_WINDOW
+        # the nearest boundary is the last one below z or the first one at/above it
+        below = cb.bounds[np.maximum(ic - 1, 0)]
+        above = cb.bounds[np.minimum(ic, len(cb.bounds) - 1)]
+        amb_code[:, cols] = np.minimum(np.abs(zc - below), np.abs(zc - above)) < CODE_WINDOW
         cval[:, cols] = cb.centroids[ic]
 
     r = y - n16[:, None] * cval
@@ -288,24 +292,23 @@ def pack(idx: np.ndarray, sbit: np.ndarray, fmt: Format) -> np.ndarray:
     are little-endian uint32.  Layout idea: the zhidx article's "block-32" layout
     (section "01 turboquant_plus：介绍与详解")."""
     n, d = idx.shape
-    words = []
-    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    chunks = []
     for blk in range(d // 32):
         B = fmt.bits_of_block(blk)
         cols = slice(32 * blk, 32 * blk + 32)
         for p in range(B):
-            bitsp = ((idx[:, cols] >> p) & 1).astype(np.uint64)
-            words.append(np.sum(bitsp * weights, axis=1))
-        words.append(np.sum(sbit[:, cols].astype(np.uint64) * weights, axis=1))
-    w = np.stack(words, axis=1).astype(np.uint32)
-    return w.astype("<u4").view(np.uint8).reshape(n, -1)
+            bitsp = ((idx[:, cols] >> p) & 1).astype(np.uint8)
+            # bit i of the word = coordinate 32*blk + i, little-endian bytes
+            chunks.append(np.packbits(bitsp, axis=1, bitorder="little"))
+        chunks.append(np.packbits(sbit[:, cols].astype(np.uint8), axis=1, bitorder="little"))
+    return np.ascontiguousarray(np.concatenate(chunks, axis=1)).reshape(n, -1)
 
 
 def unpack(rec: np.ndarray, fmt: Format):
     """Inverse of ``pack``: (idx [n, d] int64, sbit [n, d] bool)."""
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
     n = rec.shape[0]
-    w = rec.view("<u4").reshape(n, -1).astype(np.int64)
+    w = rec.view("<u4").reshape(n, fmt.words_per_vector()).astype(np.int64)
     idx = np.zeros((n, fmt.d), dtype=np.int64)
     sbit = np.zeros((n, fmt.d), dtype=bool)
     k = 0

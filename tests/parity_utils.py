@@ -15,10 +15,20 @@ def oracle_codebooks(d, bits_lo, bits_hi):
     return O.codebook(d, bits_lo), O.codebook(d, bits_hi)
 
 
-def oracle_quantize(x64, fmt: O.Format, signs, S):
+KEEP = ("idx", "sbit", "n16", "r16", "amb_code", "amb_sign", "amb_n16", "amb_r16", "z", "r", "u")
+
+
+def oracle_quantize(x, fmt: O.Format, signs, S, chunk: int = 8192, bf16: bool = False):
+    """Oracle quantize + pack, applied to row chunks (each vector is independent; chunks
+    only keep temporaries small).  x: float rows, or bf16 bit patterns with bf16=True."""
     lo, hi = oracle_codebooks(fmt.d, fmt.bits_lo, fmt.bits_hi)
-    qz = O.quantize(x64, fmt, signs, S, lo, hi)
-    qz["records"] = O.pack(qz["idx"], qz["sbit"], fmt)
+    parts = []
+    for s in range(0, max(1, x.shape[0]), chunk):
+        xc = TI.bf16_to_f64(x[s:s + chunk]) if bf16 else np.asarray(x[s:s + chunk], dtype=np.float64)
+        q = O.quantize(xc, fmt, signs, S, lo, hi)
+        q["records"] = O.pack(q["idx"], q["sbit"], fmt)
+        parts.append({k: q[k] for k in KEEP + ("records",)})
+    qz = {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
     qz["norms"] = np.stack([qz["n16"], qz["r16"]], axis=1).astype(np.uint16)
     return qz
 
@@ -69,3 +79,43 @@ def to_f64(x_np, dtype: str):
     if dtype == "bf16":
         return TI.bf16_to_f64(x_np)
     return np.asarray(x_np, dtype=np.float64)
+
+
+def oracle_pack_cache(x_bhtd, fmt: O.Format, signs, S, bf16: bool = False):
+    """Quantize a cache [batch, hkv, ntok, d] with the oracle; returns records
+    [batch, hkv, ntok, rb] uint8, norms [batch, hkv, ntok, 2] uint16 and the quantize dict."""
+    b, h, t, d = x_bhtd.shape
+    qz = oracle_quantize(x_bhtd.reshape(-1, d), fmt, signs, S, bf16=bf16)
+    return (qz["records"].reshape(b, h, t, -1), qz["norms"].reshape(b, h, t, 2), qz)
+
+
+def oracle_decode(q64, rec_k, nrm_k, rec_v, nrm_v, seq_lens, fmt_k, fmt_v, signs_k, S_k, signs_v,
+                  S_v, scale, tau=0.0):
+    """Oracle attention for every (batch, q head): explicit dequantization of the packed
+    bytes, then textbook softmax attention.  Returns out [b, hq, d], logits list, logit
+    scales list, dropped-row counts and masses."""
+    batch, hq, d = q64.shape
+    hkv = rec_k.shape[1]
+    G = hq // hkv
+    cbk = oracle_codebooks(d, fmt_k.bits_lo, fmt_k.bits_hi)
+    cbv = oracle_codebooks(d, fmt_v.bits_lo, fmt_v.bits_hi)
+    out = np.zeros((batch, hq, d))
+    logits, scales, drops, masses = {}, {}, {}, {}
+    for bi in range(batch):
+        L = int(seq_lens[bi])
+        for kh in range(hkv):
+            ik, sk = O.unpack(rec_k[bi, kh, :L], fmt_k)
+            iv, sv = O.unpack(rec_v[bi, kh, :L], fmt_v)
+            kt = O.dequantize(ik, sk, nrm_k[bi, kh, :L, 0], nrm_k[bi, kh, :L, 1], fmt_k, signs_k,
+                              S_k, *cbk)
+            vt = O.dequantize(iv, sv, nrm_v[bi, kh, :L, 0], nrm_v[bi, kh, :L, 1], fmt_v, signs_v,
+                              S_v, *cbv)
+            for g in range(G):
+                h = kh * G + g
+                o, lg, p, nd, dm = O.attend(q64[bi, h], kt, vt, scale, tau)
+                out[bi, h] = o
+                _, esc = O.estimator_dot(q64[bi, h], ik, sk, nrm_k[bi, kh, :L, 0],
+                                         nrm_k[bi, kh, :L, 1], fmt_k, signs_k, S_k, *cbk)
+                logits[(bi, h)], scales[(bi, h)] = lg, esc * scale
+                drops[(bi, h)], masses[(bi, h)] = nd, dm
+    return out, logits, scales, drops, masses

@@ -1,0 +1,131 @@
+"""GPU parity: tq_attend_decode (through the C ABI) on packed caches written by the oracle,
+against the oracle's explicit dequantization + textbook softmax attention of the same
+bytes.  Logits within 1e-4 relative to their absolute-sum scale; outputs (fp32) within
+2e-3 max-abs; Sparse-V gated output within 5e-3 of the ungated oracle."""
+import math
+
+import numpy as np
+import pytest
+
+import tq_inputs as TI
+from oracle import tq_oracle as O
+from parity_utils import oracle_decode, oracle_pack_cache
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_RTOL = 1e-4
+OUT_ATOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import compressed_attention_rotate_amd as tq
+    tq.load()
+    return torch
+
+
+def _gpu_decode(torch, q_np, q_dtype, rk, nk, rv, nv, seq_lens, fk, fv, signs_k, S_k, signs_v,
+                S_v, tau=0.0, logits=True):
+    import compressed_attention_rotate_amd as tq
+    fmt_k, fmt_v = tq.Format(*fk), tq.Format(*fv)
+    tk = tq.Tables(fmt_k, signs_k, torch.from_numpy(S_k).cuda())
+    tv = tq.Tables(fmt_v, signs_v, torch.from_numpy(S_v).cuda())
+    if q_dtype == "bf16":
+        q = torch.from_numpy(q_np.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        q = torch.from_numpy(np.ascontiguousarray(q_np, dtype=np.float32)).cuda()
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    sk = torch.zeros(1, dtype=torch.int64, device="cuda")
+    res = tq.attend_decode(q, to_dev(rk), to_dev(nk.view(np.int16)).view(torch.float16), to_dev(rv),
+                           to_dev(nv.view(np.int16)).view(torch.float16),
+                           to_dev(np.asarray(seq_lens, dtype=np.int32)), fmt_k, tk, fmt_v, tv,
+                           tau=tau, logits=logits, skipped=sk)
+    torch.cuda.synchronize()
+    out, lg = res if logits else (res, None)
+    return out.cpu().numpy(), (lg.cpu().numpy() if logits else None), int(sk.item())
+
+
+def _compare(out_g, lg_g, out_o, lg_o, sc_o, seq_lens, atol=OUT_ATOL):
+    worst = 0.0
+    for (bi, h), lo in lg_o.items():
+        L = int(seq_lens[bi])
+        err = np.abs(lg_g[bi, h, :L] - lo)
+        bound = LOGIT_RTOL * (np.abs(lo) + sc_o[(bi, h)])
+        assert np.all(err <= bound), f"logits differ (b={bi}, h={h}): max ratio {np.max(err / bound)}"
+        worst = max(worst, float(np.max(err / bound)) if L else 0.0)
+    dmax = float(np.max(np.abs(out_g - out_o)))
+    assert dmax <= atol, f"outputs differ by {dmax}"
+    return worst, dmax
+
+
+def _case(torch, batch, hq, hkv, ntok, seq_lens, fk, fv, seed, q_dtype="bf16", spikes=0.0,
+          tau=0.0, atol=OUT_ATOL):
+    d = 128
+    kb, vb, _ = TI.kv_layer(batch, hkv, ntok, d, seed=seed, spike_frac=spikes)
+    q_bits = TI.decode_queries(batch, hq, d, seed)
+    signs, S = TI.rotation(d, seed + 500000)
+    rk, nk, _ = oracle_pack_cache(kb, O.Format(*fk), signs, S, bf16=True)
+    rv, nv, _ = oracle_pack_cache(vb, O.Format(*fv), signs, S, bf16=True)
+    q64 = TI.bf16_to_f64(q_bits)
+    out_g, lg_g, skipped = _gpu_decode(torch, q_bits, q_dtype, rk, nk, rv, nv, seq_lens, fk, fv,
+                                       signs, S, signs, S, tau=tau)
+    out_o, lg_o, sc_o, dr, dm = oracle_decode(q64, rk, nk, rv, nv, seq_lens, O.Format(*fk),
+                                              O.Format(*fv), signs, S, signs, S,
+                                              1 / math.sqrt(d), 0.0)
+    worst, dmax = _compare(out_g, lg_g, out_o, lg_o, sc_o, seq_lens, atol)
+    print(f"\nb={batch} hq={hq} hkv={hkv} L={seq_lens} K{fk} V{fv} tau={tau}: logit err/bound "
+          f"{worst:.3g}, out max|diff| {dmax:.3g}, skipped rows {skipped}")
+    return out_g, out_o, skipped
+
+
+def test_llama_layer_shape_b4(torch_gpu):
+    _case(torch_gpu, 1, 32, 8, 2048, [2000], (128, 3, 3, 128), (128, 3, 3, 128), 2000)
+
+
+def test_ragged_batch_and_empty_sequences(torch_gpu):
+    _case(torch_gpu, 4, 8, 2, 700, [700, 0, 1, 333], (128, 3, 3, 128), (128, 3, 3, 128), 2100)
+
+
+def test_mixed_width_b3_5(torch_gpu):
+    _case(torch_gpu, 2, 32, 8, 1100, [1100, 1000], (128, 3, 2, 64), (128, 3, 2, 64), 3000)
+
+
+def test_asymmetric_kv_and_group_sizes(torch_gpu):
+    _case(torch_gpu, 1, 8, 8, 900, [900], (128, 3, 3, 128), (128, 2, 2, 128), 4000)     # G = 1
+    _case(torch_gpu, 1, 8, 4, 900, [877], (128, 2, 2, 128), (128, 2, 2, 128), 4001)     # G = 2
+    _case(torch_gpu, 1, 16, 2, 600, [600], (128, 1, 1, 128), (128, 1, 1, 128), 4002)    # G = 8
+
+
+def test_single_head_64_queries(torch_gpu):
+    """One KV head, d = 128, 4096 keys/values N(0,1) fp32 with 4 channels x20, 64 queries,
+    b = 3 (2-bit codebook + 1 QJL bit): 64 query heads sharing one KV head."""
+    torch = torch_gpu
+    k, v, q, _ = TI.c1_inputs(seed=1000)
+    d = 128
+    signs, S = TI.rotation(d, TI.rotation_seed(1))
+    fmt = O.Format(128, 2, 2, 128)
+    rk, nk, _ = oracle_pack_cache(k.astype(np.float64)[None, None], fmt, signs, S)
+    rv, nv, _ = oracle_pack_cache(v.astype(np.float64)[None, None], fmt, signs, S)
+    q3 = q[None]                                                       # [1, 64, 128]
+    out_g, lg_g, _ = _gpu_decode(torch, q3, "f32", rk, nk, rv, nv, [4096], (128, 2, 2, 128),
+                                 (128, 2, 2, 128), signs, S, signs, S)
+    out_o, lg_o, sc_o, _, _ = oracle_decode(q3.astype(np.float64), rk, nk, rv, nv, [4096], fmt, fmt,
+                                            signs, S, signs, S, 1 / math.sqrt(d))
+    worst, dmax = _compare(out_g, lg_g, out_o, lg_o, sc_o, [4096])
+    print(f"\nsingle head: logit err/bound {worst:.3g}, out max|diff| {dmax:.3g}")
+
+
+def test_sparse_v_gate_with_spikes(torch_gpu):
+    """Keys with 1% x10 norm spikes, K b = 4 / V b = 3, gate tau = 1e-4: the gated GPU output
+    stays within 5e-3 of the ungated oracle and reads fewer value rows."""
+    out_g, out_o, skipped = _case(torch_gpu, 2, 32, 8, 4096, [4096, 3000], (128, 3, 3, 128),
+                                  (128, 2, 2, 128), 5000, spikes=0.01, tau=1e-4, atol=5e-3)
+    assert skipped > 0
+
+
+def test_full_context_llama_layer(torch_gpu):
+    """Full 32768-token cache, 32 query / 8 KV heads, b = 4, launched as bench.py times it;
+    every head checked."""
+    _case(torch_gpu, 1, 32, 8, 32768, [32768], (128, 3, 3, 128), (128, 3, 3, 128), TI.data_seed(2))

@@ -90,7 +90,7 @@ def test_full_layer_sampled(torch_gpu):
     codes, norms, cnt, signs, S = _run(torch_gpu, x, "bf16", (128, 3, 3, 128), TI.rotation_seed(2))
     rows = np.sort(TI.gen(99).choice(x.shape[0], size=6000, replace=False))
     rows = np.concatenate([rows, np.arange(x.shape[0] - 40, x.shape[0])])
-    qz = oracle_quantize(TI.bf16_to_f64(x[rows]), O.Format(128, 3, 3, 128), signs, S)
+    qz = oracle_quantize(x[rows], O.Format(128, 3, 3, 128), signs, S, bf16=True)
     rep = compare_quantize(codes[rows], norms[rows], qz, O.Format(128, 3, 3, 128))
     print(f"\nfull layer: {rep} counters={cnt}")
     assert cnt[3] == 0
