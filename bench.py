@@ -1,0 +1,215 @@
+"""Benchmark of the TurboQuant hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input shaped like a
+Llama-3.1-8B decode layer with a 32K-token context (32 query / 8 KV heads, head dim 128,
+keys and values bf16 with per-channel std log-uniform in [0.5, 8], b = 4 for K and V):
+  1. quantize the layer's 32768 keys and 32768 values of all 8 KV heads
+     (rotation, norm, codebook, residual, JL projection on MFMA, packing);
+  2. one decode step of attention for the 32 query heads straight from a packed cache.
+The timed steps rotate over SLOTS independent inputs/caches; step k quantizes slot k and
+decodes slot k+1 (written SLOTS-1 steps earlier), so the decoded cache is not resident in
+the 256 MB MALL.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (see the README of the repository for the fields).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFS = 157.3     # MI355X dense fp32 matrix
+SLOTS = 8
+BATCH, HQ, HKV, NTOK, D = 1, 32, 8, 32768, 128
+BITS = 3                        # codebook bits; b = 4 total with the QJL bit
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def _traffic(kernel_src: str, summary: str):
+    """HBM traffic per launch from a committed rocprofv3 --pmc summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(os.path.join(ROOT, kernel_src), "rb").read()).hexdigest()
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(kb, vb, qb, signs, S):
+    """The oracle as it stands, on the host cores, on a bounded sample of the same workload:
+    quantize + pack the keys and values of 2 of the 8 KV heads over the first 8192 tokens,
+    then decode attention for those heads' 8 query heads over that sample."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from threadpoolctl import threadpool_info
+    from oracle import tq_oracle as O
+    from parity_utils import oracle_decode, oracle_pack_cache
+    import tq_inputs as TI
+    nt, nh = 8192, 2
+    fmt = O.Format.uniform(D, BITS)
+    t0 = time.perf_counter()
+    rk, nk, _ = oracle_pack_cache(kb[:, :nh, :nt], fmt, signs, S, bf16=True)
+    rv, nv, _ = oracle_pack_cache(vb[:, :nh, :nt], fmt, signs, S, bf16=True)
+    t1 = time.perf_counter()
+    oracle_decode(TI.bf16_to_f64(qb[:, :nh * (HQ // HKV)]), rk, nk, rv, nv, [nt], fmt, fmt,
+                  signs, S, signs, S, 1 / math.sqrt(D))
+    t2 = time.perf_counter()
+    packed = 2 * nh * nt * (fmt.record_bytes() + 4)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": packed / (t2 - t1) / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{nh} of 8 KV heads x {nt} tokens: quantize+pack {2 * nh * nt} vectors "
+                      f"({t1 - t0:.2f} s, {nt / (t1 - t0) * (nh / HKV):.3g} layer-tokens/s), "
+                      f"decode {nh * HQ // HKV} query heads ({t2 - t1:.2f} s); value = packed "
+                      f"K+V bytes decoded per second",
+            "quantize_tokens_per_s": nt * nh / HKV / (t1 - t0)}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the path is single-GPU (sharding is described "
+              "in DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import compressed_attention_rotate_amd as tq
+    import tq_inputs as TI
+    tq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    seed = TI.data_seed(2)
+    kb, vb, _ = TI.kv_layer(BATCH, HKV, NTOK, D, seed=seed)
+    qb = TI.decode_queries(BATCH, HQ, D, seed)
+    signs, S = TI.rotation(D, TI.rotation_seed(2))
+    fmt = tq.Format.uniform(D, BITS)
+    tab = tq.Tables(fmt, signs, torch.from_numpy(S).to(dev))
+    rb = fmt.record_bytes()
+    nvec = BATCH * HKV * NTOK
+
+    k0 = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
+    v0 = torch.from_numpy(vb.view(np.int16)).to(dev).view(torch.bfloat16)
+    # SLOTS distinct inputs (token order rotated per slot: same law, different bytes)
+    ks = [torch.roll(k0, shifts=4099 * i, dims=2).contiguous() for i in range(SLOTS)]
+    vs = [torch.roll(v0, shifts=4099 * i, dims=2).contiguous() for i in range(SLOTS)]
+    del k0, v0
+    codes_k = [torch.empty((BATCH, HKV, NTOK, rb), dtype=torch.uint8, device=dev) for _ in range(SLOTS)]
+    codes_v = [torch.empty_like(c) for c in codes_k]
+    norms_k = [torch.empty((BATCH, HKV, NTOK, 2), dtype=torch.float16, device=dev) for _ in range(SLOTS)]
+    norms_v = [torch.empty_like(n) for n in norms_k]
+    q = torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16)
+    seq = torch.full((BATCH,), NTOK, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.attend_workspace_bytes(BATCH, HQ, HKV, NTOK, D), dtype=torch.uint8, device=dev)
+    out = torch.empty((BATCH, HQ, D), dtype=torch.float32, device=dev)
+
+    def quantize(s):
+        tq.quantize_kv(ks[s].view(-1, D), fmt, tab, codes=codes_k[s].view(nvec, rb),
+                       norms=norms_k[s].view(nvec, 2))
+
+    def quantize_v(s):
+        tq.quantize_kv(vs[s].view(-1, D), fmt, tab, codes=codes_v[s].view(nvec, rb),
+                       norms=norms_v[s].view(nvec, 2))
+
+    def decode(s):
+        tq.attend_decode(q, codes_k[s], norms_k[s], codes_v[s], norms_v[s], seq, fmt, tab,
+                         workspace=ws, out=out)
+
+    for s in range(SLOTS):              # every slot holds a packed cache before timing
+        quantize(s)
+        quantize_v(s)
+    for k in range(args.warmup):
+        quantize(k % SLOTS); quantize_v(k % SLOTS); decode((k + 1) % SLOTS)
+    torch.cuda.synchronize()
+
+    steps = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        e = ev[k]
+        e[0].record()
+        quantize(k % SLOTS)
+        e[1].record()
+        quantize_v(k % SLOTS)
+        e[2].record()
+        decode((k + 1) % SLOTS)
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    qk = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    qv = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    dc = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    packed_bytes = 2 * nvec * (rb + 4)                      # K + V records and norms read
+    decode_gbs = packed_bytes * steps / dc.sum() / 1e9
+    q_launch = float(np.concatenate([qk, qv]).mean())
+    flops_launch = 2.0 * D * D * nvec                         # S r per vector
+    q_tfs = flops_launch / q_launch / 1e12
+    qtoks = NTOK * BATCH * steps / (qk.sum() + qv.sum())
+    trafq = _traffic("compressed_attention_rotate_amd/csrc/tq_quantize.hip",
+                     "quantize_llama8b_32k_traffic.txt")
+    trafd = _traffic("compressed_attention_rotate_amd/csrc/tq_decode.hip",
+                     "decode_llama8b_32k_traffic.txt")
+
+    line = {
+        "metric": "decode-attn packed-KV GB/s & % HBM peak; quantize tokens/s (32K ctx, b=4)",
+        "value": round(decode_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped decode layer: batch 1, 32 q / 8 kv heads, "
+                               "head_dim 128, 32768 cached tokens, bf16 K/V (per-channel std "
+                               "log-uniform [0.5, 8]), b=4 (3-bit codebook + 1 QJL bit)",
+                   "global_batch": BATCH, "seq_len": NTOK, "parallelism": "none (1 GPU)"},
+        "decode_pct_hbm_peak": round(100.0 * decode_gbs / HBM_PEAK_GBS, 2),
+        "decode_us": round(float(dc.mean()) * 1e6, 3),
+        "quantize_tokens_per_s": round(qtoks, 1),
+        "quantize_us_per_launch": round(q_launch * 1e6, 3),
+        "roofline": {"bound": "mfma", "kernel": "quantize_kernel<128,3,3>",
+                     "achieved": round(q_tfs, 3), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(q_tfs / FP32_MFMA_PEAK_TFS, 4), "traffic": trafq},
+        "roofline_decode": {"bound": "hbm", "kernel": "decode_prologue+decode_scan+decode_combine",
+                            "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": trafd},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(kb, vb, qb, signs, S)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
