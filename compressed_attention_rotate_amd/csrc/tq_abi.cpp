@@ -114,7 +114,7 @@ int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
   int rc = tq_check_format(fk);
   if (rc) return rc;
   if ((rc = tq_check_format(fv))) return rc;
-  if (fk->d != 128 || fv->d != 128) return TQ_ERR_SHAPE;
+  if (fk->d != 128 || fv->d != 128 || !tq_decode_formats_supported(fk, fv)) return TQ_ERR_SHAPE;
   if (batch <= 0 || hq <= 0 || hkv <= 0 || capacity < 0) return TQ_ERR_ARG;
   if (hq % hkv) return TQ_ERR_SHAPE;
   const int g = hq / hkv;

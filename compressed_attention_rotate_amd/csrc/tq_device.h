@@ -55,10 +55,45 @@ __device__ __forceinline__ float half_sum(float v) {
 
 __device__ __forceinline__ double shfl_xor_d(double v, int m) { return __shfl_xor(v, m, 64); }
 
+template <int M>
+__device__ __forceinline__ double xchg_d(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __float_as_uint(xchg<M>(__uint_as_float((uint32_t)u)));
+  const uint32_t hi = __float_as_uint(xchg<M>(__uint_as_float((uint32_t)(u >> 32))));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum over the 32 lanes of each half-wave in fp64 (DPP / ds_swizzle exchanges).
 __device__ __forceinline__ double half_sum_d(double v) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) v += shfl_xor_d(v, m);
+  v += xchg_d<1>(v);
+  v += xchg_d<2>(v);
+  v += xchg_d<4>(v);
+  v += xchg_d<8>(v);
+  v += xchg_d<16>(v);
   return v;
+}
+
+// Reductions over all 64 lanes: DPP / swizzle within each half, then the two halves
+// combined through readlane (result is wave-uniform).
+__device__ __forceinline__ float wave_sum_fast(float v) {
+  v = half_sum(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+}
+
+__device__ __forceinline__ float half_max(float v) {
+  v = fmaxf(v, xchg<1>(v));
+  v = fmaxf(v, xchg<2>(v));
+  v = fmaxf(v, xchg<4>(v));
+  v = fmaxf(v, xchg<8>(v));
+  v = fmaxf(v, xchg<16>(v));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_fast(float v) {
+  v = half_max(v);
+  return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {

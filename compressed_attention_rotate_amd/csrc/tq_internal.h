@@ -18,9 +18,13 @@ struct tq_decode_plan {
   int32_t parts;          // partial results per (batch, q head) = n_split * waves
   int64_t tokens_per_split;
   int64_t ws_qrot_off;    // byte offsets inside the workspace
+  int64_t ws_nib_off;
   int64_t ws_part_off;
   int64_t ws_bytes;
 };
+
+// Key/value format pairs the decode kernels are instantiated for.
+bool tq_decode_formats_supported(const tq_format* fk, const tq_format* fv);
 
 tq_decode_plan tq_plan_decode(int32_t batch, int32_t hq, int32_t hkv, int64_t capacity, int32_t d);
 

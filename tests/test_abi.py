@@ -1,0 +1,139 @@
+"""C ABI checks that need no GPU: the library loads, exports every function tq.h declares,
+its host-side codebook builder matches the oracle's tables, and argument validation
+rejects bad calls before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_attention_rotate_amd as tq
+from compressed_attention_rotate_amd._lib import c_format, c_tables
+from oracle import tq_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = tq.load()
+    names = _declared()
+    assert {"tq_build_codebook", "tq_quantize_kv", "tq_attend_decode", "tq_ip_search"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in tq.h but not exported"
+
+
+@pytest.mark.parametrize("d", [8, 128, 256, 1024])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_host_codebook_matches_oracle_tables(d, bits):
+    c, b, mse = tq.build_codebook(d, bits)
+    ref = O.codebook(d, bits)
+    assert np.array_equal(c.astype(np.float64), ref.centroids)
+    assert np.array_equal(b.astype(np.float64), ref.bounds)
+    assert abs(mse - ref.mse) < 1e-9 * ref.mse + 1e-15
+
+
+def test_codebook_argument_errors():
+    lib = tq.load()
+    c = np.zeros(16, np.float32)
+    b = np.zeros(15, np.float32)
+    assert lib.tq_build_codebook(100, 2, c.ctypes.data, b.ctypes.data, None) == tq._lib.TQ_ERR_SHAPE
+    assert lib.tq_build_codebook(128, 5, c.ctypes.data, b.ctypes.data, None) == tq._lib.TQ_ERR_SHAPE
+    assert lib.tq_build_codebook(128, 2, None, b.ctypes.data, None) == tq._lib.TQ_ERR_ARG
+
+
+def test_record_bytes_and_formats():
+    assert tq.Format(128, 3, 3, 128).record_bytes() == 64          # b = 4: 4.25 bit/value with norms
+    assert tq.Format(128, 2, 2, 128).record_bytes() == 48          # b = 3
+    assert tq.Format(128, 3, 2, 64).record_bytes() == 56           # b = 3.5 mixed
+    assert tq.Format(256, 3, 3, 256).record_bytes() == 128
+    for f in (O.Format(128, 3, 3, 128), O.Format(128, 3, 2, 64), O.Format(256, 2, 2, 256)):
+        assert tq.Format(f.d, f.bits_lo, f.bits_hi, f.split).record_bytes() == f.record_bytes()
+    lib = tq.load()
+    for bad in ((64, 3, 3, 64), (128, 4, 4, 128), (128, 3, 2, 48), (128, 3, 2, 128), (256, 1, 1, 256)):
+        f = c_format(*bad)
+        assert lib.tq_check_format(ctypes.byref(f)) == tq._lib.TQ_ERR_SHAPE
+        assert lib.tq_record_bytes(ctypes.byref(f)) < 0
+
+
+def _tables(fmt, S_ptr=0x10000):
+    c, b, _ = tq.build_codebook(fmt.d, fmt.bits_lo)
+    ch, bh, _ = tq.build_codebook(fmt.d, fmt.bits_hi)
+    signs = np.ones(fmt.d, np.int8)
+    keep = (c, b, ch, bh, signs)
+    return c_tables(c.ctypes.data, b.ctypes.data, ch.ctypes.data, bh.ctypes.data, signs.ctypes.data,
+                    S_ptr), keep
+
+
+def test_quantize_validation_before_launch():
+    lib = tq.load()
+    f = c_format(128, 3, 3, 128)
+    t, keep = _tables(tq.Format(128, 3, 3, 128))
+    fake = ctypes.c_void_p(0x20000)
+    Q = lambda **kw: lib.tq_quantize_kv(ctypes.byref(kw.get("f", f)), ctypes.byref(kw.get("t", t)),
+                                        kw.get("x", fake), kw.get("dt", 1), kw.get("n", 4),
+                                        kw.get("d_in", 128), kw.get("ld", 128), kw.get("codes", fake),
+                                        kw.get("norms", fake), None, None)
+    E = tq._lib
+    assert Q(n=-1) == E.TQ_ERR_ARG
+    assert Q(dt=7) == E.TQ_ERR_ARG
+    assert Q(d_in=129) == E.TQ_ERR_SHAPE
+    assert Q(ld=100) == E.TQ_ERR_SHAPE
+    assert Q(codes=ctypes.c_void_p(0x20004)) == E.TQ_ERR_ALIGN
+    assert Q(x=None) == E.TQ_ERR_ARG
+    assert Q(n=0) == E.TQ_OK                                          # empty is a no-op
+    t2, keep2 = _tables(tq.Format(128, 3, 3, 128), S_ptr=0x10008)
+    assert Q(t=t2) == E.TQ_ERR_ALIGN
+    bad_signs = np.full(128, 2, np.int8)
+    t3 = c_tables(t.centroids_lo, t.bounds_lo, t.centroids_hi, t.bounds_hi, bad_signs.ctypes.data, 0x10000)
+    assert Q(t=t3) == E.TQ_ERR_ARG
+    asym = np.array(keep[0]); asym[0] += 1e-3                         # codebook not mirror-symmetric
+    t4 = c_tables(asym.ctypes.data, t.bounds_lo, t.centroids_hi, t.bounds_hi, t.signs, 0x10000)
+    assert Q(t=t4) == E.TQ_ERR_ARG
+
+
+def test_decode_and_search_validation_before_launch():
+    lib = tq.load()
+    E = tq._lib
+    f = c_format(128, 3, 3, 128)
+    t, keep = _tables(tq.Format(128, 3, 3, 128))
+    p = ctypes.c_void_p(0x40000)
+    ws = tq.attend_workspace_bytes(1, 32, 8, 4096)
+    assert ws > 0 and tq.attend_workspace_bytes(2, 32, 8, 4096) > ws
+
+    def D(hq=32, hkv=8, ws_bytes=ws, tau=0.0, fv=f, q=p):
+        return lib.tq_attend_decode(ctypes.byref(f), ctypes.byref(t), ctypes.byref(fv), ctypes.byref(t),
+                                    q, 1, 1, hq, hkv, p, p, p, p, 4096, p, 0.088, tau, p, None, None,
+                                    p, ws_bytes, None)
+    assert D(hq=30) == E.TQ_ERR_SHAPE              # hq % hkv
+    assert D(hq=24) == E.TQ_ERR_SHAPE              # group 3 unsupported
+    assert D(ws_bytes=ws - 1) == E.TQ_ERR_WORKSPACE
+    assert D(tau=-0.5) == E.TQ_ERR_ARG
+    assert D(q=None) == E.TQ_ERR_ARG
+    fv_bad = c_format(256, 3, 3, 256)
+    assert D(fv=fv_bad) == E.TQ_ERR_SHAPE
+    f2 = c_format(256, 3, 3, 256)
+    t2, keep2 = _tables(tq.Format(256, 3, 3, 256))
+    wsb = tq.search_workspace_bytes(100, 10, 10 ** 6, 256)
+    assert wsb > 0
+
+    def S(k=10, n_db=10 ** 6, d_in=200, ws_bytes=wsb):
+        return lib.tq_ip_search(ctypes.byref(f2), ctypes.byref(t2), p, p, n_db, p, d_in, 100, k, p, p,
+                                p, ws_bytes, None)
+    assert S(k=0) == E.TQ_ERR_ARG
+    assert S(k=65) == E.TQ_ERR_ARG
+    assert S(n_db=5) == E.TQ_ERR_ARG
+    assert S(d_in=300) == E.TQ_ERR_SHAPE
+    assert S(ws_bytes=wsb - 1) == E.TQ_ERR_WORKSPACE
+
+
+def test_strerror_names_every_code():
+    lib = tq.load()
+    seen = {lib.tq_strerror(c).decode() for c in range(0, -7, -1)}
+    assert len(seen) == 7 and lib.tq_strerror(-99).decode() == "unknown status code"
