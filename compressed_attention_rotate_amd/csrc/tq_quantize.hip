@@ -15,13 +15,17 @@
 //   phase 1 (VALU): two vectors per pass, one per 32-lane half, two passes interleaved.
 //             Lane c holds coordinates 32*s + c (s = 0 .. D/32-1), so FWHT stages on
 //             coordinate bits >= 5 are in-lane and bits 0..4 are DPP / ds_swizzle
-//             butterflies, and one ballot per compare yields a code bit-plane word of both
-//             vectors.  ||x|| is accumulated in fp64 (so the fp16 norm is correctly
-//             rounded); rotation, codes and residual run in fp32.
-//   phase 2 (MFMA): U = R^ S^T with v_mfma_f32_16x16x4f32 (the d x d projection is the
-//             one dense contraction of the path); each 16x16 accumulator block gives sign
-//             bits by ballot.  Entries with |u| < 1e-5 (fp32 error is ~1e-7) are recomputed
-//             in fp64 from x, so every stored sign is the sign of the exact projection.
+//             butterflies.  One ballot per compare yields a code bit-plane word of both
+//             vectors; lane 0 drops the 64-bit ballots into an LDS table and the records
+//             are assembled from it when the tile is stored.  ||x|| is accumulated in fp64
+//             (so the fp16 norm is correctly rounded); rotation, codes and residual run in
+//             fp32.  The unit residual is split into fp16 hi + lo (scaled by 2^12).
+//   phase 2 (MFMA): U = R^ S^T, the one dense contraction of the path, as three fp16
+//             products (hi.hi + hi.lo + lo.hi, S scaled by 2^10 and split the same way) on
+//             v_mfma_f32_16x16x32_f16 with fp32 accumulation: relative error ~2^-22 per
+//             term.  Sign bits come from ballots over each 16x16 accumulator block; every
+//             entry with |u| < 1e-5 is recomputed in fp64 from x, so each stored sign is the
+//             sign of the exact projection.
 // With 8 waves per workgroup (2 per SIMD) one wave's VALU phase overlaps another's MFMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,9 +37,13 @@ namespace tqk {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr float kGuard = 1e-5f;   // fp32 projections below this are rechecked in fp64
+constexpr float kGuard = 1e-5f;   // projections below this are rechecked in fp64
 constexpr float kWindow = 1e-6f;  // ambiguity window reported through the counters
+constexpr float kRScale = 4096.0f;   // unit residual scale before the fp16 split
+constexpr float kSScale = 1024.0f;   // S scale before the fp16 split
+constexpr float kUScale = kRScale * kSScale;
 
 template <int D>
 struct QCfg {
@@ -44,41 +52,27 @@ struct QCfg {
   static constexpr int NW = (D == 128) ? 8 : 4;      // waves per workgroup
   static constexpr bool kResidentS = (D == 128);     // S stays in LDS (else 32-row slices)
   static constexpr int kSRows = kResidentS ? D : 32;
-  static constexpr int kWaveF = TV * D + TV * 32 + TV;  // rhat/input, record staging, norms
-  static constexpr int MAXC = TV * D * 4 / 16 / 64;     // 16-byte input chunks per lane
-  static constexpr int PG = 2;                          // passes interleaved in phase 1
+  static constexpr int kRowB = 4 * D;                // bytes of one [hi | lo] fp16 row
+  static constexpr int kBal = (TV / 2) * NB * 4;     // code-plane ballots per tile (uint64)
+  static constexpr int kSBal = NB * 8;               // sign ballots per tile (uint64)
+  // per wave: r^ tile (doubles as input staging), ballots, sign ballots, norms
+  static constexpr int kWaveB = TV * kRowB + 8 * (kBal + kSBal) + 4 * TV;
+  static constexpr int MAXC = TV * D * 4 / 16 / 64;  // 16-byte input chunks per lane
+  static constexpr int PG = 2;                       // passes interleaved in phase 1
 };
 
-// LDS word offset of element (row, col) of a [rows][D] fp32 tile; 16-byte units are XOR-
-// swizzled by (row & 15) so 16 lanes reading the same column chunk of 16 rows (MFMA
-// operand reads) hit distinct banks.
+// Byte offset of fp16 element (row, col) of half `lo` (0 = hi, 1 = lo) in a tile whose
+// rows are [hi D fp16 | lo D fp16]; 16-byte units swizzled by (row & 15) so 16 lanes
+// reading one column unit of 16 rows (MFMA operand reads) hit distinct banks.
 template <int D>
-__device__ __forceinline__ int swz(int row, int col) {
-  return row * D + ((((col >> 2) ^ (row & 15))) << 2) + (col & 3);
+__device__ __forceinline__ int hoff(int row, int col, int lo) {
+  return row * (4 * D) + lo * (2 * D) + ((((col >> 3) ^ (row & 15))) << 4) + 2 * (col & 7);
 }
 
 template <int B>
 struct Thermo {
   static constexpr int H = 1 << (B - 1);  // positive centroids
 };
-
-// Code plane words from the thermometer ballots T[1..H-1] and the sign ballot P:
-// idx = P ? H + k : H - 1 - k, k = #{j : t_j < |z|}.  Bit q of k is the XOR of T_j over
-// the multiples j of 2^q; plane q (< B-1) is that bit, complemented when z <= 0; plane
-// B-1 is P.
-template <int B>
-__device__ __forceinline__ void planes_from_ballots(const uint64_t (&T)[(1 << (B - 1)) > 1 ? (1 << (B - 1)) : 2],
-                                                    uint64_t P, uint64_t (&out)[B]) {
-  constexpr int H = Thermo<B>::H;
-#pragma unroll
-  for (int q = 0; q + 1 < B; ++q) {
-    uint64_t k = 0;
-#pragma unroll
-    for (int j = (1 << q); j < H; j += (1 << q)) k ^= T[j];
-    out[q] = ~(k ^ P);
-  }
-  out[B - 1] = P;
-}
 
 struct QParams {
   const void* x;
@@ -89,7 +83,6 @@ struct QParams {
   int64_t n;
   int64_t ld_x;          // elements
   int32_t d_in;
-  int32_t x_dtype;
   int32_t esize;         // bytes per input element
   int32_t staged;        // rows are 16-byte aligned with a 16-byte multiple of valid bytes
   int32_t cpr;           // 16-byte chunks per row (staged path)
@@ -100,16 +93,23 @@ struct QParams {
   float cent_lo[16], cent_hi[16];
 };
 
-// Encode one slot (block) of the two vectors of a pass: returns the signed centroid of
-// this lane's coordinate and deposits the B code-plane words of both vectors into `myword`
-// (lane L of half h receives word L of that half's vector).
-template <int B>
+// 16-bit input element -> fp32 (bf16 or fp16)
+template <int XT>
+__device__ __forceinline__ float cvt16(uint32_t h) {
+  if constexpr (XT == 1) return __uint_as_float(h << 16);
+  else return f16_bits_to_f32(h);
+}
+
+// Encode one slot (block) of the two vectors of a pass.  Returns the signed centroid of
+// this lane's coordinate; the B code-plane ballots go to planes[] (plane q = bit q of idx).
+// idx = #{m : t_m < z}: with a' = |z| nudged one float up when z <= 0, one strict compare
+// t_j < a' per positive boundary gives k = #{j : t_j < a'} and idx = z > 0 ? H + k : H-1-k;
+// bit q of k is the XOR of the thermometer ballots over multiples of 2^q.
+template <int B, bool COUNT>
 __device__ __forceinline__ float encode_slot(float z, const float* cpos_lds, const float* tpos,
-                                             int off, uint32_t& myword, int& amb, bool count) {
+                                             uint64_t* planes, int& amb) {
   constexpr int H = Thermo<B>::H;
   const bool pos = z > 0.0f;
-  // a' = |z|, nudged to the next float up when z <= 0 so that one strict compare
-  // t_j < a' realises idx = #{m : t_m < z} for both signs (ties go to the lower cell)
   const float az = fabsf(z);
   const float a = as_f(as_u(az) + (pos ? 0u : 1u));
   uint64_t T[H > 1 ? H : 2];
@@ -122,11 +122,15 @@ __device__ __forceinline__ float encode_slot(float z, const float* cpos_lds, con
   }
   const float cv = cpos_lds[k];
   const uint64_t P = __ballot(pos);
-  uint64_t planes[B];
-  planes_from_ballots<B>(T, P, planes);
 #pragma unroll
-  for (int q = 0; q < B; ++q) myword = deposit(myword, planes[q], off + q);
-  if (count) {
+  for (int q = 0; q + 1 < B; ++q) {
+    uint64_t kq = 0;
+#pragma unroll
+    for (int j = (1 << q); j < H; j += (1 << q)) kq ^= T[j];
+    planes[q] = ~(kq ^ P);
+  }
+  planes[B - 1] = P;
+  if constexpr (COUNT) {
     float dmin = az;
 #pragma unroll
     for (int j = 1; j < H; ++j) dmin = fminf(dmin, fabsf(az - tpos[j]));
@@ -135,22 +139,25 @@ __device__ __forceinline__ float encode_slot(float z, const float* cpos_lds, con
   return pos ? cv : -cv;
 }
 
-// fp64 recomputation of projection n of local vector m (rare path, whole wave).
-template <int D>
-__device__ void guard_fix(const QParams& p, int64_t v, int m, int n, const float* S_rows,
-                          int s_row0, uint32_t* stage, const uint32_t* stage_norms,
-                          const float* cent_lds, const int* word_off, const int* blk_bits,
-                          unsigned long long& cnt_zero) {
+// fp64 recomputation of projection n of local vector m (rare path, whole wave).  Codes are
+// read back from the tile's ballot table; S from global memory (exact fp32 values).
+template <int D, int XT>
+__device__ void guard_fix(const QParams& p, int64_t v, int m, int n, const uint64_t* bal,
+                          uint64_t* sbal, const uint32_t* snorm, const float* cent_lds, int blo,
+                          int bhi, unsigned long long& cnt_zero) {
   constexpr int NE = D / 64;
+  constexpr int NB = D / 32;
   const int lane = lane_id();
   double xd[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
     const int j = lane + 64 * e;
-    float xv = (j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, p.x_dtype) : 0.0f;
-    if ((p.sign_mask[j >> 5] >> (j & 31)) & 1u) xv = -xv;
+    float xv = (j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
     xd[e] = (double)xv;
   }
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+    if ((p.sign_mask[(lane + 64 * e) >> 5] >> ((lane + 64 * e) & 31)) & 1u) xd[e] = -xd[e];
 #pragma unroll
   for (int h = 1; h < NE; h <<= 1)
 #pragma unroll
@@ -168,31 +175,33 @@ __device__ void guard_fix(const QParams& p, int64_t v, int m, int n, const float
       xd[e] = (lane & mm) ? t - xd[e] : xd[e] + t;
     }
   const double isd = 1.0 / sqrt((double)D);
-  const double n16 = (double)f16_bits_to_f32(stage_norms[m] & 0xFFFFu);
+  const double n16 = (double)f16_bits_to_f32(snorm[m] & 0xFFFFu);
+  const int pass = m >> 1, half = m & 1;
   double dot = 0.0, rr = 0.0;
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
     const int j = lane + 64 * e;
     const int blk = j >> 5, bit = j & 31;
+    const int nb = blk < p.split_blocks ? blo : bhi;
     int idx = 0;
-    for (int q = 0; q < blk_bits[blk]; ++q) idx |= ((stage[m * 32 + word_off[blk] + q] >> bit) & 1u) << q;
+    for (int q = 0; q < nb; ++q)
+      idx |= (int)((bal[(pass * NB + blk) * 4 + q] >> (32 * half + bit)) & 1u) << q;
     const float c = cent_lds[(blk < p.split_blocks ? 0 : 16) + idx];
     const double r = xd[e] * isd - n16 * (double)c;
-    dot += (double)S_rows[swz<D>(n - s_row0, j)] * r;
+    dot += (double)p.S[(int64_t)n * D + j] * r;
     rr += r * r;
   }
   dot = wave_sum_d(dot);
   rr = wave_sum_d(rr);
   if (lane == 0) {
-    uint32_t* w = &stage[m * 32 + word_off[n >> 5] + blk_bits[n >> 5]];
-    const uint32_t bitmask = 1u << (n & 31);
+    // sign ballot of (block, t, r): bit 16 (m / 4) + n % 16 of entry ((n/32)*2 + t)*4 + m%4
+    uint64_t* w = &sbal[((n >> 5) * 2 + ((n >> 4) & 1)) * 4 + (m & 3)];
+    const uint64_t bitmask = 1ull << (16 * (m >> 2) + (n & 15));
     *w = (dot >= 0.0) ? (*w | bitmask) : (*w & ~bitmask);
   }
   if (rr == 0.0 || fabs(dot) < (double)kWindow * sqrt(rr)) cnt_zero += 1;
 }
 
-// Input chunk plan of one lane (fixed for every tile): global byte offset inside the tile
-// and LDS byte offset of each 16-byte chunk it moves; -1 = no chunk.
 template <int D>
 struct ChunkPlan {
   int64_t goff[QCfg<D>::MAXC];
@@ -213,30 +222,33 @@ __device__ __forceinline__ void fetch_tile(const QParams& p, const ChunkPlan<D>&
 
 template <int D>
 __device__ __forceinline__ void stash_tile(const ChunkPlan<D>& cp, const u32x4 (&buf)[QCfg<D>::MAXC],
-                                           float* tile) {
+                                           char* tile) {
 #pragma unroll
   for (int i = 0; i < QCfg<D>::MAXC; ++i)
-    if (cp.loff[i] >= 0) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(tile) + cp.loff[i]) = buf[i];
+    if (cp.loff[i] >= 0) *reinterpret_cast<u32x4*>(tile + cp.loff[i]) = buf[i];
 }
 
-template <int D, int BLO, int BHI>
+// XT: 0 fp32, 1 bf16, 2 fp16 input.  COUNT: accumulate the diagnostic counters.
+template <int D, int BLO, int BHI, int XT, bool COUNT>
 __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
   using C = QCfg<D>;
   constexpr int NB = C::NB;
   constexpr int NW = C::NW;
   constexpr int TV = C::TV;
   constexpr int PG = C::PG;
-  extern __shared__ __attribute__((aligned(16))) float lds[];
-  float* S_l = lds;                                   // [kSRows][D] swizzled
+  constexpr bool UNI = (BLO == BHI);
+  extern __shared__ __attribute__((aligned(16))) char lds_b[];
+  char* S_l = lds_b;                                   // [kSRows] rows of [hi | lo] fp16
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  float* wl = lds + C::kSRows * D + wave * C::kWaveF;
-  float* rhat = wl;                                               // [TV][D]: input, then rhat
-  uint32_t* stage = reinterpret_cast<uint32_t*>(wl + TV * D);     // [TV][32] record words
-  uint32_t* snorm = stage + TV * 32;                              // [TV]
+  char* wl = lds_b + C::kSRows * C::kRowB + wave * C::kWaveB;
+  char* tileb = wl;                                                  // [TV][hi|lo]
+  uint64_t* bal = reinterpret_cast<uint64_t*>(wl + TV * C::kRowB);   // [pass][blk][4]
+  uint64_t* sbal = bal + C::kBal;                                    // [blk][t][r]
+  uint32_t* snorm = reinterpret_cast<uint32_t*>(sbal + C::kSBal);   // [TV]
   __shared__ float cent_lds[32];
   __shared__ float cpos_lds[16];  // positive centroids: lo table, then hi table
-  __shared__ int word_off_s[8], blk_bits_s[8];
+  __shared__ int wmap[32];        // record word -> (block << 8) | plane, plane 0xFF = signs
 
   if (threadIdx.x < 16) {
     cent_lds[threadIdx.x] = p.cent_lo[threadIdx.x];
@@ -244,21 +256,29 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     cpos_lds[threadIdx.x] = threadIdx.x < 8 ? p.cpos_lo[threadIdx.x] : p.cpos_hi[threadIdx.x - 8];
   }
   if (threadIdx.x == 0) {
-    int off = 0;
+    int w = 0;
     for (int b = 0; b < NB; ++b) {
       const int bb = b < p.split_blocks ? BLO : BHI;
-      word_off_s[b] = off;
-      blk_bits_s[b] = bb;
-      off += bb + 1;
+      for (int q = 0; q < bb; ++q) wmap[w++] = (b << 8) | q;
+      wmap[w++] = (b << 8) | 0xFF;
     }
   }
-  if constexpr (C::kResidentS) {
-    for (int i = threadIdx.x; i < D * D / 4; i += blockDim.x) {
+  auto load_s_rows = [&](int row0, int nrows) {
+    // fp32 S rows -> scaled fp16 hi / lo halves, swizzled
+    for (int i = threadIdx.x; i < nrows * D / 4; i += blockDim.x) {
       const int row = (4 * i) / D, col = (4 * i) % D;
-      const f32x4 v = reinterpret_cast<const f32x4*>(p.S)[i];
-      *reinterpret_cast<f32x4*>(&S_l[swz<D>(row, col)]) = v;
+      const f32x4 v = reinterpret_cast<const f32x4*>(p.S + (int64_t)row0 * D)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sv = v[e] * kSScale;
+        const _Float16 hi = (_Float16)sv;
+        const _Float16 lo = (_Float16)(sv - (float)hi);
+        *reinterpret_cast<_Float16*>(S_l + hoff<D>(row, col + e, 0)) = hi;
+        *reinterpret_cast<_Float16*>(S_l + hoff<D>(row, col + e, 1)) = lo;
+      }
     }
-  }
+  };
+  if constexpr (C::kResidentS) load_s_rows(0, D);
   __syncthreads();
 
   const int h = lane >> 5, c = lane & 31;
@@ -276,9 +296,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     tpl[k] = p.tpos_lo[k];
     tph[k] = p.tpos_hi[k];
   }
-  const bool count = p.counters != nullptr;
 
-  // per-lane input chunk plan (the same for every tile)
   ChunkPlan<D> cp;
 #pragma unroll
   for (int i = 0; i < C::MAXC; ++i) {
@@ -288,7 +306,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     const bool ok = p.staged && row < TV;
     cp.row[i] = row;
     cp.goff[i] = (int64_t)row * p.ld_x * p.esize + 16 * cc;
-    cp.loff[i] = ok ? row * D * 4 + 16 * cc : -1;
+    cp.loff[i] = ok ? row * C::kRowB + 16 * cc : -1;
   }
 
   unsigned long long cnt_amb = 0, cnt_zero = 0, cnt_guard = 0, cnt_ovf = 0;
@@ -304,7 +322,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     const int64_t v0 = tile * TV;
     const bool active = tile < ntiles;
     if (active) {
-      if (p.staged) stash_tile<D>(cp, pre, rhat);
+      if (p.staged) stash_tile<D>(cp, pre, tileb);
       // ---------------- phase 1: rotation, norm, codes, residual (PG passes at once)
       for (int pp0 = 0; pp0 < TV / 2; pp0 += PG) {
         float xv[PG][NB];
@@ -317,21 +335,17 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           const int64_t v = v0 + vloc[gg];
           valid[gg] = v < p.n;
           ss[gg] = 0.0;
+          const char* rowp = tileb + vloc[gg] * C::kRowB;
 #pragma unroll
           for (int s = 0; s < NB; ++s) {
             const int j = 32 * s + c;
-            float x = 0.0f;
-            if (valid[gg] && j < p.d_in) {
-              if (p.staged) {
-                const char* rowp = reinterpret_cast<const char*>(rhat) + vloc[gg] * D * 4;
-                if (p.x_dtype == 0) x = *reinterpret_cast<const float*>(rowp + 4 * j);
-                else {
-                  const uint32_t hb = *reinterpret_cast<const uint16_t*>(rowp + 2 * j);
-                  x = (p.x_dtype == 1) ? __uint_as_float(hb << 16) : f16_bits_to_f32(hb);
-                }
-              } else {
-                x = load_elem(p.x, v * p.ld_x + j, p.x_dtype);
-              }
+            float x;
+            if (p.staged) {
+              if constexpr (XT == 0) x = *reinterpret_cast<const float*>(rowp + 4 * j);
+              else x = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * j));
+              x = (valid[gg] && j < p.d_in) ? x : 0.0f;
+            } else {
+              x = (valid[gg] && j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
             }
             ss[gg] = fma((double)x, (double)x, ss[gg]);
             xv[gg][s] = x * dsg[s];
@@ -381,116 +395,146 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           const float n16f = f16_bits_to_f32(n16[gg]);
           const float nf = (float)nrm;
           const float zinv = nf > 0.0f ? __builtin_amdgcn_rcpf(nf * sqrt_d) : 0.0f;
-          uint32_t myword = 0;
-          int amb = 0;
           rsq[gg] = 0.0f;
+          int amb = 0;
 #pragma unroll
           for (int s = 0; s < NB; ++s) {
             const float z = xv[gg][s] * zinv;
-            const int off = s < p.split_blocks ? s * (BLO + 1)
-                                               : p.split_blocks * (BLO + 1) + (s - p.split_blocks) * (BHI + 1);
-            const float cv = (s < p.split_blocks)
-                                 ? encode_slot<BLO>(z, cpos_lds, tpl, off, myword, amb, count)
-                                 : encode_slot<BHI>(z, cpos_lds + 8, tph, off, myword, amb, count);
+            uint64_t pl[3];
+            float cv;
+            int nb;
+            if constexpr (UNI) {
+              cv = encode_slot<BLO, COUNT>(z, cpos_lds, tpl, pl, amb);
+              nb = BLO;
+            } else {
+              if (s < p.split_blocks) {
+                cv = encode_slot<BLO, COUNT>(z, cpos_lds, tpl, pl, amb);
+                nb = BLO;
+              } else {
+                cv = encode_slot<BHI, COUNT>(z, cpos_lds + 8, tph, pl, amb);
+                nb = BHI;
+              }
+            }
+            // lane 0 drops the plane ballots into the tile's ballot table
+            if (lane == 0) {
+#pragma unroll
+              for (int q = 0; q < 3; ++q)
+                if (q < nb) bal[((pp0 + gg) * NB + s) * 4 + q] = pl[q];
+            }
             r[gg][s] = fmaf(xv[gg][s], inv_sqrt_d, -n16f * cv);
             rsq[gg] = fmaf(r[gg][s], r[gg][s], rsq[gg]);
           }
-          if (c < p.words) stage[vloc[gg] * 32 + c] = myword;
-          if (count) cnt_amb += valid[gg] ? (unsigned long long)amb : 0ull;
+          if constexpr (COUNT) cnt_amb += valid[gg] ? (unsigned long long)amb : 0ull;
         }
 #pragma unroll
         for (int gg = 0; gg < PG; ++gg) {
           const float rs = half_sum(rsq[gg]);
           const float rn = sqrtf(rs);
           const uint32_t r16 = f32_to_f16_bits(rn);
-          const float rinv = rn > 0.0f ? 1.0f / rn : 0.0f;
+          const float rinv = rn > 0.0f ? kRScale / rn : 0.0f;
 #pragma unroll
-          for (int s = 0; s < NB; ++s) rhat[swz<D>(vloc[gg], 32 * s + c)] = r[gg][s] * rinv;
+          for (int s = 0; s < NB; ++s) {
+            const float rv = r[gg][s] * rinv;
+            const _Float16 hi = (_Float16)rv;
+            const _Float16 lo = (_Float16)(rv - (float)hi);
+            *reinterpret_cast<_Float16*>(tileb + hoff<D>(vloc[gg], 32 * s + c, 0)) = hi;
+            *reinterpret_cast<_Float16*>(tileb + hoff<D>(vloc[gg], 32 * s + c, 1)) = lo;
+          }
           if (c == 0) snorm[vloc[gg]] = n16[gg] | (r16 << 16);
-          if (count && c == 0 && valid[gg] && n16[gg] == 0x7C00u) cnt_ovf += 1;  // lanes 0, 32
+          if constexpr (COUNT)
+            if (c == 0 && valid[gg] && n16[gg] == 0x7C00u) cnt_ovf += 1;  // lanes 0, 32
         }
       }
       // next tile's input is fetched while this one is on the MFMA pipe
       const int64_t gn = g + gridDim.x;
       if (p.staged && gn < ngroups && gn * NW + wave < ntiles) fetch_tile<D>(p, cp, (gn * NW + wave) * TV, pre);
     }
-    // ---------------- phase 2: JL projection on MFMA, sign words (one block per step)
+    // ---------------- phase 2: JL projection on MFMA (3 fp16 products), sign ballots
     for (int blk = 0; blk < NB; ++blk) {
       if constexpr (!C::kResidentS) {
         __syncthreads();
-        for (int i = threadIdx.x; i < 32 * D / 4; i += blockDim.x) {
-          const int row = (4 * i) / D, col = (4 * i) % D;
-          const f32x4 v = reinterpret_cast<const f32x4*>(p.S + (int64_t)blk * 32 * D)[i];
-          *reinterpret_cast<f32x4*>(&S_l[swz<D>(row, col)]) = v;
-        }
+        load_s_rows(blk * 32, 32);
         __syncthreads();
       }
       if (!active) continue;
       const int s_row0 = C::kResidentS ? 0 : blk * 32;
-      const int arow = lane & 15, kg = (lane >> 4) * (D / 4);
+      const int arow = lane & 15, kg = 8 * (lane >> 4);
+      const int brow = blk * 32 + arow - s_row0;
       f32x4 acc0 = {}, acc1 = {};
-      const int brow0 = blk * 32 + arow - s_row0;
-#pragma unroll 4
-      for (int kc = 0; kc < D / 16; ++kc) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&rhat[swz<D>(arow, kg + 4 * kc)]);
-        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&S_l[swz<D>(brow0, kg + 4 * kc)]);
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&S_l[swz<D>(brow0 + 16, kg + 4 * kc)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i], b4[i], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i], c4[i], acc1, 0, 0, 0);
-        }
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const int col = 32 * ks + kg;
+        const f16x8 ah = *reinterpret_cast<const f16x8*>(tileb + hoff<D>(arow, col, 0));
+        const f16x8 al = *reinterpret_cast<const f16x8*>(tileb + hoff<D>(arow, col, 1));
+        const f16x8 bh0 = *reinterpret_cast<const f16x8*>(S_l + hoff<D>(brow, col, 0));
+        const f16x8 bl0 = *reinterpret_cast<const f16x8*>(S_l + hoff<D>(brow, col, 1));
+        const f16x8 bh1 = *reinterpret_cast<const f16x8*>(S_l + hoff<D>(brow + 16, col, 0));
+        const f16x8 bl1 = *reinterpret_cast<const f16x8*>(S_l + hoff<D>(brow + 16, col, 1));
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh1, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl1, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh1, acc1, 0, 0, 0);
       }
-      // acc_t[r] of lane l: u[vector 4(l/16) + r][32 blk + 16 t + l%16]
-      uint64_t sg0[4], sg1[4];
+      // acc_t[r] of lane l: kUScale * u[vector 4(l/16) + r][32 blk + 16 t + l%16]
+      uint64_t sg[2][4], gm[2][4];
       bool any_guard = false;
-      uint64_t gm0[4], gm1[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        sg0[rr] = __ballot(acc0[rr] >= 0.0f);
-        sg1[rr] = __ballot(acc1[rr] >= 0.0f);
-        gm0[rr] = __ballot(fabsf(acc0[rr]) < kGuard);
-        gm1[rr] = __ballot(fabsf(acc1[rr]) < kGuard);
-        any_guard |= (gm0[rr] | gm1[rr]) != 0;
+        sg[0][rr] = __ballot(acc0[rr] >= 0.0f);
+        sg[1][rr] = __ballot(acc1[rr] >= 0.0f);
+        gm[0][rr] = __ballot(fabsf(acc0[rr]) < kGuard * kUScale);
+        gm[1][rr] = __ballot(fabsf(acc1[rr]) < kGuard * kUScale);
+        any_guard |= (gm[0][rr] | gm[1][rr]) != 0;
       }
-      // lane v (< 16) assembles the sign word of vector v for this block
-      uint32_t sword = 0;
-      const int vq = lane & 3, vsh = 16 * ((lane >> 2) & 3);
+      if (lane == 0) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const uint32_t w = (uint32_t)((sg0[rr] >> vsh) & 0xFFFFu) |
-                           ((uint32_t)((sg1[rr] >> vsh) & 0xFFFFu) << 16);
-        sword = (vq == rr) ? w : sword;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) sbal[(blk * 2 + t) * 4 + rr] = sg[t][rr];
       }
-      const int sw_off = word_off_s[blk] + blk_bits_s[blk];
-      if (lane < TV) stage[lane * 32 + sw_off] = sword;
       if (any_guard) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            uint64_t gm = t ? gm1[rr] : gm0[rr];
-            while (gm) {
-              const int L = __builtin_ctzll(gm);
-              gm &= gm - 1;
+            uint64_t gmk = gm[t][rr];
+            while (gmk) {
+              const int L = __builtin_ctzll(gmk);
+              gmk &= gmk - 1;
               const int m = 4 * (L >> 4) + rr;
               const int64_t v = v0 + m;
               if (v >= p.n) continue;
               cnt_guard += (lane == 0);
-              guard_fix<D>(p, v, m, blk * 32 + 16 * t + (L & 15), S_l, s_row0, stage, snorm,
-                           cent_lds, word_off_s, blk_bits_s, cnt_zero);
+              guard_fix<D, XT>(p, v, m, blk * 32 + 16 * t + (L & 15), bal, sbal, snorm, cent_lds,
+                           BLO, BHI, cnt_zero);
             }
           }
       }
     }
     if (!active) continue;
-    // ---------------- store the tile: records (contiguous) and norms
+    // ---------------- store the tile: assemble record words from the ballot tables
     const int nvalid = (int)((p.n - v0) < TV ? (p.n - v0) : TV);
     uint32_t* dst = p.codes + v0 * p.words;
-    for (int i = lane; i < nvalid * p.words; i += 64) dst[i] = stage[(i / p.words) * 32 + (i % p.words)];
+    const uint32_t* b32 = reinterpret_cast<const uint32_t*>(bal);
+    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(sbal);
+    for (int i = lane; i < nvalid * p.words; i += 64) {
+      const int v = i / p.words, w = i - v * p.words;
+      const int wm = wmap[w], blk = wm >> 8, q = wm & 0xFF;
+      uint32_t word;
+      if (q != 0xFF) {
+        word = b32[(((v >> 1) * NB + blk) * 4 + q) * 2 + (v & 1)];
+      } else {
+        const int rr = v & 3, gq = v >> 2;
+        word = (uint32_t)s16[((blk * 2 + 0) * 4 + rr) * 4 + gq] |
+               ((uint32_t)s16[((blk * 2 + 1) * 4 + rr) * 4 + gq] << 16);
+      }
+      dst[i] = word;
+    }
     if (lane < nvalid) p.norms[v0 + lane] = snorm[lane];
   }
-  if (count) {
+  if constexpr (COUNT) {
     unsigned long long tot = cnt_amb, ovf = cnt_ovf;
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
@@ -506,13 +550,13 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
   }
 }
 
-template <int D, int BLO, int BHI>
-static int launch_quantize(const QParams& p, hipStream_t stream, int num_cu) {
+template <int D, int BLO, int BHI, int XT, bool COUNT>
+static int launch_q(const QParams& p, hipStream_t stream, int num_cu) {
   using C = QCfg<D>;
-  const size_t lds = sizeof(float) * (size_t)(C::kSRows * D + C::NW * C::kWaveF);
+  const size_t lds = (size_t)C::kSRows * C::kRowB + (size_t)C::NW * C::kWaveB;
   static bool attr_set = false;  // per template instance
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)quantize_kernel<D, BLO, BHI>,
+    if (hipFuncSetAttribute((const void*)quantize_kernel<D, BLO, BHI, XT, COUNT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return TQ_ERR_HIP;
     attr_set = true;
@@ -520,9 +564,20 @@ static int launch_quantize(const QParams& p, hipStream_t stream, int num_cu) {
   const int64_t ntiles = (p.n + C::TV - 1) / C::TV;
   const int64_t ngroups = (ntiles + C::NW - 1) / C::NW;
   const int64_t grid = ngroups < (int64_t)num_cu ? ngroups : (int64_t)num_cu;
-  hipLaunchKernelGGL((quantize_kernel<D, BLO, BHI>), dim3((unsigned)grid), dim3(64 * C::NW), lds,
-                     stream, p);
+  hipLaunchKernelGGL((quantize_kernel<D, BLO, BHI, XT, COUNT>), dim3((unsigned)grid),
+                     dim3(64 * C::NW), lds, stream, p);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+template <int D, int BLO, int BHI>
+static int launch_quantize(const QParams& p, int xt, hipStream_t stream, int num_cu) {
+  const bool count = p.counters != nullptr;
+  if (xt == 0) return count ? launch_q<D, BLO, BHI, 0, true>(p, stream, num_cu)
+                            : launch_q<D, BLO, BHI, 0, false>(p, stream, num_cu);
+  if (xt == 1) return count ? launch_q<D, BLO, BHI, 1, true>(p, stream, num_cu)
+                            : launch_q<D, BLO, BHI, 1, false>(p, stream, num_cu);
+  return count ? launch_q<D, BLO, BHI, 2, true>(p, stream, num_cu)
+               : launch_q<D, BLO, BHI, 2, false>(p, stream, num_cu);
 }
 
 }  // namespace tqk
@@ -541,7 +596,6 @@ int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, in
   p.n = n;
   p.ld_x = ld_x;
   p.d_in = d_in;
-  p.x_dtype = x_dtype;
   p.esize = x_dtype == TQ_F32 ? 4 : 2;
   const int64_t row_bytes = (int64_t)d_in * p.esize;
   p.staged = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && ((ld_x * p.esize) % 16 == 0) &&
@@ -563,16 +617,16 @@ int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, in
   fill(f->bits_hi, t->centroids_hi, t->bounds_hi, p.cpos_hi, p.tpos_hi, p.cent_hi);
   const int ncu = tq_num_cus();
   if (ncu <= 0) return TQ_ERR_HIP;
-  const int lo = f->bits_lo, hi = f->bits_hi;
+  const int lo = f->bits_lo, hi = f->bits_hi, xt = x_dtype;
   if (f->d == 128) {
-    if (lo == 1 && hi == 1) return launch_quantize<128, 1, 1>(p, stream, ncu);
-    if (lo == 2 && hi == 2) return launch_quantize<128, 2, 2>(p, stream, ncu);
-    if (lo == 3 && hi == 3) return launch_quantize<128, 3, 3>(p, stream, ncu);
-    if (lo == 3 && hi == 2) return launch_quantize<128, 3, 2>(p, stream, ncu);
-    if (lo == 2 && hi == 1) return launch_quantize<128, 2, 1>(p, stream, ncu);
+    if (lo == 1 && hi == 1) return launch_quantize<128, 1, 1>(p, xt, stream, ncu);
+    if (lo == 2 && hi == 2) return launch_quantize<128, 2, 2>(p, xt, stream, ncu);
+    if (lo == 3 && hi == 3) return launch_quantize<128, 3, 3>(p, xt, stream, ncu);
+    if (lo == 3 && hi == 2) return launch_quantize<128, 3, 2>(p, xt, stream, ncu);
+    if (lo == 2 && hi == 1) return launch_quantize<128, 2, 1>(p, xt, stream, ncu);
   } else if (f->d == 256) {
-    if (lo == 2 && hi == 2) return launch_quantize<256, 2, 2>(p, stream, ncu);
-    if (lo == 3 && hi == 3) return launch_quantize<256, 3, 3>(p, stream, ncu);
+    if (lo == 2 && hi == 2) return launch_quantize<256, 2, 2>(p, xt, stream, ncu);
+    if (lo == 3 && hi == 3) return launch_quantize<256, 3, 3>(p, xt, stream, ncu);
   }
   return TQ_ERR_SHAPE;
 }
