@@ -67,15 +67,15 @@ def _traffic(kernel_src: str, summary: str):
 
 
 def cpu_baseline(kb, vb, qb, signs, S):
-    """The oracle as it stands, on the host cores, on a bounded sample of the same workload:
-    quantize + pack the keys and values of 2 of the 8 KV heads over the first 8192 tokens,
-    then decode attention for those heads' 8 query heads over that sample."""
+    """The oracle as it stands, on the host cores, over the same layer (about 15 s of CPU
+    work): quantize + pack the keys and values of all 8 KV heads x 32768 tokens, then one
+    decode step of attention for the 32 query heads."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from threadpoolctl import threadpool_info
     from oracle import tq_oracle as O
     from parity_utils import oracle_decode, oracle_pack_cache
     import tq_inputs as TI
-    nt, nh = 8192, 2
+    nt, nh = NTOK, HKV
     fmt = O.Format.uniform(D, BITS)
     t0 = time.perf_counter()
     rk, nk, _ = oracle_pack_cache(kb[:, :nh, :nt], fmt, signs, S, bf16=True)
@@ -88,7 +88,7 @@ def cpu_baseline(kb, vb, qb, signs, S):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": packed / (t2 - t1) / 1e9, "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{nh} of 8 KV heads x {nt} tokens: quantize+pack {2 * nh * nt} vectors "
+            "sample": f"whole layer, {nh} KV heads x {nt} tokens: quantize+pack {2 * nh * nt} vectors "
                       f"({t1 - t0:.2f} s, {nt / (t1 - t0) * (nh / HKV):.3g} layer-tokens/s), "
                       f"decode {nh * HQ // HKV} query heads ({t2 - t1:.2f} s); value = packed "
                       f"K+V bytes decoded per second",
