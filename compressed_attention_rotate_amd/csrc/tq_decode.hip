@@ -7,24 +7,27 @@
 // rotated back per token: values are accumulated in the rotated domain and each head's
 // result is mapped back once (S^T, then D H / sqrt(d)).
 //
-// Three launches:
-//   prologue: per (batch, KV head, chunk of GC query heads) one workgroup: q_rot and
-//             S q_rot of the GC heads, and their nibble subset-sum tables (sums of w over
-//             the set bits of a 4-bit index, for every 4-coordinate group).
-//   scan:     grid (split, batch * KV head * chunk), about one workgroup per CU.  The
-//             workgroup expands the nibble tables into byte-indexed tables in LDS,
-//             T[g][m] = sum of w_{8g+i} over the set bits i of m (one float per head), so
-//             a sign dot product <w, 2b - 1> over 128 coordinates is 16 table reads: the
-//             QJL term directly, and the codebook term through the Walsh expansion of the
-//             symmetric codebook, c[idx] = sum_S alpha_S prod_{k in S} (2 b_k - 1) over odd
-//             subsets S of the code bit-planes (the planes, and for 3 bits their XOR).
-//             Keys: lane = token; records of the next 64-token tile are prefetched into
+// Two launches:
+//   scan:     grid (split, batch * KV head * chunk of GC query heads), about one
+//             workgroup of 8 waves per CU.  The workgroup first derives its own query
+//             tables (while its first cache tile is already in flight): q_rot of the GC
+//             heads (FWHT over the wave), S q_rot (S rows from L2), and in LDS
+//               Tq[g][m] = sum of q_rot over the set bits of byte m of coordinate group g
+//               Ts[g][n] = 2 * sum of S q_rot over the set bits of nibble n,
+//             one float per head.  A sign dot product <w, 2b - 1> over 128 coordinates is
+//             then 16 byte (or 32 nibble) table reads: the codebook term through the Walsh
+//             expansion of the symmetric codebook, c[idx] = sum_S alpha_S prod_{k in S}
+//             (2 b_k - 1) over odd subsets S of the code bit-planes (the planes, and for
+//             3 bits their XOR), the QJL term directly.
+//             Keys: lane = token, records of the wave's next 64-token tile prefetched into
 //             registers.  Online softmax per head with wavefront reductions; the Sparse-V
 //             gate (zhidx turboquant_plus article, section "01 turboquant_plus：介绍与详解")
 //             drops a value row for a head when its running weight estimate is below tau,
-//             and skips reading rows dropped by every head.  Values: lane = coordinate
-//             pair, fp32 accumulation of w n16 c[idx] and w gamma r16 sigma per head.  The
-//             waves' partial (m, l, acc) are merged in LDS: one partial per workgroup.
+//             and skips reading rows dropped by every head.  Values: each lane owns 4
+//             coordinates, the two half-waves take alternate kept tokens; the centroid
+//             pair of two coordinates comes from one read of a table indexed by their
+//             code bits; fp32 accumulation of w n16 c[idx] and w gamma r16 sigma per head.
+//             The waves' partial (m, l, acc) are merged in LDS: one partial per workgroup.
 //   combine:  per (batch, query head) one workgroup merges the splits in a fixed order and
 //             maps back: out = D H (A + S^T Q) / (sqrt(d) l).
 #include <hip/hip_runtime.h>
@@ -44,18 +47,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kNB = kD / 32;
-constexpr int kScanWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;
 constexpr int kPartFloats = 2 + 2 * kD;  // m (log2 domain), l, A[d], Q[d]
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kNibFloats = 2 * 16 * 2 * 16;  // per head: [vec][group][half][nibble]
-// per-unit stride of the nibble tables + 2 constants per head, kept a multiple of 16 bytes
-__host__ __device__ constexpr int nib_stride(int gc) { return ((kNibFloats + 2) * gc + 3) / 4 * 4; }
 
-template <int B>
-struct Walsh {  // number of odd plane subsets of a B-bit code: the Walsh planes used
-  static constexpr int N = (B == 3) ? 4 : B;
-};
+__host__ __device__ constexpr int round4(int x) { return (x + 3) / 4 * 4; }
 
 // Record layout of a format with SPLITB blocks of BLO bits then blocks of BHI bits.
 template <int BLO, int BHI, int SPLITB>
@@ -63,7 +61,7 @@ struct Rec {
   static constexpr int W = SPLITB * (BLO + 1) + (kNB - SPLITB) * (BHI + 1);  // words
   static constexpr int VEC = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);      // load width
   static constexpr int bits(int blk) { return blk < SPLITB ? BLO : BHI; }
-  static constexpr int off(int blk) {
+  __host__ __device__ static constexpr int off(int blk) {
     return blk < SPLITB ? blk * (BLO + 1) : SPLITB * (BLO + 1) + (blk - SPLITB) * (BHI + 1);
   }
 };
@@ -88,6 +86,14 @@ __device__ __forceinline__ void load_record(const uint32_t* rec, uint32_t (&w)[W
   }
 }
 
+// Entries of the centroid-pair table of a B-bit codebook.  A lane's 4 coordinates have
+// code-bit nibbles b0, b1, b2 (one per plane); f = b0 << 1 | b1 << 5 | b2 << 9 holds
+// the 2-bit fields of coordinates (2, 3) at bits 3-4, 7-8, 11-12, so (f & 0x1998) is 8
+// times the sparse pattern P = p0 | p1 << 4 | p2 << 8 of that coordinate pair, and
+// ((f << 2) & 0x1998) the same for coordinates (0, 1).  Entry P = (c[lo], c[hi]).
+__host__ __device__ constexpr int pat_entries(int B) { return B == 3 ? 0x334 : (B == 2 ? 0x34 : 4); }
+constexpr uint32_t kPatMask = 0x1998u;
+
 struct DecodeParams {
   const void* q;
   const uint32_t* codes_k;
@@ -100,12 +106,10 @@ struct DecodeParams {
   float* out;
   float* logits;
   unsigned long long* skipped;
-  float* ws_qrot;   // [batch*hq][2][d]: q_rot, S_k q_rot
-  float* ws_nib;    // [units][kNibFloats][GC] + [units][2][GC] constants
   float* ws_part;   // [batch*hq][n_split][kPartFloats]
   int64_t capacity;
   int64_t tokens_per_split;
-  int32_t batch, hq, hkv, group, gc, q_dtype, n_split;
+  int32_t batch, hq, hkv, group, q_dtype, n_split;
   float scale, tau, gamma;
   uint32_t sign_k[4], sign_v[4];
   float alpha_k[2][4];  // Walsh coefficients of the key codebooks (lo, hi parts)
@@ -113,27 +117,125 @@ struct DecodeParams {
   int32_t ksplitb;
 };
 
-// ----------------------------------------------------------------------------- prologue
-// One workgroup of 128 threads per (batch, query head): q_rot = H D q / sqrt(d),
-// S q_rot, this head's slice of the nibble subset-sum tables of its chunk, and the two
-// constants of <w, 2b - 1> = 2 <w, b> - sum(w).
+// LDS layout of one scan workgroup (floats).
+template <int GC, int VW, int BVLO, int BVHI, int VSPLIT>
+struct ScanLds {
+  static constexpr int kTq = 16 * 256 * GC;   // [16 byte groups][256][GC]
+  static constexpr int kTs = 32 * 16 * GC;    // [32 nibble groups][16][GC]
+  static constexpr int kCpLo = round4(2 * pat_entries(BVLO));
+  static constexpr int kCpHi = VSPLIT < kNB ? round4(2 * pat_entries(BVHI)) : 0;
+  static constexpr int kSp = 16 * 4;
+  static constexpr int kW0 = 2 * GC <= 4 ? 4 : 8;        // row: u[GC], u'[GC] | value record
+  static constexpr int kRS = round4(kW0 + VW);           // row stride (words)
+  static constexpr int kArea = (kTile + 1) * kRS + 4;    // 64 token rows + zero row + pad
+  static constexpr int oTq = 0, oTs = kTq, oCpLo = oTs + kTs, oCpHi = oCpLo + kCpLo;
+  static constexpr int oSp = oCpHi + kCpHi, oArea = oSp + kSp;
+  static constexpr int kTotal = oArea + kWaves * kArea;
+  static constexpr int kMerge = round4(2 * GC) + 2 * kD * GC;  // per wave, aliases Tq
+  static_assert(kWaves * kMerge <= kTq, "merge area must fit in the byte tables");
+  static_assert(2 * GC * kD + 16 * 2 * 16 * GC <= kWaves * kArea, "setup scratch must fit");
+};
+
 template <int GC>
-__global__ __launch_bounds__(128) void decode_prologue(DecodeParams p) {
-  const int bh = blockIdx.x;               // b * hq + h
-  const int b = bh / p.hq, h = bh % p.hq;
-  const int bk = b * p.hkv + h / p.group;  // kv unit
-  const int hin = h % p.group;
-  const int unit = bk * (p.group / GC) + hin / GC;
-  const int hh = hin % GC;                 // head slot inside the chunk
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  __shared__ float wv[2][kD];
-  __shared__ float red[4];
-  if (wave == 0) {
+__device__ __forceinline__ void table_read(const float* T, int idx, float (&out)[GC]) {
+  if constexpr (GC == 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(T + 4 * idx);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  } else if constexpr (GC == 2) {
+    const f32x2 v = *reinterpret_cast<const f32x2*>(T + 2 * idx);
+    out[0] = v[0]; out[1] = v[1];
+  } else {
+    out[0] = T[idx];
+  }
+}
+
+// acc += alpha * (byte-table reads of one 32-bit plane word, byte groups g0 .. g0+3); the
+// four reads are summed pairwise first so every read is consumed right away.
+template <int GC>
+__device__ __forceinline__ void lut_byte(const float* Tq, int g0, uint32_t w, float alpha,
+                                         float (&acc)[GC]) {
+  float t0[GC], t1[GC], t2[GC], t3[GC];
+  table_read<GC>(Tq, (g0 + 0) * 256 + (w & 0xFFu), t0);
+  table_read<GC>(Tq, (g0 + 1) * 256 + ((w >> 8) & 0xFFu), t1);
+  table_read<GC>(Tq, (g0 + 2) * 256 + ((w >> 16) & 0xFFu), t2);
+  table_read<GC>(Tq, (g0 + 3) * 256 + (w >> 24), t3);
+#pragma unroll
+  for (int h = 0; h < GC; ++h) acc[h] = fmaf(alpha, (t0[h] + t1[h]) + (t2[h] + t3[h]), acc[h]);
+}
+
+// acc += nibble-table reads of one 32-bit sign word (nibble groups g0 .. g0+7), summed as
+// a tree.
+template <int GC>
+__device__ __forceinline__ void lut_nib(const float* Ts, int g0, uint32_t w, float (&acc)[GC]) {
+  float t[8][GC];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) table_read<GC>(Ts, (g0 + i) * 16 + ((w >> (4 * i)) & 0xFu), t[i]);
+#pragma unroll
+  for (int h = 0; h < GC; ++h)
+    acc[h] += ((t[0][h] + t[1][h]) + (t[2][h] + t[3][h])) + ((t[4][h] + t[5][h]) + (t[6][h] + t[7][h]));
+}
+
+template <int BKLO, int BKHI, int KSPLIT, int BVLO, int BVHI, int VSPLIT, int GC>
+__global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
+  using KR = Rec<BKLO, BKHI, KSPLIT>;
+  using VR = Rec<BVLO, BVHI, VSPLIT>;
+  constexpr int KW = KR::W, VW = VR::W;
+  using L = ScanLds<GC, VW, BVLO, BVHI, VSPLIT>;
+  constexpr int kW0 = L::kW0, kRS = L::kRS;
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  float* Tq = lds + L::oTq;
+  float* Ts = lds + L::oTs;
+  float* cpLo = lds + L::oCpLo;
+  float* cpHi = lds + L::oCpHi;
+  float* spat = lds + L::oSp;
+  __shared__ float cconst[2][GC];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
+  const int nchunk = p.group / GC;
+  const int unit = blockIdx.y;
+  const int chunk = unit % nchunk;
+  const int bk = unit / nchunk;  // b * hkv + kv head
+  const int b = bk / p.hkv;
+  const int h0 = (bk % p.hkv) * p.group + chunk * GC;
+  const int64_t seq = p.seq_lens[b];
+  const int64_t t_begin = (int64_t)blockIdx.x * p.tokens_per_split;
+  int64_t t_end = t_begin + p.tokens_per_split;
+  if (t_end > seq) t_end = seq;
+  const int64_t kv_base = (int64_t)bk * p.capacity;
+  const bool gated = p.tau > 0.0f;
+
+  // ---- register prefetch of the wave's first tile: key record, value record, norms
+  uint32_t kw[KW], vwr[VW], knr = 0, vnr = 0;
+  auto fetch = [&](int64_t tt0) {
+    const int64_t t = tt0 + lane;
+    if (tt0 < t_end && t < t_end) {
+      load_record<KW, KR::VEC>(p.codes_k + (kv_base + t) * KW, kw);
+      if (!gated) load_record<VW, VR::VEC>(p.codes_v + (kv_base + t) * VW, vwr);
+      knr = p.norms_k[kv_base + t];
+      vnr = p.norms_v[kv_base + t];
+    }
+  };
+  int64_t t0 = t_begin + (int64_t)wave * kTile;
+  fetch(t0);
+
+  // ---- query tables
+  float* qs = lds + L::oArea;             // [2][GC][kD]: q_rot, S q_rot (setup scratch)
+  float* nibq = qs + 2 * GC * kD;         // [16 groups][2 halves][16][GC]
+  const int srow = tid >> 2, sq4 = tid & 3;
+  f32x4 sr[8];  // S[srow][32 sq4 .. 32 sq4 + 31]
+  {
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.S_k + (int64_t)srow * kD + 32 * sq4);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sr[c] = src[c];
+  }
+  if (wave < GC) {  // q_rot of head h0 + wave
     float v[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int j = lane + 64 * e;
-      float x = load_elem(p.q, (int64_t)bh * kD + j, p.q_dtype);
+      float x = load_elem(p.q, ((int64_t)b * p.hq + h0 + wave) * kD + j, p.q_dtype);
       if ((p.sign_k[j >> 5] >> (j & 31)) & 1u) x = -x;
       v[e] = x;
     }
@@ -150,190 +252,103 @@ __global__ __launch_bounds__(128) void decode_prologue(DecodeParams p) {
         v[e] = (lane & m) ? t - v[e] : v[e] + t;
       }
     const float isd = 1.0f / sqrtf((float)kD);
-    wv[0][lane] = v[0] * isd;
-    wv[0][lane + 64] = v[1] * isd;
+    qs[wave * kD + lane] = v[0] * isd;
+    qs[wave * kD + lane + 64] = v[1] * isd;
   }
   __syncthreads();
-  // S q_rot: thread t computes row t (16-byte reads of the row)
-  {
-    const f32x4* row = reinterpret_cast<const f32x4*>(p.S_k + (int64_t)tid * kD);
-    float s = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < kD / 4; ++k) {
-      const f32x4 a = row[k];
-      s = fmaf(a[0], wv[0][4 * k], s);
-      s = fmaf(a[1], wv[0][4 * k + 1], s);
-      s = fmaf(a[2], wv[0][4 * k + 2], s);
-      s = fmaf(a[3], wv[0][4 * k + 3], s);
+  {  // S q_rot: thread (row srow, quarter sq4) sums 32 columns, then the 4 quarter lanes
+    float acc[GC];
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+      float s = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + h * kD + 32 * sq4 + 4 * c);
+        s = fmaf(sr[c][0], qv[0], s);
+        s = fmaf(sr[c][1], qv[1], s);
+        s = fmaf(sr[c][2], qv[2], s);
+        s = fmaf(sr[c][3], qv[3], s);
+      }
+      s += xchg<1>(s);
+      s += xchg<2>(s);
+      acc[h] = s;
     }
-    wv[1][tid] = s;
-    float* dst = p.ws_qrot + (int64_t)bh * 2 * kD;
-    dst[tid] = wv[0][tid];
-    dst[kD + tid] = s;
+    if (sq4 == 0) {
+#pragma unroll
+      for (int h = 0; h < GC; ++h) qs[(GC + h) * kD + srow] = acc[h];
+    }
   }
   __syncthreads();
-  // nibble subset sums [vec][group][half][nibble][GC], this head's slot
-  float* nib = p.ws_nib + (int64_t)unit * nib_stride(GC);
-  for (int i = tid; i < kNibFloats; i += 128) {
-    const int n = i % 16, half = (i / 16) % 2, g = (i / 32) % 16, vv = i / 512;
-    float sum = 0.0f;
+  if (wave < GC) {  // constants: codebook term (sum_k alpha_k) sum_j q_j per block; sum S q
+    const int h = wave;
+    float asum[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      asum[0] += p.alpha_k[0][k];
+      asum[1] += p.alpha_k[1][k];
+    }
+    const int blk0 = lane >> 5, blk1 = 2 + (lane >> 5);  // blocks of j = lane, lane + 64
+    const float v = (blk0 < p.ksplitb ? asum[0] : asum[1]) * qs[h * kD + lane] +
+                    (blk1 < p.ksplitb ? asum[0] : asum[1]) * qs[h * kD + lane + 64];
+    const float cq = wave_sum_fast(v);
+    const float ws = wave_sum_fast(qs[(GC + h) * kD + lane] + qs[(GC + h) * kD + lane + 64]);
+    if (lane == 0) {
+      cconst[0][h] = cq;
+      cconst[1][h] = ws;
+    }
+  }
+  for (int i = tid; i < 16 * 2 * 16 * GC; i += kThreads) {  // nibble sums of q_rot
+    const int h = i % GC, n = (i / GC) % 16, half = (i / (16 * GC)) % 2, g = i / (32 * GC);
+    const float* src = qs + h * kD + 8 * g + 4 * half;
+    float s = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if ((n >> k) & 1) sum += wv[vv][8 * g + 4 * half + k];
-    nib[i * GC + hh] = sum;
+      if ((n >> k) & 1) s += src[k];
+    nibq[i] = s;
   }
-  // constants: codebook term sum_blk (sum_k alpha_k) W_blk, QJL term sum(S q_rot)
-  {
-    const int blk = tid >> 5;  // 4 blocks of 32 coordinates over the 128 threads
-    const float wb = half_sum(wv[0][tid]);
-    const bool lo = blk < p.ksplitb;
-    float asum = 0.0f;
-    for (int k = 0; k < 4; ++k) asum += p.alpha_k[lo ? 0 : 1][k];
-    const float ss = half_sum(wv[1][tid]);
-    __shared__ float sred[4];
-    if ((tid & 31) == 0) {
-      red[blk] = asum * wb;
-      sred[blk] = ss;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      nib[kNibFloats * GC + hh] = ((red[0] + red[1]) + red[2]) + red[3];
-      nib[kNibFloats * GC + GC + hh] = ((sred[0] + sred[1]) + sred[2]) + sred[3];
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------- scan
-template <int GC, int VW>
-struct ScanLds {
-  static constexpr int kTable = 2 * 16 * 256 * GC;     // [vec][16 groups][256][GC]
-  static constexpr int kWave = (kTile + 1) * 2 * GC + (kTile + 1) * VW + 4;  // weights + V staging
-  static constexpr int kPartW = 2 * GC + 2 * kD * GC;  // merged partial of one wave
-  static constexpr int kArea = (kWave > kPartW ? kWave : kPartW);
-  static constexpr int kTotal = kTable + kScanWaves * kArea;
-  static_assert(kScanWaves * kArea >= kNibFloats * GC, "nibble tables alias the wave areas");
-};
-
-template <int GC>
-__device__ __forceinline__ void table_read(const float* T, int idx, float (&out)[GC]) {
-  if constexpr (GC == 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(T + 4 * idx);
-    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
-  } else if constexpr (GC == 2) {
-    const f32x2 v = *reinterpret_cast<const f32x2*>(T + 2 * idx);
-    out[0] = v[0]; out[1] = v[1];
-  } else {
-    out[0] = T[idx];
-  }
-}
-
-// Add alpha times the byte-table reads of one 32-bit sign word (groups g0 .. g0+3).
-template <int GC>
-__device__ __forceinline__ void lut_word(const float* T, int g0, uint32_t w, float alpha,
-                                         float (&acc)[GC]) {
+  for (int i = tid; i < 32 * 16 * GC; i += kThreads) {  // Ts: 2 * nibble sums of S q_rot
+    const int h = i % GC, n = (i / GC) % 16, g = i / (16 * GC);
+    const float* src = qs + (GC + h) * kD + 4 * g;
+    float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float t[GC];
-    table_read<GC>(T, (g0 + i) * 256 + ((w >> (8 * i)) & 0xFFu), t);
-#pragma unroll
-    for (int h = 0; h < GC; ++h) acc[h] = fmaf(alpha, t[h], acc[h]);
+    for (int k = 0; k < 4; ++k)
+      if ((n >> k) & 1) s += src[k];
+    Ts[i] = 2.0f * s;
   }
-}
-
-template <int B, int GC>
-__device__ __forceinline__ void key_block(const float* Tq, int blk, const uint32_t* w,
-                                          const float* alpha, float (&acc)[GC]) {
-  lut_word<GC>(Tq, 4 * blk, w[0], alpha[0], acc);
-  if constexpr (B >= 2) lut_word<GC>(Tq, 4 * blk, w[1], alpha[1], acc);
-  if constexpr (B >= 3) {
-    lut_word<GC>(Tq, 4 * blk, w[2], alpha[2], acc);
-    lut_word<GC>(Tq, 4 * blk, w[0] ^ w[1] ^ w[2], alpha[3], acc);
+  for (int i = tid; i < pat_entries(BVLO) + (VSPLIT < kNB ? pat_entries(BVHI) : 0); i += kThreads) {
+    const bool hi = i >= pat_entries(BVLO);
+    const int P = hi ? i - pat_entries(BVLO) : i;
+    const int nb = hi ? BVHI : BVLO;
+    const int mask = (1 << nb) - 1;
+    const int p0 = P & 15, p1 = (P >> 4) & 15, p2 = (P >> 8) & 15;
+    const int ilo = ((p0 & 1) | ((p1 & 1) << 1) | ((p2 & 1) << 2)) & mask;
+    const int ihi = (((p0 >> 1) & 1) | (((p1 >> 1) & 1) << 1) | (((p2 >> 1) & 1) << 2)) & mask;
+    float* dst = hi ? cpHi : cpLo;
+    dst[2 * P] = p.cent_v[hi ? 1 : 0][ilo];
+    dst[2 * P + 1] = p.cent_v[hi ? 1 : 0][ihi];
   }
-}
-
-template <int BKLO, int BKHI, int KSPLIT, int BVLO, int BVHI, int VSPLIT, int GC>
-__global__ __launch_bounds__(64 * kScanWaves) void decode_scan(DecodeParams p) {
-  using KR = Rec<BKLO, BKHI, KSPLIT>;
-  using VR = Rec<BVLO, BVHI, VSPLIT>;
-  constexpr int KW = KR::W, VW = VR::W;
-  using L = ScanLds<GC, VW>;
-  extern __shared__ __attribute__((aligned(16))) float lds[];
-  float* Tq = lds;                         // [16][256][GC]
-  float* Ts = lds + 16 * 256 * GC;         // [16][256][GC]
-  float* nib = lds + L::kTable;            // aliases the wave areas during setup
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  float* area = lds + L::kTable + wave * L::kArea;
-  float* wts = area;                                                        // [65][2*GC]
-  uint32_t* vst = reinterpret_cast<uint32_t*>(area + (kTile + 1) * 2 * GC);  // [65][VW] + 4
-  __shared__ float centv[16];
-  __shared__ __attribute__((aligned(16))) float cpair_s[2][128];  // [part][6-bit pair index][2]
-  __shared__ f32x2 spair[4];
-  __shared__ float cconst[2][GC];
-
-  const int nchunk = p.group / GC;
-  const int unit = blockIdx.y;
-  const int chunk = unit % nchunk;
-  const int bk = unit / nchunk;  // b * hkv + kv head
-  const int b = bk / p.hkv;
-  const int h0 = (bk % p.hkv) * p.group + chunk * GC;
-  const int64_t seq = p.seq_lens[b];
-  const int64_t t_begin = (int64_t)blockIdx.x * p.tokens_per_split;
-  int64_t t_end = t_begin + p.tokens_per_split;
-  if (t_end > seq) t_end = seq;
-
-  // ---- tables: nibble sums -> LDS -> byte tables
-  {
-    const float* src = p.ws_nib + (int64_t)unit * nib_stride(GC);
-    for (int i = threadIdx.x; i < kNibFloats * GC / 4; i += blockDim.x)
-      reinterpret_cast<f32x4*>(nib)[i] = reinterpret_cast<const f32x4*>(src)[i];
-    if (threadIdx.x < 2 * GC) (&cconst[0][0])[threadIdx.x] = src[kNibFloats * GC + threadIdx.x];
-    if (threadIdx.x < 16) centv[threadIdx.x] = (&p.cent_v[0][0])[threadIdx.x];
-    if (threadIdx.x < 128) {
-      // pair index f = (plane-0 bits, plane-1 bits, plane-2 bits) of two coordinates
-      const int part = threadIdx.x >> 6, f = threadIdx.x & 63;
-      const int nb = part == 0 ? BVLO : BVHI;
-      const int mask = (1 << nb) - 1;
-      const int i0 = ((f & 1) | (((f >> 2) & 1) << 1) | (((f >> 4) & 1) << 2)) & mask;
-      const int i1 = (((f >> 1) & 1) | (((f >> 3) & 1) << 1) | (((f >> 5) & 1) << 2)) & mask;
-      cpair_s[part][2 * f] = p.cent_v[part][i0];
-      cpair_s[part][2 * f + 1] = p.cent_v[part][i1];
-    }
-    if (threadIdx.x < 4) {
-      const f32x2 v = {(threadIdx.x & 1) ? 1.0f : -1.0f, (threadIdx.x & 2) ? 1.0f : -1.0f};
-      spair[threadIdx.x] = v;
-    }
-  }
+  if (tid < 64) spat[tid] = ((tid >> 2) >> (tid & 3)) & 1 ? 1.0f : -1.0f;
   __syncthreads();
-  for (int i = threadIdx.x; i < 2 * 16 * 16; i += blockDim.x) {
-    // thread: (vec, group, low nibble); loops over the high nibble
-    const int lo = i % 16, g = (i / 16) % 16, vv = i / 256;
-    float a[GC];
-    const float* nl = nib + (((vv * 16 + g) * 2 + 0) * 16 + lo) * GC;
+  for (int i = tid; i < 16 * 256; i += kThreads) {  // byte tables from nibble sums
+    const int g = i >> 8, m = i & 255;
+    float lo[GC], hi[GC];
+    table_read<GC>(nibq + ((g * 2 + 0) * 16) * GC, m & 15, lo);
+    table_read<GC>(nibq + ((g * 2 + 1) * 16) * GC, m >> 4, hi);
+    if constexpr (GC == 4) {
+      const f32x4 o = {lo[0] + hi[0], lo[1] + hi[1], lo[2] + hi[2], lo[3] + hi[3]};
+      *reinterpret_cast<f32x4*>(Tq + i * 4) = o;
+    } else {
 #pragma unroll
-    for (int h = 0; h < GC; ++h) a[h] = nl[h];
-    float* dst = (vv == 0 ? Tq : Ts) + (g * 256 + lo) * GC;
-    const float* nh = nib + (((vv * 16 + g) * 2 + 1) * 16) * GC;
-#pragma unroll 4
-    for (int hi = 0; hi < 16; ++hi) {
-      float hv[GC];
-      table_read<GC>(nh, hi, hv);
-      if constexpr (GC == 4) {
-        f32x4 o = {a[0] + hv[0], a[1] + hv[1], a[2] + hv[2], a[3] + hv[3]};
-        *reinterpret_cast<f32x4*>(dst + hi * 16 * GC) = o;
-      } else {
-#pragma unroll
-        for (int h = 0; h < GC; ++h) dst[hi * 16 * GC + h] = a[h] + hv[h];
-      }
+      for (int h = 0; h < GC; ++h) Tq[i * GC + h] = lo[h] + hi[h];
     }
   }
   __syncthreads();
 
-  float cq[GC], ws[GC];
+  float cq[GC], wsum[GC];
 #pragma unroll
   for (int h = 0; h < GC; ++h) {
     cq[h] = cconst[0][h];
-    ws[h] = cconst[1][h];
+    wsum[h] = cconst[1][h];
   }
   float alo[4], ahi[4];
 #pragma unroll
@@ -342,44 +357,67 @@ __global__ __launch_bounds__(64 * kScanWaves) void decode_scan(DecodeParams p) {
     ahi[k] = 2.0f * p.alpha_k[1][k];
   }
 
-  // value lane mapping: lane -> coordinates j0 = 32 (lane / 16) + 2 (lane % 16), j0 + 1
-  const int vblk = lane >> 4, vbit = 2 * (lane & 15);
+  // ---- per-wave area: 64 token rows + one all-zero row used to pad odd token counts
+  float* area = lds + L::oArea + wave * L::kArea;
+  for (int i = lane; i < kRS + 4; i += 64) area[kTile * kRS + i] = 0.0f;
+  // value lane mapping: half-wave hw takes alternate tokens; lane owns coordinates
+  // 4 c4 .. 4 c4 + 3 of block vblk, bits vbit .. vbit + 3 of its plane words
+  const int hw = lane >> 5, c4 = lane & 31;
+  const int vblk = c4 >> 3, vbit = 4 * (c4 & 7);
   const bool vlo = vblk < VSPLIT;
   const int vnb = vlo ? BVLO : BVHI;
-  const int voff = vlo ? vblk * (BVLO + 1) : VSPLIT * (BVLO + 1) + (vblk - VSPLIT) * (BVHI + 1);
-  const float* cpair = cpair_s[vlo ? 0 : 1];
-  // the zero row used to pad the 4-token value steps
-  for (int i = lane; i < 2 * GC; i += 64) wts[kTile * 2 * GC + i] = 0.0f;
-  for (int i = lane; i < VW + 4; i += 64) vst[kTile * VW + i] = 0u;
+  const int voff = kW0 + VR::off(vblk);
+  const char* cpb = reinterpret_cast<const char*>(vlo ? cpLo : cpHi);
+  const char* spb = reinterpret_cast<const char*>(spat);
 
-  float m_run[GC], l_run[GC], am[GC][2], aq[GC][2];
+  float m_run[GC], l_run[GC], am[GC][4], aq[GC][4];
 #pragma unroll
   for (int h = 0; h < GC; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.0f;
-    am[h][0] = am[h][1] = aq[h][0] = aq[h][1] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) am[h][k] = aq[h][k] = 0.0f;
   }
   unsigned long long n_skipped = 0;
-  const int64_t kv_base = (int64_t)bk * p.capacity;
   const float kscale = p.scale * kLog2e;
 
-  // register prefetch of one tile: key record, value record, both norms
-  uint32_t kw[KW], vwr[VW], knr = 0, vnr = 0;
-  int64_t t0 = t_begin + (int64_t)wave * kTile;
-  // with the Sparse-V gate on, value records are read only for rows that survive it
-  const bool gated = p.tau > 0.0f;
-  auto fetch = [&](int64_t tt0) {
-    const int64_t t = tt0 + lane;
-    if (tt0 < t_end && t < t_end) {
-      load_record<KW, KR::VEC>(p.codes_k + (kv_base + t) * KW, kw);
-      if (!gated) load_record<VW, VR::VEC>(p.codes_v + (kv_base + t) * VW, vwr);
-      knr = p.norms_k[kv_base + t];
-      vnr = p.norms_v[kv_base + t];
+  // one value row (this lane's 4 coordinates) accumulated with the row's weights
+  auto value_row = [&](const float* r) {
+    const uint32_t* rw = reinterpret_cast<const uint32_t*>(r) + voff;
+    uint32_t p0, p1 = 0, p2 = 0, sg;
+    if constexpr (BVLO == 3 && BVHI == 3) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(rw);
+      p0 = x[0]; p1 = x[1]; p2 = x[2]; sg = x[3];
+    } else {
+      const uint32_t x0 = rw[0], x1 = rw[1], x2 = rw[2], x3 = rw[3];
+      p0 = x0;
+      p1 = vnb >= 2 ? x1 : 0u;
+      p2 = vnb == 3 ? x2 : 0u;
+      sg = vnb == 3 ? x3 : (vnb == 2 ? x2 : x1);
+    }
+    const uint32_t f = (__builtin_amdgcn_ubfe(p0, vbit, 4) << 1) |
+                       (__builtin_amdgcn_ubfe(p1, vbit, 4) << 5) |
+                       (__builtin_amdgcn_ubfe(p2, vbit, 4) << 9);
+    const f32x2 cA = *reinterpret_cast<const f32x2*>(cpb + ((f << 2) & kPatMask));
+    const f32x2 cB = *reinterpret_cast<const f32x2*>(cpb + (f & kPatMask));
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(spb + 16 * __builtin_amdgcn_ubfe(sg, vbit, 4));
+    float u[GC], u2[GC];
+    table_read<GC>(r, 0, u);
+    table_read<GC>(r + GC, 0, u2);
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+      am[h][0] = fmaf(u[h], cA[0], am[h][0]);
+      am[h][1] = fmaf(u[h], cA[1], am[h][1]);
+      am[h][2] = fmaf(u[h], cB[0], am[h][2]);
+      am[h][3] = fmaf(u[h], cB[1], am[h][3]);
+      aq[h][0] = fmaf(u2[h], sv[0], aq[h][0]);
+      aq[h][1] = fmaf(u2[h], sv[1], aq[h][1]);
+      aq[h][2] = fmaf(u2[h], sv[2], aq[h][2]);
+      aq[h][3] = fmaf(u2[h], sv[3], aq[h][3]);
     }
   };
-  fetch(t0);
 
-  for (; t0 < t_end; t0 += (int64_t)kScanWaves * kTile) {
+  for (; t0 < t_end; t0 += (int64_t)kWaves * kTile) {
     const int64_t t = t0 + lane;
     const bool valid = t < t_end;
     uint32_t w[KW], vrec[VW];
@@ -388,34 +426,40 @@ __global__ __launch_bounds__(64 * kScanWaves) void decode_scan(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < VW; ++i) vrec[i] = vwr[i];
     const uint32_t kn = knr, vn = vnr;
-    fetch(t0 + (int64_t)kScanWaves * kTile);
+    fetch(t0 + (int64_t)kWaves * kTile);
     // ---------------- keys: lane = token
     float mse[GC], qjl[GC];
 #pragma unroll
     for (int h = 0; h < GC; ++h) mse[h] = qjl[h] = 0.0f;
 #pragma unroll
     for (int blk = 0; blk < kNB; ++blk) {
-      if (blk < KSPLIT) {
-        key_block<BKLO, GC>(Tq, blk, w + KR::off(blk), alo, mse);
-        lut_word<GC>(Ts, 4 * blk, w[KR::off(blk) + BKLO], 2.0f, qjl);
-      } else {
-        key_block<BKHI, GC>(Tq, blk, w + KR::off(blk), ahi, mse);
-        lut_word<GC>(Ts, 4 * blk, w[KR::off(blk) + BKHI], 2.0f, qjl);
+      const uint32_t* wb = w + KR::off(blk);
+      const int nb = blk < KSPLIT ? BKLO : BKHI;
+      const float* al = blk < KSPLIT ? alo : ahi;
+      lut_byte<GC>(Tq, 4 * blk, wb[0], al[0], mse);
+      if (nb >= 2) lut_byte<GC>(Tq, 4 * blk, wb[1], al[1], mse);
+      if (nb >= 3) {
+        lut_byte<GC>(Tq, 4 * blk, wb[2], al[2], mse);
+        lut_byte<GC>(Tq, 4 * blk, wb[0] ^ wb[1] ^ wb[2], al[3], mse);
       }
+      lut_nib<GC>(Ts, 8 * blk, wb[nb], qjl);
     }
     const float n16 = f16_bits_to_f32(kn), r16 = f16_bits_to_f32(kn >> 16);
-    float lg[GC];
+    float est[GC], lg[GC];
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
-      const float est = n16 * (mse[h] - cq[h]) + p.gamma * r16 * (qjl[h] - ws[h]);
-      lg[h] = valid ? est * kscale : -INFINITY;  // log2 domain
-      if (p.logits && valid)
-        p.logits[((int64_t)b * p.hq + h0 + h) * p.capacity + t] = est * p.scale;
+      est[h] = n16 * (mse[h] - cq[h]) + p.gamma * r16 * (qjl[h] - wsum[h]);
+      lg[h] = valid ? est[h] * kscale : -INFINITY;  // log2 domain
+    }
+    if (p.logits && valid) {
+#pragma unroll
+      for (int h = 0; h < GC; ++h)
+        p.logits[((int64_t)b * p.hq + h0 + h) * p.capacity + t] = est[h] * p.scale;
     }
     // ---------------- online softmax (per head, wavefront reductions)
     const float vn16 = f16_bits_to_f32(vn), vr16 = f16_bits_to_f32(vn >> 16);
     bool any_keep = false;
-    float* wrow = wts + lane * 2 * GC;
+    float u[GC], u2[GC];
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
       const float mt = wave_max_fast(lg[h]);
@@ -424,65 +468,67 @@ __global__ __launch_bounds__(64 * kScanWaves) void decode_scan(DecodeParams p) {
       float wgt = valid ? exp2f(lg[h] - mn) : 0.0f;
       l_run[h] = l_run[h] * corr + wave_sum_fast(wgt);
       m_run[h] = mn;
-      if (p.tau > 0.0f && wgt < p.tau * l_run[h]) wgt = 0.0f;
+      wgt = (gated && wgt < p.tau * l_run[h]) ? 0.0f : wgt;
       any_keep |= wgt > 0.0f;
-      am[h][0] *= corr;
-      am[h][1] *= corr;
-      aq[h][0] *= corr;
-      aq[h][1] *= corr;
-      wrow[h] = wgt * vn16;
-      wrow[GC + h] = wgt * p.gamma * vr16;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        am[h][k] *= corr;
+        aq[h][k] *= corr;
+      }
+      u[h] = wgt * vn16;
+      u2[h] = wgt * p.gamma * vr16;
     }
-    uint64_t keep = __ballot(any_keep);
+    const uint64_t keep = __ballot(any_keep);
     n_skipped += (unsigned long long)__popcll(__ballot(valid) & ~keep);
-    // value rows of kept tokens to LDS
-    if (any_keep) {
-      if (gated) load_record<VW, VR::VEC>(p.codes_v + (kv_base + t) * VW, vrec);
-#pragma unroll
-      for (int i = 0; i < VW; ++i) vst[lane * VW + i] = vrec[i];
-    }
-    // ---------------- values: lane = coordinate pair, loop over kept tokens, 4 at a time
-    // (missing slots point at the all-zero row kTile)
-    while (keep) {
-      int tl[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        tl[u] = keep ? __builtin_ctzll(keep) : kTile;
-        keep &= keep - 1;
-      }
-      float c0[4], c1[4], s0[4], s1[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t* vw = vst + tl[u] * VW + voff;
-        const uint32_t w0 = vw[0], w1 = vw[1], w2 = vw[2], w3 = vw[3];
-        const uint32_t p2 = (vnb == 3) ? w2 : 0u;
-        const uint32_t sg = (vnb == 3) ? w3 : ((vnb == 2) ? w2 : w1);
-        const uint32_t p1 = (vnb >= 2) ? w1 : 0u;
-        const uint32_t f = ((w0 >> vbit) & 3u) | (((p1 >> vbit) & 3u) << 2) | (((p2 >> vbit) & 3u) << 4);
-        const f32x2 cc = *reinterpret_cast<const f32x2*>(cpair + 2 * f);
-        const f32x2 ss = spair[(sg >> vbit) & 3u];
-        c0[u] = cc[0]; c1[u] = cc[1]; s0[u] = ss[0]; s1[u] = ss[1];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float* wr = wts + tl[u] * 2 * GC;
-        float uu[GC], uq[GC];
-        table_read<GC>(wr, 0, uu);
-        table_read<GC>(wr + GC, 0, uq);
+    // this token's row: weights, then the value record (read only when kept if gated)
+    {
+      float* row = area + lane * kRS;
+      if constexpr (GC == 4) {
+        *reinterpret_cast<f32x4*>(row) = f32x4{u[0], u[1], u[2], u[3]};
+        *reinterpret_cast<f32x4*>(row + 4) = f32x4{u2[0], u2[1], u2[2], u2[3]};
+      } else {
 #pragma unroll
         for (int h = 0; h < GC; ++h) {
-          am[h][0] = fmaf(uu[h], c0[u], am[h][0]);
-          am[h][1] = fmaf(uu[h], c1[u], am[h][1]);
-          aq[h][0] = fmaf(uq[h], s0[u], aq[h][0]);
-          aq[h][1] = fmaf(uq[h], s1[u], aq[h][1]);
+          row[h] = u[h];
+          row[GC + h] = u2[h];
         }
+      }
+      if (any_keep) {
+        if (gated) load_record<VW, VR::VEC>(p.codes_v + (kv_base + t) * VW, vrec);
+        uint32_t* rv = reinterpret_cast<uint32_t*>(row + kW0);
+#pragma unroll
+        for (int i = 0; i < VW; ++i) rv[i] = vrec[i];
+      }
+    }
+    // ---------------- values: half-wave hw takes every other kept token
+    if (keep == ~0ull) {
+      const float* r = area + hw * kRS;
+#pragma unroll 4
+      for (int s = 0; s < kTile / 2; ++s) value_row(r + 2 * s * kRS);
+    } else {
+      uint64_t kk = keep;
+      while (kk) {
+        const int ta = __builtin_ctzll(kk);
+        kk &= kk - 1;
+        int tb = kTile;
+        if (kk) {
+          tb = __builtin_ctzll(kk);
+          kk &= kk - 1;
+        }
+        value_row(area + (hw ? tb : ta) * kRS);
       }
     }
   }
-  // ---------------- merge the waves' partials in LDS, one partial per workgroup
+  // ---------------- merge: half-waves, then the waves' partials in LDS (aliases Tq)
+#pragma unroll
+  for (int h = 0; h < GC; ++h)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      am[h][k] += __shfl_xor(am[h][k], 32, 64);
+      aq[h][k] += __shfl_xor(aq[h][k], 32, 64);
+    }
   __syncthreads();
-  float* mine = lds + L::kTable + wave * L::kArea;  // [2*GC] m, l then [GC][2][kD]
-  const int j0 = 32 * vblk + vbit;
+  float* mine = lds + wave * L::kMerge;  // [2*GC] m, l | [GC][2][kD]
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
@@ -490,29 +536,28 @@ __global__ __launch_bounds__(64 * kScanWaves) void decode_scan(DecodeParams p) {
       mine[GC + h] = l_run[h];
     }
   }
+  if (lane < 32) {
 #pragma unroll
-  for (int h = 0; h < GC; ++h) {
-    float* a = mine + 2 * GC + h * 2 * kD;
-    a[j0] = am[h][0];
-    a[j0 + 1] = am[h][1];
-    a[kD + j0] = aq[h][0];
-    a[kD + j0 + 1] = aq[h][1];
+    for (int h = 0; h < GC; ++h) {
+      float* a = mine + round4(2 * GC) + h * 2 * kD + 4 * c4;
+      *reinterpret_cast<f32x4*>(a) = f32x4{am[h][0], am[h][1], am[h][2], am[h][3]};
+      *reinterpret_cast<f32x4*>(a + kD) = f32x4{aq[h][0], aq[h][1], aq[h][2], aq[h][3]};
+    }
   }
   __syncthreads();
-  // thread t: head h = t / 64 (when GC >= ...), coordinates handled in a loop
-  for (int i = threadIdx.x; i < GC * 2 * kD; i += blockDim.x) {
+  for (int i = tid; i < GC * 2 * kD; i += kThreads) {
     const int h = i / (2 * kD), k = i % (2 * kD);
     float M = -INFINITY;
 #pragma unroll
-    for (int w2 = 0; w2 < kScanWaves; ++w2) M = fmaxf(M, lds[L::kTable + w2 * L::kArea + h]);
+    for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, lds[w2 * L::kMerge + h]);
     float acc = 0.0f, lsum = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w2 = 0; w2 < kScanWaves; ++w2) {
-        const float* o = lds + L::kTable + w2 * L::kArea;
+      for (int w2 = 0; w2 < kWaves; ++w2) {
+        const float* o = lds + w2 * L::kMerge;
         if (o[h] == -INFINITY) continue;
         const float sc = exp2f(o[h] - M);
-        acc = fmaf(o[2 * GC + h * 2 * kD + k], sc, acc);
+        acc = fmaf(o[round4(2 * GC) + h * 2 * kD + k], sc, acc);
         lsum = fmaf(o[GC + h], sc, lsum);
       }
     }
@@ -530,60 +575,73 @@ __global__ __launch_bounds__(64 * kScanWaves) void decode_scan(DecodeParams p) {
 }
 
 // ----------------------------------------------------------------------------- combine
+// One workgroup per (batch, query head): every load it needs (S_v column slices, the
+// split maxima, the first 32 splits' partial sums) is issued before the first use.
+constexpr int kCombChunk = 32;
+
 __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   const int bh = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   __shared__ float scl[1024];
-  __shared__ float red[256];
+  __shared__ float red[8];
   __shared__ float vec[2][kD];
-  __shared__ float Lsh;
+  __shared__ float part_s[256];
   const float* parts = p.ws_part + (int64_t)bh * p.n_split * kPartFloats;
   const int np = p.n_split;
-  // global max over splits
+  const int j = tid & 127, half = tid >> 7;
+  float sv[64];  // S_v[64 half + i][j]
+#pragma unroll
+  for (int i = 0; i < 64; ++i) sv[i] = p.S_v[(int64_t)(64 * half + i) * kD + j];
+  float pv[kCombChunk];
+#pragma unroll
+  for (int c = 0; c < kCombChunk; ++c)
+    pv[c] = c < np ? parts[(int64_t)c * kPartFloats + 2 + tid] : 0.0f;
   float M = -INFINITY;
   for (int i = tid; i < np; i += 256) M = fmaxf(M, parts[(int64_t)i * kPartFloats]);
-  red[tid] = M;
+  M = wave_max_fast(M);
+  if (lane == 0) red[wave] = M;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float lpart = 0.0f;
   for (int i = tid; i < np; i += 256) {
     const float m = parts[(int64_t)i * kPartFloats];
-    scl[i] = (m == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(m - M);
+    const float s = (m == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(m - M);
+    scl[i] = s;
+    lpart += s * parts[(int64_t)i * kPartFloats + 1];
   }
+  lpart = wave_sum_fast(lpart);
   __syncthreads();
-  // thread t: component t / 128 (A or Q), coordinate t % 128; fixed order over splits
-  {
-    const int k = tid;  // 0 .. 255 = [A | Q]
-    float acc = 0.0f;
-    for (int i = 0; i < np; ++i) acc = fmaf(parts[(int64_t)i * kPartFloats + 2 + k], scl[i], acc);
-    vec[k >> 7][k & 127] = acc;
-    if (tid == 0) {
-      float L = 0.0f;
-      for (int i = 0; i < np; ++i) L = fmaf(parts[(int64_t)i * kPartFloats + 1], scl[i], L);
-      Lsh = L;
-    }
+  if (lane == 0) red[4 + wave] = lpart;
+  // thread tid: component tid / 128 (A or Q), coordinate tid % 128; fixed order over splits
+  float acc = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kCombChunk; ++c)
+    if (c < np) acc = fmaf(pv[c], scl[c], acc);
+  for (int c0 = kCombChunk; c0 < np; c0 += kCombChunk) {
+#pragma unroll
+    for (int c = 0; c < kCombChunk; ++c)
+      pv[c] = c0 + c < np ? parts[(int64_t)(c0 + c) * kPartFloats + 2 + tid] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < kCombChunk; ++c)
+      if (c0 + c < np) acc = fmaf(pv[c], scl[c0 + c], acc);
   }
+  vec[half][j] = acc;
   __syncthreads();
-  // S^T Q: thread (j, half) sums half of the 128 rows
+  const float Ltot = (red[4] + red[5]) + (red[6] + red[7]);
+  // S^T Q: thread (j, half) sums its 64 rows
   {
-    const int j = tid & 127, half = tid >> 7;
     float s = 0.0f;
-#pragma unroll 8
-    for (int i = 64 * half; i < 64 * half + 64; ++i) s = fmaf(p.S_v[(int64_t)i * kD + j], vec[1][i], s);
-    red[tid] = s;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) s = fmaf(sv[i], vec[1][64 * half + i], s);
+    part_s[tid] = s;
   }
   __syncthreads();
   if (tid < 64) {
-    const int lane = tid;
     float v[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int j = lane + 64 * e;
-      v[e] = vec[0][j] + red[j] + red[128 + j];
+      const int jj = lane + 64 * e;
+      v[e] = vec[0][jj] + part_s[jj] + part_s[128 + jj];
     }
     {
       const float x = v[0], y = v[1];
@@ -597,21 +655,20 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
         const float t = __shfl_xor(v[e], m, 64);
         v[e] = (lane & m) ? t - v[e] : v[e] + t;
       }
-    const float L = Lsh;
-    const float inv = (L > 0.0f) ? 1.0f / (L * sqrtf((float)kD)) : 0.0f;
+    const float inv = (Ltot > 0.0f) ? 1.0f / (Ltot * sqrtf((float)kD)) : 0.0f;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int j = lane + 64 * e;
+      const int jj = lane + 64 * e;
       float o = v[e] * inv;
-      if ((p.sign_v[j >> 5] >> (j & 31)) & 1u) o = -o;
-      p.out[(int64_t)bh * kD + j] = o;
+      if ((p.sign_v[jj >> 5] >> (jj & 31)) & 1u) o = -o;
+      p.out[(int64_t)bh * kD + jj] = o;
     }
   }
 }
 
 template <int BKLO, int BKHI, int KS, int BVLO, int BVHI, int VS, int GC>
 static int launch_scan(const DecodeParams& p, dim3 grid, hipStream_t stream) {
-  const size_t lds = sizeof(float) * (size_t)ScanLds<GC, Rec<BVLO, BVHI, VS>::W>::kTotal;
+  const size_t lds = sizeof(float) * (size_t)ScanLds<GC, Rec<BVLO, BVHI, VS>::W, BVLO, BVHI, VS>::kTotal;
   static bool attr = false;
   if (!attr) {
     if (hipFuncSetAttribute((const void*)decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, GC>,
@@ -619,8 +676,8 @@ static int launch_scan(const DecodeParams& p, dim3 grid, hipStream_t stream) {
       return TQ_ERR_HIP;
     attr = true;
   }
-  hipLaunchKernelGGL((decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, GC>), grid, dim3(64 * kScanWaves),
-                     lds, stream, p);
+  hipLaunchKernelGGL((decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, GC>), grid, dim3(kThreads), lds,
+                     stream, p);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
@@ -644,7 +701,7 @@ static int dispatch_scan(const tq_format* fk, const tq_format* fv, const DecodeP
 }
 
 // Walsh coefficients alpha_S = 2^-B sum_idx c[idx] prod_{k in S} (2 b_k(idx) - 1) for the odd
-// subsets S in the order used by key_block: {0}, {1}, {2}, {0,1,2}.
+// subsets S in the order the scan reads the planes: {0}, {1}, {2}, {0,1,2}.
 static void walsh(int bits, const float* c, float* alpha) {
   const int L = 1 << bits;
   const int subsets[4] = {1, 2, 4, 7};
@@ -675,12 +732,13 @@ bool tq_decode_formats_supported(const tq_format* fk, const tq_format* fv) {
 
 tq_decode_plan tq_plan_decode(int32_t batch, int32_t hq, int32_t hkv, int64_t capacity, int32_t d) {
   using namespace tqk;
+  (void)d;
   tq_decode_plan p{};
   const int group = hq / hkv;
   const int gc = group >= 4 ? 4 : group;
   const int64_t units = (int64_t)batch * hkv * (group / gc);
   // about one workgroup per compute unit of a 256-CU MI355X, at least one tile per wave
-  const int64_t per_wg = (int64_t)kTile * kScanWaves;
+  const int64_t per_wg = (int64_t)kTile * kWaves;
   int64_t max_split = (capacity + per_wg - 1) / per_wg;
   if (max_split < 1) max_split = 1;
   int64_t n_split = (256 + units - 1) / units;
@@ -691,15 +749,11 @@ tq_decode_plan tq_plan_decode(int32_t batch, int32_t hq, int32_t hkv, int64_t ca
   tps = ((tps + kTile - 1) / kTile) * kTile;
   if (tps < kTile) tps = kTile;
   p.n_split = (int32_t)n_split;
-  p.waves = kScanWaves;
+  p.waves = kWaves;
   p.parts = (int32_t)n_split;
   p.tokens_per_split = tps;
-  p.ws_qrot_off = 0;
-  const int64_t qrot_bytes = (int64_t)batch * hq * 2 * d * 4;
-  p.ws_nib_off = (qrot_bytes + 255) / 256 * 256;
-  const int64_t nib_bytes = units * nib_stride(gc) * 4;
-  p.ws_part_off = p.ws_nib_off + (nib_bytes + 255) / 256 * 256;
-  p.ws_bytes = p.ws_part_off + (int64_t)batch * hq * p.parts * kPartFloats * 4;
+  p.ws_part_off = 0;
+  p.ws_bytes = (int64_t)batch * hq * p.parts * kPartFloats * 4;
   return p;
 }
 
@@ -723,17 +777,13 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
   p.out = out;
   p.logits = logits;
   p.skipped = reinterpret_cast<unsigned long long*>(skipped);
-  char* ws = reinterpret_cast<char*>(workspace);
-  p.ws_qrot = reinterpret_cast<float*>(ws + plan.ws_qrot_off);
-  p.ws_nib = reinterpret_cast<float*>(ws + plan.ws_nib_off);
-  p.ws_part = reinterpret_cast<float*>(ws + plan.ws_part_off);
+  p.ws_part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.ws_part_off);
   p.capacity = capacity;
   p.tokens_per_split = plan.tokens_per_split;
   p.batch = batch;
   p.hq = hq;
   p.hkv = hkv;
   p.group = hq / hkv;
-  p.gc = p.group >= 4 ? 4 : p.group;
   p.q_dtype = q_dtype;
   p.n_split = plan.n_split;
   p.ksplitb = fk->split / 32;
@@ -751,13 +801,9 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
     p.cent_v[0][i] = i < (1 << fv->bits_lo) ? tv->centroids_lo[i] : 0.0f;
     p.cent_v[1][i] = i < (1 << fv->bits_hi) ? tv->centroids_hi[i] : 0.0f;
   }
-  const int gc = p.gc;
+  const int gc = p.group >= 4 ? 4 : p.group;
   const int nchunk = p.group / gc;
   const unsigned units = (unsigned)(batch * hkv * nchunk);
-  if (gc == 4) hipLaunchKernelGGL(decode_prologue<4>, dim3(batch * hq), dim3(128), 0, stream, p);
-  else if (gc == 2) hipLaunchKernelGGL(decode_prologue<2>, dim3(batch * hq), dim3(128), 0, stream, p);
-  else hipLaunchKernelGGL(decode_prologue<1>, dim3(batch * hq), dim3(128), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   const dim3 grid((unsigned)plan.n_split, units);
   int rc;
   if (gc == 4) rc = dispatch_scan<4>(fk, fv, p, grid, stream);

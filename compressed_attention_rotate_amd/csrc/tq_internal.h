@@ -15,11 +15,9 @@ int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, in
 struct tq_decode_plan {
   int32_t n_split;        // token splits per (batch, kv head)
   int32_t waves;          // waves per scan workgroup
-  int32_t parts;          // partial results per (batch, q head) = n_split * waves
+  int32_t parts;          // partial results per (batch, q head) = n_split
   int64_t tokens_per_split;
-  int64_t ws_qrot_off;    // byte offsets inside the workspace
-  int64_t ws_nib_off;
-  int64_t ws_part_off;
+  int64_t ws_part_off;    // byte offset of the split partials inside the workspace
   int64_t ws_bytes;
 };
 
