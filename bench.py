@@ -137,7 +137,7 @@ def main():
     norms_v = [torch.empty_like(n) for n in norms_k]
     q = torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16)
     seq = torch.full((BATCH,), NTOK, dtype=torch.int32, device=dev)
-    ws = torch.empty(tq.attend_workspace_bytes(BATCH, HQ, HKV, NTOK, D), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(tq.attend_workspace_bytes(BATCH, HQ, HKV, NTOK, D), dtype=torch.uint8, device=dev)
     out = torch.empty((BATCH, HQ, D), dtype=torch.float32, device=dev)
 
     def quantize(s):

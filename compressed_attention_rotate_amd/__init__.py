@@ -113,7 +113,7 @@ def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
     lg = torch.empty((batch, hq, capacity), dtype=torch.float32, device=q.device) if logits else None
     wsb = attend_workspace_bytes(batch, hq, hkv, capacity, d)
-    if workspace is None or workspace.numel() < wsb:
+    if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
     fk, fv, tk, tv = fmt_k.c(), fmt_v.c(), tables_k.c(), tables_v.c()
     rc = load().tq_attend_decode(ctypes.byref(fk), ctypes.byref(tk), ctypes.byref(fv),

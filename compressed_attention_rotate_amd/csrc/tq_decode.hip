@@ -10,7 +10,7 @@
 // Two launches:
 //   scan:     grid (split, batch * KV head * chunk of GC query heads), about one
 //             workgroup of 8 waves per CU.  The workgroup first derives its own query
-//             tables (while its first cache tile is already in flight): q_rot of the GC
+//             tables (while its first cache tile is in flight): q_rot of the GC
 //             heads (FWHT over the wave), S q_rot (S rows from L2), and in LDS
 //               Tq[g][m] = sum of q_rot over the set bits of byte m of coordinate group g
 //               Ts[g][n] = 2 * sum of S q_rot over the set bits of nibble n,
@@ -128,12 +128,15 @@ struct ScanLds {
   static constexpr int kW0 = 2 * GC <= 4 ? 4 : 8;        // row: u[GC], u'[GC] | value record
   static constexpr int kRS = round4(kW0 + VW);           // row stride (words)
   static constexpr int kArea = (kTile + 1) * kRS + 4;    // 64 token rows + zero row + pad
-  static constexpr int oTq = 0, oTs = kTq, oCpLo = oTs + kTs, oCpHi = oCpLo + kCpLo;
-  static constexpr int oSp = oCpHi + kCpHi, oArea = oSp + kSp;
+  // small tables first so their reads use the instruction's immediate offset
+  static constexpr int oCpLo = 0, oCpHi = oCpLo + kCpLo, oSp = oCpHi + kCpHi, oTs = oSp + kSp;
+  static constexpr int oCc = oTs + kTs;                   // [2][GC] per-head constants
+  static constexpr int oTq = oCc + round4(2 * GC), oArea = oTq + kTq;
   static constexpr int kTotal = oArea + kWaves * kArea;
-  static constexpr int kMerge = round4(2 * GC) + 2 * kD * GC;  // per wave, aliases Tq
+  static constexpr int kMerge = round4(2 * GC) + 2 * kD * GC;  // per wave
+  static constexpr int oWM = oTq;  // the waves' partials after the scan (aliases Tq)
   static_assert(kWaves * kMerge <= kTq, "merge area must fit in the byte tables");
-  static_assert(2 * GC * kD + 16 * 2 * 16 * GC <= kWaves * kArea, "setup scratch must fit");
+  static_assert(2 * GC * kD + 16 * 2 * 16 * GC + 16 <= kWaves * kArea, "setup scratch must fit");
 };
 
 template <int GC>
@@ -146,6 +149,39 @@ __device__ __forceinline__ void table_read(const float* T, int idx, float (&out)
     out[0] = v[0]; out[1] = v[1];
   } else {
     out[0] = T[idx];
+  }
+}
+
+// Value of lane (lane ^ 32): v_permlane32_swap exchanges the two half-waves.
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((lane_id() & 32) ? r[0] : r[1]);
+}
+
+template <int M>
+__device__ __forceinline__ float hbfly(float x, int lane) {  // lower lane a + b, upper a - b
+  const float t = (M == 32) ? other_half(x) : xchg<(M < 32 ? M : 1)>(x);
+  return (lane & M) ? t - x : x + t;
+}
+
+// Unnormalized natural-order Walsh-Hadamard transform of 128 values held by one wave as
+// v[0] = x[lane], v[1] = x[lane + 64].
+__device__ __forceinline__ void fwht128(float (&v)[2], int lane) {
+  {
+    const float a = v[0], c = v[1];
+    v[0] = a + c;
+    v[1] = a - c;
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    float x = v[e];
+    x = hbfly<1>(x, lane);
+    x = hbfly<2>(x, lane);
+    x = hbfly<4>(x, lane);
+    x = hbfly<8>(x, lane);
+    x = hbfly<16>(x, lane);
+    x = hbfly<32>(x, lane);
+    v[e] = x;
   }
 }
 
@@ -182,13 +218,13 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   constexpr int KW = KR::W, VW = VR::W;
   using L = ScanLds<GC, VW, BVLO, BVHI, VSPLIT>;
   constexpr int kW0 = L::kW0, kRS = L::kRS;
-  extern __shared__ __attribute__((aligned(16))) float lds[];
+  __shared__ __attribute__((aligned(16))) float lds[L::kTotal];
   float* Tq = lds + L::oTq;
   float* Ts = lds + L::oTs;
   float* cpLo = lds + L::oCpLo;
   float* cpHi = lds + L::oCpHi;
   float* spat = lds + L::oSp;
-  __shared__ float cconst[2][GC];
+  float* cconst = lds + L::oCc;  // [2][GC]: codebook-term and QJL-term constants per head
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -206,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   const int64_t kv_base = (int64_t)bk * p.capacity;
   const bool gated = p.tau > 0.0f;
 
-  // ---- register prefetch of the wave's first tile: key record, value record, norms
+  // ---- register prefetch of one tile: key record, value record, norms
   uint32_t kw[KW], vwr[VW], knr = 0, vnr = 0;
   auto fetch = [&](int64_t tt0) {
     const int64_t t = tt0 + lane;
@@ -218,17 +254,25 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     }
   };
   int64_t t0 = t_begin + (int64_t)wave * kTile;
-  fetch(t0);
 
   // ---- query tables
   float* qs = lds + L::oArea;             // [2][GC][kD]: q_rot, S q_rot (setup scratch)
   float* nibq = qs + 2 * GC * kD;         // [16 groups][2 halves][16][GC]
   const int srow = tid >> 2, sq4 = tid & 3;
-  f32x4 sr[8];  // S[srow][32 sq4 .. 32 sq4 + 31]
+  f32x4 sr[8];  // S_k[srow][32 sq4 .. 32 sq4 + 31]
   {
     const f32x4* src = reinterpret_cast<const f32x4*>(p.S_k + (int64_t)srow * kD + 32 * sq4);
 #pragma unroll
     for (int c = 0; c < 8; ++c) sr[c] = src[c];
+  }
+
+  float* cents = qs + 2 * GC * kD + 16 * 2 * 16 * GC;  // [2][8] value codebooks
+  if (tid == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      cents[k] = p.cent_v[0][k];
+      cents[8 + k] = p.cent_v[1][k];
+    }
   }
   if (wave < GC) {  // q_rot of head h0 + wave
     float v[2];
@@ -236,25 +280,18 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     for (int e = 0; e < 2; ++e) {
       const int j = lane + 64 * e;
       float x = load_elem(p.q, ((int64_t)b * p.hq + h0 + wave) * kD + j, p.q_dtype);
-      if ((p.sign_k[j >> 5] >> (j & 31)) & 1u) x = -x;
+      const uint32_t sw = (lane & 32) ? uniform_u32(p.sign_k[2 * e + 1]) : uniform_u32(p.sign_k[2 * e]);
+      if ((sw >> (j & 31)) & 1u) x = -x;
       v[e] = x;
     }
-    {
-      const float a = v[0], c = v[1];
-      v[0] = a + c;
-      v[1] = a - c;
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float t = __shfl_xor(v[e], m, 64);
-        v[e] = (lane & m) ? t - v[e] : v[e] + t;
-      }
+    fwht128(v, lane);
     const float isd = 1.0f / sqrtf((float)kD);
     qs[wave * kD + lane] = v[0] * isd;
     qs[wave * kD + lane + 64] = v[1] * isd;
   }
+  // the first tile is requested only now: waits on the S and q loads above must not also
+  // wait for it (vector-memory counters complete in issue order)
+  fetch(t0);
   __syncthreads();
   {  // S q_rot: thread (row srow, quarter sq4) sums 32 columns, then the 4 quarter lanes
     float acc[GC];
@@ -293,29 +330,39 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     const float cq = wave_sum_fast(v);
     const float ws = wave_sum_fast(qs[(GC + h) * kD + lane] + qs[(GC + h) * kD + lane + 64]);
     if (lane == 0) {
-      cconst[0][h] = cq;
-      cconst[1][h] = ws;
+      cconst[h] = cq;
+      cconst[GC + h] = ws;
     }
   }
-  for (int i = tid; i < 16 * 2 * 16 * GC; i += kThreads) {  // nibble sums of q_rot
+  static_assert((16 * 2 * 16 * GC) % kThreads == 0 && (16 * 256) % kThreads == 0, "setup split");
+  float nibsum_q[16 * 2 * 16 * GC / kThreads], nibsum_s[32 * 16 * GC / kThreads];
+#pragma unroll
+  for (int r = 0; r < 16 * 2 * 16 * GC / kThreads; ++r) {  // nibble sums of q_rot
+    // (all reads of an entry before its write: the write may alias later reads for the
+    // compiler, which would otherwise serialize every round trip)
+    const int i = tid + r * kThreads;
     const int h = i % GC, n = (i / GC) % 16, half = (i / (16 * GC)) % 2, g = i / (32 * GC);
-    const float* src = qs + h * kD + 8 * g + 4 * half;
-    float s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if ((n >> k) & 1) s += src[k];
-    nibq[i] = s;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(qs + h * kD + 8 * g + 4 * half);
+    nibsum_q[r] = ((n & 1) ? x[0] : 0.0f) + ((n & 2) ? x[1] : 0.0f) + ((n & 4) ? x[2] : 0.0f) +
+                  ((n & 8) ? x[3] : 0.0f);
   }
-  for (int i = tid; i < 32 * 16 * GC; i += kThreads) {  // Ts: 2 * nibble sums of S q_rot
+#pragma unroll
+  for (int r = 0; r < 32 * 16 * GC / kThreads; ++r) {  // Ts: 2 * nibble sums of S q_rot
+    const int i = tid + r * kThreads;
     const int h = i % GC, n = (i / GC) % 16, g = i / (16 * GC);
-    const float* src = qs + (GC + h) * kD + 4 * g;
-    float s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if ((n >> k) & 1) s += src[k];
-    Ts[i] = 2.0f * s;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(qs + (GC + h) * kD + 4 * g);
+    nibsum_s[r] = 2.0f * (((n & 1) ? x[0] : 0.0f) + ((n & 2) ? x[1] : 0.0f) +
+                          ((n & 4) ? x[2] : 0.0f) + ((n & 8) ? x[3] : 0.0f));
   }
-  for (int i = tid; i < pat_entries(BVLO) + (VSPLIT < kNB ? pat_entries(BVHI) : 0); i += kThreads) {
+#pragma unroll
+  for (int r = 0; r < 16 * 2 * 16 * GC / kThreads; ++r) nibq[tid + r * kThreads] = nibsum_q[r];
+#pragma unroll
+  for (int r = 0; r < 32 * 16 * GC / kThreads; ++r) Ts[tid + r * kThreads] = nibsum_s[r];
+  constexpr int kPat = pat_entries(BVLO) + (VSPLIT < kNB ? pat_entries(BVHI) : 0);
+#pragma unroll
+  for (int r = 0; r < (kPat + kThreads - 1) / kThreads; ++r) {
+    const int i = tid + r * kThreads;
+    if (i >= kPat) break;
     const bool hi = i >= pat_entries(BVLO);
     const int P = hi ? i - pat_entries(BVLO) : i;
     const int nb = hi ? BVHI : BVLO;
@@ -324,22 +371,30 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     const int ilo = ((p0 & 1) | ((p1 & 1) << 1) | ((p2 & 1) << 2)) & mask;
     const int ihi = (((p0 >> 1) & 1) | (((p1 >> 1) & 1) << 1) | (((p2 >> 1) & 1) << 2)) & mask;
     float* dst = hi ? cpHi : cpLo;
-    dst[2 * P] = p.cent_v[hi ? 1 : 0][ilo];
-    dst[2 * P + 1] = p.cent_v[hi ? 1 : 0][ihi];
+    dst[2 * P] = cents[(hi ? 8 : 0) + ilo];
+    dst[2 * P + 1] = cents[(hi ? 8 : 0) + ihi];
   }
   if (tid < 64) spat[tid] = ((tid >> 2) >> (tid & 3)) & 1 ? 1.0f : -1.0f;
   __syncthreads();
-  for (int i = tid; i < 16 * 256; i += kThreads) {  // byte tables from nibble sums
+  float tq_v[16 * 256 / kThreads][GC];
+#pragma unroll
+  for (int r = 0; r < 16 * 256 / kThreads; ++r) {  // byte tables from nibble sums
+    const int i = tid + r * kThreads;
     const int g = i >> 8, m = i & 255;
     float lo[GC], hi[GC];
     table_read<GC>(nibq + ((g * 2 + 0) * 16) * GC, m & 15, lo);
     table_read<GC>(nibq + ((g * 2 + 1) * 16) * GC, m >> 4, hi);
+#pragma unroll
+    for (int h = 0; h < GC; ++h) tq_v[r][h] = lo[h] + hi[h];
+  }
+#pragma unroll
+  for (int r = 0; r < 16 * 256 / kThreads; ++r) {
+    const int i = tid + r * kThreads;
     if constexpr (GC == 4) {
-      const f32x4 o = {lo[0] + hi[0], lo[1] + hi[1], lo[2] + hi[2], lo[3] + hi[3]};
-      *reinterpret_cast<f32x4*>(Tq + i * 4) = o;
+      *reinterpret_cast<f32x4*>(Tq + i * 4) = f32x4{tq_v[r][0], tq_v[r][1], tq_v[r][2], tq_v[r][3]};
     } else {
 #pragma unroll
-      for (int h = 0; h < GC; ++h) Tq[i * GC + h] = lo[h] + hi[h];
+      for (int h = 0; h < GC; ++h) Tq[i * GC + h] = tq_v[r][h];
     }
   }
   __syncthreads();
@@ -347,8 +402,8 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   float cq[GC], wsum[GC];
 #pragma unroll
   for (int h = 0; h < GC; ++h) {
-    cq[h] = cconst[0][h];
-    wsum[h] = cconst[1][h];
+    cq[h] = cconst[h];
+    wsum[h] = cconst[GC + h];
   }
   float alo[4], ahi[4];
 #pragma unroll
@@ -357,8 +412,12 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     ahi[k] = 2.0f * p.alpha_k[1][k];
   }
 
-  // ---- per-wave area: 64 token rows + one all-zero row used to pad odd token counts
-  float* area = lds + L::oArea + wave * L::kArea;
+  // ---- per-wave area: 64 token rows + one all-zero row used to pad odd token counts.
+  // Row bases are kept opaque to the compiler so that row and field offsets fold into the
+  // LDS instructions' 16-bit immediate instead of being re-added per access.
+  int area_off = L::oArea + wave * L::kArea;
+  asm volatile("" : "+v"(area_off));
+  float* area = lds + area_off;
   for (int i = lane; i < kRS + 4; i += 64) area[kTile * kRS + i] = 0.0f;
   // value lane mapping: half-wave hw takes alternate tokens; lane owns coordinates
   // 4 c4 .. 4 c4 + 3 of block vblk, bits vbit .. vbit + 3 of its plane words
@@ -482,7 +541,9 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     n_skipped += (unsigned long long)__popcll(__ballot(valid) & ~keep);
     // this token's row: weights, then the value record (read only when kept if gated)
     {
-      float* row = area + lane * kRS;
+      int own = area_off + lane * kRS;
+      asm volatile("" : "+v"(own));
+      float* row = lds + own;
       if constexpr (GC == 4) {
         *reinterpret_cast<f32x4*>(row) = f32x4{u[0], u[1], u[2], u[3]};
         *reinterpret_cast<f32x4*>(row + 4) = f32x4{u2[0], u2[1], u2[2], u2[3]};
@@ -502,7 +563,9 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     }
     // ---------------- values: half-wave hw takes every other kept token
     if (keep == ~0ull) {
-      const float* r = area + hw * kRS;
+      int roff = area_off + hw * kRS;
+      asm volatile("" : "+v"(roff));
+      const float* r = lds + roff;
 #pragma unroll 4
       for (int s = 0; s < kTile / 2; ++s) value_row(r + 2 * s * kRS);
     } else {
@@ -519,16 +582,17 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
       }
     }
   }
-  // ---------------- merge: half-waves, then the waves' partials in LDS (aliases Tq)
+  // ---------------- workgroup epilogue: the half-waves, then the waves' partials are
+  // merged in LDS (aliases Tq) and stored at device scope
 #pragma unroll
   for (int h = 0; h < GC; ++h)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      am[h][k] += __shfl_xor(am[h][k], 32, 64);
-      aq[h][k] += __shfl_xor(aq[h][k], 32, 64);
+      am[h][k] += other_half(am[h][k]);
+      aq[h][k] += other_half(aq[h][k]);
     }
   __syncthreads();
-  float* mine = lds + wave * L::kMerge;  // [2*GC] m, l | [GC][2][kD]
+  float* mine = lds + L::oWM + wave * L::kMerge;  // [2*GC] m, l | [GC][2][kD]
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
@@ -545,16 +609,19 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < GC * 2 * kD; i += kThreads) {
+#pragma unroll
+  for (int r = 0; r < (GC * 2 * kD + kThreads - 1) / kThreads; ++r) {
+    const int i = tid + r * kThreads;
+    if (i >= GC * 2 * kD) break;
     const int h = i / (2 * kD), k = i % (2 * kD);
     float M = -INFINITY;
 #pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, lds[w2 * L::kMerge + h]);
+    for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, lds[L::oWM + w2 * L::kMerge + h]);
     float acc = 0.0f, lsum = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w2 = 0; w2 < kWaves; ++w2) {
-        const float* o = lds + w2 * L::kMerge;
+        const float* o = lds + L::oWM + w2 * L::kMerge;
         if (o[h] == -INFINITY) continue;
         const float sc = exp2f(o[h] - M);
         acc = fmaf(o[round4(2 * GC) + h * 2 * kD + k], sc, acc);
@@ -643,24 +710,14 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
       const int jj = lane + 64 * e;
       v[e] = vec[0][jj] + part_s[jj] + part_s[128 + jj];
     }
-    {
-      const float x = v[0], y = v[1];
-      v[0] = x + y;
-      v[1] = x - y;
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float t = __shfl_xor(v[e], m, 64);
-        v[e] = (lane & m) ? t - v[e] : v[e] + t;
-      }
+    fwht128(v, lane);
     const float inv = (Ltot > 0.0f) ? 1.0f / (Ltot * sqrtf((float)kD)) : 0.0f;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int jj = lane + 64 * e;
       float o = v[e] * inv;
-      if ((p.sign_v[jj >> 5] >> (jj & 31)) & 1u) o = -o;
+      const uint32_t sw = (lane & 32) ? uniform_u32(p.sign_v[2 * e + 1]) : uniform_u32(p.sign_v[2 * e]);
+      if ((sw >> (jj & 31)) & 1u) o = -o;
       p.out[(int64_t)bh * kD + jj] = o;
     }
   }
@@ -668,15 +725,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
 
 template <int BKLO, int BKHI, int KS, int BVLO, int BVHI, int VS, int GC>
 static int launch_scan(const DecodeParams& p, dim3 grid, hipStream_t stream) {
-  const size_t lds = sizeof(float) * (size_t)ScanLds<GC, Rec<BVLO, BVHI, VS>::W, BVLO, BVHI, VS>::kTotal;
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute((const void*)decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, GC>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return TQ_ERR_HIP;
-    attr = true;
-  }
-  hipLaunchKernelGGL((decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, GC>), grid, dim3(kThreads), lds,
+  hipLaunchKernelGGL((decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, GC>), grid, dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
@@ -752,6 +801,7 @@ tq_decode_plan tq_plan_decode(int32_t batch, int32_t hq, int32_t hkv, int64_t ca
   p.waves = kWaves;
   p.parts = (int32_t)n_split;
   p.tokens_per_split = tps;
+  p.units = units;
   p.ws_part_off = 0;
   p.ws_bytes = (int64_t)batch * hq * p.parts * kPartFloats * 4;
   return p;

@@ -146,6 +146,15 @@ __device__ __forceinline__ uint32_t f64_to_f16_bits(double v) {
   return f32_to_f16_bits(f);
 }
 
+// A wave-uniform 32-bit value (a kernel-argument word read with a constant index) kept
+// in an SGPR and opaque to the optimizer.  Selecting among such values per lane avoids a
+// per-lane indexed read of kernel-argument memory, which would become a vector load from
+// the argument segment instead of scalar loads.
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
 __device__ __forceinline__ float load_elem(const void* base, int64_t i, int dtype) {
   if (dtype == 0) return reinterpret_cast<const float*>(base)[i];
   uint32_t h = reinterpret_cast<const uint16_t*>(base)[i];

@@ -17,6 +17,7 @@ struct tq_decode_plan {
   int32_t waves;          // waves per scan workgroup
   int32_t parts;          // partial results per (batch, q head) = n_split
   int64_t tokens_per_split;
+  int64_t units;          // (batch, kv head, chunk) units = scan grid height
   int64_t ws_part_off;    // byte offset of the split partials inside the workspace
   int64_t ws_bytes;
 };

@@ -156,8 +156,10 @@ __device__ void guard_fix(const QParams& p, int64_t v, int m, int n, const uint6
     xd[e] = (double)xv;
   }
 #pragma unroll
-  for (int e = 0; e < NE; ++e)
-    if ((p.sign_mask[(lane + 64 * e) >> 5] >> ((lane + 64 * e) & 31)) & 1u) xd[e] = -xd[e];
+  for (int e = 0; e < NE; ++e) {
+    const uint32_t sw = (lane & 32) ? uniform_u32(p.sign_mask[2 * e + 1]) : uniform_u32(p.sign_mask[2 * e]);
+    if ((sw >> (lane & 31)) & 1u) xd[e] = -xd[e];
+  }
 #pragma unroll
   for (int h = 1; h < NE; h <<= 1)
 #pragma unroll
@@ -250,10 +252,17 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
   __shared__ float cpos_lds[16];  // positive centroids: lo table, then hi table
   __shared__ int wmap[32];        // record word -> (block << 8) | plane, plane 0xFF = signs
 
-  if (threadIdx.x < 16) {
-    cent_lds[threadIdx.x] = p.cent_lo[threadIdx.x];
-    cent_lds[16 + threadIdx.x] = p.cent_hi[threadIdx.x];
-    cpos_lds[threadIdx.x] = threadIdx.x < 8 ? p.cpos_lo[threadIdx.x] : p.cpos_hi[threadIdx.x - 8];
+  if (threadIdx.x == 0) {  // constant indices: scalar reads of the kernel arguments
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      cent_lds[k] = p.cent_lo[k];
+      cent_lds[16 + k] = p.cent_hi[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      cpos_lds[k] = p.cpos_lo[k];
+      cpos_lds[8 + k] = p.cpos_hi[k];
+    }
   }
   if (threadIdx.x == 0) {
     int w = 0;

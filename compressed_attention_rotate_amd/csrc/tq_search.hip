@@ -80,7 +80,9 @@ __global__ __launch_bounds__(256) void search_prologue(SearchParams p) {
     for (int e = 0; e < NE; ++e) {
       const int j = lane + 64 * e;
       float x = (j < p.d_in) ? p.queries[qi * p.d_in + j] : 0.0f;
-      if ((p.sign_mask[j >> 5] >> (j & 31)) & 1u) x = -x;
+      uint32_t sw = uniform_u32(p.sign_mask[2 * e]);
+      if (lane & 32) sw = uniform_u32(p.sign_mask[2 * e + 1]);
+      if ((sw >> (j & 31)) & 1u) x = -x;
       v[e] = x;
     }
 #pragma unroll

@@ -148,6 +148,7 @@ int64_t tq_attend_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int64_
  *   skipped  : device, nullable, int64 the call ADDS the number of value rows it
  *              did not read to
  *   workspace: device, >= tq_attend_workspace_bytes(...) bytes, no initial contents
+ *              (split partials); calls that share a workspace must not overlap in time
  * Errors: TQ_ERR_ARG, TQ_ERR_SHAPE (d != 128, hq % hkv, unsupported widths),
  * TQ_ERR_ALIGN, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* fv,

@@ -129,3 +129,35 @@ def test_full_context_llama_layer(torch_gpu):
     """Full 32768-token cache, 32 query / 8 KV heads, b = 4, launched as bench.py times it;
     every head checked."""
     _case(torch_gpu, 1, 32, 8, 32768, [32768], (128, 3, 3, 128), (128, 3, 3, 128), TI.data_seed(2))
+
+
+def test_workspace_reuse(torch_gpu):
+    """Calls that reuse one workspace (holding whatever the previous call left), with
+    different shapes and lengths, must equal calls on fresh workspaces bit for bit."""
+    import compressed_attention_rotate_amd as tq
+    torch = torch_gpu
+    d, seed = 128, TI.data_seed(2) + 31
+    fmt = tq.Format.uniform(d, 3)
+    signs, S = TI.rotation(d, seed + 500000)
+    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    cases = [(1, 32, 8, 4096, [4096]), (2, 8, 2, 3000, [3000, 17]), (1, 32, 8, 4096, [1000]),
+             (3, 16, 4, 700, [0, 700, 333])]
+    ws_bytes = max(tq.attend_workspace_bytes(b, hq, hkv, n) for b, hq, hkv, n, _ in cases)
+    ws = torch.full((ws_bytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for b, hq, hkv, n, lens in cases:
+            kb, vb, _ = TI.kv_layer(b, hkv, n, d, seed=seed + n)
+            q = torch.from_numpy(TI.decode_queries(b, hq, d, seed + n).view(np.int16)).cuda() \
+                .view(torch.bfloat16)
+            ck, nk = tq.quantize_kv(torch.from_numpy(kb.view(np.int16)).cuda()
+                                    .view(torch.bfloat16).view(-1, d), fmt, tab)
+            cv, nv = tq.quantize_kv(torch.from_numpy(vb.view(np.int16)).cuda()
+                                    .view(torch.bfloat16).view(-1, d), fmt, tab)
+            rb = fmt.record_bytes()
+            args = (q, ck.view(b, hkv, n, rb), nk.view(b, hkv, n, 2), cv.view(b, hkv, n, rb),
+                    nv.view(b, hkv, n, 2), torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                    fmt, tab)
+            shared = tq.attend_decode(*args, workspace=ws).clone()
+            fresh = tq.attend_decode(*args)
+            torch.cuda.synchronize()
+            assert torch.equal(shared, fresh), f"shape {(b, hq, hkv, n, lens)} rep {rep}"
