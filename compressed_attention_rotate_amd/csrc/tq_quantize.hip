@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -106,21 +108,21 @@ __device__ __forceinline__ float cvt16(uint32_t h) {
 // t_j < a' per positive boundary gives k = #{j : t_j < a'} and idx = z > 0 ? H + k : H-1-k;
 // bit q of k is the XOR of the thermometer ballots over multiples of 2^q.
 template <int B, bool COUNT>
-__device__ __forceinline__ float encode_slot(float z, const float* cpos_lds, const float* tpos,
+__device__ __forceinline__ float encode_slot(float z, const float* cpos, const float* tpos,
                                              uint64_t* planes, int& amb) {
   constexpr int H = Thermo<B>::H;
   const bool pos = z > 0.0f;
   const float az = fabsf(z);
   const float a = as_f(as_u(az) + (pos ? 0u : 1u));
   uint64_t T[H > 1 ? H : 2];
-  int k = 0;
+  float cv = cpos[0];  // the thresholds ascend, so the last true compare picks the centroid
 #pragma unroll
   for (int j = 1; j < H; ++j) {
     const bool cj = tpos[j] < a;
     T[j] = __ballot(cj);
-    k += cj ? 1 : 0;
+    cv = cj ? cpos[j] : cv;
+    asm("" : "+v"(cv));  // keeps the chain of selects (no indexed read of a private copy)
   }
-  const float cv = cpos_lds[k];
   const uint64_t P = __ballot(pos);
 #pragma unroll
   for (int q = 0; q + 1 < B; ++q) {
@@ -137,6 +139,15 @@ __device__ __forceinline__ float encode_slot(float z, const float* cpos_lds, con
     amb += dmin < kWindow ? 1 : 0;
   }
   return pos ? cv : -cv;
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 (compile-time loop index).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // fp64 recomputation of projection n of local vector m (rare path, whole wave).  Codes are
@@ -299,11 +310,13 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
   const float bs16 = (c & 16) ? -1.0f : 1.0f;
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const float sqrt_d = sqrtf((float)D);
-  float tpl[8], tph[8];
+  float tpl[8], tph[8], cpl[8], cph[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     tpl[k] = p.tpos_lo[k];
     tph[k] = p.tpos_hi[k];
+    cpl[k] = p.cpos_lo[k];
+    cph[k] = p.cpos_hi[k];
   }
 
   ChunkPlan<D> cp;
@@ -406,32 +419,39 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           const float zinv = nf > 0.0f ? __builtin_amdgcn_rcpf(nf * sqrt_d) : 0.0f;
           rsq[gg] = 0.0f;
           int amb = 0;
-#pragma unroll
-          for (int s = 0; s < NB; ++s) {
+          uint64_t pls[NB][3];  // this pass's plane ballots, stored by lane 0 below
+          static_for<0, NB>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int s = decltype(sc)::value;
             const float z = xv[gg][s] * zinv;
-            uint64_t pl[3];
             float cv;
-            int nb;
             if constexpr (UNI) {
-              cv = encode_slot<BLO, COUNT>(z, cpos_lds, tpl, pl, amb);
-              nb = BLO;
-            } else {
+              cv = encode_slot<BLO, COUNT>(z, cpl, tpl, pls[s], amb);
+            } else {  // mixed widths (run-time split): lane 0 stores this slot right away
+              uint64_t pl[3];
+              int nb;
               if (s < p.split_blocks) {
-                cv = encode_slot<BLO, COUNT>(z, cpos_lds, tpl, pl, amb);
+                cv = encode_slot<BLO, COUNT>(z, cpl, tpl, pl, amb);
                 nb = BLO;
               } else {
-                cv = encode_slot<BHI, COUNT>(z, cpos_lds + 8, tph, pl, amb);
+                cv = encode_slot<BHI, COUNT>(z, cph, tph, pl, amb);
                 nb = BHI;
               }
-            }
-            // lane 0 drops the plane ballots into the tile's ballot table
-            if (lane == 0) {
+              if (lane == 0) {
 #pragma unroll
-              for (int q = 0; q < 3; ++q)
-                if (q < nb) bal[((pp0 + gg) * NB + s) * 4 + q] = pl[q];
+                for (int q = 0; q < 3; ++q)
+                  if (q < nb) bal[((pp0 + gg) * NB + s) * 4 + q] = pl[q];
+              }
             }
             r[gg][s] = fmaf(xv[gg][s], inv_sqrt_d, -n16f * cv);
             rsq[gg] = fmaf(r[gg][s], r[gg][s], rsq[gg]);
+          });
+          if constexpr (UNI) {
+            if (lane == 0) {
+#pragma unroll
+              for (int s = 0; s < NB; ++s)
+#pragma unroll
+                for (int q = 0; q < BLO; ++q) bal[((pp0 + gg) * NB + s) * 4 + q] = pls[s][q];
+            }
           }
           if constexpr (COUNT) cnt_amb += valid[gg] ? (unsigned long long)amb : 0ull;
         }
@@ -441,13 +461,19 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           const float rn = sqrtf(rs);
           const uint32_t r16 = f32_to_f16_bits(rn);
           const float rinv = rn > 0.0f ? kRScale / rn : 0.0f;
+          // hoff(row, 32 s + c, lo): the 16-byte unit 4 s + (c >> 3) is XORed with row & 15,
+          // i.e. s with (row >> 2) & 3 and c >> 3 with row & 3
+          const int row = vloc[gg];
+          const int abase = row * (4 * D) + ((((c >> 3) ^ (row & 3))) << 4) + 2 * (c & 7);
+          const int rx2 = (row >> 2) & 3;
 #pragma unroll
           for (int s = 0; s < NB; ++s) {
             const float rv = r[gg][s] * rinv;
             const _Float16 hi = (_Float16)rv;
             const _Float16 lo = (_Float16)(rv - (float)hi);
-            *reinterpret_cast<_Float16*>(tileb + hoff<D>(vloc[gg], 32 * s + c, 0)) = hi;
-            *reinterpret_cast<_Float16*>(tileb + hoff<D>(vloc[gg], 32 * s + c, 1)) = lo;
+            _Float16* dst = reinterpret_cast<_Float16*>(tileb + abase + ((s ^ rx2) << 6));
+            dst[0] = hi;
+            dst[D] = lo;  // lo half: 2 D bytes further
           }
           if (c == 0) snorm[vloc[gg]] = n16[gg] | (r16 << 16);
           if constexpr (COUNT)
