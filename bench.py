@@ -213,7 +213,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "quantize_kernel<128,3,3>",
                      "achieved": round(q_tfs, 3), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(q_tfs / FP32_MFMA_PEAK_TFS, 4), "traffic": trafq},
-        "roofline_decode": {"bound": "hbm", "kernel": "decode_prologue+decode_scan+decode_combine",
+        "roofline_decode": {"bound": "hbm", "kernel": "decode_scan+decode_combine",
                             "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": trafd},
     }
