@@ -161,3 +161,78 @@ def test_workspace_reuse(torch_gpu):
             fresh = tq.attend_decode(*args)
             torch.cuda.synchronize()
             assert torch.equal(shared, fresh), f"shape {(b, hq, hkv, n, lens)} rep {rep}"
+
+
+def _full_size_sampled(torch, batch, hq, hkv, ntok, fk, fv, seed, spikes, tau, units):
+    """Full-size decode on the GPU with sampled oracle checks.  The GPU quantizes the whole
+    cache (product path); for each sampled (batch, KV head) unit the records are replaced by
+    the oracle's own packing of the same inputs, so the GPU decodes, for those heads, exactly
+    the bytes the oracle decodes.  Logits of the unit's query heads within the logit bar,
+    ungated outputs within 2e-3, gated outputs (tau > 0) within 5e-3 of the ungated oracle."""
+    import compressed_attention_rotate_amd as tq
+    d, G = 128, hq // hkv
+    kb, vb, _ = TI.kv_layer(batch, hkv, ntok, d, seed=seed, spike_frac=spikes)
+    q_bits = TI.decode_queries(batch, hq, d, seed)
+    signs, S = TI.rotation(d, seed + 500000)
+    fmt_k, fmt_v = tq.Format(*fk), tq.Format(*fv)
+    Sd = torch.from_numpy(S).cuda()
+    tk, tv = tq.Tables(fmt_k, signs, Sd), tq.Tables(fmt_v, signs, Sd)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    rbk, rbv = fmt_k.record_bytes(), fmt_v.record_bytes()
+    ck, nk = tq.quantize_kv(bf(kb).view(-1, d), fmt_k, tk)
+    cv, nv = tq.quantize_kv(bf(vb).view(-1, d), fmt_v, tv)
+    ck, nk = ck.view(batch, hkv, ntok, rbk), nk.view(batch, hkv, ntok, 2)
+    cv, nv = cv.view(batch, hkv, ntok, rbv), nv.view(batch, hkv, ntok, 2)
+    oracle = {}
+    for bi, kh in units:
+        rk, nko, _ = oracle_pack_cache(kb[bi:bi + 1, kh:kh + 1], O.Format(*fk), signs, S, bf16=True)
+        rv, nvo, _ = oracle_pack_cache(vb[bi:bi + 1, kh:kh + 1], O.Format(*fv), signs, S, bf16=True)
+        ck[bi, kh] = torch.from_numpy(np.ascontiguousarray(rk[0, 0])).cuda()
+        cv[bi, kh] = torch.from_numpy(np.ascontiguousarray(rv[0, 0])).cuda()
+        nk[bi, kh] = torch.from_numpy(np.ascontiguousarray(nko[0, 0]).view(np.int16)).cuda().view(torch.float16)
+        nv[bi, kh] = torch.from_numpy(np.ascontiguousarray(nvo[0, 0]).view(np.int16)).cuda().view(torch.float16)
+        oracle[(bi, kh)] = (rk, nko, rv, nvo)
+    q = bf(q_bits)
+    seq = torch.full((batch,), ntok, dtype=torch.int32, device="cuda")
+    out_u, lg = tq.attend_decode(q, ck, nk, cv, nv, seq, fmt_k, tk, fmt_v, tv, logits=True)
+    sk = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out_g = tq.attend_decode(q, ck, nk, cv, nv, seq, fmt_k, tk, fmt_v, tv, tau=tau, skipped=sk) \
+        if tau > 0 else None
+    torch.cuda.synchronize()
+    q64 = TI.bf16_to_f64(q_bits)
+    for (bi, kh), (rk, nko, rv, nvo) in oracle.items():
+        hs = slice(kh * G, (kh + 1) * G)
+        out_o, lg_o, sc_o, _, _ = oracle_decode(
+            q64[bi:bi + 1, hs], rk, nko, rv, nvo, [ntok], O.Format(*fk), O.Format(*fv),
+            signs, S, signs, S, 1 / math.sqrt(d), 0.0)
+        lg_g = lg[bi:bi + 1, hs].cpu().numpy()
+        worst, dmax = _compare(out_u[bi:bi + 1, hs].cpu().numpy(), lg_g, out_o, lg_o, sc_o, [ntok])
+        msg = f"\nunit (b={bi}, kv={kh}) of {batch}x{ntok}: logit err/bound {worst:.3g}, out max|diff| {dmax:.3g}"
+        if out_g is not None:
+            _, _, _, drops, mass = oracle_decode(
+                q64[bi:bi + 1, hs], rk, nko, rv, nvo, [ntok], O.Format(*fk), O.Format(*fv),
+                signs, S, signs, S, 1 / math.sqrt(d), tau)
+            gmax = float(np.max(np.abs(out_g[bi:bi + 1, hs].cpu().numpy() - out_o)))
+            assert gmax <= 5e-3, f"gated output differs from the ungated oracle by {gmax}"
+            msg += (f", gated vs ungated oracle {gmax:.3g}, rows skipped (whole batch) "
+                    f"{int(sk.item())}, oracle drops {sum(drops.values())} mass "
+                    f"{max(mass.values()):.3g}")
+        print(msg)
+    return int(sk.item())
+
+
+def test_full_size_batch16_mixed_width(torch_gpu):
+    """Batch 16 x 32768 tokens of the Llama-3.1-8B layer, b = 3.5 (3-bit codebook on rotated
+    coordinates 0-63, 2-bit on 64-127, + QJL) for K and V: the GPU decodes the whole batch;
+    two sampled (batch, KV head) units are checked against the oracle."""
+    _full_size_sampled(torch_gpu, 16, 32, 8, 32768, (128, 3, 2, 64), (128, 3, 2, 64),
+                       TI.data_seed(3), 0.0, 0.0, [(11, 2), (0, 7)])
+
+
+def test_full_size_long_context_sparse_v(torch_gpu):
+    """Batch 4 x 131072 tokens, 1% of token positions with x10 keys, K b = 4, V b = 3,
+    Sparse-V gate tau = 1e-4: the GPU decodes the whole batch gated and ungated; one sampled
+    (batch, KV head) unit is checked against the oracle, and the gate skips rows."""
+    skipped = _full_size_sampled(torch_gpu, 4, 32, 8, 131072, (128, 3, 3, 128), (128, 2, 2, 128),
+                                 TI.data_seed(4), 0.01, 1e-4, [(2, 5)])
+    assert skipped > 0
