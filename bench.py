@@ -95,6 +95,34 @@ def cpu_baseline(kb, vb, qb, signs, S):
             "quantize_tokens_per_s": nt * nh / HKV / (t1 - t0)}
 
 
+def _mse_only_values(tq, torch, dev, v, q, ck, nk, seq, ws, out, fmt_k, tab, signs, S, steps, nvec):
+    """The same layer with the values stored MSE-only (codebook planes and norms, no QJL sign
+    words): quantize time of the value tensor and decode time, timed like the main step."""
+    fmt_v = tq.Format.uniform(D, BITS, qjl=False)
+    tab_v = tq.Tables(fmt_v, signs, torch.from_numpy(S).to(dev))
+    rb = fmt_v.record_bytes()
+    cv = torch.empty((BATCH, HKV, NTOK, rb), dtype=torch.uint8, device=dev)
+    nv = torch.empty((BATCH, HKV, NTOK, 2), dtype=torch.float16, device=dev)
+    qv = lambda: tq.quantize_kv(v.view(-1, D), fmt_v, tab_v, codes=cv.view(nvec, rb),
+                                norms=nv.view(nvec, 2))
+    dc = lambda: tq.attend_decode(q, ck, nk, cv, nv, seq, fmt_k, tab, fmt_v, tab_v, workspace=ws,
+                                  out=out)
+    for _ in range(3):
+        qv(); dc()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record(); qv(); ev[k][1].record(); dc(); ev[k][2].record()
+    torch.cuda.synchronize()
+    tq_s = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    td_s = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    nbytes = nvec * (fmt_k.record_bytes() + 4) + nvec * (rb + 4)
+    return {"format_v": f"{BITS}-bit codebook, no QJL ({rb} B/vector)",
+            "quantize_v_us": round(float(tq_s) * 1e6, 3),
+            "decode_us": round(float(td_s) * 1e6, 3),
+            "decode_gbs": round(nbytes / td_s / 1e9, 2)}
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -217,6 +245,8 @@ def main():
                             "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": trafd},
     }
+    line["mse_only_values"] = _mse_only_values(tq, torch, dev, vs[0], q, codes_k[0], norms_k[0],
+                                               seq, ws, out, fmt, tab, signs, S, steps, nvec)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(kb, vb, qb, signs, S)
     print(json.dumps(line), flush=True)

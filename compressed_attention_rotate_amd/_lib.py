@@ -25,7 +25,8 @@ class TQError(RuntimeError):
 
 class c_format(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("bits_lo", ctypes.c_int32),
-                ("bits_hi", ctypes.c_int32), ("split", ctypes.c_int32)]
+                ("bits_hi", ctypes.c_int32), ("split", ctypes.c_int32),
+                ("qjl", ctypes.c_int32)]
 
 
 class c_tables(ctypes.Structure):
@@ -80,18 +81,20 @@ def _check(code: int, what: str) -> None:
 
 @dataclass(frozen=True)
 class Format:
-    """Packed format: codebook bits for coordinates < split and >= split, head dim d."""
+    """Packed format: codebook bits for coordinates < split and >= split, head dim d; qjl
+    False stores the tensor MSE-only (no QJL sign words)."""
     d: int
     bits_lo: int
     bits_hi: int
     split: int
+    qjl: bool = True
 
     @staticmethod
-    def uniform(d: int, bits: int) -> "Format":
-        return Format(d, bits, bits, d)
+    def uniform(d: int, bits: int, qjl: bool = True) -> "Format":
+        return Format(d, bits, bits, d, qjl)
 
     def c(self) -> c_format:
-        return c_format(self.d, self.bits_lo, self.bits_hi, self.split)
+        return c_format(self.d, self.bits_lo, self.bits_hi, self.split, 1 if self.qjl else 0)
 
     def record_bytes(self) -> int:
         f = self.c()

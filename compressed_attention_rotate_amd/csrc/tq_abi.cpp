@@ -71,13 +71,14 @@ int tq_check_format(const tq_format* f) {
   const int hi = (f->split == f->d) ? f->bits_lo : f->bits_hi;
   if (f->split == f->d && f->bits_hi != f->bits_lo) return TQ_ERR_SHAPE;
   if (!supported_widths(f->d, f->bits_lo, hi)) return TQ_ERR_SHAPE;
+  if (f->qjl != 0 && f->qjl != 1) return TQ_ERR_ARG;
   return TQ_OK;
 }
 
 int64_t tq_record_bytes(const tq_format* f) {
   if (tq_check_format(f) != TQ_OK) return -1;
   const int lo_blocks = f->split / 32, hi_blocks = (f->d - f->split) / 32;
-  return 4 * ((int64_t)lo_blocks * (f->bits_lo + 1) + (int64_t)hi_blocks * (f->bits_hi + 1));
+  return 4 * ((int64_t)lo_blocks * (f->bits_lo + f->qjl) + (int64_t)hi_blocks * (f->bits_hi + f->qjl));
 }
 
 int tq_quantize_kv(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
@@ -145,6 +146,7 @@ int tq_ip_search(const tq_format* f, const tq_tables* t, const void* codes_db,
                  int64_t workspace_bytes, tq_stream_t stream) {
   int rc = tq_check_format(f);
   if (rc) return rc;
+  if (!f->qjl) return TQ_ERR_SHAPE;  // the score is the estimator with the QJL term
   if (n_q < 0 || n_db < 0 || k < 1 || k > 64 || k > n_db) return TQ_ERR_ARG;
   if (d_in <= 0 || d_in > f->d) return TQ_ERR_SHAPE;
   if ((rc = check_tables(f, t))) return rc;

@@ -28,6 +28,7 @@
 //             pair of two coordinates comes from one read of a table indexed by their
 //             code bits; fp32 accumulation of w n16 c[idx] and w gamma r16 sigma per head.
 //             The waves' partial (m, l, acc) are merged in LDS: one partial per workgroup.
+//             MSE-only values (no sign words) drop the QJL term of the value sum.
 //   combine:  per (batch, query head) one workgroup merges the splits in a fixed order and
 //             maps back: out = D H (A + S^T Q) / (sqrt(d) l).
 #include <hip/hip_runtime.h>
@@ -55,14 +56,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __host__ __device__ constexpr int round4(int x) { return (x + 3) / 4 * 4; }
 
-// Record layout of a format with SPLITB blocks of BLO bits then blocks of BHI bits.
-template <int BLO, int BHI, int SPLITB>
+// Record layout of a format with SPLITB blocks of BLO bits then blocks of BHI bits; each
+// block holds its code planes and, when Q is 1, one QJL sign word.
+template <int BLO, int BHI, int SPLITB, int Q = 1>
 struct Rec {
-  static constexpr int W = SPLITB * (BLO + 1) + (kNB - SPLITB) * (BHI + 1);  // words
+  static constexpr int W = SPLITB * (BLO + Q) + (kNB - SPLITB) * (BHI + Q);  // words
   static constexpr int VEC = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);      // load width
   static constexpr int bits(int blk) { return blk < SPLITB ? BLO : BHI; }
   __host__ __device__ static constexpr int off(int blk) {
-    return blk < SPLITB ? blk * (BLO + 1) : SPLITB * (BLO + 1) + (blk - SPLITB) * (BHI + 1);
+    return blk < SPLITB ? blk * (BLO + Q) : SPLITB * (BLO + Q) + (blk - SPLITB) * (BHI + Q);
   }
 };
 
@@ -211,10 +213,11 @@ __device__ __forceinline__ void lut_nib(const float* Ts, int g0, uint32_t w, flo
     acc[h] += ((t[0][h] + t[1][h]) + (t[2][h] + t[3][h])) + ((t[4][h] + t[5][h]) + (t[6][h] + t[7][h]));
 }
 
-template <int BKLO, int BKHI, int KSPLIT, int BVLO, int BVHI, int VSPLIT, int GC>
+// VQ: the value records carry QJL sign words (else MSE-only values: no residual term).
+template <int BKLO, int BKHI, int KSPLIT, int BVLO, int BVHI, int VSPLIT, bool VQ, int GC>
 __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   using KR = Rec<BKLO, BKHI, KSPLIT>;
-  using VR = Rec<BVLO, BVHI, VSPLIT>;
+  using VR = Rec<BVLO, BVHI, VSPLIT, VQ ? 1 : 0>;
   constexpr int KW = KR::W, VW = VR::W;
   using L = ScanLds<GC, VW, BVLO, BVHI, VSPLIT>;
   constexpr int kW0 = L::kW0, kRS = L::kRS;
@@ -443,8 +446,12 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   // one value row (this lane's 4 coordinates) accumulated with the row's weights
   auto value_row = [&](const float* r) {
     const uint32_t* rw = reinterpret_cast<const uint32_t*>(r) + voff;
-    uint32_t p0, p1 = 0, p2 = 0, sg;
-    if constexpr (BVLO == 3 && BVHI == 3) {
+    uint32_t p0, p1 = 0, p2 = 0, sg = 0;
+    if constexpr (!VQ) {
+      p0 = rw[0];
+      if constexpr (BVLO >= 2 || BVHI >= 2) p1 = vnb >= 2 ? rw[1] : 0u;
+      if constexpr (BVLO == 3 || BVHI == 3) p2 = vnb == 3 ? rw[2] : 0u;
+    } else if constexpr (BVLO == 3 && BVHI == 3) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(rw);
       p0 = x[0]; p1 = x[1]; p2 = x[2]; sg = x[3];
     } else {
@@ -459,20 +466,26 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
                        (__builtin_amdgcn_ubfe(p2, vbit, 4) << 9);
     const f32x2 cA = *reinterpret_cast<const f32x2*>(cpb + ((f << 2) & kPatMask));
     const f32x2 cB = *reinterpret_cast<const f32x2*>(cpb + (f & kPatMask));
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(spb + 16 * __builtin_amdgcn_ubfe(sg, vbit, 4));
-    float u[GC], u2[GC];
+    float u[GC];
     table_read<GC>(r, 0, u);
-    table_read<GC>(r + GC, 0, u2);
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
       am[h][0] = fmaf(u[h], cA[0], am[h][0]);
       am[h][1] = fmaf(u[h], cA[1], am[h][1]);
       am[h][2] = fmaf(u[h], cB[0], am[h][2]);
       am[h][3] = fmaf(u[h], cB[1], am[h][3]);
-      aq[h][0] = fmaf(u2[h], sv[0], aq[h][0]);
-      aq[h][1] = fmaf(u2[h], sv[1], aq[h][1]);
-      aq[h][2] = fmaf(u2[h], sv[2], aq[h][2]);
-      aq[h][3] = fmaf(u2[h], sv[3], aq[h][3]);
+    }
+    if constexpr (VQ) {
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(spb + 16 * __builtin_amdgcn_ubfe(sg, vbit, 4));
+      float u2[GC];
+      table_read<GC>(r + GC, 0, u2);
+#pragma unroll
+      for (int h = 0; h < GC; ++h) {
+        aq[h][0] = fmaf(u2[h], sv[0], aq[h][0]);
+        aq[h][1] = fmaf(u2[h], sv[1], aq[h][1]);
+        aq[h][2] = fmaf(u2[h], sv[2], aq[h][2]);
+        aq[h][3] = fmaf(u2[h], sv[3], aq[h][3]);
+      }
     }
   };
 
@@ -546,12 +559,12 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
       float* row = lds + own;
       if constexpr (GC == 4) {
         *reinterpret_cast<f32x4*>(row) = f32x4{u[0], u[1], u[2], u[3]};
-        *reinterpret_cast<f32x4*>(row + 4) = f32x4{u2[0], u2[1], u2[2], u2[3]};
+        if constexpr (VQ) *reinterpret_cast<f32x4*>(row + 4) = f32x4{u2[0], u2[1], u2[2], u2[3]};
       } else {
 #pragma unroll
         for (int h = 0; h < GC; ++h) {
           row[h] = u[h];
-          row[GC + h] = u2[h];
+          if constexpr (VQ) row[GC + h] = u2[h];
         }
       }
       if (any_keep) {
@@ -724,9 +737,13 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
 }
 
 template <int BKLO, int BKHI, int KS, int BVLO, int BVHI, int VS, int GC>
-static int launch_scan(const DecodeParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, GC>), grid, dim3(kThreads), 0,
-                     stream, p);
+static int launch_scan(const DecodeParams& p, bool vq, dim3 grid, hipStream_t stream) {
+  if (vq)
+    hipLaunchKernelGGL((decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, true, GC>), grid, dim3(kThreads),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, false, GC>), grid,
+                       dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
@@ -737,15 +754,15 @@ static int dispatch_scan(const tq_format* fk, const tq_format* fv, const DecodeP
   const int kl = fk->bits_lo, kh = fk->split == fk->d ? fk->bits_lo : fk->bits_hi;
   const int vl = fv->bits_lo, vh = fv->split == fv->d ? fv->bits_lo : fv->bits_hi;
   const int ks = fk->split / 32, vs = fv->split / 32;
-  const bool ku = kl == kh, vu = vl == vh;
+  const bool ku = kl == kh, vu = vl == vh, vq = fv->qjl != 0;
   if (ku && vu) {
-    if (kl == 3 && vl == 3) return launch_scan<3, 3, 4, 3, 3, 4, GC>(p, grid, s);
-    if (kl == 3 && vl == 2) return launch_scan<3, 3, 4, 2, 2, 4, GC>(p, grid, s);
-    if (kl == 2 && vl == 2) return launch_scan<2, 2, 4, 2, 2, 4, GC>(p, grid, s);
-    if (kl == 1 && vl == 1) return launch_scan<1, 1, 4, 1, 1, 4, GC>(p, grid, s);
+    if (kl == 3 && vl == 3) return launch_scan<3, 3, 4, 3, 3, 4, GC>(p, vq, grid, s);
+    if (kl == 3 && vl == 2) return launch_scan<3, 3, 4, 2, 2, 4, GC>(p, vq, grid, s);
+    if (kl == 2 && vl == 2) return launch_scan<2, 2, 4, 2, 2, 4, GC>(p, vq, grid, s);
+    if (kl == 1 && vl == 1) return launch_scan<1, 1, 4, 1, 1, 4, GC>(p, vq, grid, s);
   }
   if (kl == 3 && kh == 2 && ks == 2 && vl == 3 && vh == 2 && vs == 2)
-    return launch_scan<3, 2, 2, 3, 2, 2, GC>(p, grid, s);
+    return launch_scan<3, 2, 2, 3, 2, 2, GC>(p, vq, grid, s);
   return TQ_ERR_SHAPE;
 }
 
@@ -772,6 +789,7 @@ static void walsh(int bits, const float* c, float* alpha) {
 
 // ---------------------------------------------------------------------------------------
 bool tq_decode_formats_supported(const tq_format* fk, const tq_format* fv) {
+  if (!fk->qjl) return false;  // the logit estimator needs the keys' QJL term
   const int kl = fk->bits_lo, kh = fk->split == fk->d ? fk->bits_lo : fk->bits_hi;
   const int vl = fv->bits_lo, vh = fv->split == fv->d ? fv->bits_lo : fv->bits_hi;
   if (kl == kh && vl == vh)

@@ -9,6 +9,9 @@
 // turboquant_plus article, section "01 turboquant_plus：介绍与详解"), done here as an
 // in-register / cross-lane FWHT.
 //
+// A format without QJL (MSE-only) skips the residual split and phase 2; ||r|| is still
+// stored.
+//
 // Per tile:
 //   staging:  the 16 input rows arrive in LDS through coalesced 16-byte loads; the next
 //             tile's rows are fetched into registers while this tile is on the MFMA pipe.
@@ -90,6 +93,7 @@ struct QParams {
   int32_t cpr;           // 16-byte chunks per row (staged path)
   int32_t split_blocks;  // blocks using the lo table
   int32_t words;         // words per vector
+  int32_t qjl;           // 0: MSE-only records (no sign words, no projection)
   uint32_t sign_mask[8]; // bit j set: coordinate j is multiplied by -1
   float cpos_lo[8], tpos_lo[8], cpos_hi[8], tpos_hi[8];  // positive halves; tpos[0] unused
   float cent_lo[16], cent_hi[16];
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     for (int b = 0; b < NB; ++b) {
       const int bb = b < p.split_blocks ? BLO : BHI;
       for (int q = 0; q < bb; ++q) wmap[w++] = (b << 8) | q;
-      wmap[w++] = (b << 8) | 0xFF;
+      if (p.qjl) wmap[w++] = (b << 8) | 0xFF;
     }
   }
   auto load_s_rows = [&](int row0, int nrows) {
@@ -298,7 +302,8 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
       }
     }
   };
-  if constexpr (C::kResidentS) load_s_rows(0, D);
+  if constexpr (C::kResidentS)
+    if (p.qjl) load_s_rows(0, D);
   __syncthreads();
 
   const int h = lane >> 5, c = lane & 31;
@@ -500,14 +505,16 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           const int row = vloc[gg];
           const int abase = row * (4 * D) + ((((c >> 3) ^ (row & 3))) << 4) + 2 * (c & 7);
           const int rx2 = (row >> 2) & 3;
+          if (p.qjl) {
 #pragma unroll
-          for (int s = 0; s < NB; ++s) {
-            const float rv = r[gg][s] * rinv;
-            const _Float16 hi = (_Float16)rv;
-            const _Float16 lo = (_Float16)(rv - (float)hi);
-            _Float16* dst = reinterpret_cast<_Float16*>(tileb + abase + ((s ^ rx2) << 6));
-            dst[0] = hi;
-            dst[D] = lo;  // lo half: 2 D bytes further
+            for (int s = 0; s < NB; ++s) {
+              const float rv = r[gg][s] * rinv;
+              const _Float16 hi = (_Float16)rv;
+              const _Float16 lo = (_Float16)(rv - (float)hi);
+              _Float16* dst = reinterpret_cast<_Float16*>(tileb + abase + ((s ^ rx2) << 6));
+              dst[0] = hi;
+              dst[D] = lo;  // lo half: 2 D bytes further
+            }
           }
           if (c == 0) snorm[vloc[gg]] = n16[gg] | (r16 << 16);
           if constexpr (COUNT)
@@ -519,7 +526,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
       if (p.staged && gn < ngroups && gn * NW + wave < ntiles) fetch_tile<D>(p, cp, (gn * NW + wave) * TV, pre);
     }
     // ---------------- phase 2: JL projection on MFMA (3 fp16 products), sign ballots
-    for (int blk = 0; blk < NB; ++blk) {
+    for (int blk = 0; blk < NB && p.qjl; ++blk) {  // p.qjl is uniform over the grid
       if constexpr (!C::kResidentS) {
         __syncthreads();
         load_s_rows(blk * 32, 32);
@@ -672,6 +679,7 @@ int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, in
   p.cpr = p.staged ? (int32_t)(row_bytes / 16) : 1;
   p.split_blocks = f->split / 32;
   p.words = (int)(tq_record_bytes(f) / 4);
+  p.qjl = f->qjl;
   for (int j = 0; j < 8; ++j) p.sign_mask[j] = 0;
   for (int j = 0; j < f->d; ++j)
     if (t->signs[j] < 0) p.sign_mask[j >> 5] |= 1u << (j & 31);

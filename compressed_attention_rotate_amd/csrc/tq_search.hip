@@ -422,7 +422,7 @@ int tq_launch_search(const tq_format* f, const tq_tables* t, const void* codes_d
                      int64_t n_q, int32_t k, int64_t* out_ids, float* out_scores, void* workspace,
                      const tq_search_plan& plan, hipStream_t stream) {
   using namespace tqk;
-  if (f->bits_lo != f->bits_hi || f->split != f->d) return TQ_ERR_SHAPE;
+  if (f->bits_lo != f->bits_hi || f->split != f->d || !f->qjl) return TQ_ERR_SHAPE;
   SearchParams p{};
   p.codes = reinterpret_cast<const uint32_t*>(codes_db);
   p.norms = reinterpret_cast<const uint32_t*>(norms_db);

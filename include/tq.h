@@ -35,6 +35,8 @@
  *   (or projection) 32*block + i; words are little-endian uint32; the words of one
  *   vector are contiguous and vectors are contiguous (tq_record_bytes() bytes each).
  *   Norms live in a separate uint16 array [n][2]: fp16 ||x|| then fp16 ||r||.
+ *   With qjl == 0 the sign word of every block is absent (MSE-only record; ||r|| is
+ *   still stored).
  *   Supported widths: d = 128: (bits_lo, bits_hi) in {(1,1), (2,2), (3,3), (3,2),
  *   (2,1)}; d = 256: (2,2), (3,3).  The "block-32" layout follows the zhidx article
  *   (section "01 turboquant_plus：介绍与详解").
@@ -73,6 +75,9 @@ typedef struct tq_format {
   int32_t bits_lo;  /* codebook bits (b - 1) for coordinates j < split */
   int32_t bits_hi;  /* codebook bits for coordinates j >= split          */
   int32_t split;    /* multiple of 32, 0 < split <= d                    */
+  int32_t qjl;      /* 1: one QJL sign word per block; 0: MSE-only ("PolarQuant
+                       alone", no residual sketch: juejin post, section "第二步：QJL"
+                       names QJL as the bias fix on top of the MSE stage)        */
 } tq_format;
 
 typedef struct tq_tables {

@@ -186,21 +186,24 @@ def codebook(d: int, bits: int) -> Codebook:
 @dataclass(frozen=True)
 class Format:
     """Per-vector packed format.  Coordinates j < split use bits_lo codebook bits, the
-    rest bits_hi (split == d means one width).  Each coordinate also gets one QJL bit."""
+    rest bits_hi (split == d means one width).  With qjl each coordinate also gets one QJL
+    bit (one sign word per block); without it the tensor is stored MSE-only ("PolarQuant
+    alone": codebook planes and norms, no residual sketch)."""
     d: int
     bits_lo: int
     bits_hi: int
     split: int
+    qjl: bool = True
 
     @staticmethod
-    def uniform(d: int, bits: int) -> "Format":
-        return Format(d, bits, bits, d)
+    def uniform(d: int, bits: int, qjl: bool = True) -> "Format":
+        return Format(d, bits, bits, d, qjl)
 
     def bits_of_block(self, blk: int) -> int:
         return self.bits_lo if 32 * blk < self.split else self.bits_hi
 
     def words_per_vector(self) -> int:
-        return sum(self.bits_of_block(b) + 1 for b in range(self.d // 32))
+        return sum(self.bits_of_block(b) + (1 if self.qjl else 0) for b in range(self.d // 32))
 
     def record_bytes(self) -> int:
         return 4 * self.words_per_vector()
@@ -287,8 +290,8 @@ def quantize(x: np.ndarray, fmt: Format, signs: np.ndarray, S: np.ndarray,
 # --------------------------------------------------------------------------------------
 def pack(idx: np.ndarray, sbit: np.ndarray, fmt: Format) -> np.ndarray:
     """Records [n, record_bytes] uint8.  For each block of 32 coordinates, in order:
-    the B code bit-planes (plane p holds bit p of each code) then one word of QJL sign
-    bits; bit i of a word belongs to coordinate (or projection) 32*block + i; words
+    the B code bit-planes (plane p holds bit p of each code) then, with QJL, one word of
+    sign bits; bit i of a word belongs to coordinate (or projection) 32*block + i; words
     are little-endian uint32.  Layout idea: the zhidx article's "block-32" layout
     (section "01 turboquant_plus：介绍与详解")."""
     n, d = idx.shape
@@ -300,12 +303,14 @@ def pack(idx: np.ndarray, sbit: np.ndarray, fmt: Format) -> np.ndarray:
             bitsp = ((idx[:, cols] >> p) & 1).astype(np.uint8)
             # bit i of the word = coordinate 32*blk + i, little-endian bytes
             chunks.append(np.packbits(bitsp, axis=1, bitorder="little"))
-        chunks.append(np.packbits(sbit[:, cols].astype(np.uint8), axis=1, bitorder="little"))
+        if fmt.qjl:
+            chunks.append(np.packbits(sbit[:, cols].astype(np.uint8), axis=1, bitorder="little"))
     return np.ascontiguousarray(np.concatenate(chunks, axis=1)).reshape(n, -1)
 
 
 def unpack(rec: np.ndarray, fmt: Format):
-    """Inverse of ``pack``: (idx [n, d] int64, sbit [n, d] bool)."""
+    """Inverse of ``pack``: (idx [n, d] int64, sbit [n, d] bool; sbit all False when the
+    format has no QJL bits)."""
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
     n = rec.shape[0]
     w = rec.view("<u4").reshape(n, fmt.words_per_vector()).astype(np.int64)
@@ -319,8 +324,9 @@ def unpack(rec: np.ndarray, fmt: Format):
         for p in range(B):
             idx[:, cols] |= ((w[:, k:k + 1] >> shifts) & 1) << p
             k += 1
-        sbit[:, cols] = ((w[:, k:k + 1] >> shifts) & 1).astype(bool)
-        k += 1
+        if fmt.qjl:
+            sbit[:, cols] = ((w[:, k:k + 1] >> shifts) & 1).astype(bool)
+            k += 1
     return idx, sbit
 
 

@@ -107,9 +107,9 @@ def oracle_decode(q64, rec_k, nrm_k, rec_v, nrm_v, seq_lens, fmt_k, fmt_v, signs
             ik, sk = O.unpack(rec_k[bi, kh, :L], fmt_k)
             iv, sv = O.unpack(rec_v[bi, kh, :L], fmt_v)
             kt = O.dequantize(ik, sk, nrm_k[bi, kh, :L, 0], nrm_k[bi, kh, :L, 1], fmt_k, signs_k,
-                              S_k, *cbk)
+                              S_k, *cbk, qjl=fmt_k.qjl)
             vt = O.dequantize(iv, sv, nrm_v[bi, kh, :L, 0], nrm_v[bi, kh, :L, 1], fmt_v, signs_v,
-                              S_v, *cbv)
+                              S_v, *cbv, qjl=fmt_v.qjl)
             for g in range(G):
                 h = kh * G + g
                 o, lg, p, nd, dm = O.attend(q64[bi, h], kt, vt, scale, tau)

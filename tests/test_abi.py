@@ -53,13 +53,23 @@ def test_record_bytes_and_formats():
     assert tq.Format(128, 2, 2, 128).record_bytes() == 48          # b = 3
     assert tq.Format(128, 3, 2, 64).record_bytes() == 56           # b = 3.5 mixed
     assert tq.Format(256, 3, 3, 256).record_bytes() == 128
-    for f in (O.Format(128, 3, 3, 128), O.Format(128, 3, 2, 64), O.Format(256, 2, 2, 256)):
-        assert tq.Format(f.d, f.bits_lo, f.bits_hi, f.split).record_bytes() == f.record_bytes()
+    # MSE-only records drop one sign word per block
+    assert tq.Format(128, 3, 3, 128, qjl=False).record_bytes() == 48
+    assert tq.Format(128, 2, 2, 128, qjl=False).record_bytes() == 32
+    assert tq.Format(128, 3, 2, 64, qjl=False).record_bytes() == 40
+    for f in (O.Format(128, 3, 3, 128), O.Format(128, 3, 2, 64), O.Format(256, 2, 2, 256),
+              O.Format(128, 3, 3, 128, False), O.Format(128, 2, 1, 96, False),
+              O.Format(256, 3, 3, 256, False)):
+        assert tq.Format(f.d, f.bits_lo, f.bits_hi, f.split, f.qjl).record_bytes() == f.record_bytes()
     lib = tq.load()
     for bad in ((64, 3, 3, 64), (128, 4, 4, 128), (128, 3, 2, 48), (128, 3, 2, 128), (256, 1, 1, 256)):
-        f = c_format(*bad)
-        assert lib.tq_check_format(ctypes.byref(f)) == tq._lib.TQ_ERR_SHAPE
-        assert lib.tq_record_bytes(ctypes.byref(f)) < 0
+        for qjl in (0, 1):
+            f = c_format(*bad, qjl)
+            assert lib.tq_check_format(ctypes.byref(f)) == tq._lib.TQ_ERR_SHAPE
+            assert lib.tq_record_bytes(ctypes.byref(f)) < 0
+    f = c_format(128, 3, 3, 128, 2)                                  # qjl must be 0 or 1
+    assert lib.tq_check_format(ctypes.byref(f)) == tq._lib.TQ_ERR_ARG
+    assert lib.tq_record_bytes(ctypes.byref(f)) < 0
 
 
 def _tables(fmt, S_ptr=0x10000):
@@ -73,7 +83,7 @@ def _tables(fmt, S_ptr=0x10000):
 
 def test_quantize_validation_before_launch():
     lib = tq.load()
-    f = c_format(128, 3, 3, 128)
+    f = c_format(128, 3, 3, 128, 1)
     t, keep = _tables(tq.Format(128, 3, 3, 128))
     fake = ctypes.c_void_p(0x20000)
     Q = lambda **kw: lib.tq_quantize_kv(ctypes.byref(kw.get("f", f)), ctypes.byref(kw.get("t", t)),
@@ -101,14 +111,14 @@ def test_quantize_validation_before_launch():
 def test_decode_and_search_validation_before_launch():
     lib = tq.load()
     E = tq._lib
-    f = c_format(128, 3, 3, 128)
+    f = c_format(128, 3, 3, 128, 1)
     t, keep = _tables(tq.Format(128, 3, 3, 128))
     p = ctypes.c_void_p(0x40000)
     ws = tq.attend_workspace_bytes(1, 32, 8, 4096)
     assert ws > 0 and tq.attend_workspace_bytes(2, 32, 8, 4096) > ws
 
-    def D(hq=32, hkv=8, ws_bytes=ws, tau=0.0, fv=f, q=p):
-        return lib.tq_attend_decode(ctypes.byref(f), ctypes.byref(t), ctypes.byref(fv), ctypes.byref(t),
+    def D(hq=32, hkv=8, ws_bytes=ws, tau=0.0, fv=f, q=p, fk=f):
+        return lib.tq_attend_decode(ctypes.byref(fk), ctypes.byref(t), ctypes.byref(fv), ctypes.byref(t),
                                     q, 1, 1, hq, hkv, p, p, p, p, 4096, p, 0.088, tau, p, None, None,
                                     p, ws_bytes, None)
     assert D(hq=30) == E.TQ_ERR_SHAPE              # hq % hkv
@@ -116,21 +126,23 @@ def test_decode_and_search_validation_before_launch():
     assert D(ws_bytes=ws - 1) == E.TQ_ERR_WORKSPACE
     assert D(tau=-0.5) == E.TQ_ERR_ARG
     assert D(q=None) == E.TQ_ERR_ARG
-    fv_bad = c_format(256, 3, 3, 256)
+    fv_bad = c_format(256, 3, 3, 256, 1)
     assert D(fv=fv_bad) == E.TQ_ERR_SHAPE
-    f2 = c_format(256, 3, 3, 256)
+    assert D(fk=c_format(128, 3, 3, 128, 0)) == E.TQ_ERR_SHAPE   # keys need the QJL term
+    f2 = c_format(256, 3, 3, 256, 1)
     t2, keep2 = _tables(tq.Format(256, 3, 3, 256))
     wsb = tq.search_workspace_bytes(100, 10, 10 ** 6, 256)
     assert wsb > 0
 
-    def S(k=10, n_db=10 ** 6, d_in=200, ws_bytes=wsb):
-        return lib.tq_ip_search(ctypes.byref(f2), ctypes.byref(t2), p, p, n_db, p, d_in, 100, k, p, p,
+    def S(k=10, n_db=10 ** 6, d_in=200, ws_bytes=wsb, f=f2):
+        return lib.tq_ip_search(ctypes.byref(f), ctypes.byref(t2), p, p, n_db, p, d_in, 100, k, p, p,
                                 p, ws_bytes, None)
     assert S(k=0) == E.TQ_ERR_ARG
     assert S(k=65) == E.TQ_ERR_ARG
     assert S(n_db=5) == E.TQ_ERR_ARG
     assert S(d_in=300) == E.TQ_ERR_SHAPE
     assert S(ws_bytes=wsb - 1) == E.TQ_ERR_WORKSPACE
+    assert S(f=c_format(256, 3, 3, 256, 0)) == E.TQ_ERR_SHAPE        # search scores need QJL
 
 
 def test_strerror_names_every_code():

@@ -98,6 +98,19 @@ def test_asymmetric_kv_and_group_sizes(torch_gpu):
     _case(torch_gpu, 1, 16, 2, 600, [600], (128, 1, 1, 128), (128, 1, 1, 128), 4002)    # G = 8
 
 
+def test_mse_only_values(torch_gpu):
+    """Values stored without QJL sign words (MSE-only), keys with them: every value width,
+    the mixed split, group sizes 1 / 2 / 4 / 8, a ragged batch and the Sparse-V gate."""
+    _case(torch_gpu, 2, 32, 8, 1300, [1300, 517], (128, 3, 3, 128), (128, 3, 3, 128, False), 4100)
+    _case(torch_gpu, 1, 8, 8, 700, [700], (128, 3, 3, 128), (128, 2, 2, 128, False), 4101)   # G = 1
+    _case(torch_gpu, 1, 8, 4, 640, [601], (128, 2, 2, 128), (128, 2, 2, 128, False), 4102)   # G = 2
+    _case(torch_gpu, 1, 16, 2, 500, [500], (128, 1, 1, 128), (128, 1, 1, 128, False), 4103)  # G = 8
+    _case(torch_gpu, 2, 32, 8, 900, [900, 0], (128, 3, 2, 64), (128, 3, 2, 64, False), 4104)
+    _, _, skipped = _case(torch_gpu, 1, 32, 8, 4096, [4096], (128, 3, 3, 128),
+                          (128, 3, 3, 128, False), 4105, spikes=0.01, tau=1e-4, atol=5e-3)
+    assert skipped > 0
+
+
 def test_single_head_64_queries(torch_gpu):
     """One KV head, d = 128, 4096 keys/values N(0,1) fp32 with 4 channels x20, 64 queries,
     b = 3 (2-bit codebook + 1 QJL bit): 64 query heads sharing one KV head."""

@@ -61,6 +61,21 @@ def test_bf16_channel_scaled(torch_gpu, fmt_t):
     _check(torch_gpu, x, "bf16", fmt_t, 5)
 
 
+@pytest.mark.parametrize("fmt_t", [(128, 3, 3, 128, False), (128, 1, 1, 128, False),
+                                   (128, 3, 2, 64, False), (128, 2, 1, 96, False)])
+def test_mse_only_formats(torch_gpu, fmt_t):
+    """Records without QJL sign words: same codes and norms as the QJL format, no signs."""
+    kb, vb, _ = TI.kv_layer(1, 2, 700, 128, seed=78)
+    x = np.concatenate([kb.reshape(-1, 128), vb.reshape(-1, 128)])
+    x = x[:1391]                                                   # ragged last tile
+    _check(torch_gpu, x, "bf16", fmt_t, 6)
+
+
+def test_mse_only_d256_padded(torch_gpu):
+    x = TI.search_set(1000, 200, seed=5006)
+    _check(torch_gpu, x, "f32", (256, 3, 3, 256, False), 5501)
+
+
 def test_ragged_and_tiny_sizes(torch_gpu):
     g = TI.gen(3)
     for n in (1, 31, 33, 127, 129, 1000):

@@ -379,3 +379,49 @@ def test_pack_layout_and_round_trip():
     w = O.pack(idx1, sb1, fmt).view("<u4")[0]
     assert list(w[:4]) == [0xFFFFFFFF, 0, 0xFFFFFFFF, 2]
     assert not w[4:].any()
+
+
+# ------------------------------------------------------------------ MSE-only ("PolarQuant alone")
+def test_mse_only_layout_is_the_qjl_layout_without_sign_words():
+    """An MSE-only record holds exactly the code planes of the QJL record, in order: each
+    block's sign word removed (4.25 -> 3.25 bit/value at b = 4 with the norms)."""
+    g = TI.gen(21)
+    for fmt in (O.Format(128, 3, 3, 128), O.Format(128, 3, 2, 64), O.Format(256, 2, 2, 256)):
+        mse = O.Format(fmt.d, fmt.bits_lo, fmt.bits_hi, fmt.split, qjl=False)
+        idx = np.stack([g.integers(0, 1 << fmt.bits_of_block(j // 32), size=40) for j in range(fmt.d)], 1)
+        sbit = g.integers(0, 2, size=(40, fmt.d)).astype(bool)
+        full = O.pack(idx, sbit, fmt).view("<u4").reshape(40, -1)
+        only = O.pack(idx, sbit, mse).view("<u4").reshape(40, -1)
+        keep, k = [], 0
+        for blk in range(fmt.d // 32):
+            B = fmt.bits_of_block(blk)
+            keep += list(range(k, k + B))
+            k += B + 1
+        assert np.array_equal(only, full[:, keep])
+        i2, s2 = O.unpack(O.pack(idx, sbit, mse), mse)
+        assert np.array_equal(i2, idx) and not s2.any()
+    assert O.Format.uniform(128, 3, qjl=False).record_bytes() == 48
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_mse_only_reconstruction_error_is_d_times_codebook_mse(bits):
+    """For unit vectors (n16 = 1 exactly) the MSE-only reconstruction x~ = Pi^T c[idx] has
+    E||x - x~||^2 = d * mse, the codebook's expected squared error per coordinate under the
+    exact marginal (computed in the oracle by quadrature), by Monte Carlo over random unit
+    directions and fresh rotations."""
+    d, n = 128, 4000
+    fmt = O.Format.uniform(d, bits, qjl=False)
+    cb = O.codebook(d, bits)
+    errs = []
+    for rep in range(5):
+        x = TI.gen(300 + rep).standard_normal((n, d))
+        x /= np.linalg.norm(x, axis=1, keepdims=True)
+        signs, S = TI.rotation(d, 900 + rep)
+        q = O.quantize(x, fmt, signs, S, cb)
+        assert np.all(q["n16"] == O.fp16_bits(np.array([1.0]))[0])
+        idx, sb = O.unpack(O.pack(q["idx"], q["sbit"], fmt), fmt)
+        xt = O.dequantize(idx, sb, q["n16"], q["r16"], fmt, signs, S, cb, qjl=False)
+        errs.append(np.sum((x - xt) ** 2, axis=1))
+    e = np.concatenate(errs)
+    se = e.std() / math.sqrt(e.size)
+    assert abs(e.mean() - d * cb.mse) < 4 * se + 1e-3 * d * cb.mse, (e.mean(), d * cb.mse, se)
