@@ -212,7 +212,7 @@ def main():
     flops_launch = 2.0 * D * D * nvec                         # S r per vector
     q_tfs = flops_launch / q_launch / 1e12
     qtoks = NTOK * BATCH * steps / (qk.sum() + qv.sum())
-    trafq = _traffic("compressed_attention_rotate_amd/csrc/tq_quantize.hip",
+    trafq = _traffic("compressed_attention_rotate_amd/csrc/tq_quantize_kernel.h",
                      "quantize_llama8b_32k_traffic.txt")
     trafd = _traffic("compressed_attention_rotate_amd/csrc/tq_decode.hip",
                      "decode_llama8b_32k_traffic.txt")

@@ -1,0 +1,8 @@
+// Quantize kernel instances: d 256 / 2 bits, d 256 / 3 bits (every input type, with and without
+// counters and QJL sign words).
+#include "tq_quantize_kernel.h"
+
+namespace tqk {
+template int launch_quantize<256, 2, 2>(const QParams&, int, bool, hipStream_t, int);
+template int launch_quantize<256, 3, 3>(const QParams&, int, bool, hipStream_t, int);
+}  // namespace tqk
