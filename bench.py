@@ -46,13 +46,17 @@ def _parse():
     return ap.parse_args()
 
 
-def _traffic(kernel_src: str, summary: str):
+def _traffic(kernel_srcs, summary: str):
     """HBM traffic per launch from a committed rocprofv3 --pmc summary, or None when the
-    summary is missing or was taken on a different kernel source."""
+    summary is missing or was taken on different kernel sources (SHA-256 over the listed
+    files' bytes, concatenated in order)."""
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(os.path.join(ROOT, kernel_src), "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for src in kernel_srcs:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    sha = h.hexdigest()
     vals = {}
     for line in open(path):
         if ":" in line:
@@ -95,32 +99,46 @@ def cpu_baseline(kb, vb, qb, signs, S):
             "quantize_tokens_per_s": nt * nh / HKV / (t1 - t0)}
 
 
-def _mse_only_values(tq, torch, dev, v, q, ck, nk, seq, ws, out, fmt_k, tab, signs, S, steps, nvec):
-    """The same layer with the values stored MSE-only (codebook planes and norms, no QJL sign
-    words): quantize time of the value tensor and decode time, timed like the main step."""
-    fmt_v = tq.Format.uniform(D, BITS, qjl=False)
+def _variant(tq, torch, dev, ks, vs, q, seq, ws, out, fmt_k, fmt_v, signs, S, steps, nvec):
+    """The same layer in other packed formats, timed like the main step: SLOTS caches rotate
+    (step i quantizes K and V into slot i and decodes slot i + 1, written SLOTS - 1 steps
+    earlier), HIP events on the launch stream around each launch."""
+    tab_k = tq.Tables(fmt_k, signs, torch.from_numpy(S).to(dev))
     tab_v = tq.Tables(fmt_v, signs, torch.from_numpy(S).to(dev))
-    rb = fmt_v.record_bytes()
-    cv = torch.empty((BATCH, HKV, NTOK, rb), dtype=torch.uint8, device=dev)
-    nv = torch.empty((BATCH, HKV, NTOK, 2), dtype=torch.float16, device=dev)
-    qv = lambda: tq.quantize_kv(v.view(-1, D), fmt_v, tab_v, codes=cv.view(nvec, rb),
-                                norms=nv.view(nvec, 2))
-    dc = lambda: tq.attend_decode(q, ck, nk, cv, nv, seq, fmt_k, tab, fmt_v, tab_v, workspace=ws,
-                                  out=out)
-    for _ in range(3):
-        qv(); dc()
+    rk, rv = fmt_k.record_bytes(), fmt_v.record_bytes()
+    ck = [torch.empty((BATCH, HKV, NTOK, rk), dtype=torch.uint8, device=dev) for _ in range(SLOTS)]
+    cv = [torch.empty((BATCH, HKV, NTOK, rv), dtype=torch.uint8, device=dev) for _ in range(SLOTS)]
+    nk = [torch.empty((BATCH, HKV, NTOK, 2), dtype=torch.float16, device=dev) for _ in range(SLOTS)]
+    nv = [torch.empty_like(x) for x in nk]
+    qk = lambda s: tq.quantize_kv(ks[s].view(-1, D), fmt_k, tab_k, codes=ck[s].view(nvec, rk),
+                                  norms=nk[s].view(nvec, 2))
+    qv = lambda s: tq.quantize_kv(vs[s].view(-1, D), fmt_v, tab_v, codes=cv[s].view(nvec, rv),
+                                  norms=nv[s].view(nvec, 2))
+    dc = lambda s: tq.attend_decode(q, ck[s], nk[s], cv[s], nv[s], seq, fmt_k, tab_k, fmt_v, tab_v,
+                                    workspace=ws, out=out)
+    for s in range(SLOTS):
+        qk(s); qv(s)
+    for i in range(3):
+        qk(i % SLOTS); qv(i % SLOTS); dc((i + 1) % SLOTS)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for k in range(steps):
-        ev[k][0].record(); qv(); ev[k][1].record(); dc(); ev[k][2].record()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(); qk(i % SLOTS); e[1].record(); qv(i % SLOTS); e[2].record()
+        dc((i + 1) % SLOTS); e[3].record()
     torch.cuda.synchronize()
-    tq_s = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    td_s = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-    nbytes = nvec * (fmt_k.record_bytes() + 4) + nvec * (rb + 4)
-    return {"format_v": f"{BITS}-bit codebook, no QJL ({rb} B/vector)",
-            "quantize_v_us": round(float(tq_s) * 1e6, 3),
-            "decode_us": round(float(td_s) * 1e6, 3),
-            "decode_gbs": round(nbytes / td_s / 1e9, 2)}
+    t_qk = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_qv = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    t_dc = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    nbytes = nvec * (rk + 4) + nvec * (rv + 4)
+    desc = lambda f: (f"{f.bits_lo}-bit codebook" if f.bits_lo == f.bits_hi else
+                      f"{f.bits_lo}/{f.bits_hi}-bit codebook split at {f.split}") + \
+        (" + 1 QJL bit" if f.qjl else ", MSE-only") + f" ({f.record_bytes()} B/vector)"
+    return {"format_k": desc(fmt_k), "format_v": desc(fmt_v),
+            "quantize_k_us": round(float(t_qk) * 1e6, 3),
+            "quantize_v_us": round(float(t_qv) * 1e6, 3),
+            "decode_us": round(float(t_dc) * 1e6, 3),
+            "decode_gbs": round(nbytes / t_dc / 1e9, 2)}
 
 
 def main():
@@ -212,9 +230,10 @@ def main():
     flops_launch = 2.0 * D * D * nvec                         # S r per vector
     q_tfs = flops_launch / q_launch / 1e12
     qtoks = NTOK * BATCH * steps / (qk.sum() + qv.sum())
-    trafq = _traffic("compressed_attention_rotate_amd/csrc/tq_quantize_kernel.h",
+    trafq = _traffic(["compressed_attention_rotate_amd/csrc/tq_quantize_kernel.h"],
                      "quantize_llama8b_32k_traffic.txt")
-    trafd = _traffic("compressed_attention_rotate_amd/csrc/tq_decode.hip",
+    trafd = _traffic(["compressed_attention_rotate_amd/csrc/tq_decode_kernel.h",
+                      "compressed_attention_rotate_amd/csrc/tq_decode.hip"],
                      "decode_llama8b_32k_traffic.txt")
 
     line = {
@@ -245,8 +264,13 @@ def main():
                             "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": trafd},
     }
-    line["mse_only_values"] = _mse_only_values(tq, torch, dev, vs[0], q, codes_k[0], norms_k[0],
-                                               seq, ws, out, fmt, tab, signs, S, steps, nvec)
+    # other formats of the same layer (not part of `value`)
+    line["variants"] = {
+        name: _variant(tq, torch, dev, ks, vs, q, seq, ws, out, fk, fv, signs, S, steps, nvec)
+        for name, fk, fv in (
+            ("b4_k_mse_only_v", fmt, tq.Format.uniform(D, BITS, qjl=False)),
+            ("b3.5_kv", tq.Format(D, 3, 2, 64), tq.Format(D, 3, 2, 64)),
+            ("b2.5_kv", tq.Format(D, 2, 1, 64), tq.Format(D, 2, 1, 64)))}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(kb, vb, qb, signs, S)
     print(json.dumps(line), flush=True)

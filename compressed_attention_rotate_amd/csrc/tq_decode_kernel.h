@@ -1,0 +1,701 @@
+// Decode attention straight from the packed cache (163.com explainer,
+// m.163.com/dy/article/KOV7P8JI0556C3J2, sections "第二步：QJL" and "速度"):
+//   logit_t = scale * ( n16_t <q_rot, c[idx_t]> + gamma r16_t <S q_rot, 2 sigma_t - 1> ),
+//   q_rot = H D q / sqrt(d), gamma = sqrt(pi/2) / d;
+//   softmax over t < seq_len; out = Pi^T ( sum_t p_t (n16 c[idx] + gamma r16 S^T sigma) ).
+// Because <q, Pi^T v> = <Pi q, v> and <q_rot, S^T s> = <S q_rot, s>, the cache is never
+// rotated back per token: values are accumulated in the rotated domain and each head's
+// result is mapped back once (S^T, then D H / sqrt(d)).
+//
+// Two launches:
+//   scan:     grid (split, batch * KV head * chunk of GC query heads), about one
+//             workgroup of 8 waves per CU.  The workgroup first derives its own query
+//             tables (while its first cache tile is in flight): q_rot of the GC
+//             heads (FWHT over the wave), S q_rot (S rows from L2), and in LDS
+//               Tq[g][m] = sum of q_rot over the set bits of byte m of coordinate group g
+//               Ts[g][n] = 2 * sum of S q_rot over the set bits of nibble n,
+//             one float per head.  A sign dot product <w, 2b - 1> over 128 coordinates is
+//             then 16 byte (or 32 nibble) table reads: the codebook term through the Walsh
+//             expansion of the symmetric codebook, c[idx] = sum_S alpha_S prod_{k in S}
+//             (2 b_k - 1) over odd subsets S of the code bit-planes (the planes, and for
+//             3 bits their XOR), the QJL term directly.
+//             Keys: lane = token, records of the wave's next 64-token tile prefetched into
+//             registers.  Online softmax per head with wavefront reductions; the Sparse-V
+//             gate (zhidx turboquant_plus article, section "01 turboquant_plus：介绍与详解")
+//             drops a value row for a head when its running weight estimate is below tau,
+//             and skips reading rows dropped by every head.  Values: each lane owns 4
+//             coordinates, the two half-waves take alternate kept tokens; the centroid
+//             pair of two coordinates comes from one read of a table indexed by their
+//             code bits; fp32 accumulation of w n16 c[idx] and w gamma r16 sigma per head.
+//             The waves' partial (m, l, acc) are merged in LDS: one partial per workgroup.
+//             MSE-only values (no sign words) drop the QJL term of the value sum.
+//   combine:  per (batch, query head) one workgroup merges the splits in a fixed order and
+//             maps back: out = D H (A + S^T Q) / (sqrt(d) l).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tqk {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;
+constexpr int kNB = kD / 32;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 64;
+constexpr int kPartFloats = 2 + 2 * kD;  // m (log2 domain), l, A[d], Q[d]
+constexpr float kLog2e = 1.4426950408889634f;
+
+__host__ __device__ constexpr int round4(int x) { return (x + 3) / 4 * 4; }
+
+// Record layout of a format with SPLITB blocks of BLO bits then blocks of BHI bits; each
+// block holds its code planes and, when Q is 1, one QJL sign word.
+template <int BLO, int BHI, int SPLITB, int Q = 1>
+struct Rec {
+  static constexpr int W = SPLITB * (BLO + Q) + (kNB - SPLITB) * (BHI + Q);  // words
+  static constexpr int VEC = (W % 4 == 0) ? 4 : ((W % 2 == 0) ? 2 : 1);      // load width
+  static constexpr int bits(int blk) { return blk < SPLITB ? BLO : BHI; }
+  __host__ __device__ static constexpr int off(int blk) {
+    return blk < SPLITB ? blk * (BLO + Q) : SPLITB * (BLO + Q) + (blk - SPLITB) * (BHI + Q);
+  }
+};
+
+template <int W, int VEC>
+__device__ __forceinline__ void load_record(const uint32_t* rec, uint32_t (&w)[W]) {
+  if constexpr (VEC == 4) {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const u32x4 v = reinterpret_cast<const u32x4*>(rec)[i];
+      w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
+    }
+  } else if constexpr (VEC == 2) {
+#pragma unroll
+    for (int i = 0; i < W / 2; ++i) {
+      const u32x2 v = reinterpret_cast<const u32x2*>(rec)[i];
+      w[2 * i] = v[0]; w[2 * i + 1] = v[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = rec[i];
+  }
+}
+
+// Entries of the centroid-pair table of a B-bit codebook.  A lane's 4 coordinates have
+// code-bit nibbles b0, b1, b2 (one per plane); f = b0 << 1 | b1 << 5 | b2 << 9 holds
+// the 2-bit fields of coordinates (2, 3) at bits 3-4, 7-8, 11-12, so (f & 0x1998) is 8
+// times the sparse pattern P = p0 | p1 << 4 | p2 << 8 of that coordinate pair, and
+// ((f << 2) & 0x1998) the same for coordinates (0, 1).  Entry P = (c[lo], c[hi]).
+__host__ __device__ constexpr int pat_entries(int B) { return B == 3 ? 0x334 : (B == 2 ? 0x34 : 4); }
+constexpr uint32_t kPatMask = 0x1998u;
+
+struct DecodeParams {
+  const void* q;
+  const uint32_t* codes_k;
+  const uint32_t* norms_k;
+  const uint32_t* codes_v;
+  const uint32_t* norms_v;
+  const int32_t* seq_lens;
+  const float* S_k;
+  const float* S_v;
+  float* out;
+  float* logits;
+  unsigned long long* skipped;
+  float* ws_part;   // [batch*hq][n_split][kPartFloats]
+  int64_t capacity;
+  int64_t tokens_per_split;
+  int32_t batch, hq, hkv, group, q_dtype, n_split;
+  float scale, tau, gamma;
+  uint32_t sign_k[4], sign_v[4];
+  float alpha_k[2][4];  // Walsh coefficients of the key codebooks (lo, hi parts)
+  float cent_v[2][8];   // value codebooks (lo, hi)
+  int32_t ksplitb;
+};
+
+// LDS layout of one scan workgroup (floats).
+template <int GC, int VW, int BVLO, int BVHI, int VSPLIT>
+struct ScanLds {
+  static constexpr int kTq = 16 * 256 * GC;   // [16 byte groups][256][GC]
+  static constexpr int kTs = 32 * 16 * GC;    // [32 nibble groups][16][GC]
+  static constexpr int kCpLo = round4(2 * pat_entries(BVLO));
+  static constexpr int kCpHi = VSPLIT < kNB ? round4(2 * pat_entries(BVHI)) : 0;
+  static constexpr int kSp = 16 * 4;
+  static constexpr int kW0 = 2 * GC <= 4 ? 4 : 8;        // row: u[GC], u'[GC] | value record
+  static constexpr int kRS = round4(kW0 + VW);           // row stride (words)
+  static constexpr int kArea = (kTile + 1) * kRS + 4;    // 64 token rows + zero row + pad
+  // small tables first so their reads use the instruction's immediate offset
+  static constexpr int oCpLo = 0, oCpHi = oCpLo + kCpLo, oSp = oCpHi + kCpHi, oTs = oSp + kSp;
+  static constexpr int oCc = oTs + kTs;                   // [2][GC] per-head constants
+  static constexpr int oTq = oCc + round4(2 * GC), oArea = oTq + kTq;
+  static constexpr int kTotal = oArea + kWaves * kArea;
+  static constexpr int kMerge = round4(2 * GC) + 2 * kD * GC;  // per wave
+  static constexpr int oWM = oTq;  // the waves' partials after the scan (aliases Tq)
+  static_assert(kWaves * kMerge <= kTq, "merge area must fit in the byte tables");
+  static_assert(2 * GC * kD + 16 * 2 * 16 * GC + 16 <= kWaves * kArea, "setup scratch must fit");
+};
+
+template <int GC>
+__device__ __forceinline__ void table_read(const float* T, int idx, float (&out)[GC]) {
+  if constexpr (GC == 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(T + 4 * idx);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  } else if constexpr (GC == 2) {
+    const f32x2 v = *reinterpret_cast<const f32x2*>(T + 2 * idx);
+    out[0] = v[0]; out[1] = v[1];
+  } else {
+    out[0] = T[idx];
+  }
+}
+
+// Value of lane (lane ^ 32): v_permlane32_swap exchanges the two half-waves.
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((lane_id() & 32) ? r[0] : r[1]);
+}
+
+template <int M>
+__device__ __forceinline__ float hbfly(float x, int lane) {  // lower lane a + b, upper a - b
+  const float t = (M == 32) ? other_half(x) : xchg<(M < 32 ? M : 1)>(x);
+  return (lane & M) ? t - x : x + t;
+}
+
+// Unnormalized natural-order Walsh-Hadamard transform of 128 values held by one wave as
+// v[0] = x[lane], v[1] = x[lane + 64].
+__device__ __forceinline__ void fwht128(float (&v)[2], int lane) {
+  {
+    const float a = v[0], c = v[1];
+    v[0] = a + c;
+    v[1] = a - c;
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    float x = v[e];
+    x = hbfly<1>(x, lane);
+    x = hbfly<2>(x, lane);
+    x = hbfly<4>(x, lane);
+    x = hbfly<8>(x, lane);
+    x = hbfly<16>(x, lane);
+    x = hbfly<32>(x, lane);
+    v[e] = x;
+  }
+}
+
+// acc += alpha * (byte-table reads of one 32-bit plane word, byte groups g0 .. g0+3); the
+// four reads are summed pairwise first so every read is consumed right away.
+template <int GC>
+__device__ __forceinline__ void lut_byte(const float* Tq, int g0, uint32_t w, float alpha,
+                                         float (&acc)[GC]) {
+  float t0[GC], t1[GC], t2[GC], t3[GC];
+  table_read<GC>(Tq, (g0 + 0) * 256 + (w & 0xFFu), t0);
+  table_read<GC>(Tq, (g0 + 1) * 256 + ((w >> 8) & 0xFFu), t1);
+  table_read<GC>(Tq, (g0 + 2) * 256 + ((w >> 16) & 0xFFu), t2);
+  table_read<GC>(Tq, (g0 + 3) * 256 + (w >> 24), t3);
+#pragma unroll
+  for (int h = 0; h < GC; ++h) acc[h] = fmaf(alpha, (t0[h] + t1[h]) + (t2[h] + t3[h]), acc[h]);
+}
+
+// acc += nibble-table reads of one 32-bit sign word (nibble groups g0 .. g0+7), summed as
+// a tree.
+template <int GC>
+__device__ __forceinline__ void lut_nib(const float* Ts, int g0, uint32_t w, float (&acc)[GC]) {
+  float t[8][GC];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) table_read<GC>(Ts, (g0 + i) * 16 + ((w >> (4 * i)) & 0xFu), t[i]);
+#pragma unroll
+  for (int h = 0; h < GC; ++h)
+    acc[h] += ((t[0][h] + t[1][h]) + (t[2][h] + t[3][h])) + ((t[4][h] + t[5][h]) + (t[6][h] + t[7][h]));
+}
+
+// VQ: the value records carry QJL sign words (else MSE-only values: no residual term).
+template <int BKLO, int BKHI, int KSPLIT, int BVLO, int BVHI, int VSPLIT, bool VQ, int GC>
+__global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
+  using KR = Rec<BKLO, BKHI, KSPLIT>;
+  using VR = Rec<BVLO, BVHI, VSPLIT, VQ ? 1 : 0>;
+  constexpr int KW = KR::W, VW = VR::W;
+  using L = ScanLds<GC, VW, BVLO, BVHI, VSPLIT>;
+  constexpr int kW0 = L::kW0, kRS = L::kRS;
+  __shared__ __attribute__((aligned(16))) float lds[L::kTotal];
+  float* Tq = lds + L::oTq;
+  float* Ts = lds + L::oTs;
+  float* cpLo = lds + L::oCpLo;
+  float* cpHi = lds + L::oCpHi;
+  float* spat = lds + L::oSp;
+  float* cconst = lds + L::oCc;  // [2][GC]: codebook-term and QJL-term constants per head
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
+  const int nchunk = p.group / GC;
+  const int unit = blockIdx.y;
+  const int chunk = unit % nchunk;
+  const int bk = unit / nchunk;  // b * hkv + kv head
+  const int b = bk / p.hkv;
+  const int h0 = (bk % p.hkv) * p.group + chunk * GC;
+  const int64_t seq = p.seq_lens[b];
+  const int64_t t_begin = (int64_t)blockIdx.x * p.tokens_per_split;
+  int64_t t_end = t_begin + p.tokens_per_split;
+  if (t_end > seq) t_end = seq;
+  const int64_t kv_base = (int64_t)bk * p.capacity;
+  const bool gated = p.tau > 0.0f;
+
+  // ---- register prefetch of one tile: key record, value record, norms
+  uint32_t kw[KW], vwr[VW], knr = 0, vnr = 0;
+  auto fetch = [&](int64_t tt0) {
+    const int64_t t = tt0 + lane;
+    if (tt0 < t_end && t < t_end) {
+      load_record<KW, KR::VEC>(p.codes_k + (kv_base + t) * KW, kw);
+      if (!gated) load_record<VW, VR::VEC>(p.codes_v + (kv_base + t) * VW, vwr);
+      knr = p.norms_k[kv_base + t];
+      vnr = p.norms_v[kv_base + t];
+    }
+  };
+  int64_t t0 = t_begin + (int64_t)wave * kTile;
+
+  // ---- query tables
+  float* qs = lds + L::oArea;             // [2][GC][kD]: q_rot, S q_rot (setup scratch)
+  float* nibq = qs + 2 * GC * kD;         // [16 groups][2 halves][16][GC]
+  const int srow = tid >> 2, sq4 = tid & 3;
+  f32x4 sr[8];  // S_k[srow][32 sq4 .. 32 sq4 + 31]
+  {
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.S_k + (int64_t)srow * kD + 32 * sq4);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sr[c] = src[c];
+  }
+
+  float* cents = qs + 2 * GC * kD + 16 * 2 * 16 * GC;  // [2][8] value codebooks
+  if (tid == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      cents[k] = p.cent_v[0][k];
+      cents[8 + k] = p.cent_v[1][k];
+    }
+  }
+  if (wave < GC) {  // q_rot of head h0 + wave
+    float v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = lane + 64 * e;
+      float x = load_elem(p.q, ((int64_t)b * p.hq + h0 + wave) * kD + j, p.q_dtype);
+      const uint32_t sw = (lane & 32) ? uniform_u32(p.sign_k[2 * e + 1]) : uniform_u32(p.sign_k[2 * e]);
+      if ((sw >> (j & 31)) & 1u) x = -x;
+      v[e] = x;
+    }
+    fwht128(v, lane);
+    const float isd = 1.0f / sqrtf((float)kD);
+    qs[wave * kD + lane] = v[0] * isd;
+    qs[wave * kD + lane + 64] = v[1] * isd;
+  }
+  // the first tile is requested only now: waits on the S and q loads above must not also
+  // wait for it (vector-memory counters complete in issue order)
+  fetch(t0);
+  __syncthreads();
+  {  // S q_rot: thread (row srow, quarter sq4) sums 32 columns, then the 4 quarter lanes
+    float acc[GC];
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+      float s = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + h * kD + 32 * sq4 + 4 * c);
+        s = fmaf(sr[c][0], qv[0], s);
+        s = fmaf(sr[c][1], qv[1], s);
+        s = fmaf(sr[c][2], qv[2], s);
+        s = fmaf(sr[c][3], qv[3], s);
+      }
+      s += xchg<1>(s);
+      s += xchg<2>(s);
+      acc[h] = s;
+    }
+    if (sq4 == 0) {
+#pragma unroll
+      for (int h = 0; h < GC; ++h) qs[(GC + h) * kD + srow] = acc[h];
+    }
+  }
+  __syncthreads();
+  if (wave < GC) {  // constants: codebook term (sum_k alpha_k) sum_j q_j per block; sum S q
+    const int h = wave;
+    float asum[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      asum[0] += p.alpha_k[0][k];
+      asum[1] += p.alpha_k[1][k];
+    }
+    const int blk0 = lane >> 5, blk1 = 2 + (lane >> 5);  // blocks of j = lane, lane + 64
+    const float v = (blk0 < p.ksplitb ? asum[0] : asum[1]) * qs[h * kD + lane] +
+                    (blk1 < p.ksplitb ? asum[0] : asum[1]) * qs[h * kD + lane + 64];
+    const float cq = wave_sum_fast(v);
+    const float ws = wave_sum_fast(qs[(GC + h) * kD + lane] + qs[(GC + h) * kD + lane + 64]);
+    if (lane == 0) {
+      cconst[h] = cq;
+      cconst[GC + h] = ws;
+    }
+  }
+  static_assert((16 * 2 * 16 * GC) % kThreads == 0 && (16 * 256) % kThreads == 0, "setup split");
+  float nibsum_q[16 * 2 * 16 * GC / kThreads], nibsum_s[32 * 16 * GC / kThreads];
+#pragma unroll
+  for (int r = 0; r < 16 * 2 * 16 * GC / kThreads; ++r) {  // nibble sums of q_rot
+    // (all reads of an entry before its write: the write may alias later reads for the
+    // compiler, which would otherwise serialize every round trip)
+    const int i = tid + r * kThreads;
+    const int h = i % GC, n = (i / GC) % 16, half = (i / (16 * GC)) % 2, g = i / (32 * GC);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(qs + h * kD + 8 * g + 4 * half);
+    nibsum_q[r] = ((n & 1) ? x[0] : 0.0f) + ((n & 2) ? x[1] : 0.0f) + ((n & 4) ? x[2] : 0.0f) +
+                  ((n & 8) ? x[3] : 0.0f);
+  }
+#pragma unroll
+  for (int r = 0; r < 32 * 16 * GC / kThreads; ++r) {  // Ts: 2 * nibble sums of S q_rot
+    const int i = tid + r * kThreads;
+    const int h = i % GC, n = (i / GC) % 16, g = i / (16 * GC);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(qs + (GC + h) * kD + 4 * g);
+    nibsum_s[r] = 2.0f * (((n & 1) ? x[0] : 0.0f) + ((n & 2) ? x[1] : 0.0f) +
+                          ((n & 4) ? x[2] : 0.0f) + ((n & 8) ? x[3] : 0.0f));
+  }
+#pragma unroll
+  for (int r = 0; r < 16 * 2 * 16 * GC / kThreads; ++r) nibq[tid + r * kThreads] = nibsum_q[r];
+#pragma unroll
+  for (int r = 0; r < 32 * 16 * GC / kThreads; ++r) Ts[tid + r * kThreads] = nibsum_s[r];
+  constexpr int kPat = pat_entries(BVLO) + (VSPLIT < kNB ? pat_entries(BVHI) : 0);
+#pragma unroll
+  for (int r = 0; r < (kPat + kThreads - 1) / kThreads; ++r) {
+    const int i = tid + r * kThreads;
+    if (i >= kPat) break;
+    const bool hi = i >= pat_entries(BVLO);
+    const int P = hi ? i - pat_entries(BVLO) : i;
+    const int nb = hi ? BVHI : BVLO;
+    const int mask = (1 << nb) - 1;
+    const int p0 = P & 15, p1 = (P >> 4) & 15, p2 = (P >> 8) & 15;
+    const int ilo = ((p0 & 1) | ((p1 & 1) << 1) | ((p2 & 1) << 2)) & mask;
+    const int ihi = (((p0 >> 1) & 1) | (((p1 >> 1) & 1) << 1) | (((p2 >> 1) & 1) << 2)) & mask;
+    float* dst = hi ? cpHi : cpLo;
+    dst[2 * P] = cents[(hi ? 8 : 0) + ilo];
+    dst[2 * P + 1] = cents[(hi ? 8 : 0) + ihi];
+  }
+  if (tid < 64) spat[tid] = ((tid >> 2) >> (tid & 3)) & 1 ? 1.0f : -1.0f;
+  __syncthreads();
+  float tq_v[16 * 256 / kThreads][GC];
+#pragma unroll
+  for (int r = 0; r < 16 * 256 / kThreads; ++r) {  // byte tables from nibble sums
+    const int i = tid + r * kThreads;
+    const int g = i >> 8, m = i & 255;
+    float lo[GC], hi[GC];
+    table_read<GC>(nibq + ((g * 2 + 0) * 16) * GC, m & 15, lo);
+    table_read<GC>(nibq + ((g * 2 + 1) * 16) * GC, m >> 4, hi);
+#pragma unroll
+    for (int h = 0; h < GC; ++h) tq_v[r][h] = lo[h] + hi[h];
+  }
+#pragma unroll
+  for (int r = 0; r < 16 * 256 / kThreads; ++r) {
+    const int i = tid + r * kThreads;
+    if constexpr (GC == 4) {
+      *reinterpret_cast<f32x4*>(Tq + i * 4) = f32x4{tq_v[r][0], tq_v[r][1], tq_v[r][2], tq_v[r][3]};
+    } else {
+#pragma unroll
+      for (int h = 0; h < GC; ++h) Tq[i * GC + h] = tq_v[r][h];
+    }
+  }
+  __syncthreads();
+
+  float cq[GC], wsum[GC];
+#pragma unroll
+  for (int h = 0; h < GC; ++h) {
+    cq[h] = cconst[h];
+    wsum[h] = cconst[GC + h];
+  }
+  float alo[4], ahi[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    alo[k] = 2.0f * p.alpha_k[0][k];
+    ahi[k] = 2.0f * p.alpha_k[1][k];
+  }
+
+  // ---- per-wave area: 64 token rows + one all-zero row used to pad odd token counts.
+  // Row bases are kept opaque to the compiler so that row and field offsets fold into the
+  // LDS instructions' 16-bit immediate instead of being re-added per access.
+  int area_off = L::oArea + wave * L::kArea;
+  asm volatile("" : "+v"(area_off));
+  float* area = lds + area_off;
+  for (int i = lane; i < kRS + 4; i += 64) area[kTile * kRS + i] = 0.0f;
+  // value lane mapping: half-wave hw takes alternate tokens; lane owns coordinates
+  // 4 c4 .. 4 c4 + 3 of block vblk, bits vbit .. vbit + 3 of its plane words
+  const int hw = lane >> 5, c4 = lane & 31;
+  const int vblk = c4 >> 3, vbit = 4 * (c4 & 7);
+  const bool vlo = vblk < VSPLIT;
+  const int vnb = vlo ? BVLO : BVHI;
+  const int voff = kW0 + VR::off(vblk);
+  const char* cpb = reinterpret_cast<const char*>(vlo ? cpLo : cpHi);
+  const char* spb = reinterpret_cast<const char*>(spat);
+
+  float m_run[GC], l_run[GC], am[GC][4], aq[GC][4];
+#pragma unroll
+  for (int h = 0; h < GC; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) am[h][k] = aq[h][k] = 0.0f;
+  }
+  unsigned long long n_skipped = 0;
+  const float kscale = p.scale * kLog2e;
+
+  // one value row (this lane's 4 coordinates) accumulated with the row's weights
+  auto value_row = [&](const float* r) {
+    const uint32_t* rw = reinterpret_cast<const uint32_t*>(r) + voff;
+    uint32_t p0, p1 = 0, p2 = 0, sg = 0;
+    if constexpr (!VQ) {
+      p0 = rw[0];
+      if constexpr (BVLO >= 2 || BVHI >= 2) p1 = vnb >= 2 ? rw[1] : 0u;
+      if constexpr (BVLO == 3 || BVHI == 3) p2 = vnb == 3 ? rw[2] : 0u;
+    } else if constexpr (BVLO == 3 && BVHI == 3) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(rw);
+      p0 = x[0]; p1 = x[1]; p2 = x[2]; sg = x[3];
+    } else {
+      const uint32_t x0 = rw[0], x1 = rw[1], x2 = rw[2], x3 = rw[3];
+      p0 = x0;
+      p1 = vnb >= 2 ? x1 : 0u;
+      p2 = vnb == 3 ? x2 : 0u;
+      sg = vnb == 3 ? x3 : (vnb == 2 ? x2 : x1);
+    }
+    const uint32_t f = (__builtin_amdgcn_ubfe(p0, vbit, 4) << 1) |
+                       (__builtin_amdgcn_ubfe(p1, vbit, 4) << 5) |
+                       (__builtin_amdgcn_ubfe(p2, vbit, 4) << 9);
+    const f32x2 cA = *reinterpret_cast<const f32x2*>(cpb + ((f << 2) & kPatMask));
+    const f32x2 cB = *reinterpret_cast<const f32x2*>(cpb + (f & kPatMask));
+    float u[GC];
+    table_read<GC>(r, 0, u);
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+      am[h][0] = fmaf(u[h], cA[0], am[h][0]);
+      am[h][1] = fmaf(u[h], cA[1], am[h][1]);
+      am[h][2] = fmaf(u[h], cB[0], am[h][2]);
+      am[h][3] = fmaf(u[h], cB[1], am[h][3]);
+    }
+    if constexpr (VQ) {
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(spb + 16 * __builtin_amdgcn_ubfe(sg, vbit, 4));
+      float u2[GC];
+      table_read<GC>(r + GC, 0, u2);
+#pragma unroll
+      for (int h = 0; h < GC; ++h) {
+        aq[h][0] = fmaf(u2[h], sv[0], aq[h][0]);
+        aq[h][1] = fmaf(u2[h], sv[1], aq[h][1]);
+        aq[h][2] = fmaf(u2[h], sv[2], aq[h][2]);
+        aq[h][3] = fmaf(u2[h], sv[3], aq[h][3]);
+      }
+    }
+  };
+
+  for (; t0 < t_end; t0 += (int64_t)kWaves * kTile) {
+    const int64_t t = t0 + lane;
+    const bool valid = t < t_end;
+    uint32_t w[KW], vrec[VW];
+#pragma unroll
+    for (int i = 0; i < KW; ++i) w[i] = kw[i];
+#pragma unroll
+    for (int i = 0; i < VW; ++i) vrec[i] = vwr[i];
+    const uint32_t kn = knr, vn = vnr;
+    fetch(t0 + (int64_t)kWaves * kTile);
+    // ---------------- keys: lane = token
+    float mse[GC], qjl[GC];
+#pragma unroll
+    for (int h = 0; h < GC; ++h) mse[h] = qjl[h] = 0.0f;
+#pragma unroll
+    for (int blk = 0; blk < kNB; ++blk) {
+      const uint32_t* wb = w + KR::off(blk);
+      const int nb = blk < KSPLIT ? BKLO : BKHI;
+      const float* al = blk < KSPLIT ? alo : ahi;
+      lut_byte<GC>(Tq, 4 * blk, wb[0], al[0], mse);
+      if (nb >= 2) lut_byte<GC>(Tq, 4 * blk, wb[1], al[1], mse);
+      if (nb >= 3) {
+        lut_byte<GC>(Tq, 4 * blk, wb[2], al[2], mse);
+        lut_byte<GC>(Tq, 4 * blk, wb[0] ^ wb[1] ^ wb[2], al[3], mse);
+      }
+      lut_nib<GC>(Ts, 8 * blk, wb[nb], qjl);
+    }
+    const float n16 = f16_bits_to_f32(kn), r16 = f16_bits_to_f32(kn >> 16);
+    float est[GC], lg[GC];
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+      est[h] = n16 * (mse[h] - cq[h]) + p.gamma * r16 * (qjl[h] - wsum[h]);
+      lg[h] = valid ? est[h] * kscale : -INFINITY;  // log2 domain
+    }
+    if (p.logits && valid) {
+#pragma unroll
+      for (int h = 0; h < GC; ++h)
+        p.logits[((int64_t)b * p.hq + h0 + h) * p.capacity + t] = est[h] * p.scale;
+    }
+    // ---------------- online softmax (per head, wavefront reductions)
+    const float vn16 = f16_bits_to_f32(vn), vr16 = f16_bits_to_f32(vn >> 16);
+    bool any_keep = false;
+    float u[GC], u2[GC];
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+      const float mt = wave_max_fast(lg[h]);
+      const float mn = fmaxf(m_run[h], mt);
+      const float corr = (m_run[h] == -INFINITY) ? 0.0f : exp2f(m_run[h] - mn);
+      float wgt = valid ? exp2f(lg[h] - mn) : 0.0f;
+      l_run[h] = l_run[h] * corr + wave_sum_fast(wgt);
+      m_run[h] = mn;
+      wgt = (gated && wgt < p.tau * l_run[h]) ? 0.0f : wgt;
+      any_keep |= wgt > 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        am[h][k] *= corr;
+        aq[h][k] *= corr;
+      }
+      u[h] = wgt * vn16;
+      u2[h] = wgt * p.gamma * vr16;
+    }
+    const uint64_t keep = __ballot(any_keep);
+    n_skipped += (unsigned long long)__popcll(__ballot(valid) & ~keep);
+    // this token's row: weights, then the value record (read only when kept if gated)
+    {
+      int own = area_off + lane * kRS;
+      asm volatile("" : "+v"(own));
+      float* row = lds + own;
+      if constexpr (GC == 4) {
+        *reinterpret_cast<f32x4*>(row) = f32x4{u[0], u[1], u[2], u[3]};
+        if constexpr (VQ) *reinterpret_cast<f32x4*>(row + 4) = f32x4{u2[0], u2[1], u2[2], u2[3]};
+      } else {
+#pragma unroll
+        for (int h = 0; h < GC; ++h) {
+          row[h] = u[h];
+          if constexpr (VQ) row[GC + h] = u2[h];
+        }
+      }
+      if (any_keep) {
+        if (gated) load_record<VW, VR::VEC>(p.codes_v + (kv_base + t) * VW, vrec);
+        uint32_t* rv = reinterpret_cast<uint32_t*>(row + kW0);
+#pragma unroll
+        for (int i = 0; i < VW; ++i) rv[i] = vrec[i];
+      }
+    }
+    // ---------------- values: half-wave hw takes every other kept token
+    if (keep == ~0ull) {
+      int roff = area_off + hw * kRS;
+      asm volatile("" : "+v"(roff));
+      const float* r = lds + roff;
+#pragma unroll 4
+      for (int s = 0; s < kTile / 2; ++s) value_row(r + 2 * s * kRS);
+    } else {
+      uint64_t kk = keep;
+      while (kk) {
+        const int ta = __builtin_ctzll(kk);
+        kk &= kk - 1;
+        int tb = kTile;
+        if (kk) {
+          tb = __builtin_ctzll(kk);
+          kk &= kk - 1;
+        }
+        value_row(area + (hw ? tb : ta) * kRS);
+      }
+    }
+  }
+  // ---------------- workgroup epilogue: the half-waves, then the waves' partials are
+  // merged in LDS (aliases Tq) and stored at device scope
+#pragma unroll
+  for (int h = 0; h < GC; ++h)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      am[h][k] += other_half(am[h][k]);
+      aq[h][k] += other_half(aq[h][k]);
+    }
+  __syncthreads();
+  float* mine = lds + L::oWM + wave * L::kMerge;  // [2*GC] m, l | [GC][2][kD]
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+      mine[h] = m_run[h];
+      mine[GC + h] = l_run[h];
+    }
+  }
+  if (lane < 32) {
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+      float* a = mine + round4(2 * GC) + h * 2 * kD + 4 * c4;
+      *reinterpret_cast<f32x4*>(a) = f32x4{am[h][0], am[h][1], am[h][2], am[h][3]};
+      *reinterpret_cast<f32x4*>(a + kD) = f32x4{aq[h][0], aq[h][1], aq[h][2], aq[h][3]};
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < (GC * 2 * kD + kThreads - 1) / kThreads; ++r) {
+    const int i = tid + r * kThreads;
+    if (i >= GC * 2 * kD) break;
+    const int h = i / (2 * kD), k = i % (2 * kD);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, lds[L::oWM + w2 * L::kMerge + h]);
+    float acc = 0.0f, lsum = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2) {
+        const float* o = lds + L::oWM + w2 * L::kMerge;
+        if (o[h] == -INFINITY) continue;
+        const float sc = exp2f(o[h] - M);
+        acc = fmaf(o[round4(2 * GC) + h * 2 * kD + k], sc, acc);
+        lsum = fmaf(o[GC + h], sc, lsum);
+      }
+    }
+    float* part = p.ws_part + (((int64_t)b * p.hq + h0 + h) * p.n_split + blockIdx.x) * kPartFloats;
+    part[2 + k] = acc;
+    if (k == 0) {
+      part[0] = M;
+      part[1] = lsum;
+    }
+  }
+  if (p.skipped) {
+    const unsigned long long tot = n_skipped;  // wave-uniform
+    if (lane == 0 && tot) atomicAdd(p.skipped, tot);
+  }
+}
+
+template <int BKLO, int BKHI, int KS, int BVLO, int BVHI, int VS, bool VQ, int GC>
+static int launch_scan(const DecodeParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, VQ, GC>), grid, dim3(kThreads), 0,
+                     stream, p);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+// Launches the scan of one (key format, value format) pair, split given in blocks of 32
+// (4 = one width); instantiated in the tq_decode_*.hip translation units.
+template <int BKLO, int BKHI, int KS, int BVLO, int BVHI, int VS>
+int launch_pair(const DecodeParams& p, bool vq, int gc, dim3 grid, hipStream_t s) {
+  if (gc == 4) return vq ? launch_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, true, 4>(p, grid, s)
+                         : launch_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, false, 4>(p, grid, s);
+  if (gc == 2) return vq ? launch_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, true, 2>(p, grid, s)
+                         : launch_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, false, 2>(p, grid, s);
+  return vq ? launch_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, true, 1>(p, grid, s)
+            : launch_scan<BKLO, BKHI, KS, BVLO, BVHI, VS, false, 1>(p, grid, s);
+}
+
+// Supported (key format, value format) pairs as (key bits below / above the split, key split
+// in blocks, value bits below / above, value split).  Values may be stored with or without
+// QJL sign words; keys carry them.
+#define TQ_DECODE_PAIRS(X) \
+  X(3, 3, 4, 3, 3, 4) /* K / V: b4 / b4 */ \
+  X(3, 3, 4, 2, 2, 4) /* K / V: b4 / b3 */ \
+  X(2, 2, 4, 2, 2, 4) /* K / V: b3 / b3 */ \
+  X(1, 1, 4, 1, 1, 4) /* K / V: b2 / b2 */ \
+  X(2, 2, 4, 1, 1, 4) /* K / V: b3 / b2 */ \
+  X(3, 2, 1, 3, 2, 1) /* K / V: 3+2 bits split at 32 (3.25 bit) */ \
+  X(3, 2, 2, 3, 2, 2) /* K / V: 3+2 bits split at 64 (3.5 bit) */ \
+  X(2, 1, 1, 2, 1, 1) /* K / V: 2+1 bits split at 32 (2.25 bit) */ \
+  X(2, 1, 2, 2, 1, 2) /* K / V: 2+1 bits split at 64 (2.5 bit) */ \
+  X(2, 1, 3, 2, 1, 3) /* K / V: 2+1 bits split at 96 (2.75 bit) */ \
+  X(3, 3, 4, 2, 1, 2) /* K / V: b4 / b2.5 */ \
+  X(3, 2, 2, 2, 1, 2) /* K / V: b3.5 / b2.5 */ \
+  X(3, 2, 2, 2, 2, 4) /* K / V: b3.5 / b3 */ \
+  /* end */
+
+#define TQ_DECODE_EXTERN(a, b, c, d, e, f) \
+  extern template int launch_pair<a, b, c, d, e, f>(const DecodeParams&, bool, int, dim3, hipStream_t);
+TQ_DECODE_PAIRS(TQ_DECODE_EXTERN)
+#undef TQ_DECODE_EXTERN
+
+}  // namespace tqk

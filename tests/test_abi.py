@@ -117,8 +117,8 @@ def test_decode_and_search_validation_before_launch():
     ws = tq.attend_workspace_bytes(1, 32, 8, 4096)
     assert ws > 0 and tq.attend_workspace_bytes(2, 32, 8, 4096) > ws
 
-    def D(hq=32, hkv=8, ws_bytes=ws, tau=0.0, fv=f, q=p, fk=f):
-        return lib.tq_attend_decode(ctypes.byref(fk), ctypes.byref(t), ctypes.byref(fv), ctypes.byref(t),
+    def D(hq=32, hkv=8, ws_bytes=ws, tau=0.0, fv=f, q=p, fk=f, tv=t):
+        return lib.tq_attend_decode(ctypes.byref(fk), ctypes.byref(t), ctypes.byref(fv), ctypes.byref(tv),
                                     q, 1, 1, hq, hkv, p, p, p, p, 4096, p, 0.088, tau, p, None, None,
                                     p, ws_bytes, None)
     assert D(hq=30) == E.TQ_ERR_SHAPE              # hq % hkv
@@ -129,6 +129,12 @@ def test_decode_and_search_validation_before_launch():
     fv_bad = c_format(256, 3, 3, 256, 1)
     assert D(fv=fv_bad) == E.TQ_ERR_SHAPE
     assert D(fk=c_format(128, 3, 3, 128, 0)) == E.TQ_ERR_SHAPE   # keys need the QJL term
+    f375 = c_format(128, 3, 2, 96, 1)                              # 3.75 bit: quantize-only
+    assert D(fk=f375, fv=f375) == E.TQ_ERR_SHAPE
+    f25 = c_format(128, 2, 1, 64, 1)                               # K b4 / V b2.5: supported
+    t25, keep25 = _tables(tq.Format(128, 2, 1, 64))
+    assert D(fv=f25, tv=t25, ws_bytes=ws - 1) == E.TQ_ERR_WORKSPACE  # (stops at the workspace check)
+    assert D(fv=f25, ws_bytes=ws - 1) == E.TQ_ERR_ARG                # tables of another width
     f2 = c_format(256, 3, 3, 256, 1)
     t2, keep2 = _tables(tq.Format(256, 3, 3, 256))
     wsb = tq.search_workspace_bytes(100, 10, 10 ** 6, 256)

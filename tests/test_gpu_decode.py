@@ -111,6 +111,23 @@ def test_mse_only_values(torch_gpu):
     assert skipped > 0
 
 
+@pytest.mark.parametrize("fk,fv,hq,hkv,seed", [
+    ((128, 2, 2, 128), (128, 1, 1, 128), 32, 8, 4200),            # K b3 / V b2
+    ((128, 3, 2, 32), (128, 3, 2, 32), 32, 8, 4201),              # 3.25 bit
+    ((128, 2, 1, 32), (128, 2, 1, 32), 16, 8, 4202),              # 2.25 bit, G = 2
+    ((128, 2, 1, 64), (128, 2, 1, 64), 32, 8, 4203),              # 2.5 bit
+    ((128, 2, 1, 64), (128, 2, 1, 64, False), 8, 8, 4204),        # 2.5 bit, MSE-only V, G = 1
+    ((128, 2, 1, 96), (128, 2, 1, 96), 32, 4, 4205),              # 2.75 bit, G = 8
+    ((128, 3, 3, 128), (128, 2, 1, 64), 32, 8, 4206),             # K b4 / V b2.5
+    ((128, 3, 2, 64), (128, 2, 1, 64), 32, 8, 4207),              # K b3.5 / V b2.5
+    ((128, 3, 2, 64), (128, 2, 2, 128, False), 32, 8, 4208),      # K b3.5 / V b3 MSE-only
+])
+def test_channel_group_bit_allocations(torch_gpu, fk, fv, hq, hkv, seed):
+    """Two-group bit allocations (codebook widths below / above a split at a 32-coordinate
+    block boundary of the rotated vector) for keys and values, incl. the 2.5-bit setting."""
+    _case(torch_gpu, 2, hq, hkv, 777, [777, 430], fk, fv, seed)
+
+
 def test_single_head_64_queries(torch_gpu):
     """One KV head, d = 128, 4096 keys/values N(0,1) fp32 with 4 channels x20, 64 queries,
     b = 3 (2-bit codebook + 1 QJL bit): 64 query heads sharing one KV head."""
