@@ -305,6 +305,11 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
   };
   if constexpr (C::kResidentS && QJ) load_s_rows(0, D);
   __syncthreads();
+  // record store mapping: lane -> (vector sv of a group of vpi, word sw); fixed per kernel
+  const int vpi = 64 / p.words;
+  const int sv = lane / p.words, sw = lane - sv * p.words;
+  const bool s_lane = sv < vpi;
+  const int swm = wmap[s_lane ? sw : 0], s_blk = swm >> 8, s_q = swm & 0xFF;
 
   const int h = lane >> 5, c = lane & 31;
   float dsg[NB];
@@ -497,9 +502,10 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
 #pragma unroll
         for (int gg = 0; gg < PG; ++gg) {
           const float rs = half_sum(rsq[gg]);
-          const float rn = sqrtf(rs);
+          const float rn = __builtin_amdgcn_sqrtf(rs);  // 1 ulp: r16 tolerates it at midpoints
           const uint32_t r16 = f32_to_f16_bits(rn);
-          const float rinv = rn > 0.0f ? kRScale / rn : 0.0f;
+          // any positive scale of r leaves the projection signs unchanged
+          const float rinv = rn > 0.0f ? kRScale * __builtin_amdgcn_rcpf(rn) : 0.0f;
           // hoff(row, 32 s + c, lo): the 16-byte unit 4 s + (c >> 3) is XORed with row & 15,
           // i.e. s with (row >> 2) & 3 and c >> 3 with row & 3
           const int row = vloc[gg];
@@ -526,6 +532,18 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
       if (p.staged && gn < ngroups && gn * NW + wave < ntiles) fetch_tile<D>(p, cp, (gn * NW + wave) * TV, pre);
     }
     // ---------------- phase 2: JL projection on MFMA (3 fp16 products), sign ballots
+    constexpr bool kHoistA = (D == 128);
+    f16x8 a_h[kHoistA ? D / 32 : 1], a_l[kHoistA ? D / 32 : 1];
+    if constexpr (kHoistA && QJ) {
+      if (active) {
+        const int arow = lane & 15, kg = 8 * (lane >> 4);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          a_h[ks] = *reinterpret_cast<const f16x8*>(tileb + hoff<D>(arow, 32 * ks + kg, 0));
+          a_l[ks] = *reinterpret_cast<const f16x8*>(tileb + hoff<D>(arow, 32 * ks + kg, 1));
+        }
+      }
+    }
     for (int blk = 0; QJ && blk < NB; ++blk) {
       if constexpr (!C::kResidentS) {
         __syncthreads();
@@ -540,8 +558,14 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
         const int col = 32 * ks + kg;
-        const f16x8 ah = *reinterpret_cast<const f16x8*>(tileb + hoff<D>(arow, col, 0));
-        const f16x8 al = *reinterpret_cast<const f16x8*>(tileb + hoff<D>(arow, col, 1));
+        f16x8 ah, al;
+        if constexpr (kHoistA) {
+          ah = a_h[ks];
+          al = a_l[ks];
+        } else {
+          ah = *reinterpret_cast<const f16x8*>(tileb + hoff<D>(arow, col, 0));
+          al = *reinterpret_cast<const f16x8*>(tileb + hoff<D>(arow, col, 1));
+        }
         const f16x8 bh0 = *reinterpret_cast<const f16x8*>(S_l + hoff<D>(brow, col, 0));
         const f16x8 bl0 = *reinterpret_cast<const f16x8*>(S_l + hoff<D>(brow, col, 1));
         const f16x8 bh1 = *reinterpret_cast<const f16x8*>(S_l + hoff<D>(brow + 16, col, 0));
@@ -595,18 +619,19 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     uint32_t* dst = p.codes + v0 * p.words;
     const uint32_t* b32 = reinterpret_cast<const uint32_t*>(bal);
     const uint16_t* s16 = reinterpret_cast<const uint16_t*>(sbal);
-    for (int i = lane; i < nvalid * p.words; i += 64) {
-      const int v = i / p.words, w = i - v * p.words;
-      const int wm = wmap[w], blk = wm >> 8, q = wm & 0xFF;
-      uint32_t word;
-      if (q != 0xFF) {
-        word = b32[(((v >> 1) * NB + blk) * 4 + q) * 2 + (v & 1)];
-      } else {
-        const int rr = v & 3, gq = v >> 2;
-        word = (uint32_t)s16[((blk * 2 + 0) * 4 + rr) * 4 + gq] |
-               ((uint32_t)s16[((blk * 2 + 1) * 4 + rr) * 4 + gq] << 16);
+    for (int vb = 0; vb < nvalid; vb += vpi) {
+      const int v = vb + sv;
+      if (s_lane && v < nvalid) {
+        uint32_t word;
+        if (s_q != 0xFF) {
+          word = b32[(((v >> 1) * NB + s_blk) * 4 + s_q) * 2 + (v & 1)];
+        } else {
+          const int rr = v & 3, gq = v >> 2;
+          word = (uint32_t)s16[((s_blk * 2 + 0) * 4 + rr) * 4 + gq] |
+                 ((uint32_t)s16[((s_blk * 2 + 1) * 4 + rr) * 4 + gq] << 16);
+        }
+        dst[v * p.words + sw] = word;
       }
-      dst[i] = word;
     }
     if (lane < nvalid) p.norms[v0 + lane] = snorm[lane];
   }
