@@ -361,24 +361,46 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
         float ss[PG];
         bool valid[PG];
         int vloc[PG];
+        float xin[PG][NB];
 #pragma unroll
         for (int gg = 0; gg < PG; ++gg) {
           vloc[gg] = 2 * (pp0 + gg) + h;
-          const int64_t v = v0 + vloc[gg];
-          valid[gg] = v < p.n;
-          const char* rowp = tileb + vloc[gg] * C::kRowB;
+          valid[gg] = v0 + vloc[gg] < p.n;
+        }
+        // one uniform branch per pass group, so that the LDS reads issue back to back
+        if (p.staged) {
+          // this lane's element of the first row, kept opaque so that the row and slot
+          // offsets fold into the reads' immediate offsets
+          constexpr int esz = XT == 0 ? 4 : 2;
+          int roff = (int)(tileb - lds_b) + vloc[0] * C::kRowB + esz * c;
+          asm volatile("" : "+v"(roff));
+          const char* r0 = lds_b + roff;
+#pragma unroll
+          for (int gg = 0; gg < PG; ++gg) {
+            const char* rowp = r0 + 2 * gg * C::kRowB;  // vloc[gg] = vloc[0] + 2 gg
+#pragma unroll
+            for (int s = 0; s < NB; ++s) {
+              if constexpr (XT == 0) xin[gg][s] = *reinterpret_cast<const float*>(rowp + 4 * 32 * s);
+              else xin[gg][s] = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * 32 * s));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int gg = 0; gg < PG; ++gg)
+#pragma unroll
+            for (int s = 0; s < NB; ++s) {
+              const int j = 32 * s + c;
+              xin[gg][s] = (valid[gg] && j < p.d_in)
+                               ? load_elem(p.x, (v0 + vloc[gg]) * p.ld_x + j, XT) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int gg = 0; gg < PG; ++gg) {
           float sq[NB];
 #pragma unroll
           for (int s = 0; s < NB; ++s) {
             const int j = 32 * s + c;
-            float x;
-            if (p.staged) {
-              if constexpr (XT == 0) x = *reinterpret_cast<const float*>(rowp + 4 * j);
-              else x = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * j));
-              x = (valid[gg] && j < p.d_in) ? x : 0.0f;
-            } else {
-              x = (valid[gg] && j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
-            }
+            const float x = (valid[gg] && j < p.d_in) ? xin[gg][s] : 0.0f;
             sq[s] = x * x;
             xv[gg][s] = x * dsg[s];
           }
