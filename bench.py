@@ -144,8 +144,8 @@ def _variant(tq, torch, dev, ks, vs, q, seq, ws, out, fmt_k, fmt_v, signs, S, st
 def main():
     args = _parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the path is single-GPU (sharding is described "
-              "in DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: this build measures the single-GPU path "
+              "(no collectives); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.calibrate_copy:

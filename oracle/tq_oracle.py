@@ -35,10 +35,13 @@ m.163.com/dy/article/KOV7P8JI0556C3J2; "juejin post" is juejin.cn/post/762107404
 * search: inner-product nearest neighbours over compressed vectors --
   163.com explainer, section "向量搜索".
 
-Readings taken where the pages are silent are listed in DESIGN.md's "Readings" table
-(rotation order D-then-H, exact Beta marginal, tie rule, residual in the rotated
-domain against the stored fp16 norm, sign of zero, ambiguity windows, Sparse-V
-semantics, plain 1/sqrt(d) logit scaling).
+Readings taken where the pages are silent: the sign flip D precedes the Hadamard
+transform; the codebook law is the exact Beta marginal, not its Gaussian limit; a value
+equal to a boundary goes to the lower cell; the residual lives in the rotated domain and
+is taken against the stored fp16 norm; a zero projection counts as a 1 bit; decisions
+within 1e-6 of a boundary are ambiguous (the windows below); Sparse V drops a value row
+whose final weight is below tau without renormalizing; logits use the plain 1/sqrt(d)
+scale.
 """
 from __future__ import annotations
 
@@ -242,14 +245,21 @@ def quantize(x: np.ndarray, fmt: Format, signs: np.ndarray, S: np.ndarray,
     u = S (r / ||r||); sign bit = 1 where u >= 0 (all ones when r = 0).
     Also returns the ambiguity masks used by parity checks.
     """
-    cb_hi = cb_lo if cb_hi is None else cb_hi
     x = np.asarray(x, dtype=np.float64)
     n, d_in = x.shape
-    d = fmt.d
-    xp = np.zeros((n, d))
+    xp = np.zeros((n, fmt.d))
     xp[:, :d_in] = x
     y = rotate(xp, signs)
     nrm = np.sqrt(np.sum(xp * xp, axis=1))
+    return encode_rotated(y, nrm, fmt, S, cb_lo, cb_hi)
+
+
+def encode_rotated(y: np.ndarray, nrm: np.ndarray, fmt: Format, S: np.ndarray,
+                   cb_lo: Codebook, cb_hi: Codebook | None = None) -> dict:
+    """The steps of ``quantize`` after the rotation: y [n, d] rotated rows, nrm [n] their
+    norms (||x|| = ||y||, the rotation being orthogonal)."""
+    cb_hi = cb_lo if cb_hi is None else cb_hi
+    n, d = y.shape
     n16b = fp16_bits(nrm)
     n16 = fp16_value(n16b)
     safe = np.where(nrm > 0.0, nrm, 1.0)
@@ -359,6 +369,20 @@ def dequantize(idx, sbit, n16b, r16b, fmt, signs, S, cb_lo, cb_hi=None, qjl=True
     """x~ = Pi^T (n16 c[idx] + gamma r16 S^T sigma): the unbiased reconstruction whose inner
     product with any y has expectation <y, x> (163.com explainer, section "第二步：QJL")."""
     return unrotate(dequantize_rotated(idx, sbit, n16b, r16b, fmt, S, cb_lo, cb_hi, qjl), signs)
+
+
+def requantize(rec, n16b, r16b, fmt_in: Format, S_in, cbi_lo: Codebook, cbi_hi: Codebook | None,
+               fmt_out: Format, S_out, cbo_lo: Codebook, cbo_hi: Codebook | None = None) -> dict:
+    """Temporal decay: stored tokens move to another (usually narrower) format -- zhidx
+    article, section "01 turboquant_plus：介绍与详解" (older tokens drop to lower precision).
+    Reading: the record's reconstruction in the rotated domain,
+    y~ = n16 c[idx] + gamma r16 S_in^T (2 sigma - 1) (the sign term only when fmt_in has
+    QJL), is encoded again as a rotated vector of norm ||y~||, by the same steps as
+    ``quantize`` after its rotation (so the rotation D, H is shared by both formats).
+    rec [n, record_bytes(fmt_in)] uint8, n16b / r16b [n] fp16 bit patterns."""
+    idx, sbit = unpack(rec, fmt_in)
+    y = dequantize_rotated(idx, sbit, n16b, r16b, fmt_in, S_in, cbi_lo, cbi_hi, qjl=fmt_in.qjl)
+    return encode_rotated(y, np.sqrt(np.sum(y * y, axis=1)), fmt_out, S_out, cbo_lo, cbo_hi)
 
 
 def estimator_dot(q, idx, sbit, n16b, r16b, fmt, signs, S, cb_lo, cb_hi=None):

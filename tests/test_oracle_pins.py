@@ -425,3 +425,79 @@ def test_mse_only_reconstruction_error_is_d_times_codebook_mse(bits):
     e = np.concatenate(errs)
     se = e.std() / math.sqrt(e.size)
     assert abs(e.mean() - d * cb.mse) < 4 * se + 1e-3 * d * cb.mse, (e.mean(), d * cb.mse, se)
+
+
+# ---------------------------------------------------------------------------- temporal decay
+def _stored(x, fmt, signs, S):
+    lo, hi = O.codebook(fmt.d, fmt.bits_lo), O.codebook(fmt.d, fmt.bits_hi)
+    q = O.quantize(x, fmt, signs, S, lo, hi)
+    return O.pack(q["idx"], q["sbit"], fmt), q["n16"], q["r16"], lo, hi
+
+
+def test_requantize_is_quantize_of_the_unrotated_reconstruction():
+    """Re-encoding a record (b4 -> b3, and b4 -> 2.5 bit) gives the same codes, signs and
+    norms as quantizing the un-rotated reconstruction x~ = Pi^T y~ from scratch: the
+    re-encode happens in the rotation both formats share."""
+    d = 128
+    signs, S = TI.rotation(d, 77)
+    _, S2 = TI.rotation(d, 78)
+    x = TI.gen(79).standard_normal((300, d)) * 3.0
+    f_in = O.Format.uniform(d, 3)
+    rec, n16, r16, lo, hi = _stored(x, f_in, signs, S)
+    for f_out, S_out in ((O.Format.uniform(d, 2), S), (O.Format(d, 2, 1, 64), S2)):
+        lo2, hi2 = O.codebook(d, f_out.bits_lo), O.codebook(d, f_out.bits_hi)
+        rq = O.requantize(rec, n16, r16, f_in, S, lo, hi, f_out, S_out, lo2, hi2)
+        idx, sb = O.unpack(rec, f_in)
+        xt = O.dequantize(idx, sb, n16, r16, f_in, signs, S, lo, hi)
+        ref = O.quantize(xt, f_out, signs, S_out, lo2, hi2)
+        ok_code = ~(rq["amb_code"] | ref["amb_code"])
+        assert np.array_equal(rq["idx"][ok_code], ref["idx"][ok_code])
+        same_codes = np.all(rq["idx"] == ref["idx"], axis=1)
+        ok_sign = ~(rq["amb_sign"] | ref["amb_sign"]) & same_codes[:, None]
+        assert np.array_equal(rq["sbit"][ok_sign], ref["sbit"][ok_sign])
+        assert np.array_equal(rq["n16"][~rq["amb_n16"]], ref["n16"][~rq["amb_n16"]])
+
+
+def test_requantize_one_bit_mse_only_is_idempotent_with_closed_form_norm():
+    """A 1-bit MSE-only record reconstructs to n16 * c0 * (+-1): re-encoding it at the same
+    format keeps every code (z = +-1/sqrt(d), far from the 0 boundary) and stores the norm
+    fp16(n16 * c0 * sqrt(d)), c0 = sqrt(2 / (pi d)) to first order, here the codebook's own
+    positive centroid."""
+    d = 128
+    fmt = O.Format.uniform(d, 1, qjl=False)
+    cb = O.codebook(d, 1)
+    signs, S = TI.rotation(d, 5)
+    x = TI.gen(6).standard_normal((200, d))
+    rec, n16, r16, _, _ = _stored(x, fmt, signs, S)
+    rq = O.requantize(rec, n16, r16, fmt, S, cb, cb, fmt, S, cb, cb)
+    idx, _ = O.unpack(rec, fmt)
+    assert np.array_equal(rq["idx"], idx)
+    c0 = cb.centroids[1]
+    assert abs(c0 - math.sqrt(2 / (math.pi * d))) < 0.01 * c0
+    want = O.fp16_bits(O.fp16_value(n16) * c0 * math.sqrt(d))
+    assert np.array_equal(rq["n16"], want)
+
+
+def test_requantized_inner_products_stay_unbiased():
+    """With a fresh JL matrix for the narrower format, the requantized reconstruction is an
+    unbiased estimate of the stored one: E_S <y, x~'> = <y, x~> (163.com explainer, section
+    "第二步：QJL", applied to x~ as the input)."""
+    d, n_seeds = 128, 6000
+    signs, S = TI.rotation(d, 11)
+    g = TI.gen(12)
+    x = g.standard_normal((1, d))
+    y = 0.5 * x[0] + g.standard_normal(d)
+    f_in, f_out = O.Format.uniform(d, 3), O.Format(d, 2, 1, 64)
+    rec, n16, r16, lo, hi = _stored(x, f_in, signs, S)
+    idx, sb = O.unpack(rec, f_in)
+    xt = O.dequantize(idx, sb, n16, r16, f_in, signs, S, lo, hi)[0]
+    lo2, hi2 = O.codebook(d, 2), O.codebook(d, 1)
+    vals = np.empty(n_seeds)
+    for s in range(n_seeds):
+        _, S2 = TI.rotation(d, 40_000 + s)
+        rq = O.requantize(rec, n16, r16, f_in, S, lo, hi, f_out, S2, lo2, hi2)
+        x2 = O.dequantize(rq["idx"], rq["sbit"], rq["n16"], rq["r16"], f_out, signs, S2, lo2, hi2)[0]
+        vals[s] = y @ x2
+    se = vals.std(ddof=1) / math.sqrt(n_seeds)
+    assert abs(vals.mean() - y @ xt) < 4 * se
+
