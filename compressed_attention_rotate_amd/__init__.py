@@ -17,7 +17,8 @@ from ._lib import (LIB_PATH, TQ_BF16, TQ_F16, TQ_F32, Format, Tables, TQError, b
                    load)
 
 __all__ = ["Format", "Tables", "TQError", "build_codebook", "quantize_kv", "attend_decode",
-           "ip_search", "attend_workspace_bytes", "search_workspace_bytes", "LIB_PATH", "load"]
+           "ip_search", "requantize", "attend_workspace_bytes", "search_workspace_bytes",
+           "requantize_workspace_bytes", "LIB_PATH", "load"]
 
 
 def _torch():
@@ -154,3 +155,40 @@ def ip_search(queries, codes_db, norms_db, fmt: Format, tables: Tables, k: int =
                              _ptr(workspace), workspace.numel(), _stream(queries.device))
     _check(rc, "tq_ip_search")
     return ids, scores
+
+
+def requantize_workspace_bytes(n, d=128) -> int:
+    m = load().tq_requantize_workspace_bytes(n, d)
+    if m < 0:
+        raise TQError(-2, "tq_requantize_workspace_bytes")
+    return int(m)
+
+
+def requantize(codes_in, norms_in, fmt_in: Format, tables_in: Tables, fmt_out: Format,
+               tables_out: Tables, codes_out=None, norms_out=None, counters=None,
+               workspace=None):
+    """Re-encode stored vectors (codes_in uint8 [n, record_bytes(fmt_in)], norms_in fp16
+    [n, 2]) at fmt_out (temporal decay).  Pass codes_out=codes_in / norms_out=norms_in to
+    rewrite in place (narrower or equal records only); the records then occupy the first
+    n * record_bytes(fmt_out) bytes.  Returns (codes_out, norms_out)."""
+    torch = _torch()
+    n = norms_in.numel() // 2
+    rb_in, rb_out = fmt_in.record_bytes(), fmt_out.record_bytes()
+    if codes_in.numel() < n * rb_in:
+        raise ValueError("codes_in too small for the norms given")
+    if codes_out is None:
+        codes_out = torch.empty((n, rb_out), dtype=torch.uint8, device=codes_in.device)
+    if norms_out is None:
+        norms_out = torch.empty((n, 2), dtype=torch.float16, device=codes_in.device)
+    if codes_out.numel() < n * rb_out or norms_out.numel() < 2 * n:
+        raise ValueError("output buffers too small")
+    if workspace is None:
+        workspace = torch.empty(requantize_workspace_bytes(n, fmt_in.d), dtype=torch.uint8,
+                                device=codes_in.device)
+    fi, ti, fo, to = fmt_in.c(), tables_in.c(), fmt_out.c(), tables_out.c()
+    rc = load().tq_requantize(ctypes.byref(fi), ctypes.byref(ti), _ptr(codes_in), _ptr(norms_in),
+                              n, ctypes.byref(fo), ctypes.byref(to), _ptr(codes_out),
+                              _ptr(norms_out), _ptr(counters), _ptr(workspace), workspace.numel(),
+                              _stream(codes_in.device))
+    _check(rc, "tq_requantize")
+    return codes_out, norms_out

@@ -161,6 +161,46 @@ int tq_ip_search(const tq_format* f, const tq_tables* t, const void* codes_db,
                           out_scores, workspace, plan, reinterpret_cast<hipStream_t>(stream));
 }
 
+int64_t tq_requantize_workspace_bytes(int64_t n, int32_t d) {
+  if (n < 0 || d != 128) return -1;
+  return (n > 0 ? n : 1) * d * 4;
+}
+
+int tq_requantize(const tq_format* f_in, const tq_tables* t_in, const void* codes_in,
+                  const uint16_t* norms_in, int64_t n, const tq_format* f_out,
+                  const tq_tables* t_out, void* codes_out, uint16_t* norms_out,
+                  int64_t* counters, void* workspace, int64_t workspace_bytes,
+                  tq_stream_t stream) {
+  int rc = tq_check_format(f_in);
+  if (rc) return rc;
+  if ((rc = tq_check_format(f_out))) return rc;
+  if (f_in->d != 128 || f_out->d != 128) return TQ_ERR_SHAPE;
+  if (n < 0) return TQ_ERR_ARG;
+  if ((rc = check_tables(f_in, t_in)) || (rc = check_tables(f_out, t_out))) return rc;
+  for (int j = 0; j < f_in->d; ++j)
+    if (t_in->signs[j] != t_out->signs[j]) return TQ_ERR_ARG;  // one shared rotation
+  if (n == 0) return TQ_OK;
+  if (!codes_in || !norms_in || !codes_out || !norms_out || !workspace) return TQ_ERR_ARG;
+  if (!aligned(codes_in, 16) || !aligned(codes_out, 16) || !aligned(norms_in, 4) ||
+      !aligned(norms_out, 4) || !aligned(workspace, 16) || (counters && !aligned(counters, 8)))
+    return TQ_ERR_ALIGN;
+  if (workspace_bytes < (int64_t)f_in->d * 4) return TQ_ERR_WORKSPACE;
+  const int64_t rbi = tq_record_bytes(f_in), rbo = tq_record_bytes(f_out);
+  auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+  };
+  if (codes_out == codes_in ? rbo > rbi : overlap(codes_in, n * rbi, codes_out, n * rbo))
+    return TQ_ERR_ARG;
+  if (norms_out != norms_in && overlap(norms_in, n * 4, norms_out, n * 4)) return TQ_ERR_ARG;
+  const int64_t ws = workspace_bytes;
+  if (overlap(workspace, ws, codes_in, n * rbi) || overlap(workspace, ws, codes_out, n * rbo) ||
+      overlap(workspace, ws, norms_in, n * 4) || overlap(workspace, ws, norms_out, n * 4))
+    return TQ_ERR_ARG;
+  return tq_launch_requant(f_in, t_in, codes_in, norms_in, n, f_out, t_out, codes_out, norms_out,
+                           counters, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
 const char* tq_strerror(int code) {
   switch (code) {
     case TQ_OK: return "ok";

@@ -156,7 +156,7 @@ __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
 }
 
 __device__ __forceinline__ float load_elem(const void* base, int64_t i, int dtype) {
-  if (dtype == 0) return reinterpret_cast<const float*>(base)[i];
+  if (dtype == 0 || dtype == 3) return reinterpret_cast<const float*>(base)[i];  // 3: fp32 rows, pre-rotated
   uint32_t h = reinterpret_cast<const uint16_t*>(base)[i];
   if (dtype == 1) return __uint_as_float(h << 16);  // bf16
   return f16_bits_to_f32(h);                       // fp16

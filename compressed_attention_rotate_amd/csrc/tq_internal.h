@@ -47,3 +47,9 @@ int tq_launch_search(const tq_format* f, const tq_tables* t, const void* codes_d
                      const uint16_t* norms_db, int64_t n_db, const float* queries, int32_t d_in,
                      int64_t n_q, int32_t k, int64_t* out_ids, float* out_scores,
                      void* workspace, const tq_search_plan& plan, hipStream_t stream);
+
+int tq_launch_requant(const tq_format* fi, const tq_tables* ti, const void* codes_in,
+                      const uint16_t* norms_in, int64_t n, const tq_format* fo,
+                      const tq_tables* to, void* codes_out, uint16_t* norms_out,
+                      int64_t* counters, void* workspace, int64_t workspace_bytes,
+                      hipStream_t stream);

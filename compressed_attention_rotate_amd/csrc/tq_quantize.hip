@@ -32,20 +32,7 @@ int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, in
   p.staged = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && ((ld_x * p.esize) % 16 == 0) &&
              (row_bytes % 16 == 0);
   p.cpr = p.staged ? (int32_t)(row_bytes / 16) : 1;
-  p.split_blocks = f->split / 32;
-  p.words = (int)(tq_record_bytes(f) / 4);
-  for (int j = 0; j < 8; ++j) p.sign_mask[j] = 0;
-  for (int j = 0; j < f->d; ++j)
-    if (t->signs[j] < 0) p.sign_mask[j >> 5] |= 1u << (j & 31);
-  auto fill = [](int bits, const float* cent, const float* bnd, float* cpos, float* tpos, float* full) {
-    const int H = 1 << (bits - 1);
-    for (int k = 0; k < 8; ++k) cpos[k] = tpos[k] = 0.0f;
-    for (int k = 0; k < H; ++k) cpos[k] = cent[H + k];
-    for (int k = 1; k < H; ++k) tpos[k] = bnd[H + k - 1];
-    for (int k = 0; k < 16; ++k) full[k] = k < (1 << bits) ? cent[k] : 0.0f;
-  };
-  fill(f->bits_lo, t->centroids_lo, t->bounds_lo, p.cpos_lo, p.tpos_lo, p.cent_lo);
-  fill(f->bits_hi, t->centroids_hi, t->bounds_hi, p.cpos_hi, p.tpos_hi, p.cent_hi);
+  fill_format_params(f, t, p);
   const int ncu = tq_num_cus();
   if (ncu <= 0) return TQ_ERR_HIP;
   const int lo = f->bits_lo, hi = f->bits_hi, xt = x_dtype;

@@ -97,7 +97,43 @@ struct QParams {
   uint32_t sign_mask[8]; // bit j set: coordinate j is multiplied by -1
   float cpos_lo[8], tpos_lo[8], cpos_hi[8], tpos_hi[8];  // positive halves; tpos[0] unused
   float cent_lo[16], cent_hi[16];
+  // Pre-rotated input (XT 3): rows reconstructed from stored records (re-encoding).  The
+  // records are kept for the rare exact fp64 recomputations, which use the stored values
+  // rather than the fp32 rows.
+  const uint32_t* src_codes;
+  const uint32_t* src_norms;
+  const float* src_S;
+  int32_t src_words, src_split_blocks, src_bits_lo, src_bits_hi, src_qjl;
+  float src_cent[16];    // source codebooks: lo table, then hi table
 };
+
+// Exact (fp64) rotated-domain value of coordinate j of source record `row`:
+// n16 c[idx_j] + gamma r16 sum_i S[i][j] (2 sigma_i - 1), gamma = sqrt(pi/2) / D.  Rare
+// path; src_cent is an LDS copy of the source codebooks.
+template <int D>
+__device__ double src_value(const QParams& p, const float* src_cent, int64_t row, int j) {
+  const uint32_t* rec = p.src_codes + row * p.src_words;
+  const int sb = p.src_split_blocks, wlo = p.src_bits_lo + p.src_qjl, whi = p.src_bits_hi + p.src_qjl;
+  auto off = [&](int b) { return b < sb ? b * wlo : sb * wlo + (b - sb) * whi; };
+  const int blk = j >> 5, bit = j & 31;
+  const int nb = blk < sb ? p.src_bits_lo : p.src_bits_hi;
+  int idx = 0;
+  for (int q = 0; q < nb; ++q) idx |= (int)((rec[off(blk) + q] >> bit) & 1u) << q;
+  const uint32_t nr = p.src_norms[row];
+  double val = (double)f16_bits_to_f32(nr & 0xFFFFu) * (double)src_cent[(blk < sb ? 0 : 8) + idx];
+  if (p.src_qjl) {
+    double acc = 0.0;
+    for (int b = 0; b < D / 32; ++b) {
+      const uint32_t sw = rec[off(b) + (b < sb ? p.src_bits_lo : p.src_bits_hi)];
+      for (int i = 0; i < 32; ++i) {
+        const double sv = (double)p.src_S[(int64_t)(32 * b + i) * D + j];
+        acc += ((sw >> i) & 1u) ? sv : -sv;
+      }
+    }
+    val += sqrt(1.5707963267948966) / D * (double)f16_bits_to_f32(nr >> 16) * acc;
+  }
+  return val;
+}
 
 // 16-bit input element -> fp32 (bf16 or fp16)
 template <int XT>
@@ -162,36 +198,43 @@ __device__ void guard_fix(const QParams& p, int64_t v, int m, int n, const uint6
                           int bhi, unsigned long long& cnt_zero) {
   constexpr int NE = D / 64;
   constexpr int NB = D / 32;
+  constexpr bool PRE = (XT == 3);  // input already in the rotated domain
   const int lane = lane_id();
   double xd[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
     const int j = lane + 64 * e;
-    float xv = (j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
-    xd[e] = (double)xv;
+    if constexpr (PRE) {
+      xd[e] = src_value<D>(p, cent_lds + 32, v, j);
+    } else {
+      float xv = (j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
+      xd[e] = (double)xv;
+    }
   }
 #pragma unroll
-  for (int e = 0; e < NE; ++e) {
+  for (int e = 0; e < NE && !PRE; ++e) {
     const uint32_t sw = (lane & 32) ? uniform_u32(p.sign_mask[2 * e + 1]) : uniform_u32(p.sign_mask[2 * e]);
     if ((sw >> (lane & 31)) & 1u) xd[e] = -xd[e];
   }
+  if constexpr (!PRE) {
 #pragma unroll
-  for (int h = 1; h < NE; h <<= 1)
+    for (int h = 1; h < NE; h <<= 1)
 #pragma unroll
-    for (int e = 0; e < NE; ++e)
-      if (!(e & h)) {
-        double a = xd[e], b = xd[e + h];
-        xd[e] = a + b;
-        xd[e + h] = a - b;
+      for (int e = 0; e < NE; ++e)
+        if (!(e & h)) {
+          double a = xd[e], b = xd[e + h];
+          xd[e] = a + b;
+          xd[e + h] = a - b;
+        }
+#pragma unroll
+    for (int mm = 1; mm < 64; mm <<= 1)
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        double t = shfl_xor_d(xd[e], mm);
+        xd[e] = (lane & mm) ? t - xd[e] : xd[e] + t;
       }
-#pragma unroll
-  for (int mm = 1; mm < 64; mm <<= 1)
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      double t = shfl_xor_d(xd[e], mm);
-      xd[e] = (lane & mm) ? t - xd[e] : xd[e] + t;
-    }
-  const double isd = 1.0 / sqrt((double)D);
+  }
+  const double isd = PRE ? 1.0 : 1.0 / sqrt((double)D);
   const double n16 = (double)f16_bits_to_f32(snorm[m] & 0xFFFFu);
   const int pass = m >> 1, half = m & 1;
   double dot = 0.0, rr = 0.0;
@@ -245,7 +288,8 @@ __device__ __forceinline__ void stash_tile(const ChunkPlan<D>& cp, const u32x4 (
     if (cp.loff[i] >= 0) *reinterpret_cast<u32x4*>(tile + cp.loff[i]) = buf[i];
 }
 
-// XT: 0 fp32, 1 bf16, 2 fp16 input.  COUNT: accumulate the diagnostic counters.  QJ: the
+// XT: 0 fp32, 1 bf16, 2 fp16 input; 3 fp32 rows already in the rotated domain (re-encoding
+// stored records: no sign flip, no Hadamard transform, no 1/sqrt(d)).  COUNT: accumulate the diagnostic counters.  QJ: the
 // records carry QJL sign words (else MSE-only: no residual split, no projection).
 template <int D, int BLO, int BHI, int XT, bool COUNT, bool QJ>
 __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
@@ -264,7 +308,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
   uint64_t* bal = reinterpret_cast<uint64_t*>(wl + TV * C::kRowB);   // [pass][blk][4]
   uint64_t* sbal = bal + C::kBal;                                    // [blk][t][r]
   uint32_t* snorm = reinterpret_cast<uint32_t*>(sbal + C::kSBal);   // [TV]
-  __shared__ float cent_lds[32];
+  __shared__ float cent_lds[48];  // lo table, hi table, then (XT 3) the source tables
   __shared__ float cpos_lds[16];  // positive centroids: lo table, then hi table
   __shared__ int wmap[32];        // record word -> (block << 8) | plane, plane 0xFF = signs
 
@@ -273,6 +317,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     for (int k = 0; k < 16; ++k) {
       cent_lds[k] = p.cent_lo[k];
       cent_lds[16 + k] = p.cent_hi[k];
+      cent_lds[32 + k] = p.src_cent[k];
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -315,11 +360,12 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
   float dsg[NB];
 #pragma unroll
   for (int s = 0; s < NB; ++s) dsg[s] = ((p.sign_mask[s] >> c) & 1u) ? -1.0f : 1.0f;
+  constexpr bool PRE = (XT == 3);  // rows already rotated: no sign flip, no FWHT
   const float bs1 = (c & 1) ? -1.0f : 1.0f, bs2 = (c & 2) ? -1.0f : 1.0f;
   const float bs4 = (c & 4) ? -1.0f : 1.0f, bs8 = (c & 8) ? -1.0f : 1.0f;
   const float bs16 = (c & 16) ? -1.0f : 1.0f;
-  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-  const float sqrt_d = sqrtf((float)D);
+  const float inv_sqrt_d = PRE ? 1.0f : 1.0f / sqrtf((float)D);
+  const float sqrt_d = PRE ? 1.0f : sqrtf((float)D);
   float tpl[8], tph[8], cpl[8], cph[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -371,7 +417,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
         if (p.staged) {
           // this lane's element of the first row, kept opaque so that the row and slot
           // offsets fold into the reads' immediate offsets
-          constexpr int esz = XT == 0 ? 4 : 2;
+          constexpr int esz = (XT == 0 || XT == 3) ? 4 : 2;
           int roff = (int)(tileb - lds_b) + vloc[0] * C::kRowB + esz * c;
           asm volatile("" : "+v"(roff));
           const char* r0 = lds_b + roff;
@@ -380,7 +426,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
             const char* rowp = r0 + 2 * gg * C::kRowB;  // vloc[gg] = vloc[0] + 2 gg
 #pragma unroll
             for (int s = 0; s < NB; ++s) {
-              if constexpr (XT == 0) xin[gg][s] = *reinterpret_cast<const float*>(rowp + 4 * 32 * s);
+              if constexpr (XT == 0 || XT == 3) xin[gg][s] = *reinterpret_cast<const float*>(rowp + 4 * 32 * s);
               else xin[gg][s] = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * 32 * s));
             }
           }
@@ -402,7 +448,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
             const int j = 32 * s + c;
             const float x = (valid[gg] && j < p.d_in) ? xin[gg][s] : 0.0f;
             sq[s] = x * x;
-            xv[gg][s] = x * dsg[s];
+            xv[gg][s] = PRE ? x : x * dsg[s];
           }
 #pragma unroll
           for (int hh = 1; hh < NB; hh <<= 1)  // pairwise (tree) sum of the squares
@@ -414,7 +460,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
         for (int gg = 0; gg < PG; ++gg) {
           ss[gg] = half_sum(ss[gg]);
 #pragma unroll
-          for (int hh = 1; hh < NB; hh <<= 1)
+          for (int hh = 1; hh < NB && !PRE; hh <<= 1)
 #pragma unroll
             for (int s = 0; s < NB; ++s)
               if (!(s & hh)) {
@@ -423,26 +469,28 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
                 xv[gg][s + hh] = a - b;
               }
         }
+        if constexpr (!PRE) {
 #pragma unroll
-        for (int s = 0; s < NB; ++s)
+          for (int s = 0; s < NB; ++s)
 #pragma unroll
-          for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<1>(xv[gg][s], bs1);
+            for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<1>(xv[gg][s], bs1);
 #pragma unroll
-        for (int s = 0; s < NB; ++s)
+          for (int s = 0; s < NB; ++s)
 #pragma unroll
-          for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<2>(xv[gg][s], bs2);
+            for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<2>(xv[gg][s], bs2);
 #pragma unroll
-        for (int s = 0; s < NB; ++s)
+          for (int s = 0; s < NB; ++s)
 #pragma unroll
-          for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<4>(xv[gg][s], bs4);
+            for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<4>(xv[gg][s], bs4);
 #pragma unroll
-        for (int s = 0; s < NB; ++s)
+          for (int s = 0; s < NB; ++s)
 #pragma unroll
-          for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<8>(xv[gg][s], bs8);
+            for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<8>(xv[gg][s], bs8);
 #pragma unroll
-        for (int s = 0; s < NB; ++s)
+          for (int s = 0; s < NB; ++s)
 #pragma unroll
-          for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<16>(xv[gg][s], bs16);
+            for (int gg = 0; gg < PG; ++gg) xv[gg][s] = butterfly<16>(xv[gg][s], bs16);
+        }
 
         float r[PG][NB];
         float rsq[PG];
@@ -453,7 +501,8 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           // error is below (log2(D) + 2) 2^-24 < 6e-7: z = y / ||x|| stays within 3e-7 of
           // exact.  The stored fp16 norm must be the correctly rounded one: when a 1e-6
           // relative interval around the estimate straddles an fp16 rounding boundary the
-          // norm is recomputed in fp64 from the input row (still in the tile).
+          // norm is recomputed in fp64 from the input row (still in the tile), or for XT 3
+          // from the source record.
           float nf = __builtin_amdgcn_sqrtf(ss[gg]);
           n16[gg] = f32_to_f16_bits(nf);
           const bool near_mid =
@@ -464,15 +513,20 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
 #pragma unroll
             for (int s = 0; s < NB; ++s) {
               const int j = 32 * s + c;
-              float x;
-              if (p.staged) {
-                if constexpr (XT == 0) x = *reinterpret_cast<const float*>(rowp + 4 * j);
-                else x = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * j));
-                x = (valid[gg] && j < p.d_in) ? x : 0.0f;
+              if constexpr (PRE) {
+                const double y = valid[gg] ? src_value<D>(p, cent_lds + 32, v0 + vloc[gg], j) : 0.0;
+                sd = fma(y, y, sd);
               } else {
-                x = (valid[gg] && j < p.d_in) ? load_elem(p.x, (v0 + vloc[gg]) * p.ld_x + j, XT) : 0.0f;
+                float x;
+                if (p.staged) {
+                  if constexpr (XT == 0) x = *reinterpret_cast<const float*>(rowp + 4 * j);
+                  else x = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * j));
+                  x = (valid[gg] && j < p.d_in) ? x : 0.0f;
+                } else {
+                  x = (valid[gg] && j < p.d_in) ? load_elem(p.x, (v0 + vloc[gg]) * p.ld_x + j, XT) : 0.0f;
+                }
+                sd = fma((double)x, (double)x, sd);
               }
-              sd = fma((double)x, (double)x, sd);
             }
             sd = half_sum_d(sd);
             const double nrm = sqrt(sd);
@@ -671,6 +725,25 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
       if (ovf) atomicAdd(&p.counters[3], ovf);
     }
   }
+}
+
+// Host: the format- and table-dependent parameters (record layout, sign flips, codebook
+// halves and thresholds).
+inline void fill_format_params(const tq_format* f, const tq_tables* t, QParams& p) {
+  p.split_blocks = f->split / 32;
+  p.words = (int)(tq_record_bytes(f) / 4);
+  for (int j = 0; j < 8; ++j) p.sign_mask[j] = 0;
+  for (int j = 0; j < f->d; ++j)
+    if (t->signs[j] < 0) p.sign_mask[j >> 5] |= 1u << (j & 31);
+  auto fill = [](int bits, const float* cent, const float* bnd, float* cpos, float* tpos, float* full) {
+    const int H = 1 << (bits - 1);
+    for (int k = 0; k < 8; ++k) cpos[k] = tpos[k] = 0.0f;
+    for (int k = 0; k < H; ++k) cpos[k] = cent[H + k];
+    for (int k = 1; k < H; ++k) tpos[k] = bnd[H + k - 1];
+    for (int k = 0; k < 16; ++k) full[k] = k < (1 << bits) ? cent[k] : 0.0f;
+  };
+  fill(f->bits_lo, t->centroids_lo, t->bounds_lo, p.cpos_lo, p.tpos_lo, p.cent_lo);
+  fill(f->bits_hi, t->centroids_hi, t->bounds_hi, p.cpos_hi, p.tpos_hi, p.cent_hi);
 }
 
 template <int D, int BLO, int BHI, int XT, bool COUNT, bool QJ>

@@ -1,0 +1,221 @@
+// Re-encoding stored records at another format (temporal decay: older tokens move to fewer
+// bits; zhidx turboquant_plus article, section "01 turboquant_plus：介绍与详解").
+//
+// What is computed: each record's reconstruction in the rotated domain,
+//   y~ = n16 c[idx] + gamma r16 S^T (2 sigma - 1)   (the sign term only with QJL),
+// is encoded again by the quantize steps that follow the rotation (norm, codes, residual,
+// QJL signs), in the rotation both formats share.  Two launches per chunk of vectors:
+//   source:    y~ rows (fp32) into the caller's workspace.  S^T (2 sigma - 1) is the dense
+//              contraction of this step: 16 records x 128 projections x 128 coordinates per
+//              wave tile on v_mfma_f32_16x16x32_f16, with the +-1 signs exact in fp16 and S
+//              split into scaled fp16 hi + lo (the same 2^-22 relative accuracy as the
+//              quantize projection); S^T stays resident in LDS.
+//   quantize:  quantize_kernel with pre-rotated fp32 rows (XT 3).  Its rare exact paths
+//              (fp16 norm near a rounding boundary, projection near zero) recompute y~ in
+//              fp64 from the records, so every decision matches the exact value outside the
+//              same 1e-6 windows as a fresh quantization.
+// In place: a chunk's source rows are complete before its records are rewritten, and a
+// narrower record never reaches the next chunk's input, so codes_out may equal codes_in.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+#include "tq_quantize_kernel.h"
+
+namespace tqk {
+
+constexpr int kRqD = 128;
+constexpr int kRqWaves = 8;
+constexpr int kRqRowB = 4 * kRqD;  // bytes of one [hi | lo] fp16 row of S^T
+
+struct RqParams {
+  const uint32_t* codes;  // source records of this chunk
+  const uint32_t* norms;  // source norms of this chunk (fp16 n16 | fp16 r16 << 16)
+  const float* S;         // source JL matrix [projection i][coordinate j]
+  float* out;             // y~ rows [n][128]
+  int64_t n;
+  int32_t words, split_blocks, bits_lo, bits_hi;
+  float gamma;            // sqrt(pi/2) / d
+  float cent[16];         // source codebooks: lo table, then hi table
+};
+
+// y~ of 16 records per wave tile.  QJ: the source records carry sign words.
+template <bool QJ>
+__global__ __launch_bounds__(64 * kRqWaves) void requant_source(RqParams p) {
+  extern __shared__ __attribute__((aligned(16))) char lds_r[];
+  char* St = lds_r;                                          // [128 rows j][hi | lo] fp16
+  uint32_t* recs = reinterpret_cast<uint32_t*>(lds_r + (QJ ? kRqD * kRqRowB : 0));
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  uint32_t* wrec = recs + wave * (16 * 16 + 16);             // 16 records (<= 16 words) + norms
+  uint32_t* wnrm = wrec + 16 * 16;
+  __shared__ float cent[16];
+  if (tid < 16) cent[tid] = tid < 8 ? p.cent[tid] : p.cent[tid];
+  if constexpr (QJ) {
+    // S^T scaled by 2^10, split hi / lo; the 16-byte units of a row are swizzled by j & 15
+    for (int e = tid; e < kRqD * kRqD; e += blockDim.x) {
+      const int i = e / kRqD, j = e % kRqD;
+      const float sv = p.S[e] * 1024.0f;
+      const _Float16 hi = (_Float16)sv;
+      const _Float16 lo = (_Float16)(sv - (float)hi);
+      const int unit = ((i >> 3) ^ (j & 15));
+      *reinterpret_cast<_Float16*>(St + j * kRqRowB + (unit << 4) + 2 * (i & 7)) = hi;
+      *reinterpret_cast<_Float16*>(St + j * kRqRowB + 2 * kRqD + (unit << 4) + 2 * (i & 7)) = lo;
+    }
+  }
+  __syncthreads();
+  const int W = p.words, sb = p.split_blocks;
+  const int wlo = p.bits_lo + (QJ ? 1 : 0), whi = p.bits_hi + (QJ ? 1 : 0);
+  auto off = [&](int b) { return b < sb ? b * wlo : sb * wlo + (b - sb) * whi; };
+  const float scaleq = p.gamma * (1.0f / 1024.0f);
+  const int64_t ntiles = (p.n + 15) / 16;
+  for (int64_t tile = (int64_t)blockIdx.x * kRqWaves + wave; tile < ntiles;
+       tile += (int64_t)gridDim.x * kRqWaves) {
+    const int64_t v0 = tile * 16;
+    const int nv = (int)((p.n - v0) < 16 ? (p.n - v0) : 16);
+    // stage the tile's records and norms (zeros past the end)
+    for (int i = lane; i < 16 * W; i += 64) wrec[i] = i < nv * W ? p.codes[v0 * W + i] : 0u;
+    if (lane < 16) wnrm[lane] = lane < nv ? p.norms[v0 + lane] : 0u;
+    asm volatile("s_waitcnt lgkmcnt(0) vmcnt(0)" ::: "memory");
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f16x8 a[4];
+    if constexpr (QJ) {
+      // operand A: row m = record lane & 15, k = 8 (lane >> 4) .. + 7 of block ks as +-1
+      const int m = lane & 15, kg = lane >> 4;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t sw = wrec[m * W + off(ks) + (ks < sb ? p.bits_lo : p.bits_hi)];
+        const uint32_t b8 = (sw >> (8 * kg)) & 0xFFu;
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // fp16 -1 is 0xBC00, +1 is 0x3C00: flip bit 15 of each half for a set bit
+          const uint32_t lo = (b8 >> (2 * q)) & 1u, hi = (b8 >> (2 * q + 1)) & 1u;
+          u[q] = 0xBC00BC00u ^ (lo << 15) ^ (hi << 31);
+        }
+        a[ks] = __builtin_bit_cast(f16x8, u);
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (QJ) {
+        const int j = 16 * jb + (lane & 15), kg = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int unit = ((4 * ks + kg) ^ (j & 15));
+          const f16x8 bh = *reinterpret_cast<const f16x8*>(St + j * kRqRowB + (unit << 4));
+          const f16x8 bl = *reinterpret_cast<const f16x8*>(St + j * kRqRowB + 2 * kRqD + (unit << 4));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], bh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], bl, acc, 0, 0, 0);
+        }
+      }
+      // acc[r] of lane l: 2^10 (S^T sigma) of record 4 (l >> 4) + r, coordinate 16 jb + l % 16
+      const int j = 16 * jb + (lane & 15), blk = j >> 5, bit = j & 31;
+      const bool lo = blk < sb;
+      const int nb = lo ? p.bits_lo : p.bits_hi;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * (lane >> 4) + r;
+        const uint32_t* rw = wrec + m * W + off(blk);
+        int idx = 0;
+        for (int q = 0; q < nb; ++q) idx |= (int)((rw[q] >> bit) & 1u) << q;
+        const uint32_t nr = wnrm[m];
+        float y = f16_bits_to_f32(nr & 0xFFFFu) * cent[(lo ? 0 : 8) + idx];
+        if constexpr (QJ) y = fmaf(scaleq * f16_bits_to_f32(nr >> 16), acc[r], y);
+        if (m < nv) p.out[(v0 + m) * kRqD + j] = y;
+      }
+    }
+  }
+}
+
+template <int BLO, int BHI>
+static int launch_reencode(const QParams& q, bool count, bool qjl, hipStream_t s, int ncu) {
+  if (count) return qjl ? launch_q<128, BLO, BHI, 3, true, true>(q, s, ncu)
+                        : launch_q<128, BLO, BHI, 3, true, false>(q, s, ncu);
+  return qjl ? launch_q<128, BLO, BHI, 3, false, true>(q, s, ncu)
+             : launch_q<128, BLO, BHI, 3, false, false>(q, s, ncu);
+}
+
+}  // namespace tqk
+
+// ---------------------------------------------------------------------------------------
+int tq_launch_requant(const tq_format* fi, const tq_tables* ti, const void* codes_in,
+                      const uint16_t* norms_in, int64_t n, const tq_format* fo,
+                      const tq_tables* to, void* codes_out, uint16_t* norms_out,
+                      int64_t* counters, void* workspace, int64_t workspace_bytes,
+                      hipStream_t stream) {
+  using namespace tqk;
+  const int ncu = tq_num_cus();
+  if (ncu <= 0) return TQ_ERR_HIP;
+  const int64_t chunk = workspace_bytes / (kRqD * 4);
+  const int wi = (int)(tq_record_bytes(fi) / 4), wo = (int)(tq_record_bytes(fo) / 4);
+  RqParams rp{};
+  rp.S = ti->S;
+  rp.out = reinterpret_cast<float*>(workspace);
+  rp.words = wi;
+  rp.split_blocks = fi->split / 32;
+  rp.bits_lo = fi->bits_lo;
+  rp.bits_hi = fi->split == fi->d ? fi->bits_lo : fi->bits_hi;
+  rp.gamma = (float)(std::sqrt(M_PI / 2.0) / kRqD);
+  for (int k = 0; k < 8; ++k) {
+    rp.cent[k] = k < (1 << rp.bits_lo) ? ti->centroids_lo[k] : 0.0f;
+    rp.cent[8 + k] = k < (1 << rp.bits_hi) ? ti->centroids_hi[k] : 0.0f;
+  }
+  QParams q{};
+  fill_format_params(fo, to, q);
+  q.S = to->S;
+  q.counters = reinterpret_cast<unsigned long long*>(counters);
+  q.ld_x = kRqD;
+  q.d_in = kRqD;
+  q.esize = 4;
+  q.staged = 1;  // workspace rows: 16-byte aligned, 512 bytes
+  q.cpr = kRqD * 4 / 16;
+  q.x = workspace;
+  q.src_S = ti->S;
+  q.src_words = wi;
+  q.src_split_blocks = rp.split_blocks;
+  q.src_bits_lo = rp.bits_lo;
+  q.src_bits_hi = rp.bits_hi;
+  q.src_qjl = fi->qjl;
+  for (int k = 0; k < 16; ++k) q.src_cent[k] = rp.cent[k];
+  const size_t src_lds = (fi->qjl ? (size_t)kRqD * kRqRowB : 0) + (size_t)kRqWaves * (16 * 16 + 16) * 4;
+  static bool attr_set[2] = {false, false};
+  if (!attr_set[fi->qjl]) {
+    const void* fn = fi->qjl ? (const void*)requant_source<true> : (const void*)requant_source<false>;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)src_lds) != hipSuccess)
+      return TQ_ERR_HIP;
+    attr_set[fi->qjl] = true;
+  }
+  const int lo = fo->bits_lo, hi = fo->split == fo->d ? fo->bits_lo : fo->bits_hi;
+  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    const int64_t m = (n - c0) < chunk ? (n - c0) : chunk;
+    rp.codes = reinterpret_cast<const uint32_t*>(codes_in) + c0 * wi;
+    rp.norms = reinterpret_cast<const uint32_t*>(norms_in) + c0;
+    rp.n = m;
+    const int64_t tiles = (m + 15) / 16;
+    int64_t grid = (tiles + kRqWaves - 1) / kRqWaves;
+    if (grid > ncu) grid = ncu;
+    if (fi->qjl)
+      hipLaunchKernelGGL(requant_source<true>, dim3((unsigned)grid), dim3(64 * kRqWaves), src_lds, stream, rp);
+    else
+      hipLaunchKernelGGL(requant_source<false>, dim3((unsigned)grid), dim3(64 * kRqWaves), src_lds, stream, rp);
+    if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+    q.n = m;
+    q.codes = reinterpret_cast<uint32_t*>(codes_out) + c0 * wo;
+    q.norms = reinterpret_cast<uint32_t*>(norms_out) + c0;
+    q.src_codes = rp.codes;
+    q.src_norms = rp.norms;
+    int rc = TQ_ERR_SHAPE;
+    const bool cnt = counters != nullptr, qj = fo->qjl != 0;
+    if (lo == 1 && hi == 1) rc = launch_reencode<1, 1>(q, cnt, qj, stream, ncu);
+    else if (lo == 2 && hi == 2) rc = launch_reencode<2, 2>(q, cnt, qj, stream, ncu);
+    else if (lo == 3 && hi == 3) rc = launch_reencode<3, 3>(q, cnt, qj, stream, ncu);
+    else if (lo == 3 && hi == 2) rc = launch_reencode<3, 2>(q, cnt, qj, stream, ncu);
+    else if (lo == 2 && hi == 1) rc = launch_reencode<2, 1>(q, cnt, qj, stream, ncu);
+    if (rc != TQ_OK) return rc;
+  }
+  return TQ_OK;
+}

@@ -183,6 +183,37 @@ int tq_ip_search(const tq_format* fmt, const tq_tables* tab, const void* codes_d
                  int64_t n_q, int32_t k, int64_t* out_ids, float* out_scores,
                  void* workspace, int64_t workspace_bytes, tq_stream_t stream);
 
+/* Workspace bytes tq_requantize uses to re-encode n vectors in one pass (n * d * 4:
+ * one fp32 row per vector).  A smaller workspace is allowed: the call then works in
+ * chunks of workspace_bytes / (d * 4) vectors. */
+int64_t tq_requantize_workspace_bytes(int64_t n, int32_t d);
+
+/* Temporal decay (zhidx article, section "01 turboquant_plus：介绍与详解": older tokens
+ * drop to lower precision): re-encode n stored vectors at another format.  Each record's
+ * reconstruction in the rotated domain, y~ = n16 c[idx] + gamma r16 S_in^T (2 sigma - 1)
+ * (the sign term only when f_in has QJL), is encoded again by the steps of
+ * tq_quantize_kv that follow the rotation: norm ||y~||, codes of f_out, residual and
+ * (with f_out QJL) its signs under t_out->S.  Both formats share the rotation, so the
+ * tables must hold the same sign flips (t_in->S and t_out->S may differ).
+ *   f_in, t_in   : format and tables of the stored records, d = 128
+ *   codes_in     : device, n records of tq_record_bytes(f_in) bytes
+ *   norms_in     : device, n * 2 uint16
+ *   f_out, t_out : the new format and tables, d = 128
+ *   codes_out    : device out, n * tq_record_bytes(f_out) bytes; may equal codes_in
+ *                  (in place) when tq_record_bytes(f_out) <= tq_record_bytes(f_in)
+ *   norms_out    : device out, n * 2 uint16; may equal norms_in
+ *                  Any other overlap between inputs and outputs is an error.
+ *   counters     : as for tq_quantize_kv, nullable
+ *   workspace    : device, >= d * 4 bytes (see tq_requantize_workspace_bytes); no
+ *                  initial contents; calls that share it must not overlap in time
+ * n == 0 is a no-op.  Errors: TQ_ERR_ARG (null pointers, different sign flips, bad
+ * overlap), TQ_ERR_SHAPE (d != 128), TQ_ERR_ALIGN, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+int tq_requantize(const tq_format* f_in, const tq_tables* t_in, const void* codes_in,
+                  const uint16_t* norms_in, int64_t n, const tq_format* f_out,
+                  const tq_tables* t_out, void* codes_out, uint16_t* norms_out,
+                  int64_t* counters, void* workspace, int64_t workspace_bytes,
+                  tq_stream_t stream);
+
 /* Static string naming a status code. */
 const char* tq_strerror(int code);
 

@@ -155,3 +155,36 @@ def test_strerror_names_every_code():
     lib = tq.load()
     seen = {lib.tq_strerror(c).decode() for c in range(0, -7, -1)}
     assert len(seen) == 7 and lib.tq_strerror(-99).decode() == "unknown status code"
+
+
+def test_requantize_validation_before_launch():
+    lib = tq.load()
+    E = tq._lib
+    fi, fo = c_format(128, 3, 3, 128, 1), c_format(128, 2, 2, 128, 1)
+    ti, k1 = _tables(tq.Format(128, 3, 3, 128))
+    to, k2 = _tables(tq.Format(128, 2, 2, 128))
+    n = 1000
+    cin, nin = 0x100000, 0x200000
+    cout, nout, ws = 0x300000, 0x400000, 0x500000
+    wsb = tq.requantize_workspace_bytes(n)
+    assert wsb == n * 512 and tq.requantize_workspace_bytes(0) == 512
+
+    def R(n=n, ci=cin, ni=nin, co=cout, no=nout, w=ws, wb=wsb, f_out=fo, t_out=to, f_in=fi, t_in=ti):
+        P = ctypes.c_void_p
+        return lib.tq_requantize(ctypes.byref(f_in), ctypes.byref(t_in), P(ci), P(ni), n,
+                                 ctypes.byref(f_out), ctypes.byref(t_out), P(co), P(no), None,
+                                 P(w), wb, None)
+    assert R(n=0) == E.TQ_OK
+    assert R(n=-1) == E.TQ_ERR_ARG
+    assert R(wb=511) == E.TQ_ERR_WORKSPACE
+    assert R(co=0x300004) == E.TQ_ERR_ALIGN
+    assert R(co=cin + 64) == E.TQ_ERR_ARG                          # overlaps the input records
+    assert R(w=nout + 16) == E.TQ_ERR_ARG                          # workspace overlaps norms
+    assert R(f_in=fo, t_in=to, f_out=fi, t_out=ti, co=cin, no=nin) == E.TQ_ERR_ARG  # wider in place
+    assert R(f_in=fo, t_in=to, f_out=fi, t_out=ti, n=0, co=cin, no=nin) == E.TQ_OK
+    flipped = np.array(k2[4]); flipped[5] = -1
+    t_flip = c_tables(to.centroids_lo, to.bounds_lo, to.centroids_hi, to.bounds_hi,
+                      flipped.ctypes.data, 0x10000)
+    assert R(t_out=t_flip) == E.TQ_ERR_ARG                         # another rotation
+    f256 = c_format(256, 2, 2, 256, 1)
+    assert R(f_out=f256) == E.TQ_ERR_SHAPE
