@@ -141,6 +141,31 @@ def _variant(tq, torch, dev, ks, vs, q, seq, ws, out, fmt_k, fmt_v, signs, S, st
             "decode_gbs": round(nbytes / t_dc / 1e9, 2)}
 
 
+def _requant_timing(tq, torch, dev, codes_k, norms_k, fmt, tab, signs, S, steps, nvec):
+    """Temporal decay on the same layer: re-encode the b=4 key cache of a slot at b=3 (into
+    a separate buffer, one workspace of the whole tensor), slots rotating as in the main
+    step.  Reports per-call time and the stored bytes read + written per second."""
+    fo = tq.Format.uniform(D, BITS - 1)
+    to = tq.Tables(fo, signs, torch.from_numpy(S).to(dev))
+    out_c = torch.empty((nvec, fo.record_bytes()), dtype=torch.uint8, device=dev)
+    out_n = torch.empty((nvec, 2), dtype=torch.float16, device=dev)
+    ws = torch.empty(tq.requantize_workspace_bytes(nvec, D), dtype=torch.uint8, device=dev)
+    call = lambda s: tq.requantize(codes_k[s].view(nvec, -1), norms_k[s].view(nvec, 2), fmt, tab,
+                                   fo, to, codes_out=out_c, norms_out=out_n, workspace=ws)
+    for i in range(3):
+        call(i % SLOTS)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record(); call(i % SLOTS)
+    ev[steps].record(); torch.cuda.synchronize()
+    t = np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e-3
+    stored = nvec * (fmt.record_bytes() + 4 + fo.record_bytes() + 4)
+    return {"format_in": "3-bit codebook + 1 QJL bit", "format_out": "2-bit codebook + 1 QJL bit",
+            "vectors": nvec, "us_per_call": round(float(t) * 1e6, 3),
+            "stored_gbs": round(stored / t / 1e9, 2)}
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -271,6 +296,8 @@ def main():
             ("b4_k_mse_only_v", fmt, tq.Format.uniform(D, BITS, qjl=False)),
             ("b3.5_kv", tq.Format(D, 3, 2, 64), tq.Format(D, 3, 2, 64)),
             ("b2.5_kv", tq.Format(D, 2, 1, 64), tq.Format(D, 2, 1, 64)))}
+    line["variants"]["requantize_b4_to_b3"] = _requant_timing(tq, torch, dev, codes_k, norms_k, fmt,
+                                                              tab, signs, S, steps, nvec)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(kb, vb, qb, signs, S)
     print(json.dumps(line), flush=True)

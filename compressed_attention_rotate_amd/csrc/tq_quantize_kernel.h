@@ -97,43 +97,7 @@ struct QParams {
   uint32_t sign_mask[8]; // bit j set: coordinate j is multiplied by -1
   float cpos_lo[8], tpos_lo[8], cpos_hi[8], tpos_hi[8];  // positive halves; tpos[0] unused
   float cent_lo[16], cent_hi[16];
-  // Pre-rotated input (XT 3): rows reconstructed from stored records (re-encoding).  The
-  // records are kept for the rare exact fp64 recomputations, which use the stored values
-  // rather than the fp32 rows.
-  const uint32_t* src_codes;
-  const uint32_t* src_norms;
-  const float* src_S;
-  int32_t src_words, src_split_blocks, src_bits_lo, src_bits_hi, src_qjl;
-  float src_cent[16];    // source codebooks: lo table, then hi table
 };
-
-// Exact (fp64) rotated-domain value of coordinate j of source record `row`:
-// n16 c[idx_j] + gamma r16 sum_i S[i][j] (2 sigma_i - 1), gamma = sqrt(pi/2) / D.  Rare
-// path; src_cent is an LDS copy of the source codebooks.
-template <int D>
-__device__ double src_value(const QParams& p, const float* src_cent, int64_t row, int j) {
-  const uint32_t* rec = p.src_codes + row * p.src_words;
-  const int sb = p.src_split_blocks, wlo = p.src_bits_lo + p.src_qjl, whi = p.src_bits_hi + p.src_qjl;
-  auto off = [&](int b) { return b < sb ? b * wlo : sb * wlo + (b - sb) * whi; };
-  const int blk = j >> 5, bit = j & 31;
-  const int nb = blk < sb ? p.src_bits_lo : p.src_bits_hi;
-  int idx = 0;
-  for (int q = 0; q < nb; ++q) idx |= (int)((rec[off(blk) + q] >> bit) & 1u) << q;
-  const uint32_t nr = p.src_norms[row];
-  double val = (double)f16_bits_to_f32(nr & 0xFFFFu) * (double)src_cent[(blk < sb ? 0 : 8) + idx];
-  if (p.src_qjl) {
-    double acc = 0.0;
-    for (int b = 0; b < D / 32; ++b) {
-      const uint32_t sw = rec[off(b) + (b < sb ? p.src_bits_lo : p.src_bits_hi)];
-      for (int i = 0; i < 32; ++i) {
-        const double sv = (double)p.src_S[(int64_t)(32 * b + i) * D + j];
-        acc += ((sw >> i) & 1u) ? sv : -sv;
-      }
-    }
-    val += sqrt(1.5707963267948966) / D * (double)f16_bits_to_f32(nr >> 16) * acc;
-  }
-  return val;
-}
 
 // 16-bit input element -> fp32 (bf16 or fp16)
 template <int XT>
@@ -204,12 +168,8 @@ __device__ void guard_fix(const QParams& p, int64_t v, int m, int n, const uint6
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
     const int j = lane + 64 * e;
-    if constexpr (PRE) {
-      xd[e] = src_value<D>(p, cent_lds + 32, v, j);
-    } else {
-      float xv = (j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
-      xd[e] = (double)xv;
-    }
+    float xv = (j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
+    xd[e] = (double)xv;
   }
 #pragma unroll
   for (int e = 0; e < NE && !PRE; ++e) {
@@ -308,7 +268,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
   uint64_t* bal = reinterpret_cast<uint64_t*>(wl + TV * C::kRowB);   // [pass][blk][4]
   uint64_t* sbal = bal + C::kBal;                                    // [blk][t][r]
   uint32_t* snorm = reinterpret_cast<uint32_t*>(sbal + C::kSBal);   // [TV]
-  __shared__ float cent_lds[48];  // lo table, hi table, then (XT 3) the source tables
+  __shared__ float cent_lds[32];
   __shared__ float cpos_lds[16];  // positive centroids: lo table, then hi table
   __shared__ int wmap[32];        // record word -> (block << 8) | plane, plane 0xFF = signs
 
@@ -317,7 +277,6 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     for (int k = 0; k < 16; ++k) {
       cent_lds[k] = p.cent_lo[k];
       cent_lds[16 + k] = p.cent_hi[k];
-      cent_lds[32 + k] = p.src_cent[k];
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -501,8 +460,7 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           // error is below (log2(D) + 2) 2^-24 < 6e-7: z = y / ||x|| stays within 3e-7 of
           // exact.  The stored fp16 norm must be the correctly rounded one: when a 1e-6
           // relative interval around the estimate straddles an fp16 rounding boundary the
-          // norm is recomputed in fp64 from the input row (still in the tile), or for XT 3
-          // from the source record.
+          // norm is recomputed in fp64 from the input row (still in the tile).
           float nf = __builtin_amdgcn_sqrtf(ss[gg]);
           n16[gg] = f32_to_f16_bits(nf);
           const bool near_mid =
@@ -513,20 +471,15 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
 #pragma unroll
             for (int s = 0; s < NB; ++s) {
               const int j = 32 * s + c;
-              if constexpr (PRE) {
-                const double y = valid[gg] ? src_value<D>(p, cent_lds + 32, v0 + vloc[gg], j) : 0.0;
-                sd = fma(y, y, sd);
+              float x;
+              if (p.staged) {
+                if constexpr (XT == 0 || XT == 3) x = *reinterpret_cast<const float*>(rowp + 4 * j);
+                else x = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * j));
+                x = (valid[gg] && j < p.d_in) ? x : 0.0f;
               } else {
-                float x;
-                if (p.staged) {
-                  if constexpr (XT == 0) x = *reinterpret_cast<const float*>(rowp + 4 * j);
-                  else x = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * j));
-                  x = (valid[gg] && j < p.d_in) ? x : 0.0f;
-                } else {
-                  x = (valid[gg] && j < p.d_in) ? load_elem(p.x, (v0 + vloc[gg]) * p.ld_x + j, XT) : 0.0f;
-                }
-                sd = fma((double)x, (double)x, sd);
+                x = (valid[gg] && j < p.d_in) ? load_elem(p.x, (v0 + vloc[gg]) * p.ld_x + j, XT) : 0.0f;
               }
+              sd = fma((double)x, (double)x, sd);
             }
             sd = half_sum_d(sd);
             const double nrm = sqrt(sd);

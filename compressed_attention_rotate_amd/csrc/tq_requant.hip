@@ -10,10 +10,10 @@
 //              wave tile on v_mfma_f32_16x16x32_f16, with the +-1 signs exact in fp16 and S
 //              split into scaled fp16 hi + lo (the same 2^-22 relative accuracy as the
 //              quantize projection); S^T stays resident in LDS.
-//   quantize:  quantize_kernel with pre-rotated fp32 rows (XT 3).  Its rare exact paths
-//              (fp16 norm near a rounding boundary, projection near zero) recompute y~ in
-//              fp64 from the records, so every decision matches the exact value outside the
-//              same 1e-6 windows as a fresh quantization.
+//   quantize:  quantize_kernel with pre-rotated fp32 rows (XT 3).  Its decisions are exact
+//              for those rows (fp64 rechecks of the norm near an fp16 rounding boundary and
+//              of projections near zero); the rows themselves carry the fp32 error of the
+//              reconstruction, about 1e-7 relative per coordinate.
 // In place: a chunk's source rows are complete before its records are rewritten, and a
 // narrower record never reaches the next chunk's input, so codes_out may equal codes_in.
 #include <hip/hip_runtime.h>
@@ -40,9 +40,15 @@ struct RqParams {
   float cent[16];         // source codebooks: lo table, then hi table
 };
 
-// y~ of 16 records per wave tile.  QJ: the source records carry sign words.
-template <bool QJ>
+// y~ of 16 records per wave tile.  BLO / BHI: source codebook widths below / above the
+// split (run time); QJ: the source records carry sign words.
+template <int BLO, int BHI, bool QJ>
 __global__ __launch_bounds__(64 * kRqWaves) void requant_source(RqParams p) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int Q = QJ ? 1 : 0;
+  constexpr int BMAX = BLO > BHI ? BLO : BHI;
   extern __shared__ __attribute__((aligned(16))) char lds_r[];
   char* St = lds_r;                                          // [128 rows j][hi | lo] fp16
   uint32_t* recs = reinterpret_cast<uint32_t*>(lds_r + (QJ ? kRqD * kRqRowB : 0));
@@ -50,7 +56,7 @@ __global__ __launch_bounds__(64 * kRqWaves) void requant_source(RqParams p) {
   uint32_t* wrec = recs + wave * (16 * 16 + 16);             // 16 records (<= 16 words) + norms
   uint32_t* wnrm = wrec + 16 * 16;
   __shared__ float cent[16];
-  if (tid < 16) cent[tid] = tid < 8 ? p.cent[tid] : p.cent[tid];
+  if (tid < 16) cent[tid] = p.cent[tid];
   if constexpr (QJ) {
     // S^T scaled by 2^10, split hi / lo; the 16-byte units of a row are swizzled by j & 15
     for (int e = tid; e < kRqD * kRqD; e += blockDim.x) {
@@ -65,29 +71,44 @@ __global__ __launch_bounds__(64 * kRqWaves) void requant_source(RqParams p) {
   }
   __syncthreads();
   const int W = p.words, sb = p.split_blocks;
-  const int wlo = p.bits_lo + (QJ ? 1 : 0), whi = p.bits_hi + (QJ ? 1 : 0);
-  auto off = [&](int b) { return b < sb ? b * wlo : sb * wlo + (b - sb) * whi; };
+  auto off = [&](int b) { return b < sb ? b * (BLO + Q) : sb * (BLO + Q) + (b - sb) * (BHI + Q); };
   const float scaleq = p.gamma * (1.0f / 1024.0f);
   const int64_t ntiles = (p.n + 15) / 16;
-  for (int64_t tile = (int64_t)blockIdx.x * kRqWaves + wave; tile < ntiles;
-       tile += (int64_t)gridDim.x * kRqWaves) {
+  const int64_t stride = (int64_t)gridDim.x * kRqWaves;
+  // register prefetch of a tile: record words lane + 64 k (k < 4) and, lanes < 16, a norm
+  uint32_t pw[4], pn = 0;
+  auto fetch = [&](int64_t tile) {
     const int64_t v0 = tile * 16;
     const int nv = (int)((p.n - v0) < 16 ? (p.n - v0) : 16);
-    // stage the tile's records and norms (zeros past the end)
-    for (int i = lane; i < 16 * W; i += 64) wrec[i] = i < nv * W ? p.codes[v0 * W + i] : 0u;
-    if (lane < 16) wnrm[lane] = lane < nv ? p.norms[v0 + lane] : 0u;
-    asm volatile("s_waitcnt lgkmcnt(0) vmcnt(0)" ::: "memory");
-    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    f16x8 a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = lane + 64 * k;
+      pw[k] = (tile < ntiles && i < nv * W) ? p.codes[v0 * W + i] : 0u;
+    }
+    pn = (tile < ntiles && lane < nv) ? p.norms[v0 + lane] : 0u;
+  };
+  int64_t tile = (int64_t)blockIdx.x * kRqWaves + wave;
+  fetch(tile);
+  for (; tile < ntiles; tile += stride) {
+    const int64_t v0 = tile * 16;
+    const int nv = (int)((p.n - v0) < 16 ? (p.n - v0) : 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (lane + 64 * k < 16 * W) wrec[lane + 64 * k] = pw[k];
+    if (lane < 16) wnrm[lane] = pn;
+    fetch(tile + stride);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's rows are visible to the wave
+    f32x4 acc[8];
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) acc[jb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (QJ) {
       // operand A: row m = record lane & 15, k = 8 (lane >> 4) .. + 7 of block ks as +-1
       const int m = lane & 15, kg = lane >> 4;
+      f16x8 a[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint32_t sw = wrec[m * W + off(ks) + (ks < sb ? p.bits_lo : p.bits_hi)];
+        const uint32_t sw = wrec[m * W + off(ks) + (ks < sb ? BLO : BHI)];
         const uint32_t b8 = (sw >> (8 * kg)) & 0xFFu;
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         u32x4 u;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -97,35 +118,44 @@ __global__ __launch_bounds__(64 * kRqWaves) void requant_source(RqParams p) {
         }
         a[ks] = __builtin_bit_cast(f16x8, u);
       }
-    }
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (QJ) {
-        const int j = 16 * jb + (lane & 15), kg = lane >> 4;
+      for (int jb = 0; jb < 8; ++jb) {
+        const int j = 16 * jb + (lane & 15);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int unit = ((4 * ks + kg) ^ (j & 15));
           const f16x8 bh = *reinterpret_cast<const f16x8*>(St + j * kRqRowB + (unit << 4));
           const f16x8 bl = *reinterpret_cast<const f16x8*>(St + j * kRqRowB + 2 * kRqD + (unit << 4));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], bh, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], bl, acc, 0, 0, 0);
+          acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], bh, acc[jb], 0, 0, 0);
+          acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], bl, acc[jb], 0, 0, 0);
         }
       }
-      // acc[r] of lane l: 2^10 (S^T sigma) of record 4 (l >> 4) + r, coordinate 16 jb + l % 16
-      const int j = 16 * jb + (lane & 15), blk = j >> 5, bit = j & 31;
-      const bool lo = blk < sb;
-      const int nb = lo ? p.bits_lo : p.bits_hi;
+    }
+    // acc[jb][r] of lane l: 2^10 (S^T sigma) of record 4 (l >> 4) + r, coordinate 16 jb + l % 16
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * (lane >> 4) + r;
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * (lane >> 4) + r;
+      const uint32_t nr = wnrm[m];
+      const float n16 = f16_bits_to_f32(nr & 0xFFFFu);
+      const float g = scaleq * f16_bits_to_f32(nr >> 16);
+      float* orow = p.out + (v0 + m) * kRqD + (lane & 15);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const bool lo = blk < sb;
         const uint32_t* rw = wrec + m * W + off(blk);
-        int idx = 0;
-        for (int q = 0; q < nb; ++q) idx |= (int)((rw[q] >> bit) & 1u) << q;
-        const uint32_t nr = wnrm[m];
-        float y = f16_bits_to_f32(nr & 0xFFFFu) * cent[(lo ? 0 : 8) + idx];
-        if constexpr (QJ) y = fmaf(scaleq * f16_bits_to_f32(nr >> 16), acc[r], y);
-        if (m < nv) p.out[(v0 + m) * kRqD + j] = y;
+        uint32_t pl[BMAX];
+#pragma unroll
+        for (int q = 0; q < BMAX; ++q) pl[q] = (q < (lo ? BLO : BHI)) ? rw[q] : 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int bit = 16 * h + (lane & 15);
+          int idx = 0;
+#pragma unroll
+          for (int q = 0; q < BMAX; ++q) idx |= (int)((pl[q] >> bit) & 1u) << q;
+          float y = n16 * cent[(lo ? 0 : 8) + idx];
+          if constexpr (QJ) y = fmaf(g, acc[2 * blk + h][r], y);
+          if (m < nv) orow[32 * blk + 16 * h] = y;
+        }
       }
     }
   }
@@ -174,21 +204,17 @@ int tq_launch_requant(const tq_format* fi, const tq_tables* ti, const void* code
   q.staged = 1;  // workspace rows: 16-byte aligned, 512 bytes
   q.cpr = kRqD * 4 / 16;
   q.x = workspace;
-  q.src_S = ti->S;
-  q.src_words = wi;
-  q.src_split_blocks = rp.split_blocks;
-  q.src_bits_lo = rp.bits_lo;
-  q.src_bits_hi = rp.bits_hi;
-  q.src_qjl = fi->qjl;
-  for (int k = 0; k < 16; ++k) q.src_cent[k] = rp.cent[k];
   const size_t src_lds = (fi->qjl ? (size_t)kRqD * kRqRowB : 0) + (size_t)kRqWaves * (16 * 16 + 16) * 4;
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[fi->qjl]) {
-    const void* fn = fi->qjl ? (const void*)requant_source<true> : (const void*)requant_source<false>;
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)src_lds) != hipSuccess)
-      return TQ_ERR_HIP;
-    attr_set[fi->qjl] = true;
-  }
+  const int ilo = rp.bits_lo, ihi = rp.bits_hi;
+  const void* src_fn = nullptr;
+#define TQ_RQ_PICK(a, b)                                                                   \
+  if (ilo == a && ihi == b)                                                                \
+    src_fn = fi->qjl ? (const void*)requant_source<a, b, true> : (const void*)requant_source<a, b, false>;
+  TQ_RQ_PICK(1, 1) TQ_RQ_PICK(2, 2) TQ_RQ_PICK(3, 3) TQ_RQ_PICK(3, 2) TQ_RQ_PICK(2, 1)
+#undef TQ_RQ_PICK
+  if (!src_fn) return TQ_ERR_SHAPE;
+  if (hipFuncSetAttribute(src_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)src_lds) != hipSuccess)
+    return TQ_ERR_HIP;
   const int lo = fo->bits_lo, hi = fo->split == fo->d ? fo->bits_lo : fo->bits_hi;
   for (int64_t c0 = 0; c0 < n; c0 += chunk) {
     const int64_t m = (n - c0) < chunk ? (n - c0) : chunk;
@@ -198,16 +224,13 @@ int tq_launch_requant(const tq_format* fi, const tq_tables* ti, const void* code
     const int64_t tiles = (m + 15) / 16;
     int64_t grid = (tiles + kRqWaves - 1) / kRqWaves;
     if (grid > ncu) grid = ncu;
-    if (fi->qjl)
-      hipLaunchKernelGGL(requant_source<true>, dim3((unsigned)grid), dim3(64 * kRqWaves), src_lds, stream, rp);
-    else
-      hipLaunchKernelGGL(requant_source<false>, dim3((unsigned)grid), dim3(64 * kRqWaves), src_lds, stream, rp);
-    if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+    void* args[] = {&rp};
+    if (hipLaunchKernel(src_fn, dim3((unsigned)grid), dim3(64 * kRqWaves), args, src_lds, stream) != hipSuccess ||
+        hipGetLastError() != hipSuccess)
+      return TQ_ERR_HIP;
     q.n = m;
     q.codes = reinterpret_cast<uint32_t*>(codes_out) + c0 * wo;
     q.norms = reinterpret_cast<uint32_t*>(norms_out) + c0;
-    q.src_codes = rp.codes;
-    q.src_norms = rp.norms;
     int rc = TQ_ERR_SHAPE;
     const bool cnt = counters != nullptr, qj = fo->qjl != 0;
     if (lo == 1 && hi == 1) rc = launch_reencode<1, 1>(q, cnt, qj, stream, ncu);

@@ -1,6 +1,12 @@
 """GPU parity: tq_requantize (temporal decay re-encode, through the C ABI) on records written
-by the oracle, against the oracle's requantize of the same bytes.  Bit-exact codes and signs
-outside the 1e-6 ambiguity windows, as for a fresh quantization."""
+by the oracle, against the oracle's requantize of the same bytes.  Bit-exact codes outside
+the 1e-6 window.  The kernel encodes an fp32 reconstruction (about 1e-7 relative error per
+coordinate, which moves a projection of the unit residual by ~3.5e-7 at one standard
+deviation), so signs are compared outside |u| < 4e-6 and the fp16 norm may differ by one ulp
+within 1e-6 (relative) of a rounding midpoint, as ||r|| may."""
+
+SIGN_WINDOW = 4e-6
+N16_REL = 1e-6
 import numpy as np
 import pytest
 
@@ -72,7 +78,7 @@ def test_requantize_matches_oracle(torch_gpu, f_in, f_out):
     _, S2 = TI.rotation(128, 6200)
     codes, norms, cnt = _gpu_requant(torch_gpu, rec, nrm, f_in, f_out, signs, S, S2)
     q = _oracle_requant(rec, nrm, O.Format(*f_in), S, O.Format(*f_out), S2)
-    rep = compare_quantize(codes, norms, q, O.Format(*f_out))
+    rep = compare_quantize(codes, norms, q, O.Format(*f_out), N16_REL, SIGN_WINDOW)
     print(f"\n{f_in} -> {f_out}: {rep} counters={cnt}")
 
 
@@ -84,7 +90,7 @@ def test_requantize_in_place_in_chunks(torch_gpu):
     codes, norms, _ = _gpu_requant(torch_gpu, rec, nrm, f_in, f_out, signs, S, S, in_place=True,
                                    ws_vectors=700)
     q = _oracle_requant(rec, nrm, O.Format(*f_in), S, O.Format(*f_out), S)
-    compare_quantize(codes, norms, q, O.Format(*f_out))
+    compare_quantize(codes, norms, q, O.Format(*f_out), N16_REL, SIGN_WINDOW)
 
 
 def test_requantize_full_layer_sampled(torch_gpu):
@@ -109,7 +115,8 @@ def test_requantize_full_layer_sampled(torch_gpu):
     q = _oracle_requant(rec, nrm, O.Format.uniform(128, 3), S, O.Format.uniform(128, 2), S)
     got_c = c3.cpu().numpy()[rows]
     got_n = n3.cpu().view(torch.int16).numpy().view(np.uint16)[rows]
-    print("\nfull layer:", compare_quantize(got_c, got_n, q, O.Format.uniform(128, 2)))
+    print("\nfull layer:", compare_quantize(got_c, got_n, q, O.Format.uniform(128, 2), N16_REL,
+                                           SIGN_WINDOW))
 
 
 def test_requantize_argument_errors(torch_gpu):
