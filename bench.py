@@ -141,6 +141,51 @@ def _variant(tq, torch, dev, ks, vs, q, seq, ws, out, fmt_k, fmt_v, signs, S, st
             "decode_gbs": round(nbytes / t_dc / 1e9, 2)}
 
 
+def _paged_timing(tq, torch, dev, ks, q, codes_k, norms_k, codes_v, norms_v, seq, ws, out, fmt,
+                  tab, steps, nvec, page=128):
+    """The same layer in a paged cache of 128-token pages in shuffled order: decode through
+    the block table (slots rotating as in the main step), and quantize-on-write of the key
+    tensor into shuffled slots."""
+    mb = NTOK // page
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(mb)).to(dev)
+    bt = perm.to(torch.int32).view(1, mb).contiguous()
+
+    def pages(t):   # [1, HKV, NTOK, w] -> [mb, HKV, page, w], block j in page perm[j]
+        blocks = t[0].view(HKV, mb, page, -1).permute(1, 0, 2, 3)
+        o = torch.empty_like(blocks)
+        o[perm] = blocks
+        return o.contiguous()
+    pk = [(pages(codes_k[s]), pages(norms_k[s]), pages(codes_v[s]), pages(norms_v[s])) for s in range(SLOTS)]
+    dc = lambda s: tq.attend_decode_paged(q, *pk[s], bt, seq, fmt, tab, workspace=ws, out=out)
+    for i in range(3):
+        dc(i % SLOTS)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record(); dc((i + 1) % SLOTS)
+    ev[steps].record(); torch.cuda.synchronize()
+    t_dec = np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e-3
+    # append: token-major copies of the key tensor, one slot per token
+    xs = [ks[s][0].permute(1, 0, 2).contiguous() for s in range(2)]
+    slots = torch.from_numpy(np.random.default_rng(6).permutation(NTOK).astype(np.int64)).to(dev)
+    rb = fmt.record_bytes()
+    cache = torch.empty((mb, HKV, page, rb), dtype=torch.uint8, device=dev)
+    cnorm = torch.empty((mb, HKV, page, 2), dtype=torch.float16, device=dev)
+    ap = lambda s: tq.quantize_kv_paged(xs[s % 2], fmt, tab, slots, cache, cnorm)
+    for i in range(3):
+        ap(i)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i].record(); ap(i)
+    ev[steps].record(); torch.cuda.synchronize()
+    t_app = np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e-3
+    nbytes = 2 * nvec * (rb + 4)
+    return {"page_tokens": page, "decode_us": round(float(t_dec) * 1e6, 3),
+            "decode_gbs": round(nbytes / t_dec / 1e9, 2),
+            "append_us_per_tensor": round(float(t_app) * 1e6, 3),
+            "append_tokens_per_s": round(NTOK * BATCH / t_app, 1)}
+
+
 def _requant_timing(tq, torch, dev, codes_k, norms_k, fmt, tab, signs, S, steps, nvec):
     """Temporal decay on the same layer: re-encode the b=4 key cache of a slot at b=3 (into
     a separate buffer, one workspace of the whole tensor), slots rotating as in the main
@@ -296,6 +341,8 @@ def main():
             ("b4_k_mse_only_v", fmt, tq.Format.uniform(D, BITS, qjl=False)),
             ("b3.5_kv", tq.Format(D, 3, 2, 64), tq.Format(D, 3, 2, 64)),
             ("b2.5_kv", tq.Format(D, 2, 1, 64), tq.Format(D, 2, 1, 64)))}
+    line["variants"]["paged_b4"] = _paged_timing(tq, torch, dev, ks, q, codes_k, norms_k, codes_v,
+                                                 norms_v, seq, ws, out, fmt, tab, steps, nvec)
     line["variants"]["requantize_b4_to_b3"] = _requant_timing(tq, torch, dev, codes_k, norms_k, fmt,
                                                               tab, signs, S, steps, nvec)
     if not args.no_cpu_baseline:

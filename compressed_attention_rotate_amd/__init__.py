@@ -18,7 +18,8 @@ from ._lib import (LIB_PATH, TQ_BF16, TQ_F16, TQ_F32, Format, Tables, TQError, b
 
 __all__ = ["Format", "Tables", "TQError", "build_codebook", "quantize_kv", "attend_decode",
            "ip_search", "requantize", "attend_workspace_bytes", "search_workspace_bytes",
-           "requantize_workspace_bytes", "LIB_PATH", "load"]
+           "requantize_workspace_bytes", "quantize_kv_paged", "attend_decode_paged", "LIB_PATH",
+           "load"]
 
 
 def _torch():
@@ -124,6 +125,81 @@ def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format
                                  _ptr(lg), _ptr(skipped), _ptr(workspace), workspace.numel(),
                                  _stream(q.device))
     _check(rc, "tq_attend_decode")
+    return (out, lg) if logits else out
+
+
+def quantize_kv_paged(x, fmt: Format, tables: Tables, slot_mapping, codes_cache, norms_cache,
+                      counters=None):
+    """Append: quantize new keys or values x [n_tokens, hkv, d_in] (CUDA, fp32 / bf16 / fp16)
+    into a paged cache codes_cache [num_pages, hkv, page_size, record_bytes] uint8,
+    norms_cache [num_pages, hkv, page_size, 2] fp16, token i going to slot slot_mapping[i]
+    (int64, page * page_size + offset; negative: skipped)."""
+    torch = _torch()
+    n_tokens, hkv, d_in = x.shape
+    num_pages, hkv2, page_size, rb = codes_cache.shape
+    if hkv2 != hkv or rb != fmt.record_bytes() or not codes_cache.is_contiguous():
+        raise ValueError("bad paged cache tensor")
+    if norms_cache.shape != (num_pages, hkv, page_size, 2) or not norms_cache.is_contiguous():
+        raise ValueError("bad paged norms tensor")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != n_tokens:
+        raise ValueError("slot_mapping must be int64 [n_tokens]")
+    x2 = x.reshape(n_tokens * hkv, d_in)
+    if x2.stride(-1) != 1:
+        x2 = x2.contiguous()
+    f, t = fmt.c(), tables.c()
+    ld = x2.stride(0) if x2.shape[0] > 1 else d_in
+    rc = load().tq_quantize_kv_paged(ctypes.byref(f), ctypes.byref(t), _ptr(x2), _dtype_code(x2),
+                                     n_tokens, hkv, d_in, ld, _ptr(slot_mapping), page_size,
+                                     num_pages, _ptr(codes_cache), _ptr(norms_cache),
+                                     _ptr(counters), _stream(x.device))
+    _check(rc, "tq_quantize_kv_paged")
+
+
+def attend_decode_paged(q, codes_k, norms_k, codes_v, norms_v, block_table, seq_lens,
+                        fmt_k: Format, tables_k: Tables, fmt_v: Format = None,
+                        tables_v: Tables = None, scale: float = None, tau: float = 0.0,
+                        logits: bool = False, skipped=None, workspace=None, out=None):
+    """One decode step over paged caches: codes_k [num_pages, hkv, page_size, rbk] uint8,
+    norms_k [num_pages, hkv, page_size, 2] fp16 (the same for v), block_table int32
+    [batch, max_blocks] of page ids, seq_lens int32 [batch].  Returns out fp32 [batch, hq, d]
+    (and logits fp32 [batch, hq, max_blocks * page_size] if asked)."""
+    torch = _torch()
+    fmt_v = fmt_k if fmt_v is None else fmt_v
+    tables_v = tables_k if tables_v is None else tables_v
+    batch, hq, d = q.shape
+    num_pages, hkv, page_size, _ = codes_k.shape
+    for t, rb in ((codes_k, fmt_k.record_bytes()), (codes_v, fmt_v.record_bytes())):
+        if t.dtype != torch.uint8 or t.shape[:3] != (num_pages, hkv, page_size) or t.shape[3] != rb \
+                or not t.is_contiguous():
+            raise ValueError("bad paged cache tensor")
+    for t in (norms_k, norms_v):
+        if t.shape != (num_pages, hkv, page_size, 2) or not t.is_contiguous():
+            raise ValueError("bad paged norms tensor")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != batch \
+            or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [batch, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != batch:
+        raise ValueError("seq_lens must be int32 [batch]")
+    max_blocks = block_table.shape[1]
+    capacity = max_blocks * page_size
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q = q.contiguous()
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
+    lg = torch.empty((batch, hq, capacity), dtype=torch.float32, device=q.device) if logits else None
+    wsb = attend_workspace_bytes(batch, hq, hkv, capacity, d)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    fk, fv, tk, tv = fmt_k.c(), fmt_v.c(), tables_k.c(), tables_v.c()
+    rc = load().tq_attend_decode_paged(ctypes.byref(fk), ctypes.byref(tk), ctypes.byref(fv),
+                                       ctypes.byref(tv), _ptr(q), _dtype_code(q), batch, hq, hkv,
+                                       _ptr(codes_k), _ptr(norms_k), _ptr(codes_v), _ptr(norms_v),
+                                       page_size, num_pages, _ptr(block_table), max_blocks,
+                                       _ptr(seq_lens), float(scale), float(tau), _ptr(out), _ptr(lg),
+                                       _ptr(skipped), _ptr(workspace), workspace.numel(),
+                                       _stream(q.device))
+    _check(rc, "tq_attend_decode_paged")
     return (out, lg) if logits else out
 
 

@@ -46,6 +46,24 @@ int check_tables(const tq_format* f, const tq_tables* t) {
 }
 
 bool dtype_ok(int dt) { return dt == TQ_F32 || dt == TQ_BF16 || dt == TQ_F16; }
+
+// log2 of a page size that is a power of two in [64, 2^20], else -1
+int page_log2(int32_t page_size) {
+  if (page_size < 64 || page_size > (1 << 20) || (page_size & (page_size - 1))) return -1;
+  int lg = 0;
+  while ((1 << lg) < page_size) ++lg;
+  return lg;
+}
+
+int quantize_checked(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
+                     int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
+                     int64_t* counters, tq_stream_t stream, const tq_paged_dst* paged);
+int decode_checked(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                   const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch, int32_t hq,
+                   int32_t hkv, const void* codes_k, const uint16_t* norms_k, const void* codes_v,
+                   const uint16_t* norms_v, int64_t capacity, const int32_t* seq_lens, float scale,
+                   float tau, float* out, float* logits, int64_t* skipped, void* workspace,
+                   int64_t workspace_bytes, tq_stream_t stream, const tq_paged_src* paged);
 uintptr_t dtype_size(int dt) { return dt == TQ_F32 ? 4 : 2; }
 
 }  // namespace
@@ -84,6 +102,29 @@ int64_t tq_record_bytes(const tq_format* f) {
 int tq_quantize_kv(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
                    int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
                    int64_t* counters, tq_stream_t stream) {
+  return quantize_checked(f, t, x, x_dtype, n, d_in, ld_x, codes, norms, counters, stream, nullptr);
+}
+
+int tq_quantize_kv_paged(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
+                         int64_t n_tokens, int32_t hkv, int32_t d_in, int64_t ld_x,
+                         const int64_t* slot_mapping, int32_t page_size, int64_t num_pages,
+                         void* codes_cache, uint16_t* norms_cache, int64_t* counters,
+                         tq_stream_t stream) {
+  const int lg = page_log2(page_size);
+  if (lg < 0 || num_pages < 1 || hkv < 1 || n_tokens < 0) return TQ_ERR_ARG;
+  if (n_tokens > 0 && !slot_mapping) return TQ_ERR_ARG;
+  if (slot_mapping && !aligned(slot_mapping, 8)) return TQ_ERR_ALIGN;
+  const tq_paged_dst dst{slot_mapping, num_pages, hkv, lg};
+  return quantize_checked(f, t, x, x_dtype, n_tokens * hkv, d_in, ld_x, codes_cache, norms_cache,
+                          counters, stream, &dst);
+}
+
+}  // extern "C"
+
+namespace {
+int quantize_checked(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
+                     int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
+                     int64_t* counters, tq_stream_t stream, const tq_paged_dst* paged) {
   int rc = tq_check_format(f);
   if (rc) return rc;
   if (n < 0 || !dtype_ok(x_dtype)) return TQ_ERR_ARG;
@@ -96,8 +137,11 @@ int tq_quantize_kv(const tq_format* f, const tq_tables* t, const void* x, int32_
       (counters && !aligned(counters, 8)))
     return TQ_ERR_ALIGN;
   return tq_launch_quantize(f, t, x, x_dtype, n, d_in, ld_x, codes, norms, counters,
-                            reinterpret_cast<hipStream_t>(stream));
+                            reinterpret_cast<hipStream_t>(stream), paged);
 }
+}  // namespace
+
+extern "C" {
 
 int64_t tq_attend_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int64_t capacity,
                                   int32_t d) {
@@ -112,6 +156,37 @@ int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      const int32_t* seq_lens, float scale, float tau, float* out,
                      float* logits, int64_t* skipped, void* workspace,
                      int64_t workspace_bytes, tq_stream_t stream) {
+  return decode_checked(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
+                        norms_v, capacity, seq_lens, scale, tau, out, logits, skipped, workspace,
+                        workspace_bytes, stream, nullptr);
+}
+
+int tq_attend_decode_paged(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                           const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
+                           int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                           const void* codes_v, const uint16_t* norms_v, int32_t page_size,
+                           int64_t num_pages, const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* seq_lens, float scale, float tau, float* out,
+                           float* logits, int64_t* skipped, void* workspace,
+                           int64_t workspace_bytes, tq_stream_t stream) {
+  const int lg = page_log2(page_size);
+  if (lg < 0 || num_pages < 1 || max_blocks < 1 || !block_table) return TQ_ERR_ARG;
+  if (!aligned(block_table, 4)) return TQ_ERR_ALIGN;
+  const tq_paged_src src{block_table, num_pages, max_blocks, lg};
+  return decode_checked(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
+                        norms_v, (int64_t)max_blocks << lg, seq_lens, scale, tau, out, logits,
+                        skipped, workspace, workspace_bytes, stream, &src);
+}
+
+}  // extern "C"
+
+namespace {
+int decode_checked(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                   const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch, int32_t hq,
+                   int32_t hkv, const void* codes_k, const uint16_t* norms_k, const void* codes_v,
+                   const uint16_t* norms_v, int64_t capacity, const int32_t* seq_lens, float scale,
+                   float tau, float* out, float* logits, int64_t* skipped, void* workspace,
+                   int64_t workspace_bytes, tq_stream_t stream, const tq_paged_src* paged) {
   int rc = tq_check_format(fk);
   if (rc) return rc;
   if ((rc = tq_check_format(fv))) return rc;
@@ -132,8 +207,11 @@ int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
   if (workspace_bytes < plan.ws_bytes) return TQ_ERR_WORKSPACE;
   return tq_launch_decode(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
                           norms_v, capacity, seq_lens, scale, tau, out, logits, skipped, workspace,
-                          plan, reinterpret_cast<hipStream_t>(stream));
+                          plan, reinterpret_cast<hipStream_t>(stream), paged);
 }
+}  // namespace
+
+extern "C" {
 
 int64_t tq_search_workspace_bytes(int64_t n_q, int32_t k, int64_t n_db, int32_t d) {
   if (n_q < 0 || k < 1 || k > 64 || n_db < k || (d != 128 && d != 256)) return -1;

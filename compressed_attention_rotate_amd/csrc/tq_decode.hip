@@ -164,9 +164,15 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      const void* codes_v, const uint16_t* norms_v, int64_t capacity,
                      const int32_t* seq_lens, float scale, float tau, float* out, float* logits,
                      int64_t* skipped, void* workspace, const tq_decode_plan& plan,
-                     hipStream_t stream) {
+                     hipStream_t stream, const tq_paged_src* paged) {
   using namespace tqk;
   DecodeParams p{};
+  if (paged) {
+    p.block_table = paged->block_table;
+    p.num_pages = paged->num_pages;
+    p.max_blocks = paged->max_blocks;
+    p.page_log2 = paged->page_log2;
+  }
   p.q = q;
   p.codes_k = reinterpret_cast<const uint32_t*>(codes_k);
   p.norms_k = reinterpret_cast<const uint32_t*>(norms_k);

@@ -118,6 +118,13 @@ struct DecodeParams {
   float alpha_k[2][4];  // Walsh coefficients of the key codebooks (lo, hi parts)
   float cent_v[2][8];   // value codebooks (lo, hi)
   int32_t ksplitb;
+  // Paged cache (block_table == nullptr: contiguous [batch][hkv][capacity] rows).  Token t
+  // of batch b, KV head h is row (page * hkv + h) * 2^page_log2 + t % 2^page_log2 with
+  // page = block_table[b * max_blocks + t / 2^page_log2]; a page id outside
+  // [0, num_pages) makes its tokens count as absent.
+  const int32_t* block_table;
+  int64_t num_pages;
+  int32_t max_blocks, page_log2;
 };
 
 // LDS layout of one scan workgroup (floats).
@@ -239,22 +246,34 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   const int bk = unit / nchunk;  // b * hkv + kv head
   const int b = bk / p.hkv;
   const int h0 = (bk % p.hkv) * p.group + chunk * GC;
-  const int64_t seq = p.seq_lens[b];
+  int64_t seq = p.seq_lens[b];
+  if (seq > p.capacity) seq = p.capacity;
   const int64_t t_begin = (int64_t)blockIdx.x * p.tokens_per_split;
   int64_t t_end = t_begin + p.tokens_per_split;
   if (t_end > seq) t_end = seq;
   const int64_t kv_base = (int64_t)bk * p.capacity;
   const bool gated = p.tau > 0.0f;
 
+  // cache row of token tt0 (a multiple of the 64-token tile, so a tile never straddles a
+  // page); -1 for a page id out of range
+  auto tile_row = [&](int64_t tt0) -> int64_t {
+    if (!p.block_table) return kv_base + tt0;
+    const int32_t pg = p.block_table[(int64_t)b * p.max_blocks + (tt0 >> p.page_log2)];
+    if (pg < 0 || (int64_t)pg >= p.num_pages) return -1;
+    return (((int64_t)pg * p.hkv + (bk % p.hkv)) << p.page_log2) + (tt0 & ((1ll << p.page_log2) - 1));
+  };
   // ---- register prefetch of one tile: key record, value record, norms
   uint32_t kw[KW], vwr[VW], knr = 0, vnr = 0;
+  int64_t prow = -1;  // cache row of the prefetched tile's first token
   auto fetch = [&](int64_t tt0) {
     const int64_t t = tt0 + lane;
-    if (tt0 < t_end && t < t_end) {
-      load_record<KW, KR::VEC>(p.codes_k + (kv_base + t) * KW, kw);
-      if (!gated) load_record<VW, VR::VEC>(p.codes_v + (kv_base + t) * VW, vwr);
-      knr = p.norms_k[kv_base + t];
-      vnr = p.norms_v[kv_base + t];
+    prow = tt0 < t_end ? tile_row(tt0) : -1;
+    if (prow >= 0 && t < t_end) {
+      const int64_t row = prow + lane;
+      load_record<KW, KR::VEC>(p.codes_k + row * KW, kw);
+      if (!gated) load_record<VW, VR::VEC>(p.codes_v + row * VW, vwr);
+      knr = p.norms_k[row];
+      vnr = p.norms_v[row];
     }
   };
   int64_t t0 = t_begin + (int64_t)wave * kTile;
@@ -492,13 +511,15 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
 
   for (; t0 < t_end; t0 += (int64_t)kWaves * kTile) {
     const int64_t t = t0 + lane;
-    const bool valid = t < t_end;
+    const int64_t row0 = prow;
+    const bool valid = t < t_end && row0 >= 0;
     uint32_t w[KW], vrec[VW];
 #pragma unroll
     for (int i = 0; i < KW; ++i) w[i] = kw[i];
 #pragma unroll
     for (int i = 0; i < VW; ++i) vrec[i] = vwr[i];
-    const uint32_t kn = knr, vn = vnr;
+    // norms of absent tokens are zeroed so a stale value never meets a zero weight
+    const uint32_t kn = valid ? knr : 0u, vn = valid ? vnr : 0u;
     fetch(t0 + (int64_t)kWaves * kTile);
     // ---------------- keys: lane = token
     float mse[GC], qjl[GC];
@@ -569,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
         }
       }
       if (any_keep) {
-        if (gated) load_record<VW, VR::VEC>(p.codes_v + (kv_base + t) * VW, vrec);
+        if (gated) load_record<VW, VR::VEC>(p.codes_v + (row0 + lane) * VW, vrec);
         uint32_t* rv = reinterpret_cast<uint32_t*>(row + kW0);
 #pragma unroll
         for (int i = 0; i < VW; ++i) rv[i] = vrec[i];

@@ -8,9 +8,17 @@
 // Compute units of the current device (cached per device); <= 0 on failure.
 int tq_num_cus();
 
+// Paged destination of a quantize launch: vector v = token * page_heads + head is written
+// to row (page * page_heads + head) * 2^page_log2 + offset of the cache.
+struct tq_paged_dst {
+  const int64_t* slots;   // device, one slot per token
+  int64_t num_pages;
+  int32_t page_heads, page_log2;
+};
+
 int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
                        int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
-                       int64_t* counters, hipStream_t stream);
+                       int64_t* counters, hipStream_t stream, const tq_paged_dst* paged = nullptr);
 
 struct tq_decode_plan {
   int32_t n_split;        // token splits per (batch, kv head)
@@ -27,13 +35,20 @@ bool tq_decode_formats_supported(const tq_format* fk, const tq_format* fv);
 
 tq_decode_plan tq_plan_decode(int32_t batch, int32_t hq, int32_t hkv, int64_t capacity, int32_t d);
 
+// Paged source of a decode launch (see DecodeParams).
+struct tq_paged_src {
+  const int32_t* block_table;  // device [batch][max_blocks]
+  int64_t num_pages;
+  int32_t max_blocks, page_log2;
+};
+
 int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
                      const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
                      int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
                      const void* codes_v, const uint16_t* norms_v, int64_t capacity,
                      const int32_t* seq_lens, float scale, float tau, float* out, float* logits,
                      int64_t* skipped, void* workspace, const tq_decode_plan& plan,
-                     hipStream_t stream);
+                     hipStream_t stream, const tq_paged_src* paged = nullptr);
 
 struct tq_search_plan {
   int32_t n_chunks;       // database chunks scanned independently

@@ -16,9 +16,15 @@ extern template int launch_quantize<256, 3, 3>(const QParams&, int, bool, hipStr
 // ---------------------------------------------------------------------------------------
 int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
                        int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
-                       int64_t* counters, hipStream_t stream) {
+                       int64_t* counters, hipStream_t stream, const tq_paged_dst* paged) {
   using namespace tqk;
   QParams p{};
+  if (paged) {
+    p.slots = paged->slots;
+    p.num_pages = paged->num_pages;
+    p.page_heads = paged->page_heads;
+    p.page_log2 = paged->page_log2;
+  }
   p.x = x;
   p.S = t->S;
   p.codes = reinterpret_cast<uint32_t*>(codes);

@@ -97,7 +97,25 @@ struct QParams {
   uint32_t sign_mask[8]; // bit j set: coordinate j is multiplied by -1
   float cpos_lo[8], tpos_lo[8], cpos_hi[8], tpos_hi[8];  // positive halves; tpos[0] unused
   float cent_lo[16], cent_hi[16];
+  // Paged output (slots == nullptr: record and norm of vector v at index v).  Vector
+  // v = token * page_heads + head goes to row (page * page_heads + head) * page_size + off
+  // of the cache, with page, off = slots[token] / page_size, % page_size; a negative slot or
+  // one at or past num_pages * page_size is not written.
+  const int64_t* slots;
+  int64_t num_pages;
+  int32_t page_heads, page_log2;
 };
+
+// Destination row of vector vg (or -1: not written).
+__device__ __forceinline__ int64_t dest_row(const QParams& p, int64_t vg) {
+  if (!p.slots) return vg;
+  const int64_t tok = vg / p.page_heads;
+  const int head = (int)(vg - tok * p.page_heads);
+  const int64_t sl = p.slots[tok];
+  const int64_t page = sl >> p.page_log2;
+  if (sl < 0 || page >= p.num_pages) return -1;
+  return ((page * p.page_heads + head) << p.page_log2) + (sl & ((1ll << p.page_log2) - 1));
+}
 
 // 16-bit input element -> fp32 (bf16 or fp16)
 template <int XT>
@@ -645,7 +663,6 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     if (!active) continue;
     // ---------------- store the tile: assemble record words from the ballot tables
     const int nvalid = (int)((p.n - v0) < TV ? (p.n - v0) : TV);
-    uint32_t* dst = p.codes + v0 * p.words;
     const uint32_t* b32 = reinterpret_cast<const uint32_t*>(bal);
     const uint16_t* s16 = reinterpret_cast<const uint16_t*>(sbal);
     for (int vb = 0; vb < nvalid; vb += vpi) {
@@ -659,10 +676,14 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           word = (uint32_t)s16[((s_blk * 2 + 0) * 4 + rr) * 4 + gq] |
                  ((uint32_t)s16[((s_blk * 2 + 1) * 4 + rr) * 4 + gq] << 16);
         }
-        dst[v * p.words + sw] = word;
+        const int64_t row = dest_row(p, v0 + v);
+        if (row >= 0) p.codes[row * p.words + sw] = word;
       }
     }
-    if (lane < nvalid) p.norms[v0 + lane] = snorm[lane];
+    if (lane < nvalid) {
+      const int64_t row = dest_row(p, v0 + lane);
+      if (row >= 0) p.norms[row] = snorm[lane];
+    }
   }
   if constexpr (COUNT) {
     unsigned long long tot = cnt_amb, ovf = cnt_ovf;

@@ -164,6 +164,43 @@ int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      float* logits, int64_t* skipped, void* workspace,
                      int64_t workspace_bytes, tq_stream_t stream);
 
+/* Paged cache.  A cache of fixed-size pages, as serving engines keep it: codes
+ * [num_pages][hkv][page_size] records and norms [num_pages][hkv][page_size][2] uint16;
+ * a sequence's token t lives in page block_table[b][t / page_size] at offset
+ * t % page_size.  page_size is a power of two in [64, 2^20].
+ *
+ * Append (quantize-on-write): quantize the keys or values of n_tokens new tokens and
+ * write each one's records into its slot.
+ *   x            : device, n_tokens * hkv rows of d_in elements ([token][kv head] order),
+ *                  dtype x_dtype, row stride ld_x elements
+ *   slot_mapping : device int64 [n_tokens]: page * page_size + offset of each token; a
+ *                  negative slot, or one >= num_pages * page_size, is not written.  Two
+ *                  tokens must not share a slot.
+ *   codes_cache, norms_cache : device, the paged cache (only the slots written change)
+ *   counters     : as for tq_quantize_kv
+ * Errors: as tq_quantize_kv, and TQ_ERR_ARG for a bad page_size / num_pages / hkv. */
+int tq_quantize_kv_paged(const tq_format* fmt, const tq_tables* tab, const void* x,
+                         int32_t x_dtype, int64_t n_tokens, int32_t hkv, int32_t d_in,
+                         int64_t ld_x, const int64_t* slot_mapping, int32_t page_size,
+                         int64_t num_pages, void* codes_cache, uint16_t* norms_cache,
+                         int64_t* counters, tq_stream_t stream);
+
+/* tq_attend_decode over paged caches.  block_table: device int32 [batch][max_blocks]
+ * page ids; the logical capacity is max_blocks * page_size (seq_lens are clamped to it,
+ * logits are laid out [batch][hq][capacity], and the workspace is
+ * tq_attend_workspace_bytes(batch, hq, hkv, max_blocks * page_size, 128)).  A page id
+ * outside [0, num_pages) makes its tokens absent (they take no part in the softmax).
+ * Errors: as tq_attend_decode, and TQ_ERR_ARG for a bad page_size / num_pages /
+ * max_blocks or a null block_table. */
+int tq_attend_decode_paged(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                           const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
+                           int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                           const void* codes_v, const uint16_t* norms_v, int32_t page_size,
+                           int64_t num_pages, const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* seq_lens, float scale, float tau, float* out,
+                           float* logits, int64_t* skipped, void* workspace,
+                           int64_t workspace_bytes, tq_stream_t stream);
+
 /* Workspace bytes tq_ip_search needs. */
 int64_t tq_search_workspace_bytes(int64_t n_q, int32_t k, int64_t n_db, int32_t d);
 

@@ -188,3 +188,40 @@ def test_requantize_validation_before_launch():
     assert R(t_out=t_flip) == E.TQ_ERR_ARG                         # another rotation
     f256 = c_format(256, 2, 2, 256, 1)
     assert R(f_out=f256) == E.TQ_ERR_SHAPE
+
+
+def test_paged_validation_before_launch():
+    lib = tq.load()
+    E = tq._lib
+    f = c_format(128, 3, 3, 128, 1)
+    t, keep = _tables(tq.Format(128, 3, 3, 128))
+    P = ctypes.c_void_p
+    x, slots, cache, norms = P(0x100000), P(0x200000), P(0x300000), P(0x400000)
+
+    def A(n_tokens=10, hkv=8, page=64, pages=4, sl=slots):
+        return lib.tq_quantize_kv_paged(ctypes.byref(f), ctypes.byref(t), x, 1, n_tokens, hkv, 128,
+                                        128, sl, page, pages, cache, norms, None, None)
+    assert A(n_tokens=0) == E.TQ_OK
+    assert A(page=96) == E.TQ_ERR_ARG                  # not a power of two
+    assert A(page=32) == E.TQ_ERR_ARG                  # below one 64-token tile
+    assert A(pages=0) == E.TQ_ERR_ARG
+    assert A(hkv=0) == E.TQ_ERR_ARG
+    assert A(sl=None) == E.TQ_ERR_ARG
+    assert A(sl=P(0x200004)) == E.TQ_ERR_ALIGN
+    bt, sl32, q, ws = P(0x500000), P(0x600000), P(0x700000), P(0x800000)
+    wsb = tq.attend_workspace_bytes(1, 32, 8, 4 * 64)
+
+    def D(page=64, pages=4, table=bt, mb=4, hq=32, wb=wsb):
+        return lib.tq_attend_decode_paged(ctypes.byref(f), ctypes.byref(t), ctypes.byref(f),
+                                          ctypes.byref(t), q, 1, 1, hq, 8, cache, norms, cache,
+                                          norms, page, pages, table, mb, sl32, 0.088, 0.0, q, None,
+                                          None, ws, wb, None)
+    assert D(page=100) == E.TQ_ERR_ARG
+    assert D(pages=0) == E.TQ_ERR_ARG
+    assert D(table=None) == E.TQ_ERR_ARG
+    assert D(mb=0) == E.TQ_ERR_ARG
+    assert D(table=P(0x500002)) == E.TQ_ERR_ALIGN
+    assert D(hq=30) == E.TQ_ERR_SHAPE
+    assert D(wb=wsb - 1) == E.TQ_ERR_WORKSPACE
+    assert tq.attend_workspace_bytes(1, 32, 8, 64 * 64) > wsb
+    assert D(mb=64) == E.TQ_ERR_WORKSPACE              # the capacity grows with max_blocks

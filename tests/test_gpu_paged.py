@@ -1,0 +1,183 @@
+"""GPU parity of the paged cache: quantize-on-write into slots of a paged cache, and decode
+through a block table, against the oracle (records at the same slots; attention over the
+gathered tokens) and, exactly, against the contiguous GPU decode of the same data."""
+import math
+
+import numpy as np
+import pytest
+
+import tq_inputs as TI
+from oracle import tq_oracle as O
+from parity_utils import compare_quantize, oracle_decode, oracle_pack_cache, oracle_quantize
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_RTOL = 1e-4
+OUT_ATOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import compressed_attention_rotate_amd as tq
+    tq.load()
+    return torch
+
+
+def _paginate(rec, nrm, seq_lens, page_size, seed, holes=()):
+    """Scatter a contiguous cache [batch, hkv, cap, ...] into shuffled pages; returns
+    (codes_pages [P, hkv, page, rb], norms_pages [P, hkv, page, 2], block_table [batch, mb])."""
+    batch, hkv, cap, rb = rec.shape
+    mb = (cap + page_size - 1) // page_size
+    need = batch * mb
+    n_pages = need + 3                                   # spare pages stay unused
+    perm = TI.gen(seed).permutation(n_pages)[:need].reshape(batch, mb).astype(np.int32)
+    cp = np.full((n_pages, hkv, page_size, rb), 0xA5, np.uint8)
+    npg = np.zeros((n_pages, hkv, page_size, 2), np.uint16)
+    for b in range(batch):
+        for blk in range(mb):
+            lo, hi = blk * page_size, min(cap, (blk + 1) * page_size)
+            cp[perm[b, blk], :, : hi - lo] = rec[b, :, lo:hi]
+            npg[perm[b, blk], :, : hi - lo] = nrm[b, :, lo:hi]
+    bt = perm.copy()
+    for b, blk in holes:
+        bt[b, blk] = -1
+    return cp, npg, bt
+
+
+def _case(torch, fk, fv, page_size, seed, batch=2, hq=32, hkv=8, ntok=1000, seq=(1000, 611),
+          holes=()):
+    import compressed_attention_rotate_amd as tq
+    d = 128
+    kb, vb, _ = TI.kv_layer(batch, hkv, ntok, d, seed=seed)
+    qb = TI.decode_queries(batch, hq, d, seed)
+    signs, S = TI.rotation(d, seed + 1)
+    rk, nk, _ = oracle_pack_cache(kb, O.Format(*fk), signs, S, bf16=True)
+    rv, nv, _ = oracle_pack_cache(vb, O.Format(*fv), signs, S, bf16=True)
+    ck, nkp, bt = _paginate(rk, nk, seq, page_size, seed + 2, holes)
+    cv, nvp, _ = _paginate(rv, nv, seq, page_size, seed + 2, holes)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    f16 = lambda a: dev(a.view(np.int16)).view(torch.float16)
+    fmt_k, fmt_v = tq.Format(*fk), tq.Format(*fv)
+    tk = tq.Tables(fmt_k, signs, torch.from_numpy(S).cuda())
+    tv = tq.Tables(fmt_v, signs, torch.from_numpy(S).cuda())
+    q = dev(qb.view(np.int16)).view(torch.bfloat16)
+    sl = dev(np.asarray(seq, np.int32))
+    out_p, lg_p = tq.attend_decode_paged(q, dev(ck), f16(nkp), dev(cv), f16(nvp), dev(bt), sl, fmt_k, tk,
+                                         fmt_v, tv, logits=True)
+    torch.cuda.synchronize()
+    out_p, lg_p = out_p.cpu().numpy(), lg_p.cpu().numpy()
+    # oracle over the tokens that are present (a hole removes its page's tokens)
+    present = np.ones((batch, ntok), bool)
+    for b, blk in holes:
+        present[b, blk * page_size:(blk + 1) * page_size] = False
+    q64 = TI.bf16_to_f64(qb)
+    for b in range(batch):
+        keep = np.nonzero(present[b, : seq[b]])[0]
+        L = len(keep)
+        o, lgo, sco, _, _ = oracle_decode(q64[b:b + 1], rk[b:b + 1, :, keep], nk[b:b + 1, :, keep],
+                                          rv[b:b + 1, :, keep], nv[b:b + 1, :, keep], [L],
+                                          O.Format(*fk), O.Format(*fv), signs, S, signs, S,
+                                          1 / math.sqrt(d))
+        assert np.max(np.abs(out_p[b] - o[0])) <= OUT_ATOL
+        for h in range(hq):
+            err = np.abs(lg_p[b, h, keep] - lgo[(0, h)])
+            assert np.all(err <= LOGIT_RTOL * (np.abs(lgo[(0, h)]) + sco[(0, h)]))
+    if not holes:   # same arithmetic as a contiguous cache of the same capacity: identical bits
+        cap = bt.shape[1] * page_size
+        pad = lambda a: np.concatenate([a, np.zeros(a.shape[:2] + (cap - a.shape[2],) + a.shape[3:], a.dtype)], 2)
+        out_c, lg_c = tq.attend_decode(q, dev(pad(rk)), f16(pad(nk)), dev(pad(rv)), f16(pad(nv)), sl, fmt_k,
+                                       tk, fmt_v, tv, logits=True)
+        torch.cuda.synchronize()
+        out_c, lg_c = out_c.cpu().numpy(), lg_c.cpu().numpy()
+        assert np.array_equal(out_p, out_c)
+        for b in range(batch):
+            assert np.array_equal(lg_p[b, :, : seq[b]], lg_c[b, :, : seq[b]])
+
+
+@pytest.mark.parametrize("page_size", [64, 128, 256])
+def test_paged_decode_b4(torch_gpu, page_size):
+    _case(torch_gpu, (128, 3, 3, 128), (128, 3, 3, 128), page_size, 7000 + page_size)
+
+
+def test_paged_decode_mixed_formats_and_groups(torch_gpu):
+    _case(torch_gpu, (128, 3, 2, 64), (128, 2, 1, 64, False), 64, 7100, hq=16, hkv=8, ntok=700, seq=(700, 1))
+    _case(torch_gpu, (128, 2, 2, 128), (128, 2, 2, 128), 128, 7101, batch=3, hq=8, hkv=8, ntok=500,
+          seq=(500, 0, 257))
+
+
+def test_paged_decode_page_holes(torch_gpu):
+    """A block-table entry of -1 inside a sequence removes that page's tokens."""
+    _case(torch_gpu, (128, 3, 3, 128), (128, 2, 2, 128), 64, 7200, holes=((0, 3), (1, 0)))
+
+
+def test_paged_append_writes_only_its_slots(torch_gpu):
+    """Quantize-on-write: records land at their slots, bit-identical to the oracle's records
+    of the same vectors; negative slots and every other slot are left untouched."""
+    torch = torch_gpu
+    import compressed_attention_rotate_amd as tq
+    d, hkv, page, n_pages, n_tok = 128, 4, 64, 12, 333
+    kb, _, _ = TI.kv_layer(1, hkv, n_tok, d, seed=7300)
+    x = np.ascontiguousarray(np.transpose(kb[0], (1, 0, 2)))          # [token][head][d]
+    signs, S = TI.rotation(d, 7301)
+    fmt = tq.Format.uniform(d, 3)
+    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    g = TI.gen(7302)
+    slots = g.permutation(n_pages * page)[:n_tok].astype(np.int64)
+    slots[::17] = -1                                                  # padding tokens
+    rb = fmt.record_bytes()
+    cache = torch.full((n_pages, hkv, page, rb), 0xA5, dtype=torch.uint8, device="cuda")
+    norms = torch.full((n_pages, hkv, page, 2), 7.0, dtype=torch.float16, device="cuda")
+    xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    tq.quantize_kv_paged(xt, fmt, tab, torch.from_numpy(slots).cuda(), cache, norms)
+    torch.cuda.synchronize()
+    c = cache.cpu().numpy()
+    nr = norms.cpu().view(torch.int16).numpy().view(np.uint16)
+    qz = oracle_quantize(x.reshape(-1, d), O.Format.uniform(d, 3), signs, S, bf16=True)
+    written = np.zeros((n_pages, hkv, page), bool)
+    got_c, got_n, rows = [], [], []
+    for i, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        pg, off = sl // page, sl % page
+        for h in range(hkv):
+            written[pg, h, off] = True
+            got_c.append(c[pg, h, off]); got_n.append(nr[pg, h, off]); rows.append(i * hkv + h)
+    sub = {k: v[rows] for k, v in qz.items()}
+    compare_quantize(np.stack(got_c), np.stack(got_n), sub, O.Format.uniform(d, 3))
+    assert np.all(c[~written] == 0xA5)
+    assert np.all(nr[~written] == np.float16(7.0).view(np.uint16))
+
+
+def test_paged_full_context_equals_contiguous(torch_gpu):
+    """The 32768-token Llama-3.1-8B-shaped layer in 128-token pages in shuffled order: the
+    paged decode returns the contiguous decode's output bit for bit."""
+    torch = torch_gpu
+    import compressed_attention_rotate_amd as tq
+    d, hq, hkv, n, page = 128, 32, 8, 32768, 128
+    kb, vb, _ = TI.kv_layer(1, hkv, n, d, seed=TI.data_seed(2))
+    qb = TI.decode_queries(1, hq, d, TI.data_seed(2))
+    signs, S = TI.rotation(d, TI.rotation_seed(2))
+    fmt = tq.Format.uniform(d, 3)
+    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    k0 = torch.from_numpy(kb.view(np.int16)).cuda().view(torch.bfloat16)
+    v0 = torch.from_numpy(vb.view(np.int16)).cuda().view(torch.bfloat16)
+    ck, nk = tq.quantize_kv(k0.view(-1, d), fmt, tab)
+    cv, nv = tq.quantize_kv(v0.view(-1, d), fmt, tab)
+    rb = fmt.record_bytes()
+    ck, nk, cv, nv = ck.view(1, hkv, n, rb), nk.view(1, hkv, n, 2), cv.view(1, hkv, n, rb), nv.view(1, hkv, n, 2)
+    mb = n // page
+    perm = torch.from_numpy(TI.gen(7400).permutation(mb).astype(np.int64)).cuda()
+    def pages(t):   # [1, hkv, n, w] -> [mb, hkv, page, w] with page perm[j] holding block j
+        blocks = t[0].view(hkv, mb, page, -1).permute(1, 0, 2, 3)
+        out = torch.empty_like(blocks)
+        out[perm] = blocks
+        return out.contiguous()
+    bt = perm.to(torch.int32).view(1, mb)
+    q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16)
+    sl = torch.full((1,), n, dtype=torch.int32, device="cuda")
+    out_c = tq.attend_decode(q, ck, nk, cv, nv, sl, fmt, tab)
+    out_p = tq.attend_decode_paged(q, pages(ck), pages(nk), pages(cv), pages(nv), bt, sl, fmt, tab)
+    torch.cuda.synchronize()
+    assert torch.equal(out_c, out_p)
