@@ -18,8 +18,8 @@ from ._lib import (LIB_PATH, TQ_BF16, TQ_F16, TQ_F32, Format, Tables, TQError, b
 
 __all__ = ["Format", "Tables", "TQError", "build_codebook", "quantize_kv", "attend_decode",
            "ip_search", "requantize", "attend_workspace_bytes", "search_workspace_bytes",
-           "requantize_workspace_bytes", "quantize_kv_paged", "attend_decode_paged", "LIB_PATH",
-           "load"]
+           "requantize_workspace_bytes", "quantize_kv_paged", "attend_decode_paged",
+           "prefill_paged", "prefill_workspace_bytes", "LIB_PATH", "load"]
 
 
 def _torch():
@@ -201,6 +201,59 @@ def attend_decode_paged(q, codes_k, norms_k, codes_v, norms_v, block_table, seq_
                                        _stream(q.device))
     _check(rc, "tq_attend_decode_paged")
     return (out, lg) if logits else out
+
+
+def prefill_workspace_bytes(n_new, hq, hkv, max_blocks, page_size) -> int:
+    n = load().tq_prefill_workspace_bytes(n_new, hq, hkv, max_blocks, page_size)
+    if n < 0:
+        raise TQError(-1, "tq_prefill_workspace_bytes")
+    return int(n)
+
+
+def prefill_paged(q, k_new, v_new, start, codes_k, norms_k, codes_v, norms_v, block_table,
+                  fmt_k: Format, tables_k: Tables, fmt_v: Format = None, tables_v: Tables = None,
+                  scale: float = None, counters=None, workspace=None, out=None):
+    """One prefill chunk of one sequence: k_new / v_new [n_new, hkv, 128] are quantized into
+    the paged caches at positions start .. start + n_new - 1 (pages from block_table, int32
+    [max_blocks]), then q [n_new, hq, 128] attends causally to the cache.  Returns out fp32
+    [n_new, hq, 128]."""
+    torch = _torch()
+    fmt_v = fmt_k if fmt_v is None else fmt_v
+    tables_v = tables_k if tables_v is None else tables_v
+    n_new, hq, d = q.shape
+    num_pages, hkv, page_size, _ = codes_k.shape
+    if k_new.shape != (n_new, hkv, d) or v_new.shape != (n_new, hkv, d) or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new / v_new must be [n_new, hkv, d] of one dtype")
+    for t, rb in ((codes_k, fmt_k.record_bytes()), (codes_v, fmt_v.record_bytes())):
+        if t.dtype != torch.uint8 or t.shape[:3] != (num_pages, hkv, page_size) or t.shape[3] != rb \
+                or not t.is_contiguous():
+            raise ValueError("bad paged cache tensor")
+    for t in (norms_k, norms_v):
+        if t.shape != (num_pages, hkv, page_size, 2) or not t.is_contiguous():
+            raise ValueError("bad paged norms tensor")
+    if block_table.dtype != torch.int32 or block_table.dim() != 1 or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [max_blocks]")
+    max_blocks = block_table.shape[0]
+    k2, v2 = k_new.reshape(-1, d).contiguous(), v_new.reshape(-1, d).contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q = q.contiguous()
+    if out is None:
+        out = torch.empty((n_new, hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(prefill_workspace_bytes(max(n_new, 1), hq, hkv, max_blocks,
+                                                            page_size), 16),
+                                dtype=torch.uint8, device=q.device)
+    fk, fv, tk, tv = fmt_k.c(), fmt_v.c(), tables_k.c(), tables_v.c()
+    rc = load().tq_prefill_paged(ctypes.byref(fk), ctypes.byref(tk), ctypes.byref(fv),
+                                 ctypes.byref(tv), _ptr(q), _dtype_code(q), n_new, hq, hkv, _ptr(k2),
+                                 _ptr(v2), _dtype_code(k2), d, int(start), _ptr(codes_k),
+                                 _ptr(norms_k), _ptr(codes_v), _ptr(norms_v), page_size, num_pages,
+                                 _ptr(block_table), max_blocks, float(scale), _ptr(out),
+                                 _ptr(counters), _ptr(workspace), workspace.numel(),
+                                 _stream(q.device))
+    _check(rc, "tq_prefill_paged")
+    return out
 
 
 def search_workspace_bytes(n_q, k, n_db, d) -> int:

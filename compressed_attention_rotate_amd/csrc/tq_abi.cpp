@@ -57,13 +57,15 @@ int page_log2(int32_t page_size) {
 
 int quantize_checked(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
                      int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
-                     int64_t* counters, tq_stream_t stream, const tq_paged_dst* paged);
+                     int64_t* counters, tq_stream_t stream, const tq_paged_dst* paged,
+                     bool launch = true);
 int decode_checked(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
                    const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch, int32_t hq,
                    int32_t hkv, const void* codes_k, const uint16_t* norms_k, const void* codes_v,
                    const uint16_t* norms_v, int64_t capacity, const int32_t* seq_lens, float scale,
                    float tau, float* out, float* logits, int64_t* skipped, void* workspace,
-                   int64_t workspace_bytes, tq_stream_t stream, const tq_paged_src* paged);
+                   int64_t workspace_bytes, tq_stream_t stream, const tq_paged_src* paged,
+                   bool launch = true);
 uintptr_t dtype_size(int dt) { return dt == TQ_F32 ? 4 : 2; }
 
 }  // namespace
@@ -114,7 +116,7 @@ int tq_quantize_kv_paged(const tq_format* f, const tq_tables* t, const void* x, 
   if (lg < 0 || num_pages < 1 || hkv < 1 || n_tokens < 0) return TQ_ERR_ARG;
   if (n_tokens > 0 && !slot_mapping) return TQ_ERR_ARG;
   if (slot_mapping && !aligned(slot_mapping, 8)) return TQ_ERR_ALIGN;
-  const tq_paged_dst dst{slot_mapping, num_pages, hkv, lg};
+  const tq_paged_dst dst{slot_mapping, num_pages, hkv, lg, nullptr, 0, 0};
   return quantize_checked(f, t, x, x_dtype, n_tokens * hkv, d_in, ld_x, codes_cache, norms_cache,
                           counters, stream, &dst);
 }
@@ -124,7 +126,8 @@ int tq_quantize_kv_paged(const tq_format* f, const tq_tables* t, const void* x, 
 namespace {
 int quantize_checked(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
                      int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
-                     int64_t* counters, tq_stream_t stream, const tq_paged_dst* paged) {
+                     int64_t* counters, tq_stream_t stream, const tq_paged_dst* paged,
+                     bool launch) {
   int rc = tq_check_format(f);
   if (rc) return rc;
   if (n < 0 || !dtype_ok(x_dtype)) return TQ_ERR_ARG;
@@ -136,6 +139,7 @@ int quantize_checked(const tq_format* f, const tq_tables* t, const void* x, int3
   if (!aligned(x, dtype_size(x_dtype)) || !aligned(codes, 16) || !aligned(norms, 4) ||
       (counters && !aligned(counters, 8)))
     return TQ_ERR_ALIGN;
+  if (!launch) return TQ_OK;
   return tq_launch_quantize(f, t, x, x_dtype, n, d_in, ld_x, codes, norms, counters,
                             reinterpret_cast<hipStream_t>(stream), paged);
 }
@@ -172,7 +176,7 @@ int tq_attend_decode_paged(const tq_format* fk, const tq_tables* tk, const tq_fo
   const int lg = page_log2(page_size);
   if (lg < 0 || num_pages < 1 || max_blocks < 1 || !block_table) return TQ_ERR_ARG;
   if (!aligned(block_table, 4)) return TQ_ERR_ALIGN;
-  const tq_paged_src src{block_table, num_pages, max_blocks, lg};
+  const tq_paged_src src{block_table, num_pages, max_blocks, lg, max_blocks, -1};
   return decode_checked(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
                         norms_v, (int64_t)max_blocks << lg, seq_lens, scale, tau, out, logits,
                         skipped, workspace, workspace_bytes, stream, &src);
@@ -186,7 +190,8 @@ int decode_checked(const tq_format* fk, const tq_tables* tk, const tq_format* fv
                    int32_t hkv, const void* codes_k, const uint16_t* norms_k, const void* codes_v,
                    const uint16_t* norms_v, int64_t capacity, const int32_t* seq_lens, float scale,
                    float tau, float* out, float* logits, int64_t* skipped, void* workspace,
-                   int64_t workspace_bytes, tq_stream_t stream, const tq_paged_src* paged) {
+                   int64_t workspace_bytes, tq_stream_t stream, const tq_paged_src* paged,
+                   bool launch) {
   int rc = tq_check_format(fk);
   if (rc) return rc;
   if ((rc = tq_check_format(fv))) return rc;
@@ -197,14 +202,16 @@ int decode_checked(const tq_format* fk, const tq_tables* tk, const tq_format* fv
   if (g != 1 && g != 2 && g % 4) return TQ_ERR_SHAPE;
   if (!dtype_ok(q_dtype) || !std::isfinite(scale) || !(tau >= 0.0f) || !(tau <= 1.0f)) return TQ_ERR_ARG;
   if ((rc = check_tables(fk, tk)) || (rc = check_tables(fv, tv))) return rc;
-  if (!q || !out || !seq_lens || !workspace) return TQ_ERR_ARG;
+  const bool need_lens = !paged || paged->causal_start < 0;
+  if (!q || !out || (need_lens && !seq_lens) || !workspace) return TQ_ERR_ARG;
   if (capacity > 0 && (!codes_k || !norms_k || !codes_v || !norms_v)) return TQ_ERR_ARG;
   if (!aligned(q, dtype_size(q_dtype)) || !aligned(codes_k, 16) || !aligned(codes_v, 16) ||
-      !aligned(norms_k, 4) || !aligned(norms_v, 4) || !aligned(seq_lens, 4) || !aligned(out, 16) ||
+      !aligned(norms_k, 4) || !aligned(norms_v, 4) || (seq_lens && !aligned(seq_lens, 4)) || !aligned(out, 16) ||
       (logits && !aligned(logits, 4)) || (skipped && !aligned(skipped, 8)) || !aligned(workspace, 16))
     return TQ_ERR_ALIGN;
   const tq_decode_plan plan = tq_plan_decode(batch, hq, hkv, capacity, fk->d);
   if (workspace_bytes < plan.ws_bytes) return TQ_ERR_WORKSPACE;
+  if (!launch) return TQ_OK;
   return tq_launch_decode(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
                           norms_v, capacity, seq_lens, scale, tau, out, logits, skipped, workspace,
                           plan, reinterpret_cast<hipStream_t>(stream), paged);
@@ -237,6 +244,50 @@ int tq_ip_search(const tq_format* f, const tq_tables* t, const void* codes_db,
   if (workspace_bytes < plan.ws_bytes) return TQ_ERR_WORKSPACE;
   return tq_launch_search(f, t, codes_db, norms_db, n_db, queries, d_in, n_q, k, out_ids,
                           out_scores, workspace, plan, reinterpret_cast<hipStream_t>(stream));
+}
+
+int64_t tq_prefill_workspace_bytes(int32_t n_new, int32_t hq, int32_t hkv, int32_t max_blocks,
+                                   int32_t page_size) {
+  const int lg = page_log2(page_size);
+  if (lg < 0 || max_blocks < 1 || n_new < 1) return -1;
+  return tq_attend_workspace_bytes(n_new, hq, hkv, (int64_t)max_blocks << lg, 128);
+}
+
+int tq_prefill_paged(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                     const tq_tables* tv, const void* q, int32_t q_dtype, int32_t n_new,
+                     int32_t hq, int32_t hkv, const void* k_new, const void* v_new,
+                     int32_t kv_dtype, int64_t ld_kv, int64_t start, void* codes_k,
+                     uint16_t* norms_k, void* codes_v, uint16_t* norms_v, int32_t page_size,
+                     int64_t num_pages, const int32_t* block_table, int32_t max_blocks, float scale,
+                     float* out, int64_t* counters, void* workspace, int64_t workspace_bytes,
+                     tq_stream_t stream) {
+  const int lg = page_log2(page_size);
+  if (lg < 0 || num_pages < 1 || max_blocks < 1 || !block_table || n_new < 0 || hkv < 1 ||
+      start < 0)
+    return TQ_ERR_ARG;
+  if (!aligned(block_table, 4)) return TQ_ERR_ALIGN;
+  const int64_t capacity = (int64_t)max_blocks << lg;
+  if (start + n_new > capacity) return TQ_ERR_SHAPE;
+  if (n_new == 0) return TQ_OK;
+  if ((fk && fk->d != 128) || (fv && fv->d != 128)) return TQ_ERR_SHAPE;
+  const tq_paged_src src{block_table, num_pages, max_blocks, lg, 0, start};
+  const tq_paged_dst dst{nullptr, num_pages, hkv, lg, block_table, start, max_blocks};
+  const int64_t nv = (int64_t)n_new * hkv;
+  // every part is validated before anything is written or launched
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool go = pass == 1;
+    int rc = quantize_checked(fk, tk, k_new, kv_dtype, nv, 128, ld_kv, codes_k, norms_k, counters,
+                              stream, &dst, go);
+    if (rc) return rc;
+    if ((rc = quantize_checked(fv, tv, v_new, kv_dtype, nv, 128, ld_kv, codes_v, norms_v, counters,
+                               stream, &dst, go)))
+      return rc;
+    if ((rc = decode_checked(fk, tk, fv, tv, q, q_dtype, n_new, hq, hkv, codes_k, norms_k, codes_v,
+                             norms_v, capacity, nullptr, scale, 0.0f, out, nullptr, nullptr,
+                             workspace, workspace_bytes, stream, &src, go)))
+      return rc;
+  }
+  return TQ_OK;
 }
 
 int64_t tq_requantize_workspace_bytes(int64_t n, int32_t d) {

@@ -167,11 +167,14 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      hipStream_t stream, const tq_paged_src* paged) {
   using namespace tqk;
   DecodeParams p{};
+  p.causal_start = -1;
   if (paged) {
     p.block_table = paged->block_table;
     p.num_pages = paged->num_pages;
     p.max_blocks = paged->max_blocks;
     p.page_log2 = paged->page_log2;
+    p.bt_stride = paged->bt_stride;
+    p.causal_start = paged->causal_start;
   }
   p.q = q;
   p.codes_k = reinterpret_cast<const uint32_t*>(codes_k);

@@ -125,6 +125,8 @@ struct DecodeParams {
   const int32_t* block_table;
   int64_t num_pages;
   int32_t max_blocks, page_log2;
+  int32_t bt_stride;      // block-table row stride (0: every query reads one table)
+  int64_t causal_start;   // >= 0: query b sees tokens t <= causal_start + b (prefill chunk)
 };
 
 // LDS layout of one scan workgroup (floats).
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   const int bk = unit / nchunk;  // b * hkv + kv head
   const int b = bk / p.hkv;
   const int h0 = (bk % p.hkv) * p.group + chunk * GC;
-  int64_t seq = p.seq_lens[b];
+  int64_t seq = p.causal_start >= 0 ? p.causal_start + b + 1 : (int64_t)p.seq_lens[b];
   if (seq > p.capacity) seq = p.capacity;
   const int64_t t_begin = (int64_t)blockIdx.x * p.tokens_per_split;
   int64_t t_end = t_begin + p.tokens_per_split;
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   // page); -1 for a page id out of range
   auto tile_row = [&](int64_t tt0) -> int64_t {
     if (!p.block_table) return kv_base + tt0;
-    const int32_t pg = p.block_table[(int64_t)b * p.max_blocks + (tt0 >> p.page_log2)];
+    const int32_t pg = p.block_table[(int64_t)b * p.bt_stride + (tt0 >> p.page_log2)];
     if (pg < 0 || (int64_t)pg >= p.num_pages) return -1;
     return (((int64_t)pg * p.hkv + (bk % p.hkv)) << p.page_log2) + (tt0 & ((1ll << p.page_log2) - 1));
   };

@@ -11,9 +11,12 @@ int tq_num_cus();
 // Paged destination of a quantize launch: vector v = token * page_heads + head is written
 // to row (page * page_heads + head) * 2^page_log2 + offset of the cache.
 struct tq_paged_dst {
-  const int64_t* slots;   // device, one slot per token
+  const int64_t* slots;   // device, one slot per token; or null and:
   int64_t num_pages;
   int32_t page_heads, page_log2;
+  const int32_t* block_table;  // the sequence's page list, token i at position pos0 + i
+  int64_t pos0;
+  int32_t max_blocks;
 };
 
 int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, int32_t x_dtype,
@@ -37,9 +40,11 @@ tq_decode_plan tq_plan_decode(int32_t batch, int32_t hq, int32_t hkv, int64_t ca
 
 // Paged source of a decode launch (see DecodeParams).
 struct tq_paged_src {
-  const int32_t* block_table;  // device [batch][max_blocks]
+  const int32_t* block_table;  // device [batch][bt_stride]
   int64_t num_pages;
   int32_t max_blocks, page_log2;
+  int32_t bt_stride;           // 0: all queries share row 0
+  int64_t causal_start;        // >= 0: query b sees tokens <= causal_start + b
 };
 
 int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* fv,

@@ -24,6 +24,9 @@ int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, in
     p.num_pages = paged->num_pages;
     p.page_heads = paged->page_heads;
     p.page_log2 = paged->page_log2;
+    p.block_table = paged->block_table;
+    p.pos0 = paged->pos0;
+    p.max_blocks = paged->max_blocks;
   }
   p.x = x;
   p.S = t->S;

@@ -104,14 +104,26 @@ struct QParams {
   const int64_t* slots;
   int64_t num_pages;
   int32_t page_heads, page_log2;
+  // slots == nullptr and block_table set: token i sits at position pos0 + i of the sequence
+  // whose pages block_table lists (max_blocks entries), i.e. slot
+  // block_table[pos / page_size] * page_size + pos % page_size
+  const int32_t* block_table;
+  int64_t pos0;
+  int32_t max_blocks;
 };
 
 // Destination row of vector vg (or -1: not written).
 __device__ __forceinline__ int64_t dest_row(const QParams& p, int64_t vg) {
-  if (!p.slots) return vg;
+  if (!p.slots && !p.block_table) return vg;
   const int64_t tok = vg / p.page_heads;
   const int head = (int)(vg - tok * p.page_heads);
-  const int64_t sl = p.slots[tok];
+  int64_t sl;
+  if (p.slots) {
+    sl = p.slots[tok];
+  } else {
+    const int64_t pos = p.pos0 + tok, blk = pos >> p.page_log2;
+    sl = blk < p.max_blocks ? ((int64_t)p.block_table[blk] << p.page_log2) + (pos & ((1ll << p.page_log2) - 1)) : -1;
+  }
   const int64_t page = sl >> p.page_log2;
   if (sl < 0 || page >= p.num_pages) return -1;
   return ((page * p.page_heads + head) << p.page_log2) + (sl & ((1ll << p.page_log2) - 1));

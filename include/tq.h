@@ -201,6 +201,36 @@ int tq_attend_decode_paged(const tq_format* fk, const tq_tables* tk, const tq_fo
                            float* logits, int64_t* skipped, void* workspace,
                            int64_t workspace_bytes, tq_stream_t stream);
 
+/* Workspace bytes tq_prefill_paged needs. */
+int64_t tq_prefill_workspace_bytes(int32_t n_new, int32_t hq, int32_t hkv, int32_t max_blocks,
+                                   int32_t page_size);
+
+/* One prefill chunk of one sequence on a paged cache: the chunk's new keys and values are
+ * quantized and written at positions start .. start + n_new - 1 of the sequence (the
+ * step before decode: quantize-on-write), then each new query attends, exactly as a
+ * decode step would (same estimator, softmax, value sum), to the cached tokens at or
+ * before its own position -- causal attention over the compressed cache.
+ *   q            : device [n_new][hq][128], dtype q_dtype
+ *   k_new, v_new : device [n_new][hkv] rows of 128 elements, dtype kv_dtype, row stride
+ *                  ld_kv elements
+ *   start        : position of the chunk's first token (the tokens before it are cached)
+ *   block_table  : device int32 [max_blocks], the sequence's pages; positions up to
+ *                  start + n_new - 1 must have a page
+ *   out          : device out fp32 [n_new][hq][128]
+ *   counters     : as for tq_quantize_kv (both tensors add to it), nullable
+ *   workspace    : device, >= tq_prefill_workspace_bytes(...)
+ * Errors: as tq_quantize_kv_paged and tq_attend_decode_paged; TQ_ERR_SHAPE when
+ * start + n_new exceeds max_blocks * page_size.  Nothing is written when the arguments
+ * are rejected. */
+int tq_prefill_paged(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                     const tq_tables* tv, const void* q, int32_t q_dtype, int32_t n_new,
+                     int32_t hq, int32_t hkv, const void* k_new, const void* v_new,
+                     int32_t kv_dtype, int64_t ld_kv, int64_t start, void* codes_k,
+                     uint16_t* norms_k, void* codes_v, uint16_t* norms_v, int32_t page_size,
+                     int64_t num_pages, const int32_t* block_table, int32_t max_blocks, float scale,
+                     float* out, int64_t* counters, void* workspace, int64_t workspace_bytes,
+                     tq_stream_t stream);
+
 /* Workspace bytes tq_ip_search needs. */
 int64_t tq_search_workspace_bytes(int64_t n_q, int32_t k, int64_t n_db, int32_t d);
 

@@ -181,3 +181,84 @@ def test_paged_full_context_equals_contiguous(torch_gpu):
     out_p = tq.attend_decode_paged(q, pages(ck), pages(nk), pages(cv), pages(nv), bt, sl, fmt, tab)
     torch.cuda.synchronize()
     assert torch.equal(out_c, out_p)
+
+
+def _prefill_case(torch, start, n_new, seed, page=64, hq=32, hkv=8, fk=(128, 3, 3, 128),
+                  fv=(128, 3, 3, 128)):
+    """A sequence with `start` cached tokens and a chunk of n_new new ones, in shuffled pages."""
+    import compressed_attention_rotate_amd as tq
+    d = 128
+    total = start + n_new
+    kb, vb, _ = TI.kv_layer(1, hkv, total, d, seed=seed)
+    qb = TI.decode_queries(n_new, hq, d, seed)                       # one query row per new token
+    signs, S = TI.rotation(d, seed + 1)
+    rk, nk, _ = oracle_pack_cache(kb, O.Format(*fk), signs, S, bf16=True)
+    rv, nv, _ = oracle_pack_cache(vb, O.Format(*fv), signs, S, bf16=True)
+    mb = (total + page - 1) // page + 1
+    n_pages = mb + 2
+    table = TI.gen(seed + 2).permutation(n_pages)[:mb].astype(np.int32)
+    fmt_k, fmt_v = tq.Format(*fk), tq.Format(*fv)
+    ck = np.full((n_pages, hkv, page, fmt_k.record_bytes()), 0x5A, np.uint8)
+    cv = np.full((n_pages, hkv, page, fmt_v.record_bytes()), 0x5A, np.uint8)
+    nkc = np.zeros((n_pages, hkv, page, 2), np.uint16)
+    nvc = np.zeros((n_pages, hkv, page, 2), np.uint16)
+    for t in range(start):                                           # the cached past
+        pg, off = table[t // page], t % page
+        ck[pg, :, off], cv[pg, :, off] = rk[0, :, t], rv[0, :, t]
+        nkc[pg, :, off], nvc[pg, :, off] = nk[0, :, t], nv[0, :, t]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    f16 = lambda a: dev(a.view(np.int16)).view(torch.float16)
+    tk = tq.Tables(fmt_k, signs, torch.from_numpy(S).cuda())
+    tv = tq.Tables(fmt_v, signs, torch.from_numpy(S).cuda())
+    new_k = np.ascontiguousarray(np.transpose(kb[0, :, start:], (1, 0, 2)))   # [n_new][hkv][d]
+    new_v = np.ascontiguousarray(np.transpose(vb[0, :, start:], (1, 0, 2)))
+    bf = lambda a: dev(a.view(np.int16)).view(torch.bfloat16)
+    gck, gnk, gcv, gnv = dev(ck), f16(nkc), dev(cv), f16(nvc)
+    out = tq.prefill_paged(bf(qb), bf(new_k), bf(new_v), start, gck, gnk, gcv, gnv, dev(table),
+                           fmt_k, tk, fmt_v, tv)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), gck.cpu().numpy(), gnk.cpu().view(torch.int16).numpy().view(np.uint16),
+            table, rk, nk, rv, nv, qb, signs, S)
+
+
+@pytest.mark.parametrize("start,n_new", [(300, 70), (0, 1), (0, 130), (511, 2)])
+def test_prefill_writes_the_chunk_and_attends_causally(torch_gpu, start, n_new):
+    """The chunk's key records land at their positions, bit-identical to the oracle's; query i
+    of the chunk gets the oracle's attention over tokens 0 .. start + i."""
+    page, fk = 64, (128, 3, 3, 128)
+    out, ck, nk_c, table, rk, nk, rv, nv, qb, signs, S = _prefill_case(torch_gpu, start, n_new, 7500 + start)
+    hkv = rk.shape[1]
+    got_c, got_n, rows = [], [], []
+    for t in range(start, start + n_new):
+        pg, off = table[t // page], t % page
+        for h in range(hkv):
+            got_c.append(ck[pg, h, off]); got_n.append(nk_c[pg, h, off])
+    # exact comparison outside the ambiguity windows: the oracle on the chunk's rows
+    kb, _, _ = TI.kv_layer(1, hkv, start + n_new, 128, seed=7500 + start)
+    rows_x = np.transpose(kb[0, :, start:], (1, 0, 2)).reshape(-1, 128)
+    qz = oracle_quantize(rows_x, O.Format(*fk), signs, S, bf16=True)
+    compare_quantize(np.stack(got_c), np.stack(got_n), qz, O.Format(*fk))
+    q64 = TI.bf16_to_f64(qb)
+    for i in range(n_new):
+        L = start + i + 1
+        o, _, _, _, _ = oracle_decode(q64[i:i + 1], rk[:, :, :L], nk[:, :, :L], rv[:, :, :L], nv[:, :, :L],
+                                      [L], O.Format(*fk), O.Format(*fk), signs, S, signs, S, 1 / math.sqrt(128))
+        assert np.max(np.abs(out[i] - o[0])) <= OUT_ATOL, (i, np.max(np.abs(out[i] - o[0])))
+
+
+def test_prefill_rejects_a_chunk_past_the_pages_and_writes_nothing(torch_gpu):
+    torch = torch_gpu
+    import compressed_attention_rotate_amd as tq
+    fmt = tq.Format.uniform(128, 3)
+    signs, S = TI.rotation(128, 1)
+    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    ck = torch.full((4, 8, 64, fmt.record_bytes()), 0x5A, dtype=torch.uint8, device="cuda")
+    nk = torch.zeros((4, 8, 64, 2), dtype=torch.float16, device="cuda")
+    cv, nv = ck.clone(), nk.clone()
+    table = torch.arange(2, dtype=torch.int32, device="cuda")         # 2 pages: capacity 128
+    q = torch.zeros((10, 32, 128), dtype=torch.bfloat16, device="cuda")
+    kn = torch.zeros((10, 8, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tq.TQError):
+        tq.prefill_paged(q, kn, kn, 120, ck, nk, cv, nv, table, fmt, tab)
+    torch.cuda.synchronize()
+    assert bool((ck == 0x5A).all()) and bool((cv == 0x5A).all())
