@@ -186,6 +186,41 @@ def _paged_timing(tq, torch, dev, ks, q, codes_k, norms_k, codes_v, norms_v, seq
             "append_tokens_per_s": round(NTOK * BATCH / t_app, 1)}
 
 
+def _prefill_timing(tq, torch, dev, ks, vs, fmt, tab, n_new=512, page=128, reps=3):
+    """A 512-token prefill chunk at the end of the 32K-token sequence: its keys and values are
+    quantized into the paged cache, then its 512 x 32 queries attend causally to the
+    32256..32767-token prefixes of the compressed cache."""
+    mb = NTOK // page
+    table = torch.from_numpy(np.random.default_rng(7).permutation(mb).astype(np.int32)).to(dev)
+    rb = fmt.record_bytes()
+    ck = torch.empty((mb, HKV, page, rb), dtype=torch.uint8, device=dev)
+    nk = torch.empty((mb, HKV, page, 2), dtype=torch.float16, device=dev)
+    cv, nv = torch.empty_like(ck), torch.empty_like(nk)
+    kx = ks[0][0].permute(1, 0, 2).contiguous()     # [token][head][d]
+    vx = vs[0][0].permute(1, 0, 2).contiguous()
+    start = NTOK - n_new
+    # the cached past: written once with the paged append
+    slots = (table.to(torch.int64)[torch.arange(start, device=dev) // page] * page
+             + torch.arange(start, device=dev) % page)
+    tq.quantize_kv_paged(kx[:start], fmt, tab, slots, ck, nk)
+    tq.quantize_kv_paged(vx[:start], fmt, tab, slots, cv, nv)
+    g = torch.Generator(device="cpu").manual_seed(8)
+    q = torch.randn((n_new, HQ, D), generator=g).to(torch.bfloat16).to(dev)
+    ws = torch.empty(tq.prefill_workspace_bytes(n_new, HQ, HKV, mb, page), dtype=torch.uint8, device=dev)
+    out = torch.empty((n_new, HQ, D), dtype=torch.float32, device=dev)
+    run = lambda: tq.prefill_paged(q, kx[start:], vx[start:], start, ck, nk, cv, nv, table, fmt, tab,
+                                   workspace=ws, out=out)
+    run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for i in range(reps):
+        ev[i].record(); run()
+    ev[reps].record(); torch.cuda.synchronize()
+    t = np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]) * 1e-3
+    return {"chunk_tokens": n_new, "context": NTOK, "page_tokens": page,
+            "ms_per_chunk": round(float(t) * 1e3, 3), "tokens_per_s": round(n_new / t, 1)}
+
+
 def _requant_timing(tq, torch, dev, codes_k, norms_k, fmt, tab, signs, S, steps, nvec):
     """Temporal decay on the same layer: re-encode the b=4 key cache of a slot at b=3 (into
     a separate buffer, one workspace of the whole tensor), slots rotating as in the main
@@ -343,6 +378,7 @@ def main():
             ("b2.5_kv", tq.Format(D, 2, 1, 64), tq.Format(D, 2, 1, 64)))}
     line["variants"]["paged_b4"] = _paged_timing(tq, torch, dev, ks, q, codes_k, norms_k, codes_v,
                                                  norms_v, seq, ws, out, fmt, tab, steps, nvec)
+    line["variants"]["prefill_chunk"] = _prefill_timing(tq, torch, dev, ks, vs, fmt, tab)
     line["variants"]["requantize_b4_to_b3"] = _requant_timing(tq, torch, dev, codes_k, norms_k, fmt,
                                                               tab, signs, S, steps, nvec)
     if not args.no_cpu_baseline:
