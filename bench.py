@@ -40,6 +40,9 @@ def _parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the other-format / paged / prefill / re-encode measurements that "
+                         "follow the timed steps (profiling runs of the main step)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 4 times (scale reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -370,6 +373,11 @@ def main():
                             "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": trafd},
     }
     # other formats of the same layer (not part of `value`)
+    if args.no_variants:
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(kb, vb, qb, signs, S)
+        print(json.dumps(line), flush=True)
+        return
     line["variants"] = {
         name: _variant(tq, torch, dev, ks, vs, q, seq, ws, out, fk, fv, signs, S, steps, nvec)
         for name, fk, fv in (
