@@ -209,7 +209,7 @@ def _prefill_timing(tq, torch, dev, ks, vs, fmt, tab, n_new=512, page=128, reps=
     tq.quantize_kv_paged(vx[:start], fmt, tab, slots, cv, nv)
     g = torch.Generator(device="cpu").manual_seed(8)
     q = torch.randn((n_new, HQ, D), generator=g).to(torch.bfloat16).to(dev)
-    ws = torch.empty(tq.prefill_workspace_bytes(n_new, HQ, HKV, mb, page), dtype=torch.uint8, device=dev)
+    ws = torch.empty(tq.prefill_workspace_bytes(n_new, HQ, HKV, start), dtype=torch.uint8, device=dev)
     out = torch.empty((n_new, HQ, D), dtype=torch.float32, device=dev)
     run = lambda: tq.prefill_paged(q, kx[start:], vx[start:], start, ck, nk, cv, nv, table, fmt, tab,
                                    workspace=ws, out=out)

@@ -203,8 +203,8 @@ def attend_decode_paged(q, codes_k, norms_k, codes_v, norms_v, block_table, seq_
     return (out, lg) if logits else out
 
 
-def prefill_workspace_bytes(n_new, hq, hkv, max_blocks, page_size) -> int:
-    n = load().tq_prefill_workspace_bytes(n_new, hq, hkv, max_blocks, page_size)
+def prefill_workspace_bytes(n_new, hq, hkv, start) -> int:
+    n = load().tq_prefill_workspace_bytes(n_new, hq, hkv, start)
     if n < 0:
         raise TQError(-1, "tq_prefill_workspace_bytes")
     return int(n)
@@ -241,8 +241,7 @@ def prefill_paged(q, k_new, v_new, start, codes_k, norms_k, codes_v, norms_v, bl
     if out is None:
         out = torch.empty((n_new, hq, d), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = torch.empty(max(prefill_workspace_bytes(max(n_new, 1), hq, hkv, max_blocks,
-                                                            page_size), 16),
+        workspace = torch.empty(max(prefill_workspace_bytes(max(n_new, 1), hq, hkv, int(start)), 16),
                                 dtype=torch.uint8, device=q.device)
     fk, fv, tk, tv = fmt_k.c(), fmt_v.c(), tables_k.c(), tables_v.c()
     rc = load().tq_prefill_paged(ctypes.byref(fk), ctypes.byref(tk), ctypes.byref(fv),

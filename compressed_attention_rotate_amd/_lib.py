@@ -62,7 +62,7 @@ def load() -> ctypes.CDLL:
             "tq_attend_decode_paged": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P, P, P, P,
                                                       I32, I64, P, I32, P, F32, F32, P, P, P, P, I64,
                                                       P]),
-            "tq_prefill_workspace_bytes": (I64, [I32, I32, I32, I32, I32]),
+            "tq_prefill_workspace_bytes": (I64, [I32, I32, I32, I64]),
             "tq_prefill_paged": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P, P, I32, I64,
                                                 I64, P, P, P, P, I32, I64, P, I32, F32, P, P, P, I64,
                                                 P]),

@@ -246,11 +246,9 @@ int tq_ip_search(const tq_format* f, const tq_tables* t, const void* codes_db,
                           out_scores, workspace, plan, reinterpret_cast<hipStream_t>(stream));
 }
 
-int64_t tq_prefill_workspace_bytes(int32_t n_new, int32_t hq, int32_t hkv, int32_t max_blocks,
-                                   int32_t page_size) {
-  const int lg = page_log2(page_size);
-  if (lg < 0 || max_blocks < 1 || n_new < 1) return -1;
-  return tq_attend_workspace_bytes(n_new, hq, hkv, (int64_t)max_blocks << lg, 128);
+int64_t tq_prefill_workspace_bytes(int32_t n_new, int32_t hq, int32_t hkv, int64_t start) {
+  if (n_new < 1 || hq < 1 || hkv < 1 || hq % hkv || start < 0) return -1;
+  return tq_plan_prefill(n_new, hq, hkv, start).ws_bytes;
 }
 
 int tq_prefill_paged(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
@@ -263,31 +261,38 @@ int tq_prefill_paged(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      tq_stream_t stream) {
   const int lg = page_log2(page_size);
   if (lg < 0 || num_pages < 1 || max_blocks < 1 || !block_table || n_new < 0 || hkv < 1 ||
-      start < 0)
+      hq < 1 || start < 0)
     return TQ_ERR_ARG;
   if (!aligned(block_table, 4)) return TQ_ERR_ALIGN;
+  if (hq % hkv) return TQ_ERR_SHAPE;
   const int64_t capacity = (int64_t)max_blocks << lg;
   if (start + n_new > capacity) return TQ_ERR_SHAPE;
+  int rc = tq_check_format(fk);
+  if (rc) return rc;
+  if ((rc = tq_check_format(fv))) return rc;
+  if (fk->d != 128 || fv->d != 128 || !fk->qjl) return TQ_ERR_SHAPE;  // logits need the QJL term
   if (n_new == 0) return TQ_OK;
-  if ((fk && fk->d != 128) || (fv && fv->d != 128)) return TQ_ERR_SHAPE;
-  const tq_paged_src src{block_table, num_pages, max_blocks, lg, 0, start};
+  if (!dtype_ok(q_dtype) || !std::isfinite(scale)) return TQ_ERR_ARG;
+  if (!q || !out || !workspace) return TQ_ERR_ARG;
+  if (!aligned(q, dtype_size(q_dtype)) || !aligned(out, 16) || !aligned(workspace, 256))
+    return TQ_ERR_ALIGN;
+  const tq_prefill_plan plan = tq_plan_prefill(n_new, hq, hkv, start);
+  if (workspace_bytes < plan.ws_bytes) return TQ_ERR_WORKSPACE;
   const tq_paged_dst dst{nullptr, num_pages, hkv, lg, block_table, start, max_blocks};
   const int64_t nv = (int64_t)n_new * hkv;
   // every part is validated before anything is written or launched
   for (int pass = 0; pass < 2; ++pass) {
     const bool go = pass == 1;
-    int rc = quantize_checked(fk, tk, k_new, kv_dtype, nv, 128, ld_kv, codes_k, norms_k, counters,
-                              stream, &dst, go);
-    if (rc) return rc;
+    if ((rc = quantize_checked(fk, tk, k_new, kv_dtype, nv, 128, ld_kv, codes_k, norms_k, counters,
+                               stream, &dst, go)))
+      return rc;
     if ((rc = quantize_checked(fv, tv, v_new, kv_dtype, nv, 128, ld_kv, codes_v, norms_v, counters,
                                stream, &dst, go)))
       return rc;
-    if ((rc = decode_checked(fk, tk, fv, tv, q, q_dtype, n_new, hq, hkv, codes_k, norms_k, codes_v,
-                             norms_v, capacity, nullptr, scale, 0.0f, out, nullptr, nullptr,
-                             workspace, workspace_bytes, stream, &src, go)))
-      return rc;
   }
-  return TQ_OK;
+  return tq_launch_prefill(fk, tk, fv, tv, q, q_dtype, n_new, hq, hkv, codes_k, norms_k, codes_v,
+                           norms_v, lg, num_pages, block_table, max_blocks, start, scale, out,
+                           workspace, plan, reinterpret_cast<hipStream_t>(stream));
 }
 
 int64_t tq_requantize_workspace_bytes(int64_t n, int32_t d) {

@@ -130,6 +130,13 @@ bool tq_decode_formats_supported(const tq_format* fk, const tq_format* fv) {
   return false;
 }
 
+// The split merge and rotation back, for callers that produce split partials in the scan's
+// format (the prefill kernel).
+int tqk::launch_decode_combine(const DecodeParams& p, int rows, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_combine, dim3(rows), dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
 tq_decode_plan tq_plan_decode(int32_t batch, int32_t hq, int32_t hkv, int64_t capacity, int32_t d) {
   using namespace tqk;
   (void)d;

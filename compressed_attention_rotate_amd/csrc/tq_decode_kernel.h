@@ -716,6 +716,10 @@ int launch_pair(const DecodeParams& p, bool vq, int gc, dim3 grid, hipStream_t s
   X(3, 2, 2, 2, 2, 4) /* K / V: b3.5 / b3 */ \
   /* end */
 
+// decode_combine over `rows` (batch * hq) partial sets (defined with the kernel in
+// tq_decode.hip).
+int launch_decode_combine(const DecodeParams& p, int rows, hipStream_t stream);
+
 #define TQ_DECODE_EXTERN(a, b, c, d, e, f) \
   extern template int launch_pair<a, b, c, d, e, f>(const DecodeParams&, bool, int, dim3, hipStream_t);
 TQ_DECODE_PAIRS(TQ_DECODE_EXTERN)

@@ -73,3 +73,20 @@ int tq_launch_requant(const tq_format* fi, const tq_tables* ti, const void* code
                       const tq_tables* to, void* codes_out, uint16_t* norms_out,
                       int64_t* counters, void* workspace, int64_t workspace_bytes,
                       hipStream_t stream);
+
+struct tq_prefill_plan {
+  int32_t n_split;         // key splits
+  int64_t keys_per_split;  // multiple of 64
+  int64_t row_blocks;      // 64-row blocks per KV head
+  int64_t ws_q_off, ws_part_off, ws_bytes;
+};
+
+tq_prefill_plan tq_plan_prefill(int32_t n_new, int32_t hq, int32_t hkv, int64_t start);
+
+int tq_launch_prefill(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                      const tq_tables* tv, const void* q, int32_t q_dtype, int32_t n_new,
+                      int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                      const void* codes_v, const uint16_t* norms_v, int32_t page_log2,
+                      int64_t num_pages, const int32_t* block_table, int32_t max_blocks,
+                      int64_t start, float scale, float* out, void* workspace,
+                      const tq_prefill_plan& pl, hipStream_t stream);

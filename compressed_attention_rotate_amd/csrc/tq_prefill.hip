@@ -1,0 +1,452 @@
+// Prefill attention on MFMA: a chunk of new queries attends causally to a paged compressed
+// cache (the chunk's own keys and values are already written to it).
+//
+// The decode estimator of each logit,
+//   n16_t <q_rot, c[idx_t]> + gamma r16_t <S q_rot, 2 sigma_t - 1>
+// (163.com explainer, sections "第二步：QJL" and "速度"), is a 256-wide dot product between a
+// query row [q_rot | gamma S q_rot] and a key row [n16 c[idx] | r16 (2 sigma - 1)]; the value
+// sum splits the same way into A = sum_t p_t n16_t c[idx_t] and Q = gamma sum_t p_t r16_t
+// (2 sigma_t - 1), rotated back once per row as in decode (out = D H (A + S^T Q) / (sqrt(d) l)).
+// With many query rows per key these are dense contractions, so they run on
+// v_mfma_f32_16x16x32_f16 (logits) and v_mfma_f32_16x16x16_f16 (values), fp32 accumulation:
+//   prefill_q:     per row, q_rot (FWHT) and gamma S q_rot as fp16 operand rows;
+//   prefill_scan:  grid (64-row block, KV head, key split); per 64-key tile the workgroup
+//                  dequantizes the keys into LDS as [key][coord] fp16 rows (n16 c, +-r16)
+//                  and the values transposed, [coord][key] (n16 c, +-r16), then each wave
+//                  computes the logits of its 16 rows transposed (keys x rows, so the
+//                  accumulator is directly the B operand of the value product), applies the
+//                  causal mask and an online softmax, and accumulates A^T and Q^T;
+//   decode_combine merges the key splits and rotates back.
+// Precision: every operand is exact in fp16 or split into fp16 hi + lo.  The per-key norms
+// are kept out of the operands (the logit is n16 * acc_c + r16 * acc_s, the value weights are
+// p n16 and p r16), so the key-side operands are codebook values (hi + lo from a table) and
+// +-1 (exact); q_rot, gamma S q_rot and the weights are split hi + lo.  Three products per
+// split pair (hi hi, hi lo, lo hi) give ~2^-22 relative accuracy with fp32 accumulation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "tq_decode_kernel.h"
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tqk {
+
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPfRows = 64;             // query rows per workgroup (4 waves x 16)
+constexpr int kPfKeys = 64;             // keys per tile
+constexpr int kPfThreads = 256;
+constexpr int kKcStride = kD + 8;       // halves per [key][coord] row (padded)
+constexpr int kVtStride = kPfKeys + 8;  // halves per [coord][key] row (padded)
+
+struct PrefillQParams {
+  const void* q;        // [n_new][hq][128]
+  const float* S;       // key JL matrix [projection][coord]
+  _Float16* qop;        // [rows][512]: q_rot hi | lo | gamma S q_rot hi | lo, rows (kv head,
+                        // query, head in group)
+  int64_t rows;
+  int32_t q_dtype, n_new, hq, group;
+  uint32_t sign[4];     // key sign flips
+  float gamma;
+};
+
+// 16 rows per workgroup, one wave per row at a time; S stays in LDS.
+__global__ __launch_bounds__(256) void prefill_q(PrefillQParams p) {
+  __shared__ float Sl[kD * (kD + 1)];   // padded rows: lane j reads row j conflict-free
+  __shared__ float qr[4][kD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  for (int e = tid; e < kD * kD; e += 256) Sl[(e / kD) * (kD + 1) + (e % kD)] = p.S[e];
+  __syncthreads();
+  const float isd = 1.0f / sqrtf((float)kD);
+  for (int k = wave; k < 16; k += 4) {
+    const int64_t R = (int64_t)blockIdx.x * 16 + k;
+    if (R >= p.rows) break;
+    // R = (kv head * n_new + query) * group + g
+    const int64_t qg = R / p.group;
+    const int g = (int)(R - qg * p.group);
+    const int64_t kvh = qg / p.n_new, qi = qg - kvh * p.n_new;
+    const int64_t head = kvh * p.group + g;
+    float v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = lane + 64 * e;
+      float x = load_elem(p.q, (qi * p.hq + head) * kD + j, p.q_dtype);
+      const uint32_t sw = (lane & 32) ? uniform_u32(p.sign[2 * e + 1]) : uniform_u32(p.sign[2 * e]);
+      if ((sw >> (j & 31)) & 1u) x = -x;
+      v[e] = x;
+    }
+    fwht128(v, lane);
+    v[0] *= isd;
+    v[1] *= isd;
+    qr[wave][lane] = v[0];
+    qr[wave][lane + 64] = v[1];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the row is visible to the wave
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = lane + 64 * e;
+      float s = 0.0f;
+#pragma unroll 8
+      for (int i = 0; i < kD; ++i) s = fmaf(Sl[j * (kD + 1) + i], qr[wave][i], s);
+      const float gs = p.gamma * s;
+      const _Float16 qh = (_Float16)v[e], sh = (_Float16)gs;
+      p.qop[R * 512 + j] = qh;
+      p.qop[R * 512 + kD + j] = (_Float16)(v[e] - (float)qh);
+      p.qop[R * 512 + 2 * kD + j] = sh;
+      p.qop[R * 512 + 3 * kD + j] = (_Float16)(gs - (float)sh);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of qr done before the next row
+  }
+}
+
+struct PrefillParams {
+  const _Float16* qop;
+  const uint32_t* codes_k;
+  const uint32_t* norms_k;
+  const uint32_t* codes_v;
+  const uint32_t* norms_v;
+  const int32_t* block_table;
+  float* ws_part;               // [n_new * hq][n_split][kPartFloats]
+  int64_t num_pages;
+  int64_t start;                // position of the chunk's first token
+  int64_t keys_per_split;       // multiple of 64
+  int32_t page_log2, max_blocks;
+  int32_t n_new, hq, hkv, group, n_split;
+  float scale_log2;             // scale * log2(e)
+  float gamma;
+  int32_t kw, ksb, kblo, kbhi;  // key record: words, split blocks, widths
+  int32_t vw, vsb, vblo, vbhi, vq;
+  float cent_k[16], cent_v[16]; // lo table, hi table
+};
+
+// Block b of one record: code planes, sign word and the codebook table (hi, lo halves).
+struct BlockBits {
+  uint32_t w0, w1, w2, ws;
+  const _Float16* ct;   // [16]: 8 hi then 8 lo values of this block's codebook
+  bool qj;
+};
+
+__device__ __forceinline__ BlockBits block_bits(const uint32_t* rec, int b, int sb, int blo,
+                                                int bhi, int qj, const _Float16* tab) {
+  BlockBits k;
+  const bool lo = b < sb;
+  const int nb = lo ? blo : bhi;
+  const int off = lo ? b * (blo + qj) : sb * (blo + qj) + (b - sb) * (bhi + qj);
+  k.w0 = rec[off];
+  k.w1 = nb >= 2 ? rec[off + 1] : 0u;
+  k.w2 = nb >= 3 ? rec[off + 2] : 0u;
+  k.ws = qj ? rec[off + nb] : 0u;
+  k.ct = tab + (lo ? 0 : 16);
+  k.qj = qj != 0;
+  return k;
+}
+
+// Coordinates 8 q .. 8 q + 7 of the block: codebook value hi, lo, and the sign as +-1 (0
+// without sign words).
+__device__ __forceinline__ void dequant8(const BlockBits& k, int q, h16x8& ch, h16x8& cl, h16x8& sv) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = 8 * q + e;
+    const int idx = (int)(((k.w0 >> c) & 1u) | (((k.w1 >> c) & 1u) << 1) | (((k.w2 >> c) & 1u) << 2));
+    ch[e] = k.ct[idx];
+    cl[e] = k.ct[8 + idx];
+    sv[e] = k.qj ? (((k.ws >> c) & 1u) ? (_Float16)1.0f : (_Float16)(-1.0f)) : (_Float16)0.0f;
+  }
+}
+
+__global__ __launch_bounds__(kPfThreads) void prefill_scan(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) _Float16 Kh[kPfKeys * kKcStride];
+  __shared__ __attribute__((aligned(16))) _Float16 Kl[kPfKeys * kKcStride];
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[kPfKeys * kKcStride];
+  __shared__ __attribute__((aligned(16))) _Float16 Vh[kD * kVtStride];
+  __shared__ __attribute__((aligned(16))) _Float16 Vl[kD * kVtStride];
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[kD * kVtStride];
+  __shared__ float knorm[2][kPfKeys], vnorm[2][kPfKeys];  // n16, r16 of the tile's keys / values
+  __shared__ _Float16 tab[64];  // key lo table (hi, lo), key hi table, value lo, value hi
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  if (tid < 32) {
+    const int which = tid >> 3, m = tid & 7;   // 0: key lo, 1: key hi, 2: value lo, 3: value hi
+    const float c = which < 2 ? p.cent_k[(which & 1) * 8 + m] : p.cent_v[(which & 1) * 8 + m];
+    const _Float16 h = (_Float16)c;
+    tab[which * 16 + m] = h;
+    tab[which * 16 + 8 + m] = (_Float16)(c - (float)h);
+  }
+  const int64_t rows_kvh = (int64_t)p.n_new * p.group;
+  const int kvh = blockIdx.y, split = blockIdx.z;
+  const int64_t rb0 = (int64_t)blockIdx.x * kPfRows;
+  // this lane's row (one of the wave's 16); lanes l, l^16, l^32, l^48 share it
+  const int64_t rloc = rb0 + wave * 16 + (lane & 15);
+  const bool row_ok = rloc < rows_kvh;
+  const int64_t qi = row_ok ? rloc / p.group : 0;
+  const int64_t limit = p.start + qi;            // the row sees keys t <= limit
+  const int64_t R = (int64_t)kvh * rows_kvh + (row_ok ? rloc : 0);
+  // query operands (B of the logit product): coords 32 ks + 8 (lane >> 4) .. + 7, hi and lo
+  h16x8 qh[4], ql[4], sh[4], sl[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const _Float16* src = p.qop + R * 512 + 32 * ks + 8 * (lane >> 4);
+    qh[ks] = row_ok ? *reinterpret_cast<const h16x8*>(src) : h16x8{};
+    ql[ks] = row_ok ? *reinterpret_cast<const h16x8*>(src + kD) : h16x8{};
+    sh[ks] = row_ok ? *reinterpret_cast<const h16x8*>(src + 2 * kD) : h16x8{};
+    sl[ks] = row_ok ? *reinterpret_cast<const h16x8*>(src + 3 * kD) : h16x8{};
+  }
+  const int64_t total = p.start + p.n_new;
+  const int64_t last_row = (rb0 + kPfRows < rows_kvh ? rb0 + kPfRows : rows_kvh) - 1;
+  int64_t t_lo = (int64_t)split * p.keys_per_split;
+  int64_t t_hi = t_lo + p.keys_per_split;
+  if (t_hi > total) t_hi = total;
+  if (t_hi > p.start + last_row / p.group + 1) t_hi = p.start + last_row / p.group + 1;
+
+  f32x4 om[8], oq[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    om[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    oq[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  for (int64_t t0 = t_lo; t0 < t_hi; t0 += kPfKeys) {
+    __syncthreads();  // the previous tile is consumed
+    {  // dequantize: thread = (key lane, block = wave); absent keys become zeros
+      const int64_t t = t0 + lane;
+      const int b = wave;
+      bool ok = t < total;
+      int64_t row = 0;
+      if (ok) {
+        const int32_t pg = p.block_table[t0 >> p.page_log2];
+        ok = pg >= 0 && (int64_t)pg < p.num_pages;
+        row = (((int64_t)pg * p.hkv + kvh) << p.page_log2) + (t & ((1ll << p.page_log2) - 1));
+      }
+      BlockBits kbits{}, vbits{};
+      kbits.ct = tab;
+      vbits.ct = tab + 32;
+      if (ok) {
+        kbits = block_bits(p.codes_k + row * p.kw, b, p.ksb, p.kblo, p.kbhi, 1, tab);
+        vbits = block_bits(p.codes_v + row * p.vw, b, p.vsb, p.vblo, p.vbhi, p.vq, tab + 32);
+      }
+      if (b == 0) {  // norms of the tile's keys and values (zero for absent keys)
+        const uint32_t nk = ok ? p.norms_k[row] : 0u, nv = ok ? p.norms_v[row] : 0u;
+        knorm[0][lane] = f16_bits_to_f32(nk & 0xFFFFu);
+        knorm[1][lane] = f16_bits_to_f32(nk >> 16);
+        vnorm[0][lane] = f16_bits_to_f32(nv & 0xFFFFu);
+        vnorm[1][lane] = f16_bits_to_f32(nv >> 16);
+      }
+      const int ko = lane * kKcStride + 32 * b;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h16x8 ch, cl, sv;
+        dequant8(kbits, q, ch, cl, sv);
+        *reinterpret_cast<h16x8*>(Kh + ko + 8 * q) = ch;
+        *reinterpret_cast<h16x8*>(Kl + ko + 8 * q) = cl;
+        *reinterpret_cast<h16x8*>(Ks + ko + 8 * q) = sv;
+        dequant8(vbits, q, ch, cl, sv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int vo = (32 * b + 8 * q + e) * kVtStride + lane;
+          Vh[vo] = ch[e];
+          Vl[vo] = cl[e];
+          Vs[vo] = sv[e];
+        }
+      }
+    }
+    __syncthreads();
+    // ---- logits, transposed: lg[kb][r] = key kb*16 + 4 (lane >> 4) + r, row lane & 15
+    float lg[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 ac = {0.0f, 0.0f, 0.0f, 0.0f}, as = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int ko = (kb * 16 + (lane & 15)) * kKcStride + 8 * (lane >> 4);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const h16x8 kh = *reinterpret_cast<const h16x8*>(Kh + ko + 32 * ks);
+        const h16x8 kl = *reinterpret_cast<const h16x8*>(Kl + ko + 32 * ks);
+        const h16x8 kss = *reinterpret_cast<const h16x8*>(Ks + ko + 32 * ks);
+        ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qh[ks], ac, 0, 0, 0);
+        ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl, qh[ks], ac, 0, 0, 0);
+        ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, ql[ks], ac, 0, 0, 0);
+        as = __builtin_amdgcn_mfma_f32_16x16x32_f16(kss, sh[ks], as, 0, 0, 0);
+        as = __builtin_amdgcn_mfma_f32_16x16x32_f16(kss, sl[ks], as, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = kb * 16 + 4 * (lane >> 4) + r;
+        const int64_t key = t0 + kk;
+        const bool vis = row_ok && key <= limit && key < t_hi;
+        const float est = fmaf(knorm[0][kk], ac[r], knorm[1][kk] * as[r]);
+        lg[kb][r] = vis ? est * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, lg[kb][r]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, other_half(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+    float psum = 0.0f;
+    // value weights p n16 and p r16 of each key, split hi + lo (B operands of the value sum)
+    h16x4 pch[4], pcl[4], psh[4], psl[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = kb * 16 + 4 * (lane >> 4) + r;
+        const float pv = (lg[kb][r] == -INFINITY) ? 0.0f : exp2f(lg[kb][r] - m_new);
+        psum += pv;
+        const float wc = pv * vnorm[0][kk], wq = pv * vnorm[1][kk];
+        const _Float16 wch = (_Float16)wc, wqh = (_Float16)wq;
+        pch[kb][r] = wch;
+        pcl[kb][r] = (_Float16)(wc - (float)wch);
+        psh[kb][r] = wqh;
+        psl[kb][r] = (_Float16)(wq - (float)wqh);
+      }
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += other_half(psum);
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      om[cb] *= corr;
+      oq[cb] *= corr;
+    }
+    // ---- values: om[cb][r] = A^T[coord cb*16 + 4 (lane >> 4) + r][row lane & 15]
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        const int off = (cb * 16 + (lane & 15)) * kVtStride + kb * 16 + 4 * (lane >> 4);
+        const h16x4 vh = *reinterpret_cast<const h16x4*>(Vh + off);
+        const h16x4 vl = *reinterpret_cast<const h16x4*>(Vl + off);
+        const h16x4 vs = *reinterpret_cast<const h16x4*>(Vs + off);
+        om[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vh, pch[kb], om[cb], 0, 0, 0);
+        om[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vl, pch[kb], om[cb], 0, 0, 0);
+        om[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vh, pcl[kb], om[cb], 0, 0, 0);
+        oq[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vs, psh[kb], oq[cb], 0, 0, 0);
+        oq[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vs, psl[kb], oq[cb], 0, 0, 0);
+      }
+    }
+  }
+  // ---- this split's partial of each row, in the decode scan's format
+  if (row_ok) {
+    const int64_t head = (int64_t)kvh * p.group + (rloc - qi * p.group);
+    float* part = p.ws_part + ((qi * p.hq + head) * p.n_split + split) * kPartFloats;
+    if ((lane >> 4) == 0) {
+      part[0] = m_run;
+      part[1] = l_run;
+    }
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int coord = cb * 16 + 4 * (lane >> 4) + r;
+        part[2 + coord] = om[cb][r];
+        part[2 + kD + coord] = p.gamma * oq[cb][r];
+      }
+  }
+}
+
+}  // namespace tqk
+
+// ---------------------------------------------------------------------------------------
+tq_prefill_plan tq_plan_prefill(int32_t n_new, int32_t hq, int32_t hkv, int64_t start) {
+  using namespace tqk;
+  tq_prefill_plan pl{};
+  const int group = hq / hkv;
+  const int64_t rows_kvh = (int64_t)n_new * group;
+  const int64_t blocks = (rows_kvh + kPfRows - 1) / kPfRows;
+  const int64_t keys = start + n_new;
+  const int64_t tiles = (keys + kPfKeys - 1) / kPfKeys;
+  int64_t n_split = (512 + blocks * hkv - 1) / (blocks * hkv);   // about two workgroups per CU
+  if (n_split > tiles) n_split = tiles;
+  if (n_split > 256) n_split = 256;
+  if (n_split < 1) n_split = 1;
+  const int64_t tps = ((tiles + n_split - 1) / n_split) * kPfKeys;
+  pl.n_split = (int32_t)n_split;
+  pl.keys_per_split = tps;
+  pl.row_blocks = blocks;
+  pl.ws_q_off = 0;
+  pl.ws_part_off = ((int64_t)hkv * rows_kvh * 512 * 2 + 255) / 256 * 256;
+  pl.ws_bytes = pl.ws_part_off + (int64_t)n_new * hq * n_split * kPartFloats * 4;
+  return pl;
+}
+
+int tq_launch_prefill(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                      const tq_tables* tv, const void* q, int32_t q_dtype, int32_t n_new,
+                      int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                      const void* codes_v, const uint16_t* norms_v, int32_t page_log2,
+                      int64_t num_pages, const int32_t* block_table, int32_t max_blocks,
+                      int64_t start, float scale, float* out, void* workspace,
+                      const tq_prefill_plan& pl, hipStream_t stream) {
+  using namespace tqk;
+  const int group = hq / hkv;
+  const int64_t rows = (int64_t)hkv * n_new * group;
+  char* ws = reinterpret_cast<char*>(workspace);
+  _Float16* qop = reinterpret_cast<_Float16*>(ws + pl.ws_q_off);
+  const float gamma = (float)(std::sqrt(M_PI / 2.0) / kD);
+  PrefillQParams qp{};
+  qp.q = q;
+  qp.S = tk->S;
+  qp.qop = qop;
+  qp.rows = rows;
+  qp.q_dtype = q_dtype;
+  qp.n_new = n_new;
+  qp.hq = hq;
+  qp.group = group;
+  qp.gamma = gamma;
+  for (int i = 0; i < 4; ++i) qp.sign[i] = 0;
+  for (int j = 0; j < kD; ++j)
+    if (tk->signs[j] < 0) qp.sign[j >> 5] |= 1u << (j & 31);
+  hipLaunchKernelGGL(prefill_q, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, qp);
+  if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+
+  PrefillParams p{};
+  p.qop = qop;
+  p.codes_k = reinterpret_cast<const uint32_t*>(codes_k);
+  p.norms_k = reinterpret_cast<const uint32_t*>(norms_k);
+  p.codes_v = reinterpret_cast<const uint32_t*>(codes_v);
+  p.norms_v = reinterpret_cast<const uint32_t*>(norms_v);
+  p.block_table = block_table;
+  p.ws_part = reinterpret_cast<float*>(ws + pl.ws_part_off);
+  p.num_pages = num_pages;
+  p.start = start;
+  p.keys_per_split = pl.keys_per_split;
+  p.page_log2 = page_log2;
+  p.max_blocks = max_blocks;
+  p.n_new = n_new;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = group;
+  p.n_split = pl.n_split;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.gamma = gamma;
+  p.kw = (int)(tq_record_bytes(fk) / 4);
+  p.ksb = fk->split / 32;
+  p.kblo = fk->bits_lo;
+  p.kbhi = fk->split == fk->d ? fk->bits_lo : fk->bits_hi;
+  p.vw = (int)(tq_record_bytes(fv) / 4);
+  p.vsb = fv->split / 32;
+  p.vblo = fv->bits_lo;
+  p.vbhi = fv->split == fv->d ? fv->bits_lo : fv->bits_hi;
+  p.vq = fv->qjl;
+  for (int i = 0; i < 8; ++i) {
+    p.cent_k[i] = i < (1 << p.kblo) ? tk->centroids_lo[i] : 0.0f;
+    p.cent_k[8 + i] = i < (1 << p.kbhi) ? tk->centroids_hi[i] : 0.0f;
+    p.cent_v[i] = i < (1 << p.vblo) ? tv->centroids_lo[i] : 0.0f;
+    p.cent_v[8 + i] = i < (1 << p.vbhi) ? tv->centroids_hi[i] : 0.0f;
+  }
+  const dim3 grid((unsigned)pl.row_blocks, (unsigned)hkv, (unsigned)pl.n_split);
+  hipLaunchKernelGGL(prefill_scan, grid, dim3(kPfThreads), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+
+  DecodeParams cp{};
+  cp.S_v = tv->S;
+  cp.out = out;
+  cp.ws_part = p.ws_part;
+  cp.n_split = pl.n_split;
+  for (int i = 0; i < 4; ++i) cp.sign_v[i] = 0;
+  for (int j = 0; j < kD; ++j)
+    if (tv->signs[j] < 0) cp.sign_v[j >> 5] |= 1u << (j & 31);
+  return launch_decode_combine(cp, n_new * hq, stream);
+}

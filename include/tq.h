@@ -201,15 +201,17 @@ int tq_attend_decode_paged(const tq_format* fk, const tq_tables* tk, const tq_fo
                            float* logits, int64_t* skipped, void* workspace,
                            int64_t workspace_bytes, tq_stream_t stream);
 
-/* Workspace bytes tq_prefill_paged needs. */
-int64_t tq_prefill_workspace_bytes(int32_t n_new, int32_t hq, int32_t hkv, int32_t max_blocks,
-                                   int32_t page_size);
+/* Workspace bytes tq_prefill_paged needs for a chunk of n_new tokens starting at `start`. */
+int64_t tq_prefill_workspace_bytes(int32_t n_new, int32_t hq, int32_t hkv, int64_t start);
 
 /* One prefill chunk of one sequence on a paged cache: the chunk's new keys and values are
  * quantized and written at positions start .. start + n_new - 1 of the sequence (the
- * step before decode: quantize-on-write), then each new query attends, exactly as a
- * decode step would (same estimator, softmax, value sum), to the cached tokens at or
- * before its own position -- causal attention over the compressed cache.
+ * step before decode: quantize-on-write), then each new query attends with the decode
+ * estimator, softmax and value sum to the cached tokens at or before its own position --
+ * causal attention over the compressed cache.  The attention runs on MFMA with fp16
+ * operands (the query rows q_rot and gamma S q_rot, the dequantized n16 c[idx] and
+ * +-r16, the softmax weights) and fp32 accumulation.  Any d = 128 formats; the keys must
+ * carry QJL.
  *   q            : device [n_new][hq][128], dtype q_dtype
  *   k_new, v_new : device [n_new][hkv] rows of 128 elements, dtype kv_dtype, row stride
  *                  ld_kv elements
@@ -218,7 +220,8 @@ int64_t tq_prefill_workspace_bytes(int32_t n_new, int32_t hq, int32_t hkv, int32
  *                  start + n_new - 1 must have a page
  *   out          : device out fp32 [n_new][hq][128]
  *   counters     : as for tq_quantize_kv (both tensors add to it), nullable
- *   workspace    : device, >= tq_prefill_workspace_bytes(...)
+ *   workspace    : device, 256-byte aligned, >= tq_prefill_workspace_bytes(n_new, hq, hkv,
+ *                  start)
  * Errors: as tq_quantize_kv_paged and tq_attend_decode_paged; TQ_ERR_SHAPE when
  * start + n_new exceeds max_blocks * page_size.  Nothing is written when the arguments
  * are rejected. */
