@@ -23,10 +23,18 @@
 //             registers.  Online softmax per head with wavefront reductions; the Sparse-V
 //             gate (zhidx turboquant_plus article, section "01 turboquant_plus：介绍与详解")
 //             drops a value row for a head when its running weight estimate is below tau,
-//             and skips reading rows dropped by every head.  Values: each lane owns 4
-//             coordinates, the two half-waves take alternate kept tokens; the centroid
-//             pair of two coordinates comes from one read of a table indexed by their
-//             code bits; fp32 accumulation of w n16 c[idx] and w gamma r16 sigma per head.
+//             and skips reading rows dropped by every head.
+//             Values: the weighted sums A = sum_t u_t c[idx_t] (u = w n16) and
+//             Q = sum_t u'_t (2 sigma_t - 1) (u' = w gamma r16) are products of a
+//             (coordinates x tokens) matrix with a (tokens x heads) matrix, so they run on
+//             v_mfma_f32_16x16x32_f16 per 32-token group: lane (q, r) expands coordinates
+//             8r .. 8r + 7 of tokens 8q .. 8q + 7 (one byte of each code plane) into fp16
+//             operands, the centroid pair of two coordinates from one read of a table
+//             indexed by their code bits, the sign pair directly from the bits.  Centroids
+//             (scaled by 2^6) and weights are split into fp16 hi + lo halves and the weight
+//             columns carry both halves (heads x {hi, lo}), so the fp32 accumulation sees
+//             the full product to ~2^-22; sign operands (+-1) are exact.  Groups with no
+//             kept token are skipped.
 //             The waves' partial (m, l, acc) are merged in LDS: one partial per workgroup.
 //             MSE-only values (no sign words) drop the QJL term of the value sum.
 //   combine:  per (batch, query head) one workgroup merges the splits in a fixed order and
@@ -46,6 +54,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 128;
 constexpr int kNB = kD / 32;
@@ -89,13 +98,16 @@ __device__ __forceinline__ void load_record(const uint32_t* rec, uint32_t (&w)[W
   }
 }
 
-// Entries of the centroid-pair table of a B-bit codebook.  A lane's 4 coordinates have
+// Entries of the centroid-pair table of a B-bit codebook.  Four coordinates have
 // code-bit nibbles b0, b1, b2 (one per plane); f = b0 << 1 | b1 << 5 | b2 << 9 holds
 // the 2-bit fields of coordinates (2, 3) at bits 3-4, 7-8, 11-12, so (f & 0x1998) is 8
 // times the sparse pattern P = p0 | p1 << 4 | p2 << 8 of that coordinate pair, and
-// ((f << 2) & 0x1998) the same for coordinates (0, 1).  Entry P = (c[lo], c[hi]).
+// ((f << 2) & 0x1998) the same for coordinates (0, 1).  Entry P (8 bytes) = fp16
+// (hi(c'[lo]), hi(c'[hi])), (lo(c'[lo]), lo(c'[hi])) with c' = 2^6 c and lo = c' - hi.
 __host__ __device__ constexpr int pat_entries(int B) { return B == 3 ? 0x334 : (B == 2 ? 0x34 : 4); }
 constexpr uint32_t kPatMask = 0x1998u;
+constexpr float kCentScale = 64.0f;   // value centroids in the operand tables are 2^6 c
+constexpr float kQjlScale = 16.0f;    // QJL value weights in the operands are 2^4 u'
 
 struct DecodeParams {
   const void* q;
@@ -136,12 +148,15 @@ struct ScanLds {
   static constexpr int kTs = 32 * 16 * GC;    // [32 nibble groups][16][GC]
   static constexpr int kCpLo = round4(2 * pat_entries(BVLO));
   static constexpr int kCpHi = VSPLIT < kNB ? round4(2 * pat_entries(BVHI)) : 0;
-  static constexpr int kSp = 16 * 4;
-  static constexpr int kW0 = 2 * GC <= 4 ? 4 : 8;        // row: u[GC], u'[GC] | value record
-  static constexpr int kRS = round4(kW0 + VW);           // row stride (words)
-  static constexpr int kArea = (kTile + 1) * kRS + 4;    // 64 token rows + zero row + pad
+  static constexpr int kRS = round4(VW);                 // value record row stride (words)
+  // per wave: 64 value records, then fp16 weight rows [17][kWS]: 0..7 codebook-term
+  // columns (u hi for the GC heads, then u lo), 8..15 QJL-term columns, 16 zero; rows
+  // padded so the 8 rows one read touches fall in distinct banks
+  static constexpr int kWRows = 17;
+  static constexpr int kWS = kTile + 8;
+  static constexpr int kArea = kTile * kRS + kWRows * kWS / 2;
   // small tables first so their reads use the instruction's immediate offset
-  static constexpr int oCpLo = 0, oCpHi = oCpLo + kCpLo, oSp = oCpHi + kCpHi, oTs = oSp + kSp;
+  static constexpr int oCpLo = 0, oCpHi = oCpLo + kCpLo, oTs = oCpHi + kCpHi;
   static constexpr int oCc = oTs + kTs;                   // [2][GC] per-head constants
   static constexpr int oTq = oCc + round4(2 * GC), oArea = oTq + kTq;
   static constexpr int kTotal = oArea + kWaves * kArea;
@@ -230,13 +245,12 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   using VR = Rec<BVLO, BVHI, VSPLIT, VQ ? 1 : 0>;
   constexpr int KW = KR::W, VW = VR::W;
   using L = ScanLds<GC, VW, BVLO, BVHI, VSPLIT>;
-  constexpr int kW0 = L::kW0, kRS = L::kRS;
+  constexpr int kRS = L::kRS;
   __shared__ __attribute__((aligned(16))) float lds[L::kTotal];
   float* Tq = lds + L::oTq;
   float* Ts = lds + L::oTs;
   float* cpLo = lds + L::oCpLo;
   float* cpHi = lds + L::oCpHi;
-  float* spat = lds + L::oSp;
   float* cconst = lds + L::oCc;  // [2][GC]: codebook-term and QJL-term constants per head
 
   const int tid = threadIdx.x;
@@ -395,11 +409,13 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     const int p0 = P & 15, p1 = (P >> 4) & 15, p2 = (P >> 8) & 15;
     const int ilo = ((p0 & 1) | ((p1 & 1) << 1) | ((p2 & 1) << 2)) & mask;
     const int ihi = (((p0 >> 1) & 1) | (((p1 >> 1) & 1) << 1) | (((p2 >> 1) & 1) << 2)) & mask;
-    float* dst = hi ? cpHi : cpLo;
-    dst[2 * P] = cents[(hi ? 8 : 0) + ilo];
-    dst[2 * P + 1] = cents[(hi ? 8 : 0) + ihi];
+    uint32_t* dst = reinterpret_cast<uint32_t*>(hi ? cpHi : cpLo);
+    const float c0 = cents[(hi ? 8 : 0) + ilo] * kCentScale, c1 = cents[(hi ? 8 : 0) + ihi] * kCentScale;
+    const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+    const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
+    dst[2 * P] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    dst[2 * P + 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
   }
-  if (tid < 64) spat[tid] = ((tid >> 2) >> (tid & 3)) & 1 ? 1.0f : -1.0f;
   __syncthreads();
   float tq_v[16 * 256 / kThreads][GC];
 #pragma unroll
@@ -437,79 +453,39 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     ahi[k] = 2.0f * p.alpha_k[1][k];
   }
 
-  // ---- per-wave area: 64 token rows + one all-zero row used to pad odd token counts.
-  // Row bases are kept opaque to the compiler so that row and field offsets fold into the
-  // LDS instructions' 16-bit immediate instead of being re-added per access.
+  // ---- per-wave area: 64 value records + the weight rows.  Row bases are kept opaque to
+  // the compiler so that row and field offsets fold into the LDS instructions' 16-bit
+  // immediate instead of being re-added per access.
   int area_off = L::oArea + wave * L::kArea;
   asm volatile("" : "+v"(area_off));
   float* area = lds + area_off;
-  for (int i = lane; i < kRS + 4; i += 64) area[kTile * kRS + i] = 0.0f;
-  // value lane mapping: half-wave hw takes alternate tokens; lane owns coordinates
-  // 4 c4 .. 4 c4 + 3 of block vblk, bits vbit .. vbit + 3 of its plane words
-  const int hw = lane >> 5, c4 = lane & 31;
-  const int vblk = c4 >> 3, vbit = 4 * (c4 & 7);
+  _Float16* wts = reinterpret_cast<_Float16*>(area + kTile * kRS);
+  for (int i = lane; i < L::kWRows * L::kWS / 2; i += 64) area[kTile * kRS + i] = 0.0f;
+  // value lane mapping: lane (vq, vr) owns tokens 4 j + vq (j = 0..7) of each 32-token
+  // group, which are k = 8 vq + j of the MFMA, and coordinates 8 vr .. 8 vr + 7 (byte
+  // vr & 3 of the plane words of block vr >> 2); it also supplies weight column vr of the
+  // B operand.  The weight rows hold token 32 g + 4 j + q at position 32 g + 8 q + j, so a
+  // lane's 8 weights are contiguous, and the 4 record rows one read touches are adjacent.
+  const int vq = lane >> 4, vr = lane & 15;
+  const int vblk = vr >> 2, vsh = 8 * (vr & 3);
   const bool vlo = vblk < VSPLIT;
   const int vnb = vlo ? BVLO : BVHI;
-  const int voff = kW0 + VR::off(vblk);
+  const int voff = VR::off(vblk);
   const char* cpb = reinterpret_cast<const char*>(vlo ? cpLo : cpHi);
-  const char* spb = reinterpret_cast<const char*>(spat);
+  const int wrow_m = vr < 8 ? vr : 16, wrow_s = vr < 8 ? 8 + vr : 16;
 
-  float m_run[GC], l_run[GC], am[GC][4], aq[GC][4];
+  float m_run[GC], l_run[GC];
 #pragma unroll
   for (int h = 0; h < GC; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) am[h][k] = aq[h][k] = 0.0f;
   }
+  // accm[e][i], accq[e][i]: coordinate 8 (4 vq + i) + e, weight column vr
+  f32x4 accm[8], accq[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) accm[e] = accq[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   unsigned long long n_skipped = 0;
   const float kscale = p.scale * kLog2e;
-
-  // one value row (this lane's 4 coordinates) accumulated with the row's weights
-  auto value_row = [&](const float* r) {
-    const uint32_t* rw = reinterpret_cast<const uint32_t*>(r) + voff;
-    uint32_t p0, p1 = 0, p2 = 0, sg = 0;
-    if constexpr (!VQ) {
-      p0 = rw[0];
-      if constexpr (BVLO >= 2 || BVHI >= 2) p1 = vnb >= 2 ? rw[1] : 0u;
-      if constexpr (BVLO == 3 || BVHI == 3) p2 = vnb == 3 ? rw[2] : 0u;
-    } else if constexpr (BVLO == 3 && BVHI == 3) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(rw);
-      p0 = x[0]; p1 = x[1]; p2 = x[2]; sg = x[3];
-    } else {
-      const uint32_t x0 = rw[0], x1 = rw[1], x2 = rw[2], x3 = rw[3];
-      p0 = x0;
-      p1 = vnb >= 2 ? x1 : 0u;
-      p2 = vnb == 3 ? x2 : 0u;
-      sg = vnb == 3 ? x3 : (vnb == 2 ? x2 : x1);
-    }
-    const uint32_t f = (__builtin_amdgcn_ubfe(p0, vbit, 4) << 1) |
-                       (__builtin_amdgcn_ubfe(p1, vbit, 4) << 5) |
-                       (__builtin_amdgcn_ubfe(p2, vbit, 4) << 9);
-    const f32x2 cA = *reinterpret_cast<const f32x2*>(cpb + ((f << 2) & kPatMask));
-    const f32x2 cB = *reinterpret_cast<const f32x2*>(cpb + (f & kPatMask));
-    float u[GC];
-    table_read<GC>(r, 0, u);
-#pragma unroll
-    for (int h = 0; h < GC; ++h) {
-      am[h][0] = fmaf(u[h], cA[0], am[h][0]);
-      am[h][1] = fmaf(u[h], cA[1], am[h][1]);
-      am[h][2] = fmaf(u[h], cB[0], am[h][2]);
-      am[h][3] = fmaf(u[h], cB[1], am[h][3]);
-    }
-    if constexpr (VQ) {
-      const f32x4 sv = *reinterpret_cast<const f32x4*>(spb + 16 * __builtin_amdgcn_ubfe(sg, vbit, 4));
-      float u2[GC];
-      table_read<GC>(r + GC, 0, u2);
-#pragma unroll
-      for (int h = 0; h < GC; ++h) {
-        aq[h][0] = fmaf(u2[h], sv[0], aq[h][0]);
-        aq[h][1] = fmaf(u2[h], sv[1], aq[h][1]);
-        aq[h][2] = fmaf(u2[h], sv[2], aq[h][2]);
-        aq[h][3] = fmaf(u2[h], sv[3], aq[h][3]);
-      }
-    }
-  };
 
   for (; t0 < t_end; t0 += (int64_t)kWaves * kTile) {
     const int64_t t = t0 + lane;
@@ -555,78 +531,135 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     // ---------------- online softmax (per head, wavefront reductions)
     const float vn16 = f16_bits_to_f32(vn), vr16 = f16_bits_to_f32(vn >> 16);
     bool any_keep = false;
-    float u[GC], u2[GC];
+    float u[GC], u2[GC], corr[GC];
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
       const float mt = wave_max_fast(lg[h]);
       const float mn = fmaxf(m_run[h], mt);
-      const float corr = (m_run[h] == -INFINITY) ? 0.0f : exp2f(m_run[h] - mn);
+      corr[h] = (m_run[h] == -INFINITY) ? 0.0f : exp2f(m_run[h] - mn);
       float wgt = valid ? exp2f(lg[h] - mn) : 0.0f;
-      l_run[h] = l_run[h] * corr + wave_sum_fast(wgt);
+      l_run[h] = l_run[h] * corr[h] + wave_sum_fast(wgt);
       m_run[h] = mn;
       wgt = (gated && wgt < p.tau * l_run[h]) ? 0.0f : wgt;
       any_keep |= wgt > 0.0f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        am[h][k] *= corr;
-        aq[h][k] *= corr;
-      }
       u[h] = wgt * vn16;
-      u2[h] = wgt * p.gamma * vr16;
+      u2[h] = wgt * (p.gamma * kQjlScale) * vr16;
+    }
+    {  // rescale the accumulators: column vr holds head vr % GC
+      float cl = corr[0];
+#pragma unroll
+      for (int h = 1; h < GC; ++h) cl = (vr & (GC - 1)) == h ? corr[h] : cl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        accm[e] *= cl;
+        if constexpr (VQ) accq[e] *= cl;
+      }
     }
     const uint64_t keep = __ballot(any_keep);
     n_skipped += (unsigned long long)__popcll(__ballot(valid) & ~keep);
-    // this token's row: weights, then the value record (read only when kept if gated)
+    // this token's weight columns (fp16 hi, lo) and value record (read only when kept if
+    // gated); a row not written keeps finite codes from an earlier tile, met by zero weights
     {
-      int own = area_off + lane * kRS;
-      asm volatile("" : "+v"(own));
-      float* row = lds + own;
-      if constexpr (GC == 4) {
-        *reinterpret_cast<f32x4*>(row) = f32x4{u[0], u[1], u[2], u[3]};
-        if constexpr (VQ) *reinterpret_cast<f32x4*>(row + 4) = f32x4{u2[0], u2[1], u2[2], u2[3]};
-      } else {
+      constexpr int kWS = L::kWS;
+      _Float16* wl = wts + ((lane & 32) | ((lane & 3) << 3) | ((lane >> 2) & 7));
 #pragma unroll
-        for (int h = 0; h < GC; ++h) {
-          row[h] = u[h];
-          if constexpr (VQ) row[GC + h] = u2[h];
+      for (int h = 0; h < GC; ++h) {
+        const _Float16 uh = (_Float16)u[h];
+        wl[h * kWS] = uh;
+        wl[(GC + h) * kWS] = (_Float16)(u[h] - (float)uh);
+        if constexpr (VQ) {
+          const _Float16 sh = (_Float16)u2[h];
+          wl[(8 + h) * kWS] = sh;
+          wl[(8 + GC + h) * kWS] = (_Float16)(u2[h] - (float)sh);
         }
       }
       if (any_keep) {
         if (gated) load_record<VW, VR::VEC>(p.codes_v + (row0 + lane) * VW, vrec);
-        uint32_t* rv = reinterpret_cast<uint32_t*>(row + kW0);
+        int own = area_off + lane * kRS;
+        asm volatile("" : "+v"(own));
+        uint32_t* rv = reinterpret_cast<uint32_t*>(lds + own);
 #pragma unroll
         for (int i = 0; i < VW; ++i) rv[i] = vrec[i];
       }
     }
-    // ---------------- values: half-wave hw takes every other kept token
-    if (keep == ~0ull) {
-      int roff = area_off + hw * kRS;
-      asm volatile("" : "+v"(roff));
-      const float* r = lds + roff;
-#pragma unroll 4
-      for (int s = 0; s < kTile / 2; ++s) value_row(r + 2 * s * kRS);
-    } else {
-      uint64_t kk = keep;
-      while (kk) {
-        const int ta = __builtin_ctzll(kk);
-        kk &= kk - 1;
-        int tb = kTile;
-        if (kk) {
-          tb = __builtin_ctzll(kk);
-          kk &= kk - 1;
+    // ---------------- values on MFMA, per 32-token group
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      if ((uint32_t)(keep >> (32 * g)) == 0u) continue;  // no kept token in the group
+      const int wb = 32 * g + 8 * vq;
+      const h16x8 bm = *reinterpret_cast<const h16x8*>(wts + wrow_m * L::kWS + wb);
+      h16x8 bs{};
+      if constexpr (VQ) bs = *reinterpret_cast<const h16x8*>(wts + wrow_s * L::kWS + wb);
+      uint32_t f[8][2], sb[8];
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        int roff = area_off + (32 * g + 4 * tt + vq) * kRS + voff;
+        asm volatile("" : "+v"(roff));
+        const uint32_t* rw = reinterpret_cast<const uint32_t*>(lds + roff);
+        uint32_t p0, p1 = 0, p2 = 0, sg = 0;
+        if constexpr (VQ && BVLO == 3 && BVHI == 3) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(rw);
+          p0 = x[0]; p1 = x[1]; p2 = x[2]; sg = x[3];
+        } else {
+          p0 = rw[0];
+          if constexpr (BVLO >= 2 || BVHI >= 2) p1 = vnb >= 2 ? rw[1] : 0u;
+          if constexpr (BVLO == 3 || BVHI == 3) p2 = vnb == 3 ? rw[2] : 0u;
+          if constexpr (VQ) sg = rw[vnb];
         }
-        value_row(area + (hw ? tb : ta) * kRS);
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          f[tt][n] = (__builtin_amdgcn_ubfe(p0, vsh + 4 * n, 4) << 1) |
+                     (__builtin_amdgcn_ubfe(p1, vsh + 4 * n, 4) << 5) |
+                     (__builtin_amdgcn_ubfe(p2, vsh + 4 * n, 4) << 9);
+        sb[tt] = VQ ? __builtin_amdgcn_ubfe(sg, vsh, 8) : 0u;
+      }
+#pragma unroll
+      for (int ep = 0; ep < 4; ++ep) {  // coordinates 2 ep, 2 ep + 1 of the lane's byte
+        u32x2 ent[8];
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          const uint32_t fv = f[tt][ep >> 1];
+          const uint32_t a = (ep & 1) ? (fv & kPatMask) : ((fv << 2) & kPatMask);
+          ent[tt] = *reinterpret_cast<const u32x2*>(cpb + a);
+        }
+        // A operands: dword i = tokens (2 i, 2 i + 1) of one coordinate
+        u32x4 ah0, ah1, al0, al1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ah0[i] = __builtin_amdgcn_perm(ent[2 * i + 1][0], ent[2 * i][0], 0x05040100u);
+          ah1[i] = __builtin_amdgcn_perm(ent[2 * i + 1][0], ent[2 * i][0], 0x07060302u);
+          al0[i] = __builtin_amdgcn_perm(ent[2 * i + 1][1], ent[2 * i][1], 0x05040100u);
+          al1[i] = __builtin_amdgcn_perm(ent[2 * i + 1][1], ent[2 * i][1], 0x07060302u);
+        }
+        const int e0 = 2 * ep;
+        accm[e0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, ah0), bm, accm[e0], 0, 0, 0);
+        accm[e0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, al0), bm, accm[e0], 0, 0, 0);
+        accm[e0 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, ah1), bm, accm[e0 + 1], 0, 0, 0);
+        accm[e0 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, al1), bm, accm[e0 + 1], 0, 0, 0);
+        if constexpr (VQ) {
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const int e = e0 + d;
+            u32x4 so;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t x = sb[2 * i] | (sb[2 * i + 1] << 16);
+              so[i] = ((x << (15 - e)) & 0x80008000u) ^ 0xBC00BC00u;  // bit 1 -> +1, 0 -> -1
+            }
+            accq[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, so), bs, accq[e], 0, 0, 0);
+          }
+        }
       }
     }
   }
-  // ---------------- workgroup epilogue: the half-waves, then the waves' partials are
-  // merged in LDS (aliases Tq) and stored at device scope
+  // ---------------- workgroup epilogue: the lo-weight columns are folded into the hi
+  // ones, then the waves' partials are merged in LDS (aliases Tq) and stored at device scope
 #pragma unroll
-  for (int h = 0; h < GC; ++h)
+  for (int e = 0; e < 8; ++e)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      am[h][k] += other_half(am[h][k]);
-      aq[h][k] += other_half(aq[h][k]);
+    for (int i = 0; i < 4; ++i) {
+      accm[e][i] += xchg<GC>(accm[e][i]);
+      if constexpr (VQ) accq[e][i] += xchg<GC>(accq[e][i]);
     }
   __syncthreads();
   float* mine = lds + L::oWM + wave * L::kMerge;  // [2*GC] m, l | [GC][2][kD]
@@ -637,13 +670,16 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
       mine[GC + h] = l_run[h];
     }
   }
-  if (lane < 32) {
+  if (vr < GC) {
+    float* a = mine + round4(2 * GC) + vr * 2 * kD;
 #pragma unroll
-    for (int h = 0; h < GC; ++h) {
-      float* a = mine + round4(2 * GC) + h * 2 * kD + 4 * c4;
-      *reinterpret_cast<f32x4*>(a) = f32x4{am[h][0], am[h][1], am[h][2], am[h][3]};
-      *reinterpret_cast<f32x4*>(a + kD) = f32x4{aq[h][0], aq[h][1], aq[h][2], aq[h][3]};
-    }
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int coord = 8 * (4 * vq + i) + e;
+        a[coord] = accm[e][i] * (1.0f / kCentScale);
+        a[kD + coord] = VQ ? accq[e][i] * (1.0f / kQjlScale) : 0.0f;
+      }
   }
   __syncthreads();
 #pragma unroll
