@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFS = 157.3     # MI355X dense fp32 matrix
+FP16_MFMA_PEAK_TFS = 2500.0    # MI355X dense fp16 matrix
 SLOTS = 8
 BATCH, HQ, HKV, NTOK, D = 1, 32, 8, 32768, 128
 BITS = 3                        # codebook bits; b = 4 total with the QJL bit
@@ -46,6 +47,9 @@ def _parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 4 times (scale reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--search-only", action="store_true",
+                    help="only time the inner-product search on the 10^6 x 200 database "
+                         "(the search_1m_x_200 variant) and print its JSON (profiling runs)")
     return ap.parse_args()
 
 
@@ -249,6 +253,48 @@ def _requant_timing(tq, torch, dev, codes_k, norms_k, fmt, tab, signs, S, steps,
             "stored_gbs": round(stored / t / 1e9, 2)}
 
 
+def _search_timing(tq, torch, dev, TI, reps=2):
+    """Inner-product search on the 10^6 x 200 database (unit vectors, std i^-0.3 per
+    coordinate), zero-padded to d = 256 and packed at b = 4; 10^4 queries from the same law,
+    top-10.  Times the index build (quantize of the database) and the search of all queries.
+    Roofline: the estimator's 2 x 256 multiply-adds per (query, vector) pair (two dot
+    products of length d) against the dense fp16 MFMA peak the scan runs on; its operands
+    are split into fp16 hi + lo halves, so it issues 5 products where the dot products
+    count 2."""
+    n_db, n_q, d_in, d, k = 10 ** 6, 10 ** 4, 200, 256, 10
+    db = torch.from_numpy(TI.search_set(n_db, d_in, seed=TI.data_seed(5))).to(dev)
+    qs = torch.from_numpy(TI.search_set(n_q, d_in, seed=TI.data_seed(5) + 1)).to(dev)
+    signs, S = TI.rotation(d, TI.rotation_seed(5))
+    fmt = tq.Format.uniform(d, BITS)
+    tab = tq.Tables(fmt, signs, torch.from_numpy(S).to(dev))
+    codes = torch.empty((n_db, fmt.record_bytes()), dtype=torch.uint8, device=dev)
+    norms = torch.empty((n_db, 2), dtype=torch.float16, device=dev)
+    build = lambda: tq.quantize_kv(db, fmt, tab, codes=codes, norms=norms)
+    ws = torch.empty(tq.search_workspace_bytes(n_q, k, n_db, d), dtype=torch.uint8, device=dev)
+    search = lambda: tq.ip_search(qs, codes, norms, fmt, tab, k=k, workspace=ws)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for i in range(reps):
+            ev[i].record(); fn()
+        ev[reps].record(); torch.cuda.synchronize()
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e-3
+
+    tb = timed(build)
+    ts = timed(search)
+    flops = 2.0 * 2 * d * n_db * n_q
+    tfs = flops / ts / 1e12
+    return {"db_vectors": n_db, "d_in": d_in, "d": d, "queries": n_q, "k": k,
+            "format": "3-bit codebook + 1 QJL bit (132 B/vector)",
+            "index_build_ms": round(tb * 1e3, 3), "index_vectors_per_s": round(n_db / tb, 1),
+            "search_ms": round(ts * 1e3, 3), "queries_per_s": round(n_q / ts, 1),
+            "roofline": {"bound": "mfma", "kernel": "search_scan", "achieved": round(tfs, 3),
+                         "peak": FP16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tfs / FP16_MFMA_PEAK_TFS, 4), "traffic": None}}
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -269,6 +315,9 @@ def main():
     tq.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.search_only:
+        print(json.dumps({"search_1m_x_200": _search_timing(tq, torch, dev, TI)}), flush=True)
+        return
 
     seed = TI.data_seed(2)
     kb, vb, _ = TI.kv_layer(BATCH, HKV, NTOK, D, seed=seed)
@@ -389,6 +438,7 @@ def main():
     line["variants"]["prefill_chunk"] = _prefill_timing(tq, torch, dev, ks, vs, fmt, tab)
     line["variants"]["requantize_b4_to_b3"] = _requant_timing(tq, torch, dev, codes_k, norms_k, fmt,
                                                               tab, signs, S, steps, nvec)
+    line["variants"]["search_1m_x_200"] = _search_timing(tq, torch, dev, TI)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(kb, vb, qb, signs, S)
     print(json.dumps(line), flush=True)

@@ -4,18 +4,26 @@
 //   score_i = n16_i <q_rot, c[idx_i]> + gamma r16_i <S q_rot, 2 sigma_i - 1>,
 // and the k largest are returned (equal scores: lower id first).
 //
-//   prologue: per query one workgroup: zero-pad to d, q_rot = H D q / sqrt(d), S q_rot,
-//             the query's slice of the nibble subset-sum tables of its query group, and the
-//             constants of <w, 2b - 1> = 2 <w, b> - sum(w).
-//   scan:     grid (query group of QG queries, database split).  The workgroup expands the
-//             nibble tables into byte-indexed tables in LDS (one float per query) and
-//             streams its database range, lane = database vector, 16 table reads per
-//             32-coordinate sign word (Walsh planes of the codebook, then the QJL word).
-//             Each wave keeps, per query, a sorted top-k list in registers (lane i holds
-//             the i-th best); a ballot finds the tile's candidates above the k-th score
-//             and each is inserted with one lane shift.  The waves' lists are merged in LDS.
-//             All workgroups walk the database in the same order, so the ones running at
-//             the same time on an XCD read the same records through its L2.
+// For a batch of queries the scores are a (vectors x coordinates) x (coordinates x queries)
+// product, so the scan runs on v_mfma_f32_16x16x32_f16 straight from the packed records:
+//   prologue: per query one workgroup: zero-pad to d, q_rot = H D q / sqrt(d), S q_rot
+//             (fp32, to the workspace).
+//   scan:     grid (block of 32 queries, database split), 4 waves.  Wave w owns the record
+//             blocks of coordinates [w d/4, (w + 1) d/4) of every 64-vector tile, for all 32
+//             queries: lane (j, r) loads block b of vector 16 m + r and expands byte j of its
+//             planes into the A operand, centroid pairs (fp16 hi and lo of 2^6 c) from one
+//             read of a table indexed by the code bits of two coordinates and +-1 pairs
+//             from the sign word; the B operands are q_rot and S q_rot of the queries, each
+//             scaled by a power of two and split into fp16 hi + lo.  Five products per 32
+//             coordinates (c hi q hi, c lo q hi, c hi q lo, sign (S q) hi, sign (S q) lo)
+//             with fp32 accumulation give the two dot products to ~2^-22.  Each wave turns
+//             its sums into partial scores (n16 and gamma r16 applied in fp32) in LDS; after
+//             one barrier wave w adds the four partials of queries 8w .. 8w + 7 (lane =
+//             vector, fixed order) and keeps their top-k lists in registers (lane i holds the
+//             i-th best; a ballot finds the tile's candidates above the k-th score and each
+//             is inserted with one lane shift).  The partial scores are double-buffered: one
+//             barrier per tile.  Concurrent workgroups walk the same database range, so the
+//             records come through the L2.
 //   merge:    per query, the lists of the database splits are merged (skipped when there is
 //             one split: the scan then writes the final result).
 #include <hip/hip_runtime.h>
@@ -29,21 +37,22 @@
 namespace tqk {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kSWaves = 4;
-constexpr int kSTile = 64;
+constexpr int kSWaves = 4;    // waves per scan workgroup (one per coordinate quarter)
+constexpr int kSTile = 64;    // database vectors per tile
+constexpr int kSQ = 32;       // queries per scan workgroup
+constexpr int kSQW = kSQ / kSWaves;  // queries whose lists one wave keeps
+constexpr uint32_t kSPatMask = 0x1998u;
+constexpr float kSCent = 64.0f;  // centroids in the operand table are 2^6 c
 
-template <int D>
-struct SCfg {
-  static constexpr int NB = D / 32;
-  static constexpr int G = D / 8;                 // byte groups
-  static constexpr int QG = (D == 256) ? 2 : 4;   // queries per workgroup (128 KB of tables)
-  static constexpr int NIB = 2 * G * 2 * 16;      // nibble floats per query
-  static constexpr int NIB_STRIDE = ((NIB + 2) * QG + 3) / 4 * 4;
-  static constexpr int kTable = 2 * G * 256 * QG;
-};
+// Entries of the centroid-pair table of a B-bit codebook: four coordinates with code-bit
+// nibbles b0, b1, b2 give f = b0 << 1 | b1 << 5 | b2 << 9; (f & 0x1998) is 8 times the
+// sparse pattern P = p0 | p1 << 4 | p2 << 8 of coordinates (2, 3) and ((f << 2) & 0x1998)
+// that of coordinates (0, 1).  Entry P: fp16 (hi(c'[lo]), hi(c'[hi])), (lo(c'[lo]), lo(c'[hi])).
+__host__ __device__ constexpr int s_pat_entries(int B) { return B == 3 ? 0x334 : (B == 2 ? 0x34 : 4); }
 
 struct SearchParams {
   const uint32_t* codes;
@@ -52,27 +61,22 @@ struct SearchParams {
   const float* S;
   int64_t* out_ids;
   float* out_scores;
-  float* ws_q;       // [n_q][2][D]
-  float* ws_nib;     // [n_groups][NIB_STRIDE]
+  float* ws_q;       // [n_q][2][D]: q_rot, S q_rot
   float* ws_cand_s;  // [n_q][n_split][k]
   int64_t* ws_cand_i;
   int64_t n_db, n_q, chunk_len;
-  int32_t d_in, k, n_split, bits, words;
+  int32_t d_in, k, n_split;
   float gamma;
   uint32_t sign_mask[8];
-  float alpha[4];    // Walsh coefficients of the codebook
+  float cent[8];     // codebook, ascending
 };
 
 // ----------------------------------------------------------------------------- prologue
 template <int D>
 __global__ __launch_bounds__(256) void search_prologue(SearchParams p) {
-  using C = SCfg<D>;
   const int64_t qi = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int64_t grp = qi / C::QG;
-  const int slot = (int)(qi % C::QG);
   __shared__ float wv[2][D];
-  __shared__ float red[2][8];
   constexpr int NE = D / 64;
   if (wave == 0) {
     float v[NE];
@@ -122,34 +126,6 @@ __global__ __launch_bounds__(256) void search_prologue(SearchParams p) {
   __syncthreads();
   float* dq = p.ws_q + qi * 2 * D;
   for (int j = tid; j < 2 * D; j += 256) dq[j] = wv[j / D][j % D];
-  float* nib = p.ws_nib + grp * C::NIB_STRIDE;
-  for (int i = tid; i < C::NIB; i += 256) {
-    const int n = i % 16, half = (i / 16) % 2, g = (i / 32) % C::G, vv = i / (32 * C::G);
-    float sum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if ((n >> k) & 1) sum += wv[vv][8 * g + 4 * half + k];
-    nib[i * C::QG + slot] = sum;
-  }
-  // constants: (sum_k alpha_k) sum(q_rot), sum(S q_rot); fixed-order reduction
-  float aq = 0.0f, as = 0.0f;
-  for (int j = tid; j < D; j += 256) {
-    aq += wv[0][j];
-    as += wv[1][j];
-  }
-  aq = wave_sum_fast(aq);
-  as = wave_sum_fast(as);
-  if (lane == 0) {
-    red[0][wave] = aq;
-    red[1][wave] = as;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float asum = 0.0f;
-    for (int k = 0; k < 4; ++k) asum += p.alpha[k];
-    nib[C::NIB * C::QG + slot] = asum * (((red[0][0] + red[0][1]) + red[0][2]) + red[0][3]);
-    nib[C::NIB * C::QG + C::QG + slot] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
-  }
 }
 
 // a before b in the result order: larger score, then lower id
@@ -178,118 +154,200 @@ __device__ __forceinline__ void list_insert(float& ls, int64_t& li, float s, int
 
 template <int D, int B>
 __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
-  using C = SCfg<D>;
-  constexpr int QG = C::QG, NB = C::NB, W = NB * (B + 1);
-  extern __shared__ __attribute__((aligned(16))) float lds[];
-  float* Tq = lds;                          // [G][256][QG]
-  float* Ts = lds + C::G * 256 * QG;        // [G][256][QG]
-  float* stage = lds + C::kTable;           // nibble staging, later the waves' lists
-  __shared__ float cst[2][QG];
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int64_t grp = blockIdx.x;
+  constexpr int NB = D / 32, W = NB * (B + 1);
+  constexpr int KS = NB / kSWaves;      // record blocks per wave
+  constexpr int kPat = s_pat_entries(B);
+  __shared__ __attribute__((aligned(16))) uint32_t cpt[2 * kPat];
+  __shared__ __attribute__((aligned(16))) float part[2][kSWaves][kSQ][kSTile];  // partial scores
+  __shared__ __attribute__((aligned(16))) uint32_t nrm[2][kSTile];              // tile norms
+  __shared__ float qscl[2][kSQ];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int64_t q0 = (int64_t)blockIdx.x * kSQ;
   const int split = blockIdx.y;
-  const int64_t q0 = grp * QG;
   const int64_t db_begin = (int64_t)split * p.chunk_len;
   int64_t db_end = db_begin + p.chunk_len;
   if (db_end > p.n_db) db_end = p.n_db;
 
-  // ---- tables
-  {
-    const float* src = p.ws_nib + grp * C::NIB_STRIDE;
-    for (int i = threadIdx.x; i < C::NIB * QG / 4; i += blockDim.x)
-      reinterpret_cast<f32x4*>(stage)[i] = reinterpret_cast<const f32x4*>(src)[i];
-    if (threadIdx.x < 2 * QG) (&cst[0][0])[threadIdx.x] = src[C::NIB * QG + threadIdx.x];
+  // ---- centroid-pair table
+  for (int P = tid; P < kPat; P += 64 * kSWaves) {
+    const int mask = (1 << B) - 1;
+    const int p0 = P & 15, p1 = (P >> 4) & 15, p2 = (P >> 8) & 15;
+    const int ilo = ((p0 & 1) | ((p1 & 1) << 1) | ((p2 & 1) << 2)) & mask;
+    const int ihi = (((p0 >> 1) & 1) | (((p1 >> 1) & 1) << 1) | (((p2 >> 1) & 1) << 2)) & mask;
+    const float c0 = p.cent[ilo] * kSCent, c1 = p.cent[ihi] * kSCent;
+    const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+    const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
+    cpt[2 * P] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    cpt[2 * P + 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 2 * C::G * 16; i += blockDim.x) {
-    const int lo = i % 16, g = (i / 16) % C::G, vv = i / (16 * C::G);
-    const float* nl = stage + (((vv * C::G + g) * 2 + 0) * 16 + lo) * QG;
-    const float* nh = stage + (((vv * C::G + g) * 2 + 1) * 16) * QG;
-    float a[QG];
+  // ---- per-query power-of-two scales putting the largest |q_rot|, |S q_rot| in [128, 256)
 #pragma unroll
-    for (int h = 0; h < QG; ++h) a[h] = nl[h];
-    float* dst = (vv == 0 ? Tq : Ts) + (g * 256 + lo) * QG;
-#pragma unroll 4
-    for (int hi = 0; hi < 16; ++hi)
+  for (int h = 0; h < kSQW; ++h) {
+    const int q = kSQW * wave + h;
+    const int64_t qi = q0 + q;
 #pragma unroll
-      for (int h = 0; h < QG; ++h) dst[hi * 16 * QG + h] = a[h] + nh[hi * QG + h];
+    for (int v = 0; v < 2; ++v) {
+      float m = 0.0f;
+      if (qi < p.n_q) {
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) m = fmaxf(m, fabsf(p.ws_q[(qi * 2 + v) * D + lane + 64 * e]));
+      }
+      m = wave_max_fast(m);
+      if (lane == 0) qscl[v][q] = m > 0.0f ? exp2f(7.0f - floorf(log2f(m))) : 1.0f;
+    }
   }
   __syncthreads();
 
-  float cq[QG], cs[QG];
+  // lane roles: A operand / loads, lane (kj, kr): byte kj of the record blocks of vector
+  // 16 m + kr; B operand, lane (kj, n): coordinates 32 b + 8 kj + e of query 16 nb + n;
+  // result, lane (kq, n): vectors 16 m + 4 kq + i of query 16 nb + n
+  const int kj = lane >> 4, kr = lane & 15;
+  const int blk0 = KS * wave;
+  u32x4 bqh[2][KS], bql[2][KS], bsh[2][KS], bsl[2][KS];
+  float kc[2], ksc[2];
 #pragma unroll
-  for (int h = 0; h < QG; ++h) {
-    cq[h] = cst[0][h];
-    cs[h] = cst[1][h];
+  for (int nb = 0; nb < 2; ++nb) {
+    const int q = 16 * nb + kr;
+    const int64_t qi = q0 + q;
+    const bool qv = qi < p.n_q;
+    const float fq = qscl[0][q], fs = qscl[1][q];
+    kc[nb] = 1.0f / (kSCent * fq);
+    ksc[nb] = p.gamma / fs;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = 32 * (blk0 + ks) + 8 * kj;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        float x0 = 0.0f, x1 = 0.0f, y0 = 0.0f, y1 = 0.0f;
+        if (qv) {
+          x0 = p.ws_q[(qi * 2) * D + c0 + 2 * d] * fq;
+          x1 = p.ws_q[(qi * 2) * D + c0 + 2 * d + 1] * fq;
+          y0 = p.ws_q[(qi * 2 + 1) * D + c0 + 2 * d] * fs;
+          y1 = p.ws_q[(qi * 2 + 1) * D + c0 + 2 * d + 1] * fs;
+        }
+        const _Float16 a0 = (_Float16)x0, a1 = (_Float16)x1, b0 = (_Float16)y0, b1 = (_Float16)y1;
+        const _Float16 a0l = (_Float16)(x0 - (float)a0), a1l = (_Float16)(x1 - (float)a1);
+        const _Float16 b0l = (_Float16)(y0 - (float)b0), b1l = (_Float16)(y1 - (float)b1);
+        auto pk = [](_Float16 u, _Float16 v) {
+          return (uint32_t)__builtin_bit_cast(uint16_t, u) | ((uint32_t)__builtin_bit_cast(uint16_t, v) << 16);
+        };
+        bqh[nb][ks][d] = pk(a0, a1);
+        bql[nb][ks][d] = pk(a0l, a1l);
+        bsh[nb][ks][d] = pk(b0, b1);
+        bsl[nb][ks][d] = pk(b0l, b1l);
+      }
+    }
   }
-  float al[4];
+
+  // ---- register prefetch of one tile's record blocks of this wave (A layout); wave 0 also
+  // fetches the norms of the tile after it (lane = vector), staged in LDS one tile ahead
+  uint32_t rw[4][KS][B + 1], nr = 0;
+  auto fetch = [&](int64_t tt0) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) al[k] = 2.0f * p.alpha[k];
+    for (int m = 0; m < 4; ++m) {
+      const int64_t v = tt0 + 16 * m + kr;
+      if (v < db_end) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint32_t* rec = p.codes + v * W + (blk0 + ks) * (B + 1);
+          if constexpr (B == 3) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(rec);
+            rw[m][ks][0] = x[0]; rw[m][ks][1] = x[1]; rw[m][ks][2] = x[2]; rw[m][ks][3] = x[3];
+          } else {
+#pragma unroll
+            for (int i = 0; i <= B; ++i) rw[m][ks][i] = rec[i];
+          }
+        }
+      }
+    }
+    if (wave == 0) nr = tt0 + kSTile + lane < db_end ? p.norms[tt0 + kSTile + lane] : 0u;
+  };
+  const char* cpb = reinterpret_cast<const char*>(cpt);
   const int k = p.k;
-
-  float ls[QG];
-  int64_t li[QG];
+  float ls[kSQW];
+  int64_t li[kSQW];
 #pragma unroll
-  for (int h = 0; h < QG; ++h) {
+  for (int h = 0; h < kSQW; ++h) {
     ls[h] = -INFINITY;
     li[h] = INT64_MAX;
   }
 
-  uint32_t rw[W], nr = 0;
-  int64_t t0 = db_begin + (int64_t)wave * kSTile;
-  auto fetch = [&](int64_t tt0) {
-    const int64_t t = tt0 + lane;
-    if (t < db_end) {
+  if (wave == 0) nrm[0][lane] = db_begin + lane < db_end ? p.norms[db_begin + lane] : 0u;
+  fetch(db_begin);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t t0 = db_begin; t0 < db_end; t0 += kSTile, buf ^= 1) {
+    // ---------------- this wave's coordinates of the tile on MFMA, one 16-vector block at a
+    // time, then its partial scores into LDS
 #pragma unroll
-      for (int i = 0; i < W / 4; ++i) {
-        const u32x4 v = reinterpret_cast<const u32x4*>(p.codes + t * W)[i];
-        rw[4 * i] = v[0]; rw[4 * i + 1] = v[1]; rw[4 * i + 2] = v[2]; rw[4 * i + 3] = v[3];
-      }
-      nr = p.norms[t];
-    }
-  };
-  fetch(t0);
-  for (; t0 < db_end; t0 += (int64_t)kSWaves * kSTile) {
-    const int64_t t = t0 + lane;
-    const bool valid = t < db_end;
-    uint32_t w[W];
+    for (int m = 0; m < 4; ++m) {
+      f32x4 ac[2], as[2];
 #pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = rw[i];
-    const uint32_t nn = nr;
-    fetch(t0 + (int64_t)kSWaves * kSTile);
-    float mse[QG], qjl[QG];
+      for (int nb = 0; nb < 2; ++nb) ac[nb] = as[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int h = 0; h < QG; ++h) mse[h] = qjl[h] = 0.0f;
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t p0 = rw[m][ks][0];
+        const uint32_t p1 = B >= 2 ? rw[m][ks][1] : 0u;
+        const uint32_t p2 = B >= 3 ? rw[m][ks][2] : 0u;
+        const uint32_t sg = rw[m][ks][B];
+        u32x4 ah, al, so;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      const uint32_t* wb = w + blk * (B + 1);
+        for (int n = 0; n < 2; ++n) {
+          const uint32_t f = (__builtin_amdgcn_ubfe(p0, 8 * kj + 4 * n, 4) << 1) |
+                             (__builtin_amdgcn_ubfe(p1, 8 * kj + 4 * n, 4) << 5) |
+                             (__builtin_amdgcn_ubfe(p2, 8 * kj + 4 * n, 4) << 9);
+          const u32x2 e0 = *reinterpret_cast<const u32x2*>(cpb + ((f << 2) & kSPatMask));
+          const u32x2 e1 = *reinterpret_cast<const u32x2*>(cpb + (f & kSPatMask));
+          ah[2 * n] = e0[0];
+          al[2 * n] = e0[1];
+          ah[2 * n + 1] = e1[0];
+          al[2 * n + 1] = e1[1];
+        }
+        {  // sign pairs: bit 2d -> half 0, bit 2d + 1 -> half 1; set bit = +1
+          const uint32_t x = __builtin_amdgcn_ubfe(sg, 8 * kj, 8);
+          const uint32_t y = x | (x << 15);
 #pragma unroll
-      for (int pl = 0; pl < (B == 3 ? 4 : B); ++pl) {
-        const uint32_t word = (pl < B) ? wb[pl] : (wb[0] ^ wb[1] ^ wb[2]);
+          for (int d = 0; d < 4; ++d) so[d] = ((y << (15 - 2 * d)) & 0x80008000u) ^ 0xBC00BC00u;
+        }
+        const h16x8 Ah = __builtin_bit_cast(h16x8, ah), Al = __builtin_bit_cast(h16x8, al);
+        const h16x8 Ao = __builtin_bit_cast(h16x8, so);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float* e = Tq + ((4 * blk + i) * 256 + ((word >> (8 * i)) & 0xFFu)) * QG;
-#pragma unroll
-          for (int h = 0; h < QG; ++h) mse[h] = fmaf(al[pl], e[h], mse[h]);
+        for (int nb = 0; nb < 2; ++nb) {
+          ac[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, __builtin_bit_cast(h16x8, bqh[nb][ks]), ac[nb], 0, 0, 0);
+          ac[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, __builtin_bit_cast(h16x8, bqh[nb][ks]), ac[nb], 0, 0, 0);
+          ac[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, __builtin_bit_cast(h16x8, bql[nb][ks]), ac[nb], 0, 0, 0);
+          as[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, __builtin_bit_cast(h16x8, bsh[nb][ks]), as[nb], 0, 0, 0);
+          as[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, __builtin_bit_cast(h16x8, bsl[nb][ks]), as[nb], 0, 0, 0);
         }
       }
-      const uint32_t sw = wb[B];
+      const u32x4 n4 = *reinterpret_cast<const u32x4*>(&nrm[buf][16 * m + 4 * kj]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float* e = Ts + ((4 * blk + i) * 256 + ((sw >> (8 * i)) & 0xFFu)) * QG;
+      for (int nb = 0; nb < 2; ++nb) {
+        f32x4 ps;
 #pragma unroll
-        for (int h = 0; h < QG; ++h) qjl[h] += e[h];
+        for (int i = 0; i < 4; ++i)
+          ps[i] = f16_bits_to_f32(n4[i] & 0xFFFFu) * ac[nb][i] * kc[nb] +
+                  f16_bits_to_f32(n4[i] >> 16) * as[nb][i] * ksc[nb];
+        *reinterpret_cast<f32x4*>(&part[buf][wave][16 * nb + kr][16 * m + 4 * kj]) = ps;
       }
     }
-    const float n16 = f16_bits_to_f32(nn), r16 = f16_bits_to_f32(nn >> 16);
+    if (wave == 0) nrm[buf ^ 1][lane] = nr;  // the next tile's norms, fetched a tile ago
+    fetch(t0 + kSTile);
+    __syncthreads();
+    // ---------------- scores and top-k lists of queries kSQW * wave + h (lane = vector)
+    const int64_t v = t0 + lane;
+    const bool valid = v < db_end;
 #pragma unroll
-    for (int h = 0; h < QG; ++h) {
-      if (q0 + h >= p.n_q) continue;
-      const float sc = valid ? n16 * (mse[h] - cq[h]) + p.gamma * r16 * (2.0f * qjl[h] - cs[h]) : -INFINITY;
-      // k-th entry of the list, then the tile's candidates that beat it
-      const float ks = __shfl(ls[h], k - 1, 64);
-      const int64_t ki = __shfl(li[h], k - 1, 64);
-      uint64_t cand = __ballot(valid && better(sc, t, ks, ki));
+    for (int h = 0; h < kSQW; ++h) {
+      const int q = kSQW * wave + h;
+      if (q0 + q >= p.n_q) continue;
+      float sc = part[buf][0][q][lane];
+#pragma unroll
+      for (int w2 = 1; w2 < kSWaves; ++w2) sc += part[buf][w2][q][lane];
+      sc = valid ? sc : -INFINITY;
+      const float kth = __shfl(ls[h], k - 1, 64);
+      const int64_t kid = __shfl(li[h], k - 1, 64);
+      uint64_t cand = __ballot(valid && better(sc, v, kth, kid));
       while (cand) {
         const int L = __builtin_ctzll(cand);
         cand &= cand - 1;
@@ -298,35 +356,17 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
       }
     }
   }
-  // ---- merge the waves' lists per query (fixed order), write candidates / result
-  __syncthreads();
-  float* lst_s = stage;                                           // [waves][QG][64]
-  int64_t* lst_i = reinterpret_cast<int64_t*>(stage + kSWaves * QG * 64);
+  // ---- results (each query's list is complete in its owner wave)
 #pragma unroll
-  for (int h = 0; h < QG; ++h) {
-    lst_s[(wave * QG + h) * 64 + lane] = ls[h];
-    lst_i[(wave * QG + h) * 64 + lane] = li[h];
-  }
-  __syncthreads();
-  if (wave < QG && q0 + wave < p.n_q) {
-    const int h = wave;
-    float ms = -INFINITY;
-    int64_t mi = INT64_MAX;
-    for (int w2 = 0; w2 < kSWaves; ++w2)
-      for (int i = 0; i < k; ++i) {
-        const float s = lst_s[(w2 * QG + h) * 64 + i];
-        const int64_t id = lst_i[(w2 * QG + h) * 64 + i];
-        if (better(s, id, __shfl(ms, k - 1, 64), __shfl(mi, k - 1, 64))) list_insert(ms, mi, s, id, k);
-      }
-    const int64_t qi = q0 + h;
-    if (lane < k) {
-      if (p.n_split == 1) {
-        p.out_scores[qi * k + lane] = ms;
-        p.out_ids[qi * k + lane] = mi;
-      } else {
-        p.ws_cand_s[(qi * p.n_split + split) * k + lane] = ms;
-        p.ws_cand_i[(qi * p.n_split + split) * k + lane] = mi;
-      }
+  for (int h = 0; h < kSQW; ++h) {
+    const int64_t qi = q0 + kSQW * wave + h;
+    if (qi >= p.n_q || lane >= k) continue;
+    if (p.n_split == 1) {
+      p.out_scores[qi * k + lane] = ls[h];
+      p.out_ids[qi * k + lane] = li[h];
+    } else {
+      p.ws_cand_s[(qi * p.n_split + split) * k + lane] = ls[h];
+      p.ws_cand_i[(qi * p.n_split + split) * k + lane] = li[h];
     }
   }
 }
@@ -350,21 +390,11 @@ __global__ __launch_bounds__(64) void search_merge(SearchParams p) {
 }
 
 template <int D, int B>
-static int launch_search(const SearchParams& p, int64_t n_groups, hipStream_t stream) {
-  using C = SCfg<D>;
-  const int nstage = (kSWaves * C::QG * 64 * 3 > C::NIB * C::QG) ? kSWaves * C::QG * 64 * 3 : C::NIB * C::QG;
-  const size_t lds = sizeof(float) * (size_t)(C::kTable + nstage);
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute((const void*)search_scan<D, B>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
-      return TQ_ERR_HIP;
-    attr = true;
-  }
+static int launch_search(const SearchParams& p, int64_t n_blocks, hipStream_t stream) {
   hipLaunchKernelGGL(search_prologue<D>, dim3((unsigned)p.n_q), dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
-  hipLaunchKernelGGL((search_scan<D, B>), dim3((unsigned)n_groups, (unsigned)p.n_split),
-                     dim3(64 * kSWaves), lds, stream, p);
+  hipLaunchKernelGGL((search_scan<D, B>), dim3((unsigned)n_blocks, (unsigned)p.n_split),
+                     dim3(64 * kSWaves), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   if (p.n_split > 1) {
     hipLaunchKernelGGL(search_merge, dim3((unsigned)p.n_q), dim3(64), 0, stream, p);
@@ -373,45 +403,26 @@ static int launch_search(const SearchParams& p, int64_t n_groups, hipStream_t st
   return TQ_OK;
 }
 
-static void walsh_s(int bits, const float* c, float* alpha) {
-  const int L = 1 << bits;
-  const int subsets[4] = {1, 2, 4, 7};
-  for (int k = 0; k < 4; ++k) alpha[k] = 0.0f;
-  const int nw = bits == 3 ? 4 : bits;
-  for (int k = 0; k < nw; ++k) {
-    double s = 0.0;
-    for (int idx = 0; idx < L; ++idx) {
-      double prod = 1.0;
-      for (int bit = 0; bit < bits; ++bit)
-        if ((subsets[k] >> bit) & 1) prod *= ((idx >> bit) & 1) ? 1.0 : -1.0;
-      s += (double)c[idx] * prod;
-    }
-    alpha[k] = (float)(s / L);
-  }
-}
-
 }  // namespace tqk
 
 // ---------------------------------------------------------------------------------------
 tq_search_plan tq_plan_search(int64_t n_q, int32_t k, int64_t n_db, int32_t d) {
   using namespace tqk;
   tq_search_plan p{};
-  const int qg = d == 256 ? SCfg<256>::QG : SCfg<128>::QG;
-  const int nib_stride = d == 256 ? SCfg<256>::NIB_STRIDE : SCfg<128>::NIB_STRIDE;
-  const int64_t groups = (n_q + qg - 1) / qg;
-  // split the database when there are too few query groups to fill a 256-CU MI355X
-  int64_t n_split = groups >= 256 ? 1 : (256 + groups - 1) / (groups > 0 ? groups : 1);
-  const int64_t max_split = (n_db + 16383) / 16384;
+  const int64_t blocks = (n_q + kSQ - 1) / kSQ;
+  // split the database so that the grid has several rounds of two workgroups per CU of a
+  // 256-CU MI355X (a short last round costs less), with at least 16 tiles per split
+  int64_t n_split = (2048 + (blocks > 0 ? blocks : 1) - 1) / (blocks > 0 ? blocks : 1);
+  const int64_t max_split = (n_db + 16 * kSTile - 1) / (16 * kSTile);
   if (n_split > max_split) n_split = max_split;
+  if (n_split > 4096) n_split = 4096;
   if (n_split < 1) n_split = 1;
   const int64_t chunk = (n_db + n_split - 1) / n_split;
   p.n_chunks = (int32_t)n_split;
   p.chunk_len = (chunk + kSTile - 1) / kSTile * kSTile;
   p.ws_q_off = 0;
   const int64_t q_bytes = (n_q > 0 ? n_q : 1) * 2 * d * 4;
-  const int64_t nib_off = (q_bytes + 255) / 256 * 256;
-  const int64_t nib_bytes = (groups > 0 ? groups : 1) * nib_stride * 4;
-  p.ws_cand_off = nib_off + (nib_bytes + 255) / 256 * 256;
+  p.ws_cand_off = (q_bytes + 255) / 256 * 256;
   const int64_t cand = (n_split > 1) ? (n_q > 0 ? n_q : 1) * n_split * k * 12 : 0;
   p.ws_bytes = p.ws_cand_off + cand + 256;
   return p;
@@ -431,10 +442,7 @@ int tq_launch_search(const tq_format* f, const tq_tables* t, const void* codes_d
   p.out_ids = out_ids;
   p.out_scores = out_scores;
   char* ws = reinterpret_cast<char*>(workspace);
-  const int64_t q_bytes = (n_q > 0 ? n_q : 1) * 2 * f->d * 4;
-  const int64_t nib_off = (q_bytes + 255) / 256 * 256;
-  p.ws_q = reinterpret_cast<float*>(ws);
-  p.ws_nib = reinterpret_cast<float*>(ws + nib_off);
+  p.ws_q = reinterpret_cast<float*>(ws + plan.ws_q_off);
   const int64_t nsk = n_q * plan.n_chunks * k;
   p.ws_cand_i = reinterpret_cast<int64_t*>(ws + plan.ws_cand_off);
   p.ws_cand_s = reinterpret_cast<float*>(ws + plan.ws_cand_off + nsk * 8);
@@ -444,22 +452,19 @@ int tq_launch_search(const tq_format* f, const tq_tables* t, const void* codes_d
   p.d_in = d_in;
   p.k = k;
   p.n_split = plan.n_chunks;
-  p.bits = f->bits_lo;
-  p.words = (int)(tq_record_bytes(f) / 4);
   p.gamma = (float)(std::sqrt(M_PI / 2.0) / f->d);
   for (int j = 0; j < 8; ++j) p.sign_mask[j] = 0;
   for (int j = 0; j < f->d; ++j)
     if (t->signs[j] < 0) p.sign_mask[j >> 5] |= 1u << (j & 31);
-  walsh_s(f->bits_lo, t->centroids_lo, p.alpha);
-  const int qg = f->d == 256 ? SCfg<256>::QG : SCfg<128>::QG;
-  const int64_t groups = (n_q + qg - 1) / qg;
+  for (int i = 0; i < 8; ++i) p.cent[i] = i < (1 << f->bits_lo) ? t->centroids_lo[i] : 0.0f;
+  const int64_t n_blocks = (n_q + kSQ - 1) / kSQ;
   if (f->d == 256) {
-    if (f->bits_lo == 3) return launch_search<256, 3>(p, groups, stream);
-    if (f->bits_lo == 2) return launch_search<256, 2>(p, groups, stream);
+    if (f->bits_lo == 3) return launch_search<256, 3>(p, n_blocks, stream);
+    if (f->bits_lo == 2) return launch_search<256, 2>(p, n_blocks, stream);
   } else {
-    if (f->bits_lo == 3) return launch_search<128, 3>(p, groups, stream);
-    if (f->bits_lo == 2) return launch_search<128, 2>(p, groups, stream);
-    if (f->bits_lo == 1) return launch_search<128, 1>(p, groups, stream);
+    if (f->bits_lo == 3) return launch_search<128, 3>(p, n_blocks, stream);
+    if (f->bits_lo == 2) return launch_search<128, 2>(p, n_blocks, stream);
+    if (f->bits_lo == 1) return launch_search<128, 1>(p, n_blocks, stream);
   }
   return TQ_ERR_SHAPE;
 }

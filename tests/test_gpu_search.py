@@ -69,7 +69,7 @@ def _gpu_search(torch, queries, rec, norms, fmt_t, signs, S, k):
 
 
 @pytest.mark.parametrize("n_db,n_q,k,bits", [(12000, 37, 10, 3), (6000, 600, 10, 3), (5000, 9, 1, 3),
-                                             (5000, 9, 64, 2)])
+                                             (5000, 9, 64, 2), (3001, 70, 10, 2)])
 def test_search_matches_oracle_estimator(torch_gpu, n_db, n_q, k, bits):
     d_in, d = 200, 256
     db = TI.search_set(n_db, d_in, seed=5001)
