@@ -158,9 +158,10 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
   constexpr int KS = NB / kSWaves;      // record blocks per wave
   constexpr int kPat = s_pat_entries(B);
   __shared__ __attribute__((aligned(16))) uint32_t cpt[2 * kPat];
-  __shared__ __attribute__((aligned(16))) float part[2][kSWaves][kSQ][kSTile];  // partial scores
-  __shared__ __attribute__((aligned(16))) uint32_t nrm[2][kSTile];              // tile norms
-  __shared__ float qscl[2][kSQ];
+  // partial scores, rows padded by 4 floats so a wave's 16-row writes hit distinct banks
+  __shared__ __attribute__((aligned(16))) float part[2][kSWaves][kSQ][kSTile + 4];
+  __shared__ __attribute__((aligned(16))) float nrm[2][kSTile][2];  // n16, 2^6 gamma r16 of the tile
+  __shared__ float qscl[kSQ];
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int64_t q0 = (int64_t)blockIdx.x * kSQ;
   const int split = blockIdx.y;
@@ -180,21 +181,19 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
     cpt[2 * P] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
     cpt[2 * P + 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
   }
-  // ---- per-query power-of-two scales putting the largest |q_rot|, |S q_rot| in [128, 256)
+  // ---- per-query power-of-two scale putting the largest of |q_rot|, |S q_rot| in [128, 256)
+  // (one scale for both, so the two terms of a score share it)
 #pragma unroll
   for (int h = 0; h < kSQW; ++h) {
     const int q = kSQW * wave + h;
     const int64_t qi = q0 + q;
+    float m = 0.0f;
+    if (qi < p.n_q) {
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      float m = 0.0f;
-      if (qi < p.n_q) {
-#pragma unroll
-        for (int e = 0; e < D / 64; ++e) m = fmaxf(m, fabsf(p.ws_q[(qi * 2 + v) * D + lane + 64 * e]));
-      }
-      m = wave_max_fast(m);
-      if (lane == 0) qscl[v][q] = m > 0.0f ? exp2f(7.0f - floorf(log2f(m))) : 1.0f;
+      for (int e = 0; e < 2 * D / 64; ++e) m = fmaxf(m, fabsf(p.ws_q[qi * 2 * D + lane + 64 * e]));
     }
+    m = wave_max_fast(m);
+    if (lane == 0) qscl[q] = m > 0.0f ? exp2f(7.0f - floorf(log2f(m))) : 1.0f;
   }
   __syncthreads();
 
@@ -204,15 +203,12 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
   const int kj = lane >> 4, kr = lane & 15;
   const int blk0 = KS * wave;
   u32x4 bqh[2][KS], bql[2][KS], bsh[2][KS], bsl[2][KS];
-  float kc[2], ksc[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int q = 16 * nb + kr;
     const int64_t qi = q0 + q;
     const bool qv = qi < p.n_q;
-    const float fq = qscl[0][q], fs = qscl[1][q];
-    kc[nb] = 1.0f / (kSCent * fq);
-    ksc[nb] = p.gamma / fs;
+    const float fq = qscl[q], fs = fq;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c0 = 32 * (blk0 + ks) + 8 * kj;
@@ -262,8 +258,18 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
     }
     if (wave == 0) nr = tt0 + kSTile + lane < db_end ? p.norms[tt0 + kSTile + lane] : 0u;
   };
+  // partial score = n16 * (c-term sum) + 2^6 gamma r16 * (sign-term sum); the query's
+  // 1 / (2^6 scale) multiplies the total
+  const float g64 = p.gamma * kSCent;
+  auto put_norm = [&](int bsel, uint32_t x) {
+    nrm[bsel][lane][0] = f16_bits_to_f32(x & 0xFFFFu);
+    nrm[bsel][lane][1] = g64 * f16_bits_to_f32(x >> 16);
+  };
   const char* cpb = reinterpret_cast<const char*>(cpt);
   const int k = p.k;
+  float qf[kSQW];  // 1 / (2^6 scale) of the wave's list queries
+#pragma unroll
+  for (int h = 0; h < kSQW; ++h) qf[h] = 1.0f / (kSCent * qscl[kSQW * wave + h]);
   float ls[kSQW];
   int64_t li[kSQW];
 #pragma unroll
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
     li[h] = INT64_MAX;
   }
 
-  if (wave == 0) nrm[0][lane] = db_begin + lane < db_end ? p.norms[db_begin + lane] : 0u;
+  if (wave == 0) put_norm(0, db_begin + lane < db_end ? p.norms[db_begin + lane] : 0u);
   fetch(db_begin);
   __syncthreads();
   int buf = 0;
@@ -320,18 +326,18 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
           as[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, __builtin_bit_cast(h16x8, bsl[nb][ks]), as[nb], 0, 0, 0);
         }
       }
-      const u32x4 n4 = *reinterpret_cast<const u32x4*>(&nrm[buf][16 * m + 4 * kj]);
+      const f32x4 na = *reinterpret_cast<const f32x4*>(&nrm[buf][16 * m + 4 * kj][0]);
+      const f32x4 nb4 = *reinterpret_cast<const f32x4*>(&nrm[buf][16 * m + 4 * kj + 2][0]);
+      const float nn[4] = {na[0], na[2], nb4[0], nb4[2]}, rr[4] = {na[1], na[3], nb4[1], nb4[3]};
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         f32x4 ps;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ps[i] = f16_bits_to_f32(n4[i] & 0xFFFFu) * ac[nb][i] * kc[nb] +
-                  f16_bits_to_f32(n4[i] >> 16) * as[nb][i] * ksc[nb];
+        for (int i = 0; i < 4; ++i) ps[i] = fmaf(nn[i], ac[nb][i], rr[i] * as[nb][i]);
         *reinterpret_cast<f32x4*>(&part[buf][wave][16 * nb + kr][16 * m + 4 * kj]) = ps;
       }
     }
-    if (wave == 0) nrm[buf ^ 1][lane] = nr;  // the next tile's norms, fetched a tile ago
+    if (wave == 0) put_norm(buf ^ 1, nr);  // the next tile's norms, fetched a tile ago
     fetch(t0 + kSTile);
     __syncthreads();
     // ---------------- scores and top-k lists of queries kSQW * wave + h (lane = vector)
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
       float sc = part[buf][0][q][lane];
 #pragma unroll
       for (int w2 = 1; w2 < kSWaves; ++w2) sc += part[buf][w2][q][lane];
-      sc = valid ? sc : -INFINITY;
+      sc = valid ? sc * qf[h] : -INFINITY;
       const float kth = __shfl(ls[h], k - 1, 64);
       const int64_t kid = __shfl(li[h], k - 1, 64);
       uint64_t cand = __ballot(valid && better(sc, v, kth, kid));
