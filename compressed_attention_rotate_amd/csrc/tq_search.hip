@@ -158,6 +158,7 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
   constexpr int KS = NB / kSWaves;      // record blocks per wave
   constexpr int kPat = s_pat_entries(B);
   __shared__ __attribute__((aligned(16))) uint32_t cpt[2 * kPat];
+  __shared__ __attribute__((aligned(16))) uint32_t spt[16][2];  // nibble -> 4 fp16 +-1 (set bit +1)
   // partial scores, rows padded by 4 floats so a wave's 16-row writes hit distinct banks
   __shared__ __attribute__((aligned(16))) float part[2][kSWaves][kSQ][kSTile + 4];
   __shared__ __attribute__((aligned(16))) float nrm[2][kSTile][2];  // n16, 2^6 gamma r16 of the tile
@@ -180,6 +181,12 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
     const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
     cpt[2 * P] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
     cpt[2 * P + 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+  }
+  if (tid < 32) {
+    const int n = tid >> 1, d = tid & 1;
+    const uint32_t lo = ((n >> (2 * d)) & 1) ? 0x3C00u : 0xBC00u;
+    const uint32_t hi = ((n >> (2 * d + 1)) & 1) ? 0x3C00u : 0xBC00u;
+    spt[n][d] = lo | (hi << 16);
   }
   // ---- per-query power-of-two scale putting the largest of |q_rot|, |S q_rot| in [128, 256)
   // (one scale for both, so the two terms of a score share it)
@@ -309,11 +316,10 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
           ah[2 * n + 1] = e1[0];
           al[2 * n + 1] = e1[1];
         }
-        {  // sign pairs: bit 2d -> half 0, bit 2d + 1 -> half 1; set bit = +1
-          const uint32_t x = __builtin_amdgcn_ubfe(sg, 8 * kj, 8);
-          const uint32_t y = x | (x << 15);
-#pragma unroll
-          for (int d = 0; d < 4; ++d) so[d] = ((y << (15 - 2 * d)) & 0x80008000u) ^ 0xBC00BC00u;
+        {  // sign pairs from the nibble table: bit 2d -> half 0, bit 2d + 1 -> half 1
+          const u32x2 s0 = *reinterpret_cast<const u32x2*>(&spt[__builtin_amdgcn_ubfe(sg, 8 * kj, 4)][0]);
+          const u32x2 s1 = *reinterpret_cast<const u32x2*>(&spt[__builtin_amdgcn_ubfe(sg, 8 * kj + 4, 4)][0]);
+          so[0] = s0[0]; so[1] = s0[1]; so[2] = s1[0]; so[3] = s1[1];
         }
         const h16x8 Ah = __builtin_bit_cast(h16x8, ah), Al = __builtin_bit_cast(h16x8, al);
         const h16x8 Ao = __builtin_bit_cast(h16x8, so);
@@ -352,8 +358,10 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
       for (int w2 = 1; w2 < kSWaves; ++w2) sc += part[buf][w2][q][lane];
       sc = valid ? sc * qf[h] : -INFINITY;
       const float kth = __shfl(ls[h], k - 1, 64);
+      uint64_t cand = __ballot(sc >= kth);  // a superset of the candidates (-inf never enters)
+      if (cand == 0) continue;
       const int64_t kid = __shfl(li[h], k - 1, 64);
-      uint64_t cand = __ballot(valid && better(sc, v, kth, kid));
+      cand = __ballot(valid && better(sc, v, kth, kid));
       while (cand) {
         const int L = __builtin_ctzll(cand);
         cand &= cand - 1;
