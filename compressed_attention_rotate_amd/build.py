@@ -24,6 +24,11 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
+# per-source extra flags: the search scan keeps its MFMA accumulators in VGPRs (it reads
+# them back every tile; the AGPR form costs one copy per accumulator)
+EXTRA = {"tq_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -33,7 +38,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, hipcc: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON, *DEVICE, "-c", src, "-o", obj]
+    cmd = [hipcc, *COMMON, *DEVICE, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc, *COMMON, "-x", "hip", *DEVICE, "-c", src, "-o", obj]
     if verbose:

@@ -157,12 +157,23 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
   constexpr int NB = D / 32, W = NB * (B + 1);
   constexpr int KS = NB / kSWaves;      // record blocks per wave
   constexpr int kPat = s_pat_entries(B);
-  __shared__ __attribute__((aligned(16))) uint32_t cpt[2 * kPat];
-  __shared__ __attribute__((aligned(16))) uint32_t spt[16][2];  // nibble -> 4 fp16 +-1 (set bit +1)
-  // partial scores, rows padded by 4 floats so a wave's 16-row writes hit distinct banks
-  __shared__ __attribute__((aligned(16))) float part[2][kSWaves][kSQ][kSTile + 4];
-  __shared__ __attribute__((aligned(16))) float nrm[2][kSTile][2];  // n16, 2^6 gamma r16 of the tile
-  __shared__ float qscl[kSQ];
+  // one LDS block carved by hand so that the centroid-pair table sits at address 0 (its
+  // masked pattern is then the whole address):
+  //   cpt  [kPat][2] u32     centroid pairs (hi, lo)
+  //   spt  [16][2] u32       nibble -> 4 fp16 +-1 (set bit +1)
+  //   part [2][waves][32][68] partial scores, rows padded by 4 floats so a wave's 16-row
+  //                          writes hit distinct banks
+  //   nrm  [2][64][2]        n16, 2^6 gamma r16 of the tile's vectors
+  //   qscl [32]              per-query scales
+  constexpr int oSpt = (2 * kPat + 3) / 4 * 4, oPart = oSpt + 32;
+  constexpr int kPartN = 2 * kSWaves * kSQ * (kSTile + 4);
+  constexpr int oNrm = oPart + kPartN, oQs = oNrm + 2 * kSTile * 2, kSmem = oQs + kSQ;
+  __shared__ __attribute__((aligned(16))) uint32_t smem[kSmem];
+  uint32_t* cpt = smem;
+  uint32_t (*spt)[2] = reinterpret_cast<uint32_t (*)[2]>(smem + oSpt);
+  float (*part)[kSWaves][kSQ][kSTile + 4] = reinterpret_cast<float (*)[kSWaves][kSQ][kSTile + 4]>(smem + oPart);
+  float (*nrm)[kSTile][2] = reinterpret_cast<float (*)[kSTile][2]>(smem + oNrm);
+  float* qscl = reinterpret_cast<float*>(smem + oQs);
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int64_t q0 = (int64_t)blockIdx.x * kSQ;
   const int split = blockIdx.y;
@@ -304,17 +315,19 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
         const uint32_t p2 = B >= 3 ? rw[m][ks][2] : 0u;
         const uint32_t sg = rw[m][ks][B];
         u32x4 ah, al, so;
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const uint32_t f = (__builtin_amdgcn_ubfe(p0, 8 * kj + 4 * n, 4) << 1) |
-                             (__builtin_amdgcn_ubfe(p1, 8 * kj + 4 * n, 4) << 5) |
-                             (__builtin_amdgcn_ubfe(p2, 8 * kj + 4 * n, 4) << 9);
-          const u32x2 e0 = *reinterpret_cast<const u32x2*>(cpb + ((f << 2) & kSPatMask));
-          const u32x2 e1 = *reinterpret_cast<const u32x2*>(cpb + (f & kSPatMask));
-          ah[2 * n] = e0[0];
-          al[2 * n] = e0[1];
-          ah[2 * n + 1] = e1[0];
-          al[2 * n + 1] = e1[1];
+        {  // F: the pattern field of the byte's low nibble in bits 0..15, high nibble in 16..31
+          // (nibble bits of plane k at 1 + 4k ..), from the three plane bytes by multiplies
+          const uint32_t F = ((__builtin_amdgcn_ubfe(p0, 8 * kj, 8) * 0x2002u) & 0x001E001Eu) |
+                             ((__builtin_amdgcn_ubfe(p1, 8 * kj, 8) * 0x20020u) & 0x01E001E0u) |
+                             ((__builtin_amdgcn_ubfe(p2, 8 * kj, 8) * 0x200200u) & 0x1E001E00u);
+          const u32x2 e0 = *reinterpret_cast<const u32x2*>(cpb + ((F << 2) & kSPatMask));
+          const u32x2 e1 = *reinterpret_cast<const u32x2*>(cpb + (F & kSPatMask));
+          const u32x2 e2 = *reinterpret_cast<const u32x2*>(cpb + ((F >> 14) & kSPatMask));
+          const u32x2 e3 = *reinterpret_cast<const u32x2*>(cpb + ((F >> 16) & kSPatMask));
+          ah[0] = e0[0]; al[0] = e0[1];
+          ah[1] = e1[0]; al[1] = e1[1];
+          ah[2] = e2[0]; al[2] = e2[1];
+          ah[3] = e3[0]; al[3] = e3[1];
         }
         {  // sign pairs from the nibble table: bit 2d -> half 0, bit 2d + 1 -> half 1
           const u32x2 s0 = *reinterpret_cast<const u32x2*>(&spt[__builtin_amdgcn_ubfe(sg, 8 * kj, 4)][0]);
