@@ -47,6 +47,9 @@ def _parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 4 times (scale reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time the 512-token prefill chunk at 32K context (the "
+                         "prefill_chunk variant) and print its JSON (profiling runs)")
     ap.add_argument("--search-only", action="store_true",
                     help="only time the inner-product search on the 10^6 x 200 database "
                          "(the search_1m_x_200 variant) and print its JSON (profiling runs)")
@@ -330,6 +333,10 @@ def main():
 
     k0 = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
     v0 = torch.from_numpy(vb.view(np.int16)).to(dev).view(torch.bfloat16)
+    if args.prefill_only:
+        print(json.dumps({"prefill_chunk": _prefill_timing(tq, torch, dev, [k0], [v0], fmt, tab)}),
+              flush=True)
+        return
     # SLOTS distinct inputs (token order rotated per slot: same law, different bytes)
     ks = [torch.roll(k0, shifts=4099 * i, dims=2).contiguous() for i in range(SLOTS)]
     vs = [torch.roll(v0, shifts=4099 * i, dims=2).contiguous() for i in range(SLOTS)]

@@ -24,9 +24,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
-# per-source extra flags: the search scan keeps its MFMA accumulators in VGPRs (it reads
-# them back every tile; the AGPR form costs one copy per accumulator)
-EXTRA = {"tq_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source extra flags: the search and prefill scans keep their MFMA accumulators in VGPRs
+# (they read them back every tile; the AGPR form costs one copy per accumulator)
+EXTRA = {"tq_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "tq_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

@@ -122,39 +122,30 @@ struct PrefillParams {
   float cent_k[16], cent_v[16]; // lo table, hi table
 };
 
-// Block b of one record: code planes, sign word and the codebook table (hi, lo halves).
-struct BlockBits {
-  uint32_t w0, w1, w2, ws;
-  const _Float16* ct;   // [16]: 8 hi then 8 lo values of this block's codebook
-  bool qj;
-};
+// Centroid-pair table of a B-bit codebook, indexed by the sparse code-bit pattern of two
+// coordinates: four coordinates with code-bit nibbles b0, b1, b2 give f = b0 << 1 |
+// b1 << 5 | b2 << 9, and (f & 0x1998) is 8 times the pattern P = p0 | p1 << 4 | p2 << 8 of
+// coordinates (2, 3), ((f << 2) & 0x1998) that of coordinates (0, 1).  Entry P holds the
+// fp16 (hi(c'[lo]), hi(c'[hi])), (lo(c'[lo]), lo(c'[hi])) of c' = 2^6 c.
+constexpr int kPfPat = 0x334;          // entries of the 3-bit table (and room for 1 or 2 bits)
+constexpr uint32_t kPfPatMask = 0x1998u;
+constexpr float kPfCent = 64.0f;
 
-__device__ __forceinline__ BlockBits block_bits(const uint32_t* rec, int b, int sb, int blo,
-                                                int bhi, int qj, const _Float16* tab) {
-  BlockBits k;
-  const bool lo = b < sb;
-  const int nb = lo ? blo : bhi;
-  const int off = lo ? b * (blo + qj) : sb * (blo + qj) + (b - sb) * (bhi + qj);
-  k.w0 = rec[off];
-  k.w1 = nb >= 2 ? rec[off + 1] : 0u;
-  k.w2 = nb >= 3 ? rec[off + 2] : 0u;
-  k.ws = qj ? rec[off + nb] : 0u;
-  k.ct = tab + (lo ? 0 : 16);
-  k.qj = qj != 0;
-  return k;
+// Pattern fields of one code byte (bits sh .. sh + 7 of the planes): the low nibble's field in
+// bits 0..15, the high nibble's in 16..31 (three byte x constant products place the plane
+// nibbles 4 bits apart).
+__device__ __forceinline__ uint32_t pattern_fields(uint32_t p0, uint32_t p1, uint32_t p2, int sh) {
+  return ((__builtin_amdgcn_ubfe(p0, sh, 8) * 0x2002u) & 0x001E001Eu) |
+         ((__builtin_amdgcn_ubfe(p1, sh, 8) * 0x20020u) & 0x01E001E0u) |
+         ((__builtin_amdgcn_ubfe(p2, sh, 8) * 0x200200u) & 0x1E001E00u);
 }
 
-// Coordinates 8 q .. 8 q + 7 of the block: codebook value hi, lo, and the sign as +-1 (0
-// without sign words).
-__device__ __forceinline__ void dequant8(const BlockBits& k, int q, h16x8& ch, h16x8& cl, h16x8& sv) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = 8 * q + e;
-    const int idx = (int)(((k.w0 >> c) & 1u) | (((k.w1 >> c) & 1u) << 1) | (((k.w2 >> c) & 1u) << 2));
-    ch[e] = k.ct[idx];
-    cl[e] = k.ct[8 + idx];
-    sv[e] = k.qj ? (((k.ws >> c) & 1u) ? (_Float16)1.0f : (_Float16)(-1.0f)) : (_Float16)0.0f;
-  }
+// The four centroid pairs (coordinates 0-1, 2-3, 4-5, 6-7 of the byte) from table cp.
+__device__ __forceinline__ void pattern_pairs(const char* cp, uint32_t F, u32x2 (&e)[4]) {
+  e[0] = *reinterpret_cast<const u32x2*>(cp + ((F << 2) & kPfPatMask));
+  e[1] = *reinterpret_cast<const u32x2*>(cp + (F & kPfPatMask));
+  e[2] = *reinterpret_cast<const u32x2*>(cp + ((F >> 14) & kPfPatMask));
+  e[3] = *reinterpret_cast<const u32x2*>(cp + ((F >> 16) & kPfPatMask));
 }
 
 __global__ __launch_bounds__(kPfThreads) void prefill_scan(PrefillParams p) {
@@ -164,15 +155,34 @@ __global__ __launch_bounds__(kPfThreads) void prefill_scan(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) _Float16 Vh[kD * kVtStride];
   __shared__ __attribute__((aligned(16))) _Float16 Vl[kD * kVtStride];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[kD * kVtStride];
-  __shared__ float knorm[2][kPfKeys], vnorm[2][kPfKeys];  // n16, r16 of the tile's keys / values
-  __shared__ _Float16 tab[64];  // key lo table (hi, lo), key hi table, value lo, value hi
+  // n16 / 2^6, r16 of the tile's keys and n16, r16 of its values (zero for absent tokens)
+  __shared__ float knorm[2][kPfKeys], vnorm[2][kPfKeys];
+  __shared__ __attribute__((aligned(16))) uint32_t cpt[4][2 * kPfPat];  // key lo, key hi, value lo, value hi
+  __shared__ __attribute__((aligned(16))) uint32_t spt[16][2];          // nibble -> 4 fp16 +-1
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  if (tid < 32) {
-    const int which = tid >> 3, m = tid & 7;   // 0: key lo, 1: key hi, 2: value lo, 3: value hi
-    const float c = which < 2 ? p.cent_k[(which & 1) * 8 + m] : p.cent_v[(which & 1) * 8 + m];
-    const _Float16 h = (_Float16)c;
-    tab[which * 16 + m] = h;
-    tab[which * 16 + 8 + m] = (_Float16)(c - (float)h);
+  {  // centroid-pair tables (every pattern slot written; unused widths stay finite) and signs
+    const int nbits[4] = {p.kblo, p.kbhi, p.vblo, p.vbhi};
+    for (int i = tid; i < 4 * kPfPat; i += kPfThreads) {
+      const int tb = i / kPfPat, P = i % kPfPat;
+      const int mask = (1 << nbits[tb]) - 1;
+      const int p0 = P & 15, p1 = (P >> 4) & 15, p2 = (P >> 8) & 15;
+      const int ilo = ((p0 & 1) | ((p1 & 1) << 1) | ((p2 & 1) << 2)) & mask;
+      const int ihi = (((p0 >> 1) & 1) | (((p1 >> 1) & 1) << 1) | (((p2 >> 1) & 1) << 2)) & mask;
+      const float* ct = tb < 2 ? p.cent_k + 8 * tb : p.cent_v + 8 * (tb - 2);
+      const float c0 = ct[ilo] * kPfCent, c1 = ct[ihi] * kPfCent;
+      const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+      const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
+      cpt[tb][2 * P] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      cpt[tb][2 * P + 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    if (tid < 32) {
+      const int n = tid >> 1, d = tid & 1;
+      const uint32_t lo = ((n >> (2 * d)) & 1) ? 0x3C00u : 0xBC00u;
+      const uint32_t hi = ((n >> (2 * d + 1)) & 1) ? 0x3C00u : 0xBC00u;
+      spt[n][d] = lo | (hi << 16);
+    }
+    if (!p.vq)  // MSE-only values: the sign operands stay zero
+      for (int i = tid; i < kD * kVtStride / 2; i += kPfThreads) reinterpret_cast<uint32_t*>(Vs)[i] = 0u;
   }
   const int64_t rows_kvh = (int64_t)p.n_new * p.group;
   const int kvh = blockIdx.y, split = blockIdx.z;
@@ -207,50 +217,88 @@ __global__ __launch_bounds__(kPfThreads) void prefill_scan(PrefillParams p) {
     oq[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   float m_run = -INFINITY, l_run = 0.0f;
+  // ---- register prefetch of one tile's records.  Keys: thread (key = lane, block = wave);
+  // values: thread (keys 2 kp, 2 kp + 1 with kp = lane & 31, block = wave, bytes 2 bh,
+  // 2 bh + 1 with bh = lane >> 5); wave 0 also takes the norms (lane = token).
+  const int b = wave, kp = lane & 31, bh = lane >> 5;
+  const bool klo = b < p.ksb, vlo = b < p.vsb;
+  const int knb = klo ? p.kblo : p.kbhi, vnb = vlo ? p.vblo : p.vbhi;
+  const int koff = klo ? b * (p.kblo + 1) : p.ksb * (p.kblo + 1) + (b - p.ksb) * (p.kbhi + 1);
+  const int voff = vlo ? b * (p.vblo + p.vq) : p.vsb * (p.vblo + p.vq) + (b - p.vsb) * (p.vbhi + p.vq);
+  const char* kcp = reinterpret_cast<const char*>(cpt[klo ? 0 : 1]);
+  const char* vcp = reinterpret_cast<const char*>(cpt[vlo ? 2 : 3]);
+  uint32_t kwr[4] = {0u, 0u, 0u, 0u}, vwr[2][4] = {}, nkr = 0, nvr = 0;
+  auto block_words = [](const uint32_t* rec, int nb, int qj, uint32_t (&w)[4]) {
+    w[0] = rec[0];
+    w[1] = nb >= 2 ? rec[1] : 0u;
+    w[2] = nb >= 3 ? rec[2] : 0u;
+    w[3] = qj ? rec[nb] : 0u;
+  };
+  auto fetch = [&](int64_t tt0) {
+    if (tt0 >= t_hi) return;
+    const int32_t pg = p.block_table[tt0 >> p.page_log2];
+    const bool pok = pg >= 0 && (int64_t)pg < p.num_pages;
+    const int64_t base = (((int64_t)(pok ? pg : 0) * p.hkv + kvh) << p.page_log2) + (tt0 & ((1ll << p.page_log2) - 1));
+    const bool kok = pok && tt0 + lane < total;
+    if (kok) block_words(p.codes_k + (base + lane) * p.kw + koff, knb, 1, kwr);
+    else kwr[0] = kwr[1] = kwr[2] = kwr[3] = 0u;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (pok && tt0 + 2 * kp + u < total) block_words(p.codes_v + (base + 2 * kp + u) * p.vw + voff, vnb, p.vq, vwr[u]);
+      else vwr[u][0] = vwr[u][1] = vwr[u][2] = vwr[u][3] = 0u;
+    }
+    if (wave == 0) {
+      nkr = kok ? p.norms_k[base + lane] : 0u;
+      nvr = kok ? p.norms_v[base + lane] : 0u;
+    }
+  };
+  fetch(t_lo);
   for (int64_t t0 = t_lo; t0 < t_hi; t0 += kPfKeys) {
     __syncthreads();  // the previous tile is consumed
-    {  // dequantize: thread = (key lane, block = wave); absent keys become zeros
-      const int64_t t = t0 + lane;
-      const int b = wave;
-      bool ok = t < total;
-      int64_t row = 0;
-      if (ok) {
-        const int32_t pg = p.block_table[t0 >> p.page_log2];
-        ok = pg >= 0 && (int64_t)pg < p.num_pages;
-        row = (((int64_t)pg * p.hkv + kvh) << p.page_log2) + (t & ((1ll << p.page_log2) - 1));
-      }
-      BlockBits kbits{}, vbits{};
-      kbits.ct = tab;
-      vbits.ct = tab + 32;
-      if (ok) {
-        kbits = block_bits(p.codes_k + row * p.kw, b, p.ksb, p.kblo, p.kbhi, 1, tab);
-        vbits = block_bits(p.codes_v + row * p.vw, b, p.vsb, p.vblo, p.vbhi, p.vq, tab + 32);
-      }
-      if (b == 0) {  // norms of the tile's keys and values (zero for absent keys)
-        const uint32_t nk = ok ? p.norms_k[row] : 0u, nv = ok ? p.norms_v[row] : 0u;
-        knorm[0][lane] = f16_bits_to_f32(nk & 0xFFFFu);
-        knorm[1][lane] = f16_bits_to_f32(nk >> 16);
-        vnorm[0][lane] = f16_bits_to_f32(nv & 0xFFFFu);
-        vnorm[1][lane] = f16_bits_to_f32(nv >> 16);
+    {  // dequantize into LDS: key rows [key][coord] and value columns [coord][key]
+      if (wave == 0) {
+        knorm[0][lane] = f16_bits_to_f32(nkr & 0xFFFFu) * (1.0f / kPfCent);
+        knorm[1][lane] = f16_bits_to_f32(nkr >> 16);
+        vnorm[0][lane] = f16_bits_to_f32(nvr & 0xFFFFu);
+        vnorm[1][lane] = f16_bits_to_f32(nvr >> 16);
       }
       const int ko = lane * kKcStride + 32 * b;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        h16x8 ch, cl, sv;
-        dequant8(kbits, q, ch, cl, sv);
-        *reinterpret_cast<h16x8*>(Kh + ko + 8 * q) = ch;
-        *reinterpret_cast<h16x8*>(Kl + ko + 8 * q) = cl;
-        *reinterpret_cast<h16x8*>(Ks + ko + 8 * q) = sv;
-        dequant8(vbits, q, ch, cl, sv);
+        u32x2 e[4];
+        pattern_pairs(kcp, pattern_fields(kwr[0], kwr[1], kwr[2], 8 * q), e);
+        *reinterpret_cast<u32x4*>(Kh + ko + 8 * q) = u32x4{e[0][0], e[1][0], e[2][0], e[3][0]};
+        *reinterpret_cast<u32x4*>(Kl + ko + 8 * q) = u32x4{e[0][1], e[1][1], e[2][1], e[3][1]};
+        const u32x2 s0 = *reinterpret_cast<const u32x2*>(&spt[__builtin_amdgcn_ubfe(kwr[3], 8 * q, 4)][0]);
+        const u32x2 s1 = *reinterpret_cast<const u32x2*>(&spt[__builtin_amdgcn_ubfe(kwr[3], 8 * q + 4, 4)][0]);
+        *reinterpret_cast<u32x4*>(Ks + ko + 8 * q) = u32x4{s0[0], s0[1], s1[0], s1[1]};
+      }
+      uint32_t* vh = reinterpret_cast<uint32_t*>(Vh);
+      uint32_t* vl = reinterpret_cast<uint32_t*>(Vl);
+      uint32_t* vs = reinterpret_cast<uint32_t*>(Vs);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int vo = (32 * b + 8 * q + e) * kVtStride + lane;
-          Vh[vo] = ch[e];
-          Vl[vo] = cl[e];
-          Vs[vo] = sv[e];
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = 2 * bh + qq;
+        u32x2 ea[4], eb[4];
+        pattern_pairs(vcp, pattern_fields(vwr[0][0], vwr[0][1], vwr[0][2], 8 * q), ea);
+        pattern_pairs(vcp, pattern_fields(vwr[1][0], vwr[1][1], vwr[1][2], 8 * q), eb);
+        const uint32_t sx = __builtin_amdgcn_ubfe(vwr[0][3], 8 * q, 8) | (__builtin_amdgcn_ubfe(vwr[1][3], 8 * q, 8) << 16);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int c = 32 * b + 8 * q + 2 * d;  // coordinates c, c + 1; keys 2 kp, 2 kp + 1
+          const int o0 = (c * kVtStride) / 2 + kp, o1 = ((c + 1) * kVtStride) / 2 + kp;
+          vh[o0] = __builtin_amdgcn_perm(eb[d][0], ea[d][0], 0x05040100u);
+          vh[o1] = __builtin_amdgcn_perm(eb[d][0], ea[d][0], 0x07060302u);
+          vl[o0] = __builtin_amdgcn_perm(eb[d][1], ea[d][1], 0x05040100u);
+          vl[o1] = __builtin_amdgcn_perm(eb[d][1], ea[d][1], 0x07060302u);
+          if (p.vq) {
+            vs[o0] = ((sx << (15 - 2 * d)) & 0x80008000u) ^ 0xBC00BC00u;
+            vs[o1] = ((sx << (14 - 2 * d)) & 0x80008000u) ^ 0xBC00BC00u;
+          }
         }
       }
     }
+    fetch(t0 + kPfKeys);
     __syncthreads();
     // ---- logits, transposed: lg[kb][r] = key kb*16 + 4 (lane >> 4) + r, row lane & 15
     float lg[4][4];
@@ -341,7 +389,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_scan(PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int coord = cb * 16 + 4 * (lane >> 4) + r;
-        part[2 + coord] = om[cb][r];
+        part[2 + coord] = om[cb][r] * (1.0f / kPfCent);
         part[2 + kD + coord] = p.gamma * oq[cb][r];
       }
   }
