@@ -281,9 +281,14 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   // ---- register prefetch of one tile: key record, value record, norms
   uint32_t kw[KW], vwr[VW], knr = 0, vnr = 0;
   int64_t prow = -1;  // cache row of the prefetched tile's first token
+  // the cache row of the tile after the prefetched one is looked up a tile ahead, so a
+  // block-table read never sits right before the record loads that depend on it
+  constexpr int64_t kStride = (int64_t)kWaves * kTile;
+  int64_t row_ahead = -1;
   auto fetch = [&](int64_t tt0) {
     const int64_t t = tt0 + lane;
-    prow = tt0 < t_end ? tile_row(tt0) : -1;
+    prow = tt0 < t_end ? row_ahead : -1;
+    row_ahead = tt0 + kStride < t_end ? tile_row(tt0 + kStride) : -1;
     if (prow >= 0 && t < t_end) {
       const int64_t row = prow + lane;
       load_record<KW, KR::VEC>(p.codes_k + row * KW, kw);
@@ -293,6 +298,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     }
   };
   int64_t t0 = t_begin + (int64_t)wave * kTile;
+  if (t0 < t_end) row_ahead = tile_row(t0);
 
   // ---- query tables
   float* qs = lds + L::oArea;             // [2][GC][kD]: q_rot, S q_rot (setup scratch)
@@ -498,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     for (int i = 0; i < VW; ++i) vrec[i] = vwr[i];
     // norms of absent tokens are zeroed so a stale value never meets a zero weight
     const uint32_t kn = valid ? knr : 0u, vn = valid ? vnr : 0u;
-    fetch(t0 + (int64_t)kWaves * kTile);
+    fetch(t0 + kStride);
     // ---------------- keys: lane = token
     float mse[GC], qjl[GC];
 #pragma unroll
