@@ -246,6 +246,24 @@ def test_prefill_writes_the_chunk_and_attends_causally(torch_gpu, start, n_new):
         assert np.max(np.abs(out[i] - o[0])) <= OUT_ATOL, (i, np.max(np.abs(out[i] - o[0])))
 
 
+@pytest.mark.parametrize("fk,fv,hq,hkv,page,start,n_new", [
+    ((128, 3, 2, 64), (128, 2, 1, 64), 8, 4, 128, 200, 45),           # 3.5 / 2.5 bit, GQA 2
+    ((128, 3, 3, 128), (128, 3, 3, 128, False), 4, 4, 64, 70, 60),   # MSE-only values, MHA
+    ((128, 2, 2, 128), (128, 3, 2, 32), 16, 2, 256, 5, 67),          # GQA 8, 3.25-bit values
+])
+def test_prefill_formats_and_groups(torch_gpu, fk, fv, hq, hkv, page, start, n_new):
+    """Prefill over mixed bit widths, MSE-only values and group sizes 1, 2 and 8: query i
+    of the chunk gets the oracle's attention over tokens 0 .. start + i."""
+    out, _, _, _, rk, nk, rv, nv, qb, signs, S = _prefill_case(torch_gpu, start, n_new, 7700 + start,
+                                                               page=page, hq=hq, hkv=hkv, fk=fk, fv=fv)
+    q64 = TI.bf16_to_f64(qb)
+    for i in range(n_new):
+        L = start + i + 1
+        o, _, _, _, _ = oracle_decode(q64[i:i + 1], rk[:, :, :L], nk[:, :, :L], rv[:, :, :L], nv[:, :, :L],
+                                      [L], O.Format(*fk), O.Format(*fv), signs, S, signs, S, 1 / math.sqrt(128))
+        assert np.max(np.abs(out[i] - o[0])) <= OUT_ATOL, (i, np.max(np.abs(out[i] - o[0])))
+
+
 def test_prefill_rejects_a_chunk_past_the_pages_and_writes_nothing(torch_gpu):
     torch = torch_gpu
     import compressed_attention_rotate_amd as tq
