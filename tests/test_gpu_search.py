@@ -84,6 +84,21 @@ def test_search_matches_oracle_estimator(torch_gpu, n_db, n_q, k, bits):
     print(f"\nn_db={n_db} n_q={n_q} k={k} b={bits + 1}: recall@{k} vs exact {O.recall_at_k(ids, exact):.3f}")
 
 
+@pytest.mark.parametrize("n_db,n_q,k,bits,d_in", [(4100, 45, 10, 3, 128), (2500, 33, 5, 2, 100),
+                                                  (3000, 20, 16, 1, 128)])
+def test_search_d128(torch_gpu, n_db, n_q, k, bits, d_in):
+    """d = 128 databases (1, 2 and 3 codebook bits), queries of d_in <= 128 coordinates."""
+    d = 128
+    db = TI.search_set(n_db, d_in, seed=5101)
+    qs = TI.search_set(n_q, d_in, seed=5102)
+    signs, S = TI.rotation(d, 5600)
+    fmt = O.Format.uniform(d, bits)
+    qz = oracle_quantize(db, fmt, signs, S)
+    ids, sc = _gpu_search(torch_gpu, qs, qz["records"], qz["norms"], (d, bits, bits, d), signs, S, k)
+    s_o, scale = _oracle_scores(qs, qz["records"], qz["norms"], fmt, signs, S)
+    _check_topk(ids, sc, s_o, RTOL * (np.abs(s_o) + scale), k)
+
+
 def test_full_size_search_sampled(torch_gpu):
     """10^6 x 200 database (unit-normalized, std i^-0.3), 10^4 queries, b = 4, top-10: the
     database is quantized and searched on the GPU; for sampled queries the oracle re-derives
