@@ -256,6 +256,32 @@ def _requant_timing(tq, torch, dev, codes_k, norms_k, fmt, tab, signs, S, steps,
             "stored_gbs": round(stored / t / 1e9, 2)}
 
 
+def _graph_decode_timing(torch, decode, reps=5):
+    """The decode step of every cache slot captured once into a HIP graph and replayed: the
+    per-step time without host launch overhead (the same kernels, caches and order as the
+    timed eager steps)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s in range(SLOTS):
+            decode(s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(SLOTS):
+            decode(s)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) * 1e-3 / (reps * SLOTS)
+
+
 def _search_timing(tq, torch, dev, TI, reps=2):
     """Inner-product search on the 10^6 x 200 database (unit vectors, std i^-0.3 per
     coordinate), zero-padded to d = 256 and packed at b = 4; 10^4 queries from the same law,
@@ -419,6 +445,7 @@ def main():
                    "global_batch": BATCH, "seq_len": NTOK, "parallelism": "none (1 GPU)"},
         "decode_pct_hbm_peak": round(100.0 * decode_gbs / HBM_PEAK_GBS, 2),
         "decode_us": round(float(dc.mean()) * 1e6, 3),
+        "decode_us_graph_replay": round(_graph_decode_timing(torch, decode) * 1e6, 3),
         "quantize_tokens_per_s": round(qtoks, 1),
         "quantize_us_per_launch": round(q_launch * 1e6, 3),
         "roofline": {"bound": "mfma", "kernel": "quantize_kernel<128,3,3>",
