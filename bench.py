@@ -53,6 +53,9 @@ def _parse():
     ap.add_argument("--search-only", action="store_true",
                     help="only time the inner-product search on the 10^6 x 200 database "
                          "(the search_1m_x_200 variant) and print its JSON (profiling runs)")
+    ap.add_argument("--sparse-v-long", action="store_true",
+                    help="only time the Sparse-V gate at long context (1 x 131072 tokens, 1%% "
+                         "spiked keys, K b=4, V b=3) gated against ungated, and print its JSON")
     return ap.parse_args()
 
 
@@ -282,6 +285,71 @@ def _graph_decode_timing(torch, decode, reps=5):
     return ev[0].elapsed_time(ev[1]) * 1e-3 / (reps * SLOTS)
 
 
+def _sparse_v_timing(tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq, ws, out, fmt_k,
+                     tab_k, fmt_v, tab_v, steps, tau=1e-4):
+    """Decode with the Sparse-V gate (tau = 1e-4) against the same decode ungated, on the same
+    packed caches: the two run interleaved (cache slots rotating), each launch bracketed by
+    HIP events on the launch stream.  skipped_frac = value rows (per KV head and token) the
+    gate left unread over all rows, counted by the kernel on one gated pass per slot."""
+    nslot = len(codes_k)
+    batch, hkv, ntok = codes_k[0].shape[:3]
+    dec = lambda s, t, sk=None: tq.attend_decode(q, codes_k[s], norms_k[s], codes_v[s], norms_v[s],
+                                                 seq, fmt_k, tab_k, fmt_v, tab_v, tau=t,
+                                                 skipped=sk, workspace=ws, out=out)
+    sk = torch.zeros(1, dtype=torch.int64, device=dev)
+    for s in range(nslot):
+        dec(s, 0.0); dec(s, tau, sk)
+    torch.cuda.synchronize()
+    skipped = int(sk.item())
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(); dec(i % nslot, 0.0); e[1].record(); dec(i % nslot, tau); e[2].record()
+    torch.cuda.synchronize()
+    t_u = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_g = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    rk, rv = fmt_k.record_bytes(), fmt_v.record_bytes()
+    rows = batch * hkv * ntok
+    return {"tau": tau, "decode_us_ungated": round(t_u * 1e6, 3),
+            "decode_us_gated": round(t_g * 1e6, 3),
+            "speedup": round(t_u / t_g, 4),
+            "skipped_frac": round(skipped / (rows * nslot), 4),
+            "packed_gbs_ungated": round(rows * (rk + rv + 8) / t_u / 1e9, 2)}
+
+
+def _sparse_v_long(tq, torch, dev, TI, steps, ntok=131072):
+    """Long-context gate timing: one sequence of 131072 tokens of the Llama-3.1-8B layer with
+    1% of token positions carrying x10 keys, K at b = 4 (3-bit codebook + QJL), V at b = 3
+    (2-bit codebook + QJL), quantized on the GPU into two cache slots (token order rotated in
+    the second), then decoded gated and ungated."""
+    seed = TI.data_seed(4)
+    kb, vb, _ = TI.kv_layer(1, HKV, ntok, D, seed=seed, spike_frac=0.01)
+    qb = TI.decode_queries(1, HQ, D, seed)
+    signs, S = TI.rotation(D, TI.rotation_seed(4))
+    fk, fv = tq.Format.uniform(D, 3), tq.Format.uniform(D, 2)
+    Sd = torch.from_numpy(S).to(dev)
+    tk, tv = tq.Tables(fk, signs, Sd), tq.Tables(fv, signs, Sd)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    k0, v0 = bf(kb), bf(vb)
+    del kb, vb
+    ck, nk, cv, nv = [], [], [], []
+    for i in range(2):
+        kk = torch.roll(k0, shifts=4099 * i, dims=2).contiguous().view(-1, D)
+        vv = torch.roll(v0, shifts=4099 * i, dims=2).contiguous().view(-1, D)
+        c, n = tq.quantize_kv(kk, fk, tk)
+        ck.append(c.view(1, HKV, ntok, -1)); nk.append(n.view(1, HKV, ntok, 2))
+        c, n = tq.quantize_kv(vv, fv, tv)
+        cv.append(c.view(1, HKV, ntok, -1)); nv.append(n.view(1, HKV, ntok, 2))
+    q = bf(qb)
+    seq = torch.full((1,), ntok, dtype=torch.int32, device=dev)
+    ws = torch.zeros(tq.attend_workspace_bytes(1, HQ, HKV, ntok, D), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, HQ, D), dtype=torch.float32, device=dev)
+    r = _sparse_v_timing(tq, torch, dev, q, ck, nk, cv, nv, seq, ws, out, fk, tk, fv, tv, steps)
+    r["workload"] = ("1 x 131072 tokens, 32 q / 8 kv heads, head_dim 128, 1% of token positions "
+                     "with x10 keys; K b=4 (3-bit codebook + QJL), V b=3 (2-bit codebook + QJL)")
+    return r
+
+
 def _search_timing(tq, torch, dev, TI, reps=2):
     """Inner-product search on the 10^6 x 200 database (unit vectors, std i^-0.3 per
     coordinate), zero-padded to d = 256 and packed at b = 4; 10^4 queries from the same law,
@@ -346,6 +414,11 @@ def main():
     torch.cuda.set_device(dev)
     if args.search_only:
         print(json.dumps({"search_1m_x_200": _search_timing(tq, torch, dev, TI)}), flush=True)
+        return
+
+    if args.sparse_v_long:
+        print(json.dumps({"sparse_v_128k": _sparse_v_long(tq, torch, dev, TI, args.steps)}),
+              flush=True)
         return
 
     seed = TI.data_seed(2)
@@ -472,6 +545,9 @@ def main():
     line["variants"]["prefill_chunk"] = _prefill_timing(tq, torch, dev, ks, vs, fmt, tab)
     line["variants"]["requantize_b4_to_b3"] = _requant_timing(tq, torch, dev, codes_k, norms_k, fmt,
                                                               tab, signs, S, steps, nvec)
+    line["variants"]["sparse_v_32k_b4"] = _sparse_v_timing(
+        tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq, ws, out, fmt, tab, fmt, tab,
+        steps)
     line["variants"]["search_1m_x_200"] = _search_timing(tq, torch, dev, TI)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(kb, vb, qb, signs, S)

@@ -19,8 +19,8 @@
 //             expansion of the symmetric codebook, c[idx] = sum_S alpha_S prod_{k in S}
 //             (2 b_k - 1) over odd subsets S of the code bit-planes (the planes, and for
 //             3 bits their XOR), the QJL term directly.
-//             Keys: lane = token, records of the wave's next 64-token tile prefetched into
-//             registers.  Online softmax per head with wavefront reductions; the Sparse-V
+//             Keys: lane = token, key records and norms of the wave's next 64-token tile
+//             prefetched into registers; value records are read after the softmax step.  Online softmax per head with wavefront reductions; the Sparse-V
 //             gate (zhidx turboquant_plus article, section "01 turboquant_plus：介绍与详解")
 //             drops a value row for a head when its running weight estimate is below tau,
 //             and skips reading rows dropped by every head.
@@ -278,8 +278,10 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     if (pg < 0 || (int64_t)pg >= p.num_pages) return -1;
     return (((int64_t)pg * p.hkv + (bk % p.hkv)) << p.page_log2) + (tt0 & ((1ll << p.page_log2) - 1));
   };
-  // ---- register prefetch of one tile: key record, value record, norms
-  uint32_t kw[KW], vwr[VW], knr = 0, vnr = 0;
+  // ---- register prefetch of one tile: key record and both norms.  The value record is
+  // read later, once the tile's weights are known (fewer live registers while the keys
+  // are scored, and no read of a row that no head keeps)
+  uint32_t kw[KW], knr = 0, vnr = 0;
   int64_t prow = -1;  // cache row of the prefetched tile's first token
   // the cache row of the tile after the prefetched one is looked up a tile ahead, so a
   // block-table read never sits right before the record loads that depend on it
@@ -292,7 +294,6 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     if (prow >= 0 && t < t_end) {
       const int64_t row = prow + lane;
       load_record<KW, KR::VEC>(p.codes_k + row * KW, kw);
-      if (!gated) load_record<VW, VR::VEC>(p.codes_v + row * VW, vwr);
       knr = p.norms_k[row];
       vnr = p.norms_v[row];
     }
@@ -500,8 +501,6 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     uint32_t w[KW], vrec[VW];
 #pragma unroll
     for (int i = 0; i < KW; ++i) w[i] = kw[i];
-#pragma unroll
-    for (int i = 0; i < VW; ++i) vrec[i] = vwr[i];
     // norms of absent tokens are zeroed so a stale value never meets a zero weight
     const uint32_t kn = valid ? knr : 0u, vn = valid ? vnr : 0u;
     fetch(t0 + kStride);
@@ -563,8 +562,9 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     }
     const uint64_t keep = __ballot(any_keep);
     n_skipped += (unsigned long long)__popcll(__ballot(valid) & ~keep);
-    // this token's weight columns (fp16 hi, lo) and value record (read only when kept if
-    // gated); a row not written keeps finite codes from an earlier tile, met by zero weights
+    // this token's weight columns (fp16 hi, lo) and value record (read only for a token
+    // some head keeps); a row not written keeps codes from an earlier tile (or LDS bits
+    // never written, which still decode to finite table entries), met by zero weights
     {
       constexpr int kWS = L::kWS;
       _Float16* wl = wts + ((lane & 32) | ((lane & 3) << 3) | ((lane >> 2) & 7));
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
         }
       }
       if (any_keep) {
-        if (gated) load_record<VW, VR::VEC>(p.codes_v + (row0 + lane) * VW, vrec);
+        load_record<VW, VR::VEC>(p.codes_v + (row0 + lane) * VW, vrec);
         int own = area_off + lane * kRS;
         asm volatile("" : "+v"(own));
         uint32_t* rv = reinterpret_cast<uint32_t*>(lds + own);
