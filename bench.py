@@ -53,9 +53,10 @@ def _parse():
     ap.add_argument("--search-only", action="store_true",
                     help="only time the inner-product search on the 10^6 x 200 database "
                          "(the search_1m_x_200 variant) and print its JSON (profiling runs)")
-    ap.add_argument("--sparse-v-long", action="store_true",
-                    help="only time the Sparse-V gate at long context (1 x 131072 tokens, 1%% "
-                         "spiked keys, K b=4, V b=3) gated against ungated, and print its JSON")
+    ap.add_argument("--large-batch", action="store_true",
+                    help="only time decode on the two full-size layers larger than the MALL "
+                         "(batch 16 x 32K at 3.5 bits; batch 4 x 128K, gated and ungated) "
+                         "and print their JSON")
     return ap.parse_args()
 
 
@@ -317,37 +318,87 @@ def _sparse_v_timing(tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq,
             "packed_gbs_ungated": round(rows * (rk + rv + 8) / t_u / 1e9, 2)}
 
 
-def _sparse_v_long(tq, torch, dev, TI, steps, ntok=131072):
-    """Long-context gate timing: one sequence of 131072 tokens of the Llama-3.1-8B layer with
-    1% of token positions carrying x10 keys, K at b = 4 (3-bit codebook + QJL), V at b = 3
-    (2-bit codebook + QJL), quantized on the GPU into two cache slots (token order rotated in
-    the second), then decoded gated and ungated."""
-    seed = TI.data_seed(4)
-    kb, vb, _ = TI.kv_layer(1, HKV, ntok, D, seed=seed, spike_frac=0.01)
-    qb = TI.decode_queries(1, HQ, D, seed)
-    signs, S = TI.rotation(D, TI.rotation_seed(4))
-    fk, fv = tq.Format.uniform(D, 3), tq.Format.uniform(D, 2)
+def _large_layer(tq, torch, dev, TI, cfg, batch, ntok, fk, fv, spikes):
+    """One full-size layer of the Llama-3.1-8B law (batch x ntok tokens, 8 KV heads),
+    quantized on the GPU; returns the packed caches, queries and decode buffers."""
+    seed = TI.data_seed(cfg)
+    kb, vb, _ = TI.kv_layer(batch, HKV, ntok, D, seed=seed, spike_frac=spikes)
+    qb = TI.decode_queries(batch, HQ, D, seed)
+    signs, S = TI.rotation(D, TI.rotation_seed(cfg))
     Sd = torch.from_numpy(S).to(dev)
     tk, tv = tq.Tables(fk, signs, Sd), tq.Tables(fv, signs, Sd)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-    k0, v0 = bf(kb), bf(vb)
+    k0, v0 = bf(kb).view(-1, D), bf(vb).view(-1, D)
     del kb, vb
-    ck, nk, cv, nv = [], [], [], []
-    for i in range(2):
-        kk = torch.roll(k0, shifts=4099 * i, dims=2).contiguous().view(-1, D)
-        vv = torch.roll(v0, shifts=4099 * i, dims=2).contiguous().view(-1, D)
-        c, n = tq.quantize_kv(kk, fk, tk)
-        ck.append(c.view(1, HKV, ntok, -1)); nk.append(n.view(1, HKV, ntok, 2))
-        c, n = tq.quantize_kv(vv, fv, tv)
-        cv.append(c.view(1, HKV, ntok, -1)); nv.append(n.view(1, HKV, ntok, 2))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tq.quantize_kv(k0, fk, tk)                       # warm-up
+    ev[0].record()
+    ck, nk = tq.quantize_kv(k0, fk, tk)
+    ev[1].record()
+    cv, nv = tq.quantize_kv(v0, fv, tv)
+    ev[2].record()
+    torch.cuda.synchronize()
+    del k0, v0
+    shp = (batch, HKV, ntok)
+    caches = (ck.view(*shp, -1), nk.view(*shp, 2), cv.view(*shp, -1), nv.view(*shp, 2))
     q = bf(qb)
-    seq = torch.full((1,), ntok, dtype=torch.int32, device=dev)
-    ws = torch.zeros(tq.attend_workspace_bytes(1, HQ, HKV, ntok, D), dtype=torch.uint8, device=dev)
-    out = torch.empty((1, HQ, D), dtype=torch.float32, device=dev)
-    r = _sparse_v_timing(tq, torch, dev, q, ck, nk, cv, nv, seq, ws, out, fk, tk, fv, tv, steps)
-    r["workload"] = ("1 x 131072 tokens, 32 q / 8 kv heads, head_dim 128, 1% of token positions "
-                     "with x10 keys; K b=4 (3-bit codebook + QJL), V b=3 (2-bit codebook + QJL)")
-    return r
+    seq = torch.full((batch,), ntok, dtype=torch.int32, device=dev)
+    ws = torch.zeros(tq.attend_workspace_bytes(batch, HQ, HKV, ntok, D), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((batch, HQ, D), dtype=torch.float32, device=dev)
+    t_q = (ev[0].elapsed_time(ev[1]) + ev[1].elapsed_time(ev[2])) * 1e-3
+    return caches, q, seq, ws, out, tk, tv, t_q
+
+
+def _large_batch(tq, torch, dev, TI, steps):
+    """The two full-size layers beside the 32K batch-1 step, each decoded from one packed
+    cache larger than the MALL: batch 16 x 32768 tokens at 3.5 bits (3-bit codebook on
+    rotated coordinates 0-63, 2-bit on 64-127, + QJL; 60 B per vector with its norms), and
+    batch 4 x 131072 tokens with 1% of token positions carrying x10 keys, K b = 4, V b = 3,
+    decoded gated (tau = 1e-4) and ungated.  For the gated layer the softmax mass of the
+    tokens under tau (from the ungated logits) bounds the mass the gate drops: a dropped
+    token's running weight estimate, which is at least its final weight, was under tau."""
+    res = {}
+    fmt = tq.Format(D, 3, 2, 64)
+    (ck, nk, cv, nv), q, seq, ws, out, tk, tv, t_q = _large_layer(
+        tq, torch, dev, TI, 3, 16, NTOK, fmt, fmt, 0.0)
+    dec = lambda: tq.attend_decode(q, ck, nk, cv, nv, seq, fmt, tk, fmt, tv, workspace=ws, out=out)
+    for _ in range(3):
+        dec()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record(); dec()
+    ev[steps].record()
+    torch.cuda.synchronize()
+    t = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])) * 1e-3
+    nbytes = 2 * ck.shape[0] * HKV * NTOK * (fmt.record_bytes() + 4)
+    res["batch16_32k_b3.5"] = {
+        "workload": "batch 16 x 32768 tokens, 32 q / 8 kv heads, head_dim 128, K and V at 3.5 "
+                    "bits (3/2-bit codebook split at 64 + QJL, 60 B per vector)",
+        "packed_bytes": nbytes, "decode_us": round(t * 1e6, 3),
+        "decode_gbs": round(nbytes / t / 1e9, 2),
+        "decode_pct_hbm_peak": round(100.0 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2),
+        "quantize_tokens_per_s": round(16 * NTOK / t_q, 1)}
+    del ck, nk, cv, nv, ws
+    torch.cuda.empty_cache()
+
+    ntok = 131072
+    fk, fv = tq.Format.uniform(D, 3), tq.Format.uniform(D, 2)
+    (ck, nk, cv, nv), q, seq, ws, out, tk, tv, t_q = _large_layer(
+        tq, torch, dev, TI, 4, 4, ntok, fk, fv, 0.01)
+    r = _sparse_v_timing(tq, torch, dev, q, [ck], [nk], [cv], [nv], seq, ws, out, fk, tk, fv, tv,
+                         steps)
+    _, lg = tq.attend_decode(q, ck, nk, cv, nv, seq, fk, tk, fv, tv, logits=True, workspace=ws)
+    p = torch.softmax(lg.double(), dim=-1)
+    below = torch.where(p < r["tau"], p, torch.zeros_like(p)).sum(dim=-1)
+    r["mass_under_tau_max"] = float(below.max())
+    r["quantize_tokens_per_s"] = round(4 * ntok / t_q, 1)
+    r["workload"] = ("batch 4 x 131072 tokens, 32 q / 8 kv heads, head_dim 128, 1% of token "
+                     "positions with x10 keys; K b=4 (3-bit codebook + QJL), V b=3 (2-bit "
+                     "codebook + QJL)")
+    res["batch4_128k_sparse_v"] = r
+    return res
 
 
 def _search_timing(tq, torch, dev, TI, reps=2):
@@ -416,9 +467,8 @@ def main():
         print(json.dumps({"search_1m_x_200": _search_timing(tq, torch, dev, TI)}), flush=True)
         return
 
-    if args.sparse_v_long:
-        print(json.dumps({"sparse_v_128k": _sparse_v_long(tq, torch, dev, TI, args.steps)}),
-              flush=True)
+    if args.large_batch:
+        print(json.dumps(_large_batch(tq, torch, dev, TI, args.steps)), flush=True)
         return
 
     seed = TI.data_seed(2)
