@@ -98,14 +98,11 @@ __device__ __forceinline__ void load_record(const uint32_t* rec, uint32_t (&w)[W
   }
 }
 
-// Entries of the centroid-pair table of a B-bit codebook.  Four coordinates have
-// code-bit nibbles b0, b1, b2 (one per plane); f = b0 << 1 | b1 << 5 | b2 << 9 holds
-// the 2-bit fields of coordinates (2, 3) at bits 3-4, 7-8, 11-12, so (f & 0x1998) is 8
-// times the sparse pattern P = p0 | p1 << 4 | p2 << 8 of that coordinate pair, and
-// ((f << 2) & 0x1998) the same for coordinates (0, 1).  Entry P (8 bytes) = fp16
-// (hi(c'[lo]), hi(c'[hi])), (lo(c'[lo]), lo(c'[hi])) with c' = 2^6 c and lo = c' - hi.
-__host__ __device__ constexpr int pat_entries(int B) { return B == 3 ? 0x334 : (B == 2 ? 0x34 : 4); }
-constexpr uint32_t kPatMask = 0x1998u;
+// Value centroid-pair tables (one per codebook width): the entry for the 6-bit index
+// x = a0 | b0 << 1 | a1 << 2 | b1 << 3 | a2 << 4 | b2 << 5, where a_k and b_k are the
+// plane-k code bits of two coordinates, is 8 bytes: fp16 (hi(c'[a]), hi(c'[b])) then
+// (lo(c'[a]), lo(c'[b])), with c' = 2^6 c, lo = c' - hi and a, b the two codes.
+constexpr int kPairEntries = 64;
 constexpr float kCentScale = 64.0f;   // value centroids in the operand tables are 2^6 c
 constexpr float kQjlScale = 16.0f;    // QJL value weights in the operands are 2^4 u'
 
@@ -146,8 +143,9 @@ template <int GC, int VW, int BVLO, int BVHI, int VSPLIT>
 struct ScanLds {
   static constexpr int kTq = 16 * 256 * GC;   // [16 byte groups][256][GC]
   static constexpr int kTs = 32 * 16 * GC;    // [32 nibble groups][16][GC]
-  static constexpr int kCpLo = round4(2 * pat_entries(BVLO));
-  static constexpr int kCpHi = VSPLIT < kNB ? round4(2 * pat_entries(BVHI)) : 0;
+  // pair tables at byte 0 and 512: an entry's address is its index times 8, OR the base
+  static constexpr int kCpLo = 2 * kPairEntries;
+  static constexpr int kCpHi = VSPLIT < kNB ? 2 * kPairEntries : 0;
   static constexpr int kRS = round4(VW);                 // value record row stride (words)
   // per wave: 64 value records, then fp16 weight rows [17][kWS]: 0..7 codebook-term
   // columns (u hi for the GC heads, then u lo), 8..15 QJL-term columns, 16 zero; rows
@@ -404,24 +402,19 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   for (int r = 0; r < 16 * 2 * 16 * GC / kThreads; ++r) nibq[tid + r * kThreads] = nibsum_q[r];
 #pragma unroll
   for (int r = 0; r < 32 * 16 * GC / kThreads; ++r) Ts[tid + r * kThreads] = nibsum_s[r];
-  constexpr int kPat = pat_entries(BVLO) + (VSPLIT < kNB ? pat_entries(BVHI) : 0);
-#pragma unroll
-  for (int r = 0; r < (kPat + kThreads - 1) / kThreads; ++r) {
-    const int i = tid + r * kThreads;
-    if (i >= kPat) break;
-    const bool hi = i >= pat_entries(BVLO);
-    const int P = hi ? i - pat_entries(BVLO) : i;
-    const int nb = hi ? BVHI : BVLO;
-    const int mask = (1 << nb) - 1;
-    const int p0 = P & 15, p1 = (P >> 4) & 15, p2 = (P >> 8) & 15;
-    const int ilo = ((p0 & 1) | ((p1 & 1) << 1) | ((p2 & 1) << 2)) & mask;
-    const int ihi = (((p0 >> 1) & 1) | (((p1 >> 1) & 1) << 1) | (((p2 >> 1) & 1) << 2)) & mask;
+  constexpr int kPat = kPairEntries * (VSPLIT < kNB ? 2 : 1);
+  if (tid < kPat) {
+    const bool hi = tid >= kPairEntries;
+    const int x = tid & (kPairEntries - 1);
+    const int mask = (1 << (hi ? BVHI : BVLO)) - 1;
+    const int ia = ((x & 1) | ((x >> 1) & 2) | ((x >> 2) & 4)) & mask;         // bits 0, 2, 4
+    const int ib = (((x >> 1) & 1) | ((x >> 2) & 2) | ((x >> 3) & 4)) & mask;  // bits 1, 3, 5
     uint32_t* dst = reinterpret_cast<uint32_t*>(hi ? cpHi : cpLo);
-    const float c0 = cents[(hi ? 8 : 0) + ilo] * kCentScale, c1 = cents[(hi ? 8 : 0) + ihi] * kCentScale;
+    const float c0 = cents[(hi ? 8 : 0) + ia] * kCentScale, c1 = cents[(hi ? 8 : 0) + ib] * kCentScale;
     const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
     const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
-    dst[2 * P] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    dst[2 * P + 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    dst[2 * x] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    dst[2 * x + 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
   }
   __syncthreads();
   float tq_v[16 * 256 / kThreads][GC];
@@ -469,17 +462,33 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   _Float16* wts = reinterpret_cast<_Float16*>(area + kTile * kRS);
   for (int i = lane; i < L::kWRows * L::kWS / 2; i += 64) area[kTile * kRS + i] = 0.0f;
   // value lane mapping: lane (vq, vr) owns tokens 4 j + vq (j = 0..7) of each 32-token
-  // group, which are k = 8 vq + j of the MFMA, and coordinates 8 vr .. 8 vr + 7 (byte
-  // vr & 3 of the plane words of block vr >> 2); it also supplies weight column vr of the
-  // B operand.  The weight rows hold token 32 g + 4 j + q at position 32 g + 8 q + j, so a
-  // lane's 8 weights are contiguous, and the 4 record rows one read touches are adjacent.
+  // group and reads block vr >> 2 of their records.  The weight rows hold token
+  // 32 g + 4 j + q at position 32 g + 8 q + j, so a lane's 8 weights are contiguous, and
+  // the 4 record rows one read touches are adjacent.
+  // Codebook term: A rows are coordinate pairs and k = (token, coordinate of the pair,
+  // fp16 hi or lo part), so two centroid-pair table entries (hi pair, lo pair) read back
+  // to back are an operand as read.  Product i (one per code byte) gives row vr the pair
+  // 32 (vr >> 2) + 8 i + 2 (vr & 3) + {0, 1}, and 8-token slab s gives lane group vq
+  // tokens j = 2 s, 2 s + 1; output column vr = (c, head, hi/lo) with c = vr & 1 the
+  // coordinate of the pair it sums, head (vr >> 1) & 3, lo weights if vr >= 8.
+  // QJL term: A rows are coordinates 8 vr .. 8 vr + 7 (byte vr & 3 of the sign word, one
+  // product per coordinate), k = the lane group's 8 tokens; column vr = weight column vr.
   const int vq = lane >> 4, vr = lane & 15;
   const int vblk = vr >> 2, vsh = 8 * (vr & 3);
   const bool vlo = vblk < VSPLIT;
   const int vnb = vlo ? BVLO : BVHI;
   const int voff = VR::off(vblk);
-  const char* cpb = reinterpret_cast<const char*>(vlo ? cpLo : cpHi);
-  const int wrow_m = vr < 8 ? vr : 16, wrow_s = vr < 8 ? 8 + vr : 16;
+  const uint32_t cpoff = (uint32_t)((vlo ? L::oCpLo : L::oCpHi) * 4);
+  const uint32_t pm0 = 0x03030303u << (2 * (vr & 3));              // plane-0 bits of the pairs
+  const uint32_t pm1 = __builtin_amdgcn_alignbit(pm0, pm0, 30);    // rotated left by 2
+  const uint32_t prs = 2 * (vr & 3) + 29;  // rotate right by 8 i + prs: pair field at bits 3-8
+  const int vh = (vr >> 1) & 3;
+  const int wrow_m = vh < GC ? (vr >> 3) * GC + vh : 16, wrow_s = vr < 8 ? 8 + vr : 16;
+  const uint32_t psel0 = (vr & 1) ? 0x01000C0Cu : 0x0C0C0100u;  // weight in the half of
+  const uint32_t psel1 = (vr & 1) ? 0x03020C0Cu : 0x0C0C0302u;  // this column's coordinate
+  // the lane's record rows (float index; the token's row offset folds into the reads)
+  int vrow = area_off + vq * kRS + voff;
+  asm volatile("" : "+v"(vrow));
 
   float m_run[GC], l_run[GC];
 #pragma unroll
@@ -487,10 +496,13 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.0f;
   }
-  // accm[e][i], accq[e][i]: coordinate 8 (4 vq + i) + e, weight column vr
-  f32x4 accm[8], accq[8];
+  // accm[i][j]: coordinate 32 vq + 8 i + 2 j + (vr & 1), column vr;
+  // accq[e][j]: coordinate 8 (4 vq + j) + e, weight column vr
+  f32x4 accm[4], accq[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) accm[e] = accq[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e = 0; e < 8; ++e) accq[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) accm[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   unsigned long long n_skipped = 0;
   const float kscale = p.scale * kLog2e;
 
@@ -550,14 +562,18 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
       u[h] = wgt * vn16;
       u2[h] = wgt * (p.gamma * kQjlScale) * vr16;
     }
-    {  // rescale the accumulators: column vr holds head vr % GC
-      float cl = corr[0];
+    {  // rescale the accumulators to the new running maxima
+      float cm = corr[0], cq = corr[0];
 #pragma unroll
-      for (int h = 1; h < GC; ++h) cl = (vr & (GC - 1)) == h ? corr[h] : cl;
+      for (int h = 1; h < GC; ++h) {
+        cm = (vh & (GC - 1)) == h ? corr[h] : cm;
+        cq = (vr & (GC - 1)) == h ? corr[h] : cq;
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        accm[e] *= cl;
-        if constexpr (VQ) accq[e] *= cl;
+      for (int i = 0; i < 4; ++i) accm[i] *= cm;
+      if constexpr (VQ) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accq[e] *= cq;
       }
     }
     const uint64_t keep = __ballot(any_keep);
@@ -593,15 +609,27 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     for (int g = 0; g < 2; ++g) {
       if ((uint32_t)(keep >> (32 * g)) == 0u) continue;  // no kept token in the group
       const int wb = 32 * g + 8 * vq;
-      const h16x8 bm = *reinterpret_cast<const h16x8*>(wts + wrow_m * L::kWS + wb);
       h16x8 bs{};
       if constexpr (VQ) bs = *reinterpret_cast<const h16x8*>(wts + wrow_s * L::kWS + wb);
-      uint32_t f[8][2], sb[8];
+      // codebook-term B operand of slab s: token j = 2 s, 2 s + 1's weight of column vr in
+      // the half of this column's coordinate (0 in the other), once for the entry's hi
+      // dword and once for its lo dword
+      u32x4 bm[4];
+      {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(wts + wrow_m * L::kWS + wb);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const uint32_t d0 = __builtin_amdgcn_perm(w[s2], w[s2], psel0);
+          const uint32_t d1 = __builtin_amdgcn_perm(w[s2], w[s2], psel1);
+          bm[s2] = u32x4{d0, d0, d1, d1};
+        }
+      }
+      // per token: the code bits of the lane's 4 coordinate pairs, plane k rotated left
+      // by 2 k, so the 6-bit table index of pair i sits at bits 8 i + 2 (vr & 3) .. + 5
+      uint32_t pf[8], sb[8];
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        int roff = area_off + (32 * g + 4 * tt + vq) * kRS + voff;
-        asm volatile("" : "+v"(roff));
-        const uint32_t* rw = reinterpret_cast<const uint32_t*>(lds + roff);
+        const uint32_t* rw = reinterpret_cast<const uint32_t*>(lds + vrow + (32 * g + 4 * tt) * kRS);
         uint32_t p0, p1 = 0, p2 = 0, sg = 0;
         if constexpr (VQ && BVLO == 3 && BVHI == 3) {
           const u32x4 x = *reinterpret_cast<const u32x4*>(rw);
@@ -612,48 +640,41 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
           if constexpr (BVLO == 3 || BVHI == 3) p2 = vnb == 3 ? rw[2] : 0u;
           if constexpr (VQ) sg = rw[vnb];
         }
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-          f[tt][n] = (__builtin_amdgcn_ubfe(p0, vsh + 4 * n, 4) << 1) |
-                     (__builtin_amdgcn_ubfe(p1, vsh + 4 * n, 4) << 5) |
-                     (__builtin_amdgcn_ubfe(p2, vsh + 4 * n, 4) << 9);
+        uint32_t t = 0;
+        if constexpr (BVLO >= 2 || BVHI >= 2) {
+          const uint32_t r1 = __builtin_amdgcn_alignbit(p1, p1, 30);
+          t = r1;
+          if constexpr (BVLO == 3 || BVHI == 3) {
+            const uint32_t r2 = __builtin_amdgcn_alignbit(p2, p2, 28);
+            t = r2 ^ ((r1 ^ r2) & pm1);
+          }
+        }
+        pf[tt] = t ^ ((p0 ^ t) & pm0);
         sb[tt] = VQ ? __builtin_amdgcn_ubfe(sg, vsh, 8) : 0u;
       }
 #pragma unroll
-      for (int ep = 0; ep < 4; ++ep) {  // coordinates 2 ep, 2 ep + 1 of the lane's byte
-        u32x2 ent[8];
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          const uint32_t fv = f[tt][ep >> 1];
-          const uint32_t a = (ep & 1) ? (fv & kPatMask) : ((fv << 2) & kPatMask);
-          ent[tt] = *reinterpret_cast<const u32x2*>(cpb + a);
-        }
-        // A operands: dword i = tokens (2 i, 2 i + 1) of one coordinate
-        u32x4 ah0, ah1, al0, al1;
+      for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ah0[i] = __builtin_amdgcn_perm(ent[2 * i + 1][0], ent[2 * i][0], 0x05040100u);
-          ah1[i] = __builtin_amdgcn_perm(ent[2 * i + 1][0], ent[2 * i][0], 0x07060302u);
-          al0[i] = __builtin_amdgcn_perm(ent[2 * i + 1][1], ent[2 * i][1], 0x05040100u);
-          al1[i] = __builtin_amdgcn_perm(ent[2 * i + 1][1], ent[2 * i][1], 0x07060302u);
+          const uint32_t x0 = pf[2 * s2], x1 = pf[2 * s2 + 1];
+          const uint32_t a0 = (__builtin_amdgcn_alignbit(x0, x0, prs + 8 * i) & 0x1F8u) | cpoff;
+          const uint32_t a1 = (__builtin_amdgcn_alignbit(x1, x1, prs + 8 * i) & 0x1F8u) | cpoff;
+          const u32x2 e0 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(lds) + a0);
+          const u32x2 e1 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(lds) + a1);
+          const u32x4 a = u32x4{e0[0], e0[1], e1[0], e1[1]};
+          accm[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, a), __builtin_bit_cast(h16x8, bm[s2]), accm[i], 0, 0, 0);
         }
-        const int e0 = 2 * ep;
-        accm[e0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, ah0), bm, accm[e0], 0, 0, 0);
-        accm[e0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, al0), bm, accm[e0], 0, 0, 0);
-        accm[e0 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, ah1), bm, accm[e0 + 1], 0, 0, 0);
-        accm[e0 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, al1), bm, accm[e0 + 1], 0, 0, 0);
-        if constexpr (VQ) {
+      }
+      if constexpr (VQ) {
 #pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const int e = e0 + d;
-            u32x4 so;
+        for (int e = 0; e < 8; ++e) {
+          u32x4 so;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t x = sb[2 * i] | (sb[2 * i + 1] << 16);
-              so[i] = ((x << (15 - e)) & 0x80008000u) ^ 0xBC00BC00u;  // bit 1 -> +1, 0 -> -1
-            }
-            accq[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, so), bs, accq[e], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t x = sb[2 * j] | (sb[2 * j + 1] << 16);
+            so[j] = ((x << (15 - e)) & 0x80008000u) ^ 0xBC00BC00u;  // bit 1 -> +1, 0 -> -1
           }
+          accq[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, so), bs, accq[e], 0, 0, 0);
         }
       }
     }
@@ -661,12 +682,15 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   // ---------------- workgroup epilogue: the lo-weight columns are folded into the hi
   // ones, then the waves' partials are merged in LDS (aliases Tq) and stored at device scope
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      accm[e][i] += xchg<GC>(accm[e][i]);
-      if constexpr (VQ) accq[e][i] += xchg<GC>(accq[e][i]);
-    }
+    for (int j = 0; j < 4; ++j) accm[i][j] += xchg<8>(accm[i][j]);
+  if constexpr (VQ) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) accq[e][j] += xchg<GC>(accq[e][j]);
+  }
   __syncthreads();
   float* mine = lds + L::oWM + wave * L::kMerge;  // [2*GC] m, l | [GC][2][kD]
   if (lane == 0) {
@@ -676,16 +700,19 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
       mine[GC + h] = l_run[h];
     }
   }
+  if (vr < 8 && vh < GC) {
+    float* a = mine + round4(2 * GC) + vh * 2 * kD + 32 * vq + (vr & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[8 * i + 2 * j] = accm[i][j] * (1.0f / kCentScale);
+  }
   if (vr < GC) {
-    float* a = mine + round4(2 * GC) + vr * 2 * kD;
+    float* a = mine + round4(2 * GC) + vr * 2 * kD + kD;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int coord = 8 * (4 * vq + i) + e;
-        a[coord] = accm[e][i] * (1.0f / kCentScale);
-        a[kD + coord] = VQ ? accq[e][i] * (1.0f / kQjlScale) : 0.0f;
-      }
+      for (int j = 0; j < 4; ++j) a[8 * (4 * vq + j) + e] = VQ ? accq[e][j] * (1.0f / kQjlScale) : 0.0f;
   }
   __syncthreads();
 #pragma unroll
