@@ -547,33 +547,44 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     }
     // ---------------- online softmax (per head, wavefront reductions)
     const float vn16 = f16_bits_to_f32(vn), vr16 = f16_bits_to_f32(vn >> 16);
-    bool any_keep = false;
+    // The running maximum moves only when some lane's logit exceeds it (a wave-uniform
+    // test), so most tiles of a long split skip the max reduction and the rescale.
+    // Ungated, l_run is a per-lane partial sum, reduced once after the scan; gated, the
+    // test against tau needs the wave's running sum every tile.
+    bool any_keep = false, grow = false;
     float u[GC], u2[GC], corr[GC];
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
-      const float mt = wave_max_fast(lg[h]);
-      const float mn = fmaxf(m_run[h], mt);
-      corr[h] = (m_run[h] == -INFINITY) ? 0.0f : exp2f(m_run[h] - mn);
-      float wgt = valid ? exp2f(lg[h] - mn) : 0.0f;
-      l_run[h] = l_run[h] * corr[h] + wave_sum_fast(wgt);
-      m_run[h] = mn;
-      wgt = (gated && wgt < p.tau * l_run[h]) ? 0.0f : wgt;
+      corr[h] = 1.0f;
+      if (__ballot(lg[h] > m_run[h]) != 0u) {
+        const float mn = fmaxf(m_run[h], wave_max_fast(lg[h]));
+        corr[h] = (m_run[h] == -INFINITY) ? 0.0f : exp2f(m_run[h] - mn);
+        m_run[h] = mn;
+        grow = true;
+      }
+      float wgt = valid ? exp2f(lg[h] - m_run[h]) : 0.0f;
+      if (gated) {
+        l_run[h] = l_run[h] * corr[h] + wave_sum_fast(wgt);
+        wgt = wgt < p.tau * l_run[h] ? 0.0f : wgt;
+      } else {
+        l_run[h] = l_run[h] * corr[h] + wgt;
+      }
       any_keep |= wgt > 0.0f;
       u[h] = wgt * vn16;
       u2[h] = wgt * (p.gamma * kQjlScale) * vr16;
     }
-    {  // rescale the accumulators to the new running maxima
-      float cm = corr[0], cq = corr[0];
+    if (grow) {  // rescale the accumulators to the new running maxima
+      float cm = corr[0], cs = corr[0];
 #pragma unroll
       for (int h = 1; h < GC; ++h) {
         cm = (vh & (GC - 1)) == h ? corr[h] : cm;
-        cq = (vr & (GC - 1)) == h ? corr[h] : cq;
+        cs = (vr & (GC - 1)) == h ? corr[h] : cs;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) accm[i] *= cm;
       if constexpr (VQ) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) accq[e] *= cq;
+        for (int e = 0; e < 8; ++e) accq[e] *= cs;
       }
     }
     const uint64_t keep = __ballot(any_keep);
@@ -681,6 +692,10 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   }
   // ---------------- workgroup epilogue: the lo-weight columns are folded into the hi
   // ones, then the waves' partials are merged in LDS (aliases Tq) and stored at device scope
+  if (!gated) {
+#pragma unroll
+    for (int h = 0; h < GC; ++h) l_run[h] = wave_sum_fast(l_run[h]);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
