@@ -260,6 +260,25 @@ def _requant_timing(tq, torch, dev, codes_k, norms_k, fmt, tab, signs, S, steps,
             "stored_gbs": round(stored / t / 1e9, 2)}
 
 
+def _copy_gbs(torch, dev, nbytes=256 << 20, reps=10):
+    """Measured HBM bandwidth of a plain device copy (nbytes read + nbytes written per
+    copy), the practical ceiling the decode rate is also compared with."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+    del src, dst
+    return 2 * nbytes / t / 1e9
+
+
 def _graph_decode_timing(torch, decode, reps=5):
     """The decode step of every cache slot captured once into a HIP graph and replayed: the
     per-step time without host launch overhead (the same kernels, caches and order as the
@@ -543,6 +562,7 @@ def main():
     flops_launch = 2.0 * D * D * nvec                         # S r per vector
     q_tfs = flops_launch / q_launch / 1e12
     qtoks = NTOK * BATCH * steps / (qk.sum() + qv.sum())
+    copy_gbs = _copy_gbs(torch, dev)
     trafq = _traffic(["compressed_attention_rotate_amd/csrc/tq_quantize_kernel.h"],
                      "quantize_llama8b_32k_traffic.txt")
     trafd = _traffic(["compressed_attention_rotate_amd/csrc/tq_decode_kernel.h",
@@ -567,6 +587,8 @@ def main():
                                "log-uniform [0.5, 8]), b=4 (3-bit codebook + 1 QJL bit)",
                    "global_batch": BATCH, "seq_len": NTOK, "parallelism": "none (1 GPU)"},
         "decode_pct_hbm_peak": round(100.0 * decode_gbs / HBM_PEAK_GBS, 2),
+        "hbm_copy_gbs": round(copy_gbs, 1),
+        "decode_pct_copy_bw": round(100.0 * decode_gbs / copy_gbs, 2),
         "decode_us": round(float(dc.mean()) * 1e6, 3),
         "decode_us_graph_replay": round(_graph_decode_timing(torch, decode) * 1e6, 3),
         "quantize_tokens_per_s": round(qtoks, 1),
