@@ -451,12 +451,19 @@ def _search_timing(tq, torch, dev, TI, reps=2):
 
     tb = timed(build)
     ts = timed(search)
+    # unbatched: one query (and one block of 32) streams the whole packed database
+    t1 = timed(lambda: tq.ip_search(qs[:1], codes, norms, fmt, tab, k=k, workspace=ws))
+    t32 = timed(lambda: tq.ip_search(qs[:32], codes, norms, fmt, tab, k=k, workspace=ws))
+    db_bytes = n_db * (fmt.record_bytes() + 4)
     flops = 2.0 * 2 * d * n_db * n_q
     tfs = flops / ts / 1e12
     return {"db_vectors": n_db, "d_in": d_in, "d": d, "queries": n_q, "k": k,
             "format": "3-bit codebook + 1 QJL bit (132 B/vector)",
             "index_build_ms": round(tb * 1e3, 3), "index_vectors_per_s": round(n_db / tb, 1),
             "search_ms": round(ts * 1e3, 3), "queries_per_s": round(n_q / ts, 1),
+            "one_query_us": round(t1 * 1e6, 2), "one_query_db_gbs": round(db_bytes / t1 / 1e9, 1),
+            "one_query_pct_hbm_peak": round(100.0 * db_bytes / t1 / 1e9 / HBM_PEAK_GBS, 2),
+            "queries_32_us": round(t32 * 1e6, 2), "queries_32_per_s": round(32 / t32, 1),
             "roofline": {"bound": "mfma", "kernel": "search_scan", "achieved": round(tfs, 3),
                          "peak": FP16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(tfs / FP16_MFMA_PEAK_TFS, 4), "traffic": None}}

@@ -399,17 +399,50 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
 }
 
 // ----------------------------------------------------------------------------- merge
-__global__ __launch_bounds__(64) void search_merge(SearchParams p) {
+// One workgroup of kMWaves waves per query.  Wave w screens a contiguous quarter of the
+// query's n_split * k split candidates, 64 at a time (one per lane): a ballot against its
+// list's current k-th entry, then the survivors are inserted in lane order.  Wave 0 then
+// inserts the other waves' lists.  (score, id) is a total order, so the result does not
+// depend on the order of the inserts.
+constexpr int kMWaves = 4;
+__global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
   const int64_t qi = blockIdx.x;
-  const int lane = lane_id(), k = p.k;
+  const int lane = lane_id(), wave = threadIdx.x >> 6, k = p.k;
+  __shared__ float xs[kMWaves][64];
+  __shared__ int64_t xi[kMWaves][64];
+  const int64_t total = (int64_t)p.n_split * k;
+  const int64_t per = (total + kMWaves - 1) / kMWaves;
+  const int64_t c0 = wave * per;
+  const int64_t c1 = c0 + per < total ? c0 + per : total;
+  const float* cs = p.ws_cand_s + qi * total;
+  const int64_t* ci = p.ws_cand_i + qi * total;
   float ms = -INFINITY;
   int64_t mi = INT64_MAX;
-  for (int s = 0; s < p.n_split; ++s)
-    for (int i = 0; i < k; ++i) {
-      const float sc = p.ws_cand_s[(qi * p.n_split + s) * k + i];
-      const int64_t id = p.ws_cand_i[(qi * p.n_split + s) * k + i];
-      if (better(sc, id, __shfl(ms, k - 1, 64), __shfl(mi, k - 1, 64))) list_insert(ms, mi, sc, id, k);
+  for (int64_t c = c0; c < c1; c += 64) {
+    const bool ok = c + lane < c1;
+    const float sc = ok ? cs[c + lane] : -INFINITY;
+    const int64_t id = ok ? ci[c + lane] : INT64_MAX;
+    uint64_t cand = __ballot(ok && better(sc, id, __shfl(ms, k - 1, 64), __shfl(mi, k - 1, 64)));
+    while (cand) {
+      const int L = __builtin_ctzll(cand);
+      cand &= cand - 1;
+      list_insert(ms, mi, __shfl(sc, L, 64), __shfl(id, L, 64), k);
     }
+  }
+  xs[wave][lane] = ms;
+  xi[wave][lane] = mi;
+  __syncthreads();
+  if (wave != 0) return;
+  for (int w = 1; w < kMWaves; ++w) {
+    const float sc = xs[w][lane];
+    const int64_t id = xi[w][lane];
+    uint64_t cand = __ballot(lane < k && better(sc, id, __shfl(ms, k - 1, 64), __shfl(mi, k - 1, 64)));
+    while (cand) {
+      const int L = __builtin_ctzll(cand);
+      cand &= cand - 1;
+      list_insert(ms, mi, __shfl(sc, L, 64), __shfl(id, L, 64), k);
+    }
+  }
   if (lane < k) {
     p.out_scores[qi * k + lane] = ms;
     p.out_ids[qi * k + lane] = mi;
@@ -424,7 +457,7 @@ static int launch_search(const SearchParams& p, int64_t n_blocks, hipStream_t st
                      dim3(64 * kSWaves), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   if (p.n_split > 1) {
-    hipLaunchKernelGGL(search_merge, dim3((unsigned)p.n_q), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(search_merge, dim3((unsigned)p.n_q), dim3(64 * kMWaves), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   }
   return TQ_OK;

@@ -84,6 +84,28 @@ def test_search_matches_oracle_estimator(torch_gpu, n_db, n_q, k, bits):
     print(f"\nn_db={n_db} n_q={n_q} k={k} b={bits + 1}: recall@{k} vs exact {O.recall_at_k(ids, exact):.3f}")
 
 
+@pytest.fixture(scope="module")
+def db_60k():
+    """60000 vectors of the search law (200 coordinates, zero-padded to 256), packed at b = 4
+    by the oracle."""
+    d_in, d = 200, 256
+    db = TI.search_set(60000, d_in, seed=5201)
+    signs, S = TI.rotation(d, 5700)
+    fmt = O.Format.uniform(d, 3)
+    return db, signs, S, fmt, oracle_quantize(db, fmt, signs, S)
+
+
+@pytest.mark.parametrize("n_q,k", [(1, 64), (2, 10), (33, 64)])
+def test_search_few_queries_many_splits(torch_gpu, db_60k, n_q, k):
+    """Few queries over 60000 vectors: one or two query blocks, so the database is cut into
+    58 splits and the merge combines up to 58 x 64 candidates per query."""
+    db, signs, S, fmt, qz = db_60k
+    qs = TI.search_set(n_q, db.shape[1], seed=5202)
+    ids, sc = _gpu_search(torch_gpu, qs, qz["records"], qz["norms"], (fmt.d, 3, 3, fmt.d), signs, S, k)
+    s_o, scale = _oracle_scores(qs, qz["records"], qz["norms"], fmt, signs, S)
+    _check_topk(ids, sc, s_o, RTOL * (np.abs(s_o) + scale), k)
+
+
 @pytest.mark.parametrize("n_db,n_q,k,bits,d_in", [(4100, 45, 10, 3, 128), (2500, 33, 5, 2, 100),
                                                   (3000, 20, 16, 1, 128)])
 def test_search_d128(torch_gpu, n_db, n_q, k, bits, d_in):
