@@ -87,25 +87,6 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   }
 }
 
-// Walsh coefficients alpha_S = 2^-B sum_idx c[idx] prod_{k in S} (2 b_k(idx) - 1) for the odd
-// subsets S in the order the scan reads the planes: {0}, {1}, {2}, {0,1,2}.
-static void walsh(int bits, const float* c, float* alpha) {
-  const int L = 1 << bits;
-  const int subsets[4] = {1, 2, 4, 7};
-  for (int k = 0; k < 4; ++k) alpha[k] = 0.0f;
-  const int nw = bits == 3 ? 4 : bits;
-  for (int k = 0; k < nw; ++k) {
-    double s = 0.0;
-    for (int idx = 0; idx < L; ++idx) {
-      double prod = 1.0;
-      for (int bit = 0; bit < bits; ++bit)
-        if ((subsets[k] >> bit) & 1) prod *= ((idx >> bit) & 1) ? 1.0 : -1.0;
-      s += (double)c[idx] * prod;
-    }
-    alpha[k] = (float)(s / L);
-  }
-}
-
 }  // namespace tqk
 
 // ---------------------------------------------------------------------------------------
@@ -212,8 +193,8 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
     if (tk->signs[j] < 0) p.sign_k[j >> 5] |= 1u << (j & 31);
     if (tv->signs[j] < 0) p.sign_v[j >> 5] |= 1u << (j & 31);
   }
-  walsh(fk->bits_lo, tk->centroids_lo, p.alpha_k[0]);
-  walsh(fk->bits_hi, tk->centroids_hi, p.alpha_k[1]);
+  tq_walsh_coeffs(fk->bits_lo, tk->centroids_lo, p.alpha_k[0]);
+  tq_walsh_coeffs(fk->bits_hi, tk->centroids_hi, p.alpha_k[1]);
   for (int i = 0; i < 8; ++i) {
     p.cent_v[0][i] = i < (1 << fv->bits_lo) ? tv->centroids_lo[i] : 0.0f;
     p.cent_v[1][i] = i < (1 << fv->bits_hi) ? tv->centroids_hi[i] : 0.0f;

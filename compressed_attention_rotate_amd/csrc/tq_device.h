@@ -162,4 +162,49 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t i, int dtyp
   return f16_bits_to_f32(h);                       // fp16
 }
 
+// ---------------------------------------------------------------------------------------
+// Subset-sum table reads (decode key scan, few-query search): entry idx of a table with one
+// float per head (GC heads side by side).
+typedef float tq_f32x4 __attribute__((ext_vector_type(4)));
+typedef float tq_f32x2 __attribute__((ext_vector_type(2)));
+
+template <int GC>
+__device__ __forceinline__ void table_read(const float* T, int idx, float (&out)[GC]) {
+  if constexpr (GC == 4) {
+    const tq_f32x4 v = *reinterpret_cast<const tq_f32x4*>(T + 4 * idx);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  } else if constexpr (GC == 2) {
+    const tq_f32x2 v = *reinterpret_cast<const tq_f32x2*>(T + 2 * idx);
+    out[0] = v[0]; out[1] = v[1];
+  } else {
+    out[0] = T[idx];
+  }
+}
+
+// acc += alpha * (byte-table reads of one 32-bit plane word, byte groups g0 .. g0+3); the
+// four reads are summed pairwise first so every read is consumed right away.
+template <int GC>
+__device__ __forceinline__ void lut_byte(const float* Tq, int g0, uint32_t w, float alpha,
+                                         float (&acc)[GC]) {
+  float t0[GC], t1[GC], t2[GC], t3[GC];
+  table_read<GC>(Tq, (g0 + 0) * 256 + (w & 0xFFu), t0);
+  table_read<GC>(Tq, (g0 + 1) * 256 + ((w >> 8) & 0xFFu), t1);
+  table_read<GC>(Tq, (g0 + 2) * 256 + ((w >> 16) & 0xFFu), t2);
+  table_read<GC>(Tq, (g0 + 3) * 256 + (w >> 24), t3);
+#pragma unroll
+  for (int h = 0; h < GC; ++h) acc[h] = fmaf(alpha, (t0[h] + t1[h]) + (t2[h] + t3[h]), acc[h]);
+}
+
+// acc += nibble-table reads of one 32-bit sign word (nibble groups g0 .. g0+7), summed as
+// a tree.
+template <int GC>
+__device__ __forceinline__ void lut_nib(const float* Ts, int g0, uint32_t w, float (&acc)[GC]) {
+  float t[8][GC];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) table_read<GC>(Ts, (g0 + i) * 16 + ((w >> (4 * i)) & 0xFu), t[i]);
+#pragma unroll
+  for (int h = 0; h < GC; ++h)
+    acc[h] += ((t[0][h] + t[1][h]) + (t[2][h] + t[3][h])) + ((t[4][h] + t[5][h]) + (t[6][h] + t[7][h]));
+}
+
 }  // namespace tqk

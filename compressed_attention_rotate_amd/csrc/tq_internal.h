@@ -90,3 +90,22 @@ int tq_launch_prefill(const tq_format* fk, const tq_tables* tk, const tq_format*
                       int64_t num_pages, const int32_t* block_table, int32_t max_blocks,
                       int64_t start, float scale, float* out, void* workspace,
                       const tq_prefill_plan& pl, hipStream_t stream);
+
+// Walsh coefficients alpha_S = 2^-B sum_idx c[idx] prod_{k in S} (2 b_k(idx) - 1) for the odd
+// subsets S in the order the scan reads the planes: {0}, {1}, {2}, {0,1,2}.
+inline void tq_walsh_coeffs(int bits, const float* c, float* alpha) {
+  const int L = 1 << bits;
+  const int subsets[4] = {1, 2, 4, 7};
+  for (int k = 0; k < 4; ++k) alpha[k] = 0.0f;
+  const int nw = bits == 3 ? 4 : bits;
+  for (int k = 0; k < nw; ++k) {
+    double s = 0.0;
+    for (int idx = 0; idx < L; ++idx) {
+      double prod = 1.0;
+      for (int bit = 0; bit < bits; ++bit)
+        if ((subsets[k] >> bit) & 1) prod *= ((idx >> bit) & 1) ? 1.0 : -1.0;
+      s += (double)c[idx] * prod;
+    }
+    alpha[k] = (float)(s / L);
+  }
+}

@@ -69,6 +69,7 @@ struct SearchParams {
   float gamma;
   uint32_t sign_mask[8];
   float cent[8];     // codebook, ascending
+  float alpha[4];    // Walsh coefficients of the codebook (few-query scan)
 };
 
 // ----------------------------------------------------------------------------- prologue
@@ -399,41 +400,57 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
 }
 
 // ----------------------------------------------------------------------------- merge
-// One workgroup of kMWaves waves per query.  Wave w screens a contiguous quarter of the
-// query's n_split * k split candidates, 64 at a time (one per lane): a ballot against its
-// list's current k-th entry, then the survivors are inserted in lane order.  Wave 0 then
-// inserts the other waves' lists.  (score, id) is a total order, so the result does not
-// depend on the order of the inserts.
-constexpr int kMWaves = 4;
+// One workgroup per query, of up to kMWaves waves (about 512 candidates per wave).  Wave w
+// screens a contiguous share of the query's n_split * k split candidates, 64 at a time (one
+// per lane): a ballot against its list's current k-th entry, then the survivors are
+// inserted in lane order.  Wave 0 then inserts the other waves' lists.  (score, id) is a
+// total order, so the result does not depend on the order of the inserts.
+constexpr int kMWaves = 16;
+__host__ __device__ inline int merge_waves(int64_t candidates) {
+  const int64_t w = (candidates + 511) / 512;
+  return w < 1 ? 1 : (w > kMWaves ? kMWaves : (int)w);
+}
 __global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
   const int64_t qi = blockIdx.x;
   const int lane = lane_id(), wave = threadIdx.x >> 6, k = p.k;
+  const int nw = (int)(blockDim.x >> 6);
   __shared__ float xs[kMWaves][64];
   __shared__ int64_t xi[kMWaves][64];
   const int64_t total = (int64_t)p.n_split * k;
-  const int64_t per = (total + kMWaves - 1) / kMWaves;
+  const int64_t per = (total + nw - 1) / nw;
   const int64_t c0 = wave * per;
   const int64_t c1 = c0 + per < total ? c0 + per : total;
   const float* cs = p.ws_cand_s + qi * total;
   const int64_t* ci = p.ws_cand_i + qi * total;
   float ms = -INFINITY;
   int64_t mi = INT64_MAX;
-  for (int64_t c = c0; c < c1; c += 64) {
-    const bool ok = c + lane < c1;
-    const float sc = ok ? cs[c + lane] : -INFINITY;
-    const int64_t id = ok ? ci[c + lane] : INT64_MAX;
-    uint64_t cand = __ballot(ok && better(sc, id, __shfl(ms, k - 1, 64), __shfl(mi, k - 1, 64)));
-    while (cand) {
-      const int L = __builtin_ctzll(cand);
-      cand &= cand - 1;
-      list_insert(ms, mi, __shfl(sc, L, 64), __shfl(id, L, 64), k);
+  constexpr int kR = 8;  // batches of 64 whose loads are issued together
+  for (int64_t c = c0; c < c1; c += 64 * kR) {
+    float scr[kR];
+    int64_t idr[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const bool ok = c + 64 * r + lane < c1;
+      scr[r] = ok ? cs[c + 64 * r + lane] : -INFINITY;
+      idr[r] = ok ? ci[c + 64 * r + lane] : INT64_MAX;
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const float sc = scr[r];
+      const int64_t id = idr[r];
+      uint64_t cand = __ballot(id != INT64_MAX && better(sc, id, __shfl(ms, k - 1, 64), __shfl(mi, k - 1, 64)));
+      while (cand) {
+        const int L = __builtin_ctzll(cand);
+        cand &= cand - 1;
+        list_insert(ms, mi, __shfl(sc, L, 64), __shfl(id, L, 64), k);
+      }
     }
   }
   xs[wave][lane] = ms;
   xi[wave][lane] = mi;
   __syncthreads();
   if (wave != 0) return;
-  for (int w = 1; w < kMWaves; ++w) {
+  for (int w = 1; w < nw; ++w) {
     const float sc = xs[w][lane];
     const int64_t id = xi[w][lane];
     uint64_t cand = __ballot(lane < k && better(sc, id, __shfl(ms, k - 1, 64), __shfl(mi, k - 1, 64)));
@@ -449,15 +466,171 @@ __global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
   }
 }
 
+// ----------------------------------------------------------------------------- few queries
+// With at most kLutQ queries the batched scan would leave most of its 32 query columns
+// empty.  This scan scores one query per workgroup with lane = database vector, as the
+// decode key scan does: in LDS, Tq[g][m] = sum of q_rot over the set bits of byte m of
+// coordinate group g and Ts[g][n] = 2 * sum of S q_rot over the set bits of nibble n; the
+// codebook term through the Walsh expansion of the symmetric codebook,
+// <q_rot, c[idx]> = sum_S alpha_S (2 T_S - sum_j q_rot_j) over the odd subsets S of the
+// code planes, and the QJL term <S q_rot, 2 sigma - 1> = Ts reads - sum_j (S q_rot)_j.
+// Each wave keeps a top-k list; the workgroup merges its waves' lists into the split's.
+constexpr int kLutQ = 4;
+constexpr int kLWaves = 4;
+
+template <int D, int B>
+__global__ __launch_bounds__(64 * kLWaves) void search_lut(SearchParams p) {
+  constexpr int NB = D / 32, W = NB * (B + 1);
+  constexpr int NG = D / 8, NN = D / 4;  // byte and nibble coordinate groups
+  constexpr int VEC = (W % 4 == 0) ? 4 : 2;
+  __shared__ float Tq[NG * 256];
+  __shared__ float Ts[NN * 16];
+  __shared__ float nib[NN * 16];  // nibble sums of q_rot
+  __shared__ float red[2][kLWaves];
+  __shared__ float xs[kLWaves][64];
+  __shared__ int64_t xi[kLWaves][64];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int64_t qi = blockIdx.y, split = blockIdx.x;
+  const int k = p.k;
+  const float* qr = p.ws_q + qi * 2 * D;  // q_rot, then S q_rot
+  const int64_t db_begin = split * p.chunk_len;
+  const int64_t db_end = db_begin + p.chunk_len < p.n_db ? db_begin + p.chunk_len : p.n_db;
+
+  // ---- the first tile is requested before the tables are built
+  uint32_t kw[W], knr = 0;
+  auto fetch = [&](int64_t tt0) {
+    const int64_t v = tt0 + lane;
+    if (v < db_end) {
+      const uint32_t* rec = p.codes + v * W;
+      if constexpr (VEC == 4) {
+#pragma unroll
+        for (int i = 0; i < W / 4; ++i) {
+          const u32x4 x = reinterpret_cast<const u32x4*>(rec)[i];
+          kw[4 * i] = x[0]; kw[4 * i + 1] = x[1]; kw[4 * i + 2] = x[2]; kw[4 * i + 3] = x[3];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < W / 2; ++i) {
+          const u32x2 x = reinterpret_cast<const u32x2*>(rec)[i];
+          kw[2 * i] = x[0]; kw[2 * i + 1] = x[1];
+        }
+      }
+      knr = p.norms[v];
+    }
+  };
+  int64_t t0 = db_begin + (int64_t)wave * 64;
+  fetch(t0);
+
+  for (int i = tid; i < 2 * NN * 16; i += 64 * kLWaves) {  // nibble sums of q_rot, S q_rot
+    const int n = i & 15, g = (i >> 4) % NN, part = i / (NN * 16);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(qr + part * D + 4 * g);
+    const float sum = ((n & 1) ? x[0] : 0.0f) + ((n & 2) ? x[1] : 0.0f) + ((n & 4) ? x[2] : 0.0f) +
+                      ((n & 8) ? x[3] : 0.0f);
+    if (part == 0) nib[i] = sum;
+    else Ts[i - NN * 16] = 2.0f * sum;
+  }
+  {  // sum_j q_rot_j and sum_j (S q_rot)_j
+    float a = 0.0f, c = 0.0f;
+    for (int j = tid; j < D; j += 64 * kLWaves) {
+      a += qr[j];
+      c += qr[D + j];
+    }
+    a = wave_sum_fast(a);
+    c = wave_sum_fast(c);
+    if (lane == 0) {
+      red[0][wave] = a;
+      red[1][wave] = c;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < NG * 256; i += 64 * kLWaves) {  // byte tables from nibble sums
+    const int m = i & 255, g = i >> 8;
+    Tq[i] = nib[(2 * g) * 16 + (m & 15)] + nib[(2 * g + 1) * 16 + (m >> 4)];
+  }
+  float sq = 0.0f, ss = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kLWaves; ++w) {
+    sq += red[0][w];
+    ss += red[1][w];
+  }
+  const float cq = (p.alpha[0] + p.alpha[1] + p.alpha[2] + p.alpha[3]) * sq;
+  float al[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) al[i] = 2.0f * p.alpha[i];
+  __syncthreads();
+
+  float ls = -INFINITY;
+  int64_t li = INT64_MAX;
+  for (; t0 < db_end; t0 += 64 * kLWaves) {
+    const int64_t v = t0 + lane;
+    const bool valid = v < db_end;
+    uint32_t w[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = kw[i];
+    const uint32_t kn = knr;
+    fetch(t0 + 64 * kLWaves);
+    float mse[1] = {0.0f}, qjl[1] = {0.0f};
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const uint32_t* wb = w + blk * (B + 1);
+      lut_byte<1>(Tq, 4 * blk, wb[0], al[0], mse);
+      if constexpr (B >= 2) lut_byte<1>(Tq, 4 * blk, wb[1], al[1], mse);
+      if constexpr (B == 3) {
+        lut_byte<1>(Tq, 4 * blk, wb[2], al[2], mse);
+        lut_byte<1>(Tq, 4 * blk, wb[0] ^ wb[1] ^ wb[2], al[3], mse);
+      }
+      lut_nib<1>(Ts, 8 * blk, wb[B], qjl);
+    }
+    const float n16 = f16_bits_to_f32(kn), r16 = f16_bits_to_f32(kn >> 16);
+    const float sc = n16 * (mse[0] - cq) + p.gamma * r16 * (qjl[0] - ss);
+    uint64_t cand = __ballot(valid && better(sc, v, __shfl(ls, k - 1, 64), __shfl(li, k - 1, 64)));
+    while (cand) {
+      const int L = __builtin_ctzll(cand);
+      cand &= cand - 1;
+      list_insert(ls, li, __shfl(sc, L, 64), t0 + L, k);
+    }
+  }
+  // ---- the waves' lists into one (wave 0)
+  xs[wave][lane] = ls;
+  xi[wave][lane] = li;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w2 = 1; w2 < kLWaves; ++w2) {
+    const float s2 = xs[w2][lane];
+    const int64_t i2 = xi[w2][lane];
+    uint64_t cand = __ballot(lane < k && better(s2, i2, __shfl(ls, k - 1, 64), __shfl(li, k - 1, 64)));
+    while (cand) {
+      const int L = __builtin_ctzll(cand);
+      cand &= cand - 1;
+      list_insert(ls, li, __shfl(s2, L, 64), __shfl(i2, L, 64), k);
+    }
+  }
+  if (lane < k) {
+    if (p.n_split == 1) {
+      p.out_scores[qi * k + lane] = ls;
+      p.out_ids[qi * k + lane] = li;
+    } else {
+      p.ws_cand_s[(qi * p.n_split + split) * k + lane] = ls;
+      p.ws_cand_i[(qi * p.n_split + split) * k + lane] = li;
+    }
+  }
+}
+
 template <int D, int B>
 static int launch_search(const SearchParams& p, int64_t n_blocks, hipStream_t stream) {
   hipLaunchKernelGGL(search_prologue<D>, dim3((unsigned)p.n_q), dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
-  hipLaunchKernelGGL((search_scan<D, B>), dim3((unsigned)n_blocks, (unsigned)p.n_split),
-                     dim3(64 * kSWaves), 0, stream, p);
+  if (p.n_q <= kLutQ)
+    hipLaunchKernelGGL((search_lut<D, B>), dim3((unsigned)p.n_split, (unsigned)p.n_q),
+                       dim3(64 * kLWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL((search_scan<D, B>), dim3((unsigned)n_blocks, (unsigned)p.n_split),
+                       dim3(64 * kSWaves), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   if (p.n_split > 1) {
-    hipLaunchKernelGGL(search_merge, dim3((unsigned)p.n_q), dim3(64 * kMWaves), 0, stream, p);
+    const int nw = merge_waves((int64_t)p.n_split * p.k);
+    hipLaunchKernelGGL(search_merge, dim3((unsigned)p.n_q), dim3(64 * nw), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   }
   return TQ_OK;
@@ -473,6 +646,8 @@ tq_search_plan tq_plan_search(int64_t n_q, int32_t k, int64_t n_db, int32_t d) {
   // split the database so that the grid has several rounds of two workgroups per CU of a
   // 256-CU MI355X (a short last round costs less), with at least 16 tiles per split
   int64_t n_split = (2048 + (blocks > 0 ? blocks : 1) - 1) / (blocks > 0 ? blocks : 1);
+  // few queries (one workgroup per query and split): about two workgroups per CU in all
+  if (n_q <= kLutQ) n_split = (512 + (n_q > 0 ? n_q : 1) - 1) / (n_q > 0 ? n_q : 1);
   const int64_t max_split = (n_db + 16 * kSTile - 1) / (16 * kSTile);
   if (n_split > max_split) n_split = max_split;
   if (n_split > 4096) n_split = 4096;
@@ -517,6 +692,7 @@ int tq_launch_search(const tq_format* f, const tq_tables* t, const void* codes_d
   for (int j = 0; j < f->d; ++j)
     if (t->signs[j] < 0) p.sign_mask[j >> 5] |= 1u << (j & 31);
   for (int i = 0; i < 8; ++i) p.cent[i] = i < (1 << f->bits_lo) ? t->centroids_lo[i] : 0.0f;
+  tq_walsh_coeffs(f->bits_lo, t->centroids_lo, p.alpha);
   const int64_t n_blocks = (n_q + kSQ - 1) / kSQ;
   if (f->d == 256) {
     if (f->bits_lo == 3) return launch_search<256, 3>(p, n_blocks, stream);

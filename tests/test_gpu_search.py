@@ -106,6 +106,22 @@ def test_search_few_queries_many_splits(torch_gpu, db_60k, n_q, k):
     _check_topk(ids, sc, s_o, RTOL * (np.abs(s_o) + scale), k)
 
 
+@pytest.mark.parametrize("n_db,n_q,k,bits,d,d_in", [(5000, 3, 10, 3, 128, 128), (4000, 4, 16, 2, 128, 100),
+                                                    (3000, 1, 5, 1, 128, 128), (6000, 2, 10, 2, 256, 200),
+                                                    (2100, 4, 64, 3, 256, 256)])
+def test_search_few_queries(torch_gpu, n_db, n_q, k, bits, d, d_in):
+    """At most four queries take the per-query table scan (lane = database vector): every
+    supported database format against the oracle's estimator."""
+    db = TI.search_set(n_db, d_in, seed=5301)
+    qs = TI.search_set(n_q, d_in, seed=5302)
+    signs, S = TI.rotation(d, 5800)
+    fmt = O.Format.uniform(d, bits)
+    qz = oracle_quantize(db, fmt, signs, S)
+    ids, sc = _gpu_search(torch_gpu, qs, qz["records"], qz["norms"], (d, bits, bits, d), signs, S, k)
+    s_o, scale = _oracle_scores(qs, qz["records"], qz["norms"], fmt, signs, S)
+    _check_topk(ids, sc, s_o, RTOL * (np.abs(s_o) + scale), k)
+
+
 @pytest.mark.parametrize("n_db,n_q,k,bits,d_in", [(4100, 45, 10, 3, 128), (2500, 33, 5, 2, 100),
                                                   (3000, 20, 16, 1, 128)])
 def test_search_d128(torch_gpu, n_db, n_q, k, bits, d_in):
