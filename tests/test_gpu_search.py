@@ -122,6 +122,33 @@ def test_search_few_queries(torch_gpu, n_db, n_q, k, bits, d, d_in):
     _check_topk(ids, sc, s_o, RTOL * (np.abs(s_o) + scale), k)
 
 
+@pytest.mark.parametrize("n_q", [1, 40])
+def test_search_ties_across_splits(torch_gpu, n_q):
+    """Exact copies of three vectors at ids spread over a 40000-vector database (so over
+    many splits) score identically; the top-k must hold the lowest ids among equal scores,
+    on the few-query path (one query) and the batched path (40 queries)."""
+    d_in, d, k = 200, 256, 20
+    base = TI.search_set(40000, d_in, seed=5401)
+    qs = TI.search_set(n_q, d_in, seed=5402)
+    # three strong vectors (aligned with the first query) copied to 12 spread ids each
+    strong = qs[0][None, :] / np.linalg.norm(qs[0]) * np.array([[1.0], [0.9], [0.8]], dtype=np.float32)
+    copies = np.random.default_rng(5403).choice(40000, size=36, replace=False)
+    db = base.copy()
+    db[copies] = np.repeat(strong, 12, axis=0).astype(np.float32)
+    signs, S = TI.rotation(d, 5900)
+    fmt = O.Format.uniform(d, 3)
+    qz = oracle_quantize(db, fmt, signs, S)
+    ids, sc = _gpu_search(torch_gpu, qs, qz["records"], qz["norms"], (d, 3, 3, d), signs, S, k)
+    s_o, scale = _oracle_scores(qs, qz["records"], qz["norms"], fmt, signs, S)
+    _check_topk(ids, sc, s_o, RTOL * (np.abs(s_o) + scale), k)
+    # query 0: the 12 copies of the strongest vector first (ascending ids), then the
+    # lowest 8 ids of the second one
+    groups = [np.sort(copies[12 * j:12 * (j + 1)]) for j in range(3)]
+    np.testing.assert_array_equal(ids[0, :12], groups[0])
+    np.testing.assert_array_equal(ids[0, 12:20], groups[1][:8])
+    assert np.all(sc[0, :12] == sc[0, 0]) and np.all(sc[0, 12:20] == sc[0, 12])
+
+
 @pytest.mark.parametrize("n_db,n_q,k,bits,d_in", [(4100, 45, 10, 3, 128), (2500, 33, 5, 2, 100),
                                                   (3000, 20, 16, 1, 128)])
 def test_search_d128(torch_gpu, n_db, n_q, k, bits, d_in):
