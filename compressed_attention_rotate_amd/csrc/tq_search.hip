@@ -141,9 +141,12 @@ __device__ __forceinline__ void list_insert(float& ls, int64_t& li, float s, int
   const bool mine_better = lane < k && better(ls, li, s, id);
   const int pos = __popcll(__ballot(mine_better));  // number of entries that stay ahead
   if (pos >= k) return;
-  // lanes > pos take the entry of lane - 1; lane pos takes the candidate
-  const float ps = __shfl_up(ls, 1, 64);
-  const int64_t pi = __shfl_up(li, 1, 64);
+  // lanes > pos take the entry of lane - 1 (a DPP shift of the whole wave by one lane);
+  // lane pos takes the candidate
+  const float ps = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ls), 0x138, 0xF, 0xF, false));
+  const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)li, 0x138, 0xF, 0xF, false);
+  const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)li >> 32), 0x138, 0xF, 0xF, false);
+  const int64_t pi = (int64_t)(((uint64_t)phi << 32) | plo);
   if (lane > pos && lane < k) {
     ls = ps;
     li = pi;
