@@ -134,6 +134,16 @@ __device__ __forceinline__ bool better(float sa, int64_t ia, float sb, int64_t i
   return sa > sb || (sa == sb && ia < ib);
 }
 
+// Value of lane L (wave-uniform) in every lane, through the scalar unit.
+__device__ __forceinline__ float lane_f(float x, int L) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), L));
+}
+__device__ __forceinline__ int64_t lane_i64(int64_t x, int L) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, L);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), L);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Insert (s, id) into the wave's sorted list (lane i < k holds the i-th best) if it beats
 // the current k-th entry.  Wave-uniform arguments.
 __device__ __forceinline__ void list_insert(float& ls, int64_t& li, float s, int64_t id, int k) {
@@ -374,15 +384,15 @@ __global__ __launch_bounds__(64 * kSWaves) void search_scan(SearchParams p) {
 #pragma unroll
       for (int w2 = 1; w2 < kSWaves; ++w2) sc += part[buf][w2][q][lane];
       sc = valid ? sc * qf[h] : -INFINITY;
-      const float kth = __shfl(ls[h], k - 1, 64);
+      const float kth = lane_f(ls[h], k - 1);
       uint64_t cand = __ballot(sc >= kth);  // a superset of the candidates (-inf never enters)
       if (cand == 0) continue;
-      const int64_t kid = __shfl(li[h], k - 1, 64);
+      const int64_t kid = lane_i64(li[h], k - 1);
       cand = __ballot(valid && better(sc, v, kth, kid));
       while (cand) {
         const int L = __builtin_ctzll(cand);
         cand &= cand - 1;
-        const float s = __shfl(sc, L, 64);
+        const float s = lane_f(sc, L);
         list_insert(ls[h], li[h], s, t0 + L, k);
       }
     }
@@ -441,11 +451,11 @@ __global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
     for (int r = 0; r < kR; ++r) {
       const float sc = scr[r];
       const int64_t id = idr[r];
-      uint64_t cand = __ballot(id != INT64_MAX && better(sc, id, __shfl(ms, k - 1, 64), __shfl(mi, k - 1, 64)));
+      uint64_t cand = __ballot(id != INT64_MAX && better(sc, id, lane_f(ms, k - 1), lane_i64(mi, k - 1)));
       while (cand) {
         const int L = __builtin_ctzll(cand);
         cand &= cand - 1;
-        list_insert(ms, mi, __shfl(sc, L, 64), __shfl(id, L, 64), k);
+        list_insert(ms, mi, lane_f(sc, L), lane_i64(id, L), k);
       }
     }
   }
@@ -456,11 +466,11 @@ __global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
   for (int w = 1; w < nw; ++w) {
     const float sc = xs[w][lane];
     const int64_t id = xi[w][lane];
-    uint64_t cand = __ballot(lane < k && better(sc, id, __shfl(ms, k - 1, 64), __shfl(mi, k - 1, 64)));
+    uint64_t cand = __ballot(lane < k && better(sc, id, lane_f(ms, k - 1), lane_i64(mi, k - 1)));
     while (cand) {
       const int L = __builtin_ctzll(cand);
       cand &= cand - 1;
-      list_insert(ms, mi, __shfl(sc, L, 64), __shfl(id, L, 64), k);
+      list_insert(ms, mi, lane_f(sc, L), lane_i64(id, L), k);
     }
   }
   if (lane < k) {
@@ -586,11 +596,11 @@ __global__ __launch_bounds__(64 * kLWaves) void search_lut(SearchParams p) {
     }
     const float n16 = f16_bits_to_f32(kn), r16 = f16_bits_to_f32(kn >> 16);
     const float sc = n16 * (mse[0] - cq) + p.gamma * r16 * (qjl[0] - ss);
-    uint64_t cand = __ballot(valid && better(sc, v, __shfl(ls, k - 1, 64), __shfl(li, k - 1, 64)));
+    uint64_t cand = __ballot(valid && better(sc, v, lane_f(ls, k - 1), lane_i64(li, k - 1)));
     while (cand) {
       const int L = __builtin_ctzll(cand);
       cand &= cand - 1;
-      list_insert(ls, li, __shfl(sc, L, 64), t0 + L, k);
+      list_insert(ls, li, lane_f(sc, L), t0 + L, k);
     }
   }
   // ---- the waves' lists into one (wave 0)
@@ -602,11 +612,11 @@ __global__ __launch_bounds__(64 * kLWaves) void search_lut(SearchParams p) {
   for (int w2 = 1; w2 < kLWaves; ++w2) {
     const float s2 = xs[w2][lane];
     const int64_t i2 = xi[w2][lane];
-    uint64_t cand = __ballot(lane < k && better(s2, i2, __shfl(ls, k - 1, 64), __shfl(li, k - 1, 64)));
+    uint64_t cand = __ballot(lane < k && better(s2, i2, lane_f(ls, k - 1), lane_i64(li, k - 1)));
     while (cand) {
       const int L = __builtin_ctzll(cand);
       cand &= cand - 1;
-      list_insert(ls, li, __shfl(s2, L, 64), __shfl(i2, L, 64), k);
+      list_insert(ls, li, lane_f(s2, L), lane_i64(i2, L), k);
     }
   }
   if (lane < k) {
