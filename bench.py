@@ -260,6 +260,46 @@ def _requant_timing(tq, torch, dev, codes_k, norms_k, fmt, tab, signs, S, steps,
             "stored_gbs": round(stored / t / 1e9, 2)}
 
 
+def _decay_timing(tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq, fmt, tab, signs, S,
+                  steps, n_old=24576):
+    """Temporal decay as a serving cache holds it: in each cache slot the oldest 24576 tokens
+    of every KV head are re-encoded at b=3 (tq_requantize on the GPU) and the newest 8192
+    stay at b=4; one decode step reads both segments (slots rotating as in the main step)."""
+    fo = tq.Format.uniform(D, BITS - 1)
+    to = tq.Tables(fo, signs, tab.S)  # one rotation: the same S array for both segments
+    nslot = len(codes_k)
+    segs = []
+    for s2 in range(nslot):
+        old_k = codes_k[s2][:, :, :n_old].contiguous().view(-1, fmt.record_bytes())
+        old_nk = norms_k[s2][:, :, :n_old].contiguous().view(-1, 2)
+        old_v = codes_v[s2][:, :, :n_old].contiguous().view(-1, fmt.record_bytes())
+        old_nv = norms_v[s2][:, :, :n_old].contiguous().view(-1, 2)
+        rk, rnk = tq.requantize(old_k, old_nk, fmt, tab, fo, to)
+        rv, rnv = tq.requantize(old_v, old_nv, fmt, tab, fo, to)
+        shp = (BATCH, HKV, n_old)
+        segs.append([(rk.view(*shp, -1), rnk.view(*shp, 2), rv.view(*shp, -1), rnv.view(*shp, 2),
+                      torch.full((BATCH,), n_old, dtype=torch.int32, device=dev), fo, to, fo, to),
+                     (codes_k[s2][:, :, n_old:].contiguous(), norms_k[s2][:, :, n_old:].contiguous(),
+                      codes_v[s2][:, :, n_old:].contiguous(), norms_v[s2][:, :, n_old:].contiguous(),
+                      seq - n_old, fmt, tab, fmt, tab)])
+    ws = torch.empty(tq.attend_segments_workspace_bytes(BATCH, HQ, HKV, [n_old, NTOK - n_old], D),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((BATCH, HQ, D), dtype=torch.float32, device=dev)
+    dec = lambda i: tq.attend_decode_segments(q, segs[i % nslot], workspace=ws, out=out)
+    for i in range(3):
+        dec(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record(); dec(i)
+    ev[steps].record(); torch.cuda.synchronize()
+    t = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])) * 1e-3
+    packed = 2 * BATCH * HKV * (n_old * (fo.record_bytes() + 4) + (NTOK - n_old) * (fmt.record_bytes() + 4))
+    return {"old_tokens": n_old, "old_format": "2-bit codebook + 1 QJL bit (48 B/vector)",
+            "new_format": "3-bit codebook + 1 QJL bit (64 B/vector)", "packed_bytes": packed,
+            "decode_us": round(t * 1e6, 3), "decode_gbs": round(packed / t / 1e9, 2)}
+
+
 def _copy_gbs(torch, dev, nbytes=256 << 20, reps=10):
     """Measured HBM bandwidth of a plain device copy (nbytes read + nbytes written per
     copy), the practical ceiling the decode rate is also compared with."""
@@ -624,6 +664,8 @@ def main():
     line["variants"]["prefill_chunk"] = _prefill_timing(tq, torch, dev, ks, vs, fmt, tab)
     line["variants"]["requantize_b4_to_b3"] = _requant_timing(tq, torch, dev, codes_k, norms_k, fmt,
                                                               tab, signs, S, steps, nvec)
+    line["variants"]["decay_24k_b3_8k_b4"] = _decay_timing(
+        tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq, fmt, tab, signs, S, steps)
     line["variants"]["sparse_v_32k_b4"] = _sparse_v_timing(
         tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq, ws, out, fmt, tab, fmt, tab,
         steps)

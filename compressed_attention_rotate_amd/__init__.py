@@ -14,9 +14,10 @@ import math
 import numpy as np
 
 from ._lib import (LIB_PATH, TQ_BF16, TQ_F16, TQ_F32, Format, Tables, TQError, build_codebook,
-                   load)
+                   load, c_cache_segment)
 
 __all__ = ["Format", "Tables", "TQError", "build_codebook", "quantize_kv", "attend_decode",
+           "attend_decode_segments", "attend_segments_workspace_bytes",
            "ip_search", "requantize", "attend_workspace_bytes", "search_workspace_bytes",
            "requantize_workspace_bytes", "quantize_kv_paged", "attend_decode_paged",
            "prefill_paged", "prefill_workspace_bytes", "LIB_PATH", "load"]
@@ -126,6 +127,58 @@ def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format
                                  _stream(q.device))
     _check(rc, "tq_attend_decode")
     return (out, lg) if logits else out
+
+
+def attend_segments_workspace_bytes(batch: int, hq: int, hkv: int, capacities, d: int = 128) -> int:
+    caps = (ctypes.c_int64 * len(capacities))(*[int(c) for c in capacities])
+    n = load().tq_attend_segments_workspace_bytes(batch, hq, hkv, len(capacities), caps, d)
+    if n < 0:
+        raise ValueError("bad shape")
+    return int(n)
+
+
+def attend_decode_segments(q, segments, scale: float = None, tau: float = 0.0, skipped=None,
+                           workspace=None, out=None):
+    """One decode step over a cache kept in segments of different formats (older tokens
+    re-encoded narrower): each query attends to its tokens of segment 0, then 1, ... with
+    one softmax.  segments: sequence of (codes_k, norms_k, codes_v, norms_v, seq_lens,
+    fmt_k, tables_k, fmt_v, tables_v) with the tensors laid out as for attend_decode; value
+    tables must share one rotation (S and signs).  Returns out fp32 [batch, hq, d]."""
+    torch = _torch()
+    batch, hq, d = q.shape
+    hkv = segments[0][0].shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    keep, segs = [], (c_cache_segment * len(segments))()
+    caps = []
+    for i, (ck, nk, cv, nv, seq, fk, tk, fv, tv) in enumerate(segments):
+        cap = ck.shape[2]
+        for t, rb in ((ck, fk.record_bytes()), (cv, fv.record_bytes())):
+            if t.dtype != torch.uint8 or t.shape[:3] != (batch, hkv, cap) or t.shape[3] != rb \
+                    or not t.is_contiguous():
+                raise ValueError(f"segment {i}: bad packed cache tensor")
+        for t in (nk, nv):
+            if t.shape != (batch, hkv, cap, 2) or not t.is_contiguous():
+                raise ValueError(f"segment {i}: bad norms tensor")
+        if seq.dtype != torch.int32 or seq.numel() != batch:
+            raise ValueError(f"segment {i}: seq_lens must be int32 [batch]")
+        c = (fk.c(), tk.c(), fv.c(), tv.c())
+        keep.append(c)
+        segs[i] = c_cache_segment(ctypes.addressof(c[0]), ctypes.addressof(c[1]),
+                                  ctypes.addressof(c[2]), ctypes.addressof(c[3]), _ptr(ck), _ptr(nk),
+                                  _ptr(cv), _ptr(nv), cap, _ptr(seq))
+        caps.append(cap)
+    q = q.contiguous()
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
+    wsb = attend_segments_workspace_bytes(batch, hq, hkv, caps, d)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    rc = load().tq_attend_decode_segments(segs, len(segments), _ptr(q), _dtype_code(q), batch, hq,
+                                          hkv, float(scale), float(tau), _ptr(out), _ptr(skipped),
+                                          _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(rc, "tq_attend_decode_segments")
+    return out
 
 
 def quantize_kv_paged(x, fmt: Format, tables: Tables, slot_mapping, codes_cache, norms_cache,

@@ -35,6 +35,13 @@ class c_tables(ctypes.Structure):
                 ("signs", ctypes.c_void_p), ("S", ctypes.c_void_p)]
 
 
+class c_cache_segment(ctypes.Structure):
+    _fields_ = [("fk", ctypes.c_void_p), ("tk", ctypes.c_void_p), ("fv", ctypes.c_void_p),
+                ("tv", ctypes.c_void_p), ("codes_k", ctypes.c_void_p), ("norms_k", ctypes.c_void_p),
+                ("codes_v", ctypes.c_void_p), ("norms_v", ctypes.c_void_p),
+                ("capacity", ctypes.c_int64), ("seq_lens", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -55,6 +62,9 @@ def load() -> ctypes.CDLL:
             "tq_attend_workspace_bytes": (I64, [I32, I32, I32, I64, I32]),
             "tq_attend_decode": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P, P, P, P, I64,
                                                 P, F32, F32, P, P, P, P, I64, P]),
+            "tq_attend_segments_workspace_bytes": (I64, [I32, I32, I32, I32, P, I32]),
+            "tq_attend_decode_segments": (ctypes.c_int, [P, I32, P, I32, I32, I32, I32, F32, F32,
+                                                         P, P, P, I64, P]),
             "tq_search_workspace_bytes": (I64, [I64, I32, I64, I32]),
             "tq_ip_search": (ctypes.c_int, [P, P, P, P, I64, P, I32, I64, I32, P, P, P, I64, P]),
             "tq_quantize_kv_paged": (ctypes.c_int, [P, P, P, I32, I64, I32, I32, I64, P, I32, I64,

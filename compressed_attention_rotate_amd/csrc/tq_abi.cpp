@@ -165,6 +165,62 @@ int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                         workspace_bytes, stream, nullptr);
 }
 
+int64_t tq_attend_segments_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv,
+                                           int32_t n_seg, const int64_t* capacities, int32_t d) {
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || d != 128 || hq % hkv) return -1;
+  if (n_seg < 1 || n_seg > 8 || !capacities) return -1;
+  // the segments' split partials side by side: each plan's partial array, summed
+  int64_t bytes = 0;
+  for (int s = 0; s < n_seg; ++s) {
+    if (capacities[s] < 0) return -1;
+    bytes += tq_plan_decode(batch, hq, hkv, capacities[s], d).ws_bytes;
+  }
+  return bytes;
+}
+
+int tq_attend_decode_segments(const tq_cache_segment* segs, int32_t n_seg, const void* q,
+                              int32_t q_dtype, int32_t batch, int32_t hq, int32_t hkv,
+                              float scale, float tau, float* out, int64_t* skipped,
+                              void* workspace, int64_t workspace_bytes, tq_stream_t stream) {
+  if (!segs || n_seg < 1 || n_seg > 8) return TQ_ERR_ARG;
+  int64_t caps[8];
+  for (int s = 0; s < n_seg; ++s) {
+    const tq_cache_segment& g = segs[s];
+    if (!g.fk || !g.tk || !g.fv || !g.tv) return TQ_ERR_ARG;
+    // every argument check of a plain decode, except the workspace size
+    const int rc = decode_checked(g.fk, g.tk, g.fv, g.tv, q, q_dtype, batch, hq, hkv, g.codes_k,
+                                  g.norms_k, g.codes_v, g.norms_v, g.capacity, g.seq_lens, scale,
+                                  tau, out, nullptr, skipped, workspace, INT64_MAX, stream,
+                                  nullptr, false);
+    if (rc) return rc;
+    // the value sums of all segments are mapped back with one rotation
+    if (g.tv->S != segs[0].tv->S) return TQ_ERR_ARG;
+    for (int j = 0; j < g.fv->d; ++j)
+      if ((g.tv->signs[j] < 0) != (segs[0].tv->signs[j] < 0)) return TQ_ERR_ARG;
+    caps[s] = g.capacity;
+  }
+  const int64_t need = tq_attend_segments_workspace_bytes(batch, hq, hkv, n_seg, caps, 128);
+  if (need < 0) return TQ_ERR_ARG;
+  if (workspace_bytes < need) return TQ_ERR_WORKSPACE;
+  int32_t total = 0, base[8];
+  tq_decode_plan plans[8];
+  for (int s = 0; s < n_seg; ++s) {
+    plans[s] = tq_plan_decode(batch, hq, hkv, caps[s], 128);
+    base[s] = total;
+    total += plans[s].n_split;
+  }
+  for (int s = 0; s < n_seg; ++s) {
+    const tq_cache_segment& g = segs[s];
+    const int rc = tq_launch_decode(g.fk, g.tk, g.fv, g.tv, q, q_dtype, batch, hq, hkv, g.codes_k,
+                                    g.norms_k, g.codes_v, g.norms_v, g.capacity, g.seq_lens,
+                                    scale, tau, out, nullptr, skipped, workspace, plans[s],
+                                    reinterpret_cast<hipStream_t>(stream), nullptr, base[s],
+                                    total, s == n_seg - 1);
+    if (rc) return rc;
+  }
+  return TQ_OK;
+}
+
 int tq_attend_decode_paged(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
                            const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
                            int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,

@@ -152,7 +152,8 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      const void* codes_v, const uint16_t* norms_v, int64_t capacity,
                      const int32_t* seq_lens, float scale, float tau, float* out, float* logits,
                      int64_t* skipped, void* workspace, const tq_decode_plan& plan,
-                     hipStream_t stream, const tq_paged_src* paged) {
+                     hipStream_t stream, const tq_paged_src* paged, int32_t split_base,
+                     int32_t split_total, bool combine) {
   using namespace tqk;
   DecodeParams p{};
   p.causal_start = -1;
@@ -183,7 +184,8 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
   p.hkv = hkv;
   p.group = hq / hkv;
   p.q_dtype = q_dtype;
-  p.n_split = plan.n_split;
+  p.n_split = split_total > 0 ? split_total : plan.n_split;
+  p.split_base = split_base;
   p.ksplitb = fk->split / 32;
   p.scale = scale;
   p.tau = tau;
@@ -214,7 +216,7 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
   else
   TQ_DECODE_PAIRS(TQ_DECODE_LAUNCH) {}
 #undef TQ_DECODE_LAUNCH
-  if (rc != TQ_OK) return rc;
+  if (rc != TQ_OK || !combine) return rc;
   hipLaunchKernelGGL(decode_combine, dim3(batch * hq), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }

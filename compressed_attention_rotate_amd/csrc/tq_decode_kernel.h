@@ -136,6 +136,7 @@ struct DecodeParams {
   int32_t max_blocks, page_log2;
   int32_t bt_stride;      // block-table row stride (0: every query reads one table)
   int64_t causal_start;   // >= 0: query b sees tokens t <= causal_start + b (prefill chunk)
+  int32_t split_base;     // index of this launch's first split among the n_split partials
 };
 
 // LDS layout of one scan workgroup (floats).
@@ -710,7 +711,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
         lsum = fmaf(o[GC + h], sc, lsum);
       }
     }
-    float* part = p.ws_part + (((int64_t)b * p.hq + h0 + h) * p.n_split + blockIdx.x) * kPartFloats;
+    float* part = p.ws_part + (((int64_t)b * p.hq + h0 + h) * p.n_split + p.split_base + blockIdx.x) * kPartFloats;
     part[2 + k] = acc;
     if (k == 0) {
       part[0] = M;

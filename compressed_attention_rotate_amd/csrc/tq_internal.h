@@ -53,7 +53,8 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      const void* codes_v, const uint16_t* norms_v, int64_t capacity,
                      const int32_t* seq_lens, float scale, float tau, float* out, float* logits,
                      int64_t* skipped, void* workspace, const tq_decode_plan& plan,
-                     hipStream_t stream, const tq_paged_src* paged = nullptr);
+                     hipStream_t stream, const tq_paged_src* paged = nullptr,
+                     int32_t split_base = 0, int32_t split_total = 0, bool combine = true);
 
 struct tq_search_plan {
   int32_t n_chunks;       // database chunks scanned independently

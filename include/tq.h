@@ -164,6 +164,44 @@ int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      float* logits, int64_t* skipped, void* workspace,
                      int64_t workspace_bytes, tq_stream_t stream);
 
+/* Decode over a cache kept in segments of different formats, as temporal decay leaves
+ * it (zhidx article, section "01 turboquant_plus：介绍与详解": older tokens drop to a
+ * narrower format, e.g. re-encoded in place by tq_requantize, while new ones are
+ * written at full width).  Each query attends to the concatenation of its tokens in
+ * segment 0, then segment 1, ...: one softmax over all of them.
+ *   segs     : host array of n_seg (1..8) segments; segment s holds its own key and value
+ *              formats and tables and its packed records [batch][hkv][capacity] with
+ *              norms, and seq_lens (device int32 [batch], each in [0, capacity]).
+ *              Key formats and tables may differ between segments.  Value tables must
+ *              share one rotation (the same S device array and equal sign diagonals),
+ *              since every segment's value sums are mapped back once; their codebook
+ *              widths may differ.
+ *   q, q_dtype, batch, hq, hkv, scale, tau, out, skipped : as tq_attend_decode
+ *   workspace: device, >= tq_attend_segments_workspace_bytes(...) bytes
+ * Errors: as tq_attend_decode; TQ_ERR_ARG for n_seg outside 1..8, a null segment
+ * array or value tables of different rotations. */
+typedef struct {
+  const tq_format* fk;
+  const tq_tables* tk;
+  const tq_format* fv;
+  const tq_tables* tv;
+  const void* codes_k;
+  const uint16_t* norms_k;
+  const void* codes_v;
+  const uint16_t* norms_v;
+  int64_t capacity;
+  const int32_t* seq_lens;
+} tq_cache_segment;
+
+/* Workspace bytes tq_attend_decode_segments needs; capacities: host array [n_seg]. */
+int64_t tq_attend_segments_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv,
+                                           int32_t n_seg, const int64_t* capacities, int32_t d);
+
+int tq_attend_decode_segments(const tq_cache_segment* segs, int32_t n_seg, const void* q,
+                              int32_t q_dtype, int32_t batch, int32_t hq, int32_t hkv,
+                              float scale, float tau, float* out, int64_t* skipped,
+                              void* workspace, int64_t workspace_bytes, tq_stream_t stream);
+
 /* Paged cache.  A cache of fixed-size pages, as serving engines keep it: codes
  * [num_pages][hkv][page_size] records and norms [num_pages][hkv][page_size][2] uint16;
  * a sequence's token t lives in page block_table[b][t / page_size] at offset

@@ -1,0 +1,177 @@
+"""GPU: decode over a cache kept in segments of different formats (temporal decay: older
+tokens re-encoded to a narrower format) against the oracle.  Expected values: each
+segment's packed bytes dequantized by the oracle with that segment's format, the token
+lists concatenated in segment order, then the oracle's textbook softmax attention."""
+import math
+
+import numpy as np
+import pytest
+
+import tq_inputs as TI
+from oracle import tq_oracle as O
+from parity_utils import oracle_codebooks, oracle_pack_cache
+
+pytestmark = pytest.mark.gpu
+
+OUT_ATOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import compressed_attention_rotate_amd as tq
+    tq.load()
+    return torch
+
+
+def _oracle_segments(q64, segs, scale, signs, S):
+    """segs: list of (rec_k, nrm_k, rec_v, nrm_v, seq_lens, fmt_k, fmt_v) packed by the oracle."""
+    batch, hq, d = q64.shape
+    hkv = segs[0][0].shape[1]
+    G = hq // hkv
+    out = np.zeros((batch, hq, d))
+    for bi in range(batch):
+        for kh in range(hkv):
+            kts, vts = [], []
+            for rk, nk, rv, nv, lens, fk, fv in segs:
+                L = int(lens[bi])
+                ik, sk = O.unpack(rk[bi, kh, :L], fk)
+                iv, sv = O.unpack(rv[bi, kh, :L], fv)
+                kts.append(O.dequantize(ik, sk, nk[bi, kh, :L, 0], nk[bi, kh, :L, 1], fk, signs, S,
+                                        *oracle_codebooks(d, fk.bits_lo, fk.bits_hi), qjl=fk.qjl))
+                vts.append(O.dequantize(iv, sv, nv[bi, kh, :L, 0], nv[bi, kh, :L, 1], fv, signs, S,
+                                        *oracle_codebooks(d, fv.bits_lo, fv.bits_hi), qjl=fv.qjl))
+            kt, vt = np.concatenate(kts), np.concatenate(vts)
+            for g in range(G):
+                out[bi, kh * G + g] = O.attend(q64[bi, kh * G + g], kt, vt, scale)[0]
+    return out
+
+
+def _gpu_segments(torch, q_bits, segs, signs, S, tau=0.0):
+    import compressed_attention_rotate_amd as tq
+    Sd = torch.from_numpy(S).cuda()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    args = []
+    for rk, nk, rv, nv, lens, fk, fv in segs:
+        tfk, tfv = tq.Format(fk.d, fk.bits_lo, fk.bits_hi, fk.split, fk.qjl), \
+            tq.Format(fv.d, fv.bits_lo, fv.bits_hi, fv.split, fv.qjl)
+        args.append((dev(rk), dev(nk.view(np.int16)).view(torch.float16), dev(rv),
+                     dev(nv.view(np.int16)).view(torch.float16),
+                     dev(np.asarray(lens, dtype=np.int32)), tfk, tq.Tables(tfk, signs, Sd), tfv,
+                     tq.Tables(tfv, signs, Sd)))
+    q = dev(q_bits.view(np.int16)).view(torch.bfloat16)
+    sk = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = tq.attend_decode_segments(q, args, tau=tau, skipped=sk)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), int(sk.item())
+
+
+def _pack(kb, vb, fk, fv, signs, S):
+    rk, nk, _ = oracle_pack_cache(kb, fk, signs, S, bf16=True)
+    rv, nv, _ = oracle_pack_cache(vb, fv, signs, S, bf16=True)
+    return rk, nk, rv, nv
+
+
+@pytest.mark.parametrize("old,new", [((128, 2, 2, 128), (128, 3, 3, 128)),
+                                     ((128, 2, 1, 64), (128, 3, 2, 64)),
+                                     ((128, 1, 1, 128), (128, 3, 3, 128))])
+def test_two_segments_against_oracle(torch_gpu, old, new):
+    """An old segment (narrower codebook) then a new one, ragged lengths incl. an empty old
+    and an empty new segment, GQA group 4."""
+    batch, hq, hkv, d = 3, 8, 2, 128
+    n_old, n_new = 530, 170
+    kb, vb, _ = TI.kv_layer(batch, hkv, n_old + n_new, d, seed=8101)
+    q_bits = TI.decode_queries(batch, hq, d, 8101)
+    signs, S = TI.rotation(d, 8102)
+    fo, fn = O.Format(*old), O.Format(*new)
+    seg_old = _pack(kb[:, :, :n_old], vb[:, :, :n_old], fo, fo, signs, S) + ([530, 0, 301], fo, fo)
+    seg_new = _pack(kb[:, :, n_old:], vb[:, :, n_old:], fn, fn, signs, S) + ([170, 99, 0], fn, fn)
+    out_g, _ = _gpu_segments(torch_gpu, q_bits, [seg_old, seg_new], signs, S)
+    out_o = _oracle_segments(TI.bf16_to_f64(q_bits), [seg_old, seg_new], 1 / math.sqrt(d), signs, S)
+    err = float(np.max(np.abs(out_g - out_o)))
+    print(f"\nold {old} new {new}: max|out - oracle| {err:.3g}")
+    assert err <= OUT_ATOL
+
+
+def test_requantized_old_segment(torch_gpu):
+    """The temporal-decay flow: 700 tokens packed at b = 4, the oldest 500 re-encoded to
+    b = 3 by the oracle's requantize, decoded as two segments (three segments, the old
+    part split in two, give the same result)."""
+    batch, hq, hkv, d = 2, 8, 2, 128
+    n, n_old = 700, 500
+    kb, vb, _ = TI.kv_layer(batch, hkv, n, d, seed=8201)
+    q_bits = TI.decode_queries(batch, hq, d, 8201)
+    signs, S = TI.rotation(d, 8202)
+    f4, f3 = O.Format.uniform(d, 3), O.Format.uniform(d, 2)
+    rk, nk, rv, nv = _pack(kb, vb, f4, f4, signs, S)
+    cb4, cb3 = oracle_codebooks(d, 3, 3), oracle_codebooks(d, 2, 2)
+
+    def decay(rec, nrm):
+        r = rec[:, :, :n_old].reshape(-1, rec.shape[-1])
+        m = nrm[:, :, :n_old].reshape(-1, 2)
+        o = O.requantize(r, m[:, 0], m[:, 1], f4, S, *cb4, f3, S, *cb3)
+        recs = O.pack(o["idx"], o["sbit"], f3).reshape(batch, hkv, n_old, -1)
+        nrms = np.stack([O.fp16_bits(o["n16"]) if o["n16"].dtype != np.uint16 else o["n16"],
+                         O.fp16_bits(o["r16"]) if o["r16"].dtype != np.uint16 else o["r16"]],
+                        axis=-1).reshape(batch, hkv, n_old, 2)
+        return recs, nrms
+    ork, onk = decay(rk, nk)
+    orv, onv = decay(rv, nv)
+    seg_old = (ork, onk, orv, onv, [n_old] * batch, f3, f3)
+    seg_new = (rk[:, :, n_old:], nk[:, :, n_old:], rv[:, :, n_old:], nv[:, :, n_old:],
+               [n - n_old, 123], f4, f4)
+    out_o = _oracle_segments(TI.bf16_to_f64(q_bits), [seg_old, seg_new], 1 / math.sqrt(d), signs, S)
+    out_2, _ = _gpu_segments(torch_gpu, q_bits, [seg_old, seg_new], signs, S)
+    cut = 256
+    seg_a = (ork[:, :, :cut], onk[:, :, :cut], orv[:, :, :cut], onv[:, :, :cut], [cut] * batch, f3, f3)
+    seg_b = (ork[:, :, cut:], onk[:, :, cut:], orv[:, :, cut:], onv[:, :, cut:], [n_old - cut] * batch,
+             f3, f3)
+    out_3, _ = _gpu_segments(torch_gpu, q_bits, [seg_a, seg_b, seg_new], signs, S)
+    err = float(np.max(np.abs(out_2 - out_o)))
+    print(f"\nrequantized old segment: max|out - oracle| {err:.3g}, "
+          f"two vs three segments {float(np.max(np.abs(out_2 - out_3))):.3g}")
+    assert err <= OUT_ATOL
+    assert float(np.max(np.abs(out_2 - out_3))) <= 1e-5
+
+
+def test_one_segment_equals_plain_decode(torch_gpu):
+    """A single segment is the plain decode: same records, same result up to fp32 rounding
+    of the split merge (the split plans are identical, so bit for bit)."""
+    import compressed_attention_rotate_amd as tq
+    torch = torch_gpu
+    batch, hq, hkv, d, n = 2, 8, 2, 128, 900
+    kb, vb, _ = TI.kv_layer(batch, hkv, n, d, seed=8301)
+    q_bits = TI.decode_queries(batch, hq, d, 8301)
+    signs, S = TI.rotation(d, 8302)
+    f = O.Format.uniform(d, 3)
+    rk, nk, rv, nv = _pack(kb, vb, f, f, signs, S)
+    out_s, _ = _gpu_segments(torch, q_bits, [(rk, nk, rv, nv, [900, 417], f, f)], signs, S)
+    tf = tq.Format.uniform(d, 3)
+    tab = tq.Tables(tf, signs, torch.from_numpy(S).cuda())
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out_p = tq.attend_decode(dev(q_bits.view(np.int16)).view(torch.bfloat16), dev(rk),
+                             dev(nk.view(np.int16)).view(torch.float16), dev(rv),
+                             dev(nv.view(np.int16)).view(torch.float16),
+                             dev(np.array([900, 417], dtype=np.int32)), tf, tab).cpu().numpy()
+    np.testing.assert_array_equal(out_s, out_p)
+
+
+def test_value_rotation_mismatch_rejected(torch_gpu):
+    """Value tables with different S arrays cannot be merged: the call is rejected before
+    any launch."""
+    import compressed_attention_rotate_amd as tq
+    torch = torch_gpu
+    d = 128
+    signs, S = TI.rotation(d, 8402)
+    tf = tq.Format.uniform(d, 3)
+    t1 = tq.Tables(tf, signs, torch.from_numpy(S).cuda())
+    t2 = tq.Tables(tf, signs, torch.from_numpy(S.copy()).cuda())
+    rb = tf.record_bytes()
+    ck = torch.zeros((1, 1, 64, rb), dtype=torch.uint8, device="cuda")
+    nk = torch.zeros((1, 1, 64, 2), dtype=torch.float16, device="cuda")
+    seq = torch.full((1,), 64, dtype=torch.int32, device="cuda")
+    q = torch.zeros((1, 1, d), dtype=torch.float32, device="cuda")
+    with pytest.raises(tq.TQError):
+        tq.attend_decode_segments(q, [(ck, nk, ck, nk, seq, tf, t1, tf, t1),
+                                      (ck, nk, ck, nk, seq, tf, t1, tf, t2)])
