@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import compressed_attention_rotate_amd as tq
-from compressed_attention_rotate_amd._lib import c_format, c_tables
+from compressed_attention_rotate_amd._lib import c_cache_segment, c_format, c_tables
 from oracle import tq_oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -149,6 +149,45 @@ def test_decode_and_search_validation_before_launch():
     assert S(d_in=300) == E.TQ_ERR_SHAPE
     assert S(ws_bytes=wsb - 1) == E.TQ_ERR_WORKSPACE
     assert S(f=c_format(256, 3, 3, 256, 0)) == E.TQ_ERR_SHAPE        # search scores need QJL
+
+
+def test_segments_validation_before_launch():
+    """tq_attend_decode_segments: every error is found on the host before any launch (the
+    calls below run without a GPU)."""
+    lib = tq.load()
+    E = tq._lib
+    f4, f3 = c_format(128, 3, 3, 128, 1), c_format(128, 2, 2, 128, 1)
+    t4, keep4 = _tables(tq.Format(128, 3, 3, 128))
+    t3, keep3 = _tables(tq.Format(128, 2, 2, 128))
+    t3_other, keep3o = _tables(tq.Format(128, 2, 2, 128), S_ptr=0x18000)   # another S array
+    p = ctypes.c_void_p(0x40000)
+    caps = (ctypes.c_int64 * 2)(24576, 8192)
+    ws = lib.tq_attend_segments_workspace_bytes(1, 32, 8, 2, caps, 128)
+    assert ws == tq.attend_workspace_bytes(1, 32, 8, 24576) + tq.attend_workspace_bytes(1, 32, 8, 8192)
+    assert lib.tq_attend_segments_workspace_bytes(1, 32, 8, 0, caps, 128) == -1
+    assert lib.tq_attend_segments_workspace_bytes(1, 32, 8, 9, caps, 128) == -1
+
+    def seg(fk, tk, fv, tv, cap):
+        return c_cache_segment(ctypes.addressof(fk), ctypes.addressof(tk), ctypes.addressof(fv),
+                               ctypes.addressof(tv), p, p, p, p, cap, p)
+
+    def G(segs, n=None, ws_bytes=ws):
+        arr = (c_cache_segment * len(segs))(*segs)
+        return lib.tq_attend_decode_segments(arr, len(segs) if n is None else n, p, 1, 1, 32, 8,
+                                             0.088, 0.0, p, None, p, ws_bytes, None)
+    good = [seg(f3, t3, f3, t3, 24576), seg(f4, t4, f4, t4, 8192)]
+    assert G(good, ws_bytes=ws - 1) == E.TQ_ERR_WORKSPACE       # (every other check passed)
+    assert G(good, n=0) == E.TQ_ERR_ARG
+    assert G(good, n=9) == E.TQ_ERR_ARG
+    assert lib.tq_attend_decode_segments(None, 2, p, 1, 1, 32, 8, 0.088, 0.0, p, None, p, ws,
+                                         None) == E.TQ_ERR_ARG
+    # value tables of another rotation cannot be merged; key tables may differ
+    assert G([seg(f3, t3, f3, t3_other, 24576), seg(f4, t4, f4, t4, 8192)]) == E.TQ_ERR_ARG
+    assert G([seg(f3, t3_other, f3, t3, 24576), seg(f4, t4, f4, t4, 8192)],
+             ws_bytes=ws - 1) == E.TQ_ERR_WORKSPACE
+    # a segment's own format checks still apply
+    assert G([seg(c_format(128, 3, 3, 128, 0), t4, f4, t4, 24576), seg(f4, t4, f4, t4, 8192)]) \
+        == E.TQ_ERR_SHAPE
 
 
 def test_strerror_names_every_code():
