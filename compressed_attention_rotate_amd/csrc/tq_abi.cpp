@@ -202,6 +202,11 @@ int tq_attend_decode_segments(const tq_cache_segment* segs, int32_t n_seg, const
   const int64_t need = tq_attend_segments_workspace_bytes(batch, hq, hkv, n_seg, caps, 128);
   if (need < 0) return TQ_ERR_ARG;
   if (workspace_bytes < need) return TQ_ERR_WORKSPACE;
+  if (n_seg == 2) {  // a fused instance runs both segments in one scan launch
+    const int rc = tq_launch_decode_pair(segs, q, q_dtype, batch, hq, hkv, scale, tau, out, skipped,
+                                         workspace, reinterpret_cast<hipStream_t>(stream));
+    if (rc != TQ_ERR_SHAPE) return rc;
+  }
   int32_t total = 0, base[8];
   tq_decode_plan plans[8];
   for (int s = 0; s < n_seg; ++s) {

@@ -146,14 +146,18 @@ tq_decode_plan tq_plan_decode(int32_t batch, int32_t hq, int32_t hkv, int64_t ca
   return p;
 }
 
-int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
-                     const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
-                     int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
-                     const void* codes_v, const uint16_t* norms_v, int64_t capacity,
-                     const int32_t* seq_lens, float scale, float tau, float* out, float* logits,
-                     int64_t* skipped, void* workspace, const tq_decode_plan& plan,
-                     hipStream_t stream, const tq_paged_src* paged, int32_t split_base,
-                     int32_t split_total, bool combine) {
+namespace {
+// Scan / combine parameters of one cache (segment): formats, tables, records, query, output
+// and the split plan (tokens per split, total partial count, this cache's first partial).
+tqk::DecodeParams make_decode_params(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                                     const tq_tables* tv, const void* q, int32_t q_dtype,
+                                     int32_t batch, int32_t hq, int32_t hkv, const void* codes_k,
+                                     const uint16_t* norms_k, const void* codes_v,
+                                     const uint16_t* norms_v, int64_t capacity,
+                                     const int32_t* seq_lens, float scale, float tau, float* out,
+                                     float* logits, int64_t* skipped, void* workspace,
+                                     const tq_decode_plan& plan, const tq_paged_src* paged,
+                                     int32_t split_base, int32_t split_total) {
   using namespace tqk;
   DecodeParams p{};
   p.causal_start = -1;
@@ -201,6 +205,23 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
     p.cent_v[0][i] = i < (1 << fv->bits_lo) ? tv->centroids_lo[i] : 0.0f;
     p.cent_v[1][i] = i < (1 << fv->bits_hi) ? tv->centroids_hi[i] : 0.0f;
   }
+  return p;
+}
+}  // namespace
+
+int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                     const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
+                     int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                     const void* codes_v, const uint16_t* norms_v, int64_t capacity,
+                     const int32_t* seq_lens, float scale, float tau, float* out, float* logits,
+                     int64_t* skipped, void* workspace, const tq_decode_plan& plan,
+                     hipStream_t stream, const tq_paged_src* paged, int32_t split_base,
+                     int32_t split_total, bool combine) {
+  using namespace tqk;
+  DecodeParams p = make_decode_params(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k,
+                                      codes_v, norms_v, capacity, seq_lens, scale, tau, out,
+                                      logits, skipped, workspace, plan, paged, split_base,
+                                      split_total);
   const int gc = p.group >= 4 ? 4 : p.group;
   const int nchunk = p.group / gc;
   const unsigned units = (unsigned)(batch * hkv * nchunk);
@@ -218,5 +239,61 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
 #undef TQ_DECODE_LAUNCH
   if (rc != TQ_OK || !combine) return rc;
   hipLaunchKernelGGL(decode_combine, dim3(batch * hq), dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+// Two segments whose format pairs have a fused instance (TQ_DECAY_PAIRS) in one scan launch:
+// the plan of the concatenated length split between the segments in proportion to their
+// capacities, then one combine.  Returns TQ_ERR_SHAPE, before launching anything, when the
+// combination, the group size or an empty segment rules the fused path out.
+int tq_launch_decode_pair(const tq_cache_segment* segs, const void* q, int32_t q_dtype,
+                          int32_t batch, int32_t hq, int32_t hkv, float scale, float tau,
+                          float* out, int64_t* skipped, void* workspace, hipStream_t stream) {
+  using namespace tqk;
+  const tq_cache_segment& s0 = segs[0];
+  const tq_cache_segment& s1 = segs[1];
+  if ((hq / hkv) % 4 || !s0.fv->qjl || !s1.fv->qjl || s0.capacity <= 0 || s1.capacity <= 0)
+    return TQ_ERR_SHAPE;
+  int sh[2][6];
+  for (int i = 0; i < 2; ++i) {
+    shape_of(segs[i].fk, sh[i][0], sh[i][1], sh[i][2]);
+    shape_of(segs[i].fv, sh[i][3], sh[i][4], sh[i][5]);
+  }
+  const int64_t cap = s0.capacity + s1.capacity;
+  const int32_t total = tq_plan_decode(batch, hq, hkv, cap, 128).n_split;
+  if (total < 2) return TQ_ERR_SHAPE;
+  int32_t n0 = (int32_t)((total * s0.capacity + cap / 2) / cap);
+  if (n0 < 1) n0 = 1;
+  if (n0 > total - 1) n0 = total - 1;
+  const int32_t n1 = total - n0;
+  tq_decode_plan pl[2];
+  for (int i = 0; i < 2; ++i) {
+    const int64_t c = segs[i].capacity, n = i == 0 ? n0 : n1;
+    pl[i] = tq_plan_decode(batch, hq, hkv, c, 128);
+    int64_t tps = (c + n - 1) / n;
+    tps = (tps + kTile - 1) / kTile * kTile;
+    pl[i].n_split = (int32_t)n;
+    pl[i].tokens_per_split = tps < kTile ? kTile : tps;
+  }
+  const DecodeParams p0 = make_decode_params(s0.fk, s0.tk, s0.fv, s0.tv, q, q_dtype, batch, hq, hkv,
+                                             s0.codes_k, s0.norms_k, s0.codes_v, s0.norms_v,
+                                             s0.capacity, s0.seq_lens, scale, tau, out, nullptr,
+                                             skipped, workspace, pl[0], nullptr, 0, total);
+  const DecodeParams p1 = make_decode_params(s1.fk, s1.tk, s1.fv, s1.tv, q, q_dtype, batch, hq, hkv,
+                                             s1.codes_k, s1.norms_k, s1.codes_v, s1.norms_v,
+                                             s1.capacity, s1.seq_lens, scale, tau, out, nullptr,
+                                             skipped, workspace, pl[1], nullptr, n0, total);
+  const dim3 grid((unsigned)total, (unsigned)(batch * hkv * (hq / hkv / 4)));
+  int rc = TQ_ERR_SHAPE;
+#define TQ_DECAY_LAUNCH(a0, a1, a2, a3, a4, a5, b0, b1, b2, b3, b4, b5)                      \
+  if (sh[0][0] == a0 && sh[0][1] == a1 && sh[0][2] == a2 && sh[0][3] == a3 &&              \
+      sh[0][4] == a4 && sh[0][5] == a5 && sh[1][0] == b0 && sh[1][1] == b1 &&              \
+      sh[1][2] == b2 && sh[1][3] == b3 && sh[1][4] == b4 && sh[1][5] == b5)                \
+    rc = launch_scan_pair<a0, a1, a2, a3, a4, a5, b0, b1, b2, b3, b4, b5>(p0, p1, n0, grid, stream); \
+  else
+  TQ_DECAY_PAIRS(TQ_DECAY_LAUNCH) {}
+#undef TQ_DECAY_LAUNCH
+  if (rc != TQ_OK) return rc;
+  hipLaunchKernelGGL(decode_combine, dim3(batch * hq), dim3(256), 0, stream, p1);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }

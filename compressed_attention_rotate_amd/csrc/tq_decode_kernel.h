@@ -198,15 +198,22 @@ __device__ __forceinline__ void fwht128(float (&v)[2], int lane) {
   }
 }
 
+// LDS floats one scan workgroup of a format pair needs.
+template <int BVLO, int BVHI, int VSPLIT, bool VQ, int GC>
+constexpr int scan_lds_floats() {
+  return ScanLds<GC, Rec<BVLO, BVHI, VSPLIT, VQ ? 1 : 0>::W, BVLO, BVHI, VSPLIT>::kTotal;
+}
+
+// The scan of split `split` of one (batch, KV head, head chunk) unit (blockIdx.y); lds is
+// the workgroup's LDS array of at least scan_lds_floats<...>() floats.
 // VQ: the value records carry QJL sign words (else MSE-only values: no residual term).
 template <int BKLO, int BKHI, int KSPLIT, int BVLO, int BVHI, int VSPLIT, bool VQ, int GC>
-__global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
+__device__ __forceinline__ void scan_body(const DecodeParams& p, float* lds, int split) {
   using KR = Rec<BKLO, BKHI, KSPLIT>;
   using VR = Rec<BVLO, BVHI, VSPLIT, VQ ? 1 : 0>;
   constexpr int KW = KR::W, VW = VR::W;
   using L = ScanLds<GC, VW, BVLO, BVHI, VSPLIT>;
   constexpr int kRS = L::kRS;
-  __shared__ __attribute__((aligned(16))) float lds[L::kTotal];
   float* Tq = lds + L::oTq;
   float* Ts = lds + L::oTs;
   float* cpLo = lds + L::oCpLo;
@@ -224,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
   const int h0 = (bk % p.hkv) * p.group + chunk * GC;
   int64_t seq = p.causal_start >= 0 ? p.causal_start + b + 1 : (int64_t)p.seq_lens[b];
   if (seq > p.capacity) seq = p.capacity;
-  const int64_t t_begin = (int64_t)blockIdx.x * p.tokens_per_split;
+  const int64_t t_begin = (int64_t)split * p.tokens_per_split;
   int64_t t_end = t_begin + p.tokens_per_split;
   if (t_end > seq) t_end = seq;
   const int64_t kv_base = (int64_t)bk * p.capacity;
@@ -711,7 +718,7 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
         lsum = fmaf(o[GC + h], sc, lsum);
       }
     }
-    float* part = p.ws_part + (((int64_t)b * p.hq + h0 + h) * p.n_split + p.split_base + blockIdx.x) * kPartFloats;
+    float* part = p.ws_part + (((int64_t)b * p.hq + h0 + h) * p.n_split + p.split_base + split) * kPartFloats;
     part[2 + k] = acc;
     if (k == 0) {
       part[0] = M;
@@ -722,6 +729,28 @@ __global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
     const unsigned long long tot = n_skipped;  // wave-uniform
     if (lane == 0 && tot) atomicAdd(p.skipped, tot);
   }
+}
+
+template <int BKLO, int BKHI, int KSPLIT, int BVLO, int BVHI, int VSPLIT, bool VQ, int GC>
+__global__ __launch_bounds__(kThreads) void decode_scan(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) float lds[scan_lds_floats<BVLO, BVHI, VSPLIT, VQ, GC>()];
+  scan_body<BKLO, BKHI, KSPLIT, BVLO, BVHI, VSPLIT, VQ, GC>(p, lds, blockIdx.x);
+}
+
+// Two cache segments of different format pairs in one launch (decode over a decayed cache):
+// workgroups x < n0 scan segment 0 (format pair A, params p0), the others segment 1 (pair
+// B, params p1, split x - n0); p1.split_base = n0 puts both segments' partials side by side
+// for one combine.
+template <int A0, int A1, int A2, int A3, int A4, int A5, int B0, int B1, int B2, int B3, int B4,
+          int B5, int GC>
+__global__ __launch_bounds__(kThreads) void decode_scan_pair(DecodeParams p0, DecodeParams p1, int n0) {
+  constexpr int kA = scan_lds_floats<A3, A4, A5, true, GC>();
+  constexpr int kB = scan_lds_floats<B3, B4, B5, true, GC>();
+  __shared__ __attribute__((aligned(16))) float lds[kA > kB ? kA : kB];
+  if ((int)blockIdx.x < n0)
+    scan_body<A0, A1, A2, A3, A4, A5, true, GC>(p0, lds, blockIdx.x);
+  else
+    scan_body<B0, B1, B2, B3, B4, B5, true, GC>(p1, lds, blockIdx.x - n0);
 }
 
 template <int BKLO, int BKHI, int KS, int BVLO, int BVHI, int VS, bool VQ, int GC>
@@ -770,5 +799,18 @@ int launch_decode_combine(const DecodeParams& p, int rows, hipStream_t stream);
   extern template int launch_pair<a, b, c, d, e, f>(const DecodeParams&, bool, int, dim3, hipStream_t);
 TQ_DECODE_PAIRS(TQ_DECODE_EXTERN)
 #undef TQ_DECODE_EXTERN
+
+// Format-pair combinations (old segment, new segment) that decode over a decayed cache in
+// one launch (values with QJL, query-head groups of a multiple of 4): b3 / b3 tokens
+// before b4 / b4 ones, and 2.5-bit before 3.5-bit.
+#define TQ_DECAY_PAIRS(X) \
+  X(2, 2, 4, 2, 2, 4, 3, 3, 4, 3, 3, 4) \
+  X(2, 1, 2, 2, 1, 2, 3, 2, 2, 3, 2, 2)
+
+// Launch of the fused two-segment scan for combination A -> B (tq_decode_decay.hip).
+template <int A0, int A1, int A2, int A3, int A4, int A5, int B0, int B1, int B2, int B3, int B4,
+          int B5>
+int launch_scan_pair(const DecodeParams& p0, const DecodeParams& p1, int n0, dim3 grid,
+                     hipStream_t s);
 
 }  // namespace tqk

@@ -56,6 +56,12 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      hipStream_t stream, const tq_paged_src* paged = nullptr,
                      int32_t split_base = 0, int32_t split_total = 0, bool combine = true);
 
+// Two decode segments in one fused scan launch + one combine, when their format pairs have
+// a fused instance; TQ_ERR_SHAPE (nothing launched) otherwise.  Arguments checked by the caller.
+int tq_launch_decode_pair(const tq_cache_segment* segs, const void* q, int32_t q_dtype,
+                          int32_t batch, int32_t hq, int32_t hkv, float scale, float tau,
+                          float* out, int64_t* skipped, void* workspace, hipStream_t stream);
+
 struct tq_search_plan {
   int32_t n_chunks;       // database chunks scanned independently
   int64_t chunk_len;
