@@ -2,6 +2,7 @@
 closed forms, textbook tables, library routines it does not use, brute force on
 tiny inputs, invariants and Monte-Carlo against closed forms.  CPU only."""
 import math
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -501,3 +502,22 @@ def test_requantized_inner_products_stay_unbiased():
     se = vals.std(ddof=1) / math.sqrt(n_seeds)
     assert abs(vals.mean() - y @ xt) < 4 * se
 
+
+
+# ---------------------------------------------------------------------------- storage rate
+def test_storage_rate_matches_printed_figure():
+    """The bytes the oracle stores per vector (packed record + the two fp16 norms), per
+    value, against the rate the golden fixture copies from the page."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "storage_rate_b4.txt")
+    rows = [l.split() for l in open(path, encoding="utf-8") if l.strip() and not l.startswith("#")]
+    assert rows
+    for d, cbits, qbits, bpv, ratio in rows:
+        d, cbits, qbits, bpv, ratio = int(d), int(cbits), int(qbits), float(bpv), float(ratio)
+        fmt = O.Format.uniform(d, cbits, qjl=qbits == 1)
+        signs, S = TI.rotation(d, 5)
+        qz = O.quantize(TI.gen(6).standard_normal((3, d)), fmt, signs, S, O.codebook(d, cbits))
+        rec = O.pack(qz["idx"], qz["sbit"], fmt)
+        stored = rec.shape[1] + np.asarray(qz["n16"]).itemsize + np.asarray(qz["r16"]).itemsize
+        assert rec.shape == (3, fmt.record_bytes())
+        assert stored * 8 / d == bpv
+        assert round(16 / bpv, 1) == ratio
