@@ -6,8 +6,8 @@
 //
 // For a batch of queries the scores are a (vectors x coordinates) x (coordinates x queries)
 // product, so the scan runs on v_mfma_f32_16x16x32_f16 straight from the packed records:
-//   prologue: per query one workgroup: zero-pad to d, q_rot = H D q / sqrt(d), S q_rot
-//             (fp32, to the workspace).
+//   prologue: per query eight workgroups: zero-pad to d, q_rot = H D q / sqrt(d), and one
+//             eighth of the rows of S q_rot each (fp32, to the workspace).
 //   scan:     grid (block of 32 queries, database split), 4 waves.  Wave w owns the record
 //             blocks of coordinates [w d/4, (w + 1) d/4) of every 64-vector tile, for all 32
 //             queries: lane (j, r) loads block b of vector 16 m + r and expands byte j of its
@@ -25,7 +25,8 @@
 //             barrier per tile.  Concurrent workgroups walk the same database range, so the
 //             records come through the L2.
 //   merge:    per query, the lists of the database splits are merged (skipped when there is
-//             one split: the scan then writes the final result).
+//             one split: the scan then writes the final result); each wave sorts its first
+//             64 candidates whole and screens the rest against its k-th entry.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,6 +74,9 @@ struct SearchParams {
 };
 
 // ----------------------------------------------------------------------------- prologue
+// the query prologue's S q_rot rows are split over this many workgroups per query
+constexpr int kPrologueSlices = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void search_prologue(SearchParams p) {
   const int64_t qi = blockIdx.x;
@@ -111,22 +115,31 @@ __global__ __launch_bounds__(256) void search_prologue(SearchParams p) {
     for (int e = 0; e < NE; ++e) wv[0][lane + 64 * e] = v[e] * isd;
   }
   __syncthreads();
-  for (int r = tid; r < D; r += 256) {
-    const f32x4* row = reinterpret_cast<const f32x4*>(p.S + (int64_t)r * D);
-    float s = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < D / 4; ++k) {
-      const f32x4 a = row[k];
-      s = fmaf(a[0], wv[0][4 * k], s);
-      s = fmaf(a[1], wv[0][4 * k + 1], s);
-      s = fmaf(a[2], wv[0][4 * k + 2], s);
-      s = fmaf(a[3], wv[0][4 * k + 3], s);
-    }
-    wv[1][r] = s;
+  // S q_rot, rows [blockIdx.y kRows, +kRows) of it: kP consecutive threads share a row and
+  // each sums every kP-th 16-byte column group, so one load instruction reads whole rows
+  // and every load of a thread is in flight at once; the kP lanes then reduce by butterfly
+  constexpr int kRows = D / kPrologueSlices, kP = 256 / kRows, kC = D / (4 * kP);
+  static_assert(kRows * kP == 256 && kP <= 64 && kC >= 1, "prologue split");
+  const int r = (int)blockIdx.y * kRows + tid / kP, part = tid % kP;
+  const f32x4* row = reinterpret_cast<const f32x4*>(p.S + (int64_t)r * D);
+  f32x4 a[kC];
+#pragma unroll
+  for (int c = 0; c < kC; ++c) a[c] = row[part + kP * c];
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    const int col = 4 * (part + kP * c);
+    s = fmaf(a[c][0], wv[0][col], s);
+    s = fmaf(a[c][1], wv[0][col + 1], s);
+    s = fmaf(a[c][2], wv[0][col + 2], s);
+    s = fmaf(a[c][3], wv[0][col + 3], s);
   }
-  __syncthreads();
+#pragma unroll
+  for (int m = 1; m < kP; m <<= 1) s += __shfl_xor(s, m, 64);
   float* dq = p.ws_q + qi * 2 * D;
-  for (int j = tid; j < 2 * D; j += 256) dq[j] = wv[j / D][j % D];
+  if (part == 0) dq[D + r] = s;
+  if (blockIdx.y == 0)
+    for (int j = tid; j < D; j += 256) dq[j] = wv[0][j];
 }
 
 // a before b in the result order: larger score, then lower id
@@ -163,6 +176,28 @@ __device__ __forceinline__ void list_insert(float& ls, int64_t& li, float s, int
   } else if (lane == pos) {
     ls = s;
     li = id;
+  }
+}
+
+// Sorts the wave's 64 (score, id) pairs into result order, lane 0 first: a bitonic network
+// of lane-xor exchanges (ids travel as two 32-bit halves).
+__device__ __forceinline__ void wave_sort(float& s, int64_t& id) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const float os = __shfl_xor(s, stride, 64);
+      const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)id, stride, 64);
+      const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)((uint64_t)id >> 32), stride, 64);
+      const int64_t oi = (int64_t)(((uint64_t)ohi << 32) | olo);
+      // the lower lane of a pair keeps the better entry in blocks sorted first-to-last
+      const bool keep_better = ((lane & stride) == 0) == ((lane & size) == 0);
+      if (keep_better ? better(os, oi, s, id) : better(s, id, os, oi)) {
+        s = os;
+        id = oi;
+      }
+    }
   }
 }
 
@@ -449,8 +484,14 @@ __global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
-      const float sc = scr[r];
-      const int64_t id = idr[r];
+      float sc = scr[r];
+      int64_t id = idr[r];
+      if (r == 0 && c == c0) {  // the list is empty: the first batch, sorted, gives it
+        wave_sort(sc, id);
+        ms = lane < k ? sc : -INFINITY;
+        mi = lane < k ? id : INT64_MAX;
+        continue;
+      }
       uint64_t cand = __ballot(id != INT64_MAX && better(sc, id, lane_f(ms, k - 1), lane_i64(mi, k - 1)));
       while (cand) {
         const int L = __builtin_ctzll(cand);
@@ -632,7 +673,7 @@ __global__ __launch_bounds__(64 * kLWaves) void search_lut(SearchParams p) {
 
 template <int D, int B>
 static int launch_search(const SearchParams& p, int64_t n_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(search_prologue<D>, dim3((unsigned)p.n_q), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(search_prologue<D>, dim3((unsigned)p.n_q, kPrologueSlices), dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   if (p.n_q <= kLutQ)
     hipLaunchKernelGGL((search_lut<D, B>), dim3((unsigned)p.n_split, (unsigned)p.n_q),
