@@ -84,7 +84,7 @@ def _traffic(kernel_srcs, summary: str):
         return None
 
 
-def cpu_baseline(kb, vb, qb, signs, S):
+def cpu_baseline(kb, vb, qb, rot_seed):
     """The oracle as it stands, on the host cores, over the same layer (about 15 s of CPU
     work): quantize + pack the keys and values of all 8 KV heads x 32768 tokens, then one
     decode step of attention for the 32 query heads."""
@@ -93,6 +93,7 @@ def cpu_baseline(kb, vb, qb, signs, S):
     from oracle import tq_oracle as O
     from parity_utils import oracle_decode, oracle_pack_cache
     import tq_inputs as TI
+    signs, S = O.make_rotation(D, rot_seed)   # the oracle's own draws of the same rotation
     nt, nh = NTOK, HKV
     fmt = O.Format.uniform(D, BITS)
     t0 = time.perf_counter()
@@ -386,7 +387,7 @@ def _large_layer(tq, torch, dev, TI, cfg, batch, ntok, fk, fv, spikes):
     seed = TI.data_seed(cfg)
     kb, vb, _ = TI.kv_layer(batch, HKV, ntok, D, seed=seed, spike_frac=spikes)
     qb = TI.decode_queries(batch, HQ, D, seed)
-    signs, S = TI.rotation(D, TI.rotation_seed(cfg))
+    signs, S = tq.make_rotation(D, TI.rotation_seed(cfg))
     Sd = torch.from_numpy(S).to(dev)
     tk, tv = tq.Tables(fk, signs, Sd), tq.Tables(fv, signs, Sd)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -474,7 +475,7 @@ def _search_timing(tq, torch, dev, TI, reps=2):
     n_db, n_q, d_in, d, k = 10 ** 6, 10 ** 4, 200, 256, 10
     db = torch.from_numpy(TI.search_set(n_db, d_in, seed=TI.data_seed(5))).to(dev)
     qs = torch.from_numpy(TI.search_set(n_q, d_in, seed=TI.data_seed(5) + 1)).to(dev)
-    signs, S = TI.rotation(d, TI.rotation_seed(5))
+    signs, S = tq.make_rotation(d, TI.rotation_seed(5))
     fmt = tq.Format.uniform(d, BITS)
     tab = tq.Tables(fmt, signs, torch.from_numpy(S).to(dev))
     codes = torch.empty((n_db, fmt.record_bytes()), dtype=torch.uint8, device=dev)
@@ -543,7 +544,7 @@ def main():
     seed = TI.data_seed(2)
     kb, vb, _ = TI.kv_layer(BATCH, HKV, NTOK, D, seed=seed)
     qb = TI.decode_queries(BATCH, HQ, D, seed)
-    signs, S = TI.rotation(D, TI.rotation_seed(2))
+    signs, S = tq.make_rotation(D, TI.rotation_seed(2))
     fmt = tq.Format.uniform(D, BITS)
     tab = tq.Tables(fmt, signs, torch.from_numpy(S).to(dev))
     rb = fmt.record_bytes()
@@ -653,7 +654,7 @@ def main():
     # other formats of the same layer (not part of `value`)
     if args.no_variants:
         if not args.no_cpu_baseline:
-            line["cpu_baseline"] = cpu_baseline(kb, vb, qb, signs, S)
+            line["cpu_baseline"] = cpu_baseline(kb, vb, qb, TI.rotation_seed(2))
         print(json.dumps(line), flush=True)
         return
     line["variants"] = {
@@ -674,7 +675,7 @@ def main():
         steps)
     line["variants"]["search_1m_x_200"] = _search_timing(tq, torch, dev, TI)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(kb, vb, qb, signs, S)
+        line["cpu_baseline"] = cpu_baseline(kb, vb, qb, TI.rotation_seed(2))
     print(json.dumps(line), flush=True)
 
 

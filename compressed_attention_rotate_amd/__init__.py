@@ -14,9 +14,9 @@ import math
 import numpy as np
 
 from ._lib import (LIB_PATH, TQ_BF16, TQ_F16, TQ_F32, Format, Tables, TQError, build_codebook,
-                   load, c_cache_segment)
+                   load, c_cache_segment, make_rotation)
 
-__all__ = ["Format", "Tables", "TQError", "build_codebook", "quantize_kv", "attend_decode",
+__all__ = ["Format", "Tables", "TQError", "build_codebook", "make_rotation", "quantize_kv", "attend_decode",
            "attend_decode_segments", "attend_segments_workspace_bytes",
            "ip_search", "requantize", "attend_workspace_bytes", "search_workspace_bytes",
            "requantize_workspace_bytes", "quantize_kv_paged", "attend_decode_paged",

@@ -56,6 +56,7 @@ def load() -> ctypes.CDLL:
         P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         sig = {
             "tq_build_codebook": (ctypes.c_int, [I32, I32, P, P, P]),
+            "tq_make_rotation": (ctypes.c_int, [I32, ctypes.c_uint64, P, P]),
             "tq_record_bytes": (I64, [P]),
             "tq_check_format": (ctypes.c_int, [P]),
             "tq_quantize_kv": (ctypes.c_int, [P, P, P, I32, I64, I32, I64, P, P, P, P]),
@@ -135,10 +136,20 @@ def build_codebook(d: int, bits: int):
     return c, b, mse.value
 
 
+def make_rotation(d: int, seed: int):
+    """Seeded rotation draws from tq_make_rotation: (signs int8 [d], S fp32 [d, d]), host."""
+    signs = np.zeros(d, dtype=np.int8)
+    S = np.zeros((d, d), dtype=np.float32)
+    _check(load().tq_make_rotation(d, ctypes.c_uint64(int(seed) & (2**64 - 1)), signs.ctypes.data,
+                                   S.ctypes.data), "tq_make_rotation")
+    return signs, S
+
+
 @dataclass
 class Tables:
     """Rotation and codebooks for one format.  signs: host int8 [d]; S: device fp32 [d, d]
-    (a torch tensor); codebooks default to tq_build_codebook's."""
+    (a torch tensor); codebooks default to tq_build_codebook's.  ``Tables.from_seed`` makes
+    the rotation with tq_make_rotation."""
     fmt: Format
     signs: np.ndarray
     S: "object"
@@ -159,6 +170,12 @@ class Tables:
                 self.centroids_hi, self.bounds_hi, _ = build_codebook(self.fmt.d, self.fmt.bits_hi)
         for name in ("centroids_lo", "bounds_lo", "centroids_hi", "bounds_hi"):
             setattr(self, name, np.ascontiguousarray(getattr(self, name), dtype=np.float32))
+
+    @staticmethod
+    def from_seed(fmt: Format, seed: int, device="cuda") -> "Tables":
+        import torch
+        signs, S = make_rotation(fmt.d, seed)
+        return Tables(fmt, signs, torch.from_numpy(S).to(device))
 
     def c(self) -> c_tables:
         S = self.S

@@ -71,15 +71,12 @@ uintptr_t dtype_size(int dt) { return dt == TQ_F32 ? 4 : 2; }
 }  // namespace
 
 int tq_num_cus() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  if (cache[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    cache[dev] = n;
-  }
-  return cache[dev];
+  // asked of the runtime on every call (it keeps the device properties), so the library
+  // holds no mutable state of its own here
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return n;
 }
 
 extern "C" {

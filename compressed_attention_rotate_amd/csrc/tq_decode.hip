@@ -7,14 +7,15 @@ namespace tqk {
 
 // ----------------------------------------------------------------------------- combine
 // One workgroup per (batch, query head): every load it needs (S_v column slices, the
-// split maxima, the first 32 splits' partial sums) is issued before the first use.
+// split maxima, the first 32 splits' partial sums) is issued before the first use.  The
+// splits are merged in index order; each split's weight 2^(m_i - M) is recomputed where it
+// is used, so any number of partials fits (segmented caches add theirs up).
 constexpr int kCombChunk = 32;
 
 __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  __shared__ float scl[1024];
-  __shared__ float red[8];
+  __shared__ float red[4];
   __shared__ float vec[2][kD];
   __shared__ float part_s[256];
   const float* parts = p.ws_part + (int64_t)bh * p.n_split * kPartFloats;
@@ -33,32 +34,28 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   if (lane == 0) red[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float lpart = 0.0f;
-  for (int i = tid; i < np; i += 256) {
-    const float m = parts[(int64_t)i * kPartFloats];
-    const float s = (m == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(m - M);
-    scl[i] = s;
-    lpart += s * parts[(int64_t)i * kPartFloats + 1];
-  }
-  lpart = wave_sum_fast(lpart);
-  __syncthreads();
-  if (lane == 0) red[4 + wave] = lpart;
-  // thread tid: component tid / 128 (A or Q), coordinate tid % 128; fixed order over splits
-  float acc = 0.0f;
+  // thread tid: component tid / 128 (A or Q), coordinate tid % 128; fixed order over splits.
+  // Every thread also forms the denominator L in the same order (uniform loads).
+  float acc = 0.0f, Ltot = 0.0f;
+  for (int c0 = 0; c0 < np; c0 += kCombChunk) {
+    if (c0 > 0) {
 #pragma unroll
-  for (int c = 0; c < kCombChunk; ++c)
-    if (c < np) acc = fmaf(pv[c], scl[c], acc);
-  for (int c0 = kCombChunk; c0 < np; c0 += kCombChunk) {
+      for (int c = 0; c < kCombChunk; ++c)
+        pv[c] = c0 + c < np ? parts[(int64_t)(c0 + c) * kPartFloats + 2 + tid] : 0.0f;
+    }
 #pragma unroll
-    for (int c = 0; c < kCombChunk; ++c)
-      pv[c] = c0 + c < np ? parts[(int64_t)(c0 + c) * kPartFloats + 2 + tid] : 0.0f;
-#pragma unroll
-    for (int c = 0; c < kCombChunk; ++c)
-      if (c0 + c < np) acc = fmaf(pv[c], scl[c0 + c], acc);
+    for (int c = 0; c < kCombChunk; ++c) {
+      if (c0 + c < np) {
+        const float m = parts[(int64_t)(c0 + c) * kPartFloats];
+        const float l = parts[(int64_t)(c0 + c) * kPartFloats + 1];
+        const float s = (m == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(m - M);
+        acc = fmaf(pv[c], s, acc);
+        Ltot = fmaf(s, l, Ltot);
+      }
+    }
   }
   vec[half][j] = acc;
   __syncthreads();
-  const float Ltot = (red[4] + red[5]) + (red[6] + red[7]);
   // S^T Q: thread (j, half) sums its 64 rows
   {
     float s = 0.0f;

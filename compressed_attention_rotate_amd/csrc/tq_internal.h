@@ -5,7 +5,7 @@
 
 #include "tq.h"
 
-// Compute units of the current device (cached per device); <= 0 on failure.
+// Compute units of the current device; <= 0 on failure.
 int tq_num_cus();
 
 // Paged destination of a quantize launch: vector v = token * page_heads + head is written

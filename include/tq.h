@@ -101,6 +101,23 @@ typedef struct tq_tables {
  * Errors: TQ_ERR_ARG, TQ_ERR_SHAPE, TQ_ERR_NOCONV. */
 int tq_build_codebook(int32_t d, int32_t bits, float* centroids, float* bounds, double* mse);
 
+/* Seeded draws of the rotation: the +-1 diagonal D of y = H (D x) / sqrt(d) and the d x d
+ * Gaussian JL matrix S (163.com explainer, sections "第一步：PolarQuant" (random rotation)
+ * and "第二步：QJL" (JL transform of the residual)).  The pages name no generator; this one
+ * is counter-based, so (d, seed) names the same tables on every machine:
+ *   x_k  = output k of SplitMix64 started at state `seed`;  u(x) = (x >> 11) * 2^-53;
+ *   signs[i] = +1 if the top bit of x_i is 0, else -1 (i = 0 .. d-1);
+ *   then, for the entries of S in row-major order two at a time, the next two draws give
+ *   u1 = 1 - u(x_a), u2 = u(x_b), and in fp64 (Box-Muller) r = sqrt(-2 ln u1),
+ *   a = 2 pi u2; S[2k] = fp32(r cos a), S[2k+1] = fp32(r sin a), rounded to nearest even.
+ * Host only, synchronous, deterministic.  The caller copies S to device memory for
+ * tq_tables.S.
+ *   d     : power of two, 8 <= d <= 4096
+ *   signs : out, host, d int8 entries (+1 / -1)
+ *   S     : out, host, d * d fp32, row-major
+ * Errors: TQ_ERR_SHAPE (d), TQ_ERR_ARG (null pointer). */
+int tq_make_rotation(int32_t d, uint64_t seed, int8_t* signs, float* S);
+
 /* Bytes of one packed vector's code words (norms excluded); < 0 on a bad format. */
 int64_t tq_record_bytes(const tq_format* fmt);
 

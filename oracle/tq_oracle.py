@@ -91,6 +91,54 @@ def unrotate(y: np.ndarray, signs: np.ndarray) -> np.ndarray:
     return (np.asarray(y, dtype=np.float64) @ H) / math.sqrt(d) * signs.astype(np.float64)
 
 
+# The seeded draws of a rotation.  The pages fix a random sign flip before the Hadamard
+# transform and a Gaussian JL matrix for the residual (163.com explainer, sections
+# "第一步：PolarQuant" and "第二步：QJL") but no generator.  Reading: SplitMix64
+# (Steele, Lea and Flood, 2014) from the seed for the raw 64-bit draws; u = (x >> 11) 2^-53;
+# sign i is -1 exactly when draw i has its top bit set; S in row-major order from
+# Box-Muller (1958) pairs in fp64 with u1 = 1 - u (so log never sees 0), each entry rounded
+# once to fp32.  Written here with Python integers and the math module, one value at a time.
+_SM64_GAMMA = 0x9E3779B97F4A7C15
+_SM64_M1 = 0xBF58476D1CE4E5B9
+_SM64_M2 = 0x94D049BB133111EB
+_U64 = (1 << 64) - 1
+_ROT_CACHE: dict = {}
+
+
+def splitmix64(seed: int, count: int) -> list:
+    """The first ``count`` outputs of SplitMix64 started at state ``seed``."""
+    state = seed & _U64
+    out = []
+    for _ in range(count):
+        state = (state + _SM64_GAMMA) & _U64
+        z = state
+        z = ((z ^ (z >> 30)) * _SM64_M1) & _U64
+        z = ((z ^ (z >> 27)) * _SM64_M2) & _U64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def make_rotation(d: int, seed: int):
+    """(signs int8 [d], S fp32 [d, d]) for one seed, by the reading stated above."""
+    key = (d, seed & _U64)
+    if key not in _ROT_CACHE:
+        draws = splitmix64(seed, d + d * d)
+        signs = np.array([-1 if (x >> 63) else 1 for x in draws[:d]], dtype=np.int8)
+        vals = []
+        for k in range(d, d + d * d, 2):
+            u1 = 1.0 - (draws[k] >> 11) * 2.0 ** -53
+            u2 = (draws[k + 1] >> 11) * 2.0 ** -53
+            r = math.sqrt(-2.0 * math.log(u1))
+            a = (2.0 * math.pi) * u2
+            vals.append(r * math.cos(a))
+            vals.append(r * math.sin(a))
+        S = np.array(vals, dtype=np.float64).astype(np.float32).reshape(d, d)
+        signs.setflags(write=False)
+        S.setflags(write=False)
+        _ROT_CACHE[key] = (signs, S)
+    return _ROT_CACHE[key]
+
+
 # --------------------------------------------------------------------------------------
 # Codebook: Lloyd-Max for the marginal law of one rotated unit-vector coordinate
 # --------------------------------------------------------------------------------------
@@ -420,33 +468,9 @@ def attend(q, k_tilde, v_tilde, scale: float, tau: float = 0.0):
     return out, logits, p, int(np.sum(~keep)), float(np.sum(p[~keep]))
 
 
-def decode_head(q, k_rec, k_norms, v_rec, v_norms, fmt_k, fmt_v, signs_k, S_k, cbk_lo, cbk_hi,
-                signs_v, S_v, cbv_lo, cbv_hi, scale, tau=0.0):
-    """One query head over one KV head's packed cache (records [L, bytes], norms [L, 2] uint16)."""
-    ik, sk = unpack(k_rec, fmt_k)
-    iv, sv = unpack(v_rec, fmt_v)
-    kt = dequantize(ik, sk, k_norms[:, 0], k_norms[:, 1], fmt_k, signs_k, S_k, cbk_lo, cbk_hi)
-    vt = dequantize(iv, sv, v_norms[:, 0], v_norms[:, 1], fmt_v, signs_v, S_v, cbv_lo, cbv_hi)
-    out, logits, p, nd, dm = attend(q, kt, vt, scale, tau)
-    est, est_scale = estimator_dot(q, ik, sk, k_norms[:, 0], k_norms[:, 1], fmt_k, signs_k, S_k,
-                                   cbk_lo, cbk_hi)
-    return dict(out=out, logits=logits, p=p, n_dropped=nd, dropped_mass=dm,
-                logit_scale=est_scale * scale, logits_fused=est * scale)
-
-
 # --------------------------------------------------------------------------------------
 # Compressed inner-product search
 # --------------------------------------------------------------------------------------
-def topk(scores: np.ndarray, k: int):
-    """Top-k of each row by score, larger first; equal scores go to the lower index."""
-    scores = np.atleast_2d(scores)
-    ids = np.empty((scores.shape[0], k), dtype=np.int64)
-    for r in range(scores.shape[0]):
-        order = np.lexsort((np.arange(scores.shape[1]), -scores[r]))
-        ids[r] = order[:k]
-    return ids, np.take_along_axis(scores, ids, axis=1)
-
-
 def search_scores(queries, x_tilde):
     """Estimated inner products <q, x~_i> (queries zero-padded to the dequantized width)."""
     qd = np.zeros((queries.shape[0], x_tilde.shape[1]))
@@ -455,6 +479,8 @@ def search_scores(queries, x_tilde):
 
 
 def recall_at_k(est_ids: np.ndarray, exact_ids: np.ndarray) -> float:
+    """Mean over queries of |est & exact| / k (recall@k of the estimated top-k against the
+    exact top-k; 163.com explainer, section "向量搜索", compares methods by this recall)."""
     k = exact_ids.shape[1]
     hits = [len(set(a.tolist()) & set(b.tolist())) for a, b in zip(est_ids, exact_ids)]
     return float(np.mean(hits)) / k

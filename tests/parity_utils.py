@@ -11,6 +11,15 @@ import tq_inputs as TI
 from oracle import tq_oracle as O
 
 
+def rotations(d, seed):
+    """Rotation draws for one seed, made by two independent implementations of one
+    definition: the oracle's ``make_rotation`` (for the oracle side) and the library's
+    ``tq_make_rotation`` (for the tables the GPU path reads).  tests/test_rotation.py pins
+    them equal bit for bit.  Returns ((signs, S) oracle, (signs, S) library)."""
+    import compressed_attention_rotate_amd as tq
+    return O.make_rotation(d, seed), tq.make_rotation(d, seed)
+
+
 def oracle_codebooks(d, bits_lo, bits_hi):
     return O.codebook(d, bits_lo), O.codebook(d, bits_hi)
 
@@ -132,3 +141,32 @@ def oracle_decode(q64, rec_k, nrm_k, rec_v, nrm_v, seq_lens, fmt_k, fmt_v, signs
                 logits[(bi, h)], scales[(bi, h)] = lg, esc * scale
                 drops[(bi, h)], masses[(bi, h)] = nd, dm
     return out, logits, scales, drops, masses
+
+
+def oracle_search_chunk(args):
+    """One chunk of a search database through the oracle, for a process pool: quantize and
+    pack the rows, then score them for each query with the oracle's fused estimator.
+    args = (rows fp32 [n, d_in], queries fp32 [nq, d_in], d, bits, rotation seed).  Returns
+    (records, norms, scores [nq, n], absolute-sum scales [nq, n], ambiguous [n])."""
+    from threadpoolctl import threadpool_limits
+    x, queries, d, bits, seed = args
+    with threadpool_limits(1):
+        return _oracle_search_chunk(x, queries, d, bits, seed)
+
+
+def _oracle_search_chunk(x, queries, d, bits, seed):
+    fmt = O.Format.uniform(d, bits)
+    signs, S = O.make_rotation(d, seed)
+    cb = O.codebook(d, bits)
+    qz = O.quantize(np.asarray(x, dtype=np.float64), fmt, signs, S, cb)
+    rec = O.pack(qz["idx"], qz["sbit"], fmt)
+    scores = np.empty((len(queries), len(x)))
+    scales = np.empty((len(queries), len(x)))
+    for i, q in enumerate(queries):
+        qp = np.zeros(d)
+        qp[:len(q)] = q
+        scores[i], scales[i] = O.estimator_dot(qp, qz["idx"], qz["sbit"], qz["n16"], qz["r16"],
+                                               fmt, signs, S, cb)
+    amb = qz["amb_code"].any(axis=1) | qz["amb_sign"].any(axis=1)
+    norms = np.stack([qz["n16"], qz["r16"]], axis=1).astype(np.uint16)
+    return rec, norms, scores, scales, amb

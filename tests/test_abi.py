@@ -264,3 +264,12 @@ def test_paged_validation_before_launch():
     assert D(wb=wsb - 1) == E.TQ_ERR_WORKSPACE
     assert tq.attend_workspace_bytes(1, 32, 8, 64 * 64) > wsb
     assert D(mb=64) == E.TQ_ERR_WORKSPACE              # the capacity grows with max_blocks
+
+
+def test_segments_plan_sizes_every_split_partial():
+    """Eight segments of 131072 tokens at batch 1 with one KV head: every segment keeps its
+    own 256 splits (2048 partials per query head, merged by one combine) and the workspace
+    holds all of them."""
+    per = 256 * 4 * (2 + 2 * 128) * 4
+    assert tq.attend_segments_workspace_bytes(1, 4, 1, [131072] * 8) == 8 * per
+    assert tq.attend_workspace_bytes(1, 4, 1, 131072) == per

@@ -9,7 +9,7 @@ import pytest
 
 import tq_inputs as TI
 from oracle import tq_oracle as O
-from parity_utils import oracle_decode, oracle_pack_cache
+from parity_utils import oracle_decode, oracle_pack_cache, rotations
 
 pytestmark = pytest.mark.gpu
 
@@ -65,12 +65,12 @@ def _case(torch, batch, hq, hkv, ntok, seq_lens, fk, fv, seed, q_dtype="bf16", s
     d = 128
     kb, vb, _ = TI.kv_layer(batch, hkv, ntok, d, seed=seed, spike_frac=spikes)
     q_bits = TI.decode_queries(batch, hq, d, seed)
-    signs, S = TI.rotation(d, seed + 500000)
+    (signs, S), (gsigns, gS) = rotations(d, seed + 500000)
     rk, nk, _ = oracle_pack_cache(kb, O.Format(*fk), signs, S, bf16=True)
     rv, nv, _ = oracle_pack_cache(vb, O.Format(*fv), signs, S, bf16=True)
     q64 = TI.bf16_to_f64(q_bits)
     out_g, lg_g, skipped = _gpu_decode(torch, q_bits, q_dtype, rk, nk, rv, nv, seq_lens, fk, fv,
-                                       signs, S, signs, S, tau=tau)
+                                       gsigns, gS, gsigns, gS, tau=tau)
     out_o, lg_o, sc_o, dr, dm = oracle_decode(q64, rk, nk, rv, nv, seq_lens, O.Format(*fk),
                                               O.Format(*fv), signs, S, signs, S,
                                               1 / math.sqrt(d), 0.0)
@@ -134,13 +134,13 @@ def test_single_head_64_queries(torch_gpu):
     torch = torch_gpu
     k, v, q, _ = TI.c1_inputs(seed=1000)
     d = 128
-    signs, S = TI.rotation(d, TI.rotation_seed(1))
+    (signs, S), (gsigns, gS) = rotations(d, TI.rotation_seed(1))
     fmt = O.Format(128, 2, 2, 128)
     rk, nk, _ = oracle_pack_cache(k.astype(np.float64)[None, None], fmt, signs, S)
     rv, nv, _ = oracle_pack_cache(v.astype(np.float64)[None, None], fmt, signs, S)
     q3 = q[None]                                                       # [1, 64, 128]
     out_g, lg_g, _ = _gpu_decode(torch, q3, "f32", rk, nk, rv, nv, [4096], (128, 2, 2, 128),
-                                 (128, 2, 2, 128), signs, S, signs, S)
+                                 (128, 2, 2, 128), gsigns, gS, gsigns, gS)
     out_o, lg_o, sc_o, _, _ = oracle_decode(q3.astype(np.float64), rk, nk, rv, nv, [4096], fmt, fmt,
                                             signs, S, signs, S, 1 / math.sqrt(d))
     worst, dmax = _compare(out_g, lg_g, out_o, lg_o, sc_o, [4096])
@@ -168,8 +168,8 @@ def test_workspace_reuse(torch_gpu):
     torch = torch_gpu
     d, seed = 128, TI.data_seed(2) + 31
     fmt = tq.Format.uniform(d, 3)
-    signs, S = TI.rotation(d, seed + 500000)
-    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    (signs, S), (gsigns, gS) = rotations(d, seed + 500000)
+    tab = tq.Tables(fmt, gsigns, torch.from_numpy(gS).cuda())
     cases = [(1, 32, 8, 4096, [4096]), (2, 8, 2, 3000, [3000, 17]), (1, 32, 8, 4096, [1000]),
              (3, 16, 4, 700, [0, 700, 333])]
     ws_bytes = max(tq.attend_workspace_bytes(b, hq, hkv, n) for b, hq, hkv, n, _ in cases)
@@ -203,10 +203,10 @@ def _full_size_sampled(torch, batch, hq, hkv, ntok, fk, fv, seed, spikes, tau, u
     d, G = 128, hq // hkv
     kb, vb, _ = TI.kv_layer(batch, hkv, ntok, d, seed=seed, spike_frac=spikes)
     q_bits = TI.decode_queries(batch, hq, d, seed)
-    signs, S = TI.rotation(d, seed + 500000)
+    (signs, S), (gsigns, gS) = rotations(d, seed + 500000)
     fmt_k, fmt_v = tq.Format(*fk), tq.Format(*fv)
-    Sd = torch.from_numpy(S).cuda()
-    tk, tv = tq.Tables(fmt_k, signs, Sd), tq.Tables(fmt_v, signs, Sd)
+    Sd = torch.from_numpy(gS).cuda()
+    tk, tv = tq.Tables(fmt_k, gsigns, Sd), tq.Tables(fmt_v, gsigns, Sd)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
     rbk, rbv = fmt_k.record_bytes(), fmt_v.record_bytes()
     ck, nk = tq.quantize_kv(bf(kb).view(-1, d), fmt_k, tk)

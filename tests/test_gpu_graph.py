@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import tq_inputs as TI
+from parity_utils import rotations
 
 pytestmark = pytest.mark.gpu
 
@@ -25,9 +26,9 @@ def test_quantize_and_decode_replay_in_a_graph(torch_gpu):
     d, hq, hkv, n = 128, 8, 2, 1000
     kb, vb, _ = TI.kv_layer(1, hkv, n, d, seed=4401)
     qb = TI.decode_queries(1, hq, d, 4401)
-    signs, S = TI.rotation(d, 4402)
+    (signs, S), (gsigns, gS) = rotations(d, 4402)
     fmt = tq.Format.uniform(d, 3)
-    tab = tq.Tables(fmt, signs, torch.from_numpy(S).to(dev))
+    tab = tq.Tables(fmt, gsigns, torch.from_numpy(gS).to(dev))
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     xk, xv, q = bf(kb).view(-1, d), bf(vb).view(-1, d), bf(qb)
     rb = fmt.record_bytes()

@@ -8,7 +8,8 @@ import pytest
 
 import tq_inputs as TI
 from oracle import tq_oracle as O
-from parity_utils import compare_quantize, oracle_decode, oracle_pack_cache, oracle_quantize
+from parity_utils import (compare_quantize, oracle_decode, oracle_pack_cache, oracle_quantize,
+                          rotations)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +53,7 @@ def _case(torch, fk, fv, page_size, seed, batch=2, hq=32, hkv=8, ntok=1000, seq=
     d = 128
     kb, vb, _ = TI.kv_layer(batch, hkv, ntok, d, seed=seed)
     qb = TI.decode_queries(batch, hq, d, seed)
-    signs, S = TI.rotation(d, seed + 1)
+    (signs, S), (gsigns, gS) = rotations(d, seed + 1)
     rk, nk, _ = oracle_pack_cache(kb, O.Format(*fk), signs, S, bf16=True)
     rv, nv, _ = oracle_pack_cache(vb, O.Format(*fv), signs, S, bf16=True)
     ck, nkp, bt = _paginate(rk, nk, seq, page_size, seed + 2, holes)
@@ -60,8 +61,8 @@ def _case(torch, fk, fv, page_size, seed, batch=2, hq=32, hkv=8, ntok=1000, seq=
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     f16 = lambda a: dev(a.view(np.int16)).view(torch.float16)
     fmt_k, fmt_v = tq.Format(*fk), tq.Format(*fv)
-    tk = tq.Tables(fmt_k, signs, torch.from_numpy(S).cuda())
-    tv = tq.Tables(fmt_v, signs, torch.from_numpy(S).cuda())
+    tk = tq.Tables(fmt_k, gsigns, torch.from_numpy(gS).cuda())
+    tv = tq.Tables(fmt_v, gsigns, torch.from_numpy(gS).cuda())
     q = dev(qb.view(np.int16)).view(torch.bfloat16)
     sl = dev(np.asarray(seq, np.int32))
     out_p, lg_p = tq.attend_decode_paged(q, dev(ck), f16(nkp), dev(cv), f16(nvp), dev(bt), sl, fmt_k, tk,
@@ -120,9 +121,9 @@ def test_paged_append_writes_only_its_slots(torch_gpu):
     d, hkv, page, n_pages, n_tok = 128, 4, 64, 12, 333
     kb, _, _ = TI.kv_layer(1, hkv, n_tok, d, seed=7300)
     x = np.ascontiguousarray(np.transpose(kb[0], (1, 0, 2)))          # [token][head][d]
-    signs, S = TI.rotation(d, 7301)
+    (signs, S), (gsigns, gS) = rotations(d, 7301)
     fmt = tq.Format.uniform(d, 3)
-    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    tab = tq.Tables(fmt, gsigns, torch.from_numpy(gS).cuda())
     g = TI.gen(7302)
     slots = g.permutation(n_pages * page)[:n_tok].astype(np.int64)
     slots[::17] = -1                                                  # padding tokens
@@ -158,9 +159,9 @@ def test_paged_full_context_equals_contiguous(torch_gpu):
     d, hq, hkv, n, page = 128, 32, 8, 32768, 128
     kb, vb, _ = TI.kv_layer(1, hkv, n, d, seed=TI.data_seed(2))
     qb = TI.decode_queries(1, hq, d, TI.data_seed(2))
-    signs, S = TI.rotation(d, TI.rotation_seed(2))
+    (signs, S), (gsigns, gS) = rotations(d, TI.rotation_seed(2))
     fmt = tq.Format.uniform(d, 3)
-    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    tab = tq.Tables(fmt, gsigns, torch.from_numpy(gS).cuda())
     k0 = torch.from_numpy(kb.view(np.int16)).cuda().view(torch.bfloat16)
     v0 = torch.from_numpy(vb.view(np.int16)).cuda().view(torch.bfloat16)
     ck, nk = tq.quantize_kv(k0.view(-1, d), fmt, tab)
@@ -191,7 +192,7 @@ def _prefill_case(torch, start, n_new, seed, page=64, hq=32, hkv=8, fk=(128, 3, 
     total = start + n_new
     kb, vb, _ = TI.kv_layer(1, hkv, total, d, seed=seed)
     qb = TI.decode_queries(n_new, hq, d, seed)                       # one query row per new token
-    signs, S = TI.rotation(d, seed + 1)
+    (signs, S), (gsigns, gS) = rotations(d, seed + 1)
     rk, nk, _ = oracle_pack_cache(kb, O.Format(*fk), signs, S, bf16=True)
     rv, nv, _ = oracle_pack_cache(vb, O.Format(*fv), signs, S, bf16=True)
     mb = (total + page - 1) // page + 1
@@ -208,8 +209,8 @@ def _prefill_case(torch, start, n_new, seed, page=64, hq=32, hkv=8, fk=(128, 3, 
         nkc[pg, :, off], nvc[pg, :, off] = nk[0, :, t], nv[0, :, t]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     f16 = lambda a: dev(a.view(np.int16)).view(torch.float16)
-    tk = tq.Tables(fmt_k, signs, torch.from_numpy(S).cuda())
-    tv = tq.Tables(fmt_v, signs, torch.from_numpy(S).cuda())
+    tk = tq.Tables(fmt_k, gsigns, torch.from_numpy(gS).cuda())
+    tv = tq.Tables(fmt_v, gsigns, torch.from_numpy(gS).cuda())
     new_k = np.ascontiguousarray(np.transpose(kb[0, :, start:], (1, 0, 2)))   # [n_new][hkv][d]
     new_v = np.ascontiguousarray(np.transpose(vb[0, :, start:], (1, 0, 2)))
     bf = lambda a: dev(a.view(np.int16)).view(torch.bfloat16)
@@ -268,8 +269,8 @@ def test_prefill_rejects_a_chunk_past_the_pages_and_writes_nothing(torch_gpu):
     torch = torch_gpu
     import compressed_attention_rotate_amd as tq
     fmt = tq.Format.uniform(128, 3)
-    signs, S = TI.rotation(128, 1)
-    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    (signs, S), (gsigns, gS) = rotations(128, 1)
+    tab = tq.Tables(fmt, gsigns, torch.from_numpy(gS).cuda())
     ck = torch.full((4, 8, 64, fmt.record_bytes()), 0x5A, dtype=torch.uint8, device="cuda")
     nk = torch.zeros((4, 8, 64, 2), dtype=torch.float16, device="cuda")
     cv, nv = ck.clone(), nk.clone()
@@ -280,3 +281,75 @@ def test_prefill_rejects_a_chunk_past_the_pages_and_writes_nothing(torch_gpu):
         tq.prefill_paged(q, kn, kn, 120, ck, nk, cv, nv, table, fmt, tab)
     torch.cuda.synchronize()
     assert bool((ck == 0x5A).all()) and bool((cv == 0x5A).all())
+
+
+def test_prefill_512_token_chunk_over_32k_context(torch_gpu):
+    """The prefill chunk as the layer benchmark runs it: 512 new tokens after 32256 cached
+    ones (32 query / 8 KV heads, b = 4, 128-token pages in shuffled order).  The cached past
+    is arbitrary packed bytes (cross-fed: the same bytes in the GPU cache and in the
+    oracle); the chunk's keys and values are quantized by the GPU inside the call and by the
+    oracle from the same inputs.  Sampled query rows of the chunk must get the oracle's causal
+    attention over tokens 0 .. start + i within 2e-3."""
+    import compressed_attention_rotate_amd as tq
+    torch = torch_gpu
+    hq, hkv, d, page, start, n_new = 32, 8, 128, 128, 32256, 512
+    total = start + n_new
+    fk = O.Format(128, 3, 3, 128)
+    g = TI.gen(7900)
+    rb = fk.record_bytes()
+    past_k = g.integers(0, 256, (hkv, start, rb), dtype=np.uint8)
+    past_v = g.integers(0, 256, (hkv, start, rb), dtype=np.uint8)
+    pnk = np.stack([O.fp16_bits(g.uniform(20.0, 60.0, (hkv, start))),
+                    O.fp16_bits(g.uniform(1.0, 8.0, (hkv, start)))], axis=-1)
+    pnv = np.stack([O.fp16_bits(g.uniform(20.0, 60.0, (hkv, start))),
+                    O.fp16_bits(g.uniform(1.0, 8.0, (hkv, start)))], axis=-1)
+    kb, vb, _ = TI.kv_layer(1, hkv, n_new, d, seed=7901)           # the chunk's keys and values
+    qb = TI.decode_queries(n_new, hq, d, 7901)
+    (signs, S), (gsigns, gS) = rotations(d, 7902)
+    mb = total // page
+    n_pages = mb + 3
+    table = TI.gen(7903).permutation(n_pages)[:mb].astype(np.int32)
+    ck = np.full((n_pages, hkv, page, rb), 0x5A, np.uint8)
+    cv = np.full((n_pages, hkv, page, rb), 0x5A, np.uint8)
+    nkc = np.zeros((n_pages, hkv, page, 2), np.uint16)
+    nvc = np.zeros((n_pages, hkv, page, 2), np.uint16)
+    for blk in range(start // page):
+        sl = slice(blk * page, (blk + 1) * page)
+        ck[table[blk]], cv[table[blk]] = past_k[:, sl], past_v[:, sl]
+        nkc[table[blk]], nvc[table[blk]] = pnk[:, sl], pnv[:, sl]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    f16 = lambda a: dev(a.view(np.int16)).view(torch.float16)
+    bf = lambda a: dev(a.view(np.int16)).view(torch.bfloat16)
+    fmt = tq.Format.uniform(d, 3)
+    tab = tq.Tables(fmt, gsigns, torch.from_numpy(gS).cuda())
+    new_k = np.ascontiguousarray(np.transpose(kb[0], (1, 0, 2)))      # [n_new][hkv][d]
+    new_v = np.ascontiguousarray(np.transpose(vb[0], (1, 0, 2)))
+    out = tq.prefill_paged(bf(qb), bf(new_k), bf(new_v), start, dev(ck), f16(nkc), dev(cv),
+                           f16(nvc), dev(table), fmt, tab, fmt, tab)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    # the oracle's cache: the past bytes, then its own packing of the chunk
+    ok = oracle_quantize(kb[0].reshape(-1, d), fk, signs, S, bf16=True)
+    ov = oracle_quantize(vb[0].reshape(-1, d), fk, signs, S, bf16=True)
+    cbk = O.codebook(d, 3)
+    q64 = TI.bf16_to_f64(qb)
+    rows = [0, 1, 63, 200, 255, 256, 384, 511]
+    G = hq // hkv
+    worst = 0.0
+    for kh in range(hkv):
+        rk = np.concatenate([past_k[kh], ok["records"].reshape(hkv, n_new, rb)[kh]])
+        rv = np.concatenate([past_v[kh], ov["records"].reshape(hkv, n_new, rb)[kh]])
+        nk = np.concatenate([pnk[kh], ok["norms"].reshape(hkv, n_new, 2)[kh]])
+        nv = np.concatenate([pnv[kh], ov["norms"].reshape(hkv, n_new, 2)[kh]])
+        ik, sk = O.unpack(rk, fk)
+        iv, sv = O.unpack(rv, fk)
+        kt = O.dequantize(ik, sk, nk[:, 0], nk[:, 1], fk, signs, S, cbk)
+        vt = O.dequantize(iv, sv, nv[:, 0], nv[:, 1], fk, signs, S, cbk)
+        for i in rows:
+            L = start + i + 1
+            for gq in range(G):
+                h = kh * G + gq
+                o = O.attend(q64[i, h], kt[:L], vt[:L], 1 / math.sqrt(d))[0]
+                worst = max(worst, float(np.max(np.abs(out[i, h] - o))))
+    print(f"\nprefill 512 over 32K: max|out - oracle| {worst:.3g} on {len(rows)} sampled rows")
+    assert worst <= OUT_ATOL

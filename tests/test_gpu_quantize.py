@@ -5,7 +5,7 @@ import pytest
 
 import tq_inputs as TI
 from oracle import tq_oracle as O
-from parity_utils import compare_quantize, oracle_quantize, to_f64
+from parity_utils import compare_quantize, oracle_quantize, rotations, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -23,8 +23,8 @@ def _run(torch, x_np, dtype, fmt_t, seed, counters=True):
     import compressed_attention_rotate_amd as tq
     d = fmt_t[0]
     fmt = tq.Format(*fmt_t)
-    signs, S = TI.rotation(d, seed)
-    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    (signs, S), (gsigns, gS) = rotations(d, seed)
+    tab = tq.Tables(fmt, gsigns, torch.from_numpy(gS).cuda())
     if dtype == "bf16":
         xt = torch.from_numpy(x_np.view(np.int16)).cuda().view(torch.bfloat16)
     elif dtype == "f16":
@@ -115,8 +115,8 @@ def test_argument_errors_launch_nothing(torch_gpu):
     import compressed_attention_rotate_amd as tq
     torch = torch_gpu
     fmt = tq.Format(128, 3, 3, 128)
-    signs, S = TI.rotation(128, 1)
-    tab = tq.Tables(fmt, signs, torch.from_numpy(S).cuda())
+    (signs, S), (gsigns, gS) = rotations(128, 1)
+    tab = tq.Tables(fmt, gsigns, torch.from_numpy(gS).cuda())
     x = torch.zeros((4, 129), device="cuda")
     with pytest.raises(tq.TQError):
         tq.quantize_kv(x, fmt, tab)            # d_in > d

@@ -12,7 +12,7 @@ import pytest
 
 import tq_inputs as TI
 from oracle import tq_oracle as O
-from parity_utils import compare_quantize, oracle_codebooks, oracle_pack_cache
+from parity_utils import compare_quantize, oracle_codebooks, oracle_pack_cache, rotations
 
 pytestmark = pytest.mark.gpu
 
@@ -60,9 +60,9 @@ def _gpu_requant(torch, rec, nrm, f_in, f_out, signs, S_in, S_out, in_place=Fals
 def _stored(n, f_in, seed, spikes=0.0):
     kb, vb, _ = TI.kv_layer(1, 2, (n + 3) // 4, 128, seed=seed, spike_frac=spikes)
     x = np.concatenate([kb.reshape(-1, 128), vb.reshape(-1, 128)])[:n]
-    signs, S = TI.rotation(128, seed + 1)
+    (signs, S), (gsigns, gS) = rotations(128, seed + 1)
     rec, nrm, _ = oracle_pack_cache(x[None, None], O.Format(*f_in), signs, S, bf16=True)
-    return rec[0, 0], nrm[0, 0], signs, S
+    return rec[0, 0], nrm[0, 0], (signs, S), (gsigns, gS)
 
 
 @pytest.mark.parametrize("f_in,f_out", [
@@ -74,9 +74,9 @@ def _stored(n, f_in, seed, spikes=0.0):
     ((128, 2, 2, 128), (128, 2, 2, 128)),                 # same width (re-sketch)
 ])
 def test_requantize_matches_oracle(torch_gpu, f_in, f_out):
-    rec, nrm, signs, S = _stored(2999, f_in, 6100)
-    _, S2 = TI.rotation(128, 6200)
-    codes, norms, cnt = _gpu_requant(torch_gpu, rec, nrm, f_in, f_out, signs, S, S2)
+    rec, nrm, (signs, S), (gsigns, gS) = _stored(2999, f_in, 6100)
+    (_, S2), (_, gS2) = rotations(128, 6200)
+    codes, norms, cnt = _gpu_requant(torch_gpu, rec, nrm, f_in, f_out, gsigns, gS, gS2)
     q = _oracle_requant(rec, nrm, O.Format(*f_in), S, O.Format(*f_out), S2)
     rep = compare_quantize(codes, norms, q, O.Format(*f_out), N16_REL, SIGN_WINDOW)
     print(f"\n{f_in} -> {f_out}: {rep} counters={cnt}")
@@ -86,8 +86,8 @@ def test_requantize_in_place_in_chunks(torch_gpu):
     """codes_out = codes_in and norms_out = norms_in, with a workspace of 700 vectors so the
     call runs in five chunks (the last one ragged)."""
     f_in, f_out = (128, 3, 3, 128), (128, 2, 1, 64)
-    rec, nrm, signs, S = _stored(3100, f_in, 6300, spikes=0.01)
-    codes, norms, _ = _gpu_requant(torch_gpu, rec, nrm, f_in, f_out, signs, S, S, in_place=True,
+    rec, nrm, (signs, S), (gsigns, gS) = _stored(3100, f_in, 6300, spikes=0.01)
+    codes, norms, _ = _gpu_requant(torch_gpu, rec, nrm, f_in, f_out, gsigns, gS, gS, in_place=True,
                                    ws_vectors=700)
     q = _oracle_requant(rec, nrm, O.Format(*f_in), S, O.Format(*f_out), S)
     compare_quantize(codes, norms, q, O.Format(*f_out), N16_REL, SIGN_WINDOW)
@@ -100,10 +100,10 @@ def test_requantize_full_layer_sampled(torch_gpu):
     import compressed_attention_rotate_amd as tq
     kb, _, _ = TI.kv_layer(1, 8, 32768, 128, seed=TI.data_seed(2))
     x = kb.reshape(-1, 128)
-    signs, S = TI.rotation(128, TI.rotation_seed(2))
+    (signs, S), (gsigns, gS) = rotations(128, TI.rotation_seed(2))
     f_in, f_out = tq.Format.uniform(128, 3), tq.Format.uniform(128, 2)
-    ti = tq.Tables(f_in, signs, torch.from_numpy(S).cuda())
-    to = tq.Tables(f_out, signs, torch.from_numpy(S).cuda())
+    ti = tq.Tables(f_in, gsigns, torch.from_numpy(gS).cuda())
+    to = tq.Tables(f_out, gsigns, torch.from_numpy(gS).cuda())
     xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
     c4, n4 = tq.quantize_kv(xt, f_in, ti)
     c3, n3 = tq.requantize(c4, n4, f_in, ti, f_out, to)
@@ -123,14 +123,14 @@ def test_requantize_argument_errors(torch_gpu):
     import compressed_attention_rotate_amd as tq
     torch = torch_gpu
     f4, f3 = tq.Format.uniform(128, 3), tq.Format.uniform(128, 2)
-    signs, S = TI.rotation(128, 3)
-    t4 = tq.Tables(f4, signs, torch.from_numpy(S).cuda())
-    t3_other = tq.Tables(f3, -signs, torch.from_numpy(S).cuda())
+    (signs, S), (gsigns, gS) = rotations(128, 3)
+    t4 = tq.Tables(f4, gsigns, torch.from_numpy(gS).cuda())
+    t3_other = tq.Tables(f3, -gsigns, torch.from_numpy(gS).cuda())
     c = torch.zeros((64, f4.record_bytes()), dtype=torch.uint8, device="cuda")
     nr = torch.zeros((64, 2), dtype=torch.float16, device="cuda")
     with pytest.raises(tq.TQError):
         tq.requantize(c, nr, f4, t4, f3, t3_other)                 # another rotation
-    t3 = tq.Tables(f3, signs, torch.from_numpy(S).cuda())
+    t3 = tq.Tables(f3, gsigns, torch.from_numpy(gS).cuda())
     buf = torch.zeros((64, f4.record_bytes()), dtype=torch.uint8, device="cuda")
     with pytest.raises(tq.TQError):                                # wider records in place
         tq.requantize(buf, nr, f3, t3, f4, t4, codes_out=buf, norms_out=nr)

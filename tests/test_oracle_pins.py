@@ -135,6 +135,35 @@ def test_fp16_rounding_is_correct():
     assert np.array_equal(got, ref)
 
 
+def _fp16_neighbours_exact(bits: int):
+    """(value, next value up, next value down) of a positive finite fp16 pattern, exact."""
+    val = lambda b: Fraction(float(np.array([b], np.uint16).view(np.float16)[0]))
+    return val(bits), val(bits + 1), val(bits - 1)
+
+
+@pytest.mark.parametrize("rel", [1e-6, 1e-12])
+def test_near_fp16_midpoint_against_exact_midpoints(rel):
+    """The window that marks norms as ambiguous: a value within rel of a point where fp16
+    rounding changes (the exact midpoint between two adjacent fp16 values, found here from
+    the bit patterns in rational arithmetic) is flagged, one 3 rel away from every such point
+    is not.  Powers of two are included, where the spacing below is half the spacing above."""
+    g = TI.gen(17)
+    pats = list(g.integers(0x0401, 0x7BFF, 300)) + [0x3C00, 0x4000, 0x0800, 0x7800, 0x5C00]
+    near, far, expect_near, expect_far = [], [], [], []
+    for b in pats:
+        h, up, dn = _fp16_neighbours_exact(int(b))
+        for mid in ((h + up) / 2, (h + dn) / 2):
+            for f in (0.5, -0.5, 0.0):
+                near.append(float(mid * (1 + Fraction(f * rel))))
+            for f in (3.0, -3.0):
+                v = mid * (1 + Fraction(f * rel))
+                # the other midpoints are at least half an fp16 spacing away
+                far.append(float(v))
+        far.append(float(h))
+    assert O._near_fp16_midpoint(np.array(near), rel).all()
+    assert not O._near_fp16_midpoint(np.array(far), rel).any()
+
+
 # ---------------------------------------------------------------------------- 2/pi bias
 def test_one_bit_mse_quantizer_has_two_over_pi_bias():
     """163.com explainer, section "第二步：QJL": a 1-bit MSE-optimal quantizer scales inner
@@ -259,6 +288,37 @@ def test_fused_estimator_equals_explicit_dequantized_dot():
         xt = O.dequantize(qz["idx"], qz["sbit"], qz["n16"], qz["r16"], fmt, signs, S, lo, hi)
         est, scale = O.estimator_dot(q, qz["idx"], qz["sbit"], qz["n16"], qz["r16"], fmt, signs, S, lo, hi)
         np.testing.assert_allclose(est, xt @ q, rtol=0, atol=1e-12 * np.max(scale))
+
+
+def test_search_scores_equal_the_fused_estimator_for_padded_queries():
+    """Search scores: queries of d_in < d coordinates are zero-padded and scored against the
+    explicit dequantized vectors; they must equal the fused estimator (n16 <q_rot, c> +
+    gamma r16 <S q_rot, sigma>) of the padded query to 1e-12."""
+    d, d_in = 256, 200
+    fmt = O.Format.uniform(d, 3)
+    cb = O.codebook(d, 3)
+    signs, S = TI.rotation(d, 23)
+    g = TI.gen(24)
+    x = g.standard_normal((40, d_in))
+    qs = g.standard_normal((5, d_in))
+    qz = O.quantize(x, fmt, signs, S, cb)
+    xt = O.dequantize(qz["idx"], qz["sbit"], qz["n16"], qz["r16"], fmt, signs, S, cb)
+    sc = O.search_scores(qs, xt)
+    assert sc.shape == (5, 40)
+    for i in range(5):
+        qp = np.zeros(d)
+        qp[:d_in] = qs[i]
+        est, scale = O.estimator_dot(qp, qz["idx"], qz["sbit"], qz["n16"], qz["r16"], fmt, signs,
+                                     S, cb)
+        np.testing.assert_allclose(sc[i], est, rtol=0, atol=1e-12 * np.max(scale))
+
+
+def test_recall_at_k_hand_cases():
+    est = np.array([[1, 2, 3], [4, 5, 6], [9, 8, 7]])
+    exact = np.array([[3, 2, 9], [7, 8, 9], [7, 8, 9]])
+    assert O.recall_at_k(est, exact) == pytest.approx((2 + 0 + 3) / 9, abs=1e-15)
+    assert O.recall_at_k(exact, exact) == 1.0
+    assert O.recall_at_k(est[:1, :1], exact[:1, :1]) == 0.0
 
 
 def test_attention_matches_hand_expanded_softmax():

@@ -4,11 +4,15 @@ This module draws random numbers and nothing else: it holds none of the method's
 arithmetic (no rotation, no codebook, no quantization). Every array it returns is
 an *input* handed identically to the CPU oracle and to the HIP path:
 
-* the rotation draws the method needs -- the +/-1 diagonal ``signs`` and the
-  d x d Gaussian JL matrix ``S`` -- are generated here and passed in to both sides;
 * key/value/query/database tensors follow the workload laws of the pages'
   settings (Llama-3.1-8B-shaped decode layers, a GloVe-like 200-d search set),
   reproduced synthetically because no datasets or weights are available.
+
+The rotation the method draws (the +/-1 diagonal and the Gaussian JL matrix) is not
+made here: the library makes it with ``tq_make_rotation`` and the oracle with its own
+implementation of the same definition (``oracle.tq_oracle.make_rotation``).  ``rotation``
+below only supplies independent random draws of that shape for Monte-Carlo checks of the
+oracle's statistics, where thousands of fresh rotations are needed.
 
 All generators are counter-based (numpy Philox) so a (seed, shape) pair gives
 the same bytes on any machine.  bf16 tensors are returned as their raw uint16
@@ -40,10 +44,8 @@ def rotation_seed(config: int, layer: int = 0) -> int:
 
 
 def rotation(d: int, seed: int):
-    """Random draws for one rotation: signs[d] in {+1,-1} (int8) and S[d,d] ~ N(0,1) (fp32).
-
-    S is drawn in fp64 and rounded once to fp32; both sides then use the fp32 values.
-    """
+    """Random draws of a rotation's shape for Monte-Carlo pins: signs[d] in {+1,-1} (int8)
+    and S[d,d] ~ N(0,1) (fp32, drawn in fp64 and rounded once)."""
     g = gen(seed)
     signs = np.where(g.integers(0, 2, size=d) == 0, 1, -1).astype(np.int8)
     S = g.standard_normal((d, d)).astype(np.float32)
