@@ -57,7 +57,8 @@ def quantize_kv(x, fmt: Format, tables: Tables, counters=None, codes=None, norms
     """Quantize the rows of x ([..., d_in], fp32 / bf16 / fp16 CUDA tensor, unit stride in
     the last dim).  Returns (codes uint8 [n, record_bytes], norms fp16 [n, 2]); pass
     preallocated `codes`/`norms` to write in place.  `counters` (int64 CUDA tensor of 4)
-    accumulates the diagnostics documented in tq.h."""
+    accumulates the diagnostics documented in tq.h.  With fmt.layout == 1 (token-sliced,
+    n a multiple of 32) codes holds the same bytes as groups: [n // 32, 32 * record_bytes]."""
     torch = _torch()
     if not x.is_cuda:
         raise ValueError("x must be a CUDA tensor")
@@ -68,7 +69,8 @@ def quantize_kv(x, fmt: Format, tables: Tables, counters=None, codes=None, norms
     n = x2.shape[0]
     rb = fmt.record_bytes()
     if codes is None:
-        codes = torch.empty((n, rb), dtype=torch.uint8, device=x.device)
+        shape = (n // 32, 32 * rb) if fmt.layout == 1 else (n, rb)
+        codes = torch.empty(shape, dtype=torch.uint8, device=x.device)
     if norms is None:
         norms = torch.empty((n, 2), dtype=torch.float16, device=x.device)
     if codes.numel() < n * rb or norms.numel() < 2 * n:
@@ -93,7 +95,8 @@ def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format
                   scale: float = None, tau: float = 0.0, logits: bool = False,
                   skipped=None, workspace=None, out=None):
     """One decode step.  q [batch, hq, d]; codes_k [batch, hkv, capacity, rbk] uint8;
-    norms_k [batch, hkv, capacity, 2] fp16; the same for v; seq_lens int32 [batch] (CUDA).
+    norms_k [batch, hkv, capacity, 2] fp16; the same for v (token-sliced values, fmt_v.layout
+    == 1: codes_v [batch, hkv, capacity // 32, 32 * rbv]); seq_lens int32 [batch] (CUDA).
     Returns out fp32 [batch, hq, d] (and logits fp32 [batch, hq, capacity] if asked)."""
     torch = _torch()
     fmt_v = fmt_k if fmt_v is None else fmt_v
@@ -102,10 +105,11 @@ def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format
     _, hkv, capacity, _ = codes_k.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    for t, rb in ((codes_k, fmt_k.record_bytes()), (codes_v, fmt_v.record_bytes())):
-        if t.dtype != torch.uint8 or t.shape[:3] != (batch, hkv, capacity) or t.shape[3] != rb \
-                or not t.is_contiguous():
-            raise ValueError("bad packed cache tensor")
+    for t, f in ((codes_k, fmt_k), (codes_v, fmt_v)):
+        rb = f.record_bytes()
+        shape = (batch, hkv, capacity // 32, 32 * rb) if f.layout == 1 else (batch, hkv, capacity, rb)
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"bad packed cache tensor: expected uint8 {shape}")
     for t in (norms_k, norms_v):
         if t.shape != (batch, hkv, capacity, 2) or not t.is_contiguous():
             raise ValueError("bad norms tensor")

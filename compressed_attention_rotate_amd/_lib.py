@@ -26,7 +26,7 @@ class TQError(RuntimeError):
 class c_format(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("bits_lo", ctypes.c_int32),
                 ("bits_hi", ctypes.c_int32), ("split", ctypes.c_int32),
-                ("qjl", ctypes.c_int32)]
+                ("qjl", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class c_tables(ctypes.Structure):
@@ -104,19 +104,26 @@ def _check(code: int, what: str) -> None:
 @dataclass(frozen=True)
 class Format:
     """Packed format: codebook bits for coordinates < split and >= split, head dim d; qjl
-    False stores the tensor MSE-only (no QJL sign words)."""
+    False stores the tensor MSE-only (no QJL sign words); layout 1 stores the tensor
+    token-sliced (groups of 32 vectors, one word per coordinate and bit-plane; tq.h)."""
     d: int
     bits_lo: int
     bits_hi: int
     split: int
     qjl: bool = True
+    layout: int = 0
 
     @staticmethod
-    def uniform(d: int, bits: int, qjl: bool = True) -> "Format":
-        return Format(d, bits, bits, d, qjl)
+    def uniform(d: int, bits: int, qjl: bool = True, layout: int = 0) -> "Format":
+        return Format(d, bits, bits, d, qjl, layout)
+
+    def sliced(self) -> "Format":
+        """The same format in the token-sliced layout."""
+        return Format(self.d, self.bits_lo, self.bits_hi, self.split, self.qjl, 1)
 
     def c(self) -> c_format:
-        return c_format(self.d, self.bits_lo, self.bits_hi, self.split, 1 if self.qjl else 0)
+        return c_format(self.d, self.bits_lo, self.bits_hi, self.split, 1 if self.qjl else 0,
+                        int(self.layout))
 
     def record_bytes(self) -> int:
         f = self.c()

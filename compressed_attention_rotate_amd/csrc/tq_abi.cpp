@@ -89,6 +89,8 @@ int tq_check_format(const tq_format* f) {
   if (f->split == f->d && f->bits_hi != f->bits_lo) return TQ_ERR_SHAPE;
   if (!supported_widths(f->d, f->bits_lo, hi)) return TQ_ERR_SHAPE;
   if (f->qjl != 0 && f->qjl != 1) return TQ_ERR_ARG;
+  if (f->layout != 0 && f->layout != 1) return TQ_ERR_ARG;
+  if (f->layout == 1 && (f->d != 128 || !f->qjl)) return TQ_ERR_SHAPE;
   return TQ_OK;
 }
 
@@ -129,6 +131,7 @@ int quantize_checked(const tq_format* f, const tq_tables* t, const void* x, int3
   if (rc) return rc;
   if (n < 0 || !dtype_ok(x_dtype)) return TQ_ERR_ARG;
   if (d_in <= 0 || d_in > f->d || ld_x < d_in) return TQ_ERR_SHAPE;
+  if (f->layout == 1 && (paged || n % 32)) return TQ_ERR_SHAPE;
   rc = check_tables(f, t);
   if (rc) return rc;
   if (n == 0) return TQ_OK;
@@ -137,8 +140,10 @@ int quantize_checked(const tq_format* f, const tq_tables* t, const void* x, int3
       (counters && !aligned(counters, 8)))
     return TQ_ERR_ALIGN;
   if (!launch) return TQ_OK;
-  return tq_launch_quantize(f, t, x, x_dtype, n, d_in, ld_x, codes, norms, counters,
-                            reinterpret_cast<hipStream_t>(stream), paged);
+  rc = tq_launch_quantize(f, t, x, x_dtype, n, d_in, ld_x, codes, norms, counters,
+                          reinterpret_cast<hipStream_t>(stream), paged);
+  if (rc || f->layout != 1) return rc;
+  return tq_launch_tiles(f, codes, n, reinterpret_cast<hipStream_t>(stream));
 }
 }  // namespace
 
@@ -184,6 +189,7 @@ int tq_attend_decode_segments(const tq_cache_segment* segs, int32_t n_seg, const
   for (int s = 0; s < n_seg; ++s) {
     const tq_cache_segment& g = segs[s];
     if (!g.fk || !g.tk || !g.fv || !g.tv) return TQ_ERR_ARG;
+    if (g.fk->layout != 0 || g.fv->layout != 0) return TQ_ERR_SHAPE;
     // every argument check of a plain decode, except the workspace size
     const int rc = decode_checked(g.fk, g.tk, g.fv, g.tv, q, q_dtype, batch, hq, hkv, g.codes_k,
                                   g.norms_k, g.codes_v, g.norms_v, g.capacity, g.seq_lens, scale,
@@ -234,6 +240,7 @@ int tq_attend_decode_paged(const tq_format* fk, const tq_tables* tk, const tq_fo
   const int lg = page_log2(page_size);
   if (lg < 0 || num_pages < 1 || max_blocks < 1 || !block_table) return TQ_ERR_ARG;
   if (!aligned(block_table, 4)) return TQ_ERR_ALIGN;
+  if ((fk && fk->layout) || (fv && fv->layout)) return TQ_ERR_SHAPE;
   const tq_paged_src src{block_table, num_pages, max_blocks, lg, max_blocks, -1};
   return decode_checked(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
                         norms_v, (int64_t)max_blocks << lg, seq_lens, scale, tau, out, logits,
@@ -253,8 +260,13 @@ int decode_checked(const tq_format* fk, const tq_tables* tk, const tq_format* fv
   int rc = tq_check_format(fk);
   if (rc) return rc;
   if ((rc = tq_check_format(fv))) return rc;
-  if (fk->d != 128 || fv->d != 128 || !tq_decode_formats_supported(fk, fv)) return TQ_ERR_SHAPE;
+  const bool sliced = fv->layout == 1;
+  if (fk->layout != 0) return TQ_ERR_SHAPE;
+  if (fk->d != 128 || fv->d != 128) return TQ_ERR_SHAPE;
+  if (sliced ? !tq_decode_mx_supported(fk, fv) : !tq_decode_formats_supported(fk, fv))
+    return TQ_ERR_SHAPE;
   if (batch <= 0 || hq <= 0 || hkv <= 0 || capacity < 0) return TQ_ERR_ARG;
+  if (sliced && (paged || capacity % 32 || (hq % hkv == 0 && (hq / hkv) % 4))) return TQ_ERR_SHAPE;
   if (hq % hkv) return TQ_ERR_SHAPE;
   const int g = hq / hkv;
   if (g != 1 && g != 2 && g % 4) return TQ_ERR_SHAPE;
@@ -267,9 +279,14 @@ int decode_checked(const tq_format* fk, const tq_tables* tk, const tq_format* fv
       !aligned(norms_k, 4) || !aligned(norms_v, 4) || (seq_lens && !aligned(seq_lens, 4)) || !aligned(out, 16) ||
       (logits && !aligned(logits, 4)) || (skipped && !aligned(skipped, 8)) || !aligned(workspace, 16))
     return TQ_ERR_ALIGN;
-  const tq_decode_plan plan = tq_plan_decode(batch, hq, hkv, capacity, fk->d);
+  const tq_decode_plan plan = sliced ? tq_plan_decode_mx(batch, hq, hkv, capacity)
+                                    : tq_plan_decode(batch, hq, hkv, capacity, fk->d);
   if (workspace_bytes < plan.ws_bytes) return TQ_ERR_WORKSPACE;
   if (!launch) return TQ_OK;
+  if (sliced)
+    return tq_launch_decode_mx(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k,
+                               codes_v, norms_v, capacity, seq_lens, scale, tau, out, logits,
+                               skipped, workspace, plan, reinterpret_cast<hipStream_t>(stream));
   return tq_launch_decode(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
                           norms_v, capacity, seq_lens, scale, tau, out, logits, skipped, workspace,
                           plan, reinterpret_cast<hipStream_t>(stream), paged);
@@ -289,7 +306,7 @@ int tq_ip_search(const tq_format* f, const tq_tables* t, const void* codes_db,
                  int64_t workspace_bytes, tq_stream_t stream) {
   int rc = tq_check_format(f);
   if (rc) return rc;
-  if (!f->qjl) return TQ_ERR_SHAPE;  // the score is the estimator with the QJL term
+  if (!f->qjl || f->layout) return TQ_ERR_SHAPE;  // the score is the estimator with the QJL term
   if (n_q < 0 || n_db < 0 || k < 1 || k > 64 || k > n_db) return TQ_ERR_ARG;
   if (d_in <= 0 || d_in > f->d) return TQ_ERR_SHAPE;
   if ((rc = check_tables(f, t))) return rc;
@@ -328,7 +345,7 @@ int tq_prefill_paged(const tq_format* fk, const tq_tables* tk, const tq_format* 
   int rc = tq_check_format(fk);
   if (rc) return rc;
   if ((rc = tq_check_format(fv))) return rc;
-  if (fk->d != 128 || fv->d != 128 || !fk->qjl) return TQ_ERR_SHAPE;  // logits need the QJL term
+  if (fk->d != 128 || fv->d != 128 || !fk->qjl || fk->layout || fv->layout) return TQ_ERR_SHAPE;
   if (n_new == 0) return TQ_OK;
   if (!dtype_ok(q_dtype) || !std::isfinite(scale)) return TQ_ERR_ARG;
   if (!q || !out || !workspace) return TQ_ERR_ARG;
@@ -366,7 +383,7 @@ int tq_requantize(const tq_format* f_in, const tq_tables* t_in, const void* code
   int rc = tq_check_format(f_in);
   if (rc) return rc;
   if ((rc = tq_check_format(f_out))) return rc;
-  if (f_in->d != 128 || f_out->d != 128) return TQ_ERR_SHAPE;
+  if (f_in->d != 128 || f_out->d != 128 || f_in->layout || f_out->layout) return TQ_ERR_SHAPE;
   if (n < 0) return TQ_ERR_ARG;
   if ((rc = check_tables(f_in, t_in)) || (rc = check_tables(f_out, t_out))) return rc;
   for (int j = 0; j < f_in->d; ++j)

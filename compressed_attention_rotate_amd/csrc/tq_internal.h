@@ -23,6 +23,9 @@ int tq_launch_quantize(const tq_format* f, const tq_tables* t, const void* x, in
                        int64_t n, int32_t d_in, int64_t ld_x, void* codes, uint16_t* norms,
                        int64_t* counters, hipStream_t stream, const tq_paged_dst* paged = nullptr);
 
+// Rewrite n (a multiple of 32) freshly quantized records in place as token-sliced groups.
+int tq_launch_tiles(const tq_format* f, void* codes, int64_t n, hipStream_t stream);
+
 struct tq_decode_plan {
   int32_t n_split;        // token splits per (batch, kv head)
   int32_t waves;          // waves per scan workgroup
@@ -55,6 +58,17 @@ int tq_launch_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      int64_t* skipped, void* workspace, const tq_decode_plan& plan,
                      hipStream_t stream, const tq_paged_src* paged = nullptr,
                      int32_t split_base = 0, int32_t split_total = 0, bool combine = true);
+
+// Decode with token-sliced values (keys per-vector): the fp8 x fp4 MFMA scan + combine.
+bool tq_decode_mx_supported(const tq_format* fk, const tq_format* fv);
+tq_decode_plan tq_plan_decode_mx(int32_t batch, int32_t hq, int32_t hkv, int64_t capacity);
+int tq_launch_decode_mx(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                        const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
+                        int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                        const void* codes_v, const uint16_t* norms_v, int64_t capacity,
+                        const int32_t* seq_lens, float scale, float tau, float* out,
+                        float* logits, int64_t* skipped, void* workspace,
+                        const tq_decode_plan& plan, hipStream_t stream);
 
 // Two decode segments in one fused scan launch + one combine, when their format pairs have
 // a fused instance; TQ_ERR_SHAPE (nothing launched) otherwise.  Arguments checked by the caller.

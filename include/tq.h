@@ -78,6 +78,14 @@ typedef struct tq_format {
   int32_t qjl;      /* 1: one QJL sign word per block; 0: MSE-only ("PolarQuant
                        alone", no residual sketch: juejin post, section "第二步：QJL"
                        names QJL as the bias fix on top of the MSE stage)        */
+  int32_t layout;   /* 0: per-vector records (above).  1: token-sliced (d = 128, QJL
+                       formats): the same bits grouped by 32 consecutive vectors; within
+                       a group, for each coordinate j in order, the words of j (its code
+                       bit-planes, then its sign bit), bit t of a word belonging to vector
+                       32 * group + t.  A group is 32 * tq_record_bytes() bytes.  Only
+                       tq_quantize_kv writes it (n a multiple of 32) and only
+                       tq_attend_decode reads it (for the values, keys in layout 0);
+                       every other entry point returns TQ_ERR_SHAPE for layout 1.     */
 } tq_format;
 
 typedef struct tq_tables {

@@ -388,6 +388,55 @@ def unpack(rec: np.ndarray, fmt: Format):
     return idx, sbit
 
 
+def tiles_from_records(rec: np.ndarray, fmt: Format) -> np.ndarray:
+    """Token-sliced layout of a tensor's records, for n a multiple of 32: for each group of
+    32 consecutive vectors, for each coordinate j = 0 .. d-1 in order, the words of that
+    coordinate -- its code bit-planes, then its QJL sign when the format has one -- where
+    bit t of a word is that bit of vector 32 * group + t.  It holds the same bits as the
+    per-vector records, sliced across tokens instead of across coordinates (the block-32
+    idea of the zhidx article, section "01 turboquant_plus：介绍与详解", applied to 32
+    tokens), so the bits of one coordinate over 32 tokens are one word.
+    Returns uint8 [n // 32, 32 * record_bytes]."""
+    idx, sbit = unpack(rec, fmt)
+    n, d = idx.shape
+    if n % 32:
+        raise ValueError("the token-sliced layout holds whole groups of 32 vectors")
+    groups = []
+    for g0 in range(0, n, 32):
+        words = []
+        for j in range(d):
+            B = fmt.bits_of_block(j // 32)
+            for p in range(B):
+                words.append(np.packbits(((idx[g0:g0 + 32, j] >> p) & 1).astype(np.uint8),
+                                         bitorder="little"))
+            if fmt.qjl:
+                words.append(np.packbits(sbit[g0:g0 + 32, j].astype(np.uint8), bitorder="little"))
+        groups.append(np.concatenate(words))
+    return np.stack(groups) if groups else np.zeros((0, 32 * fmt.record_bytes()), np.uint8)
+
+
+def records_from_tiles(tiles: np.ndarray, fmt: Format) -> np.ndarray:
+    """Inverse of ``tiles_from_records``: per-vector records [n, record_bytes]."""
+    tiles = np.ascontiguousarray(tiles, dtype=np.uint8)
+    ng = tiles.shape[0]
+    d = fmt.d
+    idx = np.zeros((32 * ng, d), dtype=np.int64)
+    sbit = np.zeros((32 * ng, d), dtype=bool)
+    t = np.arange(32)
+    for g in range(ng):
+        w = tiles[g].view("<u4").astype(np.int64)
+        k = 0
+        for j in range(d):
+            B = fmt.bits_of_block(j // 32)
+            for p in range(B):
+                idx[32 * g:32 * g + 32, j] |= ((w[k] >> t) & 1) << p
+                k += 1
+            if fmt.qjl:
+                sbit[32 * g:32 * g + 32, j] = ((w[k] >> t) & 1).astype(bool)
+                k += 1
+    return pack(idx, sbit, fmt)
+
+
 # --------------------------------------------------------------------------------------
 # Dequantize and the estimator
 # --------------------------------------------------------------------------------------

@@ -443,6 +443,34 @@ def test_pack_layout_and_round_trip():
 
 
 # ------------------------------------------------------------------ MSE-only ("PolarQuant alone")
+def test_token_sliced_layout_hand_built():
+    """The token-sliced layout on a hand-built case: vector 5 of the second group of 32 has
+    code 0b101 and sign 1 at coordinate 37 (b = 4: 3 planes + sign per coordinate), every
+    other bit 0.  Coordinate 37's words are words 4*37 .. 4*37+3 of group 1 and carry bit 5
+    in planes 0 and 2 and in the sign word; nothing else is set."""
+    fmt = O.Format.uniform(128, 3)
+    idx = np.zeros((64, 128), np.int64)
+    sb = np.zeros((64, 128), bool)
+    idx[37, 37] = 0b101
+    sb[37, 37] = True
+    tiles = O.tiles_from_records(O.pack(idx, sb, fmt), fmt)
+    assert tiles.shape == (2, 32 * 64)
+    w = tiles.view("<u4")
+    assert not w[0].any()
+    expect = np.zeros(32 * 16, np.uint32)
+    expect[4 * 37 + 0] = 1 << 5
+    expect[4 * 37 + 2] = 1 << 5
+    expect[4 * 37 + 3] = 1 << 5
+    assert np.array_equal(w[1], expect)
+    # mixed widths: coordinates >= 64 have 2 planes + sign (3 words) after 64 x 4 words
+    fm = O.Format(128, 3, 2, 64)
+    idx2 = np.zeros((32, 128), np.int64)
+    idx2[31, 100] = 0b10
+    t2 = O.tiles_from_records(O.pack(idx2, np.zeros((32, 128), bool), fm), fm).view("<u4")[0]
+    k = 64 * 4 + (100 - 64) * 3 + 1
+    assert t2[k] == 1 << 31 and np.count_nonzero(t2) == 1
+
+
 def test_mse_only_layout_is_the_qjl_layout_without_sign_words():
     """An MSE-only record holds exactly the code planes of the QJL record, in order: each
     block's sign word removed (4.25 -> 3.25 bit/value at b = 4 with the norms)."""
