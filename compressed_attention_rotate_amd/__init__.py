@@ -17,6 +17,7 @@ from ._lib import (LIB_PATH, TQ_BF16, TQ_F16, TQ_F32, Format, Tables, TQError, b
                    load, c_cache_segment, make_rotation)
 
 __all__ = ["Format", "Tables", "TQError", "build_codebook", "make_rotation", "quantize_kv", "attend_decode",
+           "attend_decode_noalloc",
            "attend_decode_segments", "attend_segments_workspace_bytes",
            "ip_search", "requantize", "attend_workspace_bytes", "search_workspace_bytes",
            "requantize_workspace_bytes", "quantize_kv_paged", "attend_decode_paged",
@@ -90,17 +91,8 @@ def attend_workspace_bytes(batch, hq, hkv, capacity, d=128) -> int:
     return int(n)
 
 
-def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format,
-                  tables_k: Tables, fmt_v: Format = None, tables_v: Tables = None,
-                  scale: float = None, tau: float = 0.0, logits: bool = False,
-                  skipped=None, workspace=None, out=None):
-    """One decode step.  q [batch, hq, d]; codes_k [batch, hkv, capacity, rbk] uint8;
-    norms_k [batch, hkv, capacity, 2] fp16; the same for v (token-sliced values, fmt_v.layout
-    == 1: codes_v [batch, hkv, capacity // 32, 32 * rbv]); seq_lens int32 [batch] (CUDA).
-    Returns out fp32 [batch, hq, d] (and logits fp32 [batch, hq, capacity] if asked)."""
+def _decode_args(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k, fmt_v, scale):
     torch = _torch()
-    fmt_v = fmt_k if fmt_v is None else fmt_v
-    tables_v = tables_k if tables_v is None else tables_v
     batch, hq, d = q.shape
     _, hkv, capacity, _ = codes_k.shape
     if scale is None:
@@ -115,7 +107,23 @@ def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format
             raise ValueError("bad norms tensor")
     if seq_lens.dtype != torch.int32 or seq_lens.numel() != batch:
         raise ValueError("seq_lens must be int32 [batch]")
+    return batch, hq, hkv, capacity, d, scale
+
+
+def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format,
+                  tables_k: Tables, fmt_v: Format = None, tables_v: Tables = None,
+                  scale: float = None, tau: float = 0.0, logits: bool = False,
+                  skipped=None, workspace=None, out=None):
+    """One decode step.  q [batch, hq, d]; codes_k [batch, hkv, capacity, rbk] uint8;
+    norms_k [batch, hkv, capacity, 2] fp16; the same for v (token-sliced values, fmt_v.layout
+    == 1: codes_v [batch, hkv, capacity // 32, 32 * rbv]); seq_lens int32 [batch] (CUDA).
+    Returns out fp32 [batch, hq, d] (and logits fp32 [batch, hq, capacity] if asked)."""
+    torch = _torch()
+    fmt_v = fmt_k if fmt_v is None else fmt_v
+    tables_v = tables_k if tables_v is None else tables_v
     q = q.contiguous()
+    batch, hq, hkv, capacity, d, scale = _decode_args(q, codes_k, norms_k, codes_v, norms_v,
+                                                      seq_lens, fmt_k, fmt_v, scale)
     if out is None:
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
     lg = torch.empty((batch, hq, capacity), dtype=torch.float32, device=q.device) if logits else None
@@ -131,6 +139,30 @@ def attend_decode(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format
                                  _stream(q.device))
     _check(rc, "tq_attend_decode")
     return (out, lg) if logits else out
+
+
+def attend_decode_noalloc(q, codes_k, norms_k, codes_v, norms_v, seq_lens, fmt_k: Format,
+                          tables_k: Tables, out, fmt_v: Format = None, tables_v: Tables = None,
+                          scale: float = None, tau: float = 0.0, logits=None, skipped=None):
+    """attend_decode through tq_attend_decode_noalloc: the caller passes every output
+    (out fp32 [batch, hq, d], optional logits fp32 [batch, hq, capacity]) and nothing is
+    allocated; the split partials live in the library's per-GPU device array.  q must be
+    contiguous."""
+    fmt_v = fmt_k if fmt_v is None else fmt_v
+    tables_v = tables_k if tables_v is None else tables_v
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    batch, hq, hkv, capacity, d, scale = _decode_args(q, codes_k, norms_k, codes_v, norms_v,
+                                                      seq_lens, fmt_k, fmt_v, scale)
+    fk, fv, tk, tv = fmt_k.c(), fmt_v.c(), tables_k.c(), tables_v.c()
+    rc = load().tq_attend_decode_noalloc(ctypes.byref(fk), ctypes.byref(tk), ctypes.byref(fv),
+                                         ctypes.byref(tv), _ptr(q), _dtype_code(q), batch, hq,
+                                         hkv, _ptr(codes_k), _ptr(norms_k), _ptr(codes_v),
+                                         _ptr(norms_v), capacity, _ptr(seq_lens), float(scale),
+                                         float(tau), _ptr(out), _ptr(logits), _ptr(skipped),
+                                         _stream(q.device))
+    _check(rc, "tq_attend_decode_noalloc")
+    return out
 
 
 def attend_segments_workspace_bytes(batch: int, hq: int, hkv: int, capacities, d: int = 128) -> int:

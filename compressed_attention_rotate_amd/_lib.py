@@ -63,6 +63,8 @@ def load() -> ctypes.CDLL:
             "tq_attend_workspace_bytes": (I64, [I32, I32, I32, I64, I32]),
             "tq_attend_decode": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P, P, P, P, I64,
                                                 P, F32, F32, P, P, P, P, I64, P]),
+            "tq_attend_decode_noalloc": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P, P, P,
+                                                        P, I64, P, F32, F32, P, P, P, P]),
             "tq_attend_segments_workspace_bytes": (I64, [I32, I32, I32, I32, P, I32]),
             "tq_attend_decode_segments": (ctypes.c_int, [P, I32, P, I32, I32, I32, I32, F32, F32,
                                                          P, P, P, I64, P]),

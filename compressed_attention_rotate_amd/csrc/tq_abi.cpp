@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "tq.h"
 #include "tq_internal.h"
@@ -67,6 +68,29 @@ int decode_checked(const tq_format* fk, const tq_tables* tk, const tq_format* fv
                    int64_t workspace_bytes, tq_stream_t stream, const tq_paged_src* paged,
                    bool launch = true);
 uintptr_t dtype_size(int dt) { return dt == TQ_F32 ? 4 : 2; }
+
+// Split-partial array of tq_attend_decode_noalloc: one copy per GPU, held until the process
+// ends.  Host code never uses the name `scratch` as an address (on the host it is only a
+// stand-in for the device symbol): its device address is asked of the runtime once per
+// device, with that device current, and kept.
+constexpr int64_t kNoAllocScratchBytes = int64_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+void* noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -165,6 +189,27 @@ int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
   return decode_checked(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
                         norms_v, capacity, seq_lens, scale, tau, out, logits, skipped, workspace,
                         workspace_bytes, stream, nullptr);
+}
+
+int tq_attend_decode_noalloc(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                             const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
+                             int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                             const void* codes_v, const uint16_t* norms_v, int64_t capacity,
+                             const int32_t* seq_lens, float scale, float tau, float* out,
+                             float* logits, int64_t* skipped, tq_stream_t stream) {
+  int rc = tq_check_format(fk);
+  if (rc) return rc;
+  if ((rc = tq_check_format(fv))) return rc;
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || capacity < 0 || hq % hkv) return TQ_ERR_ARG;
+  // the split partials must fit the library's own device array
+  const tq_decode_plan plan = fv->layout == 1 ? tq_plan_decode_mx(batch, hq, hkv, capacity)
+                                              : tq_plan_decode(batch, hq, hkv, capacity, fk->d);
+  if (plan.ws_bytes > kNoAllocScratchBytes) return TQ_ERR_WORKSPACE;
+  void* ws = noalloc_scratch();
+  if (!ws) return TQ_ERR_HIP;
+  return decode_checked(fk, tk, fv, tv, q, q_dtype, batch, hq, hkv, codes_k, norms_k, codes_v,
+                        norms_v, capacity, seq_lens, scale, tau, out, logits, skipped, ws,
+                        kNoAllocScratchBytes, stream, nullptr);
 }
 
 int64_t tq_attend_segments_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv,

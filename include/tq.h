@@ -189,6 +189,21 @@ int tq_attend_decode(const tq_format* fk, const tq_tables* tk, const tq_format* 
                      float* logits, int64_t* skipped, void* workspace,
                      int64_t workspace_bytes, tq_stream_t stream);
 
+/* tq_attend_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments
+ * without a workspace, the same kernels and results.  The split partials go to a device
+ * array of 8 MiB inside the library, one per GPU, held until the process ends; the call
+ * allocates nothing.  Every call on a GPU shares that GPU's array, so calls that overlap in
+ * time on one GPU (other streams, other threads) race and must be ordered by the caller.
+ * Errors: as tq_attend_decode; TQ_ERR_WORKSPACE when tq_attend_workspace_bytes for the
+ * shape exceeds 8 MiB; TQ_ERR_HIP when the array's device address cannot be obtained. */
+int tq_attend_decode_noalloc(const tq_format* fk, const tq_tables* tk, const tq_format* fv,
+                             const tq_tables* tv, const void* q, int32_t q_dtype, int32_t batch,
+                             int32_t hq, int32_t hkv, const void* codes_k, const uint16_t* norms_k,
+                             const void* codes_v, const uint16_t* norms_v, int64_t capacity,
+                             const int32_t* seq_lens, float scale, float tau, float* out,
+                             float* logits, int64_t* skipped, tq_stream_t stream);
+
 /* Decode over a cache kept in segments of different formats, as temporal decay leaves
  * it (zhidx article, section "01 turboquant_plus：介绍与详解": older tokens drop to a
  * narrower format, e.g. re-encoded in place by tq_requantize, while new ones are
