@@ -24,10 +24,12 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
-# per-source extra flags: the search and prefill scans keep their MFMA accumulators in VGPRs
-# (they read them back every tile; the AGPR form costs one copy per accumulator)
+# per-source extra flags: the search, prefill and token-sliced decode scans keep their MFMA
+# accumulators in VGPRs (they read them back every tile; the AGPR form costs one copy per
+# accumulator)
 EXTRA = {"tq_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "tq_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "tq_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "tq_decode_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

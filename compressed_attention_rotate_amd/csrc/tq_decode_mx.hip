@@ -148,10 +148,63 @@ struct Fmt {
 
 // Column n of a key group k (0..7) of the tile: token 32 (2x + g0) + 16 s + 4 i + dd with
 // k = 4x + i and n = 8 g0 + 4 s + dd.  Lane (h, n) then holds, for each x, the weights of
-// 4 tokens that form one dword of the value A operand (see exchange below).
+// 4 tokens with consecutive K indices of the value A operand (see the hand-off below).
 __device__ __forceinline__ int key_token(int k, int n) {
   return 32 * (2 * (k >> 2) + (n >> 3)) + 16 * ((n >> 2) & 1) + 4 * (k & 3) + (n & 3);
 }
+
+typedef int i32x4s __attribute__((ext_vector_type(4)));
+constexpr int kRsrcFlags = 0x00020000;   // raw (unformatted) 32-bit buffer, gfx9 family
+
+// A buffer resource (V#) over [base, base + bytes), wave-uniform: loads past the end return
+// zero.  base and bytes must be the same in every lane.
+__device__ __forceinline__ i32x4s make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return (i32x4s){__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                  __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu)),
+                  __builtin_amdgcn_readfirstlane(n), kRsrcFlags};
+}
+
+// Buffer loads straight to LDS: lane L's SZ bytes from rsrc at voffset + soffset land at the
+// LDS address m0 + L * 16 (SZ = 16, 12) or m0 + L * 4 (SZ = 4).  Written as instructions so
+// that the compiler, which cannot tell the LDS image from the rest of LDS, does not wait
+// for them before every LDS access; the caller waits (vmcnt) before reading the image.
+// No register is written.
+template <int SZ>
+__device__ __forceinline__ void load_lds(const i32x4s& rsrc, uint32_t lds_addr, int voffset, int soffset) {
+  if constexpr (SZ == 16)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
+  else if constexpr (SZ == 12)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx3 %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS image of one 128-token tile, filled by buffer loads straight to LDS (lane L's bytes of
+// one load land at L * 16 for 16- and 12-byte loads, L * 4 for 4-byte loads): dword offsets
+constexpr int kTKw = 0;                 // [8 key groups][64 lanes][4]
+constexpr int kTKn = kTKw + 8 * 64 * 4;  // [8][64] key norms
+constexpr int kTVn = kTKn + 8 * 64;      // [8][64] value norms
+constexpr int kTVw = kTVn + 8 * 64;      // [8 coordinate blocks][64 lanes][4]
+constexpr int kTileDw = kTVw + 8 * 64 * 4;
+
+// s_waitcnt immediates (gfx9 encoding): all vector memory done / all LDS operations done
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// The records of one 128-token tile as this lane reads them.
+struct TileRegs {
+  u32x4 kw[8];        // key block g of token key_token(k, n)
+  uint32_t kn[8];     // key norms (fp16 ||x|| | fp16 ||r|| << 16) of the same tokens
+  uint32_t vn[8];     // value norms of the same tokens
+  u32x4 vw[8];        // value words of coordinate 16 c + n, 32-token group g of the tile
+};
 
 template <int KLO, int KHI, int KSB, int VLO, int VHI, int VSB>
 __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -170,15 +223,17 @@ void decode_mx_scan(MxParams p) {
   __shared__ uint32_t s_x[kXWaves][2][4][kXTile];         // rounded weights [type][head][K]
   __shared__ float s_m[kXWaves][4][2];
   __shared__ float s_red[kXWaves][4][2 * kD];
+  __shared__ __align__(16) uint32_t s_tile[kXWaves][kTileDw];   // next tile, in flight
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int split = blockIdx.x;
   const int unit = blockIdx.y;
   const int nchunk = p.group >> 2;
   const int bkv = unit / nchunk;                  // batch * hkv + kv head
   const int b = bkv / p.hkv;
   const int h0 = (bkv % p.hkv) * p.group + (unit % nchunk) * 4;  // first query head
-  const int len = (int)min((int64_t)p.seq_lens[b], p.capacity);
+  const int len = __builtin_amdgcn_readfirstlane((int)min((int64_t)p.seq_lens[b], p.capacity));
   const int64_t t_beg = (int64_t)split * p.tokens_per_split;
   const int64_t t_end = min(t_beg + p.tokens_per_split, (int64_t)len);
   const int64_t vbase = (int64_t)bkv * p.capacity;   // first vector of this (batch, KV head)
@@ -187,73 +242,79 @@ void decode_mx_scan(MxParams p) {
   const int n = lane & 15, g = lane >> 4;          // B operand: column n, K block g
   const int hh = lane >> 4;                        // C layout: head of this lane
   const int dd = n & 3;                            // token position mod 4 of this lane's tokens
-  const float fd = dd == 0 ? 4.0f : dd == 1 ? 2.0f : dd == 2 ? 1.0f : -2.0f;
 
-  // ---- tile loads
-  auto tile_start = [&](int it) -> int64_t { return t_beg + (int64_t)(wave + kXWaves * it) * kXTile; };
-  uint32_t kw[8][4];       // key block g of token key_token(k, n)
-  uint32_t kn[8], vn[8];   // key / value norms of token key_token(k, n) (logit lanes)
-  uint32_t vw[8][4];       // value words: coordinate 16 c + n of group g
-  auto fetch = [&](int64_t t0, uint32_t (&kw_)[8][4], uint32_t (&kn_)[8], uint32_t (&vn_)[8],
-                   uint32_t (&vw_)[8][4]) {
-    const int64_t last = p.capacity - 1;
+  // ---- query loads first: waits for them must not wait for the tile loads issued later
+  float qx[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) qx[e] = load_elem(p.q, ((int64_t)b * p.hq + h0 + wave) * kD + lane + 64 * e, p.q_dtype);
+  f32x4 srow[16];   // S rows 32 wave + lane / 2, columns 64 (lane & 1) ..
+  {
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.S_k + (int64_t)(32 * wave + (lane >> 1)) * kD + 64 * (lane & 1));
+#pragma unroll
+    for (int c = 0; c < 16; ++c) srow[c] = src[c];
+  }
+
+  // ---- tile loads through buffer resources based at the tile: per-lane offsets are
+  // constants, the tile start only moves the (scalar) base
+  auto tile_start = [&](int i) -> int64_t { return t_beg + (int64_t)(wave + kXWaves * i) * kXTile; };
+  const int tok0 = key_token(0, n);                         // + 64 (k >> 2) + 4 (k & 3)
+  const int koff = tok0 * FK::RW * 4 + FK::off(g) * 4;
+  const int noff = tok0 * 4;
+  // value words of coordinate j = 16 c + n in group g: the lo-width region for j < 32 VSB
+  const int voff_lo = g * VGW * 4 + n * (VLO + 1) * 4;
+  const int voff_hi = g * VGW * 4 + (32 * VSB * (VLO + 1) + n * (VHI + 1)) * 4;
+  uint32_t* tl = &s_tile[wave][0];
+  const uint32_t tl_addr = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)tl));   // LDS byte address
+  // issue the loads of the tile at t0 into this wave's LDS image (no registers)
+  auto dma = [&](int64_t t0) {
+    const int64_t left = p.capacity - t0;   // tokens of this (batch, KV head) from t0 on
+    const i32x4s rk = make_rsrc(p.codes_k + (vbase + t0) * FK::RW, left * FK::RW * 4);
+    const i32x4s rnk = make_rsrc(p.norms_k + vbase + t0, left * 4);
+    const i32x4s rnv = make_rsrc(p.norms_v + vbase + t0, left * 4);
+    const i32x4s rv = make_rsrc(p.codes_v + ((vbase + t0) >> 5) * VGW, (left >> 5) * VGW * 4);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      int64_t t = t0 + key_token(k, n);
-      t = t > last ? last : t;
-      const uint32_t* rec = p.codes_k + (vbase + t) * FK::RW + FK::off(g);
-      if constexpr (KLO == KHI) {
-        if constexpr (KLO == 3) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(rec);
-          kw_[k][0] = w[0]; kw_[k][1] = w[1]; kw_[k][2] = w[2]; kw_[k][3] = w[3];
-        } else if constexpr (KLO == 2) {
-          kw_[k][0] = rec[0]; kw_[k][1] = rec[1]; kw_[k][2] = rec[2]; kw_[k][3] = 0;
-        } else {
-          kw_[k][0] = rec[0]; kw_[k][1] = rec[1]; kw_[k][2] = 0; kw_[k][3] = 0;
-        }
-      } else {
-        kw_[k][0] = rec[0]; kw_[k][1] = rec[1]; kw_[k][2] = rec[2];
-        kw_[k][3] = FK::bits(g) >= 3 ? rec[3] : 0;
-      }
-      kn_[k] = p.norms_k[vbase + t];
-      vn_[k] = p.norms_v[vbase + t];
+      const int dt = 64 * (k >> 2) + 4 * (k & 3);   // token offset of key group k
+      load_lds<16>(rk, tl_addr + 4 * (kTKw + k * 256), koff, dt * FK::RW * 4);
+      load_lds<4>(rnk, tl_addr + 4 * (kTKn + k * 64), noff, dt * 4);
+      load_lds<4>(rnv, tl_addr + 4 * (kTVn + k * 64), noff, dt * 4);
     }
-    int64_t grp = (vbase + t0) / 32 + g;
-    const int64_t glast = (vbase + p.capacity) / 32 - 1;
-    grp = grp > glast ? glast : grp;
-    const uint32_t* gw = p.codes_v + grp * VGW;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int blk = c >> 1;                     // 32-coordinate block of coordinate 16 c + n
-      const int j = 16 * c + n;
-      const uint32_t* w = gw + (blk < VSB ? j * (VLO + 1) : 32 * VSB * (VLO + 1) + (j - 32 * VSB) * (VHI + 1));
-      const int nb = FV::words(blk);
-      if (nb == 4) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(w);
-        vw_[c][0] = v[0]; vw_[c][1] = v[1]; vw_[c][2] = v[2]; vw_[c][3] = v[3];
-      } else if (nb == 3) {
-        vw_[c][0] = w[0]; vw_[c][1] = w[1]; vw_[c][2] = w[2]; vw_[c][3] = 0;
-      } else {
-        vw_[c][0] = w[0]; vw_[c][1] = w[1]; vw_[c][2] = 0; vw_[c][3] = 0;
-      }
+      const int blk = c >> 1;
+      const int vo = blk < VSB ? voff_lo : voff_hi;
+      const int so = blk < VSB ? 16 * c * (VLO + 1) * 4 : (16 * c - 32 * VSB) * (VHI + 1) * 4;
+      if (FV::words(blk) == 4)
+        load_lds<16>(rv, tl_addr + 4 * (kTVw + c * 256), vo, so);
+      else
+        load_lds<12>(rv, tl_addr + 4 * (kTVw + c * 256), vo, so);
+    }
+  };
+  // this lane's part of the LDS image into registers (after the tile's loads completed)
+  auto read_tile = [&](TileRegs& T) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      T.kw[k] = *reinterpret_cast<const u32x4*>(tl + kTKw + k * 256 + 4 * lane);
+      T.kn[k] = tl[kTKn + k * 64 + lane];
+      T.vn[k] = tl[kTVn + k * 64 + lane];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(tl + kTVw + c * 256 + 4 * lane);
+      T.vw[c] = FV::words(c >> 1) == 4 ? w : (u32x4){w[0], w[1], w[2], 0u};
     }
   };
 
-  int it = 0;
-  const bool has_tile0 = tile_start(0) < t_end;
-  if (has_tile0) fetch(tile_start(0), kw, kn, vn, vw);
-
-  // ---- query prologue: q_rot = H D q / sqrt(d), S q_rot, scales, constants, key operands
+  // ---- query prologue: q_rot = H D q / sqrt(d) (wave = head), then S q_rot
   {
-    const int hd = wave;  // head h0 + wave
+    const int hd = wave;
     float v[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int j = lane + 64 * e;
-      float x = load_elem(p.q, ((int64_t)b * p.hq + h0 + hd) * kD + j, p.q_dtype);
       const uint32_t sw = (lane & 32) ? uniform_u32(p.sign_k[2 * e + 1]) : uniform_u32(p.sign_k[2 * e]);
-      if ((sw >> (j & 31)) & 1u) x = -x;
-      v[e] = x;
+      v[e] = ((sw >> (j & 31)) & 1u) ? -qx[e] : qx[e];
     }
     fwht128(v, lane);
     const float isd = 1.0f / sqrtf((float)kD);
@@ -263,11 +324,10 @@ void decode_mx_scan(MxParams p) {
   __syncthreads();
   {  // S q_rot: wave w rows 32 w .. 32 w + 31; lane (row, half of the columns)
     const int row = 32 * wave + (lane >> 1), half = lane & 1;
-    const f32x4* src = reinterpret_cast<const f32x4*>(p.S_k + (int64_t)row * kD + 64 * half);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      const f32x4 s = src[c];
+      const f32x4 s = srow[c];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const f32x4 qv = *reinterpret_cast<const f32x4*>(&s_qrot[h][64 * half + 4 * c]);
@@ -279,10 +339,12 @@ void decode_mx_scan(MxParams p) {
     }
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float tot = acc[h] + __shfl_xor(acc[h], 1, 64);
+      const float tot = acc[h] + xchg<1>(acc[h]);
       if (!half) s_sq[h][row] = tot;
     }
   }
+  // the first tile in flight while the key operands are built
+  if (tile_start(0) < t_end) dma(tile_start(0));
   __syncthreads();
   {  // per head (wave): the constants removed after the products
     const int hd = wave;
@@ -310,7 +372,7 @@ void decode_mx_scan(MxParams p) {
   // digit m % 4) for K = 32 g .. 32 g + 31.  K = 32 g + p is coordinate j = 32 g + 4 (p % 8) +
   // p / 8 (nibble p % 8 of dword p / 8 of the B operand), whose nibble weight is f_{p / 8}.
   // a_j = f alpha_k q_rot_j (codebook planes) or f (S q_rot)_j (sign plane); x = |a| 2^-e is
-  // truncated to 32 bits: digits 0-3 in one operand, 4-7 in the other.
+  // truncated to 32 bits (x 2^32 as an integer): digits 0-3 in one operand, 4-7 in the other.
   {
     const int ga = lane >> 4, m = lane & 15, hd = m >> 2, l = m & 3;
     for (int k = wave; k <= NPK; k += kXWaves) {
@@ -326,18 +388,14 @@ void decode_mx_scan(MxParams p) {
         amax = fmaxf(amax, fabsf(av[q]));
       }
       const int e = block_exp(amax);
+      const int shh = 28 - 4 * l, shl = 12 - 4 * l;   // digit l and digit 4 + l of x 2^32
       f32x16 hev, hod, lev, lod;
 #pragma unroll
       for (int q = 0; q < 32; ++q) {
-        const float x = e == kZeroExp ? 0.0f : ldexpf(fabsf(av[q]), -e);
-        // digit n of x: floor(x 16^(n+1)) - 16 floor(x 16^n), exact in fp32
-        const float t0 = floorf(ldexpf(x, 4 * l)), t1 = floorf(ldexpf(x, 4 * l + 4));
-        const float t4 = floorf(ldexpf(x, 4 * l + 16)), t5 = floorf(ldexpf(x, 4 * l + 20));
-        float dh = fmaf(-16.0f, t0, t1), dl = fmaf(-16.0f, t4, t5);
-        if (av[q] < 0.0f) {
-          dh = -dh;
-          dl = -dl;
-        }
+        const uint32_t r = e == kZeroExp ? 0u : (uint32_t)ldexpf(fabsf(av[q]), 32 - e);
+        const uint32_t sgn = __float_as_uint(av[q]) & 0x80000000u;
+        const float dh = __uint_as_float(__float_as_uint((float)((r >> shh) & 15u)) | sgn);
+        const float dl = __uint_as_float(__float_as_uint((float)((r >> shl) & 15u)) | sgn);
         if (q & 1) {
           hod[q >> 1] = dh;
           lod[q >> 1] = dl;
@@ -373,73 +431,76 @@ void decode_mx_scan(MxParams p) {
   const float cc_h = s_hc[hh][0], cs_h = s_hc[hh][1];
   const float lsg = lscale * p.gamma;
 
-  // ---- running state (lane (hh, n))
+  // ---- running state (lane (hh, n)).  The running max moves only when a tile's max
+  // exceeds it by more than kLazy (log2 units): weights then stay below 2^kLazy and the
+  // accumulators are rescaled rarely.
+  constexpr float kLazy = 8.0f;
   float m_run = -INFINITY, l_part = 0.f, u3 = 0.f, u3s = 0.f;
   unsigned long long n_skip = 0;
-  // value sums: arun[c] = sum_k alpha_k (products of plane k), one fp32 sum per digit row,
-  // updated after each tile; accs[c] = sign products (one plane, kept on the MFMA)
+  // value sums, one fp32 sum per digit row and 16-coordinate block: arun[c] = sum_k alpha_k
+  // (products of codebook plane k), folded after each tile; accs[c] = sign products, kept on
+  // the matrix cores
   f32x4 arun[8], accs[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    accs[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
     arun[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    accs[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   uint32_t* xw = &s_x[wave][0][0][0];
   const int g0 = n >> 3, sx = (n >> 2) & 1;
-  const int gA_w = 2 * g0 + (dd >> 1);            // value A lane group of this lane's tokens
   const float fv = dd == 0 ? 4.0f : dd == 1 ? 2.0f : dd == 2 ? 1.0f : 2.0f;  // value A weights
   const float fvi = 1.0f / fv;
   int* ve = &s_ve[wave][0][0][0];
 
-  for (; tile_start(it) < t_end; ++it) {
-    const int64_t t0 = tile_start(it);
-    // next tile in flight while this one is computed
-    uint32_t nkw[8][4], nkn[8], nvn[8], nvw[8][4];
-    const bool more = tile_start(it + 1) < t_end;
-    if (more) fetch(tile_start(it + 1), nkw, nkn, nvn, nvw);
-
+  auto process = [&](const TileRegs& T, const int64_t t0) {
     // -- keys: logits of head hh for tokens key_token(k, n)
     float lg[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t p0 = kw[k][0], p1 = kw[k][1];
+      const uint32_t p0 = T.kw[k][0], p1 = T.kw[k][1];
       uint32_t p2, sg;
       if constexpr (KLO == KHI) {
-        p2 = KLO >= 3 ? kw[k][2] : 0u;
-        sg = kw[k][KLO];
+        p2 = KLO >= 3 ? T.kw[k][2] : 0u;
+        sg = T.kw[k][KLO];
       } else {
         const bool w3 = FK::bits(g) >= 3;
-        p2 = w3 ? kw[k][2] : 0u;
-        sg = w3 ? kw[k][3] : kw[k][2];
+        p2 = w3 ? T.kw[k][2] : 0u;
+        sg = w3 ? T.kw[k][3] : T.kw[k][2];
       }
-      f32x4 ac = {0.f, 0.f, 0.f, 0.f}, as = {0.f, 0.f, 0.f, 0.f};
+      // digits 0-3 and 4-7 in two chains (independent accumulators)
+      f32x4 ach = {0.f, 0.f, 0.f, 0.f}, acl = {0.f, 0.f, 0.f, 0.f};
+      f32x4 ash = {0.f, 0.f, 0.f, 0.f}, asl = {0.f, 0.f, 0.f, 0.f};
       {
         const i32x4 b0 = fp4_of(p0);
-        ac = mma(akh[0], b0, ac, ksh[0]);
-        ac = mma(akl[0], b0, ac, ksl[0]);
+        ach = mma(akh[0], b0, ach, ksh[0]);
+        acl = mma(akl[0], b0, acl, ksl[0]);
       }
       if constexpr (NPK >= 2) {
         const i32x4 b1 = fp4_of(p1);
-        ac = mma(akh[1], b1, ac, ksh[1]);
-        ac = mma(akl[1], b1, ac, ksl[1]);
+        ach = mma(akh[1], b1, ach, ksh[1]);
+        acl = mma(akl[1], b1, acl, ksl[1]);
       }
       if constexpr (NPK >= 3) {
         const i32x4 b2 = fp4_of(p2), b3 = fp4_of(p0 ^ p1 ^ p2);
-        ac = mma(akh[2], b2, ac, ksh[2]);
-        ac = mma(akl[2], b2, ac, ksl[2]);
-        ac = mma(akh[3], b3, ac, ksh[3]);
-        ac = mma(akl[3], b3, ac, ksl[3]);
+        ach = mma(akh[2], b2, ach, ksh[2]);
+        acl = mma(akl[2], b2, acl, ksl[2]);
+        ach = mma(akh[3], b3, ach, ksh[3]);
+        acl = mma(akl[3], b3, acl, ksl[3]);
       }
       {
         const i32x4 bs = fp4_of(sg);
-        as = mma(akh[NPK], bs, as, ksh[NPK]);
-        as = mma(akl[NPK], bs, as, ksl[NPK]);
+        ash = mma(akh[NPK], bs, ash, ksh[NPK]);
+        asl = mma(akl[NPK], bs, asl, ksl[NPK]);
       }
+      const f32x4 ac = ach + acl, as = ash + asl;
       const float dc = ((ac[0] + ac[1]) + (ac[2] + ac[3]) - cc_h) * lscale;
       const float ds = ((as[0] + as[1]) + (as[2] + as[3]) - cs_h) * lsg;
-      const float n16 = f16_bits_to_f32(kn[k]), r16 = f16_bits_to_f32(kn[k] >> 16);
-      const int64_t t = t0 + key_token(k, n);
-      lg[k] = t < t_end ? fmaf(n16, dc, r16 * ds) : -INFINITY;
+      const float n16 = f16_bits_to_f32(T.kn[k]), r16 = f16_bits_to_f32(T.kn[k] >> 16);
+      float v = fmaf(n16, dc, r16 * ds);
+      // computed in every lane before the mask: the products must not move under a branch
+      // on the token index (their B operands come from other lanes)
+      asm volatile("" : "+v"(v));
+      lg[k] = t0 + key_token(k, n) < t_end ? v : -INFINITY;
     }
     if (p.logits) {
 #pragma unroll
@@ -449,28 +510,26 @@ void decode_mx_scan(MxParams p) {
           p.logits[((int64_t)b * p.hq + h0 + hh) * p.capacity + t] = lg[k] * 0.6931471805599453f;
       }
     }
-    // -- online softmax (head hh spans the 16 lanes of its row)
-    float tm = lg[0];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) tm = fmaxf(tm, lg[k]);
-    tm = fmaxf(tm, __shfl_xor(tm, 1, 64));
-    tm = fmaxf(tm, __shfl_xor(tm, 2, 64));
-    tm = fmaxf(tm, __shfl_xor(tm, 4, 64));
-    tm = fmaxf(tm, __shfl_xor(tm, 8, 64));
-    const float m_new = fmaxf(m_run, tm);
-    const bool rescale_m = m_new > m_run && m_run != -INFINITY;
-    if (__ballot(rescale_m) != 0) {
-      const float fm = rescale_m ? exp2f(m_run - m_new) : 1.0f;
+    // -- online softmax (head hh spans the 16 lanes of its DPP row)
+    float tm = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])), fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
+    tm = fmaxf(tm, xchg<1>(tm));
+    tm = fmaxf(tm, xchg<2>(tm));
+    tm = fmaxf(tm, xchg<4>(tm));
+    tm = fmaxf(tm, xchg<8>(tm));
+    const bool grow = tm > m_run + kLazy;   // also the first finite max
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? tm : m_run;
+      const float fm = (grow && m_run != -INFINITY) ? exp2f(m_run - m_new) : 1.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        accs[c] *= fm;
         arun[c] *= fm;
+        accs[c] *= fm;
       }
       l_part *= fm;
       u3 *= fm;
       u3s *= fm;
+      m_run = m_new;
     }
-    m_run = m_new;
     float w[8];
     float tsum = 0.f;
 #pragma unroll
@@ -481,10 +540,10 @@ void decode_mx_scan(MxParams p) {
     l_part += tsum;
     if (p.tau > 0.0f) {  // Sparse V: drop weights below tau times the running sum (an upper bound)
       float lrun = l_part;
-      lrun += __shfl_xor(lrun, 1, 64);
-      lrun += __shfl_xor(lrun, 2, 64);
-      lrun += __shfl_xor(lrun, 4, 64);
-      lrun += __shfl_xor(lrun, 8, 64);
+      lrun += xchg<1>(lrun);
+      lrun += xchg<2>(lrun);
+      lrun += xchg<4>(lrun);
+      lrun += xchg<8>(lrun);
       const float thr = p.tau * lrun;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -502,7 +561,7 @@ void decode_mx_scan(MxParams p) {
       float u[8], us[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float n16 = f16_bits_to_f32(vn[k]), r16 = f16_bits_to_f32(vn[k] >> 16);
+        const float n16 = f16_bits_to_f32(T.vn[k]), r16 = f16_bits_to_f32(T.vn[k] >> 16);
         u[k] = w[k] > 0.0f ? w[k] * n16 * fv : 0.0f;
         us[k] = w[k] > 0.0f ? w[k] * r16 * fv : 0.0f;
       }
@@ -547,6 +606,7 @@ void decode_mx_scan(MxParams p) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_sched_barrier(0);
     // A lane (g, m): row m = (head m / 4, digit m % 4) of the 32 tokens of group g
     i32x8 au, as_;
     int vsu, vss;
@@ -573,6 +633,7 @@ void decode_mx_scan(MxParams p) {
           as_ = op;
           vss = sc;
         }
+        __builtin_amdgcn_sched_barrier(0);   // one type's 32 weights live at a time
       }
     }
     // -- values: one product per plane and 16-coordinate block over the 128 tokens; the
@@ -581,12 +642,12 @@ void decode_mx_scan(MxParams p) {
     for (int c = 0; c < 8; ++c) {
       const int bits = FV::bits(c >> 1);
       const int wsel = (c >> 1) < VSB ? 0 : 1;
-      const uint32_t p0 = vw[c][0], p1 = vw[c][1];
-      const uint32_t p2 = bits >= 3 ? vw[c][2] : 0u;
-      const uint32_t sg = vw[c][bits];
+      const uint32_t p0 = T.vw[c][0], p1 = T.vw[c][1];
+      const uint32_t p2 = bits >= 3 ? T.vw[c][2] : 0u;
+      const uint32_t sg = T.vw[c][bits];
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 t0 = mma(au, fp4_pos(p0), z, vsu);
-      f32x4 a = arun[c] + p.alpha_v[wsel][0] * t0;
+      const f32x4 t0v = mma(au, fp4_pos(p0), z, vsu);
+      f32x4 a = arun[c] + p.alpha_v[wsel][0] * t0v;
       if (bits >= 2) {
         const f32x4 t1 = mma(au, fp4_pos(p1), z, vsu);
         a += p.alpha_v[wsel][1] * t1;
@@ -600,29 +661,35 @@ void decode_mx_scan(MxParams p) {
       arun[c] = a;
       accs[c] = mma(as_, fp4_pos(sg), accs[c], vss);
     }
-    if (more) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        kn[k] = nkn[k];
-        vn[k] = nvn[k];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kw[k][i] = nkw[k][i];
-          vw[k][i] = nvw[k][i];
-        }
-      }
-    }
+  };
+
+  // ---- main loop: take the tile out of LDS, put the next one in flight, compute
+  for (int it = 0; tile_start(it) < t_end; ++it) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);      // this tile's loads (the only ones in flight)
+    asm volatile("" ::: "memory");
+    TileRegs T;
+    read_tile(T);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);    // reads done before the image is overwritten
+    asm volatile("" ::: "memory");
+    if (tile_start(it + 1) < t_end) dma(tile_start(it + 1));
+    process(T, tile_start(it));
   }
 
   // ---- wave partial: per head the running max, the sum of weights and the rotated-domain
   // sums A[j] = sum_k alpha_k (sum_t u_t s_k,t,j), Q[j] = sum_t u'_t sigma_t,j
   float lh = l_part, u3h = u3, u3sh = u3s;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    lh += __shfl_xor(lh, o, 64);
-    u3h += __shfl_xor(u3h, o, 64);
-    u3sh += __shfl_xor(u3sh, o, 64);
-  }
+  lh += xchg<1>(lh);
+  u3h += xchg<1>(u3h);
+  u3sh += xchg<1>(u3sh);
+  lh += xchg<2>(lh);
+  u3h += xchg<2>(u3h);
+  u3sh += xchg<2>(u3sh);
+  lh += xchg<4>(lh);
+  u3h += xchg<4>(u3h);
+  u3sh += xchg<4>(u3sh);
+  lh += xchg<8>(lh);
+  u3h += xchg<8>(u3h);
+  u3sh += xchg<8>(u3sh);
   if (n == 0) {
     s_m[wave][hh][0] = m_run;
     s_m[wave][hh][1] = lh;
