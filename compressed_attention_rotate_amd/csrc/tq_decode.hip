@@ -6,16 +6,20 @@
 namespace tqk {
 
 // ----------------------------------------------------------------------------- combine
-// One workgroup per (batch, query head): every load it needs (S_v column slices, the
-// split maxima, the first 32 splits' partial sums) is issued before the first use.  The
-// splits are merged in index order; each split's weight 2^(m_i - M) is recomputed where it
-// is used, so any number of partials fits (segmented caches add theirs up).
-constexpr int kCombChunk = 32;
+// One workgroup per (batch, query head).  Every load of the first 256 splits is issued
+// before the first use: S_v column slices, each split's (m, l) (thread i loads split i) and
+// the first 32 splits' partial sums.  The splits' weights 2^(m_i - M) go through LDS in
+// chunks of 256 splits, so any number of partials fits (segmented caches add theirs up); the
+// sums run in split order, the same order for every thread.
+constexpr int kCombChunk = 32;    // partial sums in flight per thread
+constexpr int kCombSplits = 256;  // split weights per LDS chunk
 
 __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  __shared__ float red[4];
+  __shared__ float red[2][4];
+  __shared__ float scl[kCombSplits];
+  __shared__ float lw[kCombSplits];
   __shared__ float vec[2][kD];
   __shared__ float part_s[256];
   const float* parts = p.ws_part + (int64_t)bh * p.n_split * kPartFloats;
@@ -24,35 +28,51 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   float sv[64];  // S_v[64 half + i][j]
 #pragma unroll
   for (int i = 0; i < 64; ++i) sv[i] = p.S_v[(int64_t)(64 * half + i) * kD + j];
+  // this thread's split of the first chunk, and the first partial sums
+  float m0 = -INFINITY, l0 = 0.0f;
+  if (tid < np) {
+    m0 = parts[(int64_t)tid * kPartFloats];
+    l0 = parts[(int64_t)tid * kPartFloats + 1];
+  }
   float pv[kCombChunk];
 #pragma unroll
   for (int c = 0; c < kCombChunk; ++c)
     pv[c] = c < np ? parts[(int64_t)c * kPartFloats + 2 + tid] : 0.0f;
-  float M = -INFINITY;
-  for (int i = tid; i < np; i += 256) M = fmaxf(M, parts[(int64_t)i * kPartFloats]);
+  // the largest split maximum
+  float M = m0;
+  for (int i = tid + kCombSplits; i < np; i += 256) M = fmaxf(M, parts[(int64_t)i * kPartFloats]);
   M = wave_max_fast(M);
-  if (lane == 0) red[wave] = M;
+  if (lane == 0) red[0][wave] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // thread tid: component tid / 128 (A or Q), coordinate tid % 128; fixed order over splits.
-  // Every thread also forms the denominator L in the same order (uniform loads).
-  float acc = 0.0f, Ltot = 0.0f;
-  for (int c0 = 0; c0 < np; c0 += kCombChunk) {
-    if (c0 > 0) {
-#pragma unroll
-      for (int c = 0; c < kCombChunk; ++c)
-        pv[c] = c0 + c < np ? parts[(int64_t)(c0 + c) * kPartFloats + 2 + tid] : 0.0f;
-    }
-#pragma unroll
-    for (int c = 0; c < kCombChunk; ++c) {
-      if (c0 + c < np) {
-        const float m = parts[(int64_t)(c0 + c) * kPartFloats];
-        const float l = parts[(int64_t)(c0 + c) * kPartFloats + 1];
-        const float s = (m == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(m - M);
-        acc = fmaf(pv[c], s, acc);
-        Ltot = fmaf(s, l, Ltot);
+  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  // thread tid: component tid / 128 (A or Q), coordinate tid % 128
+  float acc = 0.0f, lsum = 0.0f;
+  for (int c0 = 0; c0 < np; c0 += kCombSplits) {
+    const int nc = np - c0 < kCombSplits ? np - c0 : kCombSplits;
+    if (tid < nc) {
+      float m = m0, l = l0;
+      if (c0 > 0) {
+        m = parts[(int64_t)(c0 + tid) * kPartFloats];
+        l = parts[(int64_t)(c0 + tid) * kPartFloats + 1];
       }
+      const float sw = (m == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(m - M);
+      scl[tid] = sw;
+      lw[tid] = sw * l;
     }
+    __syncthreads();
+    for (int c = 0; c < nc; c += kCombChunk) {
+      if (c0 + c > 0) {
+#pragma unroll
+        for (int k = 0; k < kCombChunk; ++k)
+          pv[k] = c + k < nc ? parts[(int64_t)(c0 + c + k) * kPartFloats + 2 + tid] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < kCombChunk; ++k)
+        if (c + k < nc) acc = fmaf(pv[k], scl[c + k], acc);
+    }
+    // the denominator, in split order (every thread reads the same LDS values)
+    for (int k = 0; k < nc; ++k) lsum += lw[k];
+    __syncthreads();
   }
   vec[half][j] = acc;
   __syncthreads();
@@ -72,7 +92,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
       v[e] = vec[0][jj] + part_s[jj] + part_s[128 + jj];
     }
     fwht128(v, lane);
-    const float inv = (Ltot > 0.0f) ? 1.0f / (Ltot * sqrtf((float)kD)) : 0.0f;
+    const float inv = (lsum > 0.0f) ? 1.0f / (lsum * sqrtf((float)kD)) : 0.0f;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int jj = lane + 64 * e;

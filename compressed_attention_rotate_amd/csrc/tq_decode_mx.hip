@@ -17,7 +17,7 @@
 // becomes the fp4 B operand of 32 contraction indices with one AND per dword: dword D keeps
 // bit D of every nibble, so nibble i of dword D is bit 4i + D of w, an e2m1 value 0.5 b,
 // b or 2 b (D = 0, 1, 2); for D = 3 the bit lands on the nibble's sign and OR-ing 0001
-// gives -+0.5 s.  Scaling the matching A entries by 4, 2, 1, -+2 turns every product into
+// gives -0.5 s.  Scaling the matching A entries by 4, 2, 1, -2 turns every product into
 // a (s + 1) or a s, and the constant sum over the first three nibble positions is removed
 // after the product.
 //
@@ -90,23 +90,16 @@ __device__ __forceinline__ f32x4 mma(const i32x8& a, const i32x4& b, f32x4 c, in
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 2, 4, 0, sa, 0, 127);
 }
 
-// fp4 B operand of one plane word (see the file comment); the nibble-sign dword gives -0.5 s
-__device__ __forceinline__ i32x4 fp4_of(uint32_t w) {
+// fp4 B operand of one plane word (see the file comment); the nibble-sign dword gives -0.5 s:
+// (w & 0x88888888) | 0x11111111 as one bitfield insert, `ones` holding 0x11111111
+__device__ __forceinline__ i32x4 fp4_of(uint32_t w, uint32_t ones) {
   i32x4 b;
   b[0] = (int)(w & 0x11111111u);
   b[1] = (int)(w & 0x22222222u);
   b[2] = (int)(w & 0x44444444u);
-  b[3] = (int)((w & 0x88888888u) | 0x11111111u);
-  return b;
-}
-
-// the same with +0.5 s for the nibble-sign dword (every A weight of the value sums >= 0)
-__device__ __forceinline__ i32x4 fp4_pos(uint32_t w) {
-  i32x4 b;
-  b[0] = (int)(w & 0x11111111u);
-  b[1] = (int)(w & 0x22222222u);
-  b[2] = (int)(w & 0x44444444u);
-  b[3] = (int)(((w ^ 0x88888888u) & 0x88888888u) | 0x11111111u);
+  uint32_t d3;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d3) : "s"(0x88888888u), "v"(w), "v"(ones));
+  b[3] = (int)d3;
   return b;
 }
 
@@ -243,7 +236,7 @@ void decode_mx_scan(MxParams p) {
   const int hh = lane >> 4;                        // C layout: head of this lane
   const int dd = n & 3;                            // token position mod 4 of this lane's tokens
 
-  // ---- query loads first: waits for them must not wait for the tile loads issued later
+  // ---- query loads first (the tile loads are issued once they have arrived)
   float qx[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) qx[e] = load_elem(p.q, ((int64_t)b * p.hq + h0 + wave) * kD + lane + 64 * e, p.q_dtype);
@@ -306,6 +299,11 @@ void decode_mx_scan(MxParams p) {
     }
   };
 
+  // the query and S rows first, then the first tile in flight while the prologue runs
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  asm volatile("" ::: "memory");
+  if (tile_start(0) < t_end) dma(tile_start(0));
+
   // ---- query prologue: q_rot = H D q / sqrt(d) (wave = head), then S q_rot
   {
     const int hd = wave;
@@ -343,8 +341,6 @@ void decode_mx_scan(MxParams p) {
       if (!half) s_sq[h][row] = tot;
     }
   }
-  // the first tile in flight while the key operands are built
-  if (tile_start(0) < t_end) dma(tile_start(0));
   __syncthreads();
   {  // per head (wave): the constants removed after the products
     const int hd = wave;
@@ -361,8 +357,8 @@ void decode_mx_scan(MxParams p) {
         cs += s_sq[hd][j];
       }
     }
-    cc = wave_sum(cc);
-    cs = wave_sum(cs);
+    cc = wave_sum_fast(cc);
+    cs = wave_sum_fast(cs);
     if (lane == 0) {
       s_hc[hd][0] = cc;
       s_hc[hd][1] = cs;
@@ -430,6 +426,7 @@ void decode_mx_scan(MxParams p) {
   const float lscale = p.scale * 1.4426950408889634f;   // logits in the log2 domain
   const float cc_h = s_hc[hh][0], cs_h = s_hc[hh][1];
   const float lsg = lscale * p.gamma;
+  const uint32_t ones = __builtin_amdgcn_readfirstlane(0x11111111);   // operand of the sign dword
 
   // ---- running state (lane (hh, n)).  The running max moves only when a tile's max
   // exceeds it by more than kLazy (log2 units): weights then stay below 2^kLazy and the
@@ -437,18 +434,19 @@ void decode_mx_scan(MxParams p) {
   constexpr float kLazy = 8.0f;
   float m_run = -INFINITY, l_part = 0.f, u3 = 0.f, u3s = 0.f;
   unsigned long long n_skip = 0;
-  // value sums, one fp32 sum per digit row and 16-coordinate block: arun[c] = sum_k alpha_k
-  // (products of codebook plane k), folded after each tile; accs[c] = sign products, kept on
-  // the matrix cores
-  f32x4 arun[8], accs[8];
+  // value sums of head hh at coordinate 16 c + n: arun[c] = sum_k alpha_k (product of codebook
+  // plane k, its 4 digit rows added), folded after each tile; accs[c] = sign products, one
+  // fp32 sum per digit row, kept on the matrix cores
+  float arun[8];
+  f32x4 accs[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    arun[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    arun[c] = 0.f;
     accs[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   uint32_t* xw = &s_x[wave][0][0][0];
   const int g0 = n >> 3, sx = (n >> 2) & 1;
-  const float fv = dd == 0 ? 4.0f : dd == 1 ? 2.0f : dd == 2 ? 1.0f : 2.0f;  // value A weights
+  const float fv = dd == 0 ? 4.0f : dd == 1 ? 2.0f : dd == 2 ? 1.0f : 2.0f;  // |value A weights|
   const float fvi = 1.0f / fv;
   int* ve = &s_ve[wave][0][0][0];
 
@@ -471,24 +469,24 @@ void decode_mx_scan(MxParams p) {
       f32x4 ach = {0.f, 0.f, 0.f, 0.f}, acl = {0.f, 0.f, 0.f, 0.f};
       f32x4 ash = {0.f, 0.f, 0.f, 0.f}, asl = {0.f, 0.f, 0.f, 0.f};
       {
-        const i32x4 b0 = fp4_of(p0);
+        const i32x4 b0 = fp4_of(p0, ones);
         ach = mma(akh[0], b0, ach, ksh[0]);
         acl = mma(akl[0], b0, acl, ksl[0]);
       }
       if constexpr (NPK >= 2) {
-        const i32x4 b1 = fp4_of(p1);
+        const i32x4 b1 = fp4_of(p1, ones);
         ach = mma(akh[1], b1, ach, ksh[1]);
         acl = mma(akl[1], b1, acl, ksl[1]);
       }
       if constexpr (NPK >= 3) {
-        const i32x4 b2 = fp4_of(p2), b3 = fp4_of(p0 ^ p1 ^ p2);
+        const i32x4 b2 = fp4_of(p2, ones), b3 = fp4_of(p0 ^ p1 ^ p2, ones);
         ach = mma(akh[2], b2, ach, ksh[2]);
         acl = mma(akl[2], b2, acl, ksl[2]);
         ach = mma(akh[3], b3, ach, ksh[3]);
         acl = mma(akl[3], b3, acl, ksl[3]);
       }
       {
-        const i32x4 bs = fp4_of(sg);
+        const i32x4 bs = fp4_of(sg, ones);
         ash = mma(akh[NPK], bs, ash, ksh[NPK]);
         asl = mma(akl[NPK], bs, asl, ksl[NPK]);
       }
@@ -618,11 +616,14 @@ void decode_mx_scan(MxParams p) {
         f32x16 ev, od;
 #pragma unroll
         for (int c4 = 0; c4 < 8; ++c4) {
+          // K = 8 D + i: the last 8 positions are D = 3, whose A weight is -2 (the B nibble
+          // gives -0.5 s there)
           const u32x4 r = *reinterpret_cast<const u32x4*>(src + 4 * c4);
-          ev[2 * c4] = (float)((r[0] >> sh) & 15u);
-          od[2 * c4] = (float)((r[1] >> sh) & 15u);
-          ev[2 * c4 + 1] = (float)((r[2] >> sh) & 15u);
-          od[2 * c4 + 1] = (float)((r[3] >> sh) & 15u);
+          const float sgn = c4 >= 6 ? -1.0f : 1.0f;
+          ev[2 * c4] = sgn * (float)((r[0] >> sh) & 15u);
+          od[2 * c4] = sgn * (float)((r[1] >> sh) & 15u);
+          ev[2 * c4 + 1] = sgn * (float)((r[2] >> sh) & 15u);
+          od[2 * c4 + 1] = sgn * (float)((r[3] >> sh) & 15u);
         }
         const i32x8 op = fp6_row(ev, od);
         const int sc = digit_scale(ve[(type * 4 + ga) * 4 + ha], lane & 3);
@@ -646,20 +647,21 @@ void decode_mx_scan(MxParams p) {
       const uint32_t p2 = bits >= 3 ? T.vw[c][2] : 0u;
       const uint32_t sg = T.vw[c][bits];
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 t0v = mma(au, fp4_pos(p0), z, vsu);
-      f32x4 a = arun[c] + p.alpha_v[wsel][0] * t0v;
+      auto rows = [](const f32x4& t) { return (t[0] + t[1]) + (t[2] + t[3]); };
+      const f32x4 t0v = mma(au, fp4_of(p0, ones), z, vsu);
+      float a = fmaf(p.alpha_v[wsel][0], rows(t0v), arun[c]);
       if (bits >= 2) {
-        const f32x4 t1 = mma(au, fp4_pos(p1), z, vsu);
-        a += p.alpha_v[wsel][1] * t1;
+        const f32x4 t1 = mma(au, fp4_of(p1, ones), z, vsu);
+        a = fmaf(p.alpha_v[wsel][1], rows(t1), a);
       }
       if (bits >= 3) {
-        const f32x4 t2 = mma(au, fp4_pos(p2), z, vsu);
-        const f32x4 t3 = mma(au, fp4_pos(p0 ^ p1 ^ p2), z, vsu);
-        a += p.alpha_v[wsel][2] * t2;
-        a += p.alpha_v[wsel][3] * t3;
+        const f32x4 t2 = mma(au, fp4_of(p2, ones), z, vsu);
+        const f32x4 t3 = mma(au, fp4_of(p0 ^ p1 ^ p2, ones), z, vsu);
+        a = fmaf(p.alpha_v[wsel][2], rows(t2), a);
+        a = fmaf(p.alpha_v[wsel][3], rows(t3), a);
       }
       arun[c] = a;
-      accs[c] = mma(as_, fp4_pos(sg), accs[c], vss);
+      accs[c] = mma(as_, fp4_of(sg, ones), accs[c], vss);
     }
   };
 
@@ -703,8 +705,7 @@ void decode_mx_scan(MxParams p) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (k < FV::planes(bits)) asum += p.alpha_v[wsel][k];
-      const f32x4 ra = arun[c];
-      const float a = ((ra[0] + ra[1]) + (ra[2] + ra[3])) - asum * u3h;
+      const float a = arun[c] - asum * u3h;
       const f32x4 r = accs[c];
       const float qv = ((r[0] + r[1]) + (r[2] + r[3])) - u3sh;
       s_red[wave][hh][16 * c + n] = a;
