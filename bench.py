@@ -4,8 +4,13 @@ One step = the whole path over one batch of synthetic input shaped like a
 Llama-3.1-8B decode layer with a 32K-token context (32 query / 8 KV heads, head dim 128,
 keys and values bf16 with per-channel std log-uniform in [0.5, 8], b = 4 for K and V):
   1. quantize the layer's 32768 keys and 32768 values of all 8 KV heads
-     (rotation, norm, codebook, residual, JL projection on MFMA, packing);
+     (rotation, norm, codebook, residual, JL projection on MFMA, packing; the values are
+     written token-sliced);
   2. one decode step of attention for the 32 query heads straight from a packed cache.
+Beside the timed step the same JSON line reports the other workloads: the single-head
+quality setting (C1), 32 full-size layers of batch 16 at 3.5 bits (C3), batch 4 x 131072
+tokens with key spikes and the Sparse-V gate (C4), and the 10^6-vector search with
+recall@10 (C5).
 The timed steps rotate over SLOTS independent inputs/caches; step k quantizes slot k and
 decodes slot k+1 (written SLOTS-1 steps earlier), so the decoded cache is not resident in
 the 256 MB MALL.  Inputs are resident in HBM before timing starts.
@@ -41,6 +46,12 @@ def _parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", default="all", choices=["all", "C1", "C2", "C3", "C4", "C5"],
+                    help="workloads to run: C2 is the timed step (the `value`); C1 quality, "
+                         "C3 32 layers of batch 16 x 32K at 3.5 bits, C4 batch 4 x 128K with the "
+                         "Sparse-V gate, C5 the 10^6 x 200 search with recall@10")
+    ap.add_argument("--seed", type=int, default=0,
+                    help="offset added to every data and rotation seed")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the other-format / paged / prefill / re-encode measurements that "
                          "follow the timed steps (profiling runs of the main step)")
@@ -54,9 +65,9 @@ def _parse():
                     help="only time the inner-product search on the 10^6 x 200 database "
                          "(the search_1m_x_200 variant) and print its JSON (profiling runs)")
     ap.add_argument("--large-batch", action="store_true",
-                    help="only time decode on the two full-size layers larger than the MALL "
-                         "(batch 16 x 32K at 3.5 bits; batch 4 x 128K, gated and ungated) "
-                         "and print their JSON")
+                    help="only run the two full-size workloads larger than the MALL (C3: 32 "
+                         "layers of batch 16 x 32K at 3.5 bits; C4: batch 4 x 128K, gated and "
+                         "ungated) and print their JSON")
     return ap.parse_args()
 
 
@@ -84,34 +95,243 @@ def _traffic(kernel_srcs, summary: str):
         return None
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(kb, vb, qb, rot_seed):
-    """The oracle as it stands, on the host cores, over the same layer (about 15 s of CPU
-    work): quantize + pack the keys and values of all 8 KV heads x 32768 tokens, then one
-    decode step of attention for the 32 query heads."""
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from threadpoolctl import threadpool_info
+    """The C++ oracle (oracle/tq_oracle.cpp: plain fp64, std::thread over every hardware
+    thread) on the host cores, over the same layer: quantize + pack the keys and values of
+    all 8 KV heads x 32768 tokens, then one decode step (dequantize the packed cache, softmax
+    attention of the 32 query heads).  The single-thread figure runs the same code on one
+    thread over a 1/8 sample (KV head 0 and its 4 query heads)."""
     from oracle import tq_oracle as O
-    from parity_utils import oracle_decode, oracle_pack_cache
-    import tq_inputs as TI
+    from oracle import tq_oracle_cpp as C
     signs, S = O.make_rotation(D, rot_seed)   # the oracle's own draws of the same rotation
-    nt, nh = NTOK, HKV
     fmt = O.Format.uniform(D, BITS)
-    t0 = time.perf_counter()
-    rk, nk, _ = oracle_pack_cache(kb[:, :nh, :nt], fmt, signs, S, bf16=True)
-    rv, nv, _ = oracle_pack_cache(vb[:, :nh, :nt], fmt, signs, S, bf16=True)
-    t1 = time.perf_counter()
-    oracle_decode(TI.bf16_to_f64(qb[:, :nh * (HQ // HKV)]), rk, nk, rv, nv, [nt], fmt, fmt,
-                  signs, S, signs, S, 1 / math.sqrt(D))
-    t2 = time.perf_counter()
-    packed = 2 * nh * nt * (fmt.record_bytes() + 4)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": packed / (t2 - t1) / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"whole layer, {nh} KV heads x {nt} tokens: quantize+pack {2 * nh * nt} vectors "
-                      f"({t1 - t0:.2f} s, {nt / (t1 - t0) * (nh / HKV):.3g} layer-tokens/s), "
-                      f"decode {nh * HQ // HKV} query heads ({t2 - t1:.2f} s); value = packed "
-                      f"K+V bytes decoded per second",
-            "quantize_tokens_per_s": nt * nh / HKV / (t1 - t0)}
+    cb = O.codebook(D, BITS)
+    G = HQ // HKV
+
+    def bf(a):
+        return a.astype(np.uint32).view(np.uint32) << 16
+
+    def run(nh, threads):
+        kx = (bf(kb[:, :nh]).view(np.float32)).reshape(-1, D).astype(np.float64)
+        vx = (bf(vb[:, :nh]).view(np.float32)).reshape(-1, D).astype(np.float64)
+        q = (bf(qb[:, :nh * G]).view(np.float32)).astype(np.float64)
+        t0 = time.perf_counter()
+        rk, nk, rrk = C.quantize(kx, fmt, signs, S, cb, threads=threads)
+        rv, nv, rrv = C.quantize(vx, fmt, signs, S, cb, threads=threads)
+        t1 = time.perf_counter()
+        kt = C.dequantize(rk, nk, rrk, fmt, signs, S, cb, threads=threads).reshape(BATCH, nh, NTOK, D)
+        vt = C.dequantize(rv, nv, rrv, fmt, signs, S, cb, threads=threads).reshape(BATCH, nh, NTOK, D)
+        C.attend(q, kt, vt, [NTOK], 1 / math.sqrt(D), threads=threads)
+        t2 = time.perf_counter()
+        packed = 2 * BATCH * nh * NTOK * (fmt.record_bytes() + 4)
+        return packed / (t2 - t1) / 1e9, BATCH * nh * NTOK / (t1 - t0), t1 - t0, t2 - t1
+
+    threads = C.hardware_threads()
+    gbs, qtok, tq_, td = run(HKV, 0)
+    gbs1, qtok1, tq1, td1 = run(1, 1)
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"C++ fp64 oracle, {threads} threads, whole layer: quantize+pack "
+                      f"{2 * HKV * NTOK} vectors ({tq_:.2f} s), decode of {HQ} query heads "
+                      f"(dequantize the packed K and V, softmax attention; {td:.2f} s); value = "
+                      f"packed K+V bytes decoded per second",
+            "quantize_tokens_per_s": round(qtok, 1),
+            "single_thread": {"value": round(gbs1, 5), "unit": "GB/s",
+                              "quantize_tokens_per_s": round(qtok1, 1),
+                              "sample": f"1 thread, KV head 0 with its {G} query heads (1/8 of "
+                                        f"the layer): quantize {tq1:.2f} s, decode {td1:.2f} s"}}
+
+
+def _softmax_rows(x):
+    m = x.max(axis=1, keepdims=True)
+    e = np.exp(x - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _c1_quality(tq, torch, dev, TI, seed):
+    """Single head, d = 128: 4096 keys and values N(0, 1) fp32 with 4 of 128 channels scaled
+    x20, 64 queries N(0, 1); b = 3 for K and V (2-bit codebook + QJL, values token-sliced),
+    quantized and decoded by the library (logits returned), against exact attention over
+    the unquantized fp32 inputs (computed here in fp64)."""
+    k, v, q, ch = TI.c1_inputs(seed=TI.data_seed(1) + seed)
+    n, d = k.shape
+    fk = tq.Format.uniform(d, 2)
+    fv = fk.sliced()
+    signs, S = tq.make_rotation(d, TI.rotation_seed(1) + seed)
+    Sd = torch.from_numpy(S).to(dev)
+    tk, tv = tq.Tables(fk, signs, Sd), tq.Tables(fv, signs, Sd)
+    ck, nk = tq.quantize_kv(torch.from_numpy(k).to(dev), fk, tk)
+    cv, nv = tq.quantize_kv(torch.from_numpy(v).to(dev), fv, tv)
+    rb = fk.record_bytes()
+    qt = torch.from_numpy(q).to(dev).view(1, q.shape[0], d)
+    seq = torch.tensor([n], dtype=torch.int32, device=dev)
+    out, lg = tq.attend_decode(qt, ck.view(1, 1, n, rb), nk.view(1, 1, n, 2),
+                               cv.view(1, 1, n // 32, 32 * rb), nv.view(1, 1, n, 2), seq, fk, tk,
+                               fv, tv, logits=True)
+    torch.cuda.synchronize()
+    lq, oq = lg[0].double().cpu().numpy(), out[0].double().cpu().numpy()
+    k64, v64, q64 = k.astype(np.float64), v.astype(np.float64), q.astype(np.float64)
+    le = q64 @ k64.T / math.sqrt(d)
+    pe, pq = _softmax_rows(le), _softmax_rows(lq)
+    oe = pe @ v64
+    kl = np.sum(pe * (np.log(np.maximum(pe, 1e-300)) - np.log(np.maximum(pq, 1e-300))), axis=1)
+    rel = np.linalg.norm(oq - oe, axis=1) / np.linalg.norm(oe, axis=1)
+    return {"workload": "single head, d=128, 4096 keys/values N(0,1) fp32 with 4 of 128 channels "
+                        "x20, 64 queries N(0,1); b=3 (2-bit codebook + 1 QJL bit), values "
+                        "token-sliced; against exact fp32-input attention",
+            "outlier_channels": [int(c) for c in ch],
+            "logit_rmse_over_sigma": float(np.sqrt(np.mean((lq - le) ** 2)) / np.std(le)),
+            "logit_max_abs_err": float(np.max(np.abs(lq - le))),
+            "softmax_max_abs_dp": float(np.max(np.abs(pq - pe))),
+            "kl_mean": float(np.mean(kl)), "kl_max": float(np.max(kl)),
+            "out_rel_l2_mean": float(np.mean(rel)), "out_rel_l2_max": float(np.max(rel))}
+
+
+def _decode_roofline(name, nbytes, t):
+    gbs = nbytes / t / 1e9
+    return {"bound": "hbm", "kernel": name, "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+
+
+def _c3_layers(tq, torch, dev, TI, seed, n_layers=32, batch=16, dec_steps=4):
+    """32 full-size layers, batch 16 x 32768 tokens each, 32 q / 8 kv heads, distinct seeds
+    per layer (data and rotation), K and V at 3.5 bits (3-bit codebook on rotated
+    coordinates 0-63, 2-bit on 64-127, + QJL; values token-sliced).  Per layer: the prefill
+    quantize of its 32768 new tokens per sequence (K then V, HIP events around each launch),
+    then steady-state decode steps over the layer's packed cache."""
+    ntok = NTOK
+    fk = tq.Format(D, 3, 2, 64)
+    fv = fk.sliced()
+    rb = fk.record_bytes()
+    nvec = batch * HKV * ntok
+    ck = torch.empty((nvec, rb), dtype=torch.uint8, device=dev)
+    nk = torch.empty((nvec, 2), dtype=torch.float16, device=dev)
+    cv = torch.empty((nvec // 32, 32 * rb), dtype=torch.uint8, device=dev)
+    nv = torch.empty((nvec, 2), dtype=torch.float16, device=dev)
+    ws = torch.empty(tq.attend_workspace_bytes(batch, HQ, HKV, ntok, D), dtype=torch.uint8, device=dev)
+    out = torch.empty((batch, HQ, D), dtype=torch.float32, device=dev)
+    seq = torch.full((batch,), ntok, dtype=torch.int32, device=dev)
+    t_q, t_d = [], []
+    for layer in range(n_layers):
+        kx, vx = TI.kv_layer_device(batch, HKV, ntok, D, TI.data_seed(3, layer) + seed, dev)
+        signs, S = tq.make_rotation(D, TI.rotation_seed(3, layer) + seed)
+        Sd = torch.from_numpy(S).to(dev)
+        tk, tv = tq.Tables(fk, signs, Sd), tq.Tables(fv, signs, Sd)
+        qb = TI.decode_queries(batch, HQ, D, TI.data_seed(3, layer) + seed)
+        q = torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        tq.quantize_kv(kx.view(-1, D), fk, tk, codes=ck, norms=nk)
+        tq.quantize_kv(vx.view(-1, D), fv, tv, codes=cv, norms=nv)
+        ev[1].record()
+        dec = lambda: tq.attend_decode(q, ck.view(batch, HKV, ntok, rb), nk.view(batch, HKV, ntok, 2),
+                                       cv.view(batch, HKV, ntok // 32, 32 * rb),
+                                       nv.view(batch, HKV, ntok, 2), seq, fk, tk, fv, tv,
+                                       workspace=ws, out=out)
+        dec()
+        ev[2].record()
+        for _ in range(dec_steps):
+            dec()
+        ev[3].record()
+        torch.cuda.synchronize()
+        t_q.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        t_d.append(ev[2].elapsed_time(ev[3]) * 1e-3 / dec_steps)
+        del kx, vx
+    packed = 2 * nvec * (rb + 4)
+    td = float(np.mean(t_d))
+    return {"workload": f"{n_layers} layers x batch {batch} x {ntok} tokens, 32 q / 8 kv heads, "
+                        "head_dim 128, distinct seeds per layer; K and V at 3.5 bits (3/2-bit "
+                        "codebook split at 64 + QJL, 60 B per vector with norms), values "
+                        "token-sliced",
+            "layers": n_layers, "packed_bytes_per_layer": packed,
+            "prefill_quantize_tokens_per_s": round(n_layers * batch * ntok / float(np.sum(t_q)), 1),
+            "prefill_quantize_ms_per_layer": round(float(np.mean(t_q)) * 1e3, 3),
+            "decode_us": round(td * 1e6, 3), "decode_us_min_layer": round(float(np.min(t_d)) * 1e6, 3),
+            "decode_us_max_layer": round(float(np.max(t_d)) * 1e6, 3),
+            "decode_gbs": round(packed / td / 1e9, 2),
+            "decode_pct_hbm_peak": round(100.0 * packed / td / 1e9 / HBM_PEAK_GBS, 2),
+            "roofline": _decode_roofline("decode_mx_scan+decode_combine", packed, td)}
+
+
+def _c4_sparse_v(tq, torch, dev, TI, seed, steps, tau=1e-4):
+    """Batch 4 x 131072 tokens, 32 q / 8 kv heads; keys at b = 4 with 1% of token positions
+    per sequence carrying x10 keys, values at b = 3 (token-sliced).  Decode gated
+    (tau = 1e-4) and ungated on the same packed cache, interleaved, HIP events around each
+    launch.  skipped_rows = value rows (KV head, token) the gate left unread, counted by the
+    kernel on one gated pass; the softmax mass of the rows under tau (from the ungated
+    logits) bounds the mass the gate dropped, since a dropped row's running weight
+    estimate, at least its final weight, was under tau."""
+    batch, ntok = 4, 131072
+    fk = tq.Format.uniform(D, 3)
+    fv = tq.Format.uniform(D, 2).sliced()
+    kx, vx = TI.kv_layer_device(batch, HKV, ntok, D, TI.data_seed(4) + seed, dev, spike_frac=0.01)
+    signs, S = tq.make_rotation(D, TI.rotation_seed(4) + seed)
+    Sd = torch.from_numpy(S).to(dev)
+    tk, tv = tq.Tables(fk, signs, Sd), tq.Tables(fv, signs, Sd)
+    qb = TI.decode_queries(batch, HQ, D, TI.data_seed(4) + seed)
+    q = torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tq.quantize_kv(kx.view(-1, D), fk, tk)   # warm-up
+    torch.cuda.synchronize()
+    ev[0].record()
+    ck, nk = tq.quantize_kv(kx.view(-1, D), fk, tk)
+    ev[1].record()
+    cv, nv = tq.quantize_kv(vx.view(-1, D), fv, tv)
+    ev[2].record()
+    torch.cuda.synchronize()
+    t_q = (ev[0].elapsed_time(ev[1]) + ev[1].elapsed_time(ev[2])) * 1e-3
+    del kx, vx
+    rbk, rbv = fk.record_bytes(), fv.record_bytes()
+    ck, nk = ck.view(batch, HKV, ntok, rbk), nk.view(batch, HKV, ntok, 2)
+    cv, nv = cv.view(batch, HKV, ntok // 32, 32 * rbv), nv.view(batch, HKV, ntok, 2)
+    seq = torch.full((batch,), ntok, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.attend_workspace_bytes(batch, HQ, HKV, ntok, D), dtype=torch.uint8, device=dev)
+    out_u = torch.empty((batch, HQ, D), dtype=torch.float32, device=dev)
+    out_g = torch.empty_like(out_u)
+    dec = lambda t, o, sk=None: tq.attend_decode(q, ck, nk, cv, nv, seq, fk, tk, fv, tv, tau=t,
+                                                 skipped=sk, workspace=ws, out=o)
+    sk = torch.zeros(1, dtype=torch.int64, device=dev)
+    dec(0.0, out_u); dec(tau, out_g, sk)
+    torch.cuda.synchronize()
+    skipped = int(sk.item())
+    out_diff = float((out_g - out_u).abs().max())
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(); dec(0.0, out_u); e[1].record(); dec(tau, out_g); e[2].record()
+    torch.cuda.synchronize()
+    t_u = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_g = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    _, lg = tq.attend_decode(q, ck, nk, cv, nv, seq, fk, tk, fv, tv, logits=True, workspace=ws)
+    p = torch.softmax(lg.double(), dim=-1)
+    below = torch.where(p < tau, p, torch.zeros_like(p)).sum(dim=-1)
+    del lg, p
+    rows = batch * HKV * ntok
+    packed = rows * (rbk + rbv + 8)
+    return {"workload": "batch 4 x 131072 tokens, 32 q / 8 kv heads, head_dim 128, 1% of token "
+                        "positions with x10 keys; K b=4 (3-bit codebook + QJL), V b=3 (2-bit "
+                        "codebook + QJL, token-sliced)",
+            "tau": tau, "packed_bytes": packed,
+            "decode_us_ungated": round(t_u * 1e6, 3), "decode_us_gated": round(t_g * 1e6, 3),
+            "decode_gbs_ungated": round(packed / t_u / 1e9, 2),
+            "decode_gbs_gated": round(packed / t_g / 1e9, 2),
+            "skipped_rows": skipped, "rows": rows, "skipped_frac": round(skipped / rows, 4),
+            "dropped_mass_bound_max": float(below.max()),
+            "dropped_mass_bound_mean": float(below.mean()),
+            "gated_vs_ungated_out_max_abs": out_diff,
+            "quantize_tokens_per_s": round(batch * ntok / t_q, 1),
+            "roofline": _decode_roofline("decode_mx_scan+decode_combine (ungated)", packed, t_u)}
 
 
 def _variant(tq, torch, dev, ks, vs, q, seq, ws, out, fmt_k, fmt_v, signs, S, steps, nvec):
@@ -349,122 +569,7 @@ def _graph_decode_timing(torch, decode, reps=5):
     return ev[0].elapsed_time(ev[1]) * 1e-3 / (reps * SLOTS)
 
 
-def _sparse_v_timing(tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq, ws, out, fmt_k,
-                     tab_k, fmt_v, tab_v, steps, tau=1e-4):
-    """Decode with the Sparse-V gate (tau = 1e-4) against the same decode ungated, on the same
-    packed caches: the two run interleaved (cache slots rotating), each launch bracketed by
-    HIP events on the launch stream.  skipped_frac = value rows (per KV head and token) the
-    gate left unread over all rows, counted by the kernel on one gated pass per slot."""
-    nslot = len(codes_k)
-    batch, hkv, ntok = codes_k[0].shape[:3]
-    dec = lambda s, t, sk=None: tq.attend_decode(q, codes_k[s], norms_k[s], codes_v[s], norms_v[s],
-                                                 seq, fmt_k, tab_k, fmt_v, tab_v, tau=t,
-                                                 skipped=sk, workspace=ws, out=out)
-    sk = torch.zeros(1, dtype=torch.int64, device=dev)
-    for s in range(nslot):
-        dec(s, 0.0); dec(s, tau, sk)
-    torch.cuda.synchronize()
-    skipped = int(sk.item())
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        e = ev[i]
-        e[0].record(); dec(i % nslot, 0.0); e[1].record(); dec(i % nslot, tau); e[2].record()
-    torch.cuda.synchronize()
-    t_u = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
-    t_g = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
-    rk, rv = fmt_k.record_bytes(), fmt_v.record_bytes()
-    rows = batch * hkv * ntok
-    return {"tau": tau, "decode_us_ungated": round(t_u * 1e6, 3),
-            "decode_us_gated": round(t_g * 1e6, 3),
-            "speedup": round(t_u / t_g, 4),
-            "skipped_frac": round(skipped / (rows * nslot), 4),
-            "packed_gbs_ungated": round(rows * (rk + rv + 8) / t_u / 1e9, 2)}
-
-
-def _large_layer(tq, torch, dev, TI, cfg, batch, ntok, fk, fv, spikes):
-    """One full-size layer of the Llama-3.1-8B law (batch x ntok tokens, 8 KV heads),
-    quantized on the GPU; returns the packed caches, queries and decode buffers."""
-    seed = TI.data_seed(cfg)
-    kb, vb, _ = TI.kv_layer(batch, HKV, ntok, D, seed=seed, spike_frac=spikes)
-    qb = TI.decode_queries(batch, HQ, D, seed)
-    signs, S = tq.make_rotation(D, TI.rotation_seed(cfg))
-    Sd = torch.from_numpy(S).to(dev)
-    tk, tv = tq.Tables(fk, signs, Sd), tq.Tables(fv, signs, Sd)
-    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-    k0, v0 = bf(kb).view(-1, D), bf(vb).view(-1, D)
-    del kb, vb
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    tq.quantize_kv(k0, fk, tk)                       # warm-up
-    ev[0].record()
-    ck, nk = tq.quantize_kv(k0, fk, tk)
-    ev[1].record()
-    cv, nv = tq.quantize_kv(v0, fv, tv)
-    ev[2].record()
-    torch.cuda.synchronize()
-    del k0, v0
-    shp = (batch, HKV, ntok)
-    caches = (ck.view(*shp, -1), nk.view(*shp, 2), cv.view(*shp, -1), nv.view(*shp, 2))
-    q = bf(qb)
-    seq = torch.full((batch,), ntok, dtype=torch.int32, device=dev)
-    ws = torch.zeros(tq.attend_workspace_bytes(batch, HQ, HKV, ntok, D), dtype=torch.uint8,
-                     device=dev)
-    out = torch.empty((batch, HQ, D), dtype=torch.float32, device=dev)
-    t_q = (ev[0].elapsed_time(ev[1]) + ev[1].elapsed_time(ev[2])) * 1e-3
-    return caches, q, seq, ws, out, tk, tv, t_q
-
-
-def _large_batch(tq, torch, dev, TI, steps):
-    """The two full-size layers beside the 32K batch-1 step, each decoded from one packed
-    cache larger than the MALL: batch 16 x 32768 tokens at 3.5 bits (3-bit codebook on
-    rotated coordinates 0-63, 2-bit on 64-127, + QJL; 60 B per vector with its norms), and
-    batch 4 x 131072 tokens with 1% of token positions carrying x10 keys, K b = 4, V b = 3,
-    decoded gated (tau = 1e-4) and ungated.  For the gated layer the softmax mass of the
-    tokens under tau (from the ungated logits) bounds the mass the gate drops: a dropped
-    token's running weight estimate, which is at least its final weight, was under tau."""
-    res = {}
-    fmt = tq.Format(D, 3, 2, 64)
-    (ck, nk, cv, nv), q, seq, ws, out, tk, tv, t_q = _large_layer(
-        tq, torch, dev, TI, 3, 16, NTOK, fmt, fmt, 0.0)
-    dec = lambda: tq.attend_decode(q, ck, nk, cv, nv, seq, fmt, tk, fmt, tv, workspace=ws, out=out)
-    for _ in range(3):
-        dec()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    for i in range(steps):
-        ev[i].record(); dec()
-    ev[steps].record()
-    torch.cuda.synchronize()
-    t = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])) * 1e-3
-    nbytes = 2 * ck.shape[0] * HKV * NTOK * (fmt.record_bytes() + 4)
-    res["batch16_32k_b3.5"] = {
-        "workload": "batch 16 x 32768 tokens, 32 q / 8 kv heads, head_dim 128, K and V at 3.5 "
-                    "bits (3/2-bit codebook split at 64 + QJL, 60 B per vector)",
-        "packed_bytes": nbytes, "decode_us": round(t * 1e6, 3),
-        "decode_gbs": round(nbytes / t / 1e9, 2),
-        "decode_pct_hbm_peak": round(100.0 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2),
-        "quantize_tokens_per_s": round(16 * NTOK / t_q, 1)}
-    del ck, nk, cv, nv, ws
-    torch.cuda.empty_cache()
-
-    ntok = 131072
-    fk, fv = tq.Format.uniform(D, 3), tq.Format.uniform(D, 2)
-    (ck, nk, cv, nv), q, seq, ws, out, tk, tv, t_q = _large_layer(
-        tq, torch, dev, TI, 4, 4, ntok, fk, fv, 0.01)
-    r = _sparse_v_timing(tq, torch, dev, q, [ck], [nk], [cv], [nv], seq, ws, out, fk, tk, fv, tv,
-                         steps)
-    _, lg = tq.attend_decode(q, ck, nk, cv, nv, seq, fk, tk, fv, tv, logits=True, workspace=ws)
-    p = torch.softmax(lg.double(), dim=-1)
-    below = torch.where(p < r["tau"], p, torch.zeros_like(p)).sum(dim=-1)
-    r["mass_under_tau_max"] = float(below.max())
-    r["quantize_tokens_per_s"] = round(4 * ntok / t_q, 1)
-    r["workload"] = ("batch 4 x 131072 tokens, 32 q / 8 kv heads, head_dim 128, 1% of token "
-                     "positions with x10 keys; K b=4 (3-bit codebook + QJL), V b=3 (2-bit "
-                     "codebook + QJL)")
-    res["batch4_128k_sparse_v"] = r
-    return res
-
-
-def _search_timing(tq, torch, dev, TI, reps=2):
+def _search_timing(tq, torch, dev, TI, reps=2, seed=0):
     """Inner-product search on the 10^6 x 200 database (unit vectors, std i^-0.3 per
     coordinate), zero-padded to d = 256 and packed at b = 4; 10^4 queries from the same law,
     top-10.  Times the index build (quantize of the database) and the search of all queries.
@@ -473,9 +578,9 @@ def _search_timing(tq, torch, dev, TI, reps=2):
     are split into fp16 hi + lo halves, so it issues 5 products where the dot products
     count 2."""
     n_db, n_q, d_in, d, k = 10 ** 6, 10 ** 4, 200, 256, 10
-    db = torch.from_numpy(TI.search_set(n_db, d_in, seed=TI.data_seed(5))).to(dev)
-    qs = torch.from_numpy(TI.search_set(n_q, d_in, seed=TI.data_seed(5) + 1)).to(dev)
-    signs, S = tq.make_rotation(d, TI.rotation_seed(5))
+    db = torch.from_numpy(TI.search_set(n_db, d_in, seed=TI.data_seed(5) + seed)).to(dev)
+    qs = torch.from_numpy(TI.search_set(n_q, d_in, seed=TI.data_seed(5) + seed + 1)).to(dev)
+    signs, S = tq.make_rotation(d, TI.rotation_seed(5) + seed)
     fmt = tq.Format.uniform(d, BITS)
     tab = tq.Tables(fmt, signs, torch.from_numpy(S).to(dev))
     codes = torch.empty((n_db, fmt.record_bytes()), dtype=torch.uint8, device=dev)
@@ -495,6 +600,16 @@ def _search_timing(tq, torch, dev, TI, reps=2):
 
     tb = timed(build)
     ts = timed(search)
+    # recall@10 against the exact top-10 of the unquantized fp32 inner products, all queries
+    ids, _ = search()
+    hit = 0
+    for s0 in range(0, n_q, 500):
+        sc = qs[s0:s0 + 500] @ db.T
+        ex = torch.topk(sc, k, dim=1).indices
+        est = ids[s0:s0 + 500]
+        hit += int((est.unsqueeze(2) == ex.unsqueeze(1)).any(dim=2).sum())
+        del sc
+    recall = hit / (n_q * k)
     # unbatched: one query (and one block of 32) streams the whole packed database
     t1 = timed(lambda: tq.ip_search(qs[:1], codes, norms, fmt, tab, k=k, workspace=ws))
     t32 = timed(lambda: tq.ip_search(qs[:32], codes, norms, fmt, tab, k=k, workspace=ws))
@@ -502,6 +617,9 @@ def _search_timing(tq, torch, dev, TI, reps=2):
     flops = 2.0 * 2 * d * n_db * n_q
     tfs = flops / ts / 1e12
     return {"db_vectors": n_db, "d_in": d_in, "d": d, "queries": n_q, "k": k,
+            "recall_at_10": round(recall, 4),
+            "recall_reference": "exact top-10 of the fp32 inner products over all 10^6 vectors, "
+                                "every query",
             "format": "3-bit codebook + 1 QJL bit (132 B/vector)",
             "index_build_ms": round(tb * 1e3, 3), "index_vectors_per_s": round(n_db / tb, 1),
             "search_ms": round(ts * 1e3, 3), "queries_per_s": round(n_q / ts, 1),
@@ -534,148 +652,170 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.search_only:
-        print(json.dumps({"search_1m_x_200": _search_timing(tq, torch, dev, TI)}), flush=True)
-        return
-
-    if args.large_batch:
-        print(json.dumps(_large_batch(tq, torch, dev, TI, args.steps)), flush=True)
-        return
-
-    seed = TI.data_seed(2)
-    kb, vb, _ = TI.kv_layer(BATCH, HKV, NTOK, D, seed=seed)
-    qb = TI.decode_queries(BATCH, HQ, D, seed)
-    signs, S = tq.make_rotation(D, TI.rotation_seed(2))
-    fmt = tq.Format.uniform(D, BITS)
-    tab = tq.Tables(fmt, signs, torch.from_numpy(S).to(dev))
-    rb = fmt.record_bytes()
-    nvec = BATCH * HKV * NTOK
-
-    k0 = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
-    v0 = torch.from_numpy(vb.view(np.int16)).to(dev).view(torch.bfloat16)
-    if args.prefill_only:
-        print(json.dumps({"prefill_chunk": _prefill_timing(tq, torch, dev, [k0], [v0], fmt, tab)}),
+        print(json.dumps({"search_1m_x_200": _search_timing(tq, torch, dev, TI, seed=args.seed)}),
               flush=True)
         return
-    # SLOTS distinct inputs (token order rotated per slot: same law, different bytes)
-    ks = [torch.roll(k0, shifts=4099 * i, dims=2).contiguous() for i in range(SLOTS)]
-    vs = [torch.roll(v0, shifts=4099 * i, dims=2).contiguous() for i in range(SLOTS)]
-    del k0, v0
-    codes_k = [torch.empty((BATCH, HKV, NTOK, rb), dtype=torch.uint8, device=dev) for _ in range(SLOTS)]
-    codes_v = [torch.empty_like(c) for c in codes_k]
-    norms_k = [torch.empty((BATCH, HKV, NTOK, 2), dtype=torch.float16, device=dev) for _ in range(SLOTS)]
-    norms_v = [torch.empty_like(n) for n in norms_k]
-    q = torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16)
-    seq = torch.full((BATCH,), NTOK, dtype=torch.int32, device=dev)
-    ws = torch.zeros(tq.attend_workspace_bytes(BATCH, HQ, HKV, NTOK, D), dtype=torch.uint8, device=dev)
-    out = torch.empty((BATCH, HQ, D), dtype=torch.float32, device=dev)
-
-    def quantize(s):
-        tq.quantize_kv(ks[s].view(-1, D), fmt, tab, codes=codes_k[s].view(nvec, rb),
-                       norms=norms_k[s].view(nvec, 2))
-
-    def quantize_v(s):
-        tq.quantize_kv(vs[s].view(-1, D), fmt, tab, codes=codes_v[s].view(nvec, rb),
-                       norms=norms_v[s].view(nvec, 2))
-
-    def decode(s):
-        tq.attend_decode(q, codes_k[s], norms_k[s], codes_v[s], norms_v[s], seq, fmt, tab,
-                         workspace=ws, out=out)
-
-    for s in range(SLOTS):              # every slot holds a packed cache before timing
-        quantize(s)
-        quantize_v(s)
-    for k in range(args.warmup):
-        quantize(k % SLOTS); quantize_v(k % SLOTS); decode((k + 1) % SLOTS)
-    torch.cuda.synchronize()
-
-    steps = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(steps):
-        e = ev[k]
-        e[0].record()
-        quantize(k % SLOTS)
-        e[1].record()
-        quantize_v(k % SLOTS)
-        e[2].record()
-        decode((k + 1) % SLOTS)
-        e[3].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    qk = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    qv = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-    dc = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
-    packed_bytes = 2 * nvec * (rb + 4)                      # K + V records and norms read
-    decode_gbs = packed_bytes * steps / dc.sum() / 1e9
-    q_launch = float(np.concatenate([qk, qv]).mean())
-    flops_launch = 2.0 * D * D * nvec                         # S r per vector
-    q_tfs = flops_launch / q_launch / 1e12
-    qtoks = NTOK * BATCH * steps / (qk.sum() + qv.sum())
-    copy_gbs = _copy_gbs(torch, dev)
-    trafq = _traffic(["compressed_attention_rotate_amd/csrc/tq_quantize_kernel.h"],
-                     "quantize_llama8b_32k_traffic.txt")
-    trafd = _traffic(["compressed_attention_rotate_amd/csrc/tq_decode_kernel.h",
-                      "compressed_attention_rotate_amd/csrc/tq_decode.hip"],
-                     "decode_llama8b_32k_traffic.txt")
+    if args.large_batch:
+        print(json.dumps({"C3": _c3_layers(tq, torch, dev, TI, args.seed),
+                          "C4": _c4_sparse_v(tq, torch, dev, TI, args.seed, args.steps)}), flush=True)
+        return
+    run = {"C1", "C2", "C3", "C4", "C5"} if args.config == "all" else {args.config}
 
     line = {
         "metric": "decode-attn packed-KV GB/s & % HBM peak; quantize tokens/s (32K ctx, b=4)",
-        "value": round(decode_gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / steps * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
         "config": {"workload": "Llama-3.1-8B-shaped decode layer: batch 1, 32 q / 8 kv heads, "
                                "head_dim 128, 32768 cached tokens, bf16 K/V (per-channel std "
-                               "log-uniform [0.5, 8]), b=4 (3-bit codebook + 1 QJL bit)",
-                   "global_batch": BATCH, "seq_len": NTOK, "parallelism": "none (1 GPU)"},
-        "decode_pct_hbm_peak": round(100.0 * decode_gbs / HBM_PEAK_GBS, 2),
-        "hbm_copy_gbs": round(copy_gbs, 1),
-        "decode_pct_copy_bw": round(100.0 * decode_gbs / copy_gbs, 2),
-        "decode_us": round(float(dc.mean()) * 1e6, 3),
-        "decode_us_graph_replay": round(_graph_decode_timing(torch, decode) * 1e6, 3),
-        "quantize_tokens_per_s": round(qtoks, 1),
-        "quantize_us_per_launch": round(q_launch * 1e6, 3),
-        "roofline": {"bound": "mfma", "kernel": "quantize_kernel<128,3,3>",
-                     "achieved": round(q_tfs, 3), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": round(q_tfs / FP32_MFMA_PEAK_TFS, 4), "traffic": trafq},
-        "roofline_decode": {"bound": "hbm", "kernel": "decode_scan+decode_combine",
-                            "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": trafd},
+                               "log-uniform [0.5, 8]), b=4 (3-bit codebook + 1 QJL bit) for K "
+                               "and V, values token-sliced",
+                   "global_batch": BATCH, "seq_len": NTOK, "parallelism": "none (1 GPU)",
+                   "seed": args.seed},
     }
-    # other formats of the same layer (not part of `value`)
-    if args.no_variants:
-        if not args.no_cpu_baseline:
-            line["cpu_baseline"] = cpu_baseline(kb, vb, qb, TI.rotation_seed(2))
-        print(json.dumps(line), flush=True)
-        return
-    line["variants"] = {
-        name: _variant(tq, torch, dev, ks, vs, q, seq, ws, out, fk, fv, signs, S, steps, nvec)
-        for name, fk, fv in (
-            ("b4_k_mse_only_v", fmt, tq.Format.uniform(D, BITS, qjl=False)),
-            ("b3.5_kv", tq.Format(D, 3, 2, 64), tq.Format(D, 3, 2, 64)),
-            ("b2.5_kv", tq.Format(D, 2, 1, 64), tq.Format(D, 2, 1, 64)))}
-    line["variants"]["paged_b4"] = _paged_timing(tq, torch, dev, ks, q, codes_k, norms_k, codes_v,
-                                                 norms_v, seq, ws, out, fmt, tab, steps, nvec)
-    line["variants"]["prefill_chunk"] = _prefill_timing(tq, torch, dev, ks, vs, fmt, tab)
-    line["variants"]["requantize_b4_to_b3"] = _requant_timing(tq, torch, dev, codes_k, norms_k, fmt,
-                                                              tab, signs, S, steps, nvec)
-    line["variants"]["decay_24k_b3_8k_b4"] = _decay_timing(
-        tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq, fmt, tab, signs, S, steps)
-    line["variants"]["sparse_v_32k_b4"] = _sparse_v_timing(
-        tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq, ws, out, fmt, tab, fmt, tab,
-        steps)
-    line["variants"]["search_1m_x_200"] = _search_timing(tq, torch, dev, TI)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(kb, vb, qb, TI.rotation_seed(2))
+    kb = vb = qb = None
+    if "C2" in run:
+        seed = TI.data_seed(2) + args.seed
+        kb, vb, _ = TI.kv_layer(BATCH, HKV, NTOK, D, seed=seed)
+        qb = TI.decode_queries(BATCH, HQ, D, seed)
+        signs, S = tq.make_rotation(D, TI.rotation_seed(2) + args.seed)
+        fmt = tq.Format.uniform(D, BITS)
+        fsl = fmt.sliced()
+        Sd = torch.from_numpy(S).to(dev)
+        tab, tsl = tq.Tables(fmt, signs, Sd), tq.Tables(fsl, signs, Sd)
+        rb = fmt.record_bytes()
+        nvec = BATCH * HKV * NTOK
+
+        k0 = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
+        v0 = torch.from_numpy(vb.view(np.int16)).to(dev).view(torch.bfloat16)
+        if args.prefill_only:
+            print(json.dumps({"prefill_chunk": _prefill_timing(tq, torch, dev, [k0], [v0], fmt, tab)}),
+                  flush=True)
+            return
+        # SLOTS distinct inputs (token order rotated per slot: same law, different bytes)
+        ks = [torch.roll(k0, shifts=4099 * i, dims=2).contiguous() for i in range(SLOTS)]
+        vs = [torch.roll(v0, shifts=4099 * i, dims=2).contiguous() for i in range(SLOTS)]
+        del k0, v0
+        codes_k = [torch.empty((BATCH, HKV, NTOK, rb), dtype=torch.uint8, device=dev) for _ in range(SLOTS)]
+        norms_k = [torch.empty((BATCH, HKV, NTOK, 2), dtype=torch.float16, device=dev) for _ in range(SLOTS)]
+        codes_vs = [torch.empty((BATCH, HKV, NTOK // 32, 32 * rb), dtype=torch.uint8, device=dev)
+                    for _ in range(SLOTS)]
+        norms_v = [torch.empty_like(n) for n in norms_k]
+        q = torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16)
+        seq = torch.full((BATCH,), NTOK, dtype=torch.int32, device=dev)
+        ws = torch.zeros(tq.attend_workspace_bytes(BATCH, HQ, HKV, NTOK, D), dtype=torch.uint8, device=dev)
+        out = torch.empty((BATCH, HQ, D), dtype=torch.float32, device=dev)
+
+        def quantize(s):
+            tq.quantize_kv(ks[s].view(-1, D), fmt, tab, codes=codes_k[s].view(nvec, rb),
+                           norms=norms_k[s].view(nvec, 2))
+
+        def quantize_v(s):
+            tq.quantize_kv(vs[s].view(-1, D), fsl, tsl, codes=codes_vs[s].view(nvec // 32, 32 * rb),
+                           norms=norms_v[s].view(nvec, 2))
+
+        def decode(s):
+            tq.attend_decode(q, codes_k[s], norms_k[s], codes_vs[s], norms_v[s], seq, fmt, tab, fsl,
+                             tsl, workspace=ws, out=out)
+
+        for s in range(SLOTS):              # every slot holds a packed cache before timing
+            quantize(s)
+            quantize_v(s)
+        for k in range(args.warmup):
+            quantize(k % SLOTS); quantize_v(k % SLOTS); decode((k + 1) % SLOTS)
+        torch.cuda.synchronize()
+
+        steps = args.steps
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            e = ev[k]
+            e[0].record()
+            quantize(k % SLOTS)
+            e[1].record()
+            quantize_v(k % SLOTS)
+            e[2].record()
+            decode((k + 1) % SLOTS)
+            e[3].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+        qk = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+        qv = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+        dc = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+        packed_bytes = 2 * nvec * (rb + 4)                      # K + V records and norms read
+        decode_gbs = packed_bytes * steps / dc.sum() / 1e9
+        q_launch = float(qk.mean())
+        flops_launch = 2.0 * D * D * nvec                         # S r per vector
+        q_tfs = flops_launch / q_launch / 1e12
+        qtoks = NTOK * BATCH * steps / (qk.sum() + qv.sum())
+        copy_gbs = _copy_gbs(torch, dev)
+        trafq = _traffic(["compressed_attention_rotate_amd/csrc/tq_quantize_kernel.h"],
+                         "quantize_llama8b_32k_traffic.txt")
+        trafd = _traffic(["compressed_attention_rotate_amd/csrc/tq_decode_mx.hip",
+                          "compressed_attention_rotate_amd/csrc/tq_decode.hip"],
+                         "decode_sliced_llama8b_32k_traffic.txt")
+        line.update({
+            "value": round(decode_gbs, 2),
+            "ms_per_step": round(wall / steps * 1e3, 4),
+            "decode_pct_hbm_peak": round(100.0 * decode_gbs / HBM_PEAK_GBS, 2),
+            "hbm_copy_gbs": round(copy_gbs, 1),
+            "decode_pct_copy_bw": round(100.0 * decode_gbs / copy_gbs, 2),
+            "decode_us": round(float(dc.mean()) * 1e6, 3),
+            "decode_us_graph_replay": round(_graph_decode_timing(torch, decode) * 1e6, 3),
+            "quantize_tokens_per_s": round(qtoks, 1),
+            "quantize_k_us_per_launch": round(q_launch * 1e6, 3),
+            "quantize_v_sliced_us_per_launch": round(float(qv.mean()) * 1e6, 3),
+            "roofline": {"bound": "mfma", "kernel": "quantize_kernel<128,3,3> (key tensor)",
+                         "achieved": round(q_tfs, 3), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(q_tfs / FP32_MFMA_PEAK_TFS, 4), "traffic": trafq},
+            "roofline_decode": {"bound": "hbm", "kernel": "decode_mx_scan+decode_combine",
+                                "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
+                                "traffic": trafd},
+        })
+        if not args.no_variants:
+            # per-vector value caches of the same slots, for the paths that read that layout
+            codes_v = [torch.empty((BATCH, HKV, NTOK, rb), dtype=torch.uint8, device=dev)
+                       for _ in range(SLOTS)]
+            for s2 in range(SLOTS):
+                tq.quantize_kv(vs[s2].view(-1, D), fmt, tab, codes=codes_v[s2].view(nvec, rb),
+                               norms=norms_v[s2].view(nvec, 2))
+            line["variants"] = {
+                name: _variant(tq, torch, dev, ks, vs, q, seq, ws, out, fk, fv, signs, S, steps, nvec)
+                for name, fk, fv in (
+                    ("b4_per_vector_values", fmt, fmt),
+                    ("b4_k_mse_only_v", fmt, tq.Format.uniform(D, BITS, qjl=False)),
+                    ("b3.5_kv", tq.Format(D, 3, 2, 64), tq.Format(D, 3, 2, 64)),
+                    ("b2.5_kv", tq.Format(D, 2, 1, 64), tq.Format(D, 2, 1, 64)))}
+            line["variants"]["paged_b4"] = _paged_timing(tq, torch, dev, ks, q, codes_k, norms_k,
+                                                         codes_v, norms_v, seq, ws, out, fmt, tab,
+                                                         steps, nvec)
+            line["variants"]["prefill_chunk"] = _prefill_timing(tq, torch, dev, ks, vs, fmt, tab)
+            line["variants"]["requantize_b4_to_b3"] = _requant_timing(tq, torch, dev, codes_k,
+                                                                      norms_k, fmt, tab, signs, S,
+                                                                      steps, nvec)
+            line["variants"]["decay_24k_b3_8k_b4"] = _decay_timing(
+                tq, torch, dev, q, codes_k, norms_k, codes_v, norms_v, seq, fmt, tab, signs, S, steps)
+            del codes_v
+        del ks, vs, codes_k, codes_vs, norms_k, norms_v, ws
+        torch.cuda.empty_cache()
+    configs = {}
+    if "C1" in run:
+        configs["C1"] = _c1_quality(tq, torch, dev, TI, args.seed)
+    if "C3" in run:
+        configs["C3"] = _c3_layers(tq, torch, dev, TI, args.seed)
+        torch.cuda.empty_cache()
+    if "C4" in run:
+        configs["C4"] = _c4_sparse_v(tq, torch, dev, TI, args.seed, min(args.steps, 20))
+        torch.cuda.empty_cache()
+    if "C5" in run:
+        configs["C5"] = _search_timing(tq, torch, dev, TI, seed=args.seed)
+    if configs:
+        line["configs"] = configs
+    if "C2" in run and not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(kb, vb, qb, TI.rotation_seed(2) + args.seed)
     print(json.dumps(line), flush=True)
 
 

@@ -10,7 +10,9 @@ from dataclasses import dataclass, field
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libtq.so")
+# TQ_LIB_PATH may name another build of the same library (the host-sanitizer test loads
+# one that way); by default the in-tree libtq.so
+LIB_PATH = os.environ.get("TQ_LIB_PATH") or os.path.join(_PKG, "libtq.so")
 
 TQ_OK, TQ_ERR_ARG, TQ_ERR_SHAPE, TQ_ERR_ALIGN, TQ_ERR_HIP, TQ_ERR_NOCONV, TQ_ERR_WORKSPACE = \
     0, -1, -2, -3, -4, -5, -6

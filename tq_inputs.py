@@ -25,7 +25,7 @@ import numpy as np
 
 __all__ = [
     "gen", "rotation", "f32_to_bf16_bits", "bf16_to_f32", "bf16_to_f64",
-    "c1_inputs", "kv_layer", "decode_queries", "search_set", "data_seed",
+    "c1_inputs", "kv_layer", "kv_layer_device", "decode_queries", "search_set", "data_seed",
     "rotation_seed",
 ]
 
@@ -110,6 +110,32 @@ def kv_layer(batch: int, hkv: int, ntok: int, d: int, seed: int,
             vv = g.standard_normal((ntok, d), dtype=np.float32) * sig_v[h]
             v_bits[b, h] = f32_to_bf16_bits(vv)
     return k_bits, v_bits, spikes
+
+
+def kv_layer_device(batch: int, hkv: int, ntok: int, d: int, seed: int, device,
+                    spike_frac: float = 0.0, spike_scale: float = 10.0):
+    """The law of ``kv_layer`` drawn on a GPU with torch's seeded generator (a different
+    stream of numbers than the CPU draw): K, V bf16 tensors [batch, hkv, ntok, d] with
+    per-(kv head, channel) std log-uniform in [0.5, 8], and round(spike_frac * ntok)
+    seed-chosen token positions per sequence whose keys are scaled by spike_scale.  For the
+    full-size layers, where a CPU draw of 10^9 values per layer would take minutes."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    lo, hi = float(np.log(0.5)), float(np.log(8.0))
+    sig_k = torch.exp(torch.empty((hkv, 1, d), device=device).uniform_(lo, hi, generator=g))
+    sig_v = torch.exp(torch.empty((hkv, 1, d), device=device).uniform_(lo, hi, generator=g))
+    k = torch.empty((batch, hkv, ntok, d), dtype=torch.bfloat16, device=device)
+    v = torch.empty_like(k)
+    n_sp = int(round(spike_frac * ntok))
+    for b in range(batch):
+        kk = torch.randn((hkv, ntok, d), generator=g, device=device) * sig_k
+        if n_sp:
+            pos = torch.randperm(ntok, generator=g, device=device)[:n_sp]
+            kk[:, pos] *= spike_scale
+        k[b] = kk.to(torch.bfloat16)
+        v[b] = (torch.randn((hkv, ntok, d), generator=g, device=device) * sig_v).to(torch.bfloat16)
+    return k, v
 
 
 def decode_queries(batch: int, hq: int, d: int, seed: int) -> np.ndarray:
