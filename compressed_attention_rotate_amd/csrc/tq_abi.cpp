@@ -417,7 +417,7 @@ int tq_prefill_paged(const tq_format* fk, const tq_tables* tk, const tq_format* 
 
 int64_t tq_requantize_workspace_bytes(int64_t n, int32_t d) {
   if (n < 0 || d != 128) return -1;
-  return (n > 0 ? n : 1) * d * 4;
+  return (n > 0 ? n : 1) * tq_requant_vector_bytes();
 }
 
 int tq_requantize(const tq_format* f_in, const tq_tables* t_in, const void* codes_in,
@@ -438,7 +438,7 @@ int tq_requantize(const tq_format* f_in, const tq_tables* t_in, const void* code
   if (!aligned(codes_in, 16) || !aligned(codes_out, 16) || !aligned(norms_in, 4) ||
       !aligned(norms_out, 4) || !aligned(workspace, 16) || (counters && !aligned(counters, 8)))
     return TQ_ERR_ALIGN;
-  if (workspace_bytes < (int64_t)f_in->d * 4) return TQ_ERR_WORKSPACE;
+  if (workspace_bytes < tq_requant_vector_bytes()) return TQ_ERR_WORKSPACE;
   const int64_t rbi = tq_record_bytes(f_in), rbo = tq_record_bytes(f_out);
   auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);

@@ -89,6 +89,10 @@ int tq_launch_search(const tq_format* f, const tq_tables* t, const void* codes_d
                      int64_t n_q, int32_t k, int64_t* out_ids, float* out_scores,
                      void* workspace, const tq_search_plan& plan, hipStream_t stream);
 
+// Workspace bytes per vector of a tq_requantize chunk (d = 128): fp32 row, record copy of
+// at most 16 words, norms.
+constexpr int64_t tq_requant_vector_bytes() { return 128 * 4 + 64 + 4; }
+
 int tq_launch_requant(const tq_format* fi, const tq_tables* ti, const void* codes_in,
                       const uint16_t* norms_in, int64_t n, const tq_format* fo,
                       const tq_tables* to, void* codes_out, uint16_t* norms_out,

@@ -110,7 +110,46 @@ struct QParams {
   const int32_t* block_table;
   int64_t pos0;
   int32_t max_blocks;
+  // Re-encoding (XT 3): the source record of each row, so that the rare fp64 rechecks
+  // (norm near an fp16 rounding boundary, projection near zero) use the exact fp64
+  // reconstruction instead of the fp32 row: record of row v at src_codes + v * src_words,
+  // its norms (fp16 n16 | r16 << 16) at src_norms[v], the source JL matrix, codebooks
+  // (lo table, then hi table) and widths.
+  const uint32_t* src_codes;
+  const uint32_t* src_norms;
+  const float* src_S;
+  int32_t src_words, src_split_blocks, src_blo, src_bhi, src_qjl;
+  float src_cent[16];
+  double src_gamma;   // sqrt(pi / 2) / d
 };
+
+// Re-encoding: coordinate j of row v's reconstruction in fp64 from its source record,
+// y~_j = n16 c[idx_j] + (gamma r16) sum_i S_in[i][j] (2 sigma_i - 1).
+__device__ __attribute__((noinline)) double src_coord(const QParams& p, int64_t v, int j) {
+  const uint32_t* rec = p.src_codes + v * p.src_words;
+  const uint32_t nr = p.src_norms[v];
+  const int sb = p.src_split_blocks, Q = p.src_qjl ? 1 : 0;
+  auto off = [&](int b) {
+    return b < sb ? b * (p.src_blo + Q) : sb * (p.src_blo + Q) + (b - sb) * (p.src_bhi + Q);
+  };
+  const int blk = j >> 5, bit = j & 31;
+  const int nb = blk < sb ? p.src_blo : p.src_bhi;
+  int idx = 0;
+  for (int q = 0; q < nb; ++q) idx |= (int)((rec[off(blk) + q] >> bit) & 1u) << q;
+  double y = (double)f16_bits_to_f32(nr & 0xFFFFu) * (double)p.src_cent[(blk < sb ? 0 : 8) + idx];
+  if (p.src_qjl) {
+    double st = 0.0;
+    for (int b2 = 0; b2 < 4; ++b2) {
+      const uint32_t sw = rec[off(b2) + (b2 < sb ? p.src_blo : p.src_bhi)];
+      for (int i = 0; i < 32; ++i) {
+        const double sv = (double)p.src_S[(int64_t)(32 * b2 + i) * 128 + j];
+        st += ((sw >> i) & 1u) ? sv : -sv;
+      }
+    }
+    y += (p.src_gamma * (double)f16_bits_to_f32(nr >> 16)) * st;
+  }
+  return y;
+}
 
 // Destination row of vector vg (or -1: not written).
 __device__ __forceinline__ int64_t dest_row(const QParams& p, int64_t vg) {
@@ -198,8 +237,12 @@ __device__ void guard_fix(const QParams& p, int64_t v, int m, int n, const uint6
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
     const int j = lane + 64 * e;
-    float xv = (j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
-    xd[e] = (double)xv;
+    if constexpr (PRE) {
+      xd[e] = (j < p.d_in) ? src_coord(p, v, j) : 0.0;
+    } else {
+      float xv = (j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
+      xd[e] = (double)xv;
+    }
   }
 #pragma unroll
   for (int e = 0; e < NE && !PRE; ++e) {
@@ -493,23 +536,29 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           // norm is recomputed in fp64 from the input row (still in the tile).
           float nf = __builtin_amdgcn_sqrtf(ss[gg]);
           n16[gg] = f32_to_f16_bits(nf);
+          // re-encoded rows carry the fp32 error of their reconstruction (about 1e-7
+          // relative per coordinate): a wider interval there, rechecked from the record
+          constexpr float kMid = PRE ? 4e-6f : 1e-6f;
           const bool near_mid =
-              f32_to_f16_bits(nf * (1.0f - 1e-6f)) != f32_to_f16_bits(nf * (1.0f + 1e-6f));
+              f32_to_f16_bits(nf * (1.0f - kMid)) != f32_to_f16_bits(nf * (1.0f + kMid));
           if (__ballot(near_mid)) {
             const char* rowp = tileb + vloc[gg] * C::kRowB;
             double sd = 0.0;
 #pragma unroll
             for (int s = 0; s < NB; ++s) {
               const int j = 32 * s + c;
-              float x;
-              if (p.staged) {
-                if constexpr (XT == 0 || XT == 3) x = *reinterpret_cast<const float*>(rowp + 4 * j);
-                else x = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * j));
-                x = (valid[gg] && j < p.d_in) ? x : 0.0f;
+              double x;
+              if constexpr (PRE) {
+                x = (valid[gg] && j < p.d_in) ? src_coord(p, v0 + vloc[gg], j) : 0.0;
+              } else if (p.staged) {
+                float xf;
+                if constexpr (XT == 0) xf = *reinterpret_cast<const float*>(rowp + 4 * j);
+                else xf = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * j));
+                x = (valid[gg] && j < p.d_in) ? (double)xf : 0.0;
               } else {
-                x = (valid[gg] && j < p.d_in) ? load_elem(p.x, (v0 + vloc[gg]) * p.ld_x + j, XT) : 0.0f;
+                x = (valid[gg] && j < p.d_in) ? (double)load_elem(p.x, (v0 + vloc[gg]) * p.ld_x + j, XT) : 0.0;
               }
-              sd = fma((double)x, (double)x, sd);
+              sd = fma(x, x, sd);
             }
             sd = half_sum_d(sd);
             const double nrm = sqrt(sd);

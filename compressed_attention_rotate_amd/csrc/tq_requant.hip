@@ -10,12 +10,15 @@
 //              wave tile on v_mfma_f32_16x16x32_f16, with the +-1 signs exact in fp16 and S
 //              split into scaled fp16 hi + lo (the same 2^-22 relative accuracy as the
 //              quantize projection); S^T stays resident in LDS.
-//   quantize:  quantize_kernel with pre-rotated fp32 rows (XT 3).  Its decisions are exact
-//              for those rows (fp64 rechecks of the norm near an fp16 rounding boundary and
-//              of projections near zero); the rows themselves carry the fp32 error of the
-//              reconstruction, about 1e-7 relative per coordinate.
-// In place: a chunk's source rows are complete before its records are rewritten, and a
-// narrower record never reaches the next chunk's input, so codes_out may equal codes_in.
+//   quantize:  quantize_kernel with pre-rotated fp32 rows (XT 3).  The rows carry the fp32
+//              error of the reconstruction, about 1e-7 relative per coordinate; its rare
+//              fp64 rechecks (a norm near an fp16 rounding boundary, a projection near
+//              zero) recompute the reconstruction exactly in fp64 from the source record,
+//              so those decisions are the ones the exact reconstruction gives.
+// The source kernel also copies each chunk's records and norms into the workspace, where
+// the rechecks read them.  In place: a chunk's rows and copies are complete before its
+// records are rewritten, and a narrower record never reaches the next chunk's input, so
+// codes_out may equal codes_in.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,6 +37,8 @@ struct RqParams {
   const uint32_t* norms;  // source norms of this chunk (fp16 n16 | fp16 r16 << 16)
   const float* S;         // source JL matrix [projection i][coordinate j]
   float* out;             // y~ rows [n][128]
+  uint32_t* rec_copy;     // copies of the records [n][words] and norms [n] (for the rechecks)
+  uint32_t* nrm_copy;
   int64_t n;
   int32_t words, split_blocks, bits_lo, bits_hi;
   float gamma;            // sqrt(pi/2) / d
@@ -93,9 +98,12 @@ __global__ __launch_bounds__(64 * kRqWaves) void requant_source(RqParams p) {
     const int64_t v0 = tile * 16;
     const int nv = (int)((p.n - v0) < 16 ? (p.n - v0) : 16);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 4; ++k) {
       if (lane + 64 * k < 16 * W) wrec[lane + 64 * k] = pw[k];
+      if (lane + 64 * k < nv * W) p.rec_copy[v0 * W + lane + 64 * k] = pw[k];
+    }
     if (lane < 16) wnrm[lane] = pn;
+    if (lane < nv) p.nrm_copy[v0 + lane] = pn;
     fetch(tile + stride);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's rows are visible to the wave
     f32x4 acc[8];
@@ -180,11 +188,16 @@ int tq_launch_requant(const tq_format* fi, const tq_tables* ti, const void* code
   using namespace tqk;
   const int ncu = tq_num_cus();
   if (ncu <= 0) return TQ_ERR_HIP;
-  const int64_t chunk = workspace_bytes / (kRqD * 4);
+  // workspace per vector of a chunk: its fp32 row, a copy of its record (at most 16 words)
+  // and of its norms
+  const int64_t chunk = workspace_bytes / tq_requant_vector_bytes();
   const int wi = (int)(tq_record_bytes(fi) / 4), wo = (int)(tq_record_bytes(fo) / 4);
+  char* wsb = reinterpret_cast<char*>(workspace);
   RqParams rp{};
   rp.S = ti->S;
-  rp.out = reinterpret_cast<float*>(workspace);
+  rp.out = reinterpret_cast<float*>(wsb);
+  rp.rec_copy = reinterpret_cast<uint32_t*>(wsb + chunk * kRqD * 4);
+  rp.nrm_copy = reinterpret_cast<uint32_t*>(wsb + chunk * (kRqD * 4 + 64));
   rp.words = wi;
   rp.split_blocks = fi->split / 32;
   rp.bits_lo = fi->bits_lo;
@@ -204,6 +217,16 @@ int tq_launch_requant(const tq_format* fi, const tq_tables* ti, const void* code
   q.staged = 1;  // workspace rows: 16-byte aligned, 512 bytes
   q.cpr = kRqD * 4 / 16;
   q.x = workspace;
+  q.src_codes = rp.rec_copy;
+  q.src_norms = rp.nrm_copy;
+  q.src_S = ti->S;
+  q.src_words = wi;
+  q.src_split_blocks = rp.split_blocks;
+  q.src_blo = rp.bits_lo;
+  q.src_bhi = rp.bits_hi;
+  q.src_qjl = fi->qjl;
+  for (int k = 0; k < 16; ++k) q.src_cent[k] = rp.cent[k];
+  q.src_gamma = std::sqrt(M_PI / 2.0) / kRqD;
   const size_t src_lds = (fi->qjl ? (size_t)kRqD * kRqRowB : 0) + (size_t)kRqWaves * (16 * 16 + 16) * 4;
   const int ilo = rp.bits_lo, ihi = rp.bits_hi;
   const void* src_fn = nullptr;

@@ -331,9 +331,10 @@ int tq_ip_search(const tq_format* fmt, const tq_tables* tab, const void* codes_d
                  int64_t n_q, int32_t k, int64_t* out_ids, float* out_scores,
                  void* workspace, int64_t workspace_bytes, tq_stream_t stream);
 
-/* Workspace bytes tq_requantize uses to re-encode n vectors in one pass (n * d * 4:
- * one fp32 row per vector).  A smaller workspace is allowed: the call then works in
- * chunks of workspace_bytes / (d * 4) vectors. */
+/* Workspace bytes tq_requantize uses to re-encode n vectors in one pass (n * 580 for
+ * d = 128: per vector one fp32 row of the reconstruction, a copy of its record and of its
+ * norms).  A smaller workspace is allowed: the call then works in chunks of
+ * workspace_bytes / 580 vectors. */
 int64_t tq_requantize_workspace_bytes(int64_t n, int32_t d);
 
 /* Temporal decay (zhidx article, section "01 turboquant_plus：介绍与详解": older tokens
@@ -352,8 +353,11 @@ int64_t tq_requantize_workspace_bytes(int64_t n, int32_t d);
  *   norms_out    : device out, n * 2 uint16; may equal norms_in
  *                  Any other overlap between inputs and outputs is an error.
  *   counters     : as for tq_quantize_kv, nullable
- *   workspace    : device, >= d * 4 bytes (see tq_requantize_workspace_bytes); no
+ *   workspace    : device, >= 580 bytes (see tq_requantize_workspace_bytes); no
  *                  initial contents; calls that share it must not overlap in time
+ * The stored norm, codes and signs are those of the exact (fp64) reconstruction outside
+ * the windows the quantize path has: decisions the fp32 reconstruction leaves within
+ * reach of a boundary are recomputed in fp64 from the stored record.
  * n == 0 is a no-op.  Errors: TQ_ERR_ARG (null pointers, different sign flips, bad
  * overlap), TQ_ERR_SHAPE (d != 128), TQ_ERR_ALIGN, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 int tq_requantize(const tq_format* f_in, const tq_tables* t_in, const void* codes_in,

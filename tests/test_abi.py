@@ -206,7 +206,7 @@ def test_requantize_validation_before_launch():
     cin, nin = 0x100000, 0x200000
     cout, nout, ws = 0x300000, 0x400000, 0x500000
     wsb = tq.requantize_workspace_bytes(n)
-    assert wsb == n * 512 and tq.requantize_workspace_bytes(0) == 512
+    assert wsb == n * 580 and tq.requantize_workspace_bytes(0) == 580
 
     def R(n=n, ci=cin, ni=nin, co=cout, no=nout, w=ws, wb=wsb, f_out=fo, t_out=to, f_in=fi, t_in=ti):
         P = ctypes.c_void_p
@@ -215,7 +215,7 @@ def test_requantize_validation_before_launch():
                                  P(w), wb, None)
     assert R(n=0) == E.TQ_OK
     assert R(n=-1) == E.TQ_ERR_ARG
-    assert R(wb=511) == E.TQ_ERR_WORKSPACE
+    assert R(wb=579) == E.TQ_ERR_WORKSPACE
     assert R(co=0x300004) == E.TQ_ERR_ALIGN
     assert R(co=cin + 64) == E.TQ_ERR_ARG                          # overlaps the input records
     assert R(w=nout + 16) == E.TQ_ERR_ARG                          # workspace overlaps norms
