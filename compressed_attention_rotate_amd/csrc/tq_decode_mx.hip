@@ -61,6 +61,9 @@ typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 constexpr int kXWaves = 4;
 constexpr int kXThreads = 64 * kXWaves;
 constexpr int kXTile = 128;      // tokens per wave tile
+// hand-off rows of 32 weights (one head, type and 32-token group) padded to 36 dwords, so the
+// 16 rows one A-operand read touches start on 16 different 4-bank groups
+constexpr int kXRow = 36;
 
 struct MxParams {
   const void* q;
@@ -213,7 +216,7 @@ void decode_mx_scan(MxParams p) {
   __shared__ uint32_t s_ak[NPK + 1][2][6][64];            // key A operands [plane][digits 0-3 / 4-7]
   __shared__ int s_ke[NPK + 1][64];                       // key block exponent of each A lane
   __shared__ int s_ve[kXWaves][2][4][4];                  // value block exponents [type][group][head]
-  __shared__ uint32_t s_x[kXWaves][2][4][kXTile];         // rounded weights [type][head][K]
+  __shared__ uint32_t s_x[kXWaves][2 * 4 * 4 * kXRow];   // rounded weights [type][head][group][K]
   __shared__ float s_m[kXWaves][4][2];
   __shared__ float s_red[kXWaves][4][2 * kD];
   __shared__ __align__(16) uint32_t s_tile[kXWaves][kTileDw];   // next tile, in flight
@@ -444,7 +447,7 @@ void decode_mx_scan(MxParams p) {
     arun[c] = 0.f;
     accs[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
-  uint32_t* xw = &s_x[wave][0][0][0];
+  uint32_t* xw = &s_x[wave][0];
   const int g0 = n >> 3, sx = (n >> 2) & 1;
   const float fv = dd == 0 ? 4.0f : dd == 1 ? 2.0f : dd == 2 ? 1.0f : 2.0f;  // |value A weights|
   const float fvi = 1.0f / fv;
@@ -465,32 +468,31 @@ void decode_mx_scan(MxParams p) {
         p2 = w3 ? T.kw[k][2] : 0u;
         sg = w3 ? T.kw[k][3] : T.kw[k][2];
       }
-      // digits 0-3 and 4-7 in two chains (independent accumulators)
-      f32x4 ach = {0.f, 0.f, 0.f, 0.f}, acl = {0.f, 0.f, 0.f, 0.f};
-      f32x4 ash = {0.f, 0.f, 0.f, 0.f}, asl = {0.f, 0.f, 0.f, 0.f};
+      // digits 0-3 and 4-7 of every plane into one accumulator per term (the 8 key groups
+      // give the scheduler independent chains)
+      f32x4 ac = {0.f, 0.f, 0.f, 0.f}, as = {0.f, 0.f, 0.f, 0.f};
       {
         const i32x4 b0 = fp4_of(p0, ones);
-        ach = mma(akh[0], b0, ach, ksh[0]);
-        acl = mma(akl[0], b0, acl, ksl[0]);
+        ac = mma(akh[0], b0, ac, ksh[0]);
+        ac = mma(akl[0], b0, ac, ksl[0]);
       }
       if constexpr (NPK >= 2) {
         const i32x4 b1 = fp4_of(p1, ones);
-        ach = mma(akh[1], b1, ach, ksh[1]);
-        acl = mma(akl[1], b1, acl, ksl[1]);
+        ac = mma(akh[1], b1, ac, ksh[1]);
+        ac = mma(akl[1], b1, ac, ksl[1]);
       }
       if constexpr (NPK >= 3) {
         const i32x4 b2 = fp4_of(p2, ones), b3 = fp4_of(p0 ^ p1 ^ p2, ones);
-        ach = mma(akh[2], b2, ach, ksh[2]);
-        acl = mma(akl[2], b2, acl, ksl[2]);
-        ach = mma(akh[3], b3, ach, ksh[3]);
-        acl = mma(akl[3], b3, acl, ksl[3]);
+        ac = mma(akh[2], b2, ac, ksh[2]);
+        ac = mma(akl[2], b2, ac, ksl[2]);
+        ac = mma(akh[3], b3, ac, ksh[3]);
+        ac = mma(akl[3], b3, ac, ksl[3]);
       }
       {
         const i32x4 bs = fp4_of(sg, ones);
-        ash = mma(akh[NPK], bs, ash, ksh[NPK]);
-        asl = mma(akl[NPK], bs, asl, ksl[NPK]);
+        as = mma(akh[NPK], bs, as, ksh[NPK]);
+        as = mma(akl[NPK], bs, as, ksl[NPK]);
       }
-      const f32x4 ac = ach + acl, as = ash + asl;
       const float dc = ((ac[0] + ac[1]) + (ac[2] + ac[3]) - cc_h) * lscale;
       const float ds = ((as[0] + as[1]) + (as[2] + as[3]) - cs_h) * lsg;
       const float n16 = f16_bits_to_f32(T.kn[k]), r16 = f16_bits_to_f32(T.kn[k] >> 16);
@@ -592,9 +594,9 @@ void decode_mx_scan(MxParams p) {
           u3 += eu == kZeroExp ? 0.0f : ldexpf(su, eu - 16) * fvi;
           u3s += es == kZeroExp ? 0.0f : ldexpf(ss, es - 16) * fvi;
         }
-        const int kk = 32 * (2 * x + g0) + 8 * dd + 4 * sx;
-        *reinterpret_cast<u32x4*>(&xw[(0 * 4 + hh) * kXTile + kk]) = ru;
-        *reinterpret_cast<u32x4*>(&xw[(1 * 4 + hh) * kXTile + kk]) = rs;
+        const int kk = (2 * x + g0) * kXRow + 8 * dd + 4 * sx;
+        *reinterpret_cast<u32x4*>(&xw[(0 * 4 + hh) * 4 * kXRow + kk]) = ru;
+        *reinterpret_cast<u32x4*>(&xw[(1 * 4 + hh) * 4 * kXRow + kk]) = rs;
         if ((n & 7) == 0) {
           ve[(0 * 4 + 2 * x + g0) * 4 + hh] = eu;
           ve[(1 * 4 + 2 * x + g0) * 4 + hh] = es;
@@ -612,7 +614,7 @@ void decode_mx_scan(MxParams p) {
       const int ga = lane >> 4, ha = (lane & 15) >> 2, sh = 12 - 4 * (lane & 3);
 #pragma unroll
       for (int type = 0; type < 2; ++type) {
-        const uint32_t* src = &xw[(type * 4 + ha) * kXTile + 32 * ga];
+        const uint32_t* src = &xw[((type * 4 + ha) * 4 + ga) * kXRow];
         f32x16 ev, od;
 #pragma unroll
         for (int c4 = 0; c4 < 8; ++c4) {
