@@ -123,32 +123,58 @@ struct QParams {
   double src_gamma;   // sqrt(pi / 2) / d
 };
 
-// Re-encoding: coordinate j of row v's reconstruction in fp64 from its source record,
-// y~_j = n16 c[idx_j] + (gamma r16) sum_i S_in[i][j] (2 sigma_i - 1).
-__device__ __attribute__((noinline)) double src_coord(const QParams& p, int64_t v, int j) {
+// Re-encoding: coordinates j0 .. j0 + N - 1 (N = 2 or 4, j0 a multiple of N, so all in one
+// block of 32) of row v's reconstruction in fp64 from its source record,
+// y~_j = n16 c[idx_j] + (gamma r16) sum_i S_in[i][j] (2 sigma_i - 1).  The N columns of a row
+// of S_in are one vector load; the 32 rows of a sign block are loaded before they are summed
+// (a rare path: 128 loads per lane, 16 rows in flight at a time).
+template <int N>
+__device__ __forceinline__ void src_coords(const QParams& p, int64_t v, int j0, double* y) {
+  static_assert(N == 2 || N == 4, "re-encoding runs at d = 128");
+  typedef float fN __attribute__((ext_vector_type(N)));
   const uint32_t* rec = p.src_codes + v * p.src_words;
   const uint32_t nr = p.src_norms[v];
   const int sb = p.src_split_blocks, Q = p.src_qjl ? 1 : 0;
   auto off = [&](int b) {
     return b < sb ? b * (p.src_blo + Q) : sb * (p.src_blo + Q) + (b - sb) * (p.src_bhi + Q);
   };
-  const int blk = j >> 5, bit = j & 31;
+  const int blk = j0 >> 5, bit0 = j0 & 31;
   const int nb = blk < sb ? p.src_blo : p.src_bhi;
-  int idx = 0;
-  for (int q = 0; q < nb; ++q) idx |= (int)((rec[off(blk) + q] >> bit) & 1u) << q;
-  double y = (double)f16_bits_to_f32(nr & 0xFFFFu) * (double)p.src_cent[(blk < sb ? 0 : 8) + idx];
+  const double n16 = (double)f16_bits_to_f32(nr & 0xFFFFu);
+  int idx[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) idx[e] = 0;
+  for (int q = 0; q < nb; ++q) {
+    const uint32_t w = rec[off(blk) + q];
+#pragma unroll
+    for (int e = 0; e < N; ++e) idx[e] |= (int)((w >> (bit0 + e)) & 1u) << q;
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) y[e] = n16 * (double)p.src_cent[(blk < sb ? 0 : 8) + idx[e]];
   if (p.src_qjl) {
-    double st = 0.0;
+    double st[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) st[e] = 0.0;
     for (int b2 = 0; b2 < 4; ++b2) {
       const uint32_t sw = rec[off(b2) + (b2 < sb ? p.src_blo : p.src_bhi)];
-      for (int i = 0; i < 32; ++i) {
-        const double sv = (double)p.src_S[(int64_t)(32 * b2 + i) * 128 + j];
-        st += ((sw >> i) & 1u) ? sv : -sv;
+      const fN* col = reinterpret_cast<const fN*>(p.src_S + (int64_t)(32 * b2) * 128 + j0);
+#pragma unroll
+      for (int i0 = 0; i0 < 32; i0 += 16) {
+        fN sv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[i] = col[(i0 + i) * (128 / N)];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool one = (sw >> (i0 + i)) & 1u;
+#pragma unroll
+          for (int e = 0; e < N; ++e) st[e] += one ? (double)sv[i][e] : -(double)sv[i][e];
+        }
       }
     }
-    y += (p.src_gamma * (double)f16_bits_to_f32(nr >> 16)) * st;
+    const double gr = p.src_gamma * (double)f16_bits_to_f32(nr >> 16);
+#pragma unroll
+    for (int e = 0; e < N; ++e) y[e] += gr * st[e];
   }
-  return y;
 }
 
 // Destination row of vector vg (or -1: not written).
@@ -233,13 +259,16 @@ __device__ void guard_fix(const QParams& p, int64_t v, int m, int n, const uint6
   constexpr int NB = D / 32;
   constexpr bool PRE = (XT == 3);  // input already in the rotated domain
   const int lane = lane_id();
+  // coordinate of element e of this lane: lane + 64 e, which the FWHT below assumes; for
+  // re-encoded rows (no FWHT) NE lane + e, so that one vector load reads a row of S_in
+  auto jof = [&](int e) { return PRE ? NE * lane + e : lane + 64 * e; };
   double xd[NE];
+  if constexpr (PRE) {
+    src_coords<NE>(p, v, NE * lane, xd);   // re-encoding: every coordinate is < d_in = D
+  } else {
 #pragma unroll
-  for (int e = 0; e < NE; ++e) {
-    const int j = lane + 64 * e;
-    if constexpr (PRE) {
-      xd[e] = (j < p.d_in) ? src_coord(p, v, j) : 0.0;
-    } else {
+    for (int e = 0; e < NE; ++e) {
+      const int j = lane + 64 * e;
       float xv = (j < p.d_in) ? load_elem(p.x, v * p.ld_x + j, XT) : 0.0f;
       xd[e] = (double)xv;
     }
@@ -273,7 +302,7 @@ __device__ void guard_fix(const QParams& p, int64_t v, int m, int n, const uint6
   double dot = 0.0, rr = 0.0;
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
-    const int j = lane + 64 * e;
+    const int j = jof(e);
     const int blk = j >> 5, bit = j & 31;
     const int nb = blk < p.split_blocks ? blo : bhi;
     int idx = 0;
@@ -537,20 +566,27 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
           float nf = __builtin_amdgcn_sqrtf(ss[gg]);
           n16[gg] = f32_to_f16_bits(nf);
           // re-encoded rows carry the fp32 error of their reconstruction (about 1e-7
-          // relative per coordinate): a wider interval there, rechecked from the record
-          constexpr float kMid = PRE ? 4e-6f : 1e-6f;
+          // relative per coordinate, a few 1e-7 of the norm at most, on top of the 6e-7
+          // above): a wider interval there, rechecked from the record
+          constexpr float kMid = PRE ? 2e-6f : 1e-6f;
           const bool near_mid =
               f32_to_f16_bits(nf * (1.0f - kMid)) != f32_to_f16_bits(nf * (1.0f + kMid));
           if (__ballot(near_mid)) {
             const char* rowp = tileb + vloc[gg] * C::kRowB;
             double sd = 0.0;
+            if constexpr (PRE) {   // coordinates NB c .. NB c + NB - 1 of the row (all < d_in)
+              if (valid[gg]) {     // uniform within the half-wave; a row past n has no record
+                double y[NB];
+                src_coords<NB>(p, v0 + vloc[gg], NB * c, y);
 #pragma unroll
-            for (int s = 0; s < NB; ++s) {
+                for (int s = 0; s < NB; ++s) sd = fma(y[s], y[s], sd);
+              }
+            }
+#pragma unroll
+            for (int s = 0; s < NB && !PRE; ++s) {
               const int j = 32 * s + c;
               double x;
-              if constexpr (PRE) {
-                x = (valid[gg] && j < p.d_in) ? src_coord(p, v0 + vloc[gg], j) : 0.0;
-              } else if (p.staged) {
+              if (p.staged) {
                 float xf;
                 if constexpr (XT == 0) xf = *reinterpret_cast<const float*>(rowp + 4 * j);
                 else xf = cvt16<XT>(*reinterpret_cast<const uint16_t*>(rowp + 2 * j));
