@@ -6,47 +6,57 @@
 namespace tqk {
 
 // ----------------------------------------------------------------------------- combine
-// One workgroup per (batch, query head).  Every load of the first 256 splits is issued
-// before the first use: S_v column slices, each split's (m, l) (thread i loads split i) and
-// the first 32 splits' partial sums.  The splits' weights 2^(m_i - M) go through LDS in
-// chunks of 256 splits, so any number of partials fits (segmented caches add theirs up); the
-// sums run in split order, the same order for every thread.
-constexpr int kCombChunk = 32;    // partial sums in flight per thread
+// One workgroup per (batch, query head).  Every load of the first splits is issued before
+// the first use, at most 34 per thread so that one round trip to memory brings them all:
+// the 16 x 4 S_v entries of this thread's part of S^T Q (16-byte loads), each split's (m, l)
+// (thread i loads split i) and the first 32 splits' partial sums, one (A | Q) float pair per
+// thread and split parity.  The splits' weights 2^(m_i - M) go through LDS in chunks of 256
+// splits, so any number of partials fits (segmented caches add theirs up); every sum runs in
+// a fixed order (the denominator in split order, the same for every thread).
+constexpr int kCombPairs = 16;    // partial-sum pairs in flight per thread (one parity)
 constexpr int kCombSplits = 256;  // split weights per LDS chunk
 
 __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int bh = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  __shared__ float red[2][4];
+  __shared__ float red[4];
   __shared__ float scl[kCombSplits];
   __shared__ float lw[kCombSplits];
-  __shared__ float vec[2][kD];
-  __shared__ float part_s[256];
+  __shared__ f32x2 accp[2][kD];      // per split parity: sums of the (A | Q) float pairs
+  __shared__ float vec[2 * kD];      // merged A | Q
+  __shared__ float part_s[8][kD];    // S^T Q over row groups of 16
   const float* parts = p.ws_part + (int64_t)bh * p.n_split * kPartFloats;
   const int np = p.n_split;
-  const int j = tid & 127, half = tid >> 7;
-  float sv[64];  // S_v[64 half + i][j]
+  // S^T Q: thread (column group j4, row group rq) holds S_v[16 rq + i][4 j4 .. 4 j4 + 3]
+  const int j4 = tid & 31, rq = tid >> 5;
+  f32x4 sv[16];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) sv[i] = p.S_v[(int64_t)(64 * half + i) * kD + j];
-  // this thread's split of the first chunk, and the first partial sums
+  for (int i = 0; i < 16; ++i)
+    sv[i] = *reinterpret_cast<const f32x4*>(p.S_v + (int64_t)(16 * rq + i) * kD + 4 * j4);
+  // merge: thread (float pair c2 of A | Q, split parity hs) sums splits hs, hs + 2, ...
+  const int c2 = tid & 127, hs = tid >> 7;
   float m0 = -INFINITY, l0 = 0.0f;
   if (tid < np) {
     m0 = parts[(int64_t)tid * kPartFloats];
     l0 = parts[(int64_t)tid * kPartFloats + 1];
   }
-  float pv[kCombChunk];
+  f32x2 pv[kCombPairs];
 #pragma unroll
-  for (int c = 0; c < kCombChunk; ++c)
-    pv[c] = c < np ? parts[(int64_t)c * kPartFloats + 2 + tid] : 0.0f;
+  for (int k = 0; k < kCombPairs; ++k) {
+    const int sp = hs + 2 * k;
+    pv[k] = sp < np ? *reinterpret_cast<const f32x2*>(parts + (int64_t)sp * kPartFloats + 2 + 2 * c2)
+                    : (f32x2){0.0f, 0.0f};
+  }
   // the largest split maximum
   float M = m0;
   for (int i = tid + kCombSplits; i < np; i += 256) M = fmaxf(M, parts[(int64_t)i * kPartFloats]);
   M = wave_max_fast(M);
-  if (lane == 0) red[0][wave] = M;
+  if (lane == 0) red[wave] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  // thread tid: component tid / 128 (A or Q), coordinate tid % 128
-  float acc = 0.0f, lsum = 0.0f;
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  f32x2 acc = {0.0f, 0.0f};
+  float lsum = 0.0f;
   for (int c0 = 0; c0 < np; c0 += kCombSplits) {
     const int nc = np - c0 < kCombSplits ? np - c0 : kCombSplits;
     if (tid < nc) {
@@ -60,28 +70,47 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
       lw[tid] = sw * l;
     }
     __syncthreads();
-    for (int c = 0; c < nc; c += kCombChunk) {
+    for (int c = 0; c < nc; c += 2 * kCombPairs) {
       if (c0 + c > 0) {
 #pragma unroll
-        for (int k = 0; k < kCombChunk; ++k)
-          pv[k] = c + k < nc ? parts[(int64_t)(c0 + c + k) * kPartFloats + 2 + tid] : 0.0f;
+        for (int k = 0; k < kCombPairs; ++k) {
+          const int sp = c + hs + 2 * k;
+          pv[k] = sp < nc ? *reinterpret_cast<const f32x2*>(parts + (int64_t)(c0 + sp) * kPartFloats + 2 + 2 * c2)
+                          : (f32x2){0.0f, 0.0f};
+        }
       }
 #pragma unroll
-      for (int k = 0; k < kCombChunk; ++k)
-        if (c + k < nc) acc = fmaf(pv[k], scl[c + k], acc);
+      for (int k = 0; k < kCombPairs; ++k) {
+        const int sp = c + hs + 2 * k;
+        if (sp < nc) {
+          acc[0] = fmaf(pv[k][0], scl[sp], acc[0]);
+          acc[1] = fmaf(pv[k][1], scl[sp], acc[1]);
+        }
+      }
     }
     // the denominator, in split order (every thread reads the same LDS values)
     for (int k = 0; k < nc; ++k) lsum += lw[k];
     __syncthreads();
   }
-  vec[half][j] = acc;
+  accp[hs][c2] = acc;
   __syncthreads();
-  // S^T Q: thread (j, half) sums its 64 rows
-  {
-    float s = 0.0f;
+  if (tid < kD) {
+    const f32x2 t = accp[0][tid] + accp[1][tid];
+    vec[2 * tid] = t[0];
+    vec[2 * tid + 1] = t[1];
+  }
+  __syncthreads();
+  {  // S^T Q over this thread's 16 rows and 4 columns
+    f32x4 ps = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 64; ++i) s = fmaf(sv[i], vec[1][64 * half + i], s);
-    part_s[tid] = s;
+    for (int i = 0; i < 16; ++i) {
+      const float qv = vec[kD + 16 * rq + i];
+      ps[0] = fmaf(sv[i][0], qv, ps[0]);
+      ps[1] = fmaf(sv[i][1], qv, ps[1]);
+      ps[2] = fmaf(sv[i][2], qv, ps[2]);
+      ps[3] = fmaf(sv[i][3], qv, ps[3]);
+    }
+    *reinterpret_cast<f32x4*>(&part_s[rq][4 * j4]) = ps;
   }
   __syncthreads();
   if (tid < 64) {
@@ -89,7 +118,10 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int jj = lane + 64 * e;
-      v[e] = vec[0][jj] + part_s[jj] + part_s[128 + jj];
+      float st = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) st += part_s[r][jj];
+      v[e] = vec[jj] + st;
     }
     fwht128(v, lane);
     const float inv = (lsum > 0.0f) ? 1.0f / (lsum * sqrtf((float)kD)) : 0.0f;

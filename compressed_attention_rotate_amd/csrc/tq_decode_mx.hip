@@ -243,11 +243,14 @@ void decode_mx_scan(MxParams p) {
   float qx[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) qx[e] = load_elem(p.q, ((int64_t)b * p.hq + h0 + wave) * kD + lane + 64 * e, p.q_dtype);
-  f32x4 srow[16];   // S rows 32 wave + lane / 2, columns 64 (lane & 1) ..
+  // S rows 32 wave .. 32 wave + 31: srow[4 r + c] holds row 32 wave + 8 r + lane / 8, columns
+  // 32 c + 4 (lane % 8) .. + 3, so the eight lanes of a row read one whole 128-byte line
+  f32x4 srow[16];
   {
-    const f32x4* src = reinterpret_cast<const f32x4*>(p.S_k + (int64_t)(32 * wave + (lane >> 1)) * kD + 64 * (lane & 1));
+    const float* src = p.S_k + (int64_t)(32 * wave + (lane >> 3)) * kD + 4 * (lane & 7);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) srow[c] = src[c];
+    for (int i = 0; i < 16; ++i)
+      srow[i] = *reinterpret_cast<const f32x4*>(src + (i >> 2) * 8 * kD + (i & 3) * 32);
   }
 
   // ---- tile loads through buffer resources based at the tile: per-lane offsets are
@@ -323,26 +326,37 @@ void decode_mx_scan(MxParams p) {
     s_qrot[hd][lane + 64] = v[1] * isd;
   }
   __syncthreads();
-  {  // S q_rot: wave w rows 32 w .. 32 w + 31; lane (row, half of the columns)
-    const int row = 32 * wave + (lane >> 1), half = lane & 1;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  {  // S q_rot: wave w rows 32 w .. 32 w + 31; eight lanes per row, summed across them
+    float acc[4][4];   // [row group r][head]
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const f32x4 s = srow[c];
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) acc[r][h] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const f32x4 qv = *reinterpret_cast<const f32x4*>(&s_qrot[h][64 * half + 4 * c]);
-        acc[h] = fmaf(s[0], qv[0], acc[h]);
-        acc[h] = fmaf(s[1], qv[1], acc[h]);
-        acc[h] = fmaf(s[2], qv[2], acc[h]);
-        acc[h] = fmaf(s[3], qv[3], acc[h]);
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(&s_qrot[h][32 * c + 4 * (lane & 7)]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 sv = srow[4 * r + c];
+          acc[r][h] = fmaf(sv[0], qv[0], acc[r][h]);
+          acc[r][h] = fmaf(sv[1], qv[1], acc[r][h]);
+          acc[r][h] = fmaf(sv[2], qv[2], acc[r][h]);
+          acc[r][h] = fmaf(sv[3], qv[3], acc[r][h]);
+        }
       }
     }
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float tot = acc[h] + xchg<1>(acc[h]);
-      if (!half) s_sq[h][row] = tot;
-    }
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float t = acc[r][h];
+        t += xchg<1>(t);
+        t += xchg<2>(t);
+        t += xchg<4>(t);
+        if ((lane & 7) == 0) s_sq[h][32 * wave + 8 * r + (lane >> 3)] = t;
+      }
   }
   __syncthreads();
   {  // per head (wave): the constants removed after the products
@@ -553,6 +567,11 @@ void decode_mx_scan(MxParams p) {
         n_skip += __builtin_popcountll(all4);
         if (drop) w[k] = 0.0f;
       }
+      // a tile whose every weight was dropped adds nothing to the value sums
+      bool kept = false;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) kept |= w[k] > 0.0f;
+      if (__ballot(kept) == 0) return;
     }
     // -- value weights u = w n16_v and u' = w r16_v (gamma applied after the sums), times the
     // nibble weight f_D, as 16-bit integers x 2^(e - 16) with a block exponent e per head and
