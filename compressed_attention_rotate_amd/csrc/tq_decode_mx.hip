@@ -117,6 +117,13 @@ __device__ __forceinline__ i32x8 fp6_row(const f32x16& ev, const f32x16& od) {
   return (i32x8){(int)r[0], (int)r[1], (int)r[2], (int)r[3], (int)r[4], (int)r[5], 0, 0};
 }
 
+// The value of the other quad of this lane's 8-lane group (DPP row_half_mirror: lane i and
+// lane 7 - i of each half row): the xor-4 partner's value once the value is uniform within
+// each quad, as it is after exchanges at distances 1 and 2.  A DPP move, not an LDS swizzle.
+__device__ __forceinline__ float quad_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+
 // Block exponent: e with |x| 2^-e in [0.5, 1); blocks below 2^-80 count as zero (e = -100)
 constexpr int kZeroExp = -100;
 __device__ __forceinline__ int block_exp(float amax) {
@@ -265,30 +272,44 @@ void decode_mx_scan(MxParams p) {
   uint32_t* tl = &s_tile[wave][0];
   const uint32_t tl_addr = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)(uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)tl));   // LDS byte address
-  // issue the loads of the tile at t0 into this wave's LDS image (no registers)
-  auto dma = [&](int64_t t0) {
-    const int64_t left = p.capacity - t0;   // tokens of this (batch, KV head) from t0 on
-    const i32x4s rk = make_rsrc(p.codes_k + (vbase + t0) * FK::RW, left * FK::RW * 4);
-    const i32x4s rnk = make_rsrc(p.norms_k + vbase + t0, left * 4);
-    const i32x4s rnv = make_rsrc(p.norms_v + vbase + t0, left * 4);
-    const i32x4s rv = make_rsrc(p.codes_v + ((vbase + t0) >> 5) * VGW, (left >> 5) * VGW * 4);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int dt = 64 * (k >> 2) + 4 * (k & 3);   // token offset of key group k
-      load_lds<16>(rk, tl_addr + 4 * (kTKw + k * 256), koff, dt * FK::RW * 4);
-      load_lds<4>(rnk, tl_addr + 4 * (kTKn + k * 64), noff, dt * 4);
-      load_lds<4>(rnv, tl_addr + 4 * (kTVn + k * 64), noff, dt * 4);
-    }
+  // the loads of the tile at t0 into this wave's LDS image (no registers), through buffer
+  // resources over the records from t0 on; with valid false the resources are empty, so the
+  // loads read nothing from memory (the image gets zeros)
+  struct TileRes {
+    i32x4s rk, rnk, rnv, rv;
+  };
+  auto tile_res = [&](int64_t t0, bool valid) {
+    const int64_t left = valid ? p.capacity - t0 : 0;   // tokens of this (batch, KV head) from t0 on
+    TileRes r;
+    r.rk = make_rsrc(p.codes_k + (vbase + t0) * FK::RW, left * FK::RW * 4);
+    r.rnk = make_rsrc(p.norms_k + vbase + t0, left * 4);
+    r.rnv = make_rsrc(p.norms_v + vbase + t0, left * 4);
+    r.rv = make_rsrc(p.codes_v + ((vbase + t0) >> 5) * VGW, (left >> 5) * VGW * 4);
+    return r;
+  };
+  auto dma_keys = [&](const TileRes& r, int k) {   // key group k: records and both norms
+    const int dt = 64 * (k >> 2) + 4 * (k & 3);      // token offset of key group k
+    load_lds<16>(r.rk, tl_addr + 4 * (kTKw + k * 256), koff, dt * FK::RW * 4);
+    load_lds<4>(r.rnk, tl_addr + 4 * (kTKn + k * 64), noff, dt * 4);
+    load_lds<4>(r.rnv, tl_addr + 4 * (kTVn + k * 64), noff, dt * 4);
+  };
+  auto dma_values = [&](const TileRes& r) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int blk = c >> 1;
       const int vo = blk < VSB ? voff_lo : voff_hi;
       const int so = blk < VSB ? 16 * c * (VLO + 1) * 4 : (16 * c - 32 * VSB) * (VHI + 1) * 4;
       if (FV::words(blk) == 4)
-        load_lds<16>(rv, tl_addr + 4 * (kTVw + c * 256), vo, so);
+        load_lds<16>(r.rv, tl_addr + 4 * (kTVw + c * 256), vo, so);
       else
-        load_lds<12>(rv, tl_addr + 4 * (kTVw + c * 256), vo, so);
+        load_lds<12>(r.rv, tl_addr + 4 * (kTVw + c * 256), vo, so);
     }
+  };
+  auto dma = [&](int64_t t0) {
+    const TileRes r = tile_res(t0, true);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dma_keys(r, k);
+    dma_values(r);
   };
   // this lane's part of the LDS image into registers (after the tile's loads completed)
   auto read_tile = [&](TileRegs& T) {
@@ -354,7 +375,7 @@ void decode_mx_scan(MxParams p) {
         float t = acc[r][h];
         t += xchg<1>(t);
         t += xchg<2>(t);
-        t += xchg<4>(t);
+        t += quad_swap(t);
         if ((lane & 7) == 0) s_sq[h][32 * wave + 8 * r + (lane >> 3)] = t;
       }
   }
@@ -381,14 +402,15 @@ void decode_mx_scan(MxParams p) {
       s_hc[hd][1] = cs;
     }
   }
-  // key A operands, wave w building planes w, w + 4: A lane (g, m) holds row m = (head m / 4,
+  // key A operands, wave w building plane w (and, for a fifth plane, waves 0 and 1 its digit
+  // rows 0-3 and 4-7): A lane (g, m) holds row m = (head m / 4,
   // digit m % 4) for K = 32 g .. 32 g + 31.  K = 32 g + p is coordinate j = 32 g + 4 (p % 8) +
   // p / 8 (nibble p % 8 of dword p / 8 of the B operand), whose nibble weight is f_{p / 8}.
   // a_j = f alpha_k q_rot_j (codebook planes) or f (S q_rot)_j (sign plane); x = |a| 2^-e is
   // truncated to 32 bits (x 2^32 as an integer): digits 0-3 in one operand, 4-7 in the other.
   {
     const int ga = lane >> 4, m = lane & 15, hd = m >> 2, l = m & 3;
-    for (int k = wave; k <= NPK; k += kXWaves) {
+    auto build = [&](int k, bool hi, bool lo) {
       const float alpha = k < NPK ? p.alpha_k[ga < KSB ? 0 : 1][k] : 1.0f;
       const float* src = k < NPK ? &s_qrot[hd][32 * ga] : &s_sq[hd][32 * ga];
       float av[32];
@@ -401,30 +423,27 @@ void decode_mx_scan(MxParams p) {
         amax = fmaxf(amax, fabsf(av[q]));
       }
       const int e = block_exp(amax);
-      const int shh = 28 - 4 * l, shl = 12 - 4 * l;   // digit l and digit 4 + l of x 2^32
-      f32x16 hev, hod, lev, lod;
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
-        const uint32_t r = e == kZeroExp ? 0u : (uint32_t)ldexpf(fabsf(av[q]), 32 - e);
-        const uint32_t sgn = __float_as_uint(av[q]) & 0x80000000u;
-        const float dh = __uint_as_float(__float_as_uint((float)((r >> shh) & 15u)) | sgn);
-        const float dl = __uint_as_float(__float_as_uint((float)((r >> shl) & 15u)) | sgn);
-        if (q & 1) {
-          hod[q >> 1] = dh;
-          lod[q >> 1] = dl;
-        } else {
-          hev[q >> 1] = dh;
-          lev[q >> 1] = dl;
+      for (int part = 0; part < 2; ++part) {
+        if (part == 0 ? !hi : !lo) continue;
+        const int sh = (part == 0 ? 28 : 12) - 4 * l;   // digit l (or 4 + l) of x 2^32
+        f32x16 ev, od;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+          const uint32_t r = e == kZeroExp ? 0u : (uint32_t)ldexpf(fabsf(av[q]), 32 - e);
+          const uint32_t sgn = __float_as_uint(av[q]) & 0x80000000u;
+          const float dg = __uint_as_float(__float_as_uint((float)((r >> sh) & 15u)) | sgn);
+          if (q & 1) od[q >> 1] = dg;
+          else ev[q >> 1] = dg;
         }
-      }
-      const i32x8 ah = fp6_row(hev, hod), al = fp6_row(lev, lod);
+        const i32x8 a = fp6_row(ev, od);
 #pragma unroll
-      for (int r = 0; r < 6; ++r) {
-        s_ak[k][0][r][lane] = (uint32_t)ah[r];
-        s_ak[k][1][r][lane] = (uint32_t)al[r];
+        for (int r = 0; r < 6; ++r) s_ak[k][part][r][lane] = (uint32_t)a[r];
       }
-      s_ke[k][lane] = e;
-    }
+      if (hi) s_ke[k][lane] = e;
+    };
+    if (wave <= NPK) build(wave, true, true);
+    if (NPK == 4 && wave < 2) build(4, wave == 0, wave == 1);
   }
   __syncthreads();
   i32x8 akh[NPK + 1], akl[NPK + 1];
@@ -467,11 +486,14 @@ void decode_mx_scan(MxParams p) {
   const float fvi = 1.0f / fv;
   int* ve = &s_ve[wave][0][0][0];
 
-  auto process = [&](const TileRegs& T, const int64_t t0) {
+  // nr: the resources of the next tile, whose loads are spread over this tile's key groups
+  // and softmax, so that the load queue never holds the wave up for long
+  auto process = [&](const TileRegs& T, const int64_t t0, const TileRes& nr) {
     // -- keys: logits of head hh for tokens key_token(k, n)
     float lg[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+      dma_keys(nr, k);
       const uint32_t p0 = T.kw[k][0], p1 = T.kw[k][1];
       uint32_t p2, sg;
       if constexpr (KLO == KHI) {
@@ -524,11 +546,12 @@ void decode_mx_scan(MxParams p) {
           p.logits[((int64_t)b * p.hq + h0 + hh) * p.capacity + t] = lg[k] * 0.6931471805599453f;
       }
     }
+    dma_values(nr);
     // -- online softmax (head hh spans the 16 lanes of its DPP row)
     float tm = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])), fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
     tm = fmaxf(tm, xchg<1>(tm));
     tm = fmaxf(tm, xchg<2>(tm));
-    tm = fmaxf(tm, xchg<4>(tm));
+    tm = fmaxf(tm, quad_swap(tm));
     tm = fmaxf(tm, xchg<8>(tm));
     const bool grow = tm > m_run + kLazy;   // also the first finite max
     if (__ballot(grow) != 0) {
@@ -556,7 +579,7 @@ void decode_mx_scan(MxParams p) {
       float lrun = l_part;
       lrun += xchg<1>(lrun);
       lrun += xchg<2>(lrun);
-      lrun += xchg<4>(lrun);
+      lrun += quad_swap(lrun);
       lrun += xchg<8>(lrun);
       const float thr = p.tau * lrun;
 #pragma unroll
@@ -593,8 +616,8 @@ void decode_mx_scan(MxParams p) {
         ms = fmaxf(ms, xchg<1>(ms));
         mu = fmaxf(mu, xchg<2>(mu));
         ms = fmaxf(ms, xchg<2>(ms));
-        mu = fmaxf(mu, xchg<4>(mu));
-        ms = fmaxf(ms, xchg<4>(ms));
+        mu = fmaxf(mu, quad_swap(mu));
+        ms = fmaxf(ms, quad_swap(ms));
         const int eu = block_exp(mu), es = block_exp(ms);
         u32x4 ru, rs;
         float su = 0.f, ss = 0.f;
@@ -694,9 +717,11 @@ void decode_mx_scan(MxParams p) {
     read_tile(T);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);    // reads done before the image is overwritten
     asm volatile("" ::: "memory");
-    if (tile_start(it + 1) < t_end) dma(tile_start(it + 1));
-    process(T, tile_start(it));
+    const int64_t tn = tile_start(it + 1);
+    process(T, tile_start(it), tile_res(tn, tn < t_end));
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the last tile's (empty) loads
+  asm volatile("" ::: "memory");
 
   // ---- wave partial: per head the running max, the sum of weights and the rotated-domain
   // sums A[j] = sum_k alpha_k (sum_t u_t s_k,t,j), Q[j] = sum_t u'_t sigma_t,j
@@ -707,9 +732,9 @@ void decode_mx_scan(MxParams p) {
   lh += xchg<2>(lh);
   u3h += xchg<2>(u3h);
   u3sh += xchg<2>(u3sh);
-  lh += xchg<4>(lh);
-  u3h += xchg<4>(u3h);
-  u3sh += xchg<4>(u3sh);
+  lh += quad_swap(lh);
+  u3h += quad_swap(u3h);
+  u3sh += quad_swap(u3sh);
   lh += xchg<8>(lh);
   u3h += xchg<8>(u3h);
   u3sh += xchg<8>(u3sh);
