@@ -106,6 +106,12 @@ __device__ __forceinline__ i32x4 fp4_of(uint32_t w, uint32_t ones) {
   return b;
 }
 
+// fp4 operand of the XOR of three plane words from theirs: every dword is the XOR of the
+// three (the sign dword's 0001 nibbles XOR to 0001 again)
+__device__ __forceinline__ i32x4 fp4_xor3(const i32x4& a, const i32x4& b, const i32x4& c) {
+  return a ^ b ^ c;
+}
+
 // A row of 32 digits (element p = K index 32 g + p of this lane) as fp6 e2m3 values d / 2;
 // the packed conversion interleaves its two sources (element 2 i from ev[i], 2 i + 1 from od[i])
 // and divides by its scale operand.  It writes its first result dwords before it has read the
@@ -489,6 +495,8 @@ void decode_mx_scan(MxParams p) {
   // nr: the resources of the next tile, whose loads are spread over this tile's key groups
   // and softmax, so that the load queue never holds the wave up for long
   auto process = [&](const TileRegs& T, const int64_t t0, const TileRes& nr) {
+    // tokens of the tile before the end of the split (key_token(k, n) < rem is valid)
+    const int rem = (int)min(t_end - t0, (int64_t)kXTile);
     // -- keys: logits of head hh for tokens key_token(k, n)
     float lg[8];
 #pragma unroll
@@ -507,18 +515,16 @@ void decode_mx_scan(MxParams p) {
       // digits 0-3 and 4-7 of every plane into one accumulator per term (the 8 key groups
       // give the scheduler independent chains)
       f32x4 ac = {0.f, 0.f, 0.f, 0.f}, as = {0.f, 0.f, 0.f, 0.f};
-      {
-        const i32x4 b0 = fp4_of(p0, ones);
-        ac = mma(akh[0], b0, ac, ksh[0]);
-        ac = mma(akl[0], b0, ac, ksl[0]);
-      }
+      const i32x4 b0 = fp4_of(p0, ones);
+      ac = mma(akh[0], b0, ac, ksh[0]);
+      ac = mma(akl[0], b0, ac, ksl[0]);
+      const i32x4 b1 = fp4_of(p1, ones);
       if constexpr (NPK >= 2) {
-        const i32x4 b1 = fp4_of(p1, ones);
         ac = mma(akh[1], b1, ac, ksh[1]);
         ac = mma(akl[1], b1, ac, ksl[1]);
       }
       if constexpr (NPK >= 3) {
-        const i32x4 b2 = fp4_of(p2, ones), b3 = fp4_of(p0 ^ p1 ^ p2, ones);
+        const i32x4 b2 = fp4_of(p2, ones), b3 = fp4_xor3(b0, b1, b2);
         ac = mma(akh[2], b2, ac, ksh[2]);
         ac = mma(akl[2], b2, ac, ksl[2]);
         ac = mma(akh[3], b3, ac, ksh[3]);
@@ -536,14 +542,13 @@ void decode_mx_scan(MxParams p) {
       // computed in every lane before the mask: the products must not move under a branch
       // on the token index (their B operands come from other lanes)
       asm volatile("" : "+v"(v));
-      lg[k] = t0 + key_token(k, n) < t_end ? v : -INFINITY;
+      lg[k] = key_token(k, n) < rem ? v : -INFINITY;
     }
     if (p.logits) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int64_t t = t0 + key_token(k, n);
-        if (t < t_end)
-          p.logits[((int64_t)b * p.hq + h0 + hh) * p.capacity + t] = lg[k] * 0.6931471805599453f;
+        if (key_token(k, n) < rem)
+          p.logits[((int64_t)b * p.hq + h0 + hh) * p.capacity + t0 + key_token(k, n)] = lg[k] * 0.6931471805599453f;
       }
     }
     dma_values(nr);
@@ -571,7 +576,8 @@ void decode_mx_scan(MxParams p) {
     float tsum = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      w[k] = lg[k] == -INFINITY ? 0.0f : exp2f(lg[k] - m_run);
+      // m_run is finite here (the tile holds a valid token), so a masked token gives 0
+      w[k] = exp2f(lg[k] - m_run);
       tsum += w[k];
     }
     l_part += tsum;
@@ -585,7 +591,7 @@ void decode_mx_scan(MxParams p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const bool drop = w[k] < thr;
-        const unsigned long long bm = __ballot(drop && t0 + key_token(k, n) < t_end);
+        const unsigned long long bm = __ballot(drop && key_token(k, n) < rem);
         const unsigned long long all4 = bm & (bm >> 16) & (bm >> 32) & (bm >> 48) & 0xFFFFull;
         n_skip += __builtin_popcountll(all4);
         if (drop) w[k] = 0.0f;
@@ -619,22 +625,23 @@ void decode_mx_scan(MxParams p) {
         mu = fmaxf(mu, quad_swap(mu));
         ms = fmaxf(ms, quad_swap(ms));
         const int eu = block_exp(mu), es = block_exp(ms);
+        // x 2^(16 - e) is at most 2^16: rounded half up and kept below 2^16 (zero blocks: 0)
+        const float scu = eu == kZeroExp ? 0.0f : ldexpf(1.0f, 16 - eu);
+        const float scs = es == kZeroExp ? 0.0f : ldexpf(1.0f, 16 - es);
         u32x4 ru, rs;
-        float su = 0.f, ss = 0.f;
+        uint32_t su = 0u, ss = 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float a = eu == kZeroExp ? 0.0f : fminf(__builtin_rintf(ldexpf(u[4 * x + i], 16 - eu)), 65535.0f);
-          const float c = es == kZeroExp ? 0.0f : fminf(__builtin_rintf(ldexpf(us[4 * x + i], 16 - es)), 65535.0f);
-          ru[i] = (uint32_t)a;
-          rs[i] = (uint32_t)c;
-          su += a;
-          ss += c;
+          ru[i] = min((uint32_t)fmaf(u[4 * x + i], scu, 0.5f), 65535u);
+          rs[i] = min((uint32_t)fmaf(us[4 * x + i], scs, 0.5f), 65535u);
+          su += ru[i];
+          ss += rs[i];
         }
         // the constant removed after the products: sum over positions D < 3 of the rounded
         // weights divided by f_D (exact: integers below 2^18 times powers of two)
         if (dd != 3) {
-          u3 += eu == kZeroExp ? 0.0f : ldexpf(su, eu - 16) * fvi;
-          u3s += es == kZeroExp ? 0.0f : ldexpf(ss, es - 16) * fvi;
+          u3 += ldexpf((float)su, eu - 16) * fvi;
+          u3s += ldexpf((float)ss, es - 16) * fvi;
         }
         const int kk = (2 * x + g0) * kXRow + 8 * dd + 4 * sx;
         *reinterpret_cast<u32x4*>(&xw[(0 * 4 + hh) * 4 * kXRow + kk]) = ru;
@@ -678,7 +685,6 @@ void decode_mx_scan(MxParams p) {
           as_ = op;
           vss = sc;
         }
-        __builtin_amdgcn_sched_barrier(0);   // one type's 32 weights live at a time
       }
     }
     // -- values: one product per plane and 16-coordinate block over the 128 tokens; the
@@ -692,15 +698,17 @@ void decode_mx_scan(MxParams p) {
       const uint32_t sg = T.vw[c][bits];
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       auto rows = [](const f32x4& t) { return (t[0] + t[1]) + (t[2] + t[3]); };
-      const f32x4 t0v = mma(au, fp4_of(p0, ones), z, vsu);
+      const i32x4 b0 = fp4_of(p0, ones), b1 = fp4_of(p1, ones);
+      const f32x4 t0v = mma(au, b0, z, vsu);
       float a = fmaf(p.alpha_v[wsel][0], rows(t0v), arun[c]);
       if (bits >= 2) {
-        const f32x4 t1 = mma(au, fp4_of(p1, ones), z, vsu);
+        const f32x4 t1 = mma(au, b1, z, vsu);
         a = fmaf(p.alpha_v[wsel][1], rows(t1), a);
       }
       if (bits >= 3) {
-        const f32x4 t2 = mma(au, fp4_of(p2, ones), z, vsu);
-        const f32x4 t3 = mma(au, fp4_of(p0 ^ p1 ^ p2, ones), z, vsu);
+        const i32x4 b2 = fp4_of(p2, ones);
+        const f32x4 t2 = mma(au, b2, z, vsu);
+        const f32x4 t3 = mma(au, fp4_xor3(b0, b1, b2), z, vsu);
         a = fmaf(p.alpha_v[wsel][2], rows(t2), a);
         a = fmaf(p.alpha_v[wsel][3], rows(t3), a);
       }
