@@ -1,5 +1,5 @@
 """GPU: the token-sliced value layout and the decode scan that reads it (keys per-vector,
-values token-sliced; both dot products on fp8 x fp4 MFMA).
+values token-sliced; both dot products on the block-scaled fp6 x fp4 MFMA).
 
 Quantize parity: the GPU's token-sliced bytes, read back into per-vector records by the
 oracle's own inverse of the layout, equal the oracle's records outside the ambiguity
