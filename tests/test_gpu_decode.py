@@ -193,7 +193,7 @@ def test_workspace_reuse(torch_gpu):
             assert torch.equal(shared, fresh), f"shape {(b, hq, hkv, n, lens)} rep {rep}"
 
 
-def _full_size_sampled(torch, batch, hq, hkv, ntok, fk, fv, seed, spikes, tau, units):
+def _full_size_sampled(torch, batch, hq, hkv, ntok, fk, fv, seed, spikes, tau, units, sliced=False):
     """Full-size decode on the GPU with sampled oracle checks.  The GPU quantizes the whole
     cache (product path); for each sampled (batch, KV head) unit the records are replaced by
     the oracle's own packing of the same inputs, so the GPU decodes, for those heads, exactly
@@ -204,7 +204,7 @@ def _full_size_sampled(torch, batch, hq, hkv, ntok, fk, fv, seed, spikes, tau, u
     kb, vb, _ = TI.kv_layer(batch, hkv, ntok, d, seed=seed, spike_frac=spikes)
     q_bits = TI.decode_queries(batch, hq, d, seed)
     (signs, S), (gsigns, gS) = rotations(d, seed + 500000)
-    fmt_k, fmt_v = tq.Format(*fk), tq.Format(*fv)
+    fmt_k, fmt_v = tq.Format(*fk), tq.Format(*fv, layout=1 if sliced else 0)
     Sd = torch.from_numpy(gS).cuda()
     tk, tv = tq.Tables(fmt_k, gsigns, Sd), tq.Tables(fmt_v, gsigns, Sd)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
@@ -212,13 +212,15 @@ def _full_size_sampled(torch, batch, hq, hkv, ntok, fk, fv, seed, spikes, tau, u
     ck, nk = tq.quantize_kv(bf(kb).view(-1, d), fmt_k, tk)
     cv, nv = tq.quantize_kv(bf(vb).view(-1, d), fmt_v, tv)
     ck, nk = ck.view(batch, hkv, ntok, rbk), nk.view(batch, hkv, ntok, 2)
-    cv, nv = cv.view(batch, hkv, ntok, rbv), nv.view(batch, hkv, ntok, 2)
+    cv = cv.view(batch, hkv, ntok // 32, 32 * rbv) if sliced else cv.view(batch, hkv, ntok, rbv)
+    nv = nv.view(batch, hkv, ntok, 2)
     oracle = {}
     for bi, kh in units:
         rk, nko, _ = oracle_pack_cache(kb[bi:bi + 1, kh:kh + 1], O.Format(*fk), signs, S, bf16=True)
         rv, nvo, _ = oracle_pack_cache(vb[bi:bi + 1, kh:kh + 1], O.Format(*fv), signs, S, bf16=True)
         ck[bi, kh] = torch.from_numpy(np.ascontiguousarray(rk[0, 0])).cuda()
-        cv[bi, kh] = torch.from_numpy(np.ascontiguousarray(rv[0, 0])).cuda()
+        rv_dev = O.tiles_from_records(rv[0, 0], O.Format(*fv)) if sliced else rv[0, 0]
+        cv[bi, kh] = torch.from_numpy(np.ascontiguousarray(rv_dev)).cuda()
         nk[bi, kh] = torch.from_numpy(np.ascontiguousarray(nko[0, 0]).view(np.int16)).cuda().view(torch.float16)
         nv[bi, kh] = torch.from_numpy(np.ascontiguousarray(nvo[0, 0]).view(np.int16)).cuda().view(torch.float16)
         oracle[(bi, kh)] = (rk, nko, rv, nvo)
@@ -265,4 +267,20 @@ def test_full_size_long_context_sparse_v(torch_gpu):
     (batch, KV head) unit is checked against the oracle, and the gate skips rows."""
     skipped = _full_size_sampled(torch_gpu, 4, 32, 8, 131072, (128, 3, 3, 128), (128, 2, 2, 128),
                                  TI.data_seed(4), 0.01, 1e-4, [(2, 5)])
+    assert skipped > 0
+
+
+def test_full_size_batch16_mixed_width_sliced(torch_gpu):
+    """The batch-16 layer of 3.5-bit K and V as the benchmark decodes it: values token-sliced
+    (the block-scaled scan); two sampled (batch, KV head) units against the oracle."""
+    _full_size_sampled(torch_gpu, 16, 32, 8, 32768, (128, 3, 2, 64), (128, 3, 2, 64),
+                       TI.data_seed(3) + 1, 0.0, 0.0, [(5, 1), (15, 6)], sliced=True)
+
+
+def test_full_size_long_context_sparse_v_sliced(torch_gpu):
+    """Batch 4 x 131072 tokens with 1% x10 keys, K b = 4, V b = 3 token-sliced, gated
+    (tau = 1e-4) and ungated, as the benchmark decodes it; one sampled unit against the
+    oracle, and the gate skips rows."""
+    skipped = _full_size_sampled(torch_gpu, 4, 32, 8, 131072, (128, 3, 3, 128), (128, 2, 2, 128),
+                                 TI.data_seed(4) + 1, 0.01, 1e-4, [(1, 3)], sliced=True)
     assert skipped > 0
