@@ -93,6 +93,21 @@ __device__ __forceinline__ f32x4 mma(const i32x8& a, const i32x4& b, f32x4 c, in
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 2, 4, 0, sa, 0, 127);
 }
 
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+
+// acc += A (fp6 digit rows, scale byte sa) x B (fp4) with acc held in accumulation registers
+// (AGPRs) across the whole scan: value sums that are only read after the last tile never take
+// vector registers or instructions.  Written as an instruction because the rest of this file
+// keeps its MFMA results in VGPRs; the leading s_nop gives the two wait states an MFMA needs
+// after a VALU write of its A or B registers (hazards the compiler does not see inside asm).
+// Readers of acc must come at least 20 wait states after the last accumulation.
+__device__ __forceinline__ void mma_acc(f32x4& acc, const i32x8& a, const i32x4& b, int sa) {
+  const i32x6 a6 = {a[0], a[1], a[2], a[3], a[4], a[5]};
+  asm("s_nop 1\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:2 blgp:4"
+      : "+a"(acc)
+      : "v"(a6), "v"(b), "v"(sa), "v"(127));
+}
+
 // fp4 B operand of one plane word (see the file comment); the nibble-sign dword gives -0.5 s:
 // (w & 0x88888888) | 0x11111111 as one bitfield insert, `ones` holding 0x11111111
 __device__ __forceinline__ i32x4 fp4_of(uint32_t w, uint32_t ones) {
@@ -215,7 +230,10 @@ struct TileRegs {
   u32x4 vw[8];        // value words of coordinate 16 c + n, 32-token group g of the tile
 };
 
-template <int KLO, int KHI, int KSB, int VLO, int VHI, int VSB>
+// LA (long scans, many tiles per wave): the value products of every codebook plane keep their
+// own accumulators over the whole scan, folded with the Walsh coefficients once at the end;
+// otherwise each tile's products are folded right away (cheaper set-up and end for a few tiles).
+template <int KLO, int KHI, int KSB, int VLO, int VHI, int VSB, bool LA>
 __global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mx_scan(MxParams p) {
   using FK = Fmt<KLO, KHI, KSB>;
@@ -476,14 +494,21 @@ void decode_mx_scan(MxParams p) {
   constexpr float kLazy = 8.0f;
   float m_run = -INFINITY, l_part = 0.f, u3 = 0.f, u3s = 0.f;
   unsigned long long n_skip = 0;
-  // value sums of head hh at coordinate 16 c + n: arun[c] = sum_k alpha_k (product of codebook
-  // plane k, its 4 digit rows added), folded after each tile; accs[c] = sign products, one
-  // fp32 sum per digit row, kept on the matrix cores
+  // value sums of head hh at coordinate 16 c + n.  accs[c]: sign products, one fp32 sum per
+  // digit row, kept on the matrix cores.  Codebook planes: with LA, acv[k][c] = products of
+  // plane k, likewise per digit row, in accumulation registers; otherwise arun[c] = sum_k
+  // alpha_k (product of plane k, its 4 digit rows added), folded after each tile.
+  f32x4 acv[4][8], accs[8];
   float arun[8];
-  f32x4 accs[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    arun[c] = 0.f;
+    if constexpr (LA) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < FV::planes(FV::bits(c >> 1))) acv[k][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    } else {
+      arun[c] = 0.f;
+    }
     accs[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   uint32_t* xw = &s_x[wave][0];
@@ -561,15 +586,34 @@ void decode_mx_scan(MxParams p) {
     const bool grow = tm > m_run + kLazy;   // also the first finite max
     if (__ballot(grow) != 0) {
       const float m_new = grow ? tm : m_run;
-      const float fm = (grow && m_run != -INFINITY) ? exp2f(m_run - m_new) : 1.0f;
+      // the sums only need rescaling where a finite max moved (they are zero before it)
+      const bool resc = grow && m_run != -INFINITY;
+      if (__ballot(resc) != 0) {
+        const float fm = resc ? exp2f(m_run - m_new) : 1.0f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        arun[c] *= fm;
-        accs[c] *= fm;
+        for (int c = 0; c < 8; ++c) {
+          if constexpr (LA) {
+            // (the barriers keep the reads of the accumulation registers inside this rarely
+            // taken branch)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (k < FV::planes(FV::bits(c >> 1))) {
+                asm volatile("" : "+a"(acv[k][c]));
+                acv[k][c] *= fm;
+                asm volatile("" : "+a"(acv[k][c]));
+              }
+            asm volatile("" : "+a"(accs[c]));
+            accs[c] *= fm;
+            asm volatile("" : "+a"(accs[c]));
+          } else {
+            arun[c] *= fm;
+            accs[c] *= fm;
+          }
+        }
+        l_part *= fm;
+        u3 *= fm;
+        u3s *= fm;
       }
-      l_part *= fm;
-      u3 *= fm;
-      u3s *= fm;
       m_run = m_new;
     }
     float w[8];
@@ -687,33 +731,43 @@ void decode_mx_scan(MxParams p) {
         }
       }
     }
-    // -- values: one product per plane and 16-coordinate block over the 128 tokens; the
-    // codebook planes' products are folded with their Walsh coefficients right away
+    // -- values: one product per plane and 16-coordinate block over the 128 tokens
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int bits = FV::bits(c >> 1);
-      const int wsel = (c >> 1) < VSB ? 0 : 1;
       const uint32_t p0 = T.vw[c][0], p1 = T.vw[c][1];
       const uint32_t p2 = bits >= 3 ? T.vw[c][2] : 0u;
       const uint32_t sg = T.vw[c][bits];
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      auto rows = [](const f32x4& t) { return (t[0] + t[1]) + (t[2] + t[3]); };
       const i32x4 b0 = fp4_of(p0, ones), b1 = fp4_of(p1, ones);
-      const f32x4 t0v = mma(au, b0, z, vsu);
-      float a = fmaf(p.alpha_v[wsel][0], rows(t0v), arun[c]);
-      if (bits >= 2) {
-        const f32x4 t1 = mma(au, b1, z, vsu);
-        a = fmaf(p.alpha_v[wsel][1], rows(t1), a);
+      if constexpr (LA) {   // each plane into its own accumulator
+        mma_acc(acv[0][c], au, b0, vsu);
+        if (bits >= 2) mma_acc(acv[1][c], au, b1, vsu);
+        if (bits >= 3) {
+          const i32x4 b2 = fp4_of(p2, ones);
+          mma_acc(acv[2][c], au, b2, vsu);
+          mma_acc(acv[3][c], au, fp4_xor3(b0, b1, b2), vsu);
+        }
+        mma_acc(accs[c], as_, fp4_of(sg, ones), vss);
+      } else {              // the planes' products folded with their Walsh coefficients now
+        const int wsel = (c >> 1) < VSB ? 0 : 1;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        auto rows = [](const f32x4& t) { return (t[0] + t[1]) + (t[2] + t[3]); };
+        const f32x4 t0v = mma(au, b0, z, vsu);
+        float a = fmaf(p.alpha_v[wsel][0], rows(t0v), arun[c]);
+        if (bits >= 2) {
+          const f32x4 t1 = mma(au, b1, z, vsu);
+          a = fmaf(p.alpha_v[wsel][1], rows(t1), a);
+        }
+        if (bits >= 3) {
+          const i32x4 b2 = fp4_of(p2, ones);
+          const f32x4 t2 = mma(au, b2, z, vsu);
+          const f32x4 t3 = mma(au, fp4_xor3(b0, b1, b2), z, vsu);
+          a = fmaf(p.alpha_v[wsel][2], rows(t2), a);
+          a = fmaf(p.alpha_v[wsel][3], rows(t3), a);
+        }
+        arun[c] = a;
+        accs[c] = mma(as_, fp4_of(sg, ones), accs[c], vss);
       }
-      if (bits >= 3) {
-        const i32x4 b2 = fp4_of(p2, ones);
-        const f32x4 t2 = mma(au, b2, z, vsu);
-        const f32x4 t3 = mma(au, fp4_xor3(b0, b1, b2), z, vsu);
-        a = fmaf(p.alpha_v[wsel][2], rows(t2), a);
-        a = fmaf(p.alpha_v[wsel][3], rows(t3), a);
-      }
-      arun[c] = a;
-      accs[c] = mma(as_, fp4_of(sg, ones), accs[c], vss);
     }
   };
 
@@ -730,6 +784,8 @@ void decode_mx_scan(MxParams p) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the last tile's (empty) loads
   asm volatile("" ::: "memory");
+  // the last accumulations complete before the sums are read
+  if constexpr (LA) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // ---- wave partial: per head the running max, the sum of weights and the rotated-domain
   // sums A[j] = sum_k alpha_k (sum_t u_t s_k,t,j), Q[j] = sum_t u'_t sigma_t,j
@@ -756,10 +812,15 @@ void decode_mx_scan(MxParams p) {
       const int bits = FV::bits(c >> 1);
       const int wsel = (c >> 1) < VSB ? 0 : 1;
       float asum = 0.f;   // sum of the Walsh coefficients: the constant's weight in A
+      float a = LA ? 0.f : arun[c];
+      auto rows = [](const f32x4& t) { return (t[0] + t[1]) + (t[2] + t[3]); };
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (k < FV::planes(bits)) asum += p.alpha_v[wsel][k];
-      const float a = arun[c] - asum * u3h;
+        if (k < FV::planes(bits)) {
+          asum += p.alpha_v[wsel][k];
+          if constexpr (LA) a = fmaf(p.alpha_v[wsel][k], rows(acv[k][c]), a);
+        }
+      a -= asum * u3h;
       const f32x4 r = accs[c];
       const float qv = ((r[0] + r[1]) + (r[2] + r[3])) - u3sh;
       s_red[wave][hh][16 * c + n] = a;
@@ -803,8 +864,11 @@ void decode_mx_scan(MxParams p) {
 }
 
 template <int KLO, int KHI, int KSB, int VLO, int VHI, int VSB>
-int launch_mx(const MxParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_mx_scan<KLO, KHI, KSB, VLO, VHI, VSB>), grid, dim3(kXThreads), 0, stream, p);
+int launch_mx(const MxParams& p, dim3 grid, bool long_scan, hipStream_t stream) {
+  if (long_scan)
+    hipLaunchKernelGGL((decode_mx_scan<KLO, KHI, KSB, VLO, VHI, VSB, true>), grid, dim3(kXThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_mx_scan<KLO, KHI, KSB, VLO, VHI, VSB, false>), grid, dim3(kXThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
@@ -888,13 +952,16 @@ int tq_launch_decode_mx(const tq_format* fk, const tq_tables* tk, const tq_forma
   tq_walsh_coeffs(fv->split == fv->d ? fv->bits_lo : fv->bits_hi,
                   fv->split == fv->d ? tv->centroids_lo : tv->centroids_hi, p.alpha_v[1]);
   const dim3 grid((unsigned)plan.n_split, (unsigned)(batch * hkv * (hq / hkv / 4)));
+  // per-plane accumulators pay off from about 8 tiles per wave (their set-up and final fold
+  // cost about as much as 4 tiles' folds)
+  const bool long_scan = plan.tokens_per_split >= 8 * (int64_t)kXTile * kXWaves;
   int kl, kh, ks, vl, vh, vs;
   mx_shape(fk, kl, kh, ks);
   mx_shape(fv, vl, vh, vs);
   int rc = TQ_ERR_SHAPE;
 #define TQ_MX_LAUNCH(a, b_, c, d, e, f)                                  \
   if (kl == a && kh == b_ && ks == c && vl == d && vh == e && vs == f)   \
-    rc = launch_mx<a, b_, c, d, e, f>(p, grid, stream);                   \
+    rc = launch_mx<a, b_, c, d, e, f>(p, grid, long_scan, stream);        \
   else
   TQ_MX_PAIRS(TQ_MX_LAUNCH) {}
 #undef TQ_MX_LAUNCH
