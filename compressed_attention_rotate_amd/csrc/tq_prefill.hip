@@ -8,7 +8,8 @@
 // sum splits the same way into A = sum_t p_t n16_t c[idx_t] and Q = gamma sum_t p_t r16_t
 // (2 sigma_t - 1), rotated back once per row as in decode (out = D H (A + S^T Q) / (sqrt(d) l)).
 // With many query rows per key these are dense contractions, so they run on
-// v_mfma_f32_16x16x32_f16 (logits) and v_mfma_f32_16x16x16_f16 (values), fp32 accumulation:
+// v_mfma_f32_16x16x32_f16 (logits and values; the 16x16x16 form takes as many cycles for
+// half the work on this part), fp32 accumulation:
 //   prefill_q:     per row, q_rot (FWHT) and gamma S q_rot as fp16 operand rows;
 //   prefill_scan:  grid (64-row block, KV head, key split); per 64-key tile the workgroup
 //                  dequantizes the keys into LDS as [key][coord] fp16 rows (n16 c, +-r16)
@@ -359,20 +360,33 @@ __global__ __launch_bounds__(kPfThreads) void prefill_scan(PrefillParams p) {
       om[cb] *= corr;
       oq[cb] *= corr;
     }
-    // ---- values: om[cb][r] = A^T[coord cb*16 + 4 (lane >> 4) + r][row lane & 15]
+    // ---- values: om[cb][r] = A^T[coord cb*16 + 4 (lane >> 4) + r][row lane & 15], 32 keys
+    // per product: K slots 8 g .. 8 g + 3 of lane group g are keys 32 j + 4 g + 0..3 and slots
+    // 8 g + 4 .. 8 g + 7 keys 32 j + 16 + 4 g + 0..3, so the B operand is this lane's weights
+    // of key blocks 2 j and 2 j + 1 as they are
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int j = 0; j < 2; ++j) {
+      const h16x8 bch = __builtin_shufflevector(pch[2 * j], pch[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const h16x8 bcl = __builtin_shufflevector(pcl[2 * j], pcl[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const h16x8 bsh = __builtin_shufflevector(psh[2 * j], psh[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const h16x8 bsl = __builtin_shufflevector(psl[2 * j], psl[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
-        const int off = (cb * 16 + (lane & 15)) * kVtStride + kb * 16 + 4 * (lane >> 4);
-        const h16x4 vh = *reinterpret_cast<const h16x4*>(Vh + off);
-        const h16x4 vl = *reinterpret_cast<const h16x4*>(Vl + off);
-        const h16x4 vs = *reinterpret_cast<const h16x4*>(Vs + off);
-        om[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vh, pch[kb], om[cb], 0, 0, 0);
-        om[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vl, pch[kb], om[cb], 0, 0, 0);
-        om[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vh, pcl[kb], om[cb], 0, 0, 0);
-        oq[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vs, psh[kb], oq[cb], 0, 0, 0);
-        oq[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vs, psl[kb], oq[cb], 0, 0, 0);
+        const int off = (cb * 16 + (lane & 15)) * kVtStride + 32 * j + 4 * (lane >> 4);
+        const h16x8 vh = __builtin_shufflevector(*reinterpret_cast<const h16x4*>(Vh + off),
+                                                 *reinterpret_cast<const h16x4*>(Vh + off + 16),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+        const h16x8 vl = __builtin_shufflevector(*reinterpret_cast<const h16x4*>(Vl + off),
+                                                 *reinterpret_cast<const h16x4*>(Vl + off + 16),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+        const h16x8 vs = __builtin_shufflevector(*reinterpret_cast<const h16x4*>(Vs + off),
+                                                 *reinterpret_cast<const h16x4*>(Vs + off + 16),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+        om[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, bch, om[cb], 0, 0, 0);
+        om[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, bch, om[cb], 0, 0, 0);
+        om[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, bcl, om[cb], 0, 0, 0);
+        oq[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vs, bsh, oq[cb], 0, 0, 0);
+        oq[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vs, bsl, oq[cb], 0, 0, 0);
       }
     }
   }
