@@ -26,10 +26,13 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 
 # per-source extra flags: the search, prefill and token-sliced decode scans keep their MFMA
 # accumulators in VGPRs (they read them back every tile; the AGPR form costs one copy per
-# accumulator)
+# accumulator).  The token-sliced decode is compiled on the assumption that its float values
+# are not NaN: fmaxf then needs no quieting of operands that come from lane exchanges (one
+# instruction each); the one place where NaN products can arise (zero weights times the
+# unbounded norms of masked tokens) selects on the bits.
 EXTRA = {"tq_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "tq_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "tq_decode_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "tq_decode_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

@@ -531,7 +531,8 @@ __device__ __forceinline__ void scan_body(const DecodeParams& p, float* lds, int
         m_run[h] = mn;
         grow = true;
       }
-      float wgt = valid ? exp2f(lg[h] - m_run[h]) : 0.0f;
+      // hardware exp2: weights below 2^-126 of the running maximum flush to zero
+      float wgt = valid ? __builtin_amdgcn_exp2f(lg[h] - m_run[h]) : 0.0f;
       if (gated) {
         l_run[h] = l_run[h] * corr[h] + wave_sum_fast(wgt);
         wgt = wgt < p.tau * l_run[h] ? 0.0f : wgt;

@@ -61,9 +61,10 @@ typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 constexpr int kXWaves = 4;
 constexpr int kXThreads = 64 * kXWaves;
 constexpr int kXTile = 128;      // tokens per wave tile
-// hand-off rows of 32 weights (one head, type and 32-token group) padded to 36 dwords, so the
-// 16 rows one A-operand read touches start on 16 different 4-bank groups
-constexpr int kXRow = 36;
+// hand-off rows of 32 16-bit weights (one head, type and 32-token group; two per dword, K order)
+// padded to 20 dwords, so the 16 rows one A-operand read touches start on 16 different 4-bank
+// groups
+constexpr int kXRow = 20;
 
 struct MxParams {
   const void* q;
@@ -135,6 +136,19 @@ __device__ __forceinline__ i32x4 fp4_xor3(const i32x4& a, const i32x4& b, const 
 __device__ __forceinline__ i32x8 fp6_row(const f32x16& ev, const f32x16& od) {
   u32x6 r;
   asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(ev), "v"(od), "v"(2.0f));
+  return (i32x8){(int)r[0], (int)r[1], (int)r[2], (int)r[3], (int)r[4], (int)r[5], 0, 0};
+}
+
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+
+// The same from digits given as f16 bit patterns: half i of dword j is element 2 j + i, its low
+// 4 bits the digit d (an f16 subnormal, d 2^-24) and bit 15 its sign, so a digit takes one
+// shift and mask of the word it sits in and no conversion to float; the packed conversion
+// divides by its scale operand, 2^-23, which gives d / 2 exactly (early-clobber result, as
+// above).
+__device__ __forceinline__ i32x8 fp6_row_f16(const u32x16& h) {
+  u32x6 r;
+  asm volatile("v_cvt_scalef32_pk32_fp6_f16 %0, %1, %2" : "=&v"(r) : "v"(h), "v"(1.1920928955078125e-07f));
   return (i32x8){(int)r[0], (int)r[1], (int)r[2], (int)r[3], (int)r[4], (int)r[5], 0, 0};
 }
 
@@ -247,7 +261,7 @@ void decode_mx_scan(MxParams p) {
   __shared__ uint32_t s_ak[NPK + 1][2][6][64];            // key A operands [plane][digits 0-3 / 4-7]
   __shared__ int s_ke[NPK + 1][64];                       // key block exponent of each A lane
   __shared__ int s_ve[kXWaves][2][4][4];                  // value block exponents [type][group][head]
-  __shared__ uint32_t s_x[kXWaves][2 * 4 * 4 * kXRow];   // rounded weights [type][head][group][K]
+  __shared__ __align__(16) uint32_t s_x[kXWaves][2 * 4 * 4 * kXRow];   // rounded weights [type][head][group][K / 2]
   __shared__ float s_m[kXWaves][4][2];
   __shared__ float s_red[kXWaves][4][2 * kD];
   __shared__ __align__(16) uint32_t s_tile[kXWaves][kTileDw];   // next tile, in flight
@@ -620,8 +634,10 @@ void decode_mx_scan(MxParams p) {
     float tsum = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      // m_run is finite here (the tile holds a valid token), so a masked token gives 0
-      w[k] = exp2f(lg[k] - m_run);
+      // m_run is finite here (the tile holds a valid token), so a masked token gives 0; the
+      // hardware exp2 (results below 2^-126, i.e. weights below 2^-126 of the largest one,
+      // flush to zero) instead of the library's denormal-preserving expansion
+      w[k] = __builtin_amdgcn_exp2f(lg[k] - m_run);
       tsum += w[k];
     }
     l_part += tsum;
@@ -653,9 +669,15 @@ void decode_mx_scan(MxParams p) {
       float u[8], us[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
+        // computed first and then selected, so that no branch is taken per token; records of
+        // masked tokens may hold any norm, infinite ones included, so the products of a zero
+        // weight can be NaN: the selection is made on the bits (this file is compiled on the
+        // assumption that float values are not NaN, which must not remove it)
         const float n16 = f16_bits_to_f32(T.vn[k]), r16 = f16_bits_to_f32(T.vn[k] >> 16);
-        u[k] = w[k] > 0.0f ? w[k] * n16 * fv : 0.0f;
-        us[k] = w[k] > 0.0f ? w[k] * r16 * fv : 0.0f;
+        const float wf = w[k] * fv;
+        const bool keep = w[k] > 0.0f;
+        u[k] = __uint_as_float(keep ? __float_as_uint(wf * n16) : 0u);
+        us[k] = __uint_as_float(keep ? __float_as_uint(wf * r16) : 0u);
       }
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
@@ -687,9 +709,11 @@ void decode_mx_scan(MxParams p) {
           u3 += ldexpf((float)su, eu - 16) * fvi;
           u3s += ldexpf((float)ss, es - 16) * fvi;
         }
-        const int kk = (2 * x + g0) * kXRow + 8 * dd + 4 * sx;
-        *reinterpret_cast<u32x4*>(&xw[(0 * 4 + hh) * 4 * kXRow + kk]) = ru;
-        *reinterpret_cast<u32x4*>(&xw[(1 * 4 + hh) * 4 * kXRow + kk]) = rs;
+        // two weights per dword (K order): K = 8 dd + 4 sx + i is half i & 1 of dword
+        // 4 dd + 2 sx + i / 2 of the row
+        const int kk = (2 * x + g0) * kXRow + 4 * dd + 2 * sx;
+        *reinterpret_cast<u32x2*>(&xw[(0 * 4 + hh) * 4 * kXRow + kk]) = (u32x2){ru[0] | (ru[1] << 16), ru[2] | (ru[3] << 16)};
+        *reinterpret_cast<u32x2*>(&xw[(1 * 4 + hh) * 4 * kXRow + kk]) = (u32x2){rs[0] | (rs[1] << 16), rs[2] | (rs[3] << 16)};
         if ((n & 7) == 0) {
           ve[(0 * 4 + 2 * x + g0) * 4 + hh] = eu;
           ve[(1 * 4 + 2 * x + g0) * 4 + hh] = es;
@@ -708,19 +732,17 @@ void decode_mx_scan(MxParams p) {
 #pragma unroll
       for (int type = 0; type < 2; ++type) {
         const uint32_t* src = &xw[((type * 4 + ha) * 4 + ga) * kXRow];
-        f32x16 ev, od;
+        u32x16 hd;
 #pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4) {
-          // K = 8 D + i: the last 8 positions are D = 3, whose A weight is -2 (the B nibble
-          // gives -0.5 s there)
+        for (int c4 = 0; c4 < 4; ++c4) {
+          // K = 8 D + i: the last 8 positions (dwords 12 .. 15) are D = 3, whose A weight is
+          // -2 (the B nibble gives -0.5 s there): the f16 sign bit set
           const u32x4 r = *reinterpret_cast<const u32x4*>(src + 4 * c4);
-          const float sgn = c4 >= 6 ? -1.0f : 1.0f;
-          ev[2 * c4] = sgn * (float)((r[0] >> sh) & 15u);
-          od[2 * c4] = sgn * (float)((r[1] >> sh) & 15u);
-          ev[2 * c4 + 1] = sgn * (float)((r[2] >> sh) & 15u);
-          od[2 * c4 + 1] = sgn * (float)((r[3] >> sh) & 15u);
+          const uint32_t sgn = c4 == 3 ? 0x80008000u : 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hd[4 * c4 + i] = ((r[i] >> sh) & 0x000F000Fu) | sgn;
         }
-        const i32x8 op = fp6_row(ev, od);
+        const i32x8 op = fp6_row_f16(hd);
         const int sc = digit_scale(ve[(type * 4 + ga) * 4 + ha], lane & 3);
         if (type == 0) {
           au = op;

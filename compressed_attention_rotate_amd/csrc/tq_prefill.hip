@@ -341,7 +341,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_scan(PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kk = kb * 16 + 4 * (lane >> 4) + r;
-        const float pv = (lg[kb][r] == -INFINITY) ? 0.0f : exp2f(lg[kb][r] - m_new);
+        // hardware exp2: weights below 2^-126 of the running maximum flush to zero
+        const float pv = (lg[kb][r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg[kb][r] - m_new);
         psum += pv;
         const float wc = pv * vnorm[0][kk], wq = pv * vnorm[1][kk];
         const _Float16 wch = (_Float16)wc, wqh = (_Float16)wq;
