@@ -48,6 +48,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "tq_decode_kernel.h"
 
@@ -123,9 +124,15 @@ __device__ __forceinline__ i32x4 fp4_of(uint32_t w, uint32_t ones) {
 }
 
 // fp4 operand of the XOR of three plane words from theirs: every dword is the XOR of the
-// three (the sign dword's 0001 nibbles XOR to 0001 again)
+// three (the sign dword's 0001 nibbles XOR to 0001 again), one three-input bit operation each
+// (truth table 0x96).  Written as instructions: the compiler builds a three-input XOR from two
+// two-input ones, and rebuilds this one from the plane words (two instructions per dword).
 __device__ __forceinline__ i32x4 fp4_xor3(const i32x4& a, const i32x4& b, const i32x4& c) {
-  return a ^ b ^ c;
+  i32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r[i]) : "v"(a[i]), "v"(b[i]), "v"(c[i]));
+  return r;
 }
 
 // A row of 32 digits (element p = K index 32 g + p of this lane) as fp6 e2m3 values d / 2;
@@ -208,18 +215,34 @@ __device__ __forceinline__ i32x4s make_rsrc(const void* base, int64_t bytes) {
 // LDS address m0 + L * 16 (SZ = 16, 12) or m0 + L * 4 (SZ = 4).  Written as instructions so
 // that the compiler, which cannot tell the LDS image from the rest of LDS, does not wait
 // for them before every LDS access; the caller waits (vmcnt) before reading the image.
-// No register is written.
-template <int SZ>
-__device__ __forceinline__ void load_lds(const i32x4s& rsrc, uint32_t lds_addr, int voffset, int soffset) {
+// The LDS address is lds_base + LOFF and the scalar offset SOFF, both compile-time constants
+// added inside the statement (kept as operands, the 40-odd constants of a tile's loads would
+// occupy scalar registers for the whole scan and push others out to vector-register lanes).
+// No vector register is written.
+template <int SZ, int LOFF, int SOFF>
+__device__ __forceinline__ void load_lds(const i32x4s& rsrc, uint32_t lds_base, int voffset) {
+  int so;
   if constexpr (SZ == 16)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
+    asm volatile("s_add_u32 m0, %1, %4\n\ts_mov_b32 %0, %5\n\tbuffer_load_dwordx4 %2, %3, %0 offen lds"
+                 : "=&s"(so) : "s"(lds_base), "v"(voffset), "s"(rsrc), "i"(LOFF), "i"(SOFF)
+                 : "memory", "m0", "scc");
   else if constexpr (SZ == 12)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx3 %1, %2, %3 offen lds"
-                 :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
+    asm volatile("s_add_u32 m0, %1, %4\n\ts_mov_b32 %0, %5\n\tbuffer_load_dwordx3 %2, %3, %0 offen lds"
+                 : "=&s"(so) : "s"(lds_base), "v"(voffset), "s"(rsrc), "i"(LOFF), "i"(SOFF)
+                 : "memory", "m0", "scc");
   else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory", "m0");
+    asm volatile("s_add_u32 m0, %1, %4\n\ts_mov_b32 %0, %5\n\tbuffer_load_dword %2, %3, %0 offen lds"
+                 : "=&s"(so) : "s"(lds_base), "v"(voffset), "s"(rsrc), "i"(LOFF), "i"(SOFF)
+                 : "memory", "m0", "scc");
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E - 1 (a loop with a compile-time index).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -325,28 +348,28 @@ void decode_mx_scan(MxParams p) {
     r.rv = make_rsrc(p.codes_v + ((vbase + t0) >> 5) * VGW, (left >> 5) * VGW * 4);
     return r;
   };
-  auto dma_keys = [&](const TileRes& r, int k) {   // key group k: records and both norms
-    const int dt = 64 * (k >> 2) + 4 * (k & 3);      // token offset of key group k
-    load_lds<16>(r.rk, tl_addr + 4 * (kTKw + k * 256), koff, dt * FK::RW * 4);
-    load_lds<4>(r.rnk, tl_addr + 4 * (kTKn + k * 64), noff, dt * 4);
-    load_lds<4>(r.rnv, tl_addr + 4 * (kTVn + k * 64), noff, dt * 4);
+  auto dma_keys = [&](const TileRes& r, auto kc) {   // key group k: records and both norms
+    constexpr int k = decltype(kc)::value;
+    constexpr int dt = 64 * (k >> 2) + 4 * (k & 3);     // token offset of key group k
+    load_lds<16, 4 * (kTKw + k * 256), dt * FK::RW * 4>(r.rk, tl_addr, koff);
+    load_lds<4, 4 * (kTKn + k * 64), dt * 4>(r.rnk, tl_addr, noff);
+    load_lds<4, 4 * (kTVn + k * 64), dt * 4>(r.rnv, tl_addr, noff);
   };
   auto dma_values = [&](const TileRes& r) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int blk = c >> 1;
+    static_for<0, 8>([&](auto cc) __attribute__((always_inline)) {
+      constexpr int c = decltype(cc)::value;
+      constexpr int blk = c >> 1;
+      constexpr int so = blk < VSB ? 16 * c * (VLO + 1) * 4 : (16 * c - 32 * VSB) * (VHI + 1) * 4;
       const int vo = blk < VSB ? voff_lo : voff_hi;
-      const int so = blk < VSB ? 16 * c * (VLO + 1) * 4 : (16 * c - 32 * VSB) * (VHI + 1) * 4;
-      if (FV::words(blk) == 4)
-        load_lds<16>(r.rv, tl_addr + 4 * (kTVw + c * 256), vo, so);
+      if constexpr (FV::words(blk) == 4)
+        load_lds<16, 4 * (kTVw + c * 256), so>(r.rv, tl_addr, vo);
       else
-        load_lds<12>(r.rv, tl_addr + 4 * (kTVw + c * 256), vo, so);
-    }
+        load_lds<12, 4 * (kTVw + c * 256), so>(r.rv, tl_addr, vo);
+    });
   };
   auto dma = [&](int64_t t0) {
     const TileRes r = tile_res(t0, true);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) dma_keys(r, k);
+    static_for<0, 8>([&](auto kc) __attribute__((always_inline)) { dma_keys(r, kc); });
     dma_values(r);
   };
   // this lane's part of the LDS image into registers (after the tile's loads completed)
@@ -498,7 +521,8 @@ void decode_mx_scan(MxParams p) {
     ksl[k] = digit_scale(e, 4 + (lane & 3));
   }
   const float lscale = p.scale * 1.4426950408889634f;   // logits in the log2 domain
-  const float cc_h = s_hc[hh][0], cs_h = s_hc[hh][1];
+  // the constants removed after the key products seed their accumulators instead
+  const f32x4 c0_c = {-s_hc[hh][0], 0.f, 0.f, 0.f}, c0_s = {-s_hc[hh][1], 0.f, 0.f, 0.f};
   const float lsg = lscale * p.gamma;
   const uint32_t ones = __builtin_amdgcn_readfirstlane(0x11111111);   // operand of the sign dword
 
@@ -538,9 +562,9 @@ void decode_mx_scan(MxParams p) {
     const int rem = (int)min(t_end - t0, (int64_t)kXTile);
     // -- keys: logits of head hh for tokens key_token(k, n)
     float lg[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      dma_keys(nr, k);
+    static_for<0, 8>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      dma_keys(nr, kc);
       const uint32_t p0 = T.kw[k][0], p1 = T.kw[k][1];
       uint32_t p2, sg;
       if constexpr (KLO == KHI) {
@@ -553,7 +577,7 @@ void decode_mx_scan(MxParams p) {
       }
       // digits 0-3 and 4-7 of every plane into one accumulator per term (the 8 key groups
       // give the scheduler independent chains)
-      f32x4 ac = {0.f, 0.f, 0.f, 0.f}, as = {0.f, 0.f, 0.f, 0.f};
+      f32x4 ac = c0_c, as = c0_s;
       const i32x4 b0 = fp4_of(p0, ones);
       ac = mma(akh[0], b0, ac, ksh[0]);
       ac = mma(akl[0], b0, ac, ksl[0]);
@@ -574,15 +598,15 @@ void decode_mx_scan(MxParams p) {
         as = mma(akh[NPK], bs, as, ksh[NPK]);
         as = mma(akl[NPK], bs, as, ksl[NPK]);
       }
-      const float dc = ((ac[0] + ac[1]) + (ac[2] + ac[3]) - cc_h) * lscale;
-      const float ds = ((as[0] + as[1]) + (as[2] + as[3]) - cs_h) * lsg;
+      const float dc = ((ac[0] + ac[1]) + (ac[2] + ac[3])) * lscale;
+      const float ds = ((as[0] + as[1]) + (as[2] + as[3])) * lsg;
       const float n16 = f16_bits_to_f32(T.kn[k]), r16 = f16_bits_to_f32(T.kn[k] >> 16);
       float v = fmaf(n16, dc, r16 * ds);
       // computed in every lane before the mask: the products must not move under a branch
       // on the token index (their B operands come from other lanes)
       asm volatile("" : "+v"(v));
       lg[k] = key_token(k, n) < rem ? v : -INFINITY;
-    }
+    });
     if (p.logits) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
