@@ -886,7 +886,7 @@ void decode_mx_scan(MxParams p) {
 #pragma unroll
       for (int w = 0; w < kXWaves; ++w) {
         const float mw = w == 0 ? m0 : w == 1 ? m1 : w == 2 ? m2 : m3;
-        const float sc = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+        const float sc = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
         acc_o = fmaf(sc, s_red[w][hd][f], acc_o);
       }
       part0[hd * hstride + 2 + f] = acc_o;
@@ -900,7 +900,7 @@ void decode_mx_scan(MxParams p) {
 #pragma unroll
       for (int w = 0; w < kXWaves; ++w) {
         const float mw = s_m[w][hd][0];
-        l_o = fmaf((mw == -INFINITY) ? 0.0f : exp2f(mw - M), s_m[w][hd][1], l_o);
+        l_o = fmaf((mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M), s_m[w][hd][1], l_o);
       }
       part0[hd * hstride] = M;
       part0[hd * hstride + 1] = l_o;
