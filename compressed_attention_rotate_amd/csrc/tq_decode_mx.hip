@@ -135,24 +135,17 @@ __device__ __forceinline__ i32x4 fp4_xor3(const i32x4& a, const i32x4& b, const 
   return r;
 }
 
-// A row of 32 digits (element p = K index 32 g + p of this lane) as fp6 e2m3 values d / 2;
-// the packed conversion interleaves its two sources (element 2 i from ev[i], 2 i + 1 from od[i])
-// and divides by its scale operand.  It writes its first result dwords before it has read the
-// last source registers, so the result must not share registers with the sources: written
-// as an instruction with an early-clobber result (the compiler's builtin may overlap them).
-__device__ __forceinline__ i32x8 fp6_row(const f32x16& ev, const f32x16& od) {
-  u32x6 r;
-  asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(ev), "v"(od), "v"(2.0f));
-  return (i32x8){(int)r[0], (int)r[1], (int)r[2], (int)r[3], (int)r[4], (int)r[5], 0, 0};
-}
-
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
-// The same from digits given as f16 bit patterns: half i of dword j is element 2 j + i, its low
-// 4 bits the digit d (an f16 subnormal, d 2^-24) and bit 15 its sign, so a digit takes one
-// shift and mask of the word it sits in and no conversion to float; the packed conversion
-// divides by its scale operand, 2^-23, which gives d / 2 exactly (early-clobber result, as
-// above).
+// A row of 32 digits (element p = K index 32 g + p of this lane) as fp6 e2m3 values d / 2,
+// from the digits given as f16 bit patterns: half i of dword j is element 2 j + i, its low 4
+// bits the digit d (an f16 subnormal, d 2^-24) and bit 15 its sign, so a digit takes a shift
+// and mask of the word it sits in and no conversion to float.  The packed conversion divides
+// by its scale operand, 2^-23, which gives d / 2 exactly (checked against the f32 form of the
+// conversion on every digit and sign).  It writes its first result dwords before it has read
+// the last source registers, so the result must not share registers with the sources:
+// written as an instruction with an early-clobber result (the compiler's builtin may overlap
+// them).
 __device__ __forceinline__ i32x8 fp6_row_f16(const u32x16& h) {
   u32x6 r;
   asm volatile("v_cvt_scalef32_pk32_fp6_f16 %0, %1, %2" : "=&v"(r) : "v"(h), "v"(1.1920928955078125e-07f));
@@ -488,16 +481,17 @@ void decode_mx_scan(MxParams p) {
       for (int part = 0; part < 2; ++part) {
         if (part == 0 ? !hi : !lo) continue;
         const int sh = (part == 0 ? 28 : 12) - 4 * l;   // digit l (or 4 + l) of x 2^32
-        f32x16 ev, od;
+        // digits as f16 bit patterns, two per dword, signs in bits 15 and 31 (see fp6_row_f16)
+        u32x16 hd16;
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-          const uint32_t r = e == kZeroExp ? 0u : (uint32_t)ldexpf(fabsf(av[q]), 32 - e);
-          const uint32_t sgn = __float_as_uint(av[q]) & 0x80000000u;
-          const float dg = __uint_as_float(__float_as_uint((float)((r >> sh) & 15u)) | sgn);
-          if (q & 1) od[q >> 1] = dg;
-          else ev[q >> 1] = dg;
+        for (int i = 0; i < 16; ++i) {
+          const float a0 = av[2 * i], a1 = av[2 * i + 1];
+          const uint32_t r0 = e == kZeroExp ? 0u : (uint32_t)ldexpf(fabsf(a0), 32 - e);
+          const uint32_t r1 = e == kZeroExp ? 0u : (uint32_t)ldexpf(fabsf(a1), 32 - e);
+          hd16[i] = ((r0 >> sh) & 15u) | (((r1 >> sh) & 15u) << 16) |
+                    ((__float_as_uint(a0) >> 16) & 0x8000u) | (__float_as_uint(a1) & 0x80000000u);
         }
-        const i32x8 a = fp6_row(ev, od);
+        const i32x8 a = fp6_row_f16(hd16);
 #pragma unroll
         for (int r = 0; r < 6; ++r) s_ak[k][part][r][lane] = (uint32_t)a[r];
       }
