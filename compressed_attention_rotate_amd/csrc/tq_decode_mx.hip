@@ -300,10 +300,22 @@ void decode_mx_scan(MxParams p) {
   const int hh = lane >> 4;                        // C layout: head of this lane
   const int dd = n & 3;                            // token position mod 4 of this lane's tokens
 
-  // ---- query loads first (the tile loads are issued once they have arrived)
-  float qx[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) qx[e] = load_elem(p.q, ((int64_t)b * p.hq + h0 + wave) * kD + lane + 64 * e, p.q_dtype);
+  // ---- query and S loads first, all in flight together (the tile loads are issued once they
+  // have arrived): the query elements lane and lane + 64 as raw bits from one uniform branch
+  // on the type, converted after the S loads are issued, so that no wait splits them
+  uint32_t qraw[2];
+  {
+    const int64_t qi = ((int64_t)b * p.hq + h0 + wave) * kD + lane;
+    if (p.q_dtype == 0 || p.q_dtype == 3) {
+      const uint32_t* qp = reinterpret_cast<const uint32_t*>(p.q) + qi;
+      qraw[0] = qp[0];
+      qraw[1] = qp[64];
+    } else {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + qi;
+      qraw[0] = qp[0];
+      qraw[1] = qp[64];
+    }
+  }
   // S rows 32 wave .. 32 wave + 31: srow[4 r + c] holds row 32 wave + 8 r + lane / 8, columns
   // 32 c + 4 (lane % 8) .. + 3, so the eight lanes of a row read one whole 128-byte line
   f32x4 srow[16];
@@ -313,6 +325,13 @@ void decode_mx_scan(MxParams p) {
     for (int i = 0; i < 16; ++i)
       srow[i] = *reinterpret_cast<const f32x4*>(src + (i >> 2) * 8 * kD + (i & 3) * 32);
   }
+
+  float qx[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    qx[e] = (p.q_dtype == 0 || p.q_dtype == 3) ? __uint_as_float(qraw[e])
+            : p.q_dtype == 1                  ? __uint_as_float(qraw[e] << 16)
+                                              : f16_bits_to_f32(qraw[e]);
 
   // ---- tile loads through buffer resources based at the tile: per-lane offsets are
   // constants, the tile start only moves the (scalar) base
