@@ -762,21 +762,30 @@ __global__ __launch_bounds__(64 * QCfg<D>::NW) void quantize_kernel(QParams p) {
     const int nvalid = (int)((p.n - v0) < TV ? (p.n - v0) : TV);
     const uint32_t* b32 = reinterpret_cast<const uint32_t*>(bal);
     const uint16_t* s16 = reinterpret_cast<const uint16_t*>(sbal);
-    for (int vb = 0; vb < nvalid; vb += vpi) {
-      const int v = vb + sv;
+    // a record has at most 4 NB words, so a group of vpi >= 16 / NB vectors covers a lane's
+    // share of the tile in at most NB passes: every word is read from the tables first and
+    // then stored, so the table reads do not wait on one another
+    uint32_t wv[NB];
+    int64_t rv[NB];
+#pragma unroll
+    for (int it = 0; it < NB; ++it) {
+      const int v = it * vpi + sv;
+      rv[it] = -1;
+      wv[it] = 0u;
       if (s_lane && v < nvalid) {
-        uint32_t word;
         if (s_q != 0xFF) {
-          word = b32[(((v >> 1) * NB + s_blk) * 4 + s_q) * 2 + (v & 1)];
+          wv[it] = b32[(((v >> 1) * NB + s_blk) * 4 + s_q) * 2 + (v & 1)];
         } else {
           const int rr = v & 3, gq = v >> 2;
-          word = (uint32_t)s16[((s_blk * 2 + 0) * 4 + rr) * 4 + gq] |
-                 ((uint32_t)s16[((s_blk * 2 + 1) * 4 + rr) * 4 + gq] << 16);
+          wv[it] = (uint32_t)s16[((s_blk * 2 + 0) * 4 + rr) * 4 + gq] |
+                   ((uint32_t)s16[((s_blk * 2 + 1) * 4 + rr) * 4 + gq] << 16);
         }
-        const int64_t row = dest_row(p, v0 + v);
-        if (row >= 0) p.codes[row * p.words + sw] = word;
+        rv[it] = dest_row(p, v0 + v);
       }
     }
+#pragma unroll
+    for (int it = 0; it < NB; ++it)
+      if (rv[it] >= 0) p.codes[rv[it] * p.words + sw] = wv[it];
     if (lane < nvalid) {
       const int64_t row = dest_row(p, v0 + lane);
       if (row >= 0) p.norms[row] = snorm[lane];
