@@ -306,7 +306,7 @@ def _c4_sparse_v(tq, torch, dev, TI, seed, steps, tau=1e-4):
     torch.cuda.synchronize()
     skipped = int(sk.item())
     out_diff = float((out_g - out_u).abs().max())
-    for _ in range(10):   # untimed pairs: clocks up after the set-up
+    for _ in range(100):   # untimed pairs (~25 ms of decode work): clocks up after the set-up
         dec(0.0, out_u); dec(tau, out_g)
     # per step, 4 ungated then 4 gated decodes back to back between events (as in C3), so
     # that a launch's set-up overlaps the previous decode as in a decode loop
