@@ -152,6 +152,134 @@ def cpu_baseline(kb, vb, qb, rot_seed):
                                         f"the layer): quantize {tq1:.2f} s, decode {td1:.2f} s"}}
 
 
+def _bf16_host(t):
+    """A bf16 device tensor -> its host bit patterns (uint16 numpy array)."""
+    return t.contiguous().view(dtype=__import__("torch").int16).cpu().numpy().view(np.uint16)
+
+
+def _f64_of_bf16(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def cpu_baseline_configs(samples, seed):
+    """The C++ oracle on bounded samples of the other workloads (the same bytes the GPU legs
+    used, copied to the host), timed on every hardware thread:
+      C1: the whole setting (quantize K and V, decode the 64 queries), with the estimator's
+          quality against exact attention computed from the oracle's own reconstruction;
+      C3: one sequence of layer 0 (32768 tokens x 8 KV heads at 3.5 bits, 1/16 of the layer),
+          with the 32-layer x 16-sequence time extrapolated from it;
+      C4: sequence 0 of 4 (131072 tokens x 8 KV heads, K b=4 / V b=3), decoded ungated and
+          gated (tau = 1e-4);
+      C5: the first 100000 database vectors and the first 100 queries: index build, the
+          estimated top-10 (dequantized database) and the exact top-10 within the sample."""
+    from oracle import tq_oracle as O
+    from oracle import tq_oracle_cpp as C
+    threads = C.hardware_threads()
+    res = {}
+    if "C1" in samples:
+        import tq_inputs as TI
+        k, v, q, _ = TI.c1_inputs(seed=TI.data_seed(1) + seed)
+        n, d = k.shape
+        fmt = O.Format.uniform(d, 2)
+        signs, S = O.make_rotation(d, TI.rotation_seed(1) + seed)
+        cb = O.codebook(d, 2)
+        t0 = time.perf_counter()
+        rk = C.quantize(k.astype(np.float64), fmt, signs, S, cb)
+        rv = C.quantize(v.astype(np.float64), fmt, signs, S, cb)
+        t1 = time.perf_counter()
+        kt = C.dequantize(*rk, fmt, signs, S, cb).reshape(1, 1, n, d)
+        vt = C.dequantize(*rv, fmt, signs, S, cb).reshape(1, 1, n, d)
+        oq, lq = C.attend(q.astype(np.float64)[None], kt, vt, [n], 1 / math.sqrt(d))
+        t2 = time.perf_counter()
+        q64, k64, v64 = q.astype(np.float64), k.astype(np.float64), v.astype(np.float64)
+        le = q64 @ k64.T / math.sqrt(d)
+        lq = lq[0]
+        pe, pq = _softmax_rows(le), _softmax_rows(lq)
+        oe = pe @ v64
+        kl = np.sum(pe * (np.log(np.maximum(pe, 1e-300)) - np.log(np.maximum(pq, 1e-300))), axis=1)
+        rel = np.linalg.norm(oq[0] - oe, axis=1) / np.linalg.norm(oe, axis=1)
+        res["C1"] = {"sample": "the whole setting (8192 vectors quantized, 64 queries decoded)",
+                     "quantize_s": round(t1 - t0, 4), "decode_s": round(t2 - t1, 4),
+                     "oracle_quality": {
+                         "logit_rmse_over_sigma": float(np.sqrt(np.mean((lq - le) ** 2)) / np.std(le)),
+                         "softmax_max_abs_dp": float(np.max(np.abs(pq - pe))),
+                         "kl_mean": float(np.mean(kl)), "out_rel_l2_mean": float(np.mean(rel))}}
+
+    def layer_sample(kbits, vbits, qbits, fk, fv, cbk, cbv, signs, S, taus):
+        nh, ntok, d = kbits.shape
+        kx, vx = _f64_of_bf16(kbits).reshape(-1, d), _f64_of_bf16(vbits).reshape(-1, d)
+        t0 = time.perf_counter()
+        rk = C.quantize(kx, fk, signs, S, *cbk)
+        rv = C.quantize(vx, fv, signs, S, *cbv)
+        t1 = time.perf_counter()
+        del kx, vx
+        kt = C.dequantize(*rk, fk, signs, S, *cbk).reshape(1, nh, ntok, d)
+        vt = C.dequantize(*rv, fv, signs, S, *cbv).reshape(1, nh, ntok, d)
+        q = _f64_of_bf16(qbits).reshape(1, -1, d)
+        t2 = time.perf_counter()
+        out = {}
+        for tau in taus:
+            ta = time.perf_counter()
+            _, _, dropped = C.attend(q, kt, vt, [ntok], 1 / math.sqrt(d), tau=tau, return_dropped=True)
+            out[tau] = (time.perf_counter() - ta, int(dropped.sum()))
+        packed = nh * ntok * (fk.record_bytes() + fv.record_bytes() + 8)
+        return t1 - t0, t2 - t1, out, packed
+
+    if "C3" in samples:
+        kbits, vbits, qbits, rseed = samples["C3"]
+        signs, S = O.make_rotation(D, rseed)
+        f = O.Format(D, 3, 2, 64)
+        cbs = (O.codebook(D, 3), O.codebook(D, 2))
+        tq_, tdq, att, packed = layer_sample(kbits, vbits, qbits, f, f, cbs, cbs, signs, S, [0.0])
+        td = tdq + att[0.0][0]
+        ntok = kbits.shape[1]
+        res["C3"] = {"sample": "sequence 0 of layer 0: 32768 tokens x 8 KV heads at 3.5 bits "
+                               "(1/16 of a layer), its 32 query heads decoded once",
+                     "quantize_tokens_per_s": round(ntok / tq_, 1),
+                     "decode_gbs": round(packed / td / 1e9, 5),
+                     "extrapolated_32_layers_x_16_sequences_s": round(32 * 16 * (tq_ + td), 1)}
+    if "C4" in samples:
+        kbits, vbits, qbits, rseed, tau = samples["C4"]
+        signs, S = O.make_rotation(D, rseed)
+        fk, fv = O.Format.uniform(D, 3), O.Format.uniform(D, 2)
+        tq_, tdq, att, packed = layer_sample(kbits, vbits, qbits, fk, fv, (O.codebook(D, 3),),
+                                             (O.codebook(D, 2),), signs, S, [0.0, tau])
+        ntok = kbits.shape[1]
+        res["C4"] = {"sample": "sequence 0 of 4: 131072 tokens x 8 KV heads, K b=4 / V b=3, "
+                               "its 32 query heads decoded ungated and gated",
+                     "quantize_tokens_per_s": round(ntok / tq_, 1),
+                     "dequantize_s": round(tdq, 3),
+                     "decode_gbs_ungated": round(packed / (tdq + att[0.0][0]) / 1e9, 5),
+                     "decode_gbs_gated": round(packed / (tdq + att[tau][0]) / 1e9, 5),
+                     "gated_rows_dropped_per_query_head": round(att[tau][1] / HQ, 1),
+                     "tau": tau}
+    if "C5" in samples:
+        db, qs, rseed = samples["C5"]
+        d = 256
+        signs, S = O.make_rotation(d, rseed)
+        fmt = O.Format.uniform(d, BITS)
+        cb = O.codebook(d, BITS)
+        t0 = time.perf_counter()
+        rec = C.quantize(db.astype(np.float64), fmt, signs, S, cb)
+        t1 = time.perf_counter()
+        xt = C.dequantize(*rec, fmt, signs, S, cb)
+        t2 = time.perf_counter()
+        qp = np.zeros((qs.shape[0], d))
+        qp[:, :qs.shape[1]] = qs
+        est, _ = C.topk_ip(qp, xt, 10)
+        t3 = time.perf_counter()
+        ex, _ = C.topk_ip(qs.astype(np.float64), db.astype(np.float64), 10)
+        pairs = qs.shape[0] * db.shape[0]
+        res["C5"] = {"sample": f"the first {db.shape[0]} database vectors and the first "
+                               f"{qs.shape[0]} queries (d=200 zero-padded to 256, b=4)",
+                     "index_vectors_per_s": round(db.shape[0] / (t1 - t0), 1),
+                     "dequantize_s": round(t2 - t1, 3),
+                     "search_pairs_per_s": round(pairs / (t3 - t2), 1),
+                     "queries_per_s_at_1e6_vectors": round(pairs / (t3 - t2) / 1e6, 3),
+                     "recall_at_10_in_sample": round(O.recall_at_k(est, ex), 4)}
+    return {"cores": int(threads), "configs": res}
+
+
 def _softmax_rows(x):
     m = x.max(axis=1, keepdims=True)
     e = np.exp(x - m)
@@ -203,7 +331,7 @@ def _decode_roofline(name, nbytes, t):
             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
 
 
-def _c3_layers(tq, torch, dev, TI, seed, n_layers=32, batch=16, dec_steps=4):
+def _c3_layers(tq, torch, dev, TI, seed, n_layers=32, batch=16, dec_steps=4, samples=None):
     """32 full-size layers, batch 16 x 32768 tokens each, 32 q / 8 kv heads, distinct seeds
     per layer (data and rotation), K and V at 3.5 bits (3-bit codebook on rotated
     coordinates 0-63, 2-bit on 64-127, + QJL; values token-sliced).  Per layer: the prefill
@@ -229,6 +357,9 @@ def _c3_layers(tq, torch, dev, TI, seed, n_layers=32, batch=16, dec_steps=4):
         tk, tv = tq.Tables(fk, signs, Sd), tq.Tables(fv, signs, Sd)
         qb = TI.decode_queries(batch, HQ, D, TI.data_seed(3, layer) + seed)
         q = torch.from_numpy(qb.view(np.int16)).to(dev).view(torch.bfloat16)
+        if samples is not None and layer == 0:   # for the CPU baseline: sequence 0 of layer 0
+            samples["C3"] = (_bf16_host(kx[0]), _bf16_host(vx[0]), qb[0].copy(),
+                             TI.rotation_seed(3, layer) + seed)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         torch.cuda.synchronize()
         ev[0].record()
@@ -264,7 +395,7 @@ def _c3_layers(tq, torch, dev, TI, seed, n_layers=32, batch=16, dec_steps=4):
             "roofline": _decode_roofline("decode_mx_scan+decode_combine", packed, td)}
 
 
-def _c4_sparse_v(tq, torch, dev, TI, seed, steps, tau=1e-4):
+def _c4_sparse_v(tq, torch, dev, TI, seed, steps, tau=1e-4, samples=None):
     """Batch 4 x 131072 tokens, 32 q / 8 kv heads; keys at b = 4 with 1% of token positions
     per sequence carrying x10 keys, values at b = 3 (token-sliced).  Decode gated
     (tau = 1e-4) and ungated on the same packed cache, interleaved in blocks of 4 launches
@@ -291,6 +422,9 @@ def _c4_sparse_v(tq, torch, dev, TI, seed, steps, tau=1e-4):
     ev[2].record()
     torch.cuda.synchronize()
     t_q = (ev[0].elapsed_time(ev[1]) + ev[1].elapsed_time(ev[2])) * 1e-3
+    if samples is not None:   # for the CPU baseline: sequence 0
+        samples["C4"] = (_bf16_host(kx[0]), _bf16_host(vx[0]), qb[0].copy(),
+                         TI.rotation_seed(4) + seed, tau)
     del kx, vx
     rbk, rbv = fk.record_bytes(), fv.record_bytes()
     ck, nk = ck.view(batch, HKV, ntok, rbk), nk.view(batch, HKV, ntok, 2)
@@ -580,7 +714,7 @@ def _graph_decode_timing(torch, decode, reps=5):
     return ev[0].elapsed_time(ev[1]) * 1e-3 / (reps * SLOTS)
 
 
-def _search_timing(tq, torch, dev, TI, reps=2, seed=0):
+def _search_timing(tq, torch, dev, TI, reps=2, seed=0, samples=None):
     """Inner-product search on the 10^6 x 200 database (unit vectors, std i^-0.3 per
     coordinate), zero-padded to d = 256 and packed at b = 4; 10^4 queries from the same law,
     top-10.  Times the index build (quantize of the database) and the search of all queries.
@@ -589,8 +723,13 @@ def _search_timing(tq, torch, dev, TI, reps=2, seed=0):
     are split into fp16 hi + lo halves, so it issues 5 products where the dot products
     count 2."""
     n_db, n_q, d_in, d, k = 10 ** 6, 10 ** 4, 200, 256, 10
-    db = torch.from_numpy(TI.search_set(n_db, d_in, seed=TI.data_seed(5) + seed)).to(dev)
-    qs = torch.from_numpy(TI.search_set(n_q, d_in, seed=TI.data_seed(5) + seed + 1)).to(dev)
+    db_h = TI.search_set(n_db, d_in, seed=TI.data_seed(5) + seed)
+    qs_h = TI.search_set(n_q, d_in, seed=TI.data_seed(5) + seed + 1)
+    if samples is not None:   # for the CPU baseline: a prefix of the database and queries
+        samples["C5"] = (db_h[:100000].copy(), qs_h[:100].copy(), TI.rotation_seed(5) + seed)
+    db = torch.from_numpy(db_h).to(dev)
+    qs = torch.from_numpy(qs_h).to(dev)
+    del db_h, qs_h
     signs, S = tq.make_rotation(d, TI.rotation_seed(5) + seed)
     fmt = tq.Format.uniform(d, BITS)
     tab = tq.Tables(fmt, signs, torch.from_numpy(S).to(dev))
@@ -774,9 +913,11 @@ def main():
             "hbm_copy_gbs": round(copy_gbs, 1),
             "decode_pct_copy_bw": round(100.0 * decode_gbs / copy_gbs, 2),
             "decode_us": round(float(dc.mean()) * 1e6, 3),
+            "decode_us_median": round(float(np.median(dc)) * 1e6, 3),
             "decode_us_graph_replay": round(_graph_decode_timing(torch, decode) * 1e6, 3),
             "quantize_tokens_per_s": round(qtoks, 1),
             "quantize_k_us_per_launch": round(q_launch * 1e6, 3),
+            "quantize_k_us_median": round(float(np.median(qk)) * 1e6, 3),
             "quantize_v_sliced_us_per_launch": round(float(qv.mean()) * 1e6, 3),
             "roofline": {"bound": "mfma", "kernel": "quantize_kernel<128,3,3> (key tensor)",
                          "achieved": round(q_tfs, 3), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
@@ -813,20 +954,28 @@ def main():
         del ks, vs, codes_k, codes_vs, norms_k, norms_v, ws
         torch.cuda.empty_cache()
     configs = {}
+    samples = None if args.no_cpu_baseline else {}
     if "C1" in run:
         configs["C1"] = _c1_quality(tq, torch, dev, TI, args.seed)
+        if samples is not None:
+            samples["C1"] = True
     if "C3" in run:
-        configs["C3"] = _c3_layers(tq, torch, dev, TI, args.seed)
+        configs["C3"] = _c3_layers(tq, torch, dev, TI, args.seed, samples=samples)
         torch.cuda.empty_cache()
     if "C4" in run:
-        configs["C4"] = _c4_sparse_v(tq, torch, dev, TI, args.seed, min(args.steps, 20))
+        configs["C4"] = _c4_sparse_v(tq, torch, dev, TI, args.seed, min(args.steps, 20),
+                                     samples=samples)
         torch.cuda.empty_cache()
     if "C5" in run:
-        configs["C5"] = _search_timing(tq, torch, dev, TI, seed=args.seed)
+        configs["C5"] = _search_timing(tq, torch, dev, TI, seed=args.seed, samples=samples)
     if configs:
         line["configs"] = configs
     if "C2" in run and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(kb, vb, qb, TI.rotation_seed(2) + args.seed)
+    if samples:
+        extra = cpu_baseline_configs(samples, args.seed)
+        line.setdefault("cpu_baseline", {"kind": "oracle", "cores": extra["cores"]})
+        line["cpu_baseline"]["configs"] = extra["configs"]
     print(json.dumps(line), flush=True)
 
 

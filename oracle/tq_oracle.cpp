@@ -22,6 +22,7 @@
 //    dequantized keys and values (163.com explainer, section "速度").
 // Work is split over rows (vectors, or query heads) among std::thread workers; each row's
 // arithmetic is the same whatever the thread count.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -264,10 +265,13 @@ void tqo_dequantize(const int32_t* fmt5, const double* cents_lo, const double* c
 // Decode one step: for each (batch b, query head h) softmax attention of q [batch][hq][d]
 // over the first lens[b] dequantized keys / values of KV head h / (hq / hkv).  kt / vt:
 // dequantized caches [batch][hkv][cap][d] (fp64, from tqo_dequantize).  out [batch][hq][d],
-// logits [batch][hq][cap] (entries t >= lens[b] untouched).
+// logits [batch][hq][cap] (entries t >= lens[b] untouched).  With tau > 0 the value rows whose
+// final softmax weight is below tau are left out of the sum (no renormalization: the Sparse-V
+// gate of the zhidx article, section "01 turboquant_plus：介绍与详解"), and dropped[bh] (when
+// not null) receives the number of rows left out for that (batch, query head).
 void tqo_attend(const double* q, const double* kt, const double* vt, const int32_t* lens,
                 int32_t batch, int32_t hq, int32_t hkv, int64_t cap, int32_t d, double scale,
-                double* out, double* logits, int32_t threads) {
+                double tau, double* out, double* logits, int64_t* dropped, int32_t threads) {
   const int G = hq / hkv;
   parallel_rows((int64_t)batch * hq, threads, [&](int64_t bh) {
     const int64_t b = bh / hq, h = bh % hq, kh = h / G;
@@ -285,12 +289,47 @@ void tqo_attend(const double* q, const double* kt, const double* vt, const int32
     }
     double* o = out + bh * d;
     for (int j = 0; j < d; ++j) o[j] = 0.0;
-    if (L == 0) return;
-    double sum = 0.0;
-    for (int64_t t = 0; t < L; ++t) sum += std::exp(lg[t] - m);
-    for (int64_t t = 0; t < L; ++t) {
-      const double p = std::exp(lg[t] - m) / sum;
-      for (int j = 0; j < d; ++j) o[j] += p * V[t * d + j];
+    int64_t n_drop = 0;
+    if (L > 0) {
+      double sum = 0.0;
+      for (int64_t t = 0; t < L; ++t) sum += std::exp(lg[t] - m);
+      for (int64_t t = 0; t < L; ++t) {
+        const double p = std::exp(lg[t] - m) / sum;
+        if (tau > 0.0 && p < tau) {
+          ++n_drop;
+          continue;
+        }
+        for (int j = 0; j < d; ++j) o[j] += p * V[t * d + j];
+      }
+    }
+    if (dropped) dropped[bh] = n_drop;
+  });
+}
+
+// Inner-product top-k (163.com explainer, section "向量搜索"): for each query i of
+// q [nq][d], the k rows of x [n][d] with the largest <q_i, x_t>, in descending order of the
+// score; equal scores are ranked by the lower row index.  ids [nq][k] (-1 and -inf past n),
+// scores [nq][k].  With x the dequantized database this is the estimator's top-k; with the
+// raw vectors it is the exact one.
+void tqo_topk_ip(const double* q, const double* x, int64_t n, int64_t nq, int32_t d, int32_t k,
+                 int64_t* ids, double* scores, int32_t threads) {
+  parallel_rows(nq, threads, [&](int64_t i) {
+    const double* qv = q + i * d;
+    std::vector<double> sc(n);
+    for (int64_t t = 0; t < n; ++t) {
+      double acc = 0.0;
+      for (int j = 0; j < d; ++j) acc += x[t * d + j] * qv[j];
+      sc[t] = acc;
+    }
+    std::vector<int64_t> idx(n);
+    for (int64_t t = 0; t < n; ++t) idx[t] = t;
+    const int64_t kk = std::min<int64_t>(k, n);
+    std::partial_sort(idx.begin(), idx.begin() + kk, idx.end(), [&](int64_t a, int64_t b) {
+      return sc[a] > sc[b] || (sc[a] == sc[b] && a < b);
+    });
+    for (int r = 0; r < k; ++r) {
+      ids[i * k + r] = r < kk ? idx[r] : -1;
+      scores[i * k + r] = r < kk ? sc[idx[r]] : -INFINITY;
     }
   });
 }

@@ -38,7 +38,8 @@ def load() -> ctypes.CDLL:
         lib.tqo_fp16_bits.argtypes = [P, I64, P]
         lib.tqo_quantize.argtypes = [P, P, P, P, P, P, P, P, I64, I32, P, P, P, I32]
         lib.tqo_dequantize.argtypes = [P, P, P, P, P, P, P, P, I64, P, I32]
-        lib.tqo_attend.argtypes = [P, P, P, P, I32, I32, I32, I64, I32, F64, P, P, I32]
+        lib.tqo_attend.argtypes = [P, P, P, P, I32, I32, I32, I64, I32, F64, F64, P, P, P, I32]
+        lib.tqo_topk_ip.argtypes = [P, P, I64, I64, I32, I32, P, P, I32]
         _lib = lib
     return _lib
 
@@ -98,9 +99,12 @@ def dequantize(records, n16, r16, fmt, signs, S, cb_lo, cb_hi=None, threads: int
     return x
 
 
-def attend(q, kt, vt, lens, scale: float, threads: int = 0):
+def attend(q, kt, vt, lens, scale: float, threads: int = 0, tau: float = 0.0,
+           return_dropped: bool = False):
     """q [batch, hq, d] against dequantized caches kt, vt [batch, hkv, cap, d] (fp64), the
-    first lens[b] tokens of each sequence -> (out [batch, hq, d], logits [batch, hq, cap])."""
+    first lens[b] tokens of each sequence -> (out [batch, hq, d], logits [batch, hq, cap]).
+    tau > 0: value rows with a final weight below tau are left out (no renormalization);
+    with return_dropped the per-(batch, head) counts of those rows come third."""
     q = np.ascontiguousarray(q, np.float64)
     kt = np.ascontiguousarray(kt, np.float64)
     vt = np.ascontiguousarray(vt, np.float64)
@@ -109,6 +113,20 @@ def attend(q, kt, vt, lens, scale: float, threads: int = 0):
     ln = np.ascontiguousarray(lens, np.int32)
     out = np.empty((batch, hq, d), np.float64)
     lg = np.full((batch, hq, cap), np.nan, np.float64)
-    load().tqo_attend(_p(q), _p(kt), _p(vt), _p(ln), batch, hq, hkv, cap, d, float(scale), _p(out),
-                      _p(lg), int(threads))
-    return out, lg
+    dropped = np.zeros((batch, hq), np.int64)
+    load().tqo_attend(_p(q), _p(kt), _p(vt), _p(ln), batch, hq, hkv, cap, d, float(scale),
+                      float(tau), _p(out), _p(lg), _p(dropped), int(threads))
+    return (out, lg, dropped) if return_dropped else (out, lg)
+
+
+def topk_ip(q, x, k: int, threads: int = 0):
+    """Top-k rows of x [n, d] by inner product with each query of q [nq, d] (fp64), ties to
+    the lower row -> (ids int64 [nq, k], scores [nq, k])."""
+    q = np.ascontiguousarray(q, np.float64)
+    x = np.ascontiguousarray(x, np.float64)
+    nq, d = q.shape
+    n = x.shape[0]
+    ids = np.empty((nq, k), np.int64)
+    sc = np.empty((nq, k), np.float64)
+    load().tqo_topk_ip(_p(q), _p(x), n, nq, d, int(k), _p(ids), _p(sc), int(threads))
+    return ids, sc

@@ -115,3 +115,51 @@ def test_attention_matches_python_oracle_and_threads_do_not_matter():
     r8 = C.quantize(kx[:64], fmt, signs, S, *cbs, threads=0)
     for a, b_ in zip(r1, r8):
         assert np.array_equal(a, b_)
+
+
+def test_gated_attention_matches_python_oracle():
+    # Sparse-V gate: rows under tau dropped, no renormalization; one head with a x10 spike so
+    # that both kept and dropped rows occur
+    d, hq, hkv, cap = 128, 4, 1, 400
+    lens = [400]
+    fmt = O.Format.uniform(d, 3)
+    kb, vb, _ = TI.kv_layer(1, hkv, cap, d, seed=4700, spike_frac=0.02)
+    qb = TI.decode_queries(1, hq, d, 4700)
+    signs, S = O.make_rotation(d, 4701)
+    cbs = oracle_codebooks(d, 3, 3)
+    kx, vx = TI.bf16_to_f64(kb).reshape(-1, d), TI.bf16_to_f64(vb).reshape(-1, d)
+    rk, nk, rrk = C.quantize(kx, fmt, signs, S, *cbs)
+    rv, nv, rrv = C.quantize(vx, fmt, signs, S, *cbs)
+    kt = C.dequantize(rk, nk, rrk, fmt, signs, S, *cbs).reshape(1, hkv, cap, d)
+    vt = C.dequantize(rv, nv, rrv, fmt, signs, S, *cbs).reshape(1, hkv, cap, d)
+    q = TI.bf16_to_f64(qb)
+    tau = 1e-3
+    out, _, dropped = C.attend(q, kt, vt, lens, 1 / math.sqrt(d), threads=2, tau=tau,
+                               return_dropped=True)
+    n_total = 0
+    for h in range(hq):
+        o, _, _, nd, _ = O.attend(q[0, h], kt[0, 0], vt[0, 0], 1 / math.sqrt(d), tau=tau)
+        assert dropped[0, h] == nd
+        n_total += nd
+        assert np.max(np.abs(out[0, h] - o)) <= 1e-12 * max(1.0, np.max(np.abs(o)))
+    assert 0 < n_total < hq * cap
+
+
+def test_topk_matches_python_oracle_scores_with_ties_to_lower_row():
+    g = np.random.default_rng(4800)
+    n, nq, d, k = 700, 9, 16, 10
+    x = g.standard_normal((n, d))
+    x[350] = x[20]          # equal scores: the lower row ranks first
+    x[600] = x[20]
+    q = g.standard_normal((nq, d))
+    q[3] = x[20] * 3.0      # row 20 and its copies are the top three of query 3
+    ids, sc = C.topk_ip(q, x, k, threads=3)
+    ref = O.search_scores(q, x)
+    for i in range(nq):
+        order = np.lexsort((np.arange(n), -ref[i]))[:k]   # score descending, then row
+        assert np.array_equal(ids[i], order)
+        assert np.max(np.abs(sc[i] - ref[i, order])) <= 1e-12 * max(1.0, np.max(np.abs(ref[i])))
+    assert list(ids[3, :3]) == [20, 350, 600]
+    # fewer rows than k: the tail is empty
+    ids2, sc2 = C.topk_ip(q[:2], x[:4], 6)
+    assert (ids2[:, 4:] == -1).all() and np.isneginf(sc2[:, 4:]).all()
