@@ -43,8 +43,12 @@ __device__ __forceinline__ uint32_t transpose32(uint32_t r, int lane) {
 }
 
 // d = 128; blocks below SPLITB use BLO code bits, the others BHI; Q sign words (0 or 1).
+// Records are read and written in the widest aligned units their word counts allow (16 or
+// 8 bytes), so that a wave issues few, dense memory instructions.
 template <int BLO, int BHI, int SPLITB, int Q>
 __global__ __launch_bounds__(256) void tile_values(uint32_t* __restrict__ codes, int64_t n_groups) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   constexpr int WLO = BLO + Q, WHI = BHI + Q;
   constexpr int W = SPLITB * WLO + (4 - SPLITB) * WHI;   // words per record
   const int lane = threadIdx.x & 63, t = lane & 31;
@@ -52,8 +56,28 @@ __global__ __launch_bounds__(256) void tile_values(uint32_t* __restrict__ codes,
   const bool valid = grp < n_groups;
   uint32_t r[W];
   uint32_t* gbase = codes + grp * 32 * W;
+  if (valid) {
+    const uint32_t* rec = gbase + (int64_t)t * W;   // 4 W bytes from a 128-byte aligned group
+    if constexpr (W % 4 == 0) {
 #pragma unroll
-  for (int k = 0; k < W; ++k) r[k] = valid ? gbase[(int64_t)t * W + k] : 0u;
+      for (int i = 0; i < W / 4; ++i) {
+        const u32x4 x = reinterpret_cast<const u32x4*>(rec)[i];
+        r[4 * i] = x[0]; r[4 * i + 1] = x[1]; r[4 * i + 2] = x[2]; r[4 * i + 3] = x[3];
+      }
+    } else if constexpr (W % 2 == 0) {
+#pragma unroll
+      for (int i = 0; i < W / 2; ++i) {
+        const u32x2 x = reinterpret_cast<const u32x2*>(rec)[i];
+        r[2 * i] = x[0]; r[2 * i + 1] = x[1];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < W; ++k) r[k] = rec[k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < W; ++k) r[k] = 0u;
+  }
   // every load of the group lands before any store overwrites it (in place)
   __syncthreads();
 #pragma unroll
@@ -66,8 +90,15 @@ __global__ __launch_bounds__(256) void tile_values(uint32_t* __restrict__ codes,
     const int j = 32 * b + t;                                                  // coordinate
     const int64_t off = j < 32 * SPLITB ? (int64_t)j * WLO
                                         : (int64_t)32 * SPLITB * WLO + (int64_t)(j - 32 * SPLITB) * WHI;
+    if (wb == 4) {          // 16-byte aligned: off is a multiple of 4 words
+      *reinterpret_cast<u32x4*>(gbase + off) = (u32x4){r[k0], r[k0 + 1], r[k0 + 2], r[k0 + 3]};
+    } else if (wb == 2) {   // 8-byte aligned: off is even
+      *reinterpret_cast<u32x2*>(gbase + off) = (u32x2){r[k0], r[k0 + 1]};
+    } else {
 #pragma unroll
-    for (int p = 0; p < wb; ++p) gbase[off + p] = r[k0 + p];
+      for (int p = 0; p < 4; ++p)
+        if (p < wb) gbase[off + p] = r[k0 + p];
+    }
   }
 }
 
