@@ -51,12 +51,11 @@
 #include <type_traits>
 
 #include "tq_decode_kernel.h"
+#include "tq_mx.h"
 
 namespace tqx {
 using namespace tqk;
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 constexpr int kXWaves = 4;
@@ -87,15 +86,6 @@ struct MxParams {
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
-
-// A (fp6 e2m3 digit rows, E8M0 scale byte `sa` of this lane's row and block) x B (fp4) + C
-__device__ __forceinline__ f32x4 mma(const i32x8& a, const i32x4& b, f32x4 c, int sa) {
-  const i32x8 bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 2, 4, 0, sa, 0, 127);
-}
-
-typedef int i32x6 __attribute__((ext_vector_type(6)));
 
 // acc += A (fp6 digit rows, scale byte sa) x B (fp4) with acc held in accumulation registers
 // (AGPRs) across the whole scan: value sums that are only read after the last tile never take
@@ -110,65 +100,11 @@ __device__ __forceinline__ void mma_acc(f32x4& acc, const i32x8& a, const i32x4&
       : "v"(a6), "v"(b), "v"(sa), "v"(127));
 }
 
-// fp4 B operand of one plane word (see the file comment); the nibble-sign dword gives -0.5 s:
-// (w & 0x88888888) | 0x11111111 as one bitfield insert, `ones` holding 0x11111111
-__device__ __forceinline__ i32x4 fp4_of(uint32_t w, uint32_t ones) {
-  i32x4 b;
-  b[0] = (int)(w & 0x11111111u);
-  b[1] = (int)(w & 0x22222222u);
-  b[2] = (int)(w & 0x44444444u);
-  uint32_t d3;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d3) : "s"(0x88888888u), "v"(w), "v"(ones));
-  b[3] = (int)d3;
-  return b;
-}
-
-// fp4 operand of the XOR of three plane words from theirs: every dword is the XOR of the
-// three (the sign dword's 0001 nibbles XOR to 0001 again), one three-input bit operation each
-// (truth table 0x96).  Written as instructions: the compiler builds a three-input XOR from two
-// two-input ones, and rebuilds this one from the plane words (two instructions per dword).
-__device__ __forceinline__ i32x4 fp4_xor3(const i32x4& a, const i32x4& b, const i32x4& c) {
-  i32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r[i]) : "v"(a[i]), "v"(b[i]), "v"(c[i]));
-  return r;
-}
-
-typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
-
-// A row of 32 digits (element p = K index 32 g + p of this lane) as fp6 e2m3 values d / 2,
-// from the digits given as f16 bit patterns: half i of dword j is element 2 j + i, its low 4
-// bits the digit d (an f16 subnormal, d 2^-24) and bit 15 its sign, so a digit takes a shift
-// and mask of the word it sits in and no conversion to float.  The packed conversion divides
-// by its scale operand, 2^-23, which gives d / 2 exactly (checked against the f32 form of the
-// conversion on every digit and sign).  It writes its first result dwords before it has read
-// the last source registers, so the result must not share registers with the sources:
-// written as an instruction with an early-clobber result (the compiler's builtin may overlap
-// them).
-__device__ __forceinline__ i32x8 fp6_row_f16(const u32x16& h) {
-  u32x6 r;
-  asm volatile("v_cvt_scalef32_pk32_fp6_f16 %0, %1, %2" : "=&v"(r) : "v"(h), "v"(1.1920928955078125e-07f));
-  return (i32x8){(int)r[0], (int)r[1], (int)r[2], (int)r[3], (int)r[4], (int)r[5], 0, 0};
-}
-
 // The value of the other quad of this lane's 8-lane group (DPP row_half_mirror: lane i and
 // lane 7 - i of each half row): the xor-4 partner's value once the value is uniform within
 // each quad, as it is after exchanges at distances 1 and 2.  A DPP move, not an LDS swizzle.
 __device__ __forceinline__ float quad_swap(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-}
-
-// Block exponent: e with |x| 2^-e in [0.5, 1); blocks below 2^-80 count as zero (e = -100)
-constexpr int kZeroExp = -100;
-__device__ __forceinline__ int block_exp(float amax) {
-  return amax >= 8.271806125530277e-25f ? __builtin_amdgcn_frexp_expf(amax) : kZeroExp;
-}
-
-// E8M0 scale byte of digit row l (digits stored as d / 2) of a block with exponent e:
-// 2^(e - 4(l + 1) + 1); zero blocks (all digits 0) get any valid byte
-__device__ __forceinline__ int digit_scale(int e, int l) {
-  return e == kZeroExp ? 127 : e - 4 * (l + 1) + 128;
 }
 
 // Format helpers (d = 128, four blocks of 32 coordinates; SB = first block of the hi width).

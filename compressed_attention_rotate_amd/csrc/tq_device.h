@@ -163,7 +163,7 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t i, int dtyp
 }
 
 // ---------------------------------------------------------------------------------------
-// Subset-sum table reads (decode key scan, few-query search): entry idx of a table with one
+// Subset-sum table reads (decode key scan over per-vector records): entry idx of a table with one
 // float per head (GC heads side by side).
 typedef float tq_f32x4 __attribute__((ext_vector_type(4)));
 typedef float tq_f32x2 __attribute__((ext_vector_type(2)));

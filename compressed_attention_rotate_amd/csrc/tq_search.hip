@@ -27,6 +27,8 @@
 //   merge:    per query, the lists of the database splits are merged (skipped when there is
 //             one split: the scan then writes the final result); each wave sorts its first
 //             64 candidates whole and screens the rest against its k-th entry.
+// At most four queries take a scan of their own on the block-scaled fp6 x fp4 matrix cores
+// (search_mxq below), which scores all of them from one pass over the records.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,6 +36,7 @@
 
 #include "tq_device.h"
 #include "tq_internal.h"
+#include "tq_mx.h"
 
 namespace tqk {
 
@@ -70,7 +73,7 @@ struct SearchParams {
   float gamma;
   uint32_t sign_mask[8];
   float cent[8];     // codebook, ascending
-  float alpha[4];    // Walsh coefficients of the codebook (few-query scan)
+  float alpha[4];    // Walsh coefficients of the codebook (few-query scan: plane weights)
 };
 
 // ----------------------------------------------------------------------------- prologue
@@ -520,153 +523,262 @@ __global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
   }
 }
 
-// ----------------------------------------------------------------------------- few queries
 // With at most kLutQ queries the batched scan would leave most of its 32 query columns
-// empty.  This scan scores one query per workgroup with lane = database vector, as the
-// decode key scan does: in LDS, Tq[g][m] = sum of q_rot over the set bits of byte m of
-// coordinate group g and Ts[g][n] = 2 * sum of S q_rot over the set bits of nibble n; the
-// codebook term through the Walsh expansion of the symmetric codebook,
-// <q_rot, c[idx]> = sum_S alpha_S (2 T_S - sum_j q_rot_j) over the odd subsets S of the
-// code planes, and the QJL term <S q_rot, 2 sigma - 1> = Ts reads - sum_j (S q_rot)_j.
-// Each wave keeps a top-k list; the workgroup merges its waves' lists into the split's.
+// empty: they go to the scan below instead.
 constexpr int kLutQ = 4;
-constexpr int kLWaves = 4;
+
+// ----------------------------------------------------------------------------- few queries
+// on the block-scaled matrix cores.  Up to four queries are scored together by
+// v_mfma_scale_f32_16x16x128_f8f6f4 straight from the records (the operand encodings are
+// described in tq_mx.h): the symmetric codebook is an odd function of the code bits, so
+// c[idx] = sum_k alpha_k s_k over the odd Walsh monomials s_k of the bit-planes (for 3 bits:
+// s0, s1, s2 and s0 s1 s2, the XOR plane), and the estimator of query q and vector x is
+//   n16 sum_k <alpha_k q_rot, s_k> + gamma r16 <S q_rot, sigma>,
+// a sum of products of real query weights with +-1 planes.  A: the weights, 16 rows = 4
+// queries x 4 base-16 digits, eight digits in two products (x truncated to 32 bits), per
+// plane and 128-coordinate K block; B: one plane word of 16 database vectors per 32-row
+// block, lane (g, n) holding block 4 kb + g of vector n.  Lane (h, n) of a result holds
+// query h's sum for vector n.  Each wave walks 32-vector tiles of the workgroup's database
+// range (the next tile's records in flight) and keeps one top-k list per query (lane i the
+// i-th best); the workgroup's lists of each query (one per wave) are merged at the end.
+constexpr int kMqWaves = 8;   // two per SIMD
+constexpr int kMqTile = 32;   // vectors per wave tile: two 16-vector products
 
 template <int D, int B>
-__global__ __launch_bounds__(64 * kLWaves) void search_lut(SearchParams p) {
-  constexpr int NB = D / 32, W = NB * (B + 1);
-  constexpr int NG = D / 8, NN = D / 4;  // byte and nibble coordinate groups
-  constexpr int VEC = (W % 4 == 0) ? 4 : 2;
-  __shared__ float Tq[NG * 256];
-  __shared__ float Ts[NN * 16];
-  __shared__ float nib[NN * 16];  // nibble sums of q_rot
-  __shared__ float red[2][kLWaves];
-  __shared__ float xs[kLWaves][64];
-  __shared__ int64_t xi[kLWaves][64];
+__global__ __launch_bounds__(64 * kMqWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void search_mxq(SearchParams p) {
+  using tqx::i32x4;
+  using tqx::i32x8;
+  constexpr int NKB = D / 128;              // K blocks of 128 coordinates
+  constexpr int NP = (B == 3) ? 4 : B;      // Walsh planes of the codebook
+  constexpr int WB = B + 1;                 // words per 32-coordinate block (planes, signs)
+  constexpr int W = (D / 32) * WB;          // words per record
+  constexpr int NU = (NP + 1) * NKB;        // A operand units: (plane or signs, K block)
+  constexpr int NG = kMqTile / 16;          // products per tile and K block
+  __shared__ float s_q[4 * 2 * D];          // per query: q_rot, then S q_rot (zero: no query)
+  __shared__ uint32_t s_ak[NU][2][6][64];   // A operands, digits 0-3 and 4-7
+  __shared__ int s_ke[NU][64];              // block exponent of each A lane
+  __shared__ float s_c[4][2];               // per query: constants of the two terms
+  __shared__ float xs[kMqWaves][4][64];
+  __shared__ int64_t xi[kMqWaves][4][64];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int64_t qi = blockIdx.y, split = blockIdx.x;
+  const int64_t split = blockIdx.x;
+  const int nq = (int)p.n_q;                // 1 .. 4
   const int k = p.k;
-  const float* qr = p.ws_q + qi * 2 * D;  // q_rot, then S q_rot
   const int64_t db_begin = split * p.chunk_len;
   const int64_t db_end = db_begin + p.chunk_len < p.n_db ? db_begin + p.chunk_len : p.n_db;
+  const int g = lane >> 4, n = lane & 15, hh = lane >> 4;
 
-  // ---- the first tile is requested before the tables are built
-  uint32_t kw[W], knr = 0;
-  auto fetch = [&](int64_t tt0) {
-    const int64_t v = tt0 + lane;
-    if (v < db_end) {
-      const uint32_t* rec = p.codes + v * W;
-      if constexpr (VEC == 4) {
+  // ---- records of a tile: lane (g, n) holds block 4 kb + g of vector t0 + 16 j + n
+  uint32_t cw[NG][NKB][WB], cn[NG];
+  auto fetch = [&](int64_t t0) {
 #pragma unroll
-        for (int i = 0; i < W / 4; ++i) {
-          const u32x4 x = reinterpret_cast<const u32x4*>(rec)[i];
-          kw[4 * i] = x[0]; kw[4 * i + 1] = x[1]; kw[4 * i + 2] = x[2]; kw[4 * i + 3] = x[3];
+    for (int j = 0; j < NG; ++j) {
+      const int64_t v = t0 + 16 * j + n;
+      if (v < db_end) {
+        const uint32_t* rec = p.codes + v * W;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const uint32_t* bw = rec + (4 * kb + g) * WB;
+          if constexpr (WB == 4) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(bw);
+            cw[j][kb][0] = x[0]; cw[j][kb][1] = x[1]; cw[j][kb][2] = x[2]; cw[j][kb][3] = x[3];
+          } else if constexpr (WB == 2) {
+            const u32x2 x = *reinterpret_cast<const u32x2*>(bw);
+            cw[j][kb][0] = x[0]; cw[j][kb][1] = x[1];
+          } else {
+#pragma unroll
+            for (int i = 0; i < WB; ++i) cw[j][kb][i] = bw[i];
+          }
         }
+        cn[j] = p.norms[v];
       } else {
 #pragma unroll
-        for (int i = 0; i < W / 2; ++i) {
-          const u32x2 x = reinterpret_cast<const u32x2*>(rec)[i];
-          kw[2 * i] = x[0]; kw[2 * i + 1] = x[1];
-        }
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < WB; ++i) cw[j][kb][i] = 0u;
+        cn[j] = 0u;
       }
-      knr = p.norms[v];
     }
   };
-  int64_t t0 = db_begin + (int64_t)wave * 64;
-  fetch(t0);
+  int64_t t0 = db_begin + (int64_t)wave * kMqTile;
+  if (t0 < db_end) fetch(t0);
 
-  for (int i = tid; i < 2 * NN * 16; i += 64 * kLWaves) {  // nibble sums of q_rot, S q_rot
-    const int n = i & 15, g = (i >> 4) % NN, part = i / (NN * 16);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(qr + part * D + 4 * g);
-    const float sum = ((n & 1) ? x[0] : 0.0f) + ((n & 2) ? x[1] : 0.0f) + ((n & 4) ? x[2] : 0.0f) +
-                      ((n & 8) ? x[3] : 0.0f);
-    if (part == 0) nib[i] = sum;
-    else Ts[i - NN * 16] = 2.0f * sum;
-  }
-  {  // sum_j q_rot_j and sum_j (S q_rot)_j
-    float a = 0.0f, c = 0.0f;
-    for (int j = tid; j < D; j += 64 * kLWaves) {
-      a += qr[j];
-      c += qr[D + j];
-    }
-    a = wave_sum_fast(a);
-    c = wave_sum_fast(c);
-    if (lane == 0) {
-      red[0][wave] = a;
-      red[1][wave] = c;
-    }
-  }
+  // ---- the queries' q_rot and S q_rot (from the prologue kernel), zero rows past n_q
+  for (int i = tid; i < 4 * 2 * D; i += 64 * kMqWaves)
+    s_q[i] = i < nq * 2 * D ? p.ws_q[i] : 0.0f;
   __syncthreads();
-  for (int i = tid; i < NG * 256; i += 64 * kLWaves) {  // byte tables from nibble sums
-    const int m = i & 255, g = i >> 8;
-    Tq[i] = nib[(2 * g) * 16 + (m & 15)] + nib[(2 * g + 1) * 16 + (m >> 4)];
-  }
-  float sq = 0.0f, ss = 0.0f;
+  if (wave < 4) {  // per query (wave): the constants left by the D < 3 nibble positions
+    const float* qr = s_q + wave * 2 * D;
+    const float asum = p.alpha[0] + p.alpha[1] + p.alpha[2] + p.alpha[3];
+    float cc = 0.f, cs = 0.f;
 #pragma unroll
-  for (int w = 0; w < kLWaves; ++w) {
-    sq += red[0][w];
-    ss += red[1][w];
-  }
-  const float cq = (p.alpha[0] + p.alpha[1] + p.alpha[2] + p.alpha[3]) * sq;
-  float al[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) al[i] = 2.0f * p.alpha[i];
-  __syncthreads();
-
-  float ls = -INFINITY;
-  int64_t li = INT64_MAX;
-  for (; t0 < db_end; t0 += 64 * kLWaves) {
-    const int64_t v = t0 + lane;
-    const bool valid = v < db_end;
-    uint32_t w[W];
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = kw[i];
-    const uint32_t kn = knr;
-    fetch(t0 + 64 * kLWaves);
-    float mse[1] = {0.0f}, qjl[1] = {0.0f};
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      const uint32_t* wb = w + blk * (B + 1);
-      lut_byte<1>(Tq, 4 * blk, wb[0], al[0], mse);
-      if constexpr (B >= 2) lut_byte<1>(Tq, 4 * blk, wb[1], al[1], mse);
-      if constexpr (B == 3) {
-        lut_byte<1>(Tq, 4 * blk, wb[2], al[2], mse);
-        lut_byte<1>(Tq, 4 * blk, wb[0] ^ wb[1] ^ wb[2], al[3], mse);
+    for (int e = 0; e < D / 64; ++e) {
+      const int j = lane + 64 * e;
+      if ((j & 3) != 3) {
+        cc = fmaf(asum, qr[j], cc);
+        cs += qr[D + j];
       }
-      lut_nib<1>(Ts, 8 * blk, wb[B], qjl);
     }
-    const float n16 = f16_bits_to_f32(kn), r16 = f16_bits_to_f32(kn >> 16);
-    const float sc = n16 * (mse[0] - cq) + p.gamma * r16 * (qjl[0] - ss);
-    uint64_t cand = __ballot(valid && better(sc, v, lane_f(ls, k - 1), lane_i64(li, k - 1)));
-    while (cand) {
-      const int L = __builtin_ctzll(cand);
-      cand &= cand - 1;
-      list_insert(ls, li, lane_f(sc, L), t0 + L, k);
+    cc = wave_sum_fast(cc);
+    cs = wave_sum_fast(cs);
+    if (lane == 0) {
+      s_c[wave][0] = cc;
+      s_c[wave][1] = cs;
     }
   }
-  // ---- the waves' lists into one (wave 0)
-  xs[wave][lane] = ls;
-  xi[wave][lane] = li;
-  __syncthreads();
-  if (wave != 0) return;
+  {  // A operands: unit u = kb (NP + 1) + plane, spread over the waves.  A lane (g, m) holds
+     // row m = (query m / 4, digit m % 4) for K = 32 g + p, coordinate
+     // 128 kb + 32 g + 4 (p % 8) + p / 8, weight f_{p / 8} alpha_k q_rot (planes) or
+     // f_{p / 8} (S q_rot) (signs); x = |a| 2^-e truncated to 32 bits, digits 0-3 and 4-7.
+    const int m = lane & 15, hq = m >> 2, l = m & 3;
+    for (int u = wave; u < NU; u += kMqWaves) {
+      const int kb = u / (NP + 1), kk = u % (NP + 1);
+      const float alpha = kk < NP ? p.alpha[kk] : 1.0f;
+      const float* src = s_q + hq * 2 * D + (kk < NP ? 0 : D) + 128 * kb + 32 * g;
+      float av[32];
+      float amax = 0.f;
 #pragma unroll
-  for (int w2 = 1; w2 < kLWaves; ++w2) {
-    const float s2 = xs[w2][lane];
-    const int64_t i2 = xi[w2][lane];
-    uint64_t cand = __ballot(lane < k && better(s2, i2, lane_f(ls, k - 1), lane_i64(li, k - 1)));
+      for (int q = 0; q < 32; ++q) {
+        const int Dn = q >> 3;
+        const float f = Dn == 0 ? 4.0f : Dn == 1 ? 2.0f : Dn == 2 ? 1.0f : -2.0f;
+        av[q] = f * (alpha * src[4 * (q & 7) + Dn]);
+        amax = fmaxf(amax, fabsf(av[q]));
+      }
+      const int e = tqx::block_exp(amax);
+      uint32_t rr[32];
+#pragma unroll
+      for (int q = 0; q < 32; ++q)
+        rr[q] = e == tqx::kZeroExp ? 0u : (uint32_t)ldexpf(fabsf(av[q]), 32 - e);
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const int sh = (part == 0 ? 28 : 12) - 4 * l;
+        tqx::u32x16 hd16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          hd16[i] = ((rr[2 * i] >> sh) & 15u) | (((rr[2 * i + 1] >> sh) & 15u) << 16) |
+                    ((__float_as_uint(av[2 * i]) >> 16) & 0x8000u) |
+                    (__float_as_uint(av[2 * i + 1]) & 0x80000000u);
+        const i32x8 a = tqx::fp6_row_f16(hd16);
+#pragma unroll
+        for (int r = 0; r < 6; ++r) s_ak[u][part][r][lane] = (uint32_t)a[r];
+      }
+      s_ke[u][lane] = e;
+    }
+  }
+  __syncthreads();
+  i32x8 akh[NU], akl[NU];
+  int ksh[NU], ksl[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      akh[u][r] = r < 6 ? (int)s_ak[u][0][r][lane] : 0;
+      akl[u][r] = r < 6 ? (int)s_ak[u][1][r][lane] : 0;
+    }
+    const int e = s_ke[u][lane];
+    ksh[u] = tqx::digit_scale(e, lane & 3);
+    ksl[u] = tqx::digit_scale(e, 4 + (lane & 3));
+  }
+  const f32x4 c0_c = {-s_c[hh][0], 0.f, 0.f, 0.f}, c0_s = {-s_c[hh][1], 0.f, 0.f, 0.f};
+  const uint32_t ones = __builtin_amdgcn_readfirstlane(0x11111111);
+
+  float ls[4], kth[4];        // per query: the list, and its k-th entry (wave-uniform)
+  int64_t li[4], kid[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    ls[h] = kth[h] = -INFINITY;
+    li[h] = kid[h] = INT64_MAX;
+  }
+  for (; t0 < db_end; t0 += (int64_t)kMqWaves * kMqTile) {
+    uint32_t w[NG][NKB][WB], wn[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      wn[j] = cn[j];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < WB; ++i) w[j][kb][i] = cw[j][kb][i];
+    }
+    const int64_t tn = t0 + (int64_t)kMqWaves * kMqTile;
+    if (tn < db_end) fetch(tn);
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      f32x4 ac = c0_c, as = c0_s;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int u0 = kb * (NP + 1);
+        const i32x4 b0 = tqx::fp4_of(w[j][kb][0], ones);
+        ac = tqx::mma(akh[u0], b0, ac, ksh[u0]);
+        ac = tqx::mma(akl[u0], b0, ac, ksl[u0]);
+        if constexpr (NP >= 2) {
+          const i32x4 b1 = tqx::fp4_of(w[j][kb][1], ones);
+          ac = tqx::mma(akh[u0 + 1], b1, ac, ksh[u0 + 1]);
+          ac = tqx::mma(akl[u0 + 1], b1, ac, ksl[u0 + 1]);
+          if constexpr (NP == 4) {
+            const i32x4 b2 = tqx::fp4_of(w[j][kb][2], ones), b3 = tqx::fp4_xor3(b0, b1, b2);
+            ac = tqx::mma(akh[u0 + 2], b2, ac, ksh[u0 + 2]);
+            ac = tqx::mma(akl[u0 + 2], b2, ac, ksl[u0 + 2]);
+            ac = tqx::mma(akh[u0 + 3], b3, ac, ksh[u0 + 3]);
+            ac = tqx::mma(akl[u0 + 3], b3, ac, ksl[u0 + 3]);
+          }
+        }
+        const i32x4 bs = tqx::fp4_of(w[j][kb][B], ones);
+        as = tqx::mma(akh[u0 + NP], bs, as, ksh[u0 + NP]);
+        as = tqx::mma(akl[u0 + NP], bs, as, ksl[u0 + NP]);
+      }
+      // lane (hh, n): query hh's score of vector t0 + 16 j + n
+      const float dc = (ac[0] + ac[1]) + (ac[2] + ac[3]);
+      const float ds = (as[0] + as[1]) + (as[2] + as[3]);
+      const float n16 = f16_bits_to_f32(wn[j] & 0xFFFFu), r16 = f16_bits_to_f32(wn[j] >> 16);
+      const float sc = fmaf(n16, dc, p.gamma * r16 * ds);
+      const int64_t vb = t0 + 16 * j;
+      const bool valid = vb + n < db_end;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if (h >= nq) break;
+        uint64_t cand = __ballot(hh == h && valid && better(sc, vb + n, kth[h], kid[h]));
+        if (cand) {
+          while (cand) {
+            const int L = __builtin_ctzll(cand);
+            cand &= cand - 1;
+            list_insert(ls[h], li[h], lane_f(sc, L), vb + (L & 15), k);
+          }
+          kth[h] = lane_f(ls[h], k - 1);
+          kid[h] = lane_i64(li[h], k - 1);
+        }
+      }
+    }
+  }
+  // ---- the waves' lists of each query into one (wave h merges query h)
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    xs[wave][h][lane] = ls[h];
+    xi[wave][h][lane] = li[h];
+  }
+  __syncthreads();
+  if (wave >= nq) return;
+  const int h = wave;
+  float ms = xs[0][h][lane];
+  int64_t mi = xi[0][h][lane];
+#pragma unroll
+  for (int w2 = 1; w2 < kMqWaves; ++w2) {
+    const float s2 = xs[w2][h][lane];
+    const int64_t i2 = xi[w2][h][lane];
+    uint64_t cand = __ballot(lane < k && better(s2, i2, lane_f(ms, k - 1), lane_i64(mi, k - 1)));
     while (cand) {
       const int L = __builtin_ctzll(cand);
       cand &= cand - 1;
-      list_insert(ls, li, lane_f(s2, L), lane_i64(i2, L), k);
+      list_insert(ms, mi, lane_f(s2, L), lane_i64(i2, L), k);
     }
   }
   if (lane < k) {
     if (p.n_split == 1) {
-      p.out_scores[qi * k + lane] = ls;
-      p.out_ids[qi * k + lane] = li;
+      p.out_scores[h * k + lane] = ms;
+      p.out_ids[h * k + lane] = mi;
     } else {
-      p.ws_cand_s[(qi * p.n_split + split) * k + lane] = ls;
-      p.ws_cand_i[(qi * p.n_split + split) * k + lane] = li;
+      p.ws_cand_s[((int64_t)h * p.n_split + split) * k + lane] = ms;
+      p.ws_cand_i[((int64_t)h * p.n_split + split) * k + lane] = mi;
     }
   }
 }
@@ -676,8 +788,8 @@ static int launch_search(const SearchParams& p, int64_t n_blocks, hipStream_t st
   hipLaunchKernelGGL(search_prologue<D>, dim3((unsigned)p.n_q, kPrologueSlices), dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   if (p.n_q <= kLutQ)
-    hipLaunchKernelGGL((search_lut<D, B>), dim3((unsigned)p.n_split, (unsigned)p.n_q),
-                       dim3(64 * kLWaves), 0, stream, p);
+    hipLaunchKernelGGL((search_mxq<D, B>), dim3((unsigned)p.n_split), dim3(64 * kMqWaves), 0,
+                       stream, p);
   else
     hipLaunchKernelGGL((search_scan<D, B>), dim3((unsigned)n_blocks, (unsigned)p.n_split),
                        dim3(64 * kSWaves), 0, stream, p);
@@ -700,8 +812,9 @@ tq_search_plan tq_plan_search(int64_t n_q, int32_t k, int64_t n_db, int32_t d) {
   // split the database so that the grid has several rounds of two workgroups per CU of a
   // 256-CU MI355X (a short last round costs less), with at least 16 tiles per split
   int64_t n_split = (2048 + (blocks > 0 ? blocks : 1) - 1) / (blocks > 0 ? blocks : 1);
-  // few queries (one workgroup per query and split): about two workgroups per CU in all
-  if (n_q <= kLutQ) n_split = (512 + (n_q > 0 ? n_q : 1) - 1) / (n_q > 0 ? n_q : 1);
+  // few queries (one workgroup of 8 waves per split for all of them): one workgroup per CU,
+  // two waves per SIMD
+  if (n_q <= kLutQ) n_split = 256;
   const int64_t max_split = (n_db + 16 * kSTile - 1) / (16 * kSTile);
   if (n_split > max_split) n_split = max_split;
   if (n_split > 4096) n_split = 4096;
