@@ -27,8 +27,8 @@
 //   merge:    per query, the lists of the database splits are merged (skipped when there is
 //             one split: the scan then writes the final result); each wave sorts its first
 //             64 candidates whole and screens the rest against its k-th entry.
-// At most four queries take a scan of their own on the block-scaled fp6 x fp4 matrix cores
-// (search_mxq below), which scores all of them from one pass over the records.
+// At most 16 queries take a scan of their own on the block-scaled fp6 x fp4 matrix cores
+// (search_mxq below), which scores each block of four from one pass over the records.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -523,9 +523,9 @@ __global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
   }
 }
 
-// With at most kLutQ queries the batched scan would leave most of its 32 query columns
-// empty: they go to the scan below instead.
-constexpr int kLutQ = 4;
+// With at most kFewQ queries (four blocks of four) the scan below, which reads the database
+// once per block of four, beats the batched scan, which expands it once per 32 queries.
+constexpr int kFewQ = 16;
 
 // ----------------------------------------------------------------------------- few queries
 // on the block-scaled matrix cores.  Up to four queries are scored together by
@@ -541,6 +541,7 @@ constexpr int kLutQ = 4;
 // query h's sum for vector n.  Each wave walks 32-vector tiles of the workgroup's database
 // range (the next tile's records in flight) and keeps one top-k list per query (lane i the
 // i-th best); the workgroup's lists of each query (one per wave) are merged at the end.
+// Grid: (database split, block of four queries).
 constexpr int kMqWaves = 8;   // two per SIMD
 constexpr int kMqTile = 32;   // vectors per wave tile: two 16-vector products
 
@@ -563,7 +564,8 @@ void search_mxq(SearchParams p) {
   __shared__ int64_t xi[kMqWaves][4][64];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int64_t split = blockIdx.x;
-  const int nq = (int)p.n_q;                // 1 .. 4
+  const int64_t q0 = (int64_t)blockIdx.y * 4;   // this workgroup's block of four queries
+  const int nq = (int)(p.n_q - q0 < 4 ? p.n_q - q0 : 4);
   const int k = p.k;
   const int64_t db_begin = split * p.chunk_len;
   const int64_t db_end = db_begin + p.chunk_len < p.n_db ? db_begin + p.chunk_len : p.n_db;
@@ -606,7 +608,7 @@ void search_mxq(SearchParams p) {
 
   // ---- the queries' q_rot and S q_rot (from the prologue kernel), zero rows past n_q
   for (int i = tid; i < 4 * 2 * D; i += 64 * kMqWaves)
-    s_q[i] = i < nq * 2 * D ? p.ws_q[i] : 0.0f;
+    s_q[i] = i < nq * 2 * D ? p.ws_q[q0 * 2 * D + i] : 0.0f;
   __syncthreads();
   if (wave < 4) {  // per query (wave): the constants left by the D < 3 nibble positions
     const float* qr = s_q + wave * 2 * D;
@@ -774,11 +776,11 @@ void search_mxq(SearchParams p) {
   }
   if (lane < k) {
     if (p.n_split == 1) {
-      p.out_scores[h * k + lane] = ms;
-      p.out_ids[h * k + lane] = mi;
+      p.out_scores[(q0 + h) * k + lane] = ms;
+      p.out_ids[(q0 + h) * k + lane] = mi;
     } else {
-      p.ws_cand_s[((int64_t)h * p.n_split + split) * k + lane] = ms;
-      p.ws_cand_i[((int64_t)h * p.n_split + split) * k + lane] = mi;
+      p.ws_cand_s[((q0 + h) * p.n_split + split) * k + lane] = ms;
+      p.ws_cand_i[((q0 + h) * p.n_split + split) * k + lane] = mi;
     }
   }
 }
@@ -787,9 +789,9 @@ template <int D, int B>
 static int launch_search(const SearchParams& p, int64_t n_blocks, hipStream_t stream) {
   hipLaunchKernelGGL(search_prologue<D>, dim3((unsigned)p.n_q, kPrologueSlices), dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
-  if (p.n_q <= kLutQ)
-    hipLaunchKernelGGL((search_mxq<D, B>), dim3((unsigned)p.n_split), dim3(64 * kMqWaves), 0,
-                       stream, p);
+  if (p.n_q <= kFewQ)
+    hipLaunchKernelGGL((search_mxq<D, B>), dim3((unsigned)p.n_split, (unsigned)((p.n_q + 3) / 4)),
+                       dim3(64 * kMqWaves), 0, stream, p);
   else
     hipLaunchKernelGGL((search_scan<D, B>), dim3((unsigned)n_blocks, (unsigned)p.n_split),
                        dim3(64 * kSWaves), 0, stream, p);
@@ -812,9 +814,9 @@ tq_search_plan tq_plan_search(int64_t n_q, int32_t k, int64_t n_db, int32_t d) {
   // split the database so that the grid has several rounds of two workgroups per CU of a
   // 256-CU MI355X (a short last round costs less), with at least 16 tiles per split
   int64_t n_split = (2048 + (blocks > 0 ? blocks : 1) - 1) / (blocks > 0 ? blocks : 1);
-  // few queries (one workgroup of 8 waves per split for all of them): one workgroup per CU,
-  // two waves per SIMD
-  if (n_q <= kLutQ) n_split = 256;
+  // few queries (one workgroup of 8 waves per split and block of four queries): one
+  // workgroup per CU and block, two waves per SIMD
+  if (n_q <= kFewQ) n_split = 256;
   const int64_t max_split = (n_db + 16 * kSTile - 1) / (16 * kSTile);
   if (n_split > max_split) n_split = max_split;
   if (n_split > 4096) n_split = 4096;
