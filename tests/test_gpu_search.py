@@ -110,11 +110,27 @@ def test_search_few_queries_many_splits(torch_gpu, db_60k, n_q, k):
                                                     (3000, 1, 5, 1, 128, 128), (6000, 2, 10, 2, 256, 200),
                                                     (2100, 4, 64, 3, 256, 256)])
 def test_search_few_queries(torch_gpu, n_db, n_q, k, bits, d, d_in):
-    """At most four queries take the per-query table scan (lane = database vector): every
-    supported database format against the oracle's estimator."""
+    """At most four queries take one block of the few-query matrix-core scan: every supported
+    database format against the oracle's estimator."""
     db = TI.search_set(n_db, d_in, seed=5301)
     qs = TI.search_set(n_q, d_in, seed=5302)
     (signs, S), (gsigns, gS) = rotations(d, 5800)
+    fmt = O.Format.uniform(d, bits)
+    qz = oracle_quantize(db, fmt, signs, S)
+    ids, sc = _gpu_search(torch_gpu, qs, qz["records"], qz["norms"], (d, bits, bits, d), gsigns, gS, k)
+    s_o, scale = _oracle_scores(qs, qz["records"], qz["norms"], fmt, signs, S)
+    _check_topk(ids, sc, s_o, RTOL * (np.abs(s_o) + scale), k)
+
+
+@pytest.mark.parametrize("n_db,n_q,k,bits,d,d_in", [(900, 13, 7, 3, 256, 200), (1000, 16, 64, 2, 128, 128),
+                                                    (9000, 5, 10, 3, 256, 256), (9000, 17, 10, 3, 128, 128)])
+def test_search_query_blocks(torch_gpu, n_db, n_q, k, bits, d, d_in):
+    """5 to 16 queries take the few-query scan in blocks of four (a ragged last block); a
+    database of at most 1024 vectors is one split, so the scan writes the results itself;
+    17 queries go to the batched scan."""
+    db = TI.search_set(n_db, d_in, seed=5311)
+    qs = TI.search_set(n_q, d_in, seed=5312)
+    (signs, S), (gsigns, gS) = rotations(d, 5810)
     fmt = O.Format.uniform(d, bits)
     qz = oracle_quantize(db, fmt, signs, S)
     ids, sc = _gpu_search(torch_gpu, qs, qz["records"], qz["norms"], (d, bits, bits, d), gsigns, gS, k)
