@@ -543,6 +543,15 @@ constexpr int kFewQ = 16;
 // i-th best); the workgroup's lists of each query (one per wave) are merged at the end.
 // Grid: (database split, block of four queries).
 constexpr int kMqWaves = 8;   // two per SIMD
+
+// A float as an int whose signed order is the float order (for an LDS maximum), and back.
+__device__ __forceinline__ int ord_of(float f) {
+  const int b = __float_as_int(f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float float_of_ord(int o) {
+  return __int_as_float(o ^ ((o >> 31) & 0x7FFFFFFF));
+}
 constexpr int kMqTile = 32;   // vectors per wave tile: two 16-vector products
 
 template <int D, int B>
@@ -560,6 +569,7 @@ void search_mxq(SearchParams p) {
   __shared__ uint32_t s_ak[NU][2][6][64];   // A operands, digits 0-3 and 4-7
   __shared__ int s_ke[NU][64];              // block exponent of each A lane
   __shared__ float s_c[4][2];               // per query: constants of the two terms
+  __shared__ int s_thr[4];                  // per query: the best k-th score of any wave's list
   __shared__ float xs[kMqWaves][4][64];
   __shared__ int64_t xi[kMqWaves][4][64];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -609,6 +619,7 @@ void search_mxq(SearchParams p) {
   // ---- the queries' q_rot and S q_rot (from the prologue kernel), zero rows past n_q
   for (int i = tid; i < 4 * 2 * D; i += 64 * kMqWaves)
     s_q[i] = i < nq * 2 * D ? p.ws_q[q0 * 2 * D + i] : 0.0f;
+  if (tid < 4) s_thr[tid] = ord_of(-INFINITY);
   __syncthreads();
   if (wave < 4) {  // per query (wave): the constants left by the D < 3 nibble positions
     const float* qr = s_q + wave * 2 * D;
@@ -685,12 +696,12 @@ void search_mxq(SearchParams p) {
   const f32x4 c0_c = {-s_c[hh][0], 0.f, 0.f, 0.f}, c0_s = {-s_c[hh][1], 0.f, 0.f, 0.f};
   const uint32_t ones = __builtin_amdgcn_readfirstlane(0x11111111);
 
-  float ls[4], kth[4];        // per query: the list, and its k-th entry (wave-uniform)
-  int64_t li[4], kid[4];
+  float ls[4];        // per query: the list (lane i the i-th best)
+  int64_t li[4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    ls[h] = kth[h] = -INFINITY;
-    li[h] = kid[h] = INT64_MAX;
+    ls[h] = -INFINITY;
+    li[h] = INT64_MAX;
   }
   for (; t0 < db_end; t0 += (int64_t)kMqWaves * kMqTile) {
     uint32_t w[NG][NKB][WB], wn[NG];
@@ -739,15 +750,21 @@ void search_mxq(SearchParams p) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         if (h >= nq) break;
-        uint64_t cand = __ballot(hh == h && valid && better(sc, vb + n, kth[h], kid[h]));
+        // a score below another wave's k-th score cannot reach the workgroup's top k (that
+        // list already holds k better entries); the shared bound only grows, so an older
+        // value read here is still a valid one
+        const float thr = float_of_ord(s_thr[h]);
+        const float kth = lane_f(ls[h], k - 1);
+        const int64_t kid = lane_i64(li[h], k - 1);
+        uint64_t cand = __ballot(hh == h && valid && sc >= thr && better(sc, vb + n, kth, kid));
         if (cand) {
           while (cand) {
             const int L = __builtin_ctzll(cand);
             cand &= cand - 1;
             list_insert(ls[h], li[h], lane_f(sc, L), vb + (L & 15), k);
           }
-          kth[h] = lane_f(ls[h], k - 1);
-          kid[h] = lane_i64(li[h], k - 1);
+          const float kth2 = lane_f(ls[h], k - 1);
+          if (lane == 0 && kth2 > -INFINITY) atomicMax(&s_thr[h], ord_of(kth2));
         }
       }
     }
