@@ -931,6 +931,14 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "quantize_kernel<128,3,3> (key tensor)",
                          "achieved": round(q_tfs, 3), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(q_tfs / FP32_MFMA_PEAK_TFS, 4), "traffic": trafq},
+            # the same launch against the two other ceilings it could meet: the three fp16
+            # products it issues (hi.hi + hi.lo + lo.hi) against the fp16 MFMA peak, and its
+            # HBM bytes (rocprof traffic, else the algorithmic bytes) against 8 TB/s
+            "roofline_quantize_other": {
+                "fp16_mfma_issued_tflops": round(3 * flops_launch / q_launch / 1e12, 3),
+                "frac_of_fp16_peak": round(3 * flops_launch / q_launch / 1e12 / FP16_MFMA_PEAK_TFS, 4),
+                "hbm_gbs": round((trafq or nvec * (2 * D + rb + 4)) / q_launch / 1e9, 1),
+                "frac_of_hbm_peak": round((trafq or nvec * (2 * D + rb + 4)) / q_launch / 1e9 / HBM_PEAK_GBS, 4)},
             "roofline_decode": {"bound": "hbm", "kernel": "decode_mx_scan+decode_combine",
                                 "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
