@@ -769,6 +769,7 @@ def _search_timing(tq, torch, dev, TI, reps=2, seed=0, samples=None):
     t1 = timed(lambda: tq.ip_search(qs[:1], codes, norms, fmt, tab, k=k, workspace=ws), n_rep=20)
     t4 = timed(lambda: tq.ip_search(qs[:4], codes, norms, fmt, tab, k=k, workspace=ws), n_rep=20)
     t16 = timed(lambda: tq.ip_search(qs[:16], codes, norms, fmt, tab, k=k, workspace=ws), n_rep=10)
+    t20 = timed(lambda: tq.ip_search(qs[:20], codes, norms, fmt, tab, k=k, workspace=ws), n_rep=10)
     t32 = timed(lambda: tq.ip_search(qs[:32], codes, norms, fmt, tab, k=k, workspace=ws), n_rep=10)
     db_bytes = n_db * (fmt.record_bytes() + 4)
     flops = 2.0 * 2 * d * n_db * n_q
@@ -784,6 +785,7 @@ def _search_timing(tq, torch, dev, TI, reps=2, seed=0, samples=None):
             "one_query_pct_hbm_peak": round(100.0 * db_bytes / t1 / 1e9 / HBM_PEAK_GBS, 2),
             "queries_4_us": round(t4 * 1e6, 2), "queries_4_per_s": round(4 / t4, 1),
             "queries_16_us": round(t16 * 1e6, 2), "queries_16_per_s": round(16 / t16, 1),
+            "queries_20_us": round(t20 * 1e6, 2), "queries_20_per_s": round(20 / t20, 1),
             "queries_32_us": round(t32 * 1e6, 2), "queries_32_per_s": round(32 / t32, 1),
             "roofline": {"bound": "mfma", "kernel": "search_scan", "achieved": round(tfs, 3),
                          "peak": FP16_MFMA_PEAK_TFS, "unit": "TFLOP/s",

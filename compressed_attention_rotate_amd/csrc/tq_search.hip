@@ -27,7 +27,7 @@
 //   merge:    per query, the lists of the database splits are merged (skipped when there is
 //             one split: the scan then writes the final result); each wave sorts its first
 //             64 candidates whole and screens the rest against its k-th entry.
-// At most 16 queries take a scan of their own on the block-scaled fp6 x fp4 matrix cores
+// At most 20 queries take a scan of their own on the block-scaled fp6 x fp4 matrix cores
 // (search_mxq below), which scores each block of four from one pass over the records.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -523,9 +523,9 @@ __global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
   }
 }
 
-// With at most kFewQ queries (four blocks of four) the scan below, which reads the database
+// With at most kFewQ queries (five blocks of four) the scan below, which reads the database
 // once per block of four, beats the batched scan, which expands it once per 32 queries.
-constexpr int kFewQ = 16;
+constexpr int kFewQ = 20;
 
 // ----------------------------------------------------------------------------- few queries
 // on the block-scaled matrix cores.  Up to four queries are scored together by

@@ -123,11 +123,12 @@ def test_search_few_queries(torch_gpu, n_db, n_q, k, bits, d, d_in):
 
 
 @pytest.mark.parametrize("n_db,n_q,k,bits,d,d_in", [(900, 13, 7, 3, 256, 200), (1000, 16, 64, 2, 128, 128),
-                                                    (9000, 5, 10, 3, 256, 256), (9000, 17, 10, 3, 128, 128)])
+                                                    (9000, 5, 10, 3, 256, 256), (9000, 20, 10, 3, 128, 128),
+                                                    (9000, 21, 10, 3, 128, 128)])
 def test_search_query_blocks(torch_gpu, n_db, n_q, k, bits, d, d_in):
-    """5 to 16 queries take the few-query scan in blocks of four (a ragged last block); a
+    """5 to 20 queries take the few-query scan in blocks of four (a ragged last block); a
     database of at most 1024 vectors is one split, so the scan writes the results itself;
-    17 queries go to the batched scan."""
+    21 queries go to the batched scan."""
     db = TI.search_set(n_db, d_in, seed=5311)
     qs = TI.search_set(n_q, d_in, seed=5312)
     (signs, S), (gsigns, gS) = rotations(d, 5810)
