@@ -527,6 +527,15 @@ __global__ __launch_bounds__(64 * kMWaves) void search_merge(SearchParams p) {
 // once per block of four, beats the batched scan, which expands it once per 32 queries.
 constexpr int kFewQ = 20;
 
+// A float as an int whose signed order is the float order (for an LDS maximum), and back.
+__device__ __forceinline__ int ord_of(float f) {
+  const int b = __float_as_int(f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float float_of_ord(int o) {
+  return __int_as_float(o ^ ((o >> 31) & 0x7FFFFFFF));
+}
+
 // ----------------------------------------------------------------------------- few queries
 // on the block-scaled matrix cores.  Up to four queries are scored together by
 // v_mfma_scale_f32_16x16x128_f8f6f4 straight from the records (the operand encodings are
@@ -543,15 +552,6 @@ constexpr int kFewQ = 20;
 // i-th best); the workgroup's lists of each query (one per wave) are merged at the end.
 // Grid: (database split, block of four queries).
 constexpr int kMqWaves = 8;   // two per SIMD
-
-// A float as an int whose signed order is the float order (for an LDS maximum), and back.
-__device__ __forceinline__ int ord_of(float f) {
-  const int b = __float_as_int(f);
-  return b ^ ((b >> 31) & 0x7FFFFFFF);
-}
-__device__ __forceinline__ float float_of_ord(int o) {
-  return __int_as_float(o ^ ((o >> 31) & 0x7FFFFFFF));
-}
 constexpr int kMqTile = 32;   // vectors per wave tile: two 16-vector products
 
 template <int D, int B>
